@@ -1,0 +1,305 @@
+"""Plain fp64 CPU oracle for Cut Cross-Entropy (linear projection + cross-entropy).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The product (the HIP library and its
+Python binding) never imports, links or calls it, and it shares no code with
+the product: it is written from the definitions on the pages, materialises the
+logits, and is slow on purpose.
+
+What is computed (all in float64, from operands passed in exactly as the GPU
+sees them: bf16 values upcast exactly, or fp32):
+
+  Z = E C^T                       logits, materialised here only
+                                  (mlx-cross-entropy README, "Usage": the
+                                  standard path that forms hidden @ classifier.T)
+  LSE_i = m_i + ln sum_j exp(Z_ij - m_i),  m_i = max_j Z_ij
+                                  (tirogla "Loss functions", "How it works"
+                                  step 1: log-sum-exp with max subtraction)
+  loss_i = LSE_i - Z_{i,y_i}      (Kamath blog: loss = -correct_token + LSE;
+                                  Wijmans et al. abstract: only the correct
+                                  token's logit plus the log-sum-exp)
+  rows with y_i == ignore_index give loss 0 and gradient 0, and are not counted
+                                  (README "API" ignore_index; tirogla "Code":
+                                  ignored rows' gradient is zero, mean over
+                                  non-ignored rows with the count floored at 1)
+  reduction: none -> loss_i; sum -> sum_i loss_i; mean -> sum / max(n_valid, 1)
+                                  (README "API" and "Computing related
+                                  quantities"; tirogla step 4)
+  G = (softmax(Z) - onehot(y)) * scale_i
+                                  (tirogla step 2: fused softmax+CE gradient
+                                  p - y)
+  dE = G C,  dC = G^T E           (chain rule through Z = E C^T)
+  scale_i = g / max(n_valid,1) (mean), g (sum), g_i (none); 0 on ignored rows.
+
+Gradient filtering (README "How it works" item 2; Wijmans et al. abstract:
+skip gradient entries below numerical precision) is modelled by
+`filter_keep`: a tile (row block b, vocab block v) of G is kept iff some valid
+row i in b has max_{j in v} softmax_ij >= 2^-12, or some valid row in b has
+its target in v.  `backward(..., keep=...)` zeroes G on dropped tiles.  The
+target-tile rule and the strict "< 2^-12 everywhere" reading are this
+implementation's readings of a criterion the pages state only loosely.
+
+Every function here is pinned by tests/test_oracle_pins.py against closed
+forms, brute force, finite differences and invariants.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+FILTER_LOG_THRESHOLD = -12.0 * math.log(2.0)   # ln(2^-12)
+_ROW_CHUNK = 256
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def valid_rows(targets, V: int, ignore_index: int = -100) -> np.ndarray:
+    """Boolean mask of non-ignored rows; any other target outside [0, V) is an error."""
+    t = np.asarray(targets, dtype=np.int64)
+    valid = t != ignore_index
+    bad = valid & ((t < 0) | (t >= V))
+    if bad.any():
+        raise ValueError(f"{int(bad.sum())} target(s) outside [0, {V}) that are not ignore_index")
+    return valid
+
+
+def logits(e, c) -> np.ndarray:
+    """Z = E C^T in float64 (the materialised logit matrix)."""
+    return _f64(e) @ _f64(c).T
+
+
+def row_logsumexp(z: np.ndarray) -> np.ndarray:
+    """LSE of each row of z by max subtraction."""
+    m = z.max(axis=1)
+    return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+
+
+@dataclass
+class Forward:
+    loss: np.ndarray        # scalar array (mean/sum) or [N] (none)
+    nll: np.ndarray         # [N] per-row loss, 0 on ignored rows
+    lse: np.ndarray         # [N] LSE of every row (ignored rows included)
+    n_valid: int
+    valid: np.ndarray       # [N] bool
+
+
+def reduce_loss(nll: np.ndarray, n_valid: int, reduction: str) -> np.ndarray:
+    if reduction == "none":
+        return nll.copy()
+    s = float(np.sum(nll))
+    if reduction == "sum":
+        return np.array(s)
+    if reduction == "mean":
+        return np.array(s / max(n_valid, 1))
+    raise ValueError(reduction)
+
+
+def forward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
+            rows=None) -> Forward:
+    """Loss and per-row LSE.  `rows` restricts the work to a subset of rows
+    (then `loss` is the reduction over that subset only and n_valid counts it)."""
+    e = _f64(e)
+    c = _f64(c)
+    t = np.asarray(targets, dtype=np.int64)
+    V = c.shape[0]
+    idx = np.arange(e.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    valid = valid_rows(t[idx], V, ignore_index)
+    lse = np.empty(len(idx))
+    nll = np.zeros(len(idx))
+    for s in range(0, len(idx), _ROW_CHUNK):
+        sl = slice(s, s + _ROW_CHUNK)
+        z = logits(e[idx[sl]], c)
+        lse[sl] = row_logsumexp(z)
+        v = valid[sl]
+        r = np.nonzero(v)[0]
+        nll[sl][r] = lse[sl][r] - z[r, t[idx[sl]][r]]
+    n_valid = int(valid.sum())
+    return Forward(reduce_loss(nll, n_valid, reduction), nll, lse, n_valid, valid)
+
+
+def grad_scale(valid: np.ndarray, reduction: str, grad_loss=1.0) -> np.ndarray:
+    """Per-row factor multiplying (softmax - onehot): d(loss)/d(nll_i) times the
+    upstream gradient; 0 on ignored rows."""
+    n_valid = int(valid.sum())
+    if reduction == "none":
+        g = np.broadcast_to(_f64(grad_loss), valid.shape).astype(np.float64)
+    elif reduction == "sum":
+        g = np.full(valid.shape, float(grad_loss))
+    elif reduction == "mean":
+        g = np.full(valid.shape, float(grad_loss) / max(n_valid, 1))
+    else:
+        raise ValueError(reduction)
+    return np.where(valid, g, 0.0)
+
+
+def tile_row_max(z: np.ndarray, Bv: int) -> np.ndarray:
+    """max_{j in vocab block v} Z_ij for each row i and block v = j // Bv."""
+    n, V = z.shape
+    nvb = -(-V // Bv)
+    pad = nvb * Bv - V
+    if pad:
+        z = np.concatenate([z, np.full((n, pad), -np.inf)], axis=1)
+    return z.reshape(n, nvb, Bv).max(axis=2)
+
+
+def filter_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100,
+                lse=None) -> np.ndarray:
+    """Keep map [ceil(N/Bn), ceil(V/Bv)] of (row block, vocab block) tiles of G.
+
+    Kept iff some valid row i of the block has max_j softmax_ij >= 2^-12 on the
+    tile, i.e. max_j Z_ij - LSE_i >= -12 ln 2, or some valid row of the block
+    has its target inside the tile's vocab range.
+    """
+    e = _f64(e)
+    c = _f64(c)
+    t = np.asarray(targets, dtype=np.int64)
+    N, V = e.shape[0], c.shape[0]
+    valid = valid_rows(t, V, ignore_index)
+    nb, nvb = -(-N // Bn), -(-V // Bv)
+    keep = np.zeros((nb, nvb), dtype=bool)
+    for b in range(nb):
+        r0, r1 = b * Bn, min(N, (b + 1) * Bn)
+        z = logits(e[r0:r1], c)
+        l = row_logsumexp(z) if lse is None else _f64(lse)[r0:r1]
+        tm = tile_row_max(z, Bv) - l[:, None]          # log of the tile's max softmax
+        v = valid[r0:r1]
+        if v.any():
+            keep[b] |= (tm[v] >= FILTER_LOG_THRESHOLD).any(axis=0)
+            keep[b, t[r0:r1][v] // Bv] = True
+    return keep
+
+
+def softmax_grad_rows(z: np.ndarray, lse: np.ndarray, t: np.ndarray, scale: np.ndarray,
+                      valid: np.ndarray) -> np.ndarray:
+    """G rows: (exp(Z - LSE) - onehot(t)) * scale, zero on ignored rows."""
+    g = np.exp(z - lse[:, None])
+    r = np.nonzero(valid)[0]
+    g[r, t[r]] -= 1.0
+    g *= scale[:, None]
+    g[~valid] = 0.0
+    return g
+
+
+@dataclass
+class Backward:
+    dE: np.ndarray
+    dC: np.ndarray
+
+
+def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
+             grad_loss=1.0, keep=None, tile=None) -> Backward:
+    """dE = G C and dC = G^T E.  With `keep` (a filter_keep map for `tile` =
+    (Bn, Bv)) G is zeroed on the dropped tiles first."""
+    e = _f64(e)
+    c = _f64(c)
+    t = np.asarray(targets, dtype=np.int64)
+    N, V = e.shape[0], c.shape[0]
+    valid = valid_rows(t, V, ignore_index)
+    scale = grad_scale(valid, reduction, grad_loss)
+    dE = np.zeros_like(e)
+    dC = np.zeros_like(c)
+    chunk = _ROW_CHUNK if keep is None else tile[0]
+    for s in range(0, N, chunk):
+        sl = slice(s, min(N, s + chunk))
+        z = logits(e[sl], c)
+        lse = row_logsumexp(z)
+        g = softmax_grad_rows(z, lse, t[sl], scale[sl], valid[sl])
+        if keep is not None:
+            Bn, Bv = tile
+            colmask = np.repeat(keep[s // Bn], Bv)[:V]
+            g[:, ~colmask] = 0.0
+        dE[sl] = g @ c
+        dC += g.T @ e[sl]
+    return Backward(dE, dC)
+
+
+# ---------------------------------------------------------------------------
+# Sampled forms for large shapes: the same definitions evaluated on a subset of
+# output rows, so full-size checks stay within seconds to a minute.
+# ---------------------------------------------------------------------------
+
+def lse_all(e, c, chunk: int = _ROW_CHUNK) -> np.ndarray:
+    """LSE of every row (the full materialised pass, row chunk by row chunk)."""
+    e = _f64(e)
+    c = _f64(c)
+    out = np.empty(e.shape[0])
+    for s in range(0, e.shape[0], chunk):
+        out[s:s + chunk] = row_logsumexp(logits(e[s:s + chunk], c))
+    return out
+
+
+def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100):
+    """One pass over all row blocks giving LSE [N] and the filter keep map."""
+    e = _f64(e)
+    c = _f64(c)
+    t = np.asarray(targets, dtype=np.int64)
+    N, V = e.shape[0], c.shape[0]
+    valid = valid_rows(t, V, ignore_index)
+    nb, nvb = -(-N // Bn), -(-V // Bv)
+    keep = np.zeros((nb, nvb), dtype=bool)
+    lse = np.empty(N)
+    for b in range(nb):
+        r0, r1 = b * Bn, min(N, (b + 1) * Bn)
+        z = logits(e[r0:r1], c)
+        l = row_logsumexp(z)
+        lse[r0:r1] = l
+        tm = tile_row_max(z, Bv) - l[:, None]
+        v = valid[r0:r1]
+        if v.any():
+            keep[b] |= (tm[v] >= FILTER_LOG_THRESHOLD).any(axis=0)
+            keep[b, t[r0:r1][v] // Bv] = True
+    return lse, keep
+
+
+def dE_rows(e, c, targets, rows, ignore_index: int = -100, reduction: str = "mean",
+            grad_loss=1.0, n_valid: int | None = None, keep=None, tile=None) -> np.ndarray:
+    """dE for selected rows: row i of G C needs only row i of Z.  For mean,
+    n_valid is the whole batch's count (pass it in); for none, grad_loss is [N]."""
+    e = _f64(e)
+    c = _f64(c)
+    t = np.asarray(targets, dtype=np.int64)
+    V = c.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    valid_all = valid_rows(t, V, ignore_index)
+    if n_valid is None:
+        n_valid = int(valid_all.sum())
+    if reduction == "mean":
+        scale = np.where(valid_all[rows], float(grad_loss) / max(n_valid, 1), 0.0)
+    else:
+        scale = grad_scale(valid_all, reduction, grad_loss)[rows]
+    z = logits(e[rows], c)
+    lse = row_logsumexp(z)
+    g = softmax_grad_rows(z, lse, t[rows], scale, valid_all[rows])
+    if keep is not None:
+        Bn, Bv = tile
+        for k, i in enumerate(rows):
+            colmask = np.repeat(keep[i // Bn], Bv)[:V]
+            g[k, ~colmask] = 0.0
+    return g @ c
+
+
+def dC_rows(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction: str = "mean",
+            grad_loss=1.0, keep=None, tile=None) -> np.ndarray:
+    """dC for selected vocabulary rows j: dC_j = sum_i G_ij e_i, which needs
+    column j of Z for all rows and every row's LSE (pass the oracle's own)."""
+    e = _f64(e)
+    c = _f64(c)
+    t = np.asarray(targets, dtype=np.int64)
+    V = c.shape[0]
+    vocab_ids = np.asarray(vocab_ids, dtype=np.int64)
+    valid = valid_rows(t, V, ignore_index)
+    scale = grad_scale(valid, reduction, grad_loss)
+    zc = e @ c[vocab_ids].T                              # [N, k] = Z[:, vocab_ids]
+    g = np.exp(zc - _f64(lse)[:, None])
+    g -= (t[:, None] == vocab_ids[None, :])
+    g *= scale[:, None]
+    g[~valid] = 0.0
+    if keep is not None:
+        Bn, Bv = tile
+        rowblk = np.arange(e.shape[0]) // Bn
+        g *= keep[rowblk][:, vocab_ids // Bv]
+    return g.T @ e

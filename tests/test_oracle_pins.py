@@ -1,0 +1,376 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself:
+closed forms, brute force in plain Python, finite differences, invariants and
+the values printed by the pages' self-tests (tests/golden/).
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term, a
+wrong sign, a transposed operand, a wrong index or count) fails it.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _rand(seed, N, D, V, scale=1.0):
+    g = np.random.default_rng(seed)
+    e = g.standard_normal((N, D)) * scale
+    c = g.standard_normal((V, D)) * scale
+    t = g.integers(0, V, N)
+    return e, c, t
+
+
+# --------------------------------------------------------------------------- golden
+def test_golden_zero_logits_1000():
+    (V, expect, dec), = _read_golden("zero_logits_1000.txt")
+    V, dec = int(V), int(dec)
+    e = np.ones((1, 3))
+    c = np.zeros((V, 3))
+    f = O.forward(e, c, [0], reduction="mean")
+    assert round(float(f.loss), dec) == float(expect)
+    assert abs(float(f.loss) - math.log(1000.0)) < 1e-12
+
+
+def test_golden_large_logit_finite():
+    (z0, z1, tgt, expect), = _read_golden("large_logit.txt")
+    # e = [1], c = [[z0], [z1]] gives the logits (z0, z1).
+    e = np.array([[1.0]])
+    c = np.array([[float(z0)], [float(z1)]])
+    f = O.forward(e, c, [int(tgt)], reduction="none")
+    assert np.isfinite(f.nll).all() and np.isfinite(f.lse).all()
+    assert abs(float(f.nll[0]) - float(expect)) < 1e-9
+    b = O.backward(e, c, [int(tgt)], reduction="sum")
+    assert np.isfinite(b.dE).all() and np.isfinite(b.dC).all()
+    # p = (1, ~0); G = p - onehot(1) = (1, -1): dE = 1*z0 - 1*z1
+    assert abs(b.dE[0, 0] - (float(z0) - float(z1))) < 1e-9
+
+
+# --------------------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_zero_classifier_closed_form(reduction):
+    """c = 0: every logit is 0, so LSE = ln V, loss = ln V on valid rows,
+    G = (1/V - onehot) * scale, dE = 0, dC_j = sum_i scale_i (1/V - [t_i = j]) e_i."""
+    N, D, V = 9, 5, 13
+    g = np.random.default_rng(3)
+    e = g.standard_normal((N, D))
+    c = np.zeros((V, D))
+    t = g.integers(0, V, N)
+    t[[2, 7]] = -100
+    nv = N - 2
+    gl = g.standard_normal(N) if reduction == "none" else 0.7
+    f = O.forward(e, c, t, reduction=reduction)
+    assert np.allclose(f.lse, math.log(V), atol=1e-13, rtol=0)
+    nll_expect = np.array([0.0 if ti == -100 else math.log(V) for ti in t])
+    assert np.allclose(f.nll, nll_expect, atol=1e-13, rtol=0)
+    if reduction == "mean":
+        assert abs(float(f.loss) - math.log(V)) < 1e-13
+    elif reduction == "sum":
+        assert abs(float(f.loss) - nv * math.log(V)) < 1e-12
+    b = O.backward(e, c, t, reduction=reduction, grad_loss=gl)
+    assert np.array_equal(b.dE, np.zeros_like(e))
+    dC = np.zeros((V, D))
+    for i in range(N):
+        if t[i] == -100:
+            continue
+        s = gl[i] if reduction == "none" else (gl / nv if reduction == "mean" else gl)
+        for j in range(V):
+            dC[j] += s * ((1.0 / V) - (1.0 if j == t[i] else 0.0)) * e[i]
+    assert np.allclose(b.dC, dC, atol=1e-13, rtol=1e-12)
+
+
+def test_single_class_vocab():
+    """V = 1: softmax is 1 on the target, so loss and gradients vanish."""
+    g = np.random.default_rng(4)
+    e, c = g.standard_normal((6, 4)), g.standard_normal((1, 4))
+    t = np.zeros(6, dtype=np.int64)
+    f = O.forward(e, c, t, reduction="sum")
+    assert abs(float(f.loss)) < 1e-12
+    b = O.backward(e, c, t, reduction="mean")
+    assert np.abs(b.dE).max() < 1e-15 and np.abs(b.dC).max() < 1e-15
+
+
+def test_two_class_is_logistic():
+    """V = 2 reduces to the logistic loss softplus(z_other - z_target) and its
+    gradient sigmoid(z_other - z_target) on the other class."""
+    g = np.random.default_rng(5)
+    N, D = 11, 3
+    e, c = g.standard_normal((N, D)) * 3, g.standard_normal((2, D))
+    t = g.integers(0, 2, N)
+    z = e @ c.T
+    d = z[np.arange(N), 1 - t] - z[np.arange(N), t]
+    f = O.forward(e, c, t, reduction="none")
+    assert np.allclose(f.nll, np.logaddexp(0.0, d), rtol=1e-13, atol=1e-14)
+    sig = 1.0 / (1.0 + np.exp(-d))
+    # dE_i = sig*(c_other - c_target) for reduction sum
+    b = O.backward(e, c, t, reduction="sum")
+    dE = sig[:, None] * (c[1 - t] - c[t])
+    assert np.allclose(b.dE, dE, rtol=1e-12, atol=1e-14)
+
+
+def test_shift_invariance():
+    """Appending a constant feature 1 to every e_i and k to every c_j shifts
+    every logit by k: LSE shifts by k and the loss does not change."""
+    e, c, t = _rand(6, 7, 4, 9)
+    for k in (0.0, 3.5, -40.0):
+        e2 = np.concatenate([e, np.ones((7, 1))], axis=1)
+        c2 = np.concatenate([c, np.full((9, 1), k)], axis=1)
+        f1 = O.forward(e, c, t, reduction="none")
+        f2 = O.forward(e2, c2, t, reduction="none")
+        assert np.allclose(f2.nll, f1.nll, rtol=1e-12, atol=1e-12)
+        assert np.allclose(f2.lse, f1.lse + k, rtol=1e-12, atol=1e-12)
+
+
+def test_translating_classifier_leaves_dE():
+    """Each valid row of G sums to zero, so adding one vector u to every c_j
+    changes no logit difference and leaves dE unchanged."""
+    e, c, t = _rand(7, 6, 5, 8)
+    u = np.random.default_rng(70).standard_normal(5)
+    b1 = O.backward(e, c, t, reduction="mean")
+    b2 = O.backward(e, c + u, t, reduction="mean")
+    # dE depends on c through G C; with Z shifted by e_i.u per row G is unchanged
+    # and G (C + u) = G C + (G 1) u^T = G C.
+    assert np.allclose(b2.dE, b1.dE, rtol=1e-11, atol=1e-13)
+
+
+def test_gradient_rows_sum_to_zero():
+    e, c, t = _rand(8, 10, 6, 17)
+    t[3] = -100
+    z = e @ c.T
+    lse = O.row_logsumexp(z)
+    valid = t != -100
+    s = O.grad_scale(valid, "sum")
+    g = O.softmax_grad_rows(z, lse, t, s, valid)
+    assert np.abs(g.sum(axis=1)).max() < 1e-14
+    assert np.array_equal(g[3], np.zeros(17))
+    # target column carries p - 1 < 0; others p > 0
+    for i in np.nonzero(valid)[0]:
+        assert g[i, t[i]] < 0 and (np.delete(g[i], t[i]) > 0).all()
+
+
+# --------------------------------------------------------------------------- brute force
+def _brute(e, c, t, reduction, gl, ignore=-100):
+    """Loops in plain Python floats: probabilities by exp(z)/sum exp(z)
+    (no max subtraction; the inputs are small), loss = -ln p_target."""
+    N, D = len(e), len(e[0])
+    V = len(c)
+    z = [[sum(float(e[i][d]) * float(c[j][d]) for d in range(D)) for j in range(V)] for i in range(N)]
+    valid = [int(t[i]) != ignore for i in range(N)]
+    nv = sum(valid)
+    nll, lse, p = [], [], []
+    for i in range(N):
+        den = sum(math.exp(z[i][j]) for j in range(V))
+        lse.append(math.log(den))
+        p.append([math.exp(z[i][j]) / den for j in range(V)])
+        nll.append(-math.log(p[i][int(t[i])]) if valid[i] else 0.0)
+    if reduction == "none":
+        loss = nll
+        sc = [gl[i] if valid[i] else 0.0 for i in range(N)]
+    elif reduction == "sum":
+        loss = sum(nll)
+        sc = [gl if valid[i] else 0.0 for i in range(N)]
+    else:
+        loss = sum(nll) / max(nv, 1)
+        sc = [gl / max(nv, 1) if valid[i] else 0.0 for i in range(N)]
+    G = [[(p[i][j] - (1.0 if j == int(t[i]) else 0.0)) * sc[i] for j in range(V)] for i in range(N)]
+    dE = [[sum(G[i][j] * float(c[j][d]) for j in range(V)) for d in range(D)] for i in range(N)]
+    dC = [[sum(G[i][j] * float(e[i][d]) for i in range(N)) for d in range(D)] for j in range(V)]
+    return loss, nll, lse, nv, np.array(dE), np.array(dC)
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_brute_force_tiny(reduction, seed):
+    g = np.random.default_rng(100 + seed)
+    N, D, V = int(g.integers(1, 9)), int(g.integers(1, 5)), int(g.integers(2, 17))
+    e = g.standard_normal((N, D))
+    c = g.standard_normal((V, D))
+    t = g.integers(0, V, N)
+    if N > 2:
+        t[g.integers(0, N)] = -100
+    gl = list(g.standard_normal(N)) if reduction == "none" else 1.3
+    loss, nll, lse, nv, dE, dC = _brute(e, c, t, reduction, gl)
+    f = O.forward(e, c, t, reduction=reduction)
+    assert f.n_valid == nv
+    assert np.allclose(f.nll, nll, rtol=1e-12, atol=1e-13)
+    assert np.allclose(f.lse, lse, rtol=1e-12, atol=1e-13)
+    assert np.allclose(f.loss, loss, rtol=1e-12, atol=1e-13)
+    b = O.backward(e, c, t, reduction=reduction, grad_loss=np.array(gl) if reduction == "none" else gl)
+    assert np.allclose(b.dE, dE, rtol=1e-11, atol=1e-13)
+    assert np.allclose(b.dC, dC, rtol=1e-11, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- finite differences
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_finite_differences(reduction):
+    """Central differences of the fp64 loss (h = 1e-6) against dE and dC; for
+    `none` the objective is sum_i g_i loss_i with a random upstream g."""
+    g = np.random.default_rng(11)
+    N, D, V = 5, 3, 7
+    e, c = g.standard_normal((N, D)), g.standard_normal((V, D))
+    t = g.integers(0, V, N)
+    t[1] = -100
+    gl = g.standard_normal(N) if reduction == "none" else 0.8
+
+    def obj(ee, cc):
+        f = O.forward(ee, cc, t, reduction=reduction)
+        return float(np.dot(gl, f.loss)) if reduction == "none" else gl * float(f.loss)
+
+    b = O.backward(e, c, t, reduction=reduction, grad_loss=gl)
+    h = 1e-6
+    for arr, grad in ((e, b.dE), (c, b.dC)):
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = obj(e, c)
+            arr[idx] = old - h
+            lm = obj(e, c)
+            arr[idx] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[idx]) < 1e-7 + 1e-6 * abs(fd), (idx, fd, grad[idx])
+
+
+# --------------------------------------------------------------------------- mask / counts
+def test_ignore_rows_and_counts():
+    e, c, t = _rand(12, 10, 4, 11)
+    t[[0, 4, 9]] = -100
+    f = O.forward(e, c, t, reduction="none")
+    assert f.n_valid == 7
+    assert (f.nll[[0, 4, 9]] == 0.0).all()
+    fs = O.forward(e, c, t, reduction="sum")
+    fm = O.forward(e, c, t, reduction="mean")
+    assert abs(float(fs.loss) - f.nll.sum()) < 1e-12
+    assert abs(float(fm.loss) - f.nll.sum() / 7) < 1e-12
+    b = O.backward(e, c, t, reduction="mean")
+    assert (b.dE[[0, 4, 9]] == 0.0).all()
+    # ignored rows contribute nothing to dC: dropping them changes nothing
+    keep = np.array([i not in (0, 4, 9) for i in range(10)])
+    b2 = O.backward(e[keep], c, t[keep], reduction="sum", grad_loss=1.0 / 7)
+    assert np.allclose(b.dC, b2.dC, rtol=1e-12, atol=1e-14)
+
+
+def test_all_ignored_mean_is_zero():
+    e, c, t = _rand(13, 4, 3, 5)
+    t[:] = -100
+    f = O.forward(e, c, t, reduction="mean")
+    assert f.n_valid == 0 and float(f.loss) == 0.0
+    b = O.backward(e, c, t, reduction="mean")
+    assert not b.dE.any() and not b.dC.any()
+
+
+def test_custom_ignore_index():
+    e, c, t = _rand(14, 6, 3, 5)
+    t[2] = 3
+    f1 = O.forward(e, c, t, ignore_index=3, reduction="none")
+    assert f1.nll[2] == 0.0 and f1.n_valid == 6 - int((t == 3).sum())
+
+
+def test_out_of_range_target_raises():
+    e, c, t = _rand(15, 4, 3, 5)
+    t[1] = 5
+    with pytest.raises(ValueError):
+        O.forward(e, c, t)
+    t[1] = -7
+    with pytest.raises(ValueError):
+        O.forward(e, c, t)
+
+
+# --------------------------------------------------------------------------- filtering
+def _brute_keep(e, c, t, Bn, Bv, ignore=-100):
+    N, V = len(e), len(c)
+    z = e @ c.T
+    nb, nvb = -(-N // Bn), -(-V // Bv)
+    keep = np.zeros((nb, nvb), dtype=bool)
+    for i in range(N):
+        if t[i] == ignore:
+            continue
+        den = sum(math.exp(z[i, j]) for j in range(V))
+        for j in range(V):
+            if math.exp(z[i, j]) / den >= 2.0 ** -12 or j == t[i]:
+                keep[i // Bn, j // Bv] = True
+    return keep
+
+
+@pytest.mark.parametrize("Bn,Bv", [(2, 3), (4, 8), (3, 5)])
+def test_filter_keep_brute_force(Bn, Bv):
+    g = np.random.default_rng(21)
+    N, D, V = 11, 4, 37
+    e, c = g.standard_normal((N, D)) * 5.0, g.standard_normal((V, D)) * 2.5
+    t = g.integers(0, V, N)
+    t[5] = -100
+    keep = O.filter_keep(e, c, t, Bn, Bv)
+    assert np.array_equal(keep, _brute_keep(e, c, t, Bn, Bv))
+    assert 0 < keep.sum() < keep.size       # the case exercises both outcomes
+    lse, keep2 = O.lse_and_keep(e, c, t, Bn, Bv)
+    assert np.array_equal(keep, keep2)
+
+
+def test_filtered_backward_drops_exactly_the_dropped_tiles():
+    g = np.random.default_rng(22)
+    N, D, V, Bn, Bv = 12, 4, 40, 3, 8
+    e, c = g.standard_normal((N, D)) * 2.5, g.standard_normal((V, D)) * 1.5
+    t = g.integers(0, V, N)
+    keep = O.filter_keep(e, c, t, Bn, Bv)
+    full = O.backward(e, c, t, reduction="sum")
+    filt = O.backward(e, c, t, reduction="sum", keep=keep, tile=(Bn, Bv))
+    # independent: sum of the dropped G entries' contributions, with loops
+    z = e @ c.T
+    dE = full.dE.copy()
+    dC = full.dC.copy()
+    for i in range(N):
+        den = np.exp(z[i]).sum()
+        for j in range(V):
+            if not keep[i // Bn, j // Bv]:
+                gij = math.exp(z[i, j]) / den - (1.0 if j == t[i] else 0.0)
+                assert abs(gij) < 2.0 ** -12      # only sub-threshold entries are dropped
+                dE[i] -= gij * c[j]
+                dC[j] -= gij * e[i]
+    assert np.allclose(filt.dE, dE, rtol=1e-12, atol=1e-14)
+    assert np.allclose(filt.dC, dC, rtol=1e-12, atol=1e-14)
+    # keep everything -> exact
+    allk = np.ones_like(keep)
+    b = O.backward(e, c, t, reduction="sum", keep=allk, tile=(Bn, Bv))
+    assert np.allclose(b.dE, full.dE, rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------------------------------- sampled forms
+def test_sampled_forms_match_full():
+    g = np.random.default_rng(31)
+    N, D, V, Bn, Bv = 40, 6, 50, 8, 16
+    e, c = g.standard_normal((N, D)) * 2.0, g.standard_normal((V, D))
+    t = g.integers(0, V, N)
+    t[[3, 17]] = -100
+    for red in ("mean", "sum", "none"):
+        gl = g.standard_normal(N) if red == "none" else 1.7
+        f = O.forward(e, c, t, reduction=red)
+        b = O.backward(e, c, t, reduction=red, grad_loss=gl)
+        rows = np.array([0, 3, 9, 39])
+        fr = O.forward(e, c, t, reduction="none", rows=rows)
+        assert np.allclose(fr.lse, f.lse[rows], rtol=1e-14)
+        assert np.allclose(fr.nll, f.nll[rows], rtol=1e-14)
+        assert np.allclose(O.dE_rows(e, c, t, rows, reduction=red, grad_loss=gl), b.dE[rows],
+                           rtol=1e-12, atol=1e-15)
+        vid = np.array([0, 7, 49, int(t[0])])
+        lse = O.lse_all(e, c, chunk=7)
+        assert np.allclose(lse, f.lse, rtol=1e-14)
+        assert np.allclose(O.dC_rows(e, c, t, vid, lse, reduction=red, grad_loss=gl), b.dC[vid],
+                           rtol=1e-12, atol=1e-15)
+    lse, keep = O.lse_and_keep(e, c, t, Bn, Bv)
+    bf = O.backward(e, c, t, reduction="mean", keep=keep, tile=(Bn, Bv))
+    assert np.allclose(O.dE_rows(e, c, t, [1, 20], keep=keep, tile=(Bn, Bv)), bf.dE[[1, 20]],
+                       rtol=1e-12, atol=1e-15)
+    assert np.allclose(O.dC_rows(e, c, t, [2, 33], lse, keep=keep, tile=(Bn, Bv)), bf.dC[[2, 33]],
+                       rtol=1e-12, atol=1e-15)
