@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused linear cross-entropy forward+backward on one MI355X.
+
+One step = cce_forward + cce_backward over one batch of synthetic input (all
+of the hot path: logit tiles with online LSE partials, gather-dot, LSE
+combine, reductions, filter, gradient tiles, dC and dE contractions).  The
+default workload is the Llama-3.1-8B classifier head: N = 4x1024 tokens,
+D = 4096, V = 128256, bf16 operands with fp32 accumulation, e ~ N(0,1),
+c ~ N(0, 0.02^2), uniform targets, per-token loss (reduction 'none').
+
+Prints one JSON line: tokens/s for forward+backward, MFMA utilisation over
+the effective (unfiltered) 8*N*V*D flops, a roofline entry for the dominant
+kernel (per-launch durations from HIP events recorded around that kernel's
+launches on its stream during the timed region) and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+KERNELS = ["fwd_tile", "rows", "reduce", "bwd_prep", "filter", "grad_tile", "dC_gemm", "dE_gemm", "dE_reduce",
+           "fill_zero"]
+MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
+# Measured HBM traffic per launch of the dominant kernel (rocprofv3 FETCH_SIZE
+# + WRITE_SIZE, scaled by a plain-copy calibration).  Set only when the
+# counters were taken on the current kernel source.
+TRAFFIC_BYTES: dict = {}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--reduction", default=None)
+    ap.add_argument("--no-filter", action="store_true")
+    ap.add_argument("--accum", default="deterministic", choices=["deterministic", "atomic"])
+    ap.add_argument("--vocab-chunk", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic(name, N, D, V, es, nVB, chunk_lens):
+    """(flops, bytes) per launch of `name`, averaged over its launches in a step."""
+    if name == "fwd_tile":
+        return 2.0 * N * V * D, (N + V) * D * es + N * nVB * 8.0
+    if name in ("grad_tile", "dC_gemm", "dE_gemm"):
+        f = [2.0 * N * cl * D for cl in chunk_lens]
+        return float(np.mean(f)), 0.0
+    if name == "rows":
+        return 2.0 * N * D, N * (2.0 * D * es + 8 + nVB * 8.0 + 8)
+    if name == "reduce":
+        return 0.0, N * 12.0
+    if name == "bwd_prep":
+        return 0.0, N * 12.0
+    if name == "filter":
+        return 0.0, N * nVB * 8.0 + N * 12.0
+    if name == "dE_reduce":
+        return 0.0, 0.0
+    return 0.0, 0.0
+
+
+def cpu_baseline(inp, rows_n):
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    e, c, t = inp["e"], inp["c"], inp["targets"]
+    rows = np.arange(rows_n)
+    t0 = time.perf_counter()
+    f = O.forward(e[rows], c, t[rows], reduction="none")
+    O.backward(e[rows], c, t[rows], reduction="none", grad_loss=np.ones(rows_n))
+    dt = time.perf_counter() - t0
+    assert np.isfinite(f.lse).all()
+    return {"value": rows_n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle forward+backward of the first {rows_n} of {e.shape[0]} tokens "
+                      f"against the full classifier (V={c.shape[0]}, D={c.shape[1]}); {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import workloads as W
+    import linear_cross_entropy_forward_amd as M
+
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    reduction = args.reduction or w.reduction
+    inp = W.generate(w)
+    dt_name = w.dtype
+    tdt = torch.bfloat16 if dt_name == "bf16" else torch.float32
+    e = torch.from_numpy(inp["e"]).to(tdt).to(dev)
+    c = torch.from_numpy(inp["c"]).to(tdt).to(dev)
+    t = torch.from_numpy(inp["targets"]).to(dev)
+    N, D = e.shape
+    V = c.shape[0]
+    es = 2 if dt_name == "bf16" else 4
+    n_valid = int((inp["targets"] != -100).sum())
+    L = M.lib()
+
+    ws = torch.empty(M.workspace_size(N, D, V, tdt, args.vocab_chunk), dtype=torch.uint8, device=dev)
+    red = {"none": 0, "sum": 1, "mean": 2}[reduction]
+    loss = torch.empty(N if red == 0 else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    nv = torch.empty(1, dtype=torch.int32, device=dev)
+    # upstream gradient: for per-token loss, 1/n_valid per row (the mean's gradient)
+    g = torch.full((N,) if red == 0 else (1,), 1.0 / n_valid if red == 0 else 1.0, dtype=torch.float32,
+                   device=dev)
+    dE = torch.empty((N, D), dtype=torch.float32, device=dev)
+    dC = torch.empty((V, D), dtype=torch.float32, device=dev)
+    dcode = 0 if dt_name == "bf16" else 1
+    flt = 0 if args.no_filter else 1
+    acc = 0 if args.accum == "deterministic" else 1
+    stream = torch.cuda.current_stream()
+
+    def step():
+        s = stream.cuda_stream
+        r1 = L.cce_forward(e.data_ptr(), c.data_ptr(), t.data_ptr(), N, D, V, dcode, -100, red, 0.0,
+                           loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(), ws.numel(), s)
+        r2 = L.cce_backward(e.data_ptr(), c.data_ptr(), t.data_ptr(), N, D, V, dcode, -100, red, 0.0,
+                            lse.data_ptr(), g.data_ptr(), flt, acc, args.vocab_chunk, dE.data_ptr(), dC.data_ptr(),
+                            ws.data_ptr(), ws.numel(), s)
+        if r1 or r2:
+            raise RuntimeError(f"cce call failed: {r1} {r2}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stats = M.read_stats(ws, N, V)
+
+    # timed region: K steps, HIP events around every kernel launch
+    for k in range(len(KERNELS)):
+        L.cce_profile_start(k, 64 * max(1, args.steps))
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    import ctypes
+    per = {}
+    for k, name in enumerate(KERNELS):
+        ms, n = ctypes.c_double(), ctypes.c_int()
+        L.cce_profile_stop(k, ctypes.byref(ms), ctypes.byref(n))
+        if n.value:
+            per[name] = {"launches_per_step": n.value / args.steps, "avg_ms": ms.value / n.value,
+                         "ms_per_step": ms.value / args.steps}
+
+    # forward alone (not part of the metric): separate short timing
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(args.steps):
+        L.cce_forward(e.data_ptr(), c.data_ptr(), t.data_ptr(), N, D, V, dcode, -100, red, 0.0, loss.data_ptr(),
+                      lse.data_ptr(), nv.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / args.steps
+
+    ms_step = total_ms / args.steps
+    tok_s = N / (ms_step * 1e-3)
+    eff_flops = 8.0 * N * V * D
+    peak = PEAK_BF16_TFLOPS if dt_name == "bf16" else PEAK_F32_TFLOPS
+    tflops = eff_flops / (ms_step * 1e-3) / 1e12
+
+    # chunk lengths of the backward, for per-launch algorithmic work
+    vc_default = ws.numel()  # placeholder, replaced below
+    Vc = args.vocab_chunk
+    if Vc == 0:
+        Npad = -(-N // 256) * 256
+        Vc = max(256, (256 << 20) // (Npad * es) // 256 * 256)
+        Vc = min(Vc, -(-V // 256) * 256)
+    chunk_lens = [min(Vc, V - s) for s in range(0, V, Vc)]
+    nVB = -(-V // 128)
+    kernels = {}
+    for name, d in per.items():
+        fl, by = algorithmic(name, N, D, V, es, nVB, chunk_lens)
+        d = dict(d)
+        d["tflops"] = fl / (d["avg_ms"] * 1e-3) / 1e12 if fl else None
+        d["gbs"] = by / (d["avg_ms"] * 1e-3) / 1e9 if by else None
+        kernels[name] = d
+    dom = max(per, key=lambda k: per[k]["ms_per_step"])
+    fl, by = algorithmic(dom, N, D, V, es, nVB, chunk_lens)
+    if dom in MFMA_KERNELS:
+        ach = fl / (per[dom]["avg_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+                "traffic": TRAFFIC_BYTES.get(dom), "kernel": dom, "avg_launch_ms": per[dom]["avg_ms"],
+                "algorithmic_flops_per_launch": fl}
+    else:
+        ach = by / (per[dom]["avg_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                "traffic": TRAFFIC_BYTES.get(dom), "kernel": dom, "avg_launch_ms": per[dom]["avg_ms"],
+                "algorithmic_bytes_per_launch": by}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows_n = args.cpu_rows or (64 if dt_name == "bf16" else N)
+        cpu = cpu_baseline(inp, min(rows_n, N))
+
+    out = {
+        "metric": "fwd+bwd tokens/sec & MFMA util % at Llama-3.1-8B head (D=4096, V=128256)",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt_name == "bf16" else "f32",
+        "data": "synthetic (seeded; e ~ N(0,1), c ~ N(0,0.02^2) bf16, uniform targets)",
+        "config": {"workload": args.workload, "N": N, "D": D, "V": V, "reduction": reduction,
+                   "filter": bool(flt), "accum": args.accum, "vocab_chunk": Vc},
+        "mfma_util_pct": 100.0 * tflops / peak,
+        "tflops_effective": tflops,
+        "fwd_ms": fwd_ms,
+        "fwd_tokens_per_s": N / (fwd_ms * 1e-3),
+        "tiles_kept_frac": stats["tiles_kept"] / max(1, stats["tiles_total"]),
+        "workspace_bytes": ws.numel(),
+        "materialized_logits_fp32_bytes": N * V * 4,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * cce.h — C ABI of libcce, a fused linear cross-entropy ("Cut Cross-Entropy")
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For token rows e_i (i < N, length D), classifier rows c_j
+ * (j < V, length D) and integer targets y_i:
+ *
+ *     LSE_i  = log sum_j exp(e_i . c_j)
+ *     loss_i = LSE_i - e_i . c_{y_i}
+ *
+ * as stated in Wijmans et al., "Cut Your Losses in Large-Vocabulary Language
+ * Models" (abstract: only the correct token's logit and a log-sum-exp over all
+ * logits evaluated on the fly) and in the blog "Cut Cross Entropy from first
+ * principles" (loss = LSE minus the correct-token logit).  The [N, V] logit
+ * matrix is never written to device memory (mlx-cross-entropy README, "The
+ * problem" and "How it works").  Rows whose target equals ignore_index give
+ * loss 0 and gradient 0 and are not counted; reductions are none / sum / mean
+ * over the non-ignored rows (README "API" table; tirogla "Loss functions",
+ * "How it works" step 4 and the "Code" section, which floors the count at 1).
+ * The backward returns dE = G C and dC = G^T E with
+ * G = (softmax - onehot(y)) * scale (tirogla step 2: the fused gradient p - y),
+ * skipping (token block, vocab block) tiles on which every softmax value is
+ * below 2^-12 (README "How it works" item 2; Wijmans et al. abstract).
+ *
+ * Conventions for every call:
+ *  - Pointers marked (device) are device memory on the current HIP device;
+ *    (host) are host memory.  The library never allocates, frees or
+ *    synchronises in cce_forward / cce_backward: it enqueues kernels on
+ *    `stream` and returns.  The caller owns every buffer, including the
+ *    workspace, and keeps them alive until the stream work completes.
+ *  - Layout: row-major, contiguous, base pointers 16-byte aligned.  e is
+ *    [N, D], c is [V, D] (D contiguous); e and c share one dtype; outputs are
+ *    float32.  D must be a multiple of 8 (bf16) or 4 (float32).
+ *  - Errors: argument and size faults are reported synchronously, before any
+ *    launch, as a negative cce_status.  A target outside [0, V) that is not
+ *    ignore_index is not a host-visible fault: its row's loss is NaN (so a
+ *    mean or sum is NaN), its gradient row is NaN, and cce_read_stats
+ *    reports it in bad_targets.  No exception crosses the ABI.
+ *  - Reentrancy: apart from the measurement hook at the end of this header,
+ *    the library keeps no global mutable state; calls on different
+ *    workspaces may run concurrently.  Two calls sharing one workspace must
+ *    be ordered on one stream.
+ */
+#ifndef CCE_H_
+#define CCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same object as hipStream_t; NULL is the default stream. */
+typedef struct ihipStream_t* cce_stream_t;
+
+typedef enum {
+  CCE_OK = 0,
+  CCE_ERR_INVALID_ARG = -1, /* null pointer, negative or zero size, bad enum, misalignment */
+  CCE_ERR_UNSUPPORTED = -2, /* softcap != 0, D not a multiple of the vector width, size limits */
+  CCE_ERR_WORKSPACE = -3,   /* workspace smaller than cce_workspace_size() */
+  CCE_ERR_HIP = -4          /* a HIP launch or copy reported an error */
+} cce_status;
+
+typedef enum { CCE_DTYPE_BF16 = 0, CCE_DTYPE_F32 = 1 } cce_dtype;
+typedef enum { CCE_REDUCTION_NONE = 0, CCE_REDUCTION_SUM = 1, CCE_REDUCTION_MEAN = 2 } cce_reduction;
+typedef enum { CCE_ACCUM_DETERMINISTIC = 0, CCE_ACCUM_ATOMIC = 1 } cce_accum;
+
+typedef struct {
+  int64_t n_valid;      /* rows whose target != ignore_index (last forward)        */
+  int64_t bad_targets;  /* non-ignored targets outside [0, V)  (last forward)      */
+  int64_t tiles_total;  /* gradient tiles of the last backward: ceil(N/Bn)*ceil(V/Bv) */
+  int64_t tiles_kept;   /* tiles the last backward computed (filter decision)      */
+  int64_t filter_rows;  /* Bn: token rows per gradient tile                        */
+  int64_t filter_vocab; /* Bv: vocabulary entries per gradient tile                */
+} cce_stats;
+
+/*
+ * Bytes of device workspace needed by cce_forward and cce_backward for this
+ * problem.  vocab_chunk = 0 picks the library default: the backward forms
+ * gradient tiles for a vocabulary chunk at a time and keeps that chunk's
+ * bf16/fp32 G block in the workspace (at most 256 MiB by default); a positive
+ * value (a multiple of 256) sets the chunk width, trading workspace for
+ * launches.  The forward uses only the first part (per-row partials,
+ * O(N + N*V/128) floats).  Returns 0 for invalid arguments.
+ */
+size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk);
+
+/*
+ * Forward.  e (device) [N, D], c (device) [V, D] of `dtype`; targets (device)
+ * int64 [N].  reduction: CCE_REDUCTION_NONE writes loss[N] (0 on ignored rows);
+ * SUM / MEAN write loss[0] (MEAN divides by max(n_valid, 1)).  lse (device)
+ * float [N] receives every row's LSE (ignored rows included).  n_valid
+ * (device) int32 [1] receives the non-ignored count; may be NULL.  softcap must
+ * be 0 (no logit soft-capping; other values return CCE_ERR_UNSUPPORTED).  ws
+ * (device) of ws_bytes >= cce_workspace_size(N, D, V, dtype, vocab_chunk) for
+ * the vocab_chunk the backward will use; it holds the per-block partials the
+ * backward's filter reads, so keep it unmodified between the two calls.
+ */
+cce_status cce_forward(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D,
+                       int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
+                       float* loss, float* lse, int32_t* n_valid, void* ws, size_t ws_bytes,
+                       cce_stream_t stream);
+
+/*
+ * Backward.  Same e, c, targets, sizes, dtype, ignore_index, reduction and
+ * softcap as the forward; lse (device) float [N] is the forward's output and
+ * ws is the forward's workspace, unmodified.  grad_loss (device) float is the
+ * upstream gradient: [N] for NONE, [1] otherwise.  filter = 1 skips tiles
+ * whose softmax is below 2^-12 everywhere (and that hold no target); 0
+ * computes every tile.  accum = CCE_ACCUM_DETERMINISTIC gives run-to-run
+ * bitwise-identical results (fixed-order split reduction);
+ * CCE_ACCUM_ATOMIC accumulates dE with fp32 atomics.  dE (device) float
+ * [N, D] and dC (device) float [V, D] are overwritten.  vocab_chunk as in
+ * cce_workspace_size.
+ */
+cce_status cce_backward(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D,
+                        int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
+                        const float* lse, const float* grad_loss, int filter, int accum,
+                        int64_t vocab_chunk, float* dE, float* dC, void* ws, size_t ws_bytes,
+                        cce_stream_t stream);
+
+/*
+ * Copies the workspace counters to `out` (host) after the work queued on
+ * `stream` so far; the one call here that synchronises (the stream).  N, V
+ * describe the problem the workspace was used for (for tiles_total).
+ */
+cce_status cce_read_stats(const void* ws, size_t ws_bytes, int64_t N, int64_t V, cce_stream_t stream,
+                          cce_stats* out);
+
+/* Static description of a status code. */
+const char* cce_status_string(int status);
+
+/* Tile geometry: gradient tile Bn x Bv and the forward partial width. */
+void cce_tile_shape(int* filter_rows, int* filter_vocab, int* partial_vocab);
+
+/*
+ * Measurement hook.  Between cce_profile_start(k, n) and cce_profile_stop(k,
+ * ...), every launch of kernel k by cce_forward / cce_backward (at most n
+ * launches) is bracketed by two HIP events recorded on the launch stream.
+ * cce_profile_stop waits for those events and returns the summed elapsed time
+ * (host double, ms) and the number of launches timed (host int).  The hook
+ * holds process-wide state: it is meant for benchmarks and is not
+ * thread-safe.  Kernel ids 0..9 are fwd_tile, rows, reduce, bwd_prep, filter,
+ * grad_tile, dC_gemm, dE_gemm, dE_reduce, fill_zero (cce_kernel_name).
+ */
+cce_status cce_profile_start(int kernel_id, int max_launches);
+cce_status cce_profile_stop(int kernel_id, double* total_ms, int* launches);
+const char* cce_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCE_H_ */

@@ -1,0 +1,219 @@
+"""Fused linear cross-entropy (Cut Cross-Entropy) for AMD MI355X (gfx950).
+
+Thin ctypes binding over libcce.so (C ABI declared in include/cce.h).  The
+binding only marshals arguments: every step of the forward and backward runs
+in the library's HIP kernels, on the caller's current torch stream.  PyTorch
+provides device memory and streams.
+
+    loss = linear_cross_entropy(e, c, targets)             # [..., D], [V, D], [...]
+    loss, lse, n_valid, ws = forward(e, c, targets)        # raw C-ABI calls
+    dE, dC = backward(e, c, targets, lse, grad, ws)
+
+There is no fallback: without the built library (or without a GPU) every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["forward", "backward", "read_stats", "workspace_size", "linear_cross_entropy", "cce_loss",
+           "tile_shape", "lib", "CCEError", "library_path"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libcce.so")
+
+CCE_OK = 0
+_REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
+_ACCUM = {"deterministic": 0, "atomic": 1}
+
+
+class CCEError(RuntimeError):
+    pass
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [("n_valid", ctypes.c_int64), ("bad_targets", ctypes.c_int64),
+                ("tiles_total", ctypes.c_int64), ("tiles_kept", ctypes.c_int64),
+                ("filter_rows", ctypes.c_int64), ("filter_vocab", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcce.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise CCEError(f"{library_path} is missing: build it with "
+                       f"`python -m linear_cross_entropy_forward_amd.build`")
+    L = ctypes.CDLL(library_path)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.cce_workspace_size.restype = sz
+    L.cce_workspace_size.argtypes = [i64, i64, i64, i32, i64]
+    L.cce_forward.restype = i32
+    L.cce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.cce_backward.restype = i32
+    L.cce_backward.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, vp, vp, i32, i32, i64, vp, vp,
+                               vp, sz, vp]
+    L.cce_read_stats.restype = i32
+    L.cce_read_stats.argtypes = [vp, sz, i64, i64, vp, ctypes.POINTER(_Stats)]
+    L.cce_status_string.restype = ctypes.c_char_p
+    L.cce_status_string.argtypes = [i32]
+    L.cce_tile_shape.restype = None
+    L.cce_tile_shape.argtypes = [ctypes.POINTER(i32)] * 3
+    L.cce_profile_start.restype = i32
+    L.cce_profile_start.argtypes = [i32, i32]
+    L.cce_profile_stop.restype = i32
+    L.cce_profile_stop.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+    L.cce_kernel_name.restype = ctypes.c_char_p
+    L.cce_kernel_name.argtypes = [i32]
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str) -> None:
+    if status != CCE_OK:
+        msg = lib().cce_status_string(status).decode()
+        raise CCEError(f"{what}: {msg} ({status})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return 0
+    if t.dtype == torch.float32:
+        return 1
+    raise CCEError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def tile_shape() -> tuple[int, int, int]:
+    """(token rows, vocab entries) of a gradient tile and the forward partial width."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    lib().cce_tile_shape(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return a.value, b.value, c.value
+
+
+def workspace_size(N: int, D: int, V: int, dtype: torch.dtype = torch.bfloat16, vocab_chunk: int = 0) -> int:
+    code = 0 if dtype == torch.bfloat16 else 1
+    n = lib().cce_workspace_size(N, D, V, code, vocab_chunk)
+    if n == 0:
+        raise CCEError("invalid sizes for cce_workspace_size")
+    return n
+
+
+def _validate(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor) -> None:
+    if not (e.is_cuda and c.is_cuda and targets.is_cuda):
+        raise CCEError("e, c and targets must be device tensors")
+    if e.dim() != 2 or c.dim() != 2 or e.shape[1] != c.shape[1]:
+        raise CCEError(f"expected e [N, D] and c [V, D], got {tuple(e.shape)} and {tuple(c.shape)}")
+    if e.dtype != c.dtype:
+        raise CCEError("e and c must share a dtype")
+    if targets.dtype != torch.int64 or targets.shape != (e.shape[0],):
+        raise CCEError("targets must be int64 [N]")
+    if not (e.is_contiguous() and c.is_contiguous() and targets.is_contiguous()):
+        raise CCEError("e, c and targets must be contiguous")
+
+
+def forward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, ignore_index: int = -100,
+            reduction: str = "mean", softcap: float = 0.0, ws: torch.Tensor | None = None,
+            vocab_chunk: int = 0):
+    """cce_forward.  Returns (loss, lse, n_valid, ws); loss is [N] for
+    reduction='none', else a 0-dim tensor.  `ws` (uint8, device) is allocated
+    if not given and must be passed unchanged to backward()."""
+    _validate(e, c, targets)
+    N, D = e.shape
+    V = c.shape[0]
+    dev = e.device
+    need = workspace_size(N, D, V, e.dtype, vocab_chunk)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    red = _REDUCTIONS[reduction]
+    loss = torch.empty(N if red == 0 else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().cce_forward(_ptr(e), _ptr(c), _ptr(targets), N, D, V, _dtype_code(e), ignore_index, red,
+                             softcap, _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(ws), ws.numel(), _stream()),
+           "cce_forward")
+    return (loss if red == 0 else loss[0]), lse, n_valid, ws
+
+
+def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor,
+             grad_loss: torch.Tensor, ws: torch.Tensor, ignore_index: int = -100, reduction: str = "mean",
+             filter: bool = True, accum: str = "deterministic", softcap: float = 0.0, vocab_chunk: int = 0,
+             dE: torch.Tensor | None = None, dC: torch.Tensor | None = None):
+    """cce_backward.  grad_loss is float32 [N] ('none') or [1]/0-dim.  Returns
+    float32 (dE [N, D], dC [V, D])."""
+    _validate(e, c, targets)
+    N, D = e.shape
+    V = c.shape[0]
+    dev = e.device
+    g = grad_loss.reshape(-1).to(torch.float32).contiguous()
+    if dE is None:
+        dE = torch.empty((N, D), dtype=torch.float32, device=dev)
+    if dC is None:
+        dC = torch.empty((V, D), dtype=torch.float32, device=dev)
+    _check(lib().cce_backward(_ptr(e), _ptr(c), _ptr(targets), N, D, V, _dtype_code(e), ignore_index,
+                              _REDUCTIONS[reduction], softcap, _ptr(lse), _ptr(g), int(bool(filter)),
+                              _ACCUM[accum], vocab_chunk, _ptr(dE), _ptr(dC), _ptr(ws), ws.numel(), _stream()),
+           "cce_backward")
+    return dE, dC
+
+
+def read_stats(ws: torch.Tensor, N: int, V: int) -> dict:
+    """Counters of the last forward/backward on `ws` (synchronises the stream)."""
+    s = _Stats()
+    _check(lib().cce_read_stats(_ptr(ws), ws.numel(), N, V, _stream(), ctypes.byref(s)), "cce_read_stats")
+    return {k: getattr(s, k) for k, _ in _Stats._fields_}
+
+
+class _CCEFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, e, c, targets, reduction, ignore_index, filter, accum):
+        loss, lse, _, ws = forward(e, c, targets, ignore_index=ignore_index, reduction=reduction)
+        ctx.save_for_backward(e, c, targets, lse, ws)
+        ctx.cfg = (reduction, ignore_index, filter, accum)
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad):
+        e, c, targets, lse, ws = ctx.saved_tensors
+        reduction, ignore_index, filter, accum = ctx.cfg
+        dE, dC = backward(e, c, targets, lse, grad, ws, ignore_index=ignore_index, reduction=reduction,
+                          filter=filter, accum=accum)
+        # autograd wants gradients in the inputs' dtype
+        return dE.to(e.dtype), dC.to(c.dtype), None, None, None, None, None
+
+
+def cce_loss(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, reduction: str = "mean",
+             ignore_index: int = -100, filter: bool = True, accum: str = "deterministic") -> torch.Tensor:
+    """Flat form: e [N, D], c [V, D], targets [N]."""
+    return _CCEFunction.apply(e.contiguous(), c.contiguous(), targets.contiguous().to(torch.int64), reduction,
+                              ignore_index, filter, accum)
+
+
+def linear_cross_entropy(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, bias=None,
+                         reduction: str = "mean", ignore_index: int = -100, filter: bool = True,
+                         accum: str = "deterministic") -> torch.Tensor:
+    """Cross-entropy of softmax(e @ c.T) against targets without forming the
+    logits.  e [..., D], c [V, D], targets [...]; 'none' returns a tensor
+    shaped like targets."""
+    if bias is not None:
+        raise NotImplementedError("classifier bias is not supported by this build")
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(_REDUCTIONS)}")
+    shape = targets.shape
+    D = e.shape[-1]
+    out = cce_loss(e.reshape(-1, D), c, targets.reshape(-1), reduction, ignore_index, filter, accum)
+    return out.reshape(shape) if reduction == "none" else out

@@ -1,0 +1,283 @@
+// C ABI of libcce: argument validation, workspace layout and the launch
+// sequence of the forward and backward.  Declarations and the contract of each
+// call are in include/cce.h.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/cce.h"
+#include "cce_internal.hpp"
+
+namespace cce {
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk, void* base) {
+  Layout L{};
+  const size_t es = dtype == kDtypeBf16 ? 2 : 4;
+  L.nVB = (int)((V + kPartialWidth - 1) / kPartialWidth);
+  L.Npad = (int)((N + kTileN - 1) / kTileN * kTileN);
+  L.nb = L.Npad / kTileN;
+  L.nvb_t = (int)((V + kTileV - 1) / kTileV);
+  const int64_t vmax = (int64_t)L.nvb_t * kTileV;
+  int64_t vc;
+  if (vocab_chunk > 0) {
+    vc = vocab_chunk;
+  } else {
+    vc = (int64_t)(kDefaultGBudget / ((size_t)L.Npad * es)) / kTileV * kTileV;
+  }
+  if (vc < kTileV) vc = kTileV;
+  if (vc > vmax) vc = vmax;
+  if (vc > (int64_t)kMaxBlocks * kTileV) vc = (int64_t)kMaxBlocks * kTileV;
+  L.Vc = (int)vc;
+  L.nchunks = (int)((V + vc - 1) / vc);
+  const int tiles_d = (int)((D + kTileV - 1) / kTileV);
+  const int tiles_de = L.nb * tiles_d;
+  const int cvb = (int)(vc / kTileV);
+  int sp = (512 + tiles_de - 1) / tiles_de;
+  if (sp > 8) sp = 8;
+  if (sp > cvb) sp = cvb;
+  if (sp < 1) sp = 1;
+  L.splits = sp;
+  int spa = (512 + tiles_de - 1) / tiles_de;
+  if (spa > 16) spa = 16;
+  if (spa > cvb) spa = cvb;
+  if (spa < 1) spa = 1;
+  L.splits_atomic = spa;
+  L.g_bytes = (size_t)L.Npad * (size_t)vc * es;
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_hdr = take(kHdrWords * 4);
+  const size_t o_part = take((size_t)N * L.nVB * sizeof(float2));
+  const size_t o_nll = take((size_t)N * 4);
+  const size_t o_scale = take((size_t)L.Npad * 4);
+  const size_t o_keep = take((size_t)L.nb * L.nvb_t);
+  const size_t o_g = take(L.g_bytes);
+  const size_t o_dep = take((size_t)(L.splits - 1) * (size_t)N * (size_t)D * 4);
+  L.total = off;
+  if (base) {
+    char* b = (char*)base;
+    L.hdr = (int32_t*)(b + o_hdr);
+    L.part = (float2*)(b + o_part);
+    L.nll_out = (float*)(b + o_nll);
+    L.scale = (float*)(b + o_scale);
+    L.keep = (uint8_t*)(b + o_keep);
+    L.G = b + o_g;
+    L.dE_part = (float*)(b + o_dep);
+  }
+  return L;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shared checks of forward and backward.  Returns CCE_OK or an error.
+static cce_status check_common(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D,
+                               int64_t V, int dtype, int reduction, float softcap, const void* ws,
+                               int64_t vocab_chunk) {
+  if (!e || !c || !targets || !ws) return CCE_ERR_INVALID_ARG;
+  if (N <= 0 || D <= 0 || V <= 0) return CCE_ERR_INVALID_ARG;
+  if (dtype != kDtypeBf16 && dtype != kDtypeF32) return CCE_ERR_INVALID_ARG;
+  if (reduction != kReductionNone && reduction != kReductionSum && reduction != kReductionMean)
+    return CCE_ERR_INVALID_ARG;
+  if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return CCE_ERR_INVALID_ARG;
+  if (!aligned16(e) || !aligned16(c) || !aligned16(ws) || ((uintptr_t)targets & 7u)) return CCE_ERR_INVALID_ARG;
+  if (softcap != 0.0f) return CCE_ERR_UNSUPPORTED;
+  const int64_t es = dtype == kDtypeBf16 ? 2 : 4;
+  if (D % (16 / es) != 0) return CCE_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets: every operand a kernel addresses from one base
+  // stays below 2 GiB; the contraction tiles list at most kMaxBlocks blocks.
+  const int64_t lim = (int64_t)1 << 31;
+  if (N * D * es >= lim || N > (int64_t)kMaxBlocks * kTileN || V >= lim / 2 || D >= lim / 2)
+    return CCE_ERR_UNSUPPORTED;
+  Layout L = make_layout(N, D, V, dtype, vocab_chunk, nullptr);
+  if ((int64_t)L.Vc * D * es >= lim || (int64_t)L.g_bytes >= lim) return CCE_ERR_UNSUPPORTED;
+  return CCE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Profiling hook: HIP events recorded on the launch stream around every launch
+// of the kernels being profiled.  Measurement aid only; not thread-safe.
+// ---------------------------------------------------------------------------
+struct ProfSlot {
+  bool active = false;
+  int cap = 0, n = 0;
+  std::vector<hipEvent_t> ev;  // start, stop per launch
+};
+static ProfSlot g_prof[kNumKernels];
+
+void prof_before(int id, hipStream_t st) {
+  ProfSlot& p = g_prof[id];
+  if (p.active && p.n < p.cap) (void)hipEventRecord(p.ev[2 * p.n], st);
+}
+void prof_after(int id, hipStream_t st) {
+  ProfSlot& p = g_prof[id];
+  if (p.active && p.n < p.cap) {
+    (void)hipEventRecord(p.ev[2 * p.n + 1], st);
+    ++p.n;
+  }
+}
+
+static void prof_release(ProfSlot& p) {
+  for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
+  p.ev.clear();
+  p.active = false;
+  p.cap = p.n = 0;
+}
+
+static const char* const kKernelNames[kNumKernels] = {
+    "fwd_tile", "rows", "reduce", "bwd_prep", "filter", "grad_tile", "dC_gemm", "dE_gemm", "dE_reduce",
+    "fill_zero"};
+
+}  // namespace cce
+
+using namespace cce;
+
+extern "C" {
+
+size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk) {
+  if (N <= 0 || D <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
+  if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return 0;
+  return make_layout(N, D, V, dtype, vocab_chunk, nullptr).total;
+}
+
+cce_status cce_forward(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D, int64_t V,
+                       int dtype, int64_t ignore_index, int reduction, float softcap, float* loss, float* lse,
+                       int32_t* n_valid, void* ws, size_t ws_bytes, cce_stream_t stream) {
+  cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, ws, 0);
+  if (st != CCE_OK) return st;
+  if (!loss || !lse) return CCE_ERR_INVALID_ARG;
+  // The forward only touches the leading (chunk-independent) part of the
+  // layout; any workspace sized for some vocab_chunk is large enough for it.
+  Layout L = make_layout(N, D, V, dtype, kTileV, ws);
+  const size_t need = (size_t)((char*)L.scale - (char*)ws);
+  if (ws_bytes < need) return CCE_ERR_WORKSPACE;
+  if (reduction == kReductionNone) L.nll_out = loss;
+  Problem P{};
+  P.e = e;
+  P.c = c;
+  P.targets = targets;
+  P.N = (int)N;
+  P.D = (int)D;
+  P.V = (int)V;
+  P.dtype = dtype;
+  P.ignore_index = ignore_index;
+  P.reduction = reduction;
+  P.loss = loss;
+  P.lse = lse;
+  P.n_valid = n_valid;
+  hipError_t err = launch_forward(P, L, (hipStream_t)stream);
+  return err == hipSuccess ? CCE_OK : CCE_ERR_HIP;
+}
+
+cce_status cce_backward(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D, int64_t V,
+                        int dtype, int64_t ignore_index, int reduction, float softcap, const float* lse,
+                        const float* grad_loss, int filter, int accum, int64_t vocab_chunk, float* dE, float* dC,
+                        void* ws, size_t ws_bytes, cce_stream_t stream) {
+  cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, ws, vocab_chunk);
+  if (st != CCE_OK) return st;
+  if (!lse || !grad_loss || !dE || !dC) return CCE_ERR_INVALID_ARG;
+  if ((filter != 0 && filter != 1) || (accum != kAccumDeterministic && accum != kAccumAtomic))
+    return CCE_ERR_INVALID_ARG;
+  if (!aligned16(dE) || !aligned16(dC)) return CCE_ERR_INVALID_ARG;
+  Layout L = make_layout(N, D, V, dtype, vocab_chunk, ws);
+  if (ws_bytes < L.total) return CCE_ERR_WORKSPACE;
+  Problem P{};
+  P.e = e;
+  P.c = c;
+  P.targets = targets;
+  P.N = (int)N;
+  P.D = (int)D;
+  P.V = (int)V;
+  P.dtype = dtype;
+  P.ignore_index = ignore_index;
+  P.reduction = reduction;
+  P.lse = (float*)lse;
+  P.grad_loss = grad_loss;
+  P.filter = filter;
+  P.accum = accum;
+  P.dE = dE;
+  P.dC = dC;
+  hipError_t err = launch_backward(P, L, (hipStream_t)stream);
+  return err == hipSuccess ? CCE_OK : CCE_ERR_HIP;
+}
+
+cce_status cce_read_stats(const void* ws, size_t ws_bytes, int64_t N, int64_t V, cce_stream_t stream,
+                          cce_stats* out) {
+  if (!ws || !out || ws_bytes < (size_t)kHdrWords * 4 || N <= 0 || V <= 0) return CCE_ERR_INVALID_ARG;
+  int32_t h[kHdrWords];
+  if (hipMemcpyAsync(h, ws, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+    return CCE_ERR_HIP;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CCE_ERR_HIP;
+  out->n_valid = h[kHdrNValid];
+  out->bad_targets = h[kHdrBadTargets];
+  out->tiles_total = ((N + kTileN - 1) / kTileN) * ((V + kTileV - 1) / kTileV);
+  out->tiles_kept = h[kHdrTilesKept];
+  out->filter_rows = kTileN;
+  out->filter_vocab = kTileV;
+  return CCE_OK;
+}
+
+const char* cce_status_string(int status) {
+  switch (status) {
+    case CCE_OK: return "ok";
+    case CCE_ERR_INVALID_ARG: return "invalid argument";
+    case CCE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case CCE_ERR_WORKSPACE: return "workspace too small";
+    case CCE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+cce_status cce_profile_start(int kernel_id, int max_launches) {
+  if (kernel_id < 0 || kernel_id >= kNumKernels || max_launches <= 0) return CCE_ERR_INVALID_ARG;
+  ProfSlot& p = g_prof[kernel_id];
+  prof_release(p);
+  p.ev.resize(2 * (size_t)max_launches);
+  for (auto& e : p.ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      prof_release(p);
+      return CCE_ERR_HIP;
+    }
+  p.cap = max_launches;
+  p.active = true;
+  return CCE_OK;
+}
+
+cce_status cce_profile_stop(int kernel_id, double* total_ms, int* launches) {
+  if (kernel_id < 0 || kernel_id >= kNumKernels || !total_ms || !launches) return CCE_ERR_INVALID_ARG;
+  ProfSlot& p = g_prof[kernel_id];
+  double tot = 0.0;
+  cce_status st = CCE_OK;
+  for (int i = 0; i < p.n; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, p.ev[2 * i], p.ev[2 * i + 1]) != hipSuccess) {
+      st = CCE_ERR_HIP;
+      break;
+    }
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = p.n;
+  prof_release(p);
+  return st;
+}
+
+const char* cce_kernel_name(int kernel_id) {
+  return (kernel_id >= 0 && kernel_id < kNumKernels) ? kKernelNames[kernel_id] : "unknown";
+}
+
+void cce_tile_shape(int* filter_rows, int* filter_vocab, int* partial_vocab) {
+  if (filter_rows) *filter_rows = kTileN;
+  if (filter_vocab) *filter_vocab = kTileV;
+  if (partial_vocab) *partial_vocab = kPartialWidth;
+}
+
+}  // extern "C"

@@ -1,0 +1,318 @@
+// LDS-tiled MFMA main loop shared by every contraction of the fused linear
+// cross-entropy: the logit tiles S = C E^T of the forward and of the gradient
+// recompute, and the two gradient contractions dE = G C and dC = G^T E.
+//
+// gfx950 (CDNA4) specifics:
+//  * bf16 operands use v_mfma_f32_32x32x16_bf16 (8 bf16 per lane per operand,
+//    fp32 accumulate); fp32 operands use v_mfma_f32_32x32x2_f32.
+//  * wave64: a 32x32 output block lives in 16 accumulator registers per lane,
+//    lane l owning column l%32 and rows 8*(r/4) + 4*(l/32) + r%4, r = 0..15.
+//  * global traffic goes through buffer resources (raw buffer loads/stores)
+//    whose range check returns zero for, or drops, every out-of-range access:
+//    ragged tiles need no branches and cannot touch memory outside a tensor.
+//  * tiles are staged in LDS with a 16-byte row pad, so that the 8 lanes which
+//    share a ds_read_b128 cycle hit disjoint banks.
+//  * operands whose contraction index is the slow (row) index in memory
+//    ("MN-major", e.g. C read as C[v][d] when contracting over v) are loaded
+//    as VECxVEC blocks and transposed in registers before the LDS store, so the
+//    fragment reads are always K-contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cce {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Pointer into LDS (address space 3): keeps fragment reads and tile stores on
+// the ds_* path instead of generic (flat) addressing.
+template <typename T> using lds_ptr = __attribute__((address_space(3))) T*;
+template <typename T> __device__ __forceinline__ lds_ptr<T> to_lds(T* p) { return (lds_ptr<T>)p; }
+
+// Word 3 of a raw (unstructured) buffer descriptor on gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+// Any byte offset at or beyond a descriptor's num_records reads as zero and is
+// dropped on store; this value is used to switch an access off.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  uint32_t n = bytes > 0x7fffffffull ? 0x7fffffffu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ float ldf(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void stf(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+__device__ __forceinline__ void st64(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+
+// ----------------------------------------------------------------------------
+// Element types.  bf16 tensors are carried as their 16-bit patterns.
+// ----------------------------------------------------------------------------
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+  static constexpr int VEC = 8;   // elements per 16-byte vector
+  static constexpr int BK = 64;   // K elements staged per main-loop step
+};
+template <> struct Elem<float> {
+  static constexpr int VEC = 4;
+  static constexpr int BK = 32;
+};
+
+// A lane's share of one 32x16 (K) operand slice: 8 consecutive K elements.
+template <typename T> struct Frag;
+template <> struct Frag<uint16_t> { u32x4 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+__device__ __forceinline__ void lds_frag(Frag<uint16_t>& f, lds_ptr<uint16_t> p) {
+  f.v = *(__attribute__((address_space(3))) u32x4*)p;
+}
+__device__ __forceinline__ void lds_frag(Frag<float>& f, lds_ptr<float> p) {
+  f.lo = *(__attribute__((address_space(3))) f32x4*)p;
+  f.hi = *(__attribute__((address_space(3))) f32x4*)(p + 4);
+}
+__device__ __forceinline__ void lds_st128(lds_ptr<uint16_t> p, u32x4 v) {
+  *(__attribute__((address_space(3))) u32x4*)p = v;
+}
+__device__ __forceinline__ void lds_st128(lds_ptr<float> p, u32x4 v) {
+  *(__attribute__((address_space(3))) u32x4*)p = v;
+}
+
+// acc += A(32x16) * B(16x32) for one K group of 16.
+__device__ __forceinline__ void mma16(f32x16& acc, const Frag<uint16_t>& a, const Frag<uint16_t>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                __builtin_bit_cast(bf16x8, b.v), acc, 0, 0, 0);
+}
+// fp32: eight K=2 steps.  Lane half h holds K elements 8h..8h+7 of the group;
+// step j pairs element j of both halves, so the eight steps cover the 16
+// elements once each with A and B indexed identically.
+__device__ __forceinline__ void mma16(f32x16& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[j], b.lo[j], acc, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[j], b.hi[j], acc, 0, 0, 0);
+}
+
+// ----------------------------------------------------------------------------
+// Register transposes of one VECxVEC block (rows in, columns out).
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ void transpose_block(u32x4 (&r)[8], const uint16_t*) {
+  // 8x8 of 16-bit elements.  Row i word q holds elements (2q, 2q+1) of row i.
+  u32x4 o[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t a = r[2 * p][q], b = r[2 * p + 1][q];
+      o[2 * q][p] = (a & 0xffffu) | (b << 16);
+      o[2 * q + 1][p] = (a >> 16) | (b & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = o[i];
+}
+__device__ __forceinline__ void transpose_block(u32x4 (&r)[4], const float*) {
+  u32x4 o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[j][i] = r[i][j];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = o[i];
+}
+
+// ----------------------------------------------------------------------------
+// Tile configuration.
+// ----------------------------------------------------------------------------
+template <typename T_, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct Cfg {
+  using T = T_;
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int BK = Elem<T>::BK;
+  static constexpr int VEC = Elem<T>::VEC;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int LDK = BK + VEC;  // padded LDS row, elements
+  static constexpr int KGROUPS = BK / 16;
+  static constexpr int STAGE_ELEMS = (BM + BN) * LDK;
+  static constexpr int LDS_BYTES = 2 * STAGE_ELEMS * (int)sizeof(T);
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
+};
+
+// One operand of the main loop.  K-major: element (row, k) at row*ld + k,
+// rows [0, rows) valid.  MN-major: element (row, k) at k*ld + row, columns
+// [0, rows) valid.  k in [0, kdim) valid.  Offsets are relative to `r`,
+// which the caller has positioned at the tile's first row (K-major) or at
+// k = 0 and the tile's first column (MN-major).
+struct Operand {
+  rsrc_t r;
+  uint32_t ld;    // elements
+  int rows;       // valid rows (K-major) or valid columns (MN-major) in the tile
+  int kdim;       // valid K extent (relative to the same origin)
+};
+
+template <class C, int ROWS, bool MN>
+struct Loader;
+
+// K-major: 16-byte chunks along K, ROWS*BK/VEC chunks per tile.
+template <class C, int ROWS>
+struct Loader<C, ROWS, false> {
+  using T = typename C::T;
+  static constexpr int CPR = C::BK / C::VEC;            // chunks per row
+  static constexpr int N = ROWS * CPR / C::NT;          // chunks per thread
+  static_assert(ROWS * CPR % C::NT == 0, "tile not evenly split");
+  u32x4 reg[N];
+  __device__ __forceinline__ void load(const Operand& op, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int c = tid + i * C::NT;
+      int row = c / CPR, kc = (c % CPR) * C::VEC + k0;
+      bool ok = row < op.rows && kc < op.kdim;
+      uint32_t off = ok ? ((uint32_t)row * op.ld + (uint32_t)kc) * (uint32_t)sizeof(T) : kOOB;
+      reg[i] = ld128(op.r, off);
+    }
+  }
+  __device__ __forceinline__ void store(lds_ptr<T> lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int c = tid + i * C::NT;
+      int row = c / CPR, kc = (c % CPR) * C::VEC;
+      lds_st128(lds + row * C::LDK + kc, reg[i]);
+    }
+  }
+};
+
+// MN-major: VECxVEC blocks, transposed in registers.
+template <class C, int ROWS>
+struct Loader<C, ROWS, true> {
+  using T = typename C::T;
+  static constexpr int V = C::VEC;
+  static constexpr int KB = C::BK / V;                  // blocks along K
+  static constexpr int UNITS = KB * (ROWS / V);
+  static constexpr int N = UNITS / C::NT;               // blocks per thread
+  static_assert(UNITS % C::NT == 0, "tile not evenly split");
+  u32x4 reg[N][V];
+  __device__ __forceinline__ void load(const Operand& op, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int u = tid + i * C::NT;
+      int kb = u % KB, mb = u / KB;
+      int col = mb * V;
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        int k = k0 + kb * V + j;
+        bool ok = k < op.kdim && col < op.rows;
+        uint32_t off = ok ? ((uint32_t)k * op.ld + (uint32_t)col) * (uint32_t)sizeof(T) : kOOB;
+        reg[i][j] = ld128(op.r, off);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(lds_ptr<T> lds, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int u = tid + i * C::NT;
+      int kb = u % KB, mb = u / KB;
+      transpose_block(reg[i], (const T*)nullptr);
+#pragma unroll
+      for (int j = 0; j < V; ++j) lds_st128(lds + (mb * V + j) * C::LDK + kb * V, reg[i][j]);
+    }
+  }
+};
+
+// Main loop: acc[fm][fn] += sum over the listed K steps of A_tile * B_tile^T.
+// `nsteps` K steps of BK each; step s covers K offset kofs(s).  With
+// `blocks` == nullptr the steps are contiguous from 0; otherwise step s lies in
+// K block blocks[s / SPB] (of SPB*BK elements) at sub-step s % SPB.
+template <class C, bool A_MN, bool B_MN, int SPB>
+__device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Operand& A,
+                                         const Operand& B, int nsteps, const uint16_t* blocks,
+                                         typename C::T* smem) {
+  using T = typename C::T;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  // stage st: A tile at st*STAGE_ELEMS, B tile right after it
+  const lds_ptr<T> base = to_lds(smem);
+  constexpr int BOFF = C::BM * C::LDK;
+
+  auto kofs = [&](int s) -> int {
+    return blocks ? blocks[s / SPB] * (SPB * C::BK) + (s % SPB) * C::BK : s * C::BK;
+  };
+
+  Loader<C, C::BM, A_MN> la;
+  Loader<C, C::BN, B_MN> lb;
+  if (nsteps <= 0) return;
+  la.load(A, kofs(0), tid);
+  lb.load(B, kofs(0), tid);
+  la.store(base, tid);
+  lb.store(base + BOFF, tid);
+  __syncthreads();
+
+  // Fragment read offsets within a stage.
+  const int frow = lane & 31;
+  const int fk = (lane >> 5) * 8;
+  const int a_base = (wm * C::WM + frow) * C::LDK + fk;
+  const int b_base = (wn * C::WN + frow) * C::LDK + fk;
+
+  for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
+    const bool more = s + 1 < nsteps;
+    if (more) {
+      int k1 = kofs(s + 1);
+      la.load(A, k1, tid);
+      lb.load(B, k1, tid);
+    }
+    const lds_ptr<T> as = base + cur * C::STAGE_ELEMS;
+    const lds_ptr<T> bs = as + BOFF;
+#pragma unroll
+    for (int g = 0; g < C::KGROUPS; ++g) {
+      Frag<T> fa[C::FM], fb[C::FN];
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) lds_frag(fa[i], as + a_base + i * 32 * C::LDK + g * 16);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) lds_frag(fb[j], bs + b_base + j * 32 * C::LDK + g * 16);
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) mma16(acc[i][j], fa[i], fb[j]);
+    }
+    if (more) {
+      la.store(base + (cur ^ 1) * C::STAGE_ELEMS, tid);
+      lb.store(base + (cur ^ 1) * C::STAGE_ELEMS + BOFF, tid);
+    }
+    __syncthreads();
+  }
+}
+
+// Output coordinates of accumulator element r of block (fm, fn) for this lane,
+// relative to the work-group tile origin.
+template <class C>
+struct AccMap {
+  int row0, col;  // row of r = row0 + fm*32 + 8*(r/4) + (r%4); col + fn*32
+  __device__ __forceinline__ AccMap() {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    row0 = wm * C::WM + 4 * (lane >> 5);
+    col = wn * C::WN + (lane & 31);
+  }
+  __device__ __forceinline__ int row(int fm, int r) const { return row0 + fm * 32 + 8 * (r >> 2) + (r & 3); }
+  __device__ __forceinline__ int colj(int fn) const { return col + fn * 32; }
+};
+
+}  // namespace cce

@@ -1,0 +1,88 @@
+// Internal constants, problem description and workspace layout shared by the
+// C-ABI host code and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cce {
+
+// Tile geometry.  The forward and gradient tiles are kTileV vocab x kTileN
+// tokens; every wave of the forward owns kPartialWidth vocab rows and writes
+// one (max, sum-exp) partial per (token, kPartialWidth-block).  The gradient
+// filter decides per (kTileN tokens, kTileV vocab) tile.
+constexpr int kTileV = 256;
+constexpr int kTileN = 256;
+constexpr int kPartialWidth = 128;
+constexpr int kMaxBlocks = 4096;  // K blocks one contraction tile can list
+
+constexpr int kDtypeBf16 = 0;
+constexpr int kDtypeF32 = 1;
+constexpr int kReductionNone = 0;
+constexpr int kReductionSum = 1;
+constexpr int kReductionMean = 2;
+constexpr int kAccumDeterministic = 0;
+constexpr int kAccumAtomic = 1;
+
+// int32 counters at the start of the workspace.
+constexpr int kHdrNValid = 0;
+constexpr int kHdrBadTargets = 1;
+constexpr int kHdrTilesKept = 2;
+constexpr int kHdrNValidBwd = 3;
+constexpr int kHdrWords = 64;  // 256 bytes
+
+// Default byte budget of the per-chunk gradient tile buffer G.
+constexpr size_t kDefaultGBudget = size_t(256) << 20;
+
+struct Problem {
+  const void* e;
+  const void* c;
+  const int64_t* targets;
+  int N, D, V;
+  int dtype;
+  int64_t ignore_index;
+  int reduction;
+  // forward outputs / backward inputs
+  float* loss;
+  float* lse;
+  int32_t* n_valid;
+  // backward
+  const float* grad_loss;
+  int filter;
+  int accum;
+  float* dE;
+  float* dC;
+};
+
+struct Layout {
+  size_t total;     // bytes
+  int32_t* hdr;
+  float2* part;     // [N][nVB]
+  float* nll_out;   // [N] per-row loss (the caller's loss buffer for 'none')
+  float* scale;     // [Npad]
+  uint8_t* keep;    // [nb][nvb_t]
+  void* G;          // [Npad][Vc] operand type
+  size_t g_bytes;
+  float* dE_part;   // [splits-1][N][D]
+  int nVB, Npad, nb, nvb_t, Vc, nchunks, splits, splits_atomic;
+};
+
+// Computes the layout for (N, D, V, dtype, vocab_chunk); with base == nullptr
+// only sizes are filled in.
+Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk, void* base);
+
+// Kernel ids of the profiling hook (cce_profile_start / cce_profile_stop).
+enum KernelId {
+  kKFwdTile = 0, kKRows, kKReduce, kKBwdPrep, kKFilter, kKGradTile, kKDC, kKDE, kKDEReduce, kKFill,
+  kNumKernels
+};
+// Records start/stop events around one launch of kernel `id` when profiling of
+// that id is active (no-op otherwise).
+void prof_before(int id, hipStream_t st);
+void prof_after(int id, hipStream_t st);
+
+hipError_t launch_forward(const Problem& P, const Layout& L, hipStream_t st);
+hipError_t launch_backward(const Problem& P, const Layout& L, hipStream_t st);
+
+}  // namespace cce

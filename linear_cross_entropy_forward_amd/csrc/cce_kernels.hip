@@ -1,0 +1,627 @@
+// HIP kernels for the fused linear cross-entropy on gfx950.
+//
+// Method (Wijmans et al., "Cut Your Losses in Large-Vocabulary Language
+// Models", abstract; mlx-cross-entropy README, "How it works"):
+//   loss_i = LSE_j(e_i . c_j) - e_i . c_{y_i}, with the [N, V] logits formed
+//   only tile by tile in registers, never in global memory.
+//
+// Forward:  fwd_tile      S^T tile = C_v E_b^T on MFMA, per (token, 128-vocab
+//                         block) max m and sum-exp s written as partials
+//           rows          correct-token gather-dot, LSE = combine of partials,
+//                         per-row loss (ignore mask)
+//           reduce        fixed-order mean / sum and the exact valid count
+// Backward: bwd_prep      per-row gradient scale (mean/sum/none, ignore mask)
+//           filter        tile keep map: a (token block, vocab block) tile is
+//                         kept iff some valid row's softmax reaches 2^-12 on it
+//                         (README "How it works" item 2, using the forward's
+//                         per-block maxima) or holds a valid row's target
+//           grad_tile     recompute S for kept tiles, G = (p - onehot) * scale
+//                         rounded to the operand type, into a vocab chunk of G
+//           dC_gemm       dC[v] = sum over kept token blocks of G^T E
+//           dE_gemm       dE   += sum over kept vocab blocks of G C
+//                         (split over vocab, fixed-order partial reduce, or
+//                         fp32 atomics)
+#include "cce_gemm.hpp"
+#include "cce_internal.hpp"
+
+namespace cce {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Work-groups are dispatched round-robin over the 8 XCDs (WG i on XCD i % 8).
+// Give each XCD a contiguous run of logical tiles so that tiles sharing an
+// operand block run on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int i, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = i & 7, j = i >> 3;
+  return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<uint16_t>(uint16_t v) {
+  return __builtin_bit_cast(float, (uint32_t)v << 16);
+}
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+
+// Four consecutive fp32 values in the operand type, packed for one store.
+__device__ __forceinline__ void store4(rsrc_t r, uint32_t off, float a, float b, float c, float d,
+                                       const uint16_t*) {
+  __bf16 x0 = (__bf16)a, x1 = (__bf16)b, x2 = (__bf16)c, x3 = (__bf16)d;
+  uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, x0) | ((uint32_t)__builtin_bit_cast(uint16_t, x1) << 16);
+  uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, x2) | ((uint32_t)__builtin_bit_cast(uint16_t, x3) << 16);
+  u32x2 v = {lo, hi};
+  st64(r, off, v);
+}
+__device__ __forceinline__ void store4(rsrc_t r, uint32_t off, float a, float b, float c, float d,
+                                       const float*) {
+  u32x4 v = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+             __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+// ============================================================================
+// Forward logit tile + per-block online LSE partials.
+// Output tile rows are vocabulary entries, columns are tokens, so each lane
+// holds 16 vocab values of one token per 32x32 block and the vocabulary
+// reduction is mostly in-lane.
+// ============================================================================
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T* __restrict__ c,
+                                                            const typename C::T* __restrict__ e,
+                                                            int N, int D, int V, float2* __restrict__ part,
+                                                            int nVB, int tiles_n, int total) {
+  using T = typename C::T;
+  __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int tv = tile / tiles_n, tn = tile % tiles_n;
+  const int v0 = tv * C::BM, n0 = tn * C::BN;
+
+  Operand A{make_rsrc(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T)), (uint32_t)D,
+            min(C::BM, V - v0), D};
+  Operand B{make_rsrc(e + (size_t)n0 * D, (uint64_t)(N - n0) * D * sizeof(T)), (uint32_t)D,
+            min(C::BN, N - n0), D};
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
+  mainloop<C, false, false, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem);
+
+  AccMap<C> am;
+  const int lane = threadIdx.x & 63;
+  const int wm = (threadIdx.x >> 6) / C::WAVES_N;
+  const int vblk = (v0 + wm * C::WM) / C::WM;
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int n = n0 + am.colj(fn);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (v0 + am.row(fm, r) < V) mx = fmaxf(mx, acc[fm][fn][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mxl = mx * kLog2e;
+    float s = 0.f;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (v0 + am.row(fm, r) < V) s += fast_exp2(__builtin_fmaf(acc[fm][fn][r], kLog2e, -mxl));
+    s += __shfl_xor(s, 32, 64);
+    if (lane < 32 && n < N && vblk < nVB) part[(size_t)n * nVB + vblk] = make_float2(mx, s);
+  }
+}
+
+// ============================================================================
+// Per-row: correct-token logit (gather-dot), LSE from the partials, loss.
+// One wave per row.
+// ============================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void rows_kernel(const T* __restrict__ e, const T* __restrict__ c,
+                                                   const int64_t* __restrict__ targets, int N, int D,
+                                                   int V, int64_t ignore_index,
+                                                   const float2* __restrict__ part, int nVB,
+                                                   float* __restrict__ lse_out, float* __restrict__ nll) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= N) return;
+  const int64_t t = targets[i];
+  const bool valid = t != ignore_index;
+  const bool inrange = t >= 0 && t < V;
+  constexpr int VEC = Elem<T>::VEC;
+
+  float zy = 0.f;
+  if (valid && inrange) {
+    rsrc_t re = make_rsrc(e + (size_t)i * D, (uint64_t)D * sizeof(T));
+    rsrc_t rc = make_rsrc(c + (size_t)t * D, (uint64_t)D * sizeof(T));
+    float acc = 0.f;
+    for (int k = lane * VEC; k < D; k += 64 * VEC) {
+      u32x4 a = ld128(re, (uint32_t)k * sizeof(T));
+      u32x4 b = ld128(rc, (uint32_t)k * sizeof(T));
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc = __builtin_fmaf(__builtin_bit_cast(float, a[q] << 16), __builtin_bit_cast(float, b[q] << 16), acc);
+          acc = __builtin_fmaf(__builtin_bit_cast(float, a[q] & 0xffff0000u),
+                               __builtin_bit_cast(float, b[q] & 0xffff0000u), acc);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc = __builtin_fmaf(__builtin_bit_cast(float, a[q]), __builtin_bit_cast(float, b[q]), acc);
+      }
+    }
+    zy = wave_sum(acc);
+  }
+
+  const float2* p = part + (size_t)i * nVB;
+  float m = -INFINITY;
+  for (int v = lane; v < nVB; v += 64) m = fmaxf(m, p[v].x);
+  m = wave_max(m);
+  const float ml = m * kLog2e;
+  float s = 0.f;
+  for (int v = lane; v < nVB; v += 64) {
+    float2 q = p[v];
+    s += q.y * fast_exp2(__builtin_fmaf(q.x, kLog2e, -ml));
+  }
+  s = wave_sum(s);
+  const float lse = m + fast_log2(s) * kLn2;
+  if (lane == 0) {
+    lse_out[i] = lse;
+    nll[i] = valid ? (inrange ? lse - zy : __builtin_nanf("")) : 0.f;
+  }
+}
+
+// ============================================================================
+// Fixed-order reduction of the per-row losses (one work-group), exact counts.
+// ============================================================================
+__global__ __launch_bounds__(1024) void reduce_kernel(const float* __restrict__ nll,
+                                                      const int64_t* __restrict__ targets, int N, int V,
+                                                      int64_t ignore_index, int reduction,
+                                                      float* __restrict__ loss, int32_t* __restrict__ n_valid,
+                                                      int32_t* __restrict__ hdr) {
+  __shared__ double ssum[1024];
+  __shared__ int scnt[1024], sbad[1024];
+  const int tid = threadIdx.x;
+  double acc = 0.0;
+  int cnt = 0, bad = 0;
+  for (int i = tid; i < N; i += 1024) {
+    const int64_t t = targets[i];
+    if (t != ignore_index) {
+      ++cnt;
+      if (t < 0 || t >= V) ++bad;
+    }
+    if (reduction != kReductionNone) acc += (double)nll[i];
+  }
+  ssum[tid] = acc;
+  scnt[tid] = cnt;
+  sbad[tid] = bad;
+  __syncthreads();
+  for (int o = 512; o >= 1; o >>= 1) {
+    if (tid < o) {
+      ssum[tid] += ssum[tid + o];
+      scnt[tid] += scnt[tid + o];
+      sbad[tid] += sbad[tid + o];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int nv = scnt[0];
+    if (reduction == kReductionSum) loss[0] = (float)ssum[0];
+    else if (reduction == kReductionMean) loss[0] = (float)(ssum[0] / (double)(nv > 0 ? nv : 1));
+    if (n_valid) n_valid[0] = nv;
+    hdr[kHdrNValid] = nv;
+    hdr[kHdrBadTargets] = sbad[0];
+  }
+}
+
+// ============================================================================
+// Backward: per-row scale  d(loss)/d(nll_i) * upstream gradient, 0 if ignored,
+// NaN for an out-of-range target; rows in [N, Npad) get 0.
+// ============================================================================
+__global__ __launch_bounds__(1024) void bwd_prep_kernel(const int64_t* __restrict__ targets, int N,
+                                                        int Npad, int V, int64_t ignore_index,
+                                                        int reduction, const float* __restrict__ grad_loss,
+                                                        float* __restrict__ scale, int32_t* __restrict__ hdr) {
+  __shared__ int scnt[1024];
+  const int tid = threadIdx.x;
+  int cnt = 0;
+  for (int i = tid; i < N; i += 1024) cnt += targets[i] != ignore_index;
+  scnt[tid] = cnt;
+  __syncthreads();
+  for (int o = 512; o >= 1; o >>= 1) {
+    if (tid < o) scnt[tid] += scnt[tid + o];
+    __syncthreads();
+  }
+  const int nv = scnt[0];
+  const float g0 = reduction == kReductionNone ? 0.f : grad_loss[0];
+  const float gm = reduction == kReductionMean ? (float)((double)g0 / (double)(nv > 0 ? nv : 1)) : g0;
+  for (int i = tid; i < Npad; i += 1024) {
+    float s = 0.f;
+    if (i < N) {
+      const int64_t t = targets[i];
+      if (t != ignore_index) {
+        s = reduction == kReductionNone ? grad_loss[i] : gm;
+        if (t < 0 || t >= V) s = __builtin_nanf("");
+      }
+    }
+    scale[i] = s;
+  }
+  if (tid == 0) {
+    hdr[kHdrNValidBwd] = nv;
+    hdr[kHdrTilesKept] = 0;
+  }
+}
+
+// ============================================================================
+// Backward: tile keep map.  Work-group = one token block x 256 vocab blocks.
+// ============================================================================
+__global__ __launch_bounds__(256) void filter_kernel(const int64_t* __restrict__ targets,
+                                                     const float* __restrict__ lse,
+                                                     const float2* __restrict__ part, int N, int V,
+                                                     int nVB, int64_t ignore_index, int Bn, int Bv,
+                                                     int PW, int nvb_t, int filter,
+                                                     uint8_t* __restrict__ keep, int32_t* __restrict__ hdr) {
+  __shared__ float s_lse[kTileN];
+  __shared__ int s_tb[kTileN];
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  for (int r = tid; r < Bn; r += blockDim.x) {
+    const int i = b * Bn + r;
+    float l = INFINITY;
+    int tb = -1;
+    if (i < N) {
+      const int64_t t = targets[i];
+      if (t != ignore_index && t >= 0 && t < V) {
+        l = lse[i];
+        tb = (int)(t / Bv);
+      }
+    }
+    s_lse[r] = l;
+    s_tb[r] = tb;
+  }
+  __syncthreads();
+  const int vb = blockIdx.x * blockDim.x + tid;
+  bool k = false;
+  if (vb < nvb_t) {
+    if (!filter) {
+      k = true;
+    } else {
+      const int ppb = Bv / PW;
+      const int rows = min(Bn, N - b * Bn);
+      const float thr = -12.0f * kLn2;
+      for (int r = 0; r < rows && !k; ++r) {
+        if (s_tb[r] == vb) { k = true; break; }
+        if (s_tb[r] < 0) continue;
+        const float2* p = part + (size_t)(b * Bn + r) * nVB + (size_t)vb * ppb;
+        float m = -INFINITY;
+        for (int q = 0; q < ppb; ++q)
+          if (vb * ppb + q < nVB) m = fmaxf(m, p[q].x);
+        if (m - s_lse[r] >= thr) k = true;
+      }
+    }
+    keep[(size_t)b * nvb_t + vb] = k ? 1 : 0;
+  }
+  const uint64_t bal = __ballot(k);
+  if ((tid & 63) == 0) atomicAdd(&hdr[kHdrTilesKept], (int)__popcll(bal));
+}
+
+// ============================================================================
+// Backward: recompute kept logit tiles and write G = (p - onehot) * scale for
+// one vocabulary chunk [cv0, cv0 + Vc) into G [Npad][Vc] (token-major).
+// ============================================================================
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
+    const typename C::T* __restrict__ c, const typename C::T* __restrict__ e,
+    const int64_t* __restrict__ targets, const float* __restrict__ lse, const float* __restrict__ scale,
+    const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int tiles_v,
+    int tiles_n, int Vc, typename C::T* __restrict__ G, size_t g_bytes) {
+  using T = typename C::T;
+  __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
+  const int total = tiles_v * tiles_n;
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int tvl = tile / tiles_n, tn = tile % tiles_n;
+  const int tv = cvb0 + tvl;
+  if (!keep[(size_t)tn * nvb_t + tv]) return;
+  const int v0 = tv * C::BM, n0 = tn * C::BN;
+
+  Operand A{make_rsrc(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T)), (uint32_t)D,
+            min(C::BM, V - v0), D};
+  Operand B{make_rsrc(e + (size_t)n0 * D, (uint64_t)max(N - n0, 0) * D * sizeof(T)), (uint32_t)D,
+            min(C::BN, N - n0), D};
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
+  mainloop<C, false, false, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem);
+
+  AccMap<C> am;
+  rsrc_t rg = make_rsrc(G, g_bytes);
+  const int vl0 = tvl * C::BM;  // chunk-local column of the tile
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int n = n0 + am.colj(fn);
+    const bool vn = n < N;
+    const float lsel = vn ? lse[n] * kLog2e : 0.f;
+    const float sc = vn ? scale[n] : 0.f;
+    const int64_t tgt = vn ? targets[n] : -1;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float g[4];
+        const int rl = am.row(fm, 4 * q);  // tile-local vocab row of element 4q
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int v = v0 + rl + u;
+          float p = fast_exp2(__builtin_fmaf(acc[fm][fn][4 * q + u], kLog2e, -lsel));
+          p -= (v == tgt) ? 1.f : 0.f;
+          g[u] = (vn && v < V) ? p * sc : 0.f;
+        }
+        const uint32_t off = ((uint32_t)n * (uint32_t)Vc + (uint32_t)(vl0 + rl)) * (uint32_t)sizeof(T);
+        store4(rg, off, g[0], g[1], g[2], g[3], (const T*)nullptr);
+      }
+    }
+  }
+}
+
+// Kept K blocks of one output tile into LDS; returns their count.
+__device__ __forceinline__ int collect_blocks(const uint8_t* __restrict__ keep, size_t base, int stride,
+                                             int count, uint16_t* list) {
+  __shared__ int s_cnt;
+  if (threadIdx.x < 64) {
+    int total = 0;
+    for (int j0 = 0; j0 < count; j0 += 64) {
+      const int j = j0 + (int)threadIdx.x;
+      const bool k = j < count && keep[base + (size_t)j * stride];
+      const uint64_t bal = __ballot(k);
+      const int pre = __popcll(bal & ((1ull << threadIdx.x) - 1ull));
+      if (k) list[total + pre] = (uint16_t)j;
+      total += __popcll(bal);
+    }
+    if (threadIdx.x == 0) s_cnt = total;
+  }
+  __syncthreads();
+  return s_cnt;
+}
+
+// ============================================================================
+// dC rows of one vocabulary chunk: dC[v][d] = sum_n G[n][v] E[n][d] over the
+// kept token blocks of the tile's vocab block.  Both operands are MN-major.
+// ============================================================================
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
+    const typename C::T* __restrict__ G, const typename C::T* __restrict__ e,
+    const uint8_t* __restrict__ keep, int N, int Npad, int D, int V, int nvb_t, int cvb0, int cv0,
+    int clen, int tiles_v, int tiles_d, int Vc, size_t g_bytes, float* __restrict__ dC) {
+  using T = typename C::T;
+  __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
+  __shared__ uint16_t blocks[kMaxBlocks];
+  const int total = tiles_v * tiles_d;
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int tvl = tile / tiles_d, td = tile % tiles_d;
+  const int vl0 = tvl * C::BM, d0 = td * C::BN;
+  const int nb = Npad / kTileN;
+  const int nk = collect_blocks(keep, (size_t)(cvb0 + tvl), nvb_t, nb, blocks);
+
+  Operand A{make_rsrc(G + vl0, g_bytes - (size_t)vl0 * sizeof(T)), (uint32_t)Vc, min(C::BM, clen - vl0),
+            Npad};
+  Operand B{make_rsrc(e + d0, ((uint64_t)N * D - d0) * sizeof(T)), (uint32_t)D, min(C::BN, D - d0), N};
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
+  constexpr int SPB = kTileN / C::BK;
+  mainloop<C, true, true, SPB>(acc, A, B, nk * SPB, blocks, smem);
+
+  AccMap<C> am;
+  const int vg0 = cv0 + vl0;
+  rsrc_t ro = make_rsrc(dC + (size_t)vg0 * D, (uint64_t)(V - vg0) * D * sizeof(float));
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int d = d0 + am.colj(fn);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int vr = am.row(fm, r);
+        const bool ok = d < D && vl0 + vr < clen;
+        stf(ro, ok ? ((uint32_t)vr * (uint32_t)D + (uint32_t)d) * 4u : kOOB, acc[fm][fn][r]);
+      }
+    }
+}
+
+// ============================================================================
+// dE for one vocabulary chunk: dE[n][d] (+)= sum_v G[n][v] C[v][d] over the
+// kept vocab blocks of the tile's token block in split `s` of the chunk.
+// A = G (K-major), B = C (MN-major).
+// ============================================================================
+template <class C>
+__global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
+    const typename C::T* __restrict__ G, const typename C::T* __restrict__ c,
+    const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
+    int cnvb, int tiles_n, int tiles_d, int splits, int Vc, size_t g_bytes, float* __restrict__ dE,
+    float* __restrict__ dE_part, int accumulate, int atomic) {
+  using T = typename C::T;
+  __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
+  __shared__ uint16_t blocks[kMaxBlocks];
+  const int total = tiles_n * tiles_d * splits;
+  const int tile = xcd_remap(blockIdx.x, total);
+  const int s = tile / (tiles_n * tiles_d);
+  const int rem = tile % (tiles_n * tiles_d);
+  const int tn = rem / tiles_d, td = rem % tiles_d;
+  const int n0 = tn * C::BM, d0 = td * C::BN;
+  // this split's vocab blocks of the chunk
+  const int vb_lo = (int)((int64_t)cnvb * s / splits), vb_hi = (int)((int64_t)cnvb * (s + 1) / splits);
+  const int nk = collect_blocks(keep, (size_t)tn * nvb_t + cvb0 + vb_lo, 1, vb_hi - vb_lo, blocks);
+  for (int j = threadIdx.x; j < nk; j += blockDim.x) blocks[j] += vb_lo;
+  __syncthreads();
+
+  Operand A{make_rsrc(G + (size_t)n0 * Vc, g_bytes - (size_t)n0 * Vc * sizeof(T)), (uint32_t)Vc,
+            min(C::BM, N - n0), clen};
+  Operand B{make_rsrc(c + (size_t)cv0 * D + d0, ((uint64_t)(V - cv0) * D - d0) * sizeof(T)), (uint32_t)D,
+            min(C::BN, D - d0), clen};
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
+  constexpr int SPB = kTileV / C::BK;
+  mainloop<C, false, true, SPB>(acc, A, B, nk * SPB, blocks, smem);
+
+  if (nk == 0 && (accumulate || atomic)) return;  // nothing to add
+  AccMap<C> am;
+  float* out = (atomic || s == 0) ? dE : dE_part + (size_t)(s - 1) * N * D;
+  float* ob = out + (size_t)n0 * D;
+  rsrc_t ro = make_rsrc(ob, (uint64_t)(N - n0) * D * sizeof(float));
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int d = d0 + am.colj(fn);
+      uint32_t off[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int nr = am.row(fm, r);
+        off[r] = (d < D && n0 + nr < N) ? ((uint32_t)nr * (uint32_t)D + (uint32_t)d) * 4u : kOOB;
+      }
+      f32x16 v = acc[fm][fn];
+      if (atomic) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (off[r] != kOOB) unsafeAtomicAdd(ob + off[r] / 4u, v[r]);
+      } else {
+        if (accumulate) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] += ldf(ro, off[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) stf(ro, off[r], v[r]);
+      }
+    }
+}
+
+// dE += dE_part[0] + dE_part[1] + ... in that order (deterministic).
+__global__ __launch_bounds__(256) void dE_reduce_kernel(float* __restrict__ dE, const float* __restrict__ part,
+                                                        size_t n4, int nparts, size_t stride4) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 v = reinterpret_cast<f32x4*>(dE)[i];
+  for (int p = 0; p < nparts; ++p) v += reinterpret_cast<const f32x4*>(part)[(size_t)p * stride4 + i];
+  reinterpret_cast<f32x4*>(dE)[i] = v;
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// ============================================================================
+// Host launchers.
+// ============================================================================
+using CfgBf16 = Cfg<uint16_t, kTileV, kTileN, 2, 2>;
+using CfgF32 = Cfg<float, kTileV, kTileN, 2, 2>;
+static_assert(CfgBf16::WM == kPartialWidth && CfgF32::WM == kPartialWidth, "partial width");
+
+template <class C>
+static hipError_t launch_forward_t(const Problem& P, const Layout& L, hipStream_t st) {
+  using T = typename C::T;
+  const T* e = (const T*)P.e;
+  const T* c = (const T*)P.c;
+  const int tiles_v = (P.V + C::BM - 1) / C::BM, tiles_n = (P.N + C::BN - 1) / C::BN;
+  const int total = tiles_v * tiles_n;
+  prof_before(kKFwdTile, st);
+  hipLaunchKernelGGL(fwd_tile_kernel<C>, dim3(total), dim3(C::NT), 0, st, c, e, P.N, P.D, P.V, L.part, L.nVB,
+                     tiles_n, total);
+  prof_after(kKFwdTile, st);
+  prof_before(kKRows, st);
+  hipLaunchKernelGGL(rows_kernel<T>, dim3((P.N + 3) / 4), dim3(256), 0, st, e, c, P.targets, P.N, P.D, P.V,
+                     P.ignore_index, L.part, L.nVB, P.lse, L.nll_out);
+  prof_after(kKRows, st);
+  prof_before(kKReduce, st);
+  hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(1024), 0, st, L.nll_out, P.targets, P.N, P.V, P.ignore_index,
+                     P.reduction, P.loss, P.n_valid, L.hdr);
+  prof_after(kKReduce, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const Problem& P, const Layout& L, hipStream_t st) {
+  return P.dtype == kDtypeBf16 ? launch_forward_t<CfgBf16>(P, L, st) : launch_forward_t<CfgF32>(P, L, st);
+}
+
+template <class C>
+static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream_t st) {
+  using T = typename C::T;
+  const T* e = (const T*)P.e;
+  const T* c = (const T*)P.c;
+  T* G = (T*)L.G;
+  prof_before(kKBwdPrep, st);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(1024), 0, st, P.targets, P.N, L.Npad, P.V, P.ignore_index,
+                     P.reduction, P.grad_loss, L.scale, L.hdr);
+  prof_after(kKBwdPrep, st);
+  prof_before(kKFilter, st);
+  hipLaunchKernelGGL(filter_kernel, dim3((L.nvb_t + 255) / 256, L.nb), dim3(256), 0, st, P.targets, P.lse,
+                     L.part, P.N, P.V, L.nVB, P.ignore_index, kTileN, kTileV, kPartialWidth, L.nvb_t, P.filter,
+                     L.keep, L.hdr);
+  prof_after(kKFilter, st);
+  if (P.accum == kAccumAtomic) {
+    const size_t n = (size_t)P.N * P.D;
+    prof_before(kKFill, st);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P.dE, n);
+    prof_after(kKFill, st);
+  }
+  const int tiles_n = L.Npad / kTileN;
+  const int tiles_d = (P.D + C::BN - 1) / C::BN;
+  for (int ch = 0; ch < L.nchunks; ++ch) {
+    const int cv0 = ch * L.Vc;
+    const int clen = min(L.Vc, P.V - cv0);
+    const int cnvb = (clen + kTileV - 1) / kTileV;
+    const int cvb0 = cv0 / kTileV;
+    prof_before(kKGradTile, st);
+    hipLaunchKernelGGL(grad_tile_kernel<C>, dim3(cnvb * tiles_n), dim3(C::NT), 0, st, c, e, P.targets, P.lse,
+                       L.scale, L.keep, P.N, P.D, P.V, L.nvb_t, cvb0, cnvb, tiles_n, L.Vc, G, L.g_bytes);
+    prof_after(kKGradTile, st);
+    prof_before(kKDC, st);
+    hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(cnvb * tiles_d), dim3(C::NT), 0, st, G, e, L.keep, P.N, L.Npad,
+                       P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_d, L.Vc, L.g_bytes, P.dC);
+    prof_after(kKDC, st);
+    const int splits = P.accum == kAccumAtomic ? L.splits_atomic : L.splits;
+    prof_before(kKDE, st);
+    hipLaunchKernelGGL(dE_gemm_kernel<C>, dim3(tiles_n * tiles_d * splits), dim3(C::NT), 0, st, G, c, L.keep,
+                       P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits, L.Vc, L.g_bytes,
+                       P.dE, L.dE_part, ch > 0 ? 1 : 0, P.accum == kAccumAtomic ? 1 : 0);
+    prof_after(kKDE, st);
+  }
+  if (P.accum != kAccumAtomic && L.splits > 1) {
+    const size_t n4 = (size_t)P.N * P.D / 4;
+    prof_before(kKDEReduce, st);
+    hipLaunchKernelGGL(dE_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, P.dE, L.dE_part,
+                       n4, L.splits - 1, n4);
+    prof_after(kKDEReduce, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const Problem& P, const Layout& L, hipStream_t st) {
+  return P.dtype == kDtypeBf16 ? launch_backward_t<CfgBf16>(P, L, st) : launch_backward_t<CfgF32>(P, L, st);
+}
+
+}  // namespace cce

@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/cce.h declares, sizes its workspace consistently, and rejects bad
+arguments synchronously, before any launch (so no device is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cce.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x100000          # aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def L():
+    import linear_cross_entropy_forward_amd as M
+    return M.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cce_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"cce_forward", "cce_backward", "cce_workspace_size", "cce_read_stats"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in cce.h but not exported"
+
+
+def test_status_strings_and_tiles(L):
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 99):
+        assert L.cce_status_string(s)
+    import linear_cross_entropy_forward_amd as M
+    bn, bv, pw = M.tile_shape()
+    assert bn == 256 and bv == 256 and pw == 128 and bv % pw == 0
+    for k in range(10):
+        assert L.cce_kernel_name(k) != b"unknown"
+    assert L.cce_kernel_name(10) == b"unknown"
+
+
+def test_workspace_size(L):
+    ws = L.cce_workspace_size
+    assert ws(0, 64, 100, 0, 0) == 0 and ws(4, 64, 100, 7, 0) == 0 and ws(4, 64, 100, 0, 100) == 0
+    a = ws(4096, 4096, 128256, 0, 0)
+    b = ws(4096, 4096, 128256, 0, 1024)
+    assert a > b > 0
+    # loss-path part: partials of N x ceil(V/128) (max, sum-exp) pairs dominate
+    part = 4096 * ((128256 + 127) // 128) * 8
+    assert b > part
+    assert ws(4096, 4096, 128256, 1, 0) >= ws(4096, 4096, 128256, 0, 0) // 2
+
+
+def _fwd(L, e=FAKE, c=FAKE, t=FAKE, N=64, D=64, V=100, dt=0, ign=-100, red=2, cap=0.0, loss=FAKE, lse=FAKE,
+         ws=FAKE, wsb=1 << 30):
+    return L.cce_forward(e, c, t, N, D, V, dt, ign, red, cap, loss, lse, None, ws, wsb, None)
+
+
+def _bwd(L, e=FAKE, N=64, D=64, V=100, dt=0, red=2, cap=0.0, flt=1, acc=0, chunk=0, dE=FAKE, wsb=1 << 30):
+    return L.cce_backward(e, FAKE, FAKE, N, D, V, dt, -100, red, cap, FAKE, FAKE, flt, acc, chunk, dE, FAKE,
+                          FAKE, wsb, None)
+
+
+def test_forward_argument_errors(L):
+    assert _fwd(L, e=None) == INVALID
+    assert _fwd(L, t=None) == INVALID
+    assert _fwd(L, loss=None) == INVALID
+    assert _fwd(L, lse=None) == INVALID
+    assert _fwd(L, ws=None) == INVALID
+    assert _fwd(L, N=0) == INVALID and _fwd(L, D=-1) == INVALID and _fwd(L, V=0) == INVALID
+    assert _fwd(L, dt=2) == INVALID
+    assert _fwd(L, red=3) == INVALID
+    assert _fwd(L, e=FAKE + 4) == INVALID            # misaligned
+    assert _fwd(L, cap=30.0) == UNSUPPORTED         # soft-capping is not defined here
+    assert _fwd(L, D=60) == UNSUPPORTED             # bf16 rows must be 16-byte multiples
+    assert _fwd(L, dt=1, D=62) == UNSUPPORTED
+    assert _fwd(L, wsb=16) == WORKSPACE
+
+
+def test_backward_argument_errors(L):
+    assert _bwd(L, e=None) == INVALID
+    assert _bwd(L, dE=None) == INVALID
+    assert _bwd(L, flt=2) == INVALID
+    assert _bwd(L, acc=5) == INVALID
+    assert _bwd(L, chunk=100) == INVALID
+    assert _bwd(L, cap=1.0) == UNSUPPORTED
+    assert _bwd(L, wsb=1024) == WORKSPACE
+    need = L.cce_workspace_size(64, 64, 100, 0, 0)
+    assert _bwd(L, wsb=need - 1) == WORKSPACE
+
+
+def test_size_limits(L):
+    # operands addressed from one base must stay below 2 GiB
+    assert _fwd(L, N=1 << 20, D=1024) == UNSUPPORTED
+    assert _fwd(L, N=(1 << 20) + 256, D=8) == UNSUPPORTED
+
+
+def test_stats_and_profile_argument_errors(L):
+    import linear_cross_entropy_forward_amd as M
+    st = M._Stats()
+    assert L.cce_read_stats(None, 1024, 1, 1, None, ctypes.byref(st)) == INVALID
+    assert L.cce_read_stats(FAKE, 8, 1, 1, None, ctypes.byref(st)) == INVALID
+    assert L.cce_profile_start(-1, 4) == INVALID
+    assert L.cce_profile_start(10, 4) == INVALID
+    assert L.cce_profile_start(0, 0) == INVALID
+    ms, n = ctypes.c_double(), ctypes.c_int()
+    assert L.cce_profile_stop(11, ctypes.byref(ms), ctypes.byref(n)) == INVALID
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    import linear_cross_entropy_forward_amd as M
+    e = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(M.CCEError):
+        M.forward(e, e, torch.zeros(4, dtype=torch.int64))

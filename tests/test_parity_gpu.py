@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Small cases span several 256x256 tiles with ragged edges in every dimension
+(N, V and D not multiples of the tile sizes) and run the whole oracle;
+full-size cases (marked slow) run the launch configuration the benchmark
+times and compare sampled outputs the oracle computes row by row.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from helpers import (GRAD_RTOL, GRAD_RTOL_FILTERED, check_grad, check_loss, check_lse, dev, dev_targets,
+                     rel_fro)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def M():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import linear_cross_entropy_forward_amd as M
+    M.lib()
+    return M
+
+
+def _grad_arg(reduction, N, seed=0):
+    import torch
+    if reduction == "none":
+        g = np.random.default_rng(seed).standard_normal(N).astype(np.float32)
+        return g, torch.from_numpy(g).cuda()
+    return 1.0, torch.ones(1, dtype=torch.float32, device="cuda")
+
+
+def run(M, inp, reduction="mean", filter=False, accum="deterministic", vocab_chunk=0, ignore_index=-100,
+        backward=True, grad_seed=0):
+    import torch
+    dt = inp.get("dtype") or inp["workload"].dtype
+    e, c, t = dev(inp["e"], dt), dev(inp["c"], dt), dev_targets(inp["targets"])
+    N, V = e.shape[0], c.shape[0]
+    loss, lse, nv, ws = M.forward(e, c, t, ignore_index=ignore_index, reduction=reduction,
+                                  vocab_chunk=vocab_chunk)
+    out = {"loss": None, "lse": None}
+    torch.cuda.synchronize()
+    out["stats_fwd"] = M.read_stats(ws, N, V)
+    if backward:
+        g_np, g = _grad_arg(reduction, N, grad_seed)
+        dE, dC = M.backward(e, c, t, lse, g, ws, ignore_index=ignore_index, reduction=reduction, filter=filter,
+                            accum=accum, vocab_chunk=vocab_chunk)
+        torch.cuda.synchronize()
+        out["dE"], out["dC"], out["g"] = dE.cpu().numpy(), dC.cpu().numpy(), g_np
+        out["stats"] = M.read_stats(ws, N, V)
+    out["loss"] = loss.cpu().numpy()
+    out["lse"] = lse.cpu().numpy()
+    out["n_valid"] = int(nv.cpu().item())
+    return out
+
+
+def full_check(M, inp, reduction, filter, accum="deterministic", vocab_chunk=0, ignore_index=-100, label=""):
+    e, c, t = inp["e"], inp["c"], inp["targets"]
+    r = run(M, inp, reduction, filter, accum, vocab_chunk, ignore_index)
+    f = O.forward(e, c, t, ignore_index=ignore_index, reduction=reduction)
+    assert r["n_valid"] == f.n_valid, label
+    assert r["stats_fwd"]["n_valid"] == f.n_valid
+    check_loss(r["loss"], f.loss, reduction, label)
+    check_lse(r["lse"], f.lse, label)
+    if reduction == "none":
+        assert (r["loss"][~f.valid] == 0.0).all(), "ignored rows must give exactly 0"
+    b = O.backward(e, c, t, ignore_index=ignore_index, reduction=reduction, grad_loss=r["g"])
+    assert (r["dE"][~f.valid] == 0.0).all(), "ignored rows must give exactly 0 gradient"
+    Bn, Bv, _ = M.tile_shape()
+    if filter:
+        lse_o, keep = O.lse_and_keep(e, c, t, Bn, Bv, ignore_index=ignore_index)
+        bf = O.backward(e, c, t, ignore_index=ignore_index, reduction=reduction, grad_loss=r["g"], keep=keep,
+                        tile=(Bn, Bv))
+        check_grad(r["dE"], bf.dE, GRAD_RTOL, label + " dE vs filtered oracle")
+        check_grad(r["dC"], bf.dC, GRAD_RTOL, label + " dC vs filtered oracle")
+        check_grad(r["dE"], b.dE, GRAD_RTOL_FILTERED, label + " dE vs exact")
+        check_grad(r["dC"], b.dC, GRAD_RTOL_FILTERED, label + " dC vs exact")
+        kept = r["stats"]["tiles_kept"]
+        assert abs(kept - int(keep.sum())) <= max(2, keep.size // 100), (kept, int(keep.sum()), keep.size)
+    else:
+        check_grad(r["dE"], b.dE, GRAD_RTOL, label + " dE")
+        check_grad(r["dC"], b.dC, GRAD_RTOL, label + " dC")
+        assert r["stats"]["tiles_kept"] == r["stats"]["tiles_total"]
+    return r
+
+
+# ----------------------------------------------------------------------------- small, whole oracle
+def test_tiny_workload_fp32(M):
+    inp = W.get("tiny")
+    for flt in (False, True):
+        full_check(M, inp, "mean", flt, label=f"tiny filter={flt}")
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_ragged_bf16(M, reduction):
+    inp = W.custom(600, 136, 1100, "bf16", seed=11, c_std=0.1, ignore_frac=0.05)
+    full_check(M, inp, reduction, False, label=f"ragged {reduction}")
+
+
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_ragged_fp32(M, reduction):
+    inp = W.custom(300, 68, 513, "f32", seed=12, c_std=0.2, ignore_frac=0.1)
+    full_check(M, inp, reduction, True, label=f"ragged fp32 {reduction}")
+
+
+@pytest.mark.parametrize("mode", ["trained", "calibrated"])
+def test_filtering_peaked(M, mode):
+    inp = W.custom(777, 264, 2600, "bf16", seed=13, e_mode=mode, targets="zipf", ignore_frac=0.03)
+    r = full_check(M, inp, "mean", True, label=f"filter {mode}")
+    assert r["stats"]["tiles_kept"] < r["stats"]["tiles_total"], "peaked softmax should skip tiles"
+
+
+@pytest.mark.parametrize("accum", ["deterministic", "atomic"])
+def test_vocab_chunks_and_splits(M, accum):
+    # 256-wide vocabulary chunks: many chunks, several dE splits, ragged last chunk
+    inp = W.custom(530, 200, 1900, "bf16", seed=14, c_std=0.08, ignore_frac=0.05)
+    full_check(M, inp, "sum", False, accum=accum, vocab_chunk=256, label=f"chunks {accum}")
+    full_check(M, inp, "mean", True, accum=accum, vocab_chunk=512, label=f"chunks filtered {accum}")
+
+
+def test_deterministic_bitwise(M):
+    inp = W.custom(700, 256, 3000, "bf16", seed=15, c_std=0.05, ignore_frac=0.02)
+    runs = [run(M, inp, "mean", True, "deterministic") for _ in range(3)]
+    for r in runs[1:]:
+        assert np.array_equal(r["loss"], runs[0]["loss"])
+        assert np.array_equal(r["lse"], runs[0]["lse"])
+        assert np.array_equal(r["dE"], runs[0]["dE"])
+        assert np.array_equal(r["dC"], runs[0]["dC"])
+    ra = run(M, inp, "mean", True, "atomic")
+    assert rel_fro(ra["dE"], runs[0]["dE"]) < 1e-5
+    assert np.array_equal(ra["dC"], runs[0]["dC"])
+
+
+# ----------------------------------------------------------------------------- edge cases
+def test_single_class_vocab(M):
+    inp = W.custom(100, 64, 1, "bf16", seed=16, c_std=0.5)
+    r = full_check(M, inp, "sum", False, label="V=1")
+    assert np.abs(r["loss"]).max() < 1e-6
+
+
+def test_two_class_vocab(M):
+    inp = W.custom(260, 40, 2, "bf16", seed=17, c_std=0.5)
+    full_check(M, inp, "none", False, label="V=2")
+
+
+def test_single_row(M):
+    inp = W.custom(1, 32, 700, "bf16", seed=18, c_std=0.3)
+    full_check(M, inp, "mean", True, label="N=1")
+
+
+def test_all_ignored(M):
+    inp = W.custom(300, 64, 900, "bf16", seed=19, c_std=0.1)
+    inp["targets"][:] = -100
+    r = run(M, inp, "mean", True)
+    assert r["n_valid"] == 0 and float(r["loss"]) == 0.0
+    assert not r["dE"].any() and not r["dC"].any()
+
+
+def test_no_ignored_and_extreme_targets(M):
+    inp = W.custom(513, 96, 1537, "bf16", seed=20, c_std=0.1)
+    t = inp["targets"]
+    t[::3] = 0
+    t[1::3] = 1536
+    full_check(M, inp, "mean", True, label="targets 0 and V-1")
+
+
+def test_repeated_targets(M):
+    inp = W.custom(400, 64, 1000, "bf16", seed=21, c_std=0.1)
+    inp["targets"][:] = 777
+    full_check(M, inp, "sum", False, label="repeated target")
+
+
+def test_large_logits(M):
+    # logits of order 1e3: the LSE must come out finite and within 2e-3
+    inp = W.custom(256, 64, 600, "bf16", seed=22, c_std=0.1)
+    inp["e"] = W.round_to_bf16(inp["e"] * 400.0)
+    r = full_check(M, inp, "none", True, label="large logits")
+    assert np.isfinite(r["lse"]).all() and np.isfinite(r["dE"]).all()
+
+
+def test_custom_ignore_index(M):
+    inp = W.custom(320, 64, 500, "bf16", seed=23, c_std=0.1)
+    inp["targets"][::4] = 7
+    full_check(M, inp, "mean", False, ignore_index=7, label="ignore_index=7")
+
+
+def test_bad_target_is_loud(M):
+    inp = W.custom(64, 32, 100, "bf16", seed=24, c_std=0.1)
+    inp["targets"][5] = 100          # out of range, not the ignore index
+    r = run(M, inp, "none", False)
+    assert math.isnan(r["loss"][5]) and np.isfinite(np.delete(r["loss"], 5)).all()
+    assert r["stats_fwd"]["bad_targets"] == 1
+    assert np.isnan(r["dE"][5]).all()
+
+
+# ----------------------------------------------------------------------------- full-size, sampled
+def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, n_vocab=24, dC_check=True):
+    import torch
+    inp = W.get(name)
+    e, c, t = inp["e"], inp["c"], inp["targets"]
+    N, V = e.shape[0], c.shape[0]
+    print(f"[full] {name} N={N} V={V} reduction={reduction} filter={filter} accum={accum}", flush=True)
+    r = run(M, inp, reduction, filter, accum)
+    rng = np.random.default_rng(99)
+    rows = np.sort(rng.choice(N, n_rows, replace=False))
+    valid = t != -100
+    assert r["n_valid"] == int(valid.sum())
+    fo = O.forward(e, c, t, reduction="none", rows=rows)
+    check_lse(r["lse"][rows], fo.lse, name)
+    if reduction == "none":
+        check_loss(r["loss"][rows], fo.nll, "none", name)
+    Bn, Bv, _ = M.tile_shape()
+    tile = (Bn, Bv)
+    if dC_check or filter:
+        lse_all, keep = O.lse_and_keep(e, c, t, Bn, Bv)
+        if reduction != "none":
+            # the reduced loss from the oracle's full pass
+            nll = np.where(valid, lse_all - np.einsum("ij,ij->i", e.astype(np.float64),
+                                                      c[np.where(valid, t, 0)].astype(np.float64)), 0.0)
+            want = nll.sum() / max(valid.sum(), 1) if reduction == "mean" else nll.sum()
+            check_loss(r["loss"], want, reduction, name)
+        kept = r["stats"]["tiles_kept"]
+        if filter:
+            assert abs(kept - int(keep.sum())) <= max(2, keep.size // 100), (kept, int(keep.sum()))
+    g = r["g"]
+    dE_x = O.dE_rows(e, c, t, rows, reduction=reduction, grad_loss=g)
+    if filter:
+        dE_f = O.dE_rows(e, c, t, rows, reduction=reduction, grad_loss=g, keep=keep, tile=tile)
+        check_grad(r["dE"][rows], dE_f, GRAD_RTOL, name + " dE vs filtered")
+        check_grad(r["dE"][rows], dE_x, GRAD_RTOL_FILTERED, name + " dE vs exact")
+    else:
+        check_grad(r["dE"][rows], dE_x, GRAD_RTOL, name + " dE")
+    if dC_check:
+        vid = np.unique(np.concatenate([rng.choice(V, n_vocab, replace=False), t[valid][:8]]))
+        dC_x = O.dC_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g)
+        if filter:
+            dC_f = O.dC_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g, keep=keep, tile=tile)
+            check_grad(r["dC"][vid], dC_f, GRAD_RTOL, name + " dC vs filtered")
+            check_grad(r["dC"][vid], dC_x, GRAD_RTOL_FILTERED, name + " dC vs exact")
+        else:
+            check_grad(r["dC"][vid], dC_x, GRAD_RTOL, name + " dC")
+    torch.cuda.empty_cache()
+    return r
+
+
+@pytest.mark.slow
+def test_full_llama8b_none_filtered(M):
+    """The benchmark's workload and launch configuration (filter on, deterministic)."""
+    _sampled_full(M, "llama8b", "none", True)
+
+
+@pytest.mark.slow
+def test_full_llama8b_mean_unfiltered(M):
+    _sampled_full(M, "llama8b", "mean", False, dC_check=False)
+
+
+@pytest.mark.slow
+def test_full_llama1b(M):
+    _sampled_full(M, "llama1b", "mean", True)
+    _sampled_full(M, "llama1b", "mean", False, dC_check=False)
+
+
+@pytest.mark.slow
+def test_full_gemma2b_calibrated(M):
+    _sampled_full(M, "gemma2b_cal", "mean", True)
