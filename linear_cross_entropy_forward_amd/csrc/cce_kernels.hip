@@ -148,23 +148,26 @@ __global__ __launch_bounds__(256) void rows_kernel(const T* __restrict__ e, cons
 
   float zy = 0.f;
   if (valid && inrange) {
-    rsrc_t re = make_rsrc(e + (size_t)i * D, (uint64_t)D * sizeof(T));
-    rsrc_t rc = make_rsrc(c + (size_t)t * D, (uint64_t)D * sizeof(T));
+    // plain global loads: the row pointers differ per wave, and the loop bound
+    // keeps every 16-byte access inside the row
+    const T* er = e + (size_t)i * D;
+    const T* cr = c + (size_t)t * D;
     float acc = 0.f;
     for (int k = lane * VEC; k < D; k += 64 * VEC) {
-      u32x4 a = ld128(re, (uint32_t)k * sizeof(T));
-      u32x4 b = ld128(rc, (uint32_t)k * sizeof(T));
-      if constexpr (sizeof(T) == 2) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(er + k);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(cr + k);
+      // (vector elements are copied to scalars before any bit cast: clang
+      // mis-lowers a bit cast applied directly to a vector-element lvalue)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc = __builtin_fmaf(__builtin_bit_cast(float, a[q] << 16), __builtin_bit_cast(float, b[q] << 16), acc);
-          acc = __builtin_fmaf(__builtin_bit_cast(float, a[q] & 0xffff0000u),
-                               __builtin_bit_cast(float, b[q] & 0xffff0000u), acc);
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x = a[q], y = b[q];
+        if constexpr (sizeof(T) == 2) {
+          acc = __builtin_fmaf(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, y << 16), acc);
+          acc = __builtin_fmaf(__builtin_bit_cast(float, x & 0xffff0000u), __builtin_bit_cast(float, y & 0xffff0000u),
+                               acc);
+        } else {
+          acc = __builtin_fmaf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y), acc);
         }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          acc = __builtin_fmaf(__builtin_bit_cast(float, a[q]), __builtin_bit_cast(float, b[q]), acc);
       }
     }
     zy = wave_sum(acc);

@@ -30,7 +30,7 @@ def rel_fro(a, b):
     return np.linalg.norm(a - b) / (den if den > 0 else 1.0)
 
 
-def check_loss(got, want, reduction, label=""):
+def check_loss(got, want, reduction, label="", n_valid=1):
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     if reduction == "none":
@@ -38,8 +38,11 @@ def check_loss(got, want, reduction, label=""):
         assert rel_fro(got, want) <= LOSS_RTOL, (label, rel_fro(got, want))
         assert np.max(np.abs(got - want)) <= LSE_ATOL, (label, np.max(np.abs(got - want)))
     else:
+        # relative bound; for a loss near zero (e.g. V = 1) the per-row LSE
+        # bound applies instead (summed over the rows a 'sum' adds up)
         err = abs(float(got) - float(want))
-        assert err <= LOSS_RTOL * max(abs(float(want)), 1e-30) or err <= 1e-6, (label, float(got), float(want))
+        rows = max(n_valid, 1) if reduction == "sum" else 1
+        assert err <= LOSS_RTOL * abs(float(want)) or err <= LSE_ATOL * rows, (label, float(got), float(want))
 
 
 def check_lse(got, want, label=""):
