@@ -239,6 +239,14 @@ struct Loader<C, ROWS, true> {
 // `nsteps` K steps of BK each; step s covers K offset kofs(s).  With
 // `blocks` == nullptr the steps are contiguous from 0; otherwise step s lies in
 // K block blocks[s / SPB] (of SPB*BK elements) at sub-step s % SPB.
+//
+// Pipeline: two register sets alternate as global prefetch buffers, so the
+// loads of step s+3 are issued in the middle of step s, right after the data
+// of step s+1 has been written to the idle LDS stage: every load has about
+// two steps of MFMA work to land.  Within a step the MFMAs of K group g run
+// while the fragments of group g+1 are read from LDS.  One barrier per step.
+// Steps past the end (the count is padded to even) address K = kdim and read
+// zeros, so the loop body has no branches.
 template <class C, bool A_MN, bool B_MN, int SPB>
 __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Operand& A,
                                          const Operand& B, int nsteps, const uint16_t* blocks,
@@ -250,53 +258,87 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Oper
   // stage st: A tile at st*STAGE_ELEMS, B tile right after it
   const lds_ptr<T> base = to_lds(smem);
   constexpr int BOFF = C::BM * C::LDK;
+  constexpr int KG = C::KGROUPS;
+  if (nsteps <= 0) return;
+  const int kend = A.kdim > B.kdim ? A.kdim : B.kdim;
 
   auto kofs = [&](int s) -> int {
-    return blocks ? blocks[s / SPB] * (SPB * C::BK) + (s % SPB) * C::BK : s * C::BK;
+    if (s >= nsteps) return kend;
+    return blocks ? (int)blocks[s / SPB] * (SPB * C::BK) + (s % SPB) * C::BK : s * C::BK;
   };
 
-  Loader<C, C::BM, A_MN> la;
-  Loader<C, C::BN, B_MN> lb;
-  if (nsteps <= 0) return;
-  la.load(A, kofs(0), tid);
-  lb.load(B, kofs(0), tid);
-  la.store(base, tid);
-  lb.store(base + BOFF, tid);
+  Loader<C, C::BM, A_MN> la0, la1;
+  Loader<C, C::BN, B_MN> lb0, lb1;
+  la0.load(A, kofs(0), tid);
+  lb0.load(B, kofs(0), tid);
+  la1.load(A, kofs(1), tid);
+  lb1.load(B, kofs(1), tid);
+  la0.store(base, tid);
+  lb0.store(base + BOFF, tid);
+  la0.load(A, kofs(2), tid);
+  lb0.load(B, kofs(2), tid);
   __syncthreads();
 
   // Fragment read offsets within a stage.
   const int frow = lane & 31;
   const int fk = (lane >> 5) * 8;
   const int a_base = (wm * C::WM + frow) * C::LDK + fk;
-  const int b_base = (wn * C::WN + frow) * C::LDK + fk;
+  const int b_base = BOFF + (wn * C::WN + frow) * C::LDK + fk;
 
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      int k1 = kofs(s + 1);
-      la.load(A, k1, tid);
-      lb.load(B, k1, tid);
-    }
-    const lds_ptr<T> as = base + cur * C::STAGE_ELEMS;
-    const lds_ptr<T> bs = as + BOFF;
+  Frag<T> fa[2][C::FM], fb[2][C::FN];
+  // MFMA instructions per K group and LDS reads per fragment for the issue
+  // pattern below
+  constexpr int MMAS = C::FM * C::FN * (sizeof(T) == 2 ? 1 : 8);
+  constexpr int LDS_READS_PER_FRAG = sizeof(T) == 2 ? 1 : 2;
+  constexpr int MMA_PER_FRAG = 1;
+  constexpr int MMA_REST = MMAS - (C::FM + C::FN) * MMA_PER_FRAG;
+  auto read_frags = [&](int buf, lds_ptr<T> st, int g) {
 #pragma unroll
-    for (int g = 0; g < C::KGROUPS; ++g) {
-      Frag<T> fa[C::FM], fb[C::FN];
+    for (int i = 0; i < C::FM; ++i) lds_frag(fa[buf][i], st + a_base + i * 32 * C::LDK + g * 16);
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) lds_frag(fa[i], as + a_base + i * 32 * C::LDK + g * 16);
+    for (int j = 0; j < C::FN; ++j) lds_frag(fb[buf][j], st + b_base + j * 32 * C::LDK + g * 16);
+  };
+  read_frags(0, base, 0);
+
+  // One step computing from stage `st`; mid-step the prefetch set (lsa, lsb),
+  // holding step s+1, goes to stage `nx` and is reloaded with step s+3.
+  auto step = [&](int s, lds_ptr<T> st, lds_ptr<T> nx, auto& lsa, auto& lsb) {
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) lds_frag(fb[j], bs + b_base + j * 32 * C::LDK + g * 16);
+    for (int g = 0; g < KG; ++g) {
+      if (g + 1 < KG) read_frags((g + 1) & 1, st, g + 1);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) mma16(acc[i][j], fa[i], fb[j]);
-    }
-    if (more) {
-      la.store(base + (cur ^ 1) * C::STAGE_ELEMS, tid);
-      lb.store(base + (cur ^ 1) * C::STAGE_ELEMS + BOFF, tid);
+        for (int j = 0; j < C::FN; ++j) mma16(acc[i][j], fa[g & 1][i], fb[g & 1][j]);
+      if (g + 1 < KG) {
+        // issue order: the next group's LDS reads alternate with this group's
+        // first MFMAs, so they land long before they are needed
+#pragma unroll
+        for (int r = 0; r < C::FM + C::FN; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, MMA_PER_FRAG, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, LDS_READS_PER_FRAG, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MMA_REST, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (g == (KG >= 2 ? KG - 2 : 0)) {
+        __builtin_amdgcn_sched_barrier(0);
+        lsa.store(nx, tid);
+        lsb.store(nx + BOFF, tid);
+        const int k3 = kofs(s + 3);
+        lsa.load(A, k3, tid);
+        lsb.load(B, k3, tid);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __syncthreads();
+    read_frags(0, nx, 0);
+  };
+
+  const lds_ptr<T> st0 = base, st1 = base + C::STAGE_ELEMS;
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, st0, st1, la1, lb1);       // set 1 holds step s+1
+    step(s + 1, st1, st0, la0, lb0);   // set 0 holds step s+2
   }
 }
 

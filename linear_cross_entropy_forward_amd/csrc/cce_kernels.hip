@@ -27,6 +27,10 @@
 namespace cce {
 
 constexpr float kLog2e = 1.4426950408889634f;
+#ifndef CCE_RASTER_GROUP
+#define CCE_RASTER_GROUP 8
+#endif
+constexpr int kRasterGroup = CCE_RASTER_GROUP;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -50,6 +54,20 @@ __device__ __forceinline__ int xcd_remap(int i, int total) {
   const int q = total >> 3, r = total & 7;
   const int x = i & 7, j = i >> 3;
   return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
+// Grouped ordering of an (tiles_m x tiles_n) tile grid: runs of `group`
+// consecutive M tiles are visited for every N tile before the next run, so
+// the ~32 work-groups an XCD holds at once cover about group x (32/group)
+// tiles and re-use group A blocks and 32/group B blocks from its L2.
+__device__ __forceinline__ void grouped_tile(int idx, int tiles_m, int tiles_n, int group, int& tm, int& tn) {
+  const int per = group * tiles_n;
+  const int g = idx / per;
+  const int first = g * group;
+  const int gm = min(tiles_m - first, group);
+  const int r = idx - g * per;
+  tm = first + r % gm;
+  tn = r / gm;
 }
 
 template <typename T> __device__ __forceinline__ float to_f(T v);
@@ -87,8 +105,8 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
                                                             int nVB, int tiles_n, int total) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int tv = tile / tiles_n, tn = tile % tiles_n;
+  int tv, tn;
+  grouped_tile(xcd_remap(blockIdx.x, total), total / tiles_n, tiles_n, kRasterGroup, tv, tn);
   const int v0 = tv * C::BM, n0 = tn * C::BN;
 
   Operand A{make_rsrc(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T)), (uint32_t)D,
@@ -338,8 +356,8 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   using T = typename C::T;
   __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
   const int total = tiles_v * tiles_n;
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int tvl = tile / tiles_n, tn = tile % tiles_n;
+  int tvl, tn;
+  grouped_tile(xcd_remap(blockIdx.x, total), tiles_v, tiles_n, kRasterGroup, tvl, tn);
   const int tv = cvb0 + tvl;
   if (!keep[(size_t)tn * nvb_t + tv]) return;
   const int v0 = tv * C::BM, n0 = tn * C::BN;
@@ -418,8 +436,8 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
   __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
   __shared__ uint16_t blocks[kMaxBlocks];
   const int total = tiles_v * tiles_d;
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int tvl = tile / tiles_d, td = tile % tiles_d;
+  int tvl, td;
+  grouped_tile(xcd_remap(blockIdx.x, total), tiles_v, tiles_d, kRasterGroup, tvl, td);
   const int vl0 = tvl * C::BM, d0 = td * C::BN;
   const int nb = Npad / kTileN;
   const int nk = collect_blocks(keep, (size_t)(cvb0 + tvl), nvb_t, nb, blocks);
@@ -469,8 +487,8 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   const int total = tiles_n * tiles_d * splits;
   const int tile = xcd_remap(blockIdx.x, total);
   const int s = tile / (tiles_n * tiles_d);
-  const int rem = tile % (tiles_n * tiles_d);
-  const int tn = rem / tiles_d, td = rem % tiles_d;
+  int tn, td;
+  grouped_tile(tile % (tiles_n * tiles_d), tiles_n, tiles_d, kRasterGroup, tn, td);
   const int n0 = tn * C::BM, d0 = td * C::BN;
   // this split's vocab blocks of the chunk
   const int vb_lo = (int)((int64_t)cnvb * s / splits), vb_hi = (int)((int64_t)cnvb * (s + 1) / splits);
