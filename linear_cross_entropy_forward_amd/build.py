@@ -27,7 +27,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into libcce.so; returns its path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-O3", f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-shared",
+    cmd = [hipcc(), "-O3", f"--offload-arch={ARCH}", "-std=c++20", "-fPIC", "-shared",
            # keep the compiler from forming packed fp32 ALU ops (v_pk_*_f32)
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wno-unused-command-line-argument",

@@ -21,6 +21,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace cce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -196,6 +199,29 @@ struct Loader<C, ROWS, false> {
       lds_st128(lds + row * C::LDK + kc, reg[i]);
     }
   }
+  // Part P of NP: chunks [P*N/NP, (P+1)*N/NP) only.
+  static constexpr int part_lo(int P, int NP) { return P * N / NP; }
+  template <int P, int NP>
+  __device__ __forceinline__ void store_part(lds_ptr<T> lds, int tid) const {
+#pragma unroll
+    for (int i = part_lo(P, NP); i < part_lo(P + 1, NP); ++i) {
+      int c = tid + i * C::NT;
+      int row = c / CPR, kc = (c % CPR) * C::VEC;
+      lds_st128(lds + row * C::LDK + kc, reg[i]);
+    }
+  }
+  template <int P, int NP>
+  __device__ __forceinline__ void load_part(const Operand& op, int k0, int tid) {
+#pragma unroll
+    for (int i = part_lo(P, NP); i < part_lo(P + 1, NP); ++i) {
+      int c = tid + i * C::NT;
+      int row = c / CPR, kc = (c % CPR) * C::VEC + k0;
+      bool ok = row < op.rows && kc < op.kdim;
+      uint32_t off = ok ? ((uint32_t)row * op.ld + (uint32_t)kc) * (uint32_t)sizeof(T) : kOOB;
+      reg[i] = ld128(op.r, off);
+    }
+  }
+  template <int NP> static constexpr int stores_in_part(int P) { return part_lo(P + 1, NP) - part_lo(P, NP); }
 };
 
 // MN-major: VECxVEC blocks, transposed in registers.
@@ -233,7 +259,66 @@ struct Loader<C, ROWS, true> {
       for (int j = 0; j < V; ++j) lds_st128(lds + (mb * V + j) * C::LDK + kb * V, reg[i][j]);
     }
   }
+  // Part P of NP: part 0 transposes every block; part P stores columns
+  // [P*V/NP, (P+1)*V/NP) of each block, and load_part reloads the same rows
+  // (their registers are free once those columns are stored).
+  static constexpr int part_lo(int P, int NP) { return P * V / NP; }
+  template <int P, int NP>
+  __device__ __forceinline__ void store_part(lds_ptr<T> lds, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int u = tid + i * C::NT;
+      int kb = u % KB, mb = u / KB;
+      if (P == 0) transpose_block(reg[i], (const T*)nullptr);
+#pragma unroll
+      for (int j = part_lo(P, NP); j < part_lo(P + 1, NP); ++j)
+        lds_st128(lds + (mb * V + j) * C::LDK + kb * V, reg[i][j]);
+    }
+  }
+  template <int P, int NP>
+  __device__ __forceinline__ void load_part(const Operand& op, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      int u = tid + i * C::NT;
+      int kb = u % KB, mb = u / KB;
+      int col = mb * V;
+#pragma unroll
+      for (int j = part_lo(P, NP); j < part_lo(P + 1, NP); ++j) {
+        int k = k0 + kb * V + j;
+        bool ok = k < op.kdim && col < op.rows;
+        uint32_t off = ok ? ((uint32_t)k * op.ld + (uint32_t)col) * (uint32_t)sizeof(T) : kOOB;
+        reg[i][j] = ld128(op.r, off);
+      }
+    }
+  }
+  template <int NP> static constexpr int stores_in_part(int P) { return N * (part_lo(P + 1, NP) - part_lo(P, NP)); }
 };
+
+// Scheduling pattern for one K group: MM MFMAs, each followed by up to PER of
+// the group's other instructions in the order NR LDS reads, NW LDS writes,
+// NL global loads (sched_group_barrier masks 0x008 MFMA, 0x100 DS read,
+// 0x200 DS write, 0x020 VMEM read).
+template <int T, int NR, int NW, int NL>
+__device__ __forceinline__ void pattern_extra() {
+  if constexpr (T < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  else if constexpr (T < NR + NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+  else if constexpr (T < NR + NW + NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+}
+template <int M, int PER, int NR, int NW, int NL>
+__device__ __forceinline__ void pattern_slot() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  [&]<int... Q>(std::integer_sequence<int, Q...>) {
+    (pattern_extra<M * PER + Q, NR, NW, NL>(), ...);
+  }(std::make_integer_sequence<int, PER>{});
+}
+template <int MM, int NR, int NW, int NL>
+__device__ __forceinline__ void issue_pattern() {
+  constexpr int extra = NR + NW + NL;
+  constexpr int per = (extra + MM - 1) / MM;
+  [&]<int... M>(std::integer_sequence<int, M...>) {
+    (pattern_slot<M, per, NR, NW, NL>(), ...);
+  }(std::make_integer_sequence<int, MM>{});
+}
 
 // Main loop: acc[fm][fn] += sum over the listed K steps of A_tile * B_tile^T.
 // `nsteps` K steps of BK each; step s covers K offset kofs(s).  With
@@ -290,8 +375,6 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Oper
   // pattern below
   constexpr int MMAS = C::FM * C::FN * (sizeof(T) == 2 ? 1 : 8);
   constexpr int LDS_READS_PER_FRAG = sizeof(T) == 2 ? 1 : 2;
-  constexpr int MMA_PER_FRAG = 1;
-  constexpr int MMA_REST = MMAS - (C::FM + C::FN) * MMA_PER_FRAG;
   auto read_frags = [&](int buf, lds_ptr<T> st, int g) {
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) lds_frag(fa[buf][i], st + a_base + i * 32 * C::LDK + g * 16);
@@ -300,37 +383,40 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Oper
   };
   read_frags(0, base, 0);
 
-  // One step computing from stage `st`; mid-step the prefetch set (lsa, lsb),
-  // holding step s+1, goes to stage `nx` and is reloaded with step s+3.
+  // One step computing from stage `st`.  The prefetch set (lsa, lsb) holds
+  // step s+1; during the first KG-1 groups it is written to stage `nx` part by
+  // part, and each part's registers are reloaded with step s+3 right after.
+  // The stores and loads are spread between the MFMAs instead of issued in one
+  // burst: a burst fills the LDS write queue and stalls the only wave on the
+  // SIMD, idling the matrix core.
+  constexpr int NP = KG > 1 ? KG - 1 : 1;
   auto step = [&](int s, lds_ptr<T> st, lds_ptr<T> nx, auto& lsa, auto& lsb) {
-#pragma unroll
-    for (int g = 0; g < KG; ++g) {
-      if (g + 1 < KG) read_frags((g + 1) & 1, st, g + 1);
+    const int k3 = kofs(s + 3);
+    auto group = [&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g + 1 < KG) read_frags((g + 1) & 1, st, g + 1);
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) mma16(acc[i][j], fa[g & 1][i], fb[g & 1][j]);
-      if (g + 1 < KG) {
-        // issue order: the next group's LDS reads alternate with this group's
-        // first MFMAs, so they land long before they are needed
-#pragma unroll
-        for (int r = 0; r < C::FM + C::FN; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, MMA_PER_FRAG, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, LDS_READS_PER_FRAG, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, MMA_REST, 0);
-        __builtin_amdgcn_sched_barrier(0);
+      if constexpr (g < NP) {
+        lsa.template store_part<g, NP>(nx, tid);
+        lsb.template store_part<g, NP>(nx + BOFF, tid);
+        lsa.template load_part<g, NP>(A, k3, tid);
+        lsb.template load_part<g, NP>(B, k3, tid);
       }
-      if (g == (KG >= 2 ? KG - 2 : 0)) {
-        __builtin_amdgcn_sched_barrier(0);
-        lsa.store(nx, tid);
-        lsb.store(nx + BOFF, tid);
-        const int k3 = kofs(s + 3);
-        lsa.load(A, k3, tid);
-        lsb.load(B, k3, tid);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+      // issue order within the group: MFMAs interleaved with the next group's
+      // fragment reads, then with this part's LDS stores and global loads
+      constexpr int nr = g + 1 < KG ? (C::FM + C::FN) * LDS_READS_PER_FRAG : 0;
+      constexpr int nw = g < NP ? std::remove_reference_t<decltype(lsa)>::template stores_in_part<NP>(g) +
+                                      std::remove_reference_t<decltype(lsb)>::template stores_in_part<NP>(g)
+                                : 0;
+      issue_pattern<MMAS, nr, nw, nw>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    [&]<int... G>(std::integer_sequence<int, G...>) {
+      (group(std::integral_constant<int, G>{}), ...);
+    }(std::make_integer_sequence<int, KG>{});
     __syncthreads();
     read_frags(0, nx, 0);
   };
