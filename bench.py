@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 KERNELS = ["fwd_tile", "rows", "reduce", "bwd_prep", "filter", "grad_tile", "dC_gemm", "dE_gemm", "dE_reduce",
-           "fill_zero"]
+           "fill_zero", "transpose_e"]
 MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # Measured HBM traffic per launch of the dominant kernel (rocprofv3 FETCH_SIZE
 # + WRITE_SIZE, scaled by a plain-copy calibration).  Set only when the
@@ -71,6 +71,8 @@ def algorithmic(name, N, D, V, es, nVB, chunk_lens):
         return 0.0, N * nVB * 8.0 + N * 12.0
     if name == "dE_reduce":
         return 0.0, 0.0
+    if name == "transpose_e":
+        return 0.0, 2.0 * N * D * es
     return 0.0, 0.0
 
 
@@ -190,7 +192,7 @@ def main():
     Vc = args.vocab_chunk
     if Vc == 0:
         Npad = -(-N // 256) * 256
-        Vc = max(256, (256 << 20) // (Npad * es) // 256 * 256)
+        Vc = max(256, (512 << 20) // (2 * Npad * es) // 256 * 256)
         Vc = min(Vc, -(-V // 256) * 256)
     chunk_lens = [min(Vc, V - s) for s in range(0, V, Vc)]
     nVB = -(-V // 128)

@@ -79,7 +79,8 @@ typedef struct {
  * Bytes of device workspace needed by cce_forward and cce_backward for this
  * problem.  vocab_chunk = 0 picks the library default: the backward forms
  * gradient tiles for a vocabulary chunk at a time and keeps that chunk's
- * bf16/fp32 G block in the workspace (at most 256 MiB by default); a positive
+ * bf16/fp32 G block, in both orientations, in the workspace (256 MiB for the
+ * two by default), plus e transposed (N*D elements); a positive
  * value (a multiple of 256) sets the chunk width, trading workspace for
  * launches.  The forward uses only the first part (per-row partials,
  * O(N + N*V/128) floats).  Returns 0 for invalid arguments.
@@ -141,8 +142,9 @@ void cce_tile_shape(int* filter_rows, int* filter_vocab, int* partial_vocab);
  * cce_profile_stop waits for those events and returns the summed elapsed time
  * (host double, ms) and the number of launches timed (host int).  The hook
  * holds process-wide state: it is meant for benchmarks and is not
- * thread-safe.  Kernel ids 0..9 are fwd_tile, rows, reduce, bwd_prep, filter,
- * grad_tile, dC_gemm, dE_gemm, dE_reduce, fill_zero (cce_kernel_name).
+ * thread-safe.  Kernel ids 0..10 are fwd_tile, rows, reduce, bwd_prep, filter,
+ * grad_tile, dC_gemm, dE_gemm, dE_reduce, fill_zero, transpose_e
+ * (cce_kernel_name).
  */
 cce_status cce_profile_start(int kernel_id, int max_launches);
 cce_status cce_profile_stop(int kernel_id, double* total_ms, int* launches);

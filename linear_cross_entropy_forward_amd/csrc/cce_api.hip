@@ -25,7 +25,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   if (vocab_chunk > 0) {
     vc = vocab_chunk;
   } else {
-    vc = (int64_t)(kDefaultGBudget / ((size_t)L.Npad * es)) / kTileV * kTileV;
+    vc = (int64_t)(kDefaultGBudget / (2 * (size_t)L.Npad * es)) / kTileV * kTileV;
   }
   if (vc < kTileV) vc = kTileV;
   if (vc > vmax) vc = vmax;
@@ -59,6 +59,8 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const size_t o_scale = take((size_t)L.Npad * 4);
   const size_t o_keep = take((size_t)L.nb * L.nvb_t);
   const size_t o_g = take(L.g_bytes);
+  const size_t o_gt = take(L.g_bytes);
+  const size_t o_et = take((size_t)D * (size_t)L.Npad * es);
   const size_t o_dep = take((size_t)(L.splits - 1) * (size_t)N * (size_t)D * 4);
   L.total = off;
   if (base) {
@@ -69,6 +71,8 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     L.scale = (float*)(b + o_scale);
     L.keep = (uint8_t*)(b + o_keep);
     L.G = b + o_g;
+    L.Gt = b + o_gt;
+    L.Et = b + o_et;
     L.dE_part = (float*)(b + o_dep);
   }
   return L;
@@ -93,7 +97,7 @@ static cce_status check_common(const void* e, const void* c, const int64_t* targ
   // 32-bit buffer offsets: every operand a kernel addresses from one base
   // stays below 2 GiB; the contraction tiles list at most kMaxBlocks blocks.
   const int64_t lim = (int64_t)1 << 31;
-  if (N * D * es >= lim || N > (int64_t)kMaxBlocks * kTileN || V >= lim / 2 || D >= lim / 2)
+  if ((N + kTileN) * D * es >= lim || N > (int64_t)kMaxBlocks * kTileN || V >= lim / 2 || D >= lim / 2)
     return CCE_ERR_UNSUPPORTED;
   Layout L = make_layout(N, D, V, dtype, vocab_chunk, nullptr);
   if ((int64_t)L.Vc * D * es >= lim || (int64_t)L.g_bytes >= lim) return CCE_ERR_UNSUPPORTED;
@@ -132,7 +136,7 @@ static void prof_release(ProfSlot& p) {
 
 static const char* const kKernelNames[kNumKernels] = {
     "fwd_tile", "rows", "reduce", "bwd_prep", "filter", "grad_tile", "dC_gemm", "dE_gemm", "dE_reduce",
-    "fill_zero"};
+    "fill_zero", "transpose_e"};
 
 }  // namespace cce
 

@@ -32,8 +32,8 @@ constexpr int kHdrTilesKept = 2;
 constexpr int kHdrNValidBwd = 3;
 constexpr int kHdrWords = 64;  // 256 bytes
 
-// Default byte budget of the per-chunk gradient tile buffer G.
-constexpr size_t kDefaultGBudget = size_t(256) << 20;
+// Default byte budget of the per-chunk gradient tile buffers G and G^T together.
+constexpr size_t kDefaultGBudget = size_t(512) << 20;
 
 struct Problem {
   const void* e;
@@ -62,8 +62,10 @@ struct Layout {
   float* nll_out;   // [N] per-row loss (the caller's loss buffer for 'none')
   float* scale;     // [Npad]
   uint8_t* keep;    // [nb][nvb_t]
-  void* G;          // [Npad][Vc] operand type
-  size_t g_bytes;
+  void* G;          // [Npad][Vc] operand type: gradient tiles of one vocab chunk
+  void* Gt;         // [Vc][Npad] the same tiles transposed
+  void* Et;         // [D][Npad] e transposed (zero rows past N)
+  size_t g_bytes;   // bytes of G (and of Gt)
   float* dE_part;   // [splits-1][N][D]
   int nVB, Npad, nb, nvb_t, Vc, nchunks, splits, splits_atomic;
 };
@@ -75,7 +77,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
 // Kernel ids of the profiling hook (cce_profile_start / cce_profile_stop).
 enum KernelId {
   kKFwdTile = 0, kKRows, kKReduce, kKBwdPrep, kKFilter, kKGradTile, kKDC, kKDE, kKDEReduce, kKFill,
-  kNumKernels
+  kKTransE, kNumKernels
 };
 // Records start/stop events around one launch of kernel `id` when profiling of
 // that id is active (no-op otherwise).

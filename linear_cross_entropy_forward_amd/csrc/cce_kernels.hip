@@ -92,6 +92,32 @@ __device__ __forceinline__ void store4(rsrc_t r, uint32_t off, float a, float b,
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 
+// One value in the operand type.
+__device__ __forceinline__ void store1(rsrc_t r, uint32_t off, float a, const uint16_t*) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)a), r, off, 0, 0);
+}
+__device__ __forceinline__ void store1(rsrc_t r, uint32_t off, float a, const float*) { stf(r, off, a); }
+
+// ============================================================================
+// e^T [D][Npad] (rows past N zero) for the dC contraction, via 64x64 LDS tiles.
+// ============================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_e_kernel(const T* __restrict__ e, T* __restrict__ et, int N, int D,
+                                                          int Npad) {
+  __shared__ T tile[64][65];
+  const int d0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int n = n0 + r, d = d0 + tx;
+    tile[r][tx] = (n < N && d < D) ? e[(size_t)n * D + d] : (T)0;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int d = d0 + r, n = n0 + tx;
+    if (d < D && n < Npad) et[(size_t)d * Npad + n] = tile[tx][r];
+  }
+}
+
 // ============================================================================
 // Forward logit tile + per-block online LSE partials.
 // Output tile rows are vocabulary entries, columns are tokens, so each lane
@@ -352,7 +378,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     const typename C::T* __restrict__ c, const typename C::T* __restrict__ e,
     const int64_t* __restrict__ targets, const float* __restrict__ lse, const float* __restrict__ scale,
     const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int tiles_v,
-    int tiles_n, int Vc, typename C::T* __restrict__ G, size_t g_bytes) {
+    int tiles_n, int Vc, int Npad, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
   const int total = tiles_v * tiles_n;
@@ -375,6 +401,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
 
   AccMap<C> am;
   rsrc_t rg = make_rsrc(G, g_bytes);
+  rsrc_t rgt = make_rsrc(Gt, g_bytes);
   const int vl0 = tvl * C::BM;  // chunk-local column of the tile
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn) {
@@ -398,6 +425,12 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
         }
         const uint32_t off = ((uint32_t)n * (uint32_t)Vc + (uint32_t)(vl0 + rl)) * (uint32_t)sizeof(T);
         store4(rg, off, g[0], g[1], g[2], g[3], (const T*)nullptr);
+        // G^T[v][n]: for each of the four vocab rows, 32 lanes write 32
+        // consecutive tokens
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          store1(rgt, ((uint32_t)(vl0 + rl + u) * (uint32_t)Npad + (uint32_t)n) * (uint32_t)sizeof(T), g[u],
+                 (const T*)nullptr);
       }
     }
   }
@@ -424,14 +457,14 @@ __device__ __forceinline__ int collect_blocks(const uint8_t* __restrict__ keep, 
 }
 
 // ============================================================================
-// dC rows of one vocabulary chunk: dC[v][d] = sum_n G[n][v] E[n][d] over the
-// kept token blocks of the tile's vocab block.  Both operands are MN-major.
+// dC rows of one vocabulary chunk: dC[v][d] = sum_n G^T[v][n] E^T[d][n] over
+// the kept token blocks of the tile's vocab block (both operands K-major).
 // ============================================================================
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
-    const typename C::T* __restrict__ G, const typename C::T* __restrict__ e,
-    const uint8_t* __restrict__ keep, int N, int Npad, int D, int V, int nvb_t, int cvb0, int cv0,
-    int clen, int tiles_v, int tiles_d, int Vc, size_t g_bytes, float* __restrict__ dC) {
+    const typename C::T* __restrict__ Gt, const typename C::T* __restrict__ Et,
+    const uint8_t* __restrict__ keep, int Npad, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
+    int tiles_v, int tiles_d, size_t g_bytes, float* __restrict__ dC) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
   __shared__ uint16_t blocks[kMaxBlocks];
@@ -442,16 +475,17 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
   const int nb = Npad / kTileN;
   const int nk = collect_blocks(keep, (size_t)(cvb0 + tvl), nvb_t, nb, blocks);
 
-  Operand A{make_rsrc(G + vl0, g_bytes - (size_t)vl0 * sizeof(T)), (uint32_t)Vc, min(C::BM, clen - vl0),
-            Npad};
-  Operand B{make_rsrc(e + d0, ((uint64_t)N * D - d0) * sizeof(T)), (uint32_t)D, min(C::BN, D - d0), N};
+  Operand A{make_rsrc(Gt + (size_t)vl0 * Npad, g_bytes - (size_t)vl0 * Npad * sizeof(T)), (uint32_t)Npad,
+            min(C::BM, clen - vl0), Npad};
+  Operand B{make_rsrc(Et + (size_t)d0 * Npad, (uint64_t)(D - d0) * Npad * sizeof(T)), (uint32_t)Npad,
+            min(C::BN, D - d0), Npad};
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   constexpr int SPB = kTileN / C::BK;
-  mainloop<C, true, true, SPB>(acc, A, B, nk * SPB, blocks, smem);
+  mainloop<C, false, false, SPB>(acc, A, B, nk * SPB, blocks, smem);
 
   AccMap<C> am;
   const int vg0 = cv0 + vl0;
@@ -603,6 +637,10 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
                      L.part, P.N, P.V, L.nVB, P.ignore_index, kTileN, kTileV, kPartialWidth, L.nvb_t, P.filter,
                      L.keep, L.hdr);
   prof_after(kKFilter, st);
+  prof_before(kKTransE, st);
+  hipLaunchKernelGGL(transpose_e_kernel<T>, dim3((P.D + 63) / 64, L.Npad / 64), dim3(256), 0, st, e, (T*)L.Et, P.N,
+                     P.D, L.Npad);
+  prof_after(kKTransE, st);
   if (P.accum == kAccumAtomic) {
     const size_t n = (size_t)P.N * P.D;
     prof_before(kKFill, st);
@@ -618,11 +656,13 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     const int cvb0 = cv0 / kTileV;
     prof_before(kKGradTile, st);
     hipLaunchKernelGGL(grad_tile_kernel<C>, dim3(cnvb * tiles_n), dim3(C::NT), 0, st, c, e, P.targets, P.lse,
-                       L.scale, L.keep, P.N, P.D, P.V, L.nvb_t, cvb0, cnvb, tiles_n, L.Vc, G, L.g_bytes);
+                       L.scale, L.keep, P.N, P.D, P.V, L.nvb_t, cvb0, cnvb, tiles_n, L.Vc, L.Npad, G, (T*)L.Gt,
+                       L.g_bytes);
     prof_after(kKGradTile, st);
     prof_before(kKDC, st);
-    hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(cnvb * tiles_d), dim3(C::NT), 0, st, G, e, L.keep, P.N, L.Npad,
-                       P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_d, L.Vc, L.g_bytes, P.dC);
+    hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(cnvb * tiles_d), dim3(C::NT), 0, st, (const T*)L.Gt,
+                       (const T*)L.Et, L.keep, L.Npad, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_d, L.g_bytes,
+                       P.dC);
     prof_after(kKDC, st);
     const int splits = P.accum == kAccumAtomic ? L.splits_atomic : L.splits;
     prof_before(kKDE, st);

@@ -39,9 +39,9 @@ def test_status_strings_and_tiles(L):
     import linear_cross_entropy_forward_amd as M
     bn, bv, pw = M.tile_shape()
     assert bn == 256 and bv == 256 and pw == 128 and bv % pw == 0
-    for k in range(10):
+    for k in range(11):
         assert L.cce_kernel_name(k) != b"unknown"
-    assert L.cce_kernel_name(10) == b"unknown"
+    assert L.cce_kernel_name(11) == b"unknown"
 
 
 def test_workspace_size(L):
@@ -106,7 +106,7 @@ def test_stats_and_profile_argument_errors(L):
     assert L.cce_read_stats(None, 1024, 1, 1, None, ctypes.byref(st)) == INVALID
     assert L.cce_read_stats(FAKE, 8, 1, 1, None, ctypes.byref(st)) == INVALID
     assert L.cce_profile_start(-1, 4) == INVALID
-    assert L.cce_profile_start(10, 4) == INVALID
+    assert L.cce_profile_start(11, 4) == INVALID
     assert L.cce_profile_start(0, 0) == INVALID
     ms, n = ctypes.c_double(), ctypes.c_int()
     assert L.cce_profile_stop(11, ctypes.byref(ms), ctypes.byref(n)) == INVALID
