@@ -51,6 +51,10 @@ def parse():
     ap.add_argument("--vocab-chunk", type=int, default=0)
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-materialized", action="store_true",
+                    help="skip the materialised-logits PyTorch comparison")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="run one plain device copy of BYTES first (HBM-counter calibration under rocprofv3)")
     return ap.parse_args()
 
 
@@ -95,6 +99,42 @@ def cpu_baseline(inp, rows_n):
                       f"against the full classifier (V={c.shape[0]}, D={c.shape[1]}); {dt:.1f} s"}
 
 
+def materialized(e, c, t, reduction, steps):
+    """The conventional head that cut cross-entropy replaces (mlx-cross-entropy,
+    "The problem"): the full logit matrix e @ c^T is materialised (here in fp32),
+    then cross-entropy (mean) and its backward.  Returns ms per forward+backward
+    step and the peak device memory it needs beyond its inputs."""
+    import torch
+    import torch.nn.functional as F
+    ec = e.detach().clone().requires_grad_(True)
+    cc = c.detach().clone().requires_grad_(True)
+
+    def run():
+        logits = (ec @ cc.t()).float()
+        loss = F.cross_entropy(logits, t, ignore_index=-100, reduction="mean")
+        loss.backward()
+        ec.grad = None
+        cc.grad = None
+
+    run()
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    run()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(steps):
+        run()
+    s1.record()
+    torch.cuda.synchronize()
+    del ec, cc
+    torch.cuda.empty_cache()
+    return s0.elapsed_time(s1) / steps, peak
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -119,6 +159,15 @@ def main():
     n_valid = int((inp["targets"] != -100).sum())
     L = M.lib()
 
+    if args.copy_calibration:
+        src = torch.empty(args.copy_calibration // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+
+    base_alloc = torch.cuda.memory_allocated()
     ws = torch.empty(M.workspace_size(N, D, V, tdt, args.vocab_chunk), dtype=torch.uint8, device=dev)
     red = {"none": 0, "sum": 1, "mean": 2}[reduction]
     loss = torch.empty(N if red == 0 else 1, dtype=torch.float32, device=dev)
@@ -188,7 +237,6 @@ def main():
     tflops = eff_flops / (ms_step * 1e-3) / 1e12
 
     # chunk lengths of the backward, for per-launch algorithmic work
-    vc_default = ws.numel()  # placeholder, replaced below
     Vc = args.vocab_chunk
     if Vc == 0:
         Npad = -(-N // 256) * 256
@@ -216,9 +264,20 @@ def main():
                 "traffic": TRAFFIC_BYTES.get(dom), "kernel": dom, "avg_launch_ms": per[dom]["avg_ms"],
                 "algorithmic_bytes_per_launch": by}
 
+    # device memory this path needs beyond its inputs: workspace, loss/LSE and
+    # the two gradient outputs
+    extra_bytes = torch.cuda.memory_allocated() - base_alloc
+    mat = None
+    if not args.no_materialized:
+        del dE, dC
+        torch.cuda.empty_cache()
+        mat_ms, mat_peak = materialized(e, c, t, reduction, max(1, min(args.steps, 3)))
+        mat = {"ms_per_step": mat_ms, "tokens_per_s": N / (mat_ms * 1e-3), "peak_extra_bytes": int(mat_peak),
+               "what": "PyTorch: fp32 logits = e @ c^T, F.cross_entropy(mean), backward"}
+
     cpu = None
     if not args.no_cpu_baseline:
-        rows_n = args.cpu_rows or (64 if dt_name == "bf16" else N)
+        rows_n = args.cpu_rows or (640 if dt_name == "bf16" else N)
         cpu = cpu_baseline(inp, min(rows_n, N))
 
     out = {
@@ -242,7 +301,10 @@ def main():
         "fwd_tokens_per_s": N / (fwd_ms * 1e-3),
         "tiles_kept_frac": stats["tiles_kept"] / max(1, stats["tiles_total"]),
         "workspace_bytes": ws.numel(),
+        "extra_hbm_bytes": int(extra_bytes),
+        "loss_path_overhead_bytes": int(N * nVB * 8 + N * 8),
         "materialized_logits_fp32_bytes": N * V * 4,
+        "materialized_baseline": mat,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

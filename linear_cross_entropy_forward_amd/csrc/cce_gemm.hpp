@@ -329,7 +329,11 @@ __device__ __forceinline__ void issue_pattern() {
 // loads of step s+3 are issued in the middle of step s, right after the data
 // of step s+1 has been written to the idle LDS stage: every load has about
 // two steps of MFMA work to land.  Within a step the MFMAs of K group g run
-// while the fragments of group g+1 are read from LDS.  One barrier per step.
+// while the fragments of group g+1 are read from LDS.  One barrier per step,
+// placed before the last K group: by then every wave has issued its last
+// fragment reads of the current stage and its stores to the next one, so the
+// last group's MFMAs cover the reads of the next step's first fragments and
+// no step starts on an LDS round trip.
 // Steps past the end (the count is padded to even) address K = kdim and read
 // zeros, so the loop body has no branches.
 template <class C, bool A_MN, bool B_MN, int SPB>
@@ -344,6 +348,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Oper
   const lds_ptr<T> base = to_lds(smem);
   constexpr int BOFF = C::BM * C::LDK;
   constexpr int KG = C::KGROUPS;
+  static_assert(KG % 2 == 0, "fragment buffers alternate per K group");
   if (nsteps <= 0) return;
   const int kend = A.kdim > B.kdim ? A.kdim : B.kdim;
 
@@ -394,7 +399,12 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Oper
     const int k3 = kofs(s + 3);
     auto group = [&](auto gc) {
       constexpr int g = decltype(gc)::value;
-      if constexpr (g + 1 < KG) read_frags((g + 1) & 1, st, g + 1);
+      if constexpr (g + 1 < KG) {
+        read_frags((g + 1) & 1, st, g + 1);
+      } else {
+        __syncthreads();
+        read_frags(0, nx, 0);
+      }
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -407,7 +417,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Oper
       }
       // issue order within the group: MFMAs interleaved with the next group's
       // fragment reads, then with this part's LDS stores and global loads
-      constexpr int nr = g + 1 < KG ? (C::FM + C::FN) * LDS_READS_PER_FRAG : 0;
+      constexpr int nr = (C::FM + C::FN) * LDS_READS_PER_FRAG;
       constexpr int nw = g < NP ? std::remove_reference_t<decltype(lsa)>::template stores_in_part<NP>(g) +
                                       std::remove_reference_t<decltype(lsb)>::template stores_in_part<NP>(g)
                                 : 0;
@@ -417,8 +427,6 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Oper
     [&]<int... G>(std::integer_sequence<int, G...>) {
       (group(std::integral_constant<int, G>{}), ...);
     }(std::make_integer_sequence<int, KG>{});
-    __syncthreads();
-    read_frags(0, nx, 0);
   };
 
   const lds_ptr<T> st0 = base, st1 = base + C::STAGE_ELEMS;
@@ -426,6 +434,7 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Oper
     step(s, st0, st1, la1, lb1);       // set 1 holds step s+1
     step(s + 1, st1, st0, la0, lb0);   // set 0 holds step s+2
   }
+  __syncthreads();  // the last group's reads are done before the caller may reuse LDS
 }
 
 // Output coordinates of accumulator element r of block (fm, fn) for this lane,
