@@ -155,6 +155,8 @@ struct Cfg {
   static constexpr int KGROUPS = BK / 16;
   static constexpr int STAGE_ELEMS = (BM + BN) * LDK;
   static constexpr int LDS_BYTES = 2 * STAGE_ELEMS * (int)sizeof(T);
+  // two stages of unpadded (swizzled) rows for the LDS-DMA main loop
+  static constexpr int LDS_DMA_BYTES = 2 * (BM + BN) * BK * (int)sizeof(T);
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be a multiple of 32");
 };
 
@@ -168,7 +170,15 @@ struct Operand {
   uint32_t ld;    // elements
   int rows;       // valid rows (K-major) or valid columns (MN-major) in the tile
   int kdim;       // valid K extent (relative to the same origin)
+  u32x4 desc;     // the descriptor of `r` as four words, for the LDS-DMA loads
 };
+
+__device__ __forceinline__ Operand make_operand(const void* base, uint64_t bytes, uint32_t ld, int rows, int kdim) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t n = bytes > 0x7fffffffull ? 0x7fffffffu : (uint32_t)bytes;
+  return Operand{make_rsrc(base, bytes), ld, rows, kdim,
+                 u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, n, (uint32_t)kRsrcWord3}};
+}
 
 template <class C, int ROWS, bool MN>
 struct Loader;
@@ -435,6 +445,224 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Oper
     step(s + 1, st1, st0, la0, lb0);   // set 0 holds step s+2
   }
   __syncthreads();  // the last group's reads are done before the caller may reuse LDS
+}
+
+// ============================================================================
+// LDS-DMA main loop for two K-major operands.
+//
+// gfx950 can write a buffer load straight into LDS (16 bytes per lane, lane l
+// landing at M0 + 16 l).  Feeding both tiles this way removes the LDS stores
+// and their staging registers from the waves: with one wave per SIMD every
+// ds_write_b128 issued between MFMAs costs the matrix core about two dozen
+// cycles, while a buffer load costs next to nothing.
+//
+// Tile layout: BK elements = 128 bytes per row, no padding.  The 16-byte chunk
+// c of row r is stored in slot c ^ (r % 8), so the eight rows that one
+// fragment read serves per LDS cycle (same chunk, consecutive rows) hit eight
+// different slots: the reads stay bank-conflict free without a pad, which a
+// contiguous 1 KB DMA write could not produce.  One DMA instruction fills 8
+// rows; lane l writes slot l % 8 of row l / 8 and therefore fetches logical
+// chunk (l % 8) ^ (l / 8) of that row.
+// ============================================================================
+
+// One 16-byte-per-lane buffer load into LDS at lds_addr + 16 * lane.  Written
+// as assembly: the instruction returns nothing to registers, and the
+// compiler's own wait insertion, which cannot tell the LDS stages apart, would
+// otherwise drain every DMA before each fragment read.  The main loop waits
+// for these loads itself (wait_vmcnt) before the barrier that publishes them.
+__device__ __forceinline__ void dma16(const u32x4& desc, uint32_t voff, uint32_t lds_addr) {
+  // one wait state between the M0 write and the LDS-DMA instruction reading it
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(desc)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+template <class C, int ROWS>
+struct DmaTile {
+  using T = typename C::T;
+  static constexpr int ROWB = C::BK * (int)sizeof(T);
+  static_assert(ROWB == 128, "DMA-fed rows are 128 bytes");
+  static constexpr int BYTES = ROWS * ROWB;
+  static constexpr int NW = C::NT / 64;
+  static constexpr int PER = BYTES / 1024 / NW;  // DMA instructions per wave per step
+  static_assert(BYTES % (1024 * NW) == 0, "tile not evenly split");
+  uint32_t roff[PER];  // byte offset of the lane's row, kOOB past the valid rows
+  uint32_t kc;         // K offset (elements) of the lane's chunk within a step
+  __device__ __forceinline__ void init(const Operand& op) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    kc = (uint32_t)(((lane & 7) ^ (lane >> 3)) * C::VEC);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int row = 8 * (wave * PER + i) + (lane >> 3);
+      roff[i] = row < op.rows ? (uint32_t)row * op.ld * (uint32_t)sizeof(T) : kOOB;
+    }
+  }
+  // DMA instruction i of this wave for the step at K offset k0 into the tile
+  // whose LDS byte address is `tile` (wave-uniform).
+  __device__ __forceinline__ void issue(int i, const Operand& op, int k0, uint32_t tile) const {
+    const uint32_t kk = (uint32_t)k0 + kc;
+    const uint32_t off = (roff[i] == kOOB || kk >= (uint32_t)op.kdim) ? kOOB : roff[i] + kk * (uint32_t)sizeof(T);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    dma16(op.desc, off, tile + (uint32_t)((wave * PER + i) * 1024));
+  }
+  // Byte offset in the tile of this lane's first fragment chunk at K group g
+  // for the 32-row block starting at row0 (a multiple of 8); fp32 fragments
+  // take a second chunk at `hi`.  Further 32-row blocks add 32 * ROWB.
+  __device__ static __forceinline__ void frag_off(int row0, int g, uint32_t& lo, uint32_t& hi) {
+    const int lane = threadIdx.x & 63;
+    const int row = row0 + (lane & 31);
+    const int sw = lane & 7;  // row % 8
+    constexpr int CPG = 16 / C::VEC;  // chunks per K group of 16
+    const int c = CPG * g + (CPG / 2) * (lane >> 5);
+    lo = (uint32_t)(row * ROWB + ((c ^ sw) << 4));
+    hi = (uint32_t)(row * ROWB + (((c + 1) ^ sw) << 4));
+  }
+};
+
+__device__ __forceinline__ void lds_frag_at(Frag<uint16_t>& f, const lds_u8* st, uint32_t lo, uint32_t) {
+  f.v = *(const __attribute__((address_space(3))) u32x4*)(st + lo);
+}
+__device__ __forceinline__ void lds_frag_at(Frag<float>& f, const lds_u8* st, uint32_t lo, uint32_t hi) {
+  f.lo = *(const __attribute__((address_space(3))) f32x4*)(st + lo);
+  f.hi = *(const __attribute__((address_space(3))) f32x4*)(st + hi);
+}
+
+// acc[fm][fn] += sum over the K steps of A_tile * B_tile^T, as mainloop()
+// (same step/offset conventions), both operands K-major and DMA-fed.
+//
+// Two LDS stages.  Within a step the MFMAs of K group g run while the
+// fragments of group g+1 are read.  Before the last group each wave waits for
+// its DMA loads of the next step and joins one barrier: after it the next
+// stage is complete and the current one is free.  A stage is therefore free
+// for one step between its last read and the first read of its next contents;
+// its DMA loads (which the memory pipeline delivers at about 64 bytes per
+// clock per CU, so a step's 64 KB needs about half a step) are issued in
+// NPARTS parts over that window: part 0 right after the barrier, in the last
+// group, and part p in group p-1 of the following step, each spread one or two
+// instructions between MFMAs so the issue never stalls the matrix core.
+// Steps past the end (the count is padded to even) read zeros.
+template <class C, int SPB, int NPARTS = (C::KGROUPS > 2 ? 3 : 1)>
+__device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const Operand& A, const Operand& B,
+                                             int nsteps, const uint16_t* blocks, void* smem) {
+  using T = typename C::T;
+  using TA = DmaTile<C, C::BM>;
+  using TB = DmaTile<C, C::BN>;
+  constexpr int KG = C::KGROUPS;
+  static_assert(KG % 2 == 0, "fragment buffers alternate per K group");
+  static_assert(NPARTS >= 1 && NPARTS < KG, "the last DMA part must precede the wait");
+  constexpr int STAGE = TA::BYTES + TB::BYTES;
+  static_assert(2 * STAGE == C::LDS_DMA_BYTES, "stage size");
+  if (nsteps <= 0) return;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int kend = A.kdim > B.kdim ? A.kdim : B.kdim;
+  auto kofs = [&](int s) -> int {
+    if (s >= nsteps) return kend;
+    return blocks ? (int)blocks[s / SPB] * (SPB * C::BK) + (s % SPB) * C::BK : s * C::BK;
+  };
+  const lds_u8* base = (const lds_u8*)smem;
+  const uint32_t base_addr = (uint32_t)(uintptr_t)base;
+
+  constexpr int NDMA = TA::PER + TB::PER;  // DMA instructions per wave per step
+  TA ta;
+  TB tb;
+  ta.init(A);
+  tb.init(B);
+  auto dma = [&](int d, int k0, uint32_t st) {
+    if (d < TA::PER) ta.issue(d, A, k0, st);
+    else tb.issue(d - TA::PER, B, k0, st + TA::BYTES);
+  };
+  // prologue: step 0 whole, part 0 of step 1 (its other parts follow in step 0)
+  constexpr int P0 = NDMA / NPARTS;
+#pragma unroll
+  for (int d = 0; d < NDMA; ++d) dma(d, kofs(0), base_addr);
+#pragma unroll
+  for (int d = 0; d < P0; ++d) dma(d, kofs(1), base_addr + STAGE);
+  wait_vmcnt<P0>();  // step 0 has landed
+  __syncthreads();
+
+  uint32_t alo[KG], ahi[KG], blo[KG], bhi[KG];
+#pragma unroll
+  for (int g = 0; g < KG; ++g) {
+    TA::frag_off(wm * C::WM, g, alo[g], ahi[g]);
+    TB::frag_off(wn * C::WN, g, blo[g], bhi[g]);
+    blo[g] += TA::BYTES;
+    bhi[g] += TA::BYTES;
+  }
+  Frag<T> fa[2][C::FM], fb[2][C::FN];
+  auto read_one = [&](int buf, const lds_u8* st, int g, int q) {
+    if (q < C::FM)
+      lds_frag_at(fa[buf][q], st, alo[g] + q * 32 * TA::ROWB, ahi[g] + q * 32 * TA::ROWB);
+    else
+      lds_frag_at(fb[buf][q - C::FM], st, blo[g] + (q - C::FM) * 32 * TB::ROWB,
+                  bhi[g] + (q - C::FM) * 32 * TB::ROWB);
+  };
+#pragma unroll
+  for (int q = 0; q < C::FM + C::FN; ++q) read_one(0, base, 0, q);
+
+  constexpr int NFR = C::FM + C::FN;
+  constexpr int BLOCKS = C::FM * C::FN;
+
+  auto step = [&](int s, const lds_u8* st, const lds_u8* nx, uint32_t st_addr, uint32_t nx_addr) {
+    const int k1 = kofs(s + 1), k2 = kofs(s + 2);
+    auto group = [&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      constexpr bool last = g + 1 == KG;
+      if constexpr (last) {
+        wait_vmcnt<0>();
+        __syncthreads();
+      }
+      // DMA share of this group: part 0 of step s+2 into this stage after the
+      // barrier, or part g+1 of step s+1 into the next stage
+      constexpr int dp = last ? 0 : g + 1;
+      constexpr bool has_dma = last || g + 1 < NPARTS;
+      constexpr int dlo = has_dma ? dp * NDMA / NPARTS : 0;
+      constexpr int dn = has_dma ? (dp + 1) * NDMA / NPARTS - dlo : 0;
+      [&]<int... Q>(std::integer_sequence<int, Q...>) {
+        (
+            [&] {
+              constexpr int b = Q;
+              mma16(acc[b / C::FN][b % C::FN], fa[g & 1][b / C::FN], fb[g & 1][b % C::FN]);
+              constexpr int r0 = b * NFR / BLOCKS, r1 = (b + 1) * NFR / BLOCKS;
+#pragma unroll
+              for (int q = r0; q < r1; ++q) {
+                if constexpr (last) read_one(0, nx, 0, q);
+                else read_one((g + 1) & 1, st, g + 1, q);
+              }
+              constexpr int d0 = b * dn / BLOCKS, d1 = (b + 1) * dn / BLOCKS;
+#pragma unroll
+              for (int d = d0; d < d1; ++d) {
+                if constexpr (last) dma(dlo + d, k2, st_addr);
+                else dma(dlo + d, k1, nx_addr);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }(),
+            ...);
+      }(std::make_integer_sequence<int, BLOCKS>{});
+    };
+    [&]<int... G>(std::integer_sequence<int, G...>) {
+      (group(std::integral_constant<int, G>{}), ...);
+    }(std::make_integer_sequence<int, KG>{});
+  };
+
+  const lds_u8* st0 = base;
+  const lds_u8* st1 = base + STAGE;
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, st0, st1, base_addr, base_addr + STAGE);
+    step(s + 1, st1, st0, base_addr + STAGE, base_addr);
+  }
+  wait_vmcnt<0>();  // the trailing loads (zeros past the end) have landed
+  __syncthreads();
 }
 
 // Output coordinates of accumulator element r of block (fm, fn) for this lane,

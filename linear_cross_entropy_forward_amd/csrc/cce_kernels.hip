@@ -130,21 +130,21 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
                                                             int N, int D, int V, float2* __restrict__ part,
                                                             int nVB, int tiles_n, int total) {
   using T = typename C::T;
-  __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   int tv, tn;
   grouped_tile(xcd_remap(blockIdx.x, total), total / tiles_n, tiles_n, kRasterGroup, tv, tn);
   const int v0 = tv * C::BM, n0 = tn * C::BN;
 
-  Operand A{make_rsrc(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T)), (uint32_t)D,
-            min(C::BM, V - v0), D};
-  Operand B{make_rsrc(e + (size_t)n0 * D, (uint64_t)(N - n0) * D * sizeof(T)), (uint32_t)D,
-            min(C::BN, N - n0), D};
+  Operand A = make_operand(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T), (uint32_t)D,
+               min(C::BM, V - v0), D);
+  Operand B = make_operand(e + (size_t)n0 * D, (uint64_t)(N - n0) * D * sizeof(T), (uint32_t)D,
+               min(C::BN, N - n0), D);
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
-  mainloop<C, false, false, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem);
+  mainloop_dma<C, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem);
 
   AccMap<C> am;
   const int lane = threadIdx.x & 63;
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int tiles_v,
     int tiles_n, int Vc, int Npad, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes) {
   using T = typename C::T;
-  __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   const int total = tiles_v * tiles_n;
   int tvl, tn;
   grouped_tile(xcd_remap(blockIdx.x, total), tiles_v, tiles_n, kRasterGroup, tvl, tn);
@@ -388,16 +388,16 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   if (!keep[(size_t)tn * nvb_t + tv]) return;
   const int v0 = tv * C::BM, n0 = tn * C::BN;
 
-  Operand A{make_rsrc(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T)), (uint32_t)D,
-            min(C::BM, V - v0), D};
-  Operand B{make_rsrc(e + (size_t)n0 * D, (uint64_t)max(N - n0, 0) * D * sizeof(T)), (uint32_t)D,
-            min(C::BN, N - n0), D};
+  Operand A = make_operand(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T), (uint32_t)D,
+               min(C::BM, V - v0), D);
+  Operand B = make_operand(e + (size_t)n0 * D, (uint64_t)max(N - n0, 0) * D * sizeof(T), (uint32_t)D,
+               min(C::BN, N - n0), D);
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
-  mainloop<C, false, false, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem);
+  mainloop_dma<C, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem);
 
   AccMap<C> am;
   rsrc_t rg = make_rsrc(G, g_bytes);
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
     const uint8_t* __restrict__ keep, int Npad, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
     int tiles_v, int tiles_d, size_t g_bytes, float* __restrict__ dC) {
   using T = typename C::T;
-  __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
   const int total = tiles_v * tiles_d;
   int tvl, td;
@@ -475,17 +475,17 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
   const int nb = Npad / kTileN;
   const int nk = collect_blocks(keep, (size_t)(cvb0 + tvl), nvb_t, nb, blocks);
 
-  Operand A{make_rsrc(Gt + (size_t)vl0 * Npad, g_bytes - (size_t)vl0 * Npad * sizeof(T)), (uint32_t)Npad,
-            min(C::BM, clen - vl0), Npad};
-  Operand B{make_rsrc(Et + (size_t)d0 * Npad, (uint64_t)(D - d0) * Npad * sizeof(T)), (uint32_t)Npad,
-            min(C::BN, D - d0), Npad};
+  Operand A = make_operand(Gt + (size_t)vl0 * Npad, g_bytes - (size_t)vl0 * Npad * sizeof(T), (uint32_t)Npad,
+               min(C::BM, clen - vl0), Npad);
+  Operand B = make_operand(Et + (size_t)d0 * Npad, (uint64_t)(D - d0) * Npad * sizeof(T), (uint32_t)Npad,
+               min(C::BN, D - d0), Npad);
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   constexpr int SPB = kTileN / C::BK;
-  mainloop<C, false, false, SPB>(acc, A, B, nk * SPB, blocks, smem);
+  mainloop_dma<C, SPB>(acc, A, B, nk * SPB, blocks, smem);
 
   AccMap<C> am;
   const int vg0 = cv0 + vl0;
@@ -530,10 +530,10 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   for (int j = threadIdx.x; j < nk; j += blockDim.x) blocks[j] += vb_lo;
   __syncthreads();
 
-  Operand A{make_rsrc(G + (size_t)n0 * Vc, g_bytes - (size_t)n0 * Vc * sizeof(T)), (uint32_t)Vc,
-            min(C::BM, N - n0), clen};
-  Operand B{make_rsrc(c + (size_t)cv0 * D + d0, ((uint64_t)(V - cv0) * D - d0) * sizeof(T)), (uint32_t)D,
-            min(C::BN, D - d0), clen};
+  Operand A = make_operand(G + (size_t)n0 * Vc, g_bytes - (size_t)n0 * Vc * sizeof(T), (uint32_t)Vc,
+               min(C::BM, N - n0), clen);
+  Operand B = make_operand(c + (size_t)cv0 * D + d0, ((uint64_t)(V - cv0) * D - d0) * sizeof(T), (uint32_t)D,
+               min(C::BN, D - d0), clen);
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
