@@ -237,11 +237,7 @@ def main():
     tflops = eff_flops / (ms_step * 1e-3) / 1e12
 
     # chunk lengths of the backward, for per-launch algorithmic work
-    Vc = args.vocab_chunk
-    if Vc == 0:
-        Npad = -(-N // 256) * 256
-        Vc = max(256, (512 << 20) // (2 * Npad * es) // 256 * 256)
-        Vc = min(Vc, -(-V // 256) * 256)
+    Vc = M.vocab_chunk(N, V, tdt, args.vocab_chunk)
     chunk_lens = [min(Vc, V - s) for s in range(0, V, Vc)]
     nVB = -(-V // 128)
     kernels = {}

@@ -79,13 +79,21 @@ typedef struct {
  * Bytes of device workspace needed by cce_forward and cce_backward for this
  * problem.  vocab_chunk = 0 picks the library default: the backward forms
  * gradient tiles for a vocabulary chunk at a time and keeps that chunk's
- * bf16/fp32 G block, in both orientations, in the workspace (256 MiB for the
- * two by default), plus e transposed (N*D elements); a positive
+ * bf16/fp32 G block, in both orientations, in the workspace (about 512 MiB for
+ * the two by default), plus e transposed (N*D elements); a positive
  * value (a multiple of 256) sets the chunk width, trading workspace for
  * launches.  The forward uses only the first part (per-row partials,
  * O(N + N*V/128) floats).  Returns 0 for invalid arguments.
  */
 size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk);
+
+/*
+ * Vocabulary entries per chunk that cce_backward uses for this problem and
+ * vocab_chunk argument (the default when vocab_chunk = 0; the value passed,
+ * clamped to the vocabulary, otherwise).  The backward launches its gradient
+ * kernels once per chunk.  Returns 0 for invalid arguments.
+ */
+int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk);
 
 /*
  * Forward.  e (device) [N, D], c (device) [V, D] of `dtype`; targets (device)

@@ -25,7 +25,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   if (vocab_chunk > 0) {
     vc = vocab_chunk;
   } else {
-    vc = (int64_t)(kDefaultGBudget / (2 * (size_t)L.Npad * es)) / kTileV * kTileV;
+    vc = (int64_t)(kDefaultGBudget / ((2 * (size_t)L.Npad + kGtPad) * es)) / kTileV * kTileV;
   }
   if (vc < kTileV) vc = kTileV;
   if (vc > vmax) vc = vmax;
@@ -46,6 +46,8 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   if (spa < 1) spa = 1;
   L.splits_atomic = spa;
   L.g_bytes = (size_t)L.Npad * (size_t)vc * es;
+  L.gt_ld = L.Npad + kGtPad;
+  L.gt_bytes = (size_t)L.gt_ld * (size_t)vc * es;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -59,7 +61,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const size_t o_scale = take((size_t)L.Npad * 4);
   const size_t o_keep = take((size_t)L.nb * L.nvb_t);
   const size_t o_g = take(L.g_bytes);
-  const size_t o_gt = take(L.g_bytes);
+  const size_t o_gt = take(L.gt_bytes);
   const size_t o_et = take((size_t)D * (size_t)L.Npad * es);
   const size_t o_dep = take((size_t)(L.splits - 1) * (size_t)N * (size_t)D * 4);
   L.total = off;
@@ -100,7 +102,8 @@ static cce_status check_common(const void* e, const void* c, const int64_t* targ
   if ((N + kTileN) * D * es >= lim || N > (int64_t)kMaxBlocks * kTileN || V >= lim / 2 || D >= lim / 2)
     return CCE_ERR_UNSUPPORTED;
   Layout L = make_layout(N, D, V, dtype, vocab_chunk, nullptr);
-  if ((int64_t)L.Vc * D * es >= lim || (int64_t)L.g_bytes >= lim) return CCE_ERR_UNSUPPORTED;
+  if ((int64_t)L.Vc * D * es >= lim || (int64_t)L.g_bytes >= lim || (int64_t)L.gt_bytes >= lim)
+    return CCE_ERR_UNSUPPORTED;
   return CCE_OK;
 }
 
@@ -148,6 +151,12 @@ size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vo
   if (N <= 0 || D <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
   if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return 0;
   return make_layout(N, D, V, dtype, vocab_chunk, nullptr).total;
+}
+
+int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk) {
+  if (N <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
+  if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return 0;
+  return make_layout(N, 1, V, dtype, vocab_chunk, nullptr).Vc;
 }
 
 cce_status cce_forward(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D, int64_t V,

@@ -31,6 +31,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -566,9 +567,13 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   const int wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int kend = A.kdim > B.kdim ? A.kdim : B.kdim;
+  // K offset of step s; steps past the end read zeros (offset kend).  The
+  // block-list index is clamped so that it stays inside the list.
+  const int last_blk = (nsteps - 1) / SPB;
   auto kofs = [&](int s) -> int {
-    if (s >= nsteps) return kend;
-    return blocks ? (int)blocks[s / SPB] * (SPB * C::BK) + (s % SPB) * C::BK : s * C::BK;
+    const int b = s / SPB < last_blk ? s / SPB : last_blk;
+    const int k = blocks ? (int)blocks[b] * (SPB * C::BK) + (s % SPB) * C::BK : s * C::BK;
+    return s < nsteps ? k : kend;
   };
   const lds_u8* base = (const lds_u8*)smem;
   const uint32_t base_addr = (uint32_t)(uintptr_t)base;
@@ -613,8 +618,12 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   constexpr int NFR = C::FM + C::FN;
   constexpr int BLOCKS = C::FM * C::FN;
 
-  auto step = [&](int s, const lds_u8* st, const lds_u8* nx, uint32_t st_addr, uint32_t nx_addr) {
-    const int k1 = kofs(s + 1), k2 = kofs(s + 2);
+  // k1 = kofs(s + 1) comes from the previous step; kofs(s + 2), first needed
+  // after the barrier, is read (from the LDS block list when there is one) at
+  // the top of the step, ahead of the step's fragment reads, so the waits for
+  // those cover it and the loop never waits on that read alone.
+  auto step = [&](int s, const lds_u8* st, const lds_u8* nx, uint32_t st_addr, uint32_t nx_addr, int k1) -> int {
+    const int k2 = kofs(s + 2);
     auto group = [&](auto gc) {
       constexpr int g = decltype(gc)::value;
       constexpr bool last = g + 1 == KG;
@@ -653,13 +662,15 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
     [&]<int... G>(std::integer_sequence<int, G...>) {
       (group(std::integral_constant<int, G>{}), ...);
     }(std::make_integer_sequence<int, KG>{});
+    return k2;
   };
 
   const lds_u8* st0 = base;
   const lds_u8* st1 = base + STAGE;
+  int kn = kofs(1);
   for (int s = 0; s < nsteps; s += 2) {
-    step(s, st0, st1, base_addr, base_addr + STAGE);
-    step(s + 1, st1, st0, base_addr + STAGE, base_addr);
+    kn = step(s, st0, st1, base_addr, base_addr + STAGE, kn);
+    kn = step(s + 1, st1, st0, base_addr + STAGE, base_addr, kn);
   }
   wait_vmcnt<0>();  // the trailing loads (zeros past the end) have landed
   __syncthreads();

@@ -34,6 +34,9 @@ constexpr int kHdrWords = 64;  // 256 bytes
 
 // Default byte budget of the per-chunk gradient tile buffers G and G^T together.
 constexpr size_t kDefaultGBudget = size_t(512) << 20;
+// Extra elements per row of the transposed gradient tiles (row pitch
+// Npad + kGtPad).  Zero: measured no faster with a padded pitch.
+constexpr int kGtPad = 0;
 
 struct Problem {
   const void* e;
@@ -63,9 +66,11 @@ struct Layout {
   float* scale;     // [Npad]
   uint8_t* keep;    // [nb][nvb_t]
   void* G;          // [Npad][Vc] operand type: gradient tiles of one vocab chunk
-  void* Gt;         // [Vc][Npad] the same tiles transposed
+  void* Gt;         // [Vc][gt_ld] the same tiles transposed (columns past Npad unused)
   void* Et;         // [D][Npad] e transposed (zero rows past N)
-  size_t g_bytes;   // bytes of G (and of Gt)
+  size_t g_bytes;   // bytes of G
+  size_t gt_bytes;  // bytes of Gt
+  int gt_ld;        // row pitch of Gt in elements: Npad + kGtPad
   float* dE_part;   // [splits-1][N][D]
   int nVB, Npad, nb, nvb_t, Vc, nchunks, splits, splits_atomic;
 };

@@ -92,11 +92,66 @@ __device__ __forceinline__ void store4(rsrc_t r, uint32_t off, float a, float b,
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 
-// One value in the operand type.
-__device__ __forceinline__ void store1(rsrc_t r, uint32_t off, float a, const uint16_t*) {
-  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)a), r, off, 0, 0);
+// Lane-quad exchange (DPP quad_perm): value of lane (k ^ 2) or (k ^ 1).
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
 }
-__device__ __forceinline__ void store1(rsrc_t r, uint32_t off, float a, const float*) { stf(r, off, a); }
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+}
+
+// 4x4 transpose of 16-bit values across a lane quad: on entry lane k holds
+// x[k][0..3] as d0 = x[k][0] | x[k][1] << 16, d1 = x[k][2] | x[k][3] << 16;
+// on exit it holds x[0..3][k] the same way.
+__device__ __forceinline__ void quad_transpose16(uint32_t& d0, uint32_t& d1) {
+  const int k = threadIdx.x & 3;
+  // rows {2,3} of lanes {0,1} <-> rows {0,1} of lanes {2,3}
+  const bool k2 = (k & 2) != 0, k1 = (k & 1) != 0;
+  const uint32_t rcv = quad_xor2(k2 ? d0 : d1);
+  d0 = k2 ? rcv : d0;
+  d1 = k2 ? d1 : rcv;
+  // 16-bit halves between neighbouring lanes (v_perm_b32 byte selects)
+  const uint32_t p0 = quad_xor1(d0), p1 = quad_xor1(d1);
+  d0 = k1 ? __builtin_amdgcn_perm(d0, p0, 0x07060302u) : __builtin_amdgcn_perm(p0, d0, 0x05040100u);
+  d1 = k1 ? __builtin_amdgcn_perm(d1, p1, 0x07060302u) : __builtin_amdgcn_perm(p1, d1, 0x05040100u);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+// Transposed store of the 4x4 fp32 block held by a lane quad.  Lane k holds
+// x[k][0..3], four consecutive rows of its own column (the accumulator
+// layout); after two quad exchanges it holds x[0..3][k] and writes them as
+// four consecutive columns of row k (one 16-byte store).  `off_row0` is the
+// byte offset of (row 0, the quad's first column), `ld` the row pitch in bytes.
+__device__ __forceinline__ void store_quad_t(rsrc_t r, uint32_t off_row0, uint32_t ld, const float (&x)[4],
+                                             const float*) {
+  const int k = threadIdx.x & 3;
+  uint32_t d[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) d[u] = __builtin_bit_cast(uint32_t, x[u]);
+  // rows {2,3} of lanes {0,1} <-> rows {0,1} of lanes {2,3}
+  const bool k2 = (k & 2) != 0, k1 = (k & 1) != 0;
+  {
+    const uint32_t s0 = quad_xor2(k2 ? d[0] : d[2]);
+    const uint32_t s1 = quad_xor2(k2 ? d[1] : d[3]);
+    d[0] = k2 ? s0 : d[0];
+    d[1] = k2 ? s1 : d[1];
+    d[2] = k2 ? d[2] : s0;
+    d[3] = k2 ? d[3] : s1;
+  }
+  // odd rows of even lanes <-> even rows of odd lanes
+  {
+    const uint32_t s0 = quad_xor1(k1 ? d[0] : d[1]);
+    const uint32_t s1 = quad_xor1(k1 ? d[2] : d[3]);
+    d[0] = k1 ? s0 : d[0];
+    d[2] = k1 ? s1 : d[2];
+    d[1] = k1 ? d[1] : s0;
+    d[3] = k1 ? d[3] : s1;
+  }
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{d[0], d[1], d[2], d[3]}, r, off_row0 + (uint32_t)k * ld, 0, 0);
+}
 
 // ============================================================================
 // e^T [D][Npad] (rows past N zero) for the dC contraction, via 64x64 LDS tiles.
@@ -378,7 +433,8 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     const typename C::T* __restrict__ c, const typename C::T* __restrict__ e,
     const int64_t* __restrict__ targets, const float* __restrict__ lse, const float* __restrict__ scale,
     const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int tiles_v,
-    int tiles_n, int Vc, int Npad, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes) {
+    int tiles_n, int Vc, int gt_ld, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes,
+    size_t gt_bytes) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   const int total = tiles_v * tiles_n;
@@ -397,42 +453,122 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
-  mainloop_dma<C, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem);
-
+  // per-column constants, fetched before the main loop so that their latency
+  // is hidden: lse in log2 units, the gradient scale, and the target's row
+  // relative to this lane's first accumulator row (outside the tile: -1, which
+  // no row offset matches)
   AccMap<C> am;
-  rsrc_t rg = make_rsrc(G, g_bytes);
-  rsrc_t rgt = make_rsrc(Gt, g_bytes);
-  const int vl0 = tvl * C::BM;  // chunk-local column of the tile
+  float lsel[C::FN], sc[C::FN];
+  int trow[C::FN];
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn) {
     const int n = n0 + am.colj(fn);
     const bool vn = n < N;
-    const float lsel = vn ? lse[n] * kLog2e : 0.f;
-    const float sc = vn ? scale[n] : 0.f;
-    const int64_t tgt = vn ? targets[n] : -1;
+    lsel[fn] = vn ? lse[n] * kLog2e : 0.f;
+    sc[fn] = vn ? scale[n] : 0.f;  // zero for padding columns: their G is zero
+    const int64_t tg = vn ? targets[n] : -1;
+    const int64_t rel = tg - (int64_t)(v0 + am.row0);
+    trow[fn] = (tg >= v0 && tg < v0 + C::BM) ? (int)rel : -1;
+  }
+  mainloop_dma<C, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem);
+
+  rsrc_t rg = make_rsrc(G, g_bytes);
+  rsrc_t rgt = make_rsrc(Gt, gt_bytes);
+  const int vl0 = tvl * C::BM;  // chunk-local column of the tile
+  // G = (softmax - onehot) * scale, rounded once to the operand type, handed
+  // to `sink(fn, fm, q, rl, g)` four consecutive vocab rows (rl..rl+3,
+  // tile-local) of one token column at a time.  Rows of the last tile past V
+  // are zeroed (their logits read zero rows of c); all other tiles take the
+  // branch-free path.
+  auto compute = [&](auto ragged, auto&& sink) {
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
+    for (int fn = 0; fn < C::FN; ++fn) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float g[4];
-        const int rl = am.row(fm, 4 * q);  // tile-local vocab row of element 4q
+      for (int fm = 0; fm < C::FM; ++fm) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int v = v0 + rl + u;
-          float p = fast_exp2(__builtin_fmaf(acc[fm][fn][4 * q + u], kLog2e, -lsel));
-          p -= (v == tgt) ? 1.f : 0.f;
-          g[u] = (vn && v < V) ? p * sc : 0.f;
+        for (int q = 0; q < 4; ++q) {
+          float g[4];
+          const int rl = am.row(fm, 4 * q);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float p = fast_exp2(__builtin_fmaf(acc[fm][fn][4 * q + u], kLog2e, -lsel[fn]));
+            const float tsc = trow[fn] == fm * 32 + 8 * q + u ? sc[fn] : 0.f;
+            g[u] = __builtin_fmaf(p, sc[fn], -tsc);
+            if constexpr (decltype(ragged)::value) g[u] = v0 + rl + u < V ? g[u] : 0.f;
+          }
+          sink(fn, fm, q, rl, g);
         }
-        const uint32_t off = ((uint32_t)n * (uint32_t)Vc + (uint32_t)(vl0 + rl)) * (uint32_t)sizeof(T);
-        store4(rg, off, g[0], g[1], g[2], g[3], (const T*)nullptr);
-        // G^T[v][n]: for each of the four vocab rows, 32 lanes write 32
-        // consecutive tokens
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          store1(rgt, ((uint32_t)(vl0 + rl + u) * (uint32_t)Npad + (uint32_t)n) * (uint32_t)sizeof(T), g[u],
-                 (const T*)nullptr);
       }
     }
+  };
+  auto run = [&](auto&& sink) {
+    if (v0 + C::BM <= V) compute(std::false_type{}, sink);
+    else compute(std::true_type{}, sink);
+  };
+
+  if constexpr (sizeof(T) == 2) {
+    // Staged through LDS (free after the main loop) twice, so that both G and
+    // G^T leave as rows of 16-byte stores from consecutive lanes (stored
+    // straight from the accumulators, one instruction would scatter 8-byte
+    // pieces over 64 rows).  A staging tile holds 256 rows of 512 bytes;
+    // 16-byte chunk j of row r sits in slot j ^ f(r).  Any f keeps the row
+    // drains conflict free; f is chosen per pass for its writes: pass 1 writes
+    // one chunk of 32 consecutive rows (f = r % 32), pass 2 two chunks of
+    // rows R..R+3 from each lane quad (f swaps the two low bit pairs of r).
+    static_assert(C::BM == 256 && C::BN == 256 && C::LDS_DMA_BYTES >= 256 * 512, "tile staging");
+    lds_u8* tile = (lds_u8*)smem;
+    auto slot = [](int r, int col, auto pass2) -> uint32_t {
+      const int f = decltype(pass2)::value ? (((r & 3) << 2) | ((r >> 2) & 3) | (r & 16)) : (r & 31);
+      return (uint32_t)(r * 512 + (((col >> 3) ^ f) << 4) + ((col & 7) << 1));
+    };
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // rows of 256 bf16 out of the staging tile, two per instruction: row
+    // `wave * 64 + 2 it + lane / 32`, chunk lane % 32, to row-major memory
+    auto drain = [&](rsrc_t r, uint32_t pitch, uint32_t row0, uint32_t col0, auto pass2) {
+#pragma unroll 4
+      for (int it = 0; it < 32; ++it) {
+        const int rr = wave * 64 + it * 2 + (lane >> 5), jc = lane & 31;
+        const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(rr, jc * 8, pass2));
+        __builtin_amdgcn_raw_buffer_store_b128(val, r, ((row0 + (uint32_t)rr) * pitch + col0 + (uint32_t)jc * 8u) * 2u,
+                                               0, 0);
+      }
+    };
+    uint32_t pk[C::FN][C::FM][4][2];
+    // pass 1: [token][vocab] -> G rows
+    run([&](int fn, int fm, int q, int rl, const float (&g)[4]) {
+      pk[fn][fm][q][0] = pack_bf16(g[0], g[1]);
+      pk[fn][fm][q][1] = pack_bf16(g[2], g[3]);
+      *(__attribute__((address_space(3))) u32x2*)(tile + slot(am.colj(fn), rl, std::false_type{})) =
+          u32x2{pk[fn][fm][q][0], pk[fn][fm][q][1]};
+    });
+    __syncthreads();
+    drain(rg, (uint32_t)Vc, (uint32_t)n0, (uint32_t)vl0, std::false_type{});
+    __syncthreads();
+    // pass 2: quad transposes turn each lane's four vocab rows of one token
+    // into four tokens of one vocab row; [vocab][token] -> G^T rows
+    const int k = lane & 3;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t d0 = pk[fn][fm][q][0], d1 = pk[fn][fm][q][1];
+          quad_transpose16(d0, d1);
+          *(__attribute__((address_space(3))) u32x2*)(
+              tile + slot(am.row(fm, 4 * q) + k, am.colj(fn) & ~3, std::true_type{})) = u32x2{d0, d1};
+        }
+    __syncthreads();
+    drain(rgt, (uint32_t)gt_ld, (uint32_t)vl0, (uint32_t)n0, std::true_type{});
+  } else {
+    run([&](int fn, int, int, int rl, const float (&g)[4]) {
+      const int n = n0 + am.colj(fn);
+      store4(rg, ((uint32_t)n * (uint32_t)Vc + (uint32_t)(vl0 + rl)) * (uint32_t)sizeof(T), g[0], g[1], g[2], g[3],
+             (const T*)nullptr);
+      // G^T[v][n]: the quad's four tokens of vocab rows rl..rl+3
+      store_quad_t(rgt, ((uint32_t)(vl0 + rl) * (uint32_t)gt_ld + (uint32_t)(n & ~3)) * (uint32_t)sizeof(T),
+                   (uint32_t)gt_ld * (uint32_t)sizeof(T), g, (const T*)nullptr);
+    });
   }
 }
 
@@ -463,8 +599,8 @@ __device__ __forceinline__ int collect_blocks(const uint8_t* __restrict__ keep, 
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
     const typename C::T* __restrict__ Gt, const typename C::T* __restrict__ Et,
-    const uint8_t* __restrict__ keep, int Npad, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
-    int tiles_v, int tiles_d, size_t g_bytes, float* __restrict__ dC) {
+    const uint8_t* __restrict__ keep, int Npad, int gt_ld, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
+    int tiles_v, int tiles_d, size_t gt_bytes, float* __restrict__ dC) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
@@ -475,7 +611,7 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
   const int nb = Npad / kTileN;
   const int nk = collect_blocks(keep, (size_t)(cvb0 + tvl), nvb_t, nb, blocks);
 
-  Operand A = make_operand(Gt + (size_t)vl0 * Npad, g_bytes - (size_t)vl0 * Npad * sizeof(T), (uint32_t)Npad,
+  Operand A = make_operand(Gt + (size_t)vl0 * gt_ld, gt_bytes - (size_t)vl0 * gt_ld * sizeof(T), (uint32_t)gt_ld,
                min(C::BM, clen - vl0), Npad);
   Operand B = make_operand(Et + (size_t)d0 * Npad, (uint64_t)(D - d0) * Npad * sizeof(T), (uint32_t)Npad,
                min(C::BN, D - d0), Npad);
@@ -485,7 +621,9 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   constexpr int SPB = kTileN / C::BK;
-  mainloop_dma<C, SPB>(acc, A, B, nk * SPB, blocks, smem);
+  // all token blocks kept (no filtering effect on this tile): contiguous K
+  if (nk == nb) mainloop_dma<C, SPB>(acc, A, B, nk * SPB, nullptr, smem);
+  else mainloop_dma<C, SPB>(acc, A, B, nk * SPB, blocks, smem);
 
   AccMap<C> am;
   const int vg0 = cv0 + vl0;
@@ -540,7 +678,18 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   constexpr int SPB = kTileV / C::BK;
-  mainloop<C, false, true, SPB>(acc, A, B, nk * SPB, blocks, smem);
+  // every vocab block of the split kept: contiguous K from the split's start
+  if (nk == vb_hi - vb_lo) {
+    A.r = make_rsrc(G + (size_t)n0 * Vc + (size_t)vb_lo * kTileV,
+                    g_bytes - ((size_t)n0 * Vc + (size_t)vb_lo * kTileV) * sizeof(T));
+    A.kdim = clen - vb_lo * kTileV;
+    B.r = make_rsrc(c + ((size_t)cv0 + (size_t)vb_lo * kTileV) * D + d0,
+                    ((uint64_t)(V - cv0 - vb_lo * kTileV) * D - d0) * sizeof(T));
+    B.kdim = A.kdim;
+    mainloop<C, false, true, SPB>(acc, A, B, nk * SPB, nullptr, smem);
+  } else {
+    mainloop<C, false, true, SPB>(acc, A, B, nk * SPB, blocks, smem);
+  }
 
   if (nk == 0 && (accumulate || atomic)) return;  // nothing to add
   AccMap<C> am;
@@ -656,13 +805,13 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     const int cvb0 = cv0 / kTileV;
     prof_before(kKGradTile, st);
     hipLaunchKernelGGL(grad_tile_kernel<C>, dim3(cnvb * tiles_n), dim3(C::NT), 0, st, c, e, P.targets, P.lse,
-                       L.scale, L.keep, P.N, P.D, P.V, L.nvb_t, cvb0, cnvb, tiles_n, L.Vc, L.Npad, G, (T*)L.Gt,
-                       L.g_bytes);
+                       L.scale, L.keep, P.N, P.D, P.V, L.nvb_t, cvb0, cnvb, tiles_n, L.Vc, L.gt_ld, G, (T*)L.Gt,
+                       L.g_bytes, L.gt_bytes);
     prof_after(kKGradTile, st);
     prof_before(kKDC, st);
     hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(cnvb * tiles_d), dim3(C::NT), 0, st, (const T*)L.Gt,
-                       (const T*)L.Et, L.keep, L.Npad, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_d, L.g_bytes,
-                       P.dC);
+                       (const T*)L.Et, L.keep, L.Npad, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_d,
+                       L.gt_bytes, P.dC);
     prof_after(kKDC, st);
     const int splits = P.accum == kAccumAtomic ? L.splits_atomic : L.splits;
     prof_before(kKDE, st);

@@ -56,6 +56,18 @@ def test_workspace_size(L):
     assert ws(4096, 4096, 128256, 1, 0) >= ws(4096, 4096, 128256, 0, 0) // 2
 
 
+def test_vocab_chunk(L):
+    vc = L.cce_vocab_chunk
+    assert vc(0, 100, 0, 0) == 0 and vc(4, 100, 7, 0) == 0 and vc(4, 100, 0, 100) == 0
+    d = vc(4096, 128256, 0, 0)
+    assert d % 256 == 0 and 256 <= d <= 128256 + 255
+    # the default keeps both orientations of a chunk's bf16 tiles within 512 MiB
+    assert 2 * 4096 * d * 2 <= 512 << 20
+    assert vc(4096, 128256, 0, 1024) == 1024
+    assert vc(64, 1000, 1, 0) == 1024          # clamped to the vocabulary, in whole tiles
+    assert vc(64, 1000, 1, 4096) == 1024
+
+
 def _fwd(L, e=FAKE, c=FAKE, t=FAKE, N=64, D=64, V=100, dt=0, ign=-100, red=2, cap=0.0, loss=FAKE, lse=FAKE,
          ws=FAKE, wsb=1 << 30):
     return L.cce_forward(e, c, t, N, D, V, dt, ign, red, cap, loss, lse, None, ws, wsb, None)
