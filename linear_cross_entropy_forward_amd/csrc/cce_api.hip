@@ -35,7 +35,10 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const int tiles_d = (int)((D + kTileV - 1) / kTileV);
   const int tiles_de = L.nb * tiles_d;
   const int cvb = (int)(vc / kTileV);
-  int sp = (512 + tiles_de - 1) / tiles_de;
+  // dE work-groups: enough vocabulary splits to fill one round of the chip
+  // (kWaveSlots work-groups, one per CU); each further split adds a partial
+  // buffer that the epilogue writes and a final pass re-reads.
+  int sp = (kWaveSlots + tiles_de - 1) / tiles_de;
   if (sp > 8) sp = 8;
   if (sp > cvb) sp = cvb;
   if (sp < 1) sp = 1;

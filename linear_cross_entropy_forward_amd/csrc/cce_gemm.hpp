@@ -488,6 +488,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
+__device__ __forceinline__ void lds_frag_at(Frag<uint16_t>& f, const lds_u8* st, uint32_t lo, uint32_t) {
+  f.v = *(const __attribute__((address_space(3))) u32x4*)(st + lo);
+}
+__device__ __forceinline__ void lds_frag_at(Frag<float>& f, const lds_u8* st, uint32_t lo, uint32_t hi) {
+  f.lo = *(const __attribute__((address_space(3))) f32x4*)(st + lo);
+  f.hi = *(const __attribute__((address_space(3))) f32x4*)(st + hi);
+}
+
+// A DMA-fed tile provides: BYTES (one stage), PER (DMA instructions per wave
+// per step), init(op) and issue(i, op, k0, tile) for the loads, and
+// frag_init(rc0) / read(f, st, g, j) for fragment j (the 32 rows or columns
+// starting at rc0 + 32 j) of K group g.
+
+// K-major operand: ROWS rows of BK elements (128 bytes).
 template <class C, int ROWS>
 struct DmaTile {
   using T = typename C::T;
@@ -497,8 +511,10 @@ struct DmaTile {
   static constexpr int NW = C::NT / 64;
   static constexpr int PER = BYTES / 1024 / NW;  // DMA instructions per wave per step
   static_assert(BYTES % (1024 * NW) == 0, "tile not evenly split");
+  static constexpr int KG = C::KGROUPS;
   uint32_t roff[PER];  // byte offset of the lane's row, kOOB past the valid rows
   uint32_t kc;         // K offset (elements) of the lane's chunk within a step
+  uint32_t flo[KG], fhi[KG];  // fragment chunk offsets by K group (fp32: two chunks)
   __device__ __forceinline__ void init(const Operand& op) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     kc = (uint32_t)(((lane & 7) ^ (lane >> 3)) * C::VEC);
@@ -516,27 +532,86 @@ struct DmaTile {
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     dma16(op.desc, off, tile + (uint32_t)((wave * PER + i) * 1024));
   }
-  // Byte offset in the tile of this lane's first fragment chunk at K group g
-  // for the 32-row block starting at row0 (a multiple of 8); fp32 fragments
-  // take a second chunk at `hi`.  Further 32-row blocks add 32 * ROWB.
-  __device__ static __forceinline__ void frag_off(int row0, int g, uint32_t& lo, uint32_t& hi) {
+  // Lane l of a fragment reads row rc0 + 32 j + l % 32 (rc0 a multiple of 8),
+  // K elements 8 (l / 32) .. +7 of the group.
+  __device__ __forceinline__ void frag_init(int rc0) {
     const int lane = threadIdx.x & 63;
-    const int row = row0 + (lane & 31);
+    const int row = rc0 + (lane & 31);
     const int sw = lane & 7;  // row % 8
     constexpr int CPG = 16 / C::VEC;  // chunks per K group of 16
-    const int c = CPG * g + (CPG / 2) * (lane >> 5);
-    lo = (uint32_t)(row * ROWB + ((c ^ sw) << 4));
-    hi = (uint32_t)(row * ROWB + (((c + 1) ^ sw) << 4));
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      const int c = CPG * g + (CPG / 2) * (lane >> 5);
+      flo[g] = (uint32_t)(row * ROWB + ((c ^ sw) << 4));
+      fhi[g] = (uint32_t)(row * ROWB + (((c + 1) ^ sw) << 4));
+    }
+  }
+  __device__ __forceinline__ void read(Frag<T>& f, const lds_u8* st, int g, int j) const {
+    lds_frag_at(f, st, flo[g] + j * 32 * ROWB, fhi[g] + j * 32 * ROWB);
   }
 };
 
-__device__ __forceinline__ void lds_frag_at(Frag<uint16_t>& f, const lds_u8* st, uint32_t lo, uint32_t) {
-  f.v = *(const __attribute__((address_space(3))) u32x4*)(st + lo);
-}
-__device__ __forceinline__ void lds_frag_at(Frag<float>& f, const lds_u8* st, uint32_t lo, uint32_t hi) {
-  f.lo = *(const __attribute__((address_space(3))) f32x4*)(st + lo);
-  f.hi = *(const __attribute__((address_space(3))) f32x4*)(st + hi);
-}
+// MN-major bf16 operand (element (col, k) at k*ld + col): BK rows, one per K
+// index, of COLS columns (512 bytes), loaded as they lie in memory.  Chunk c
+// (columns 8c..8c+7) of K row k sits in slot c ^ 2 (k % 4).  Fragments come
+// from the transposing read ds_read_b64_tr_b16: within each group of 16
+// lanes, output lane i element e is element i % 4 of the 8 bytes addressed by
+// source lane i / 4 + 4 e.  Source lane s addresses K row k0 + s / 4, columns
+// c0 + 4 (s % 4) .. +3, so output lane i receives column c0 + i at K rows
+// k0..k0+3; two such reads give a lane its 8 K elements.  The sixteen 8-byte
+// pieces of one group cover four rows and two chunks, eight distinct slots
+// under the swizzle: no bank conflicts.
+template <class C, int COLS>
+struct DmaTileMN {
+  using T = typename C::T;
+  static_assert(sizeof(T) == 2, "transposing fragment reads are for 16-bit operands");
+  static constexpr int ROWB = COLS * (int)sizeof(T);
+  static_assert(ROWB == 512, "DMA-fed K rows are 512 bytes");
+  static constexpr int RPI = 1024 / ROWB;  // K rows per DMA instruction
+  static constexpr int BYTES = C::BK * ROWB;
+  static constexpr int NW = C::NT / 64;
+  static constexpr int PER = BYTES / 1024 / NW;
+  static_assert(BYTES % (1024 * NW) == 0 && PER % 2 == 0, "tile not evenly split");
+  static constexpr int FN = C::FN;  // fragments per wave
+  __device__ static constexpr int swz(int k) { return 2 * (k & 3); }
+  uint32_t coff[2];  // byte offset of the lane's chunk in its K row, by instruction parity; kOOB past the columns
+  uint32_t foff[FN];
+  __device__ __forceinline__ void init(const Operand& op) {
+    const int lane = threadIdx.x & 63;
+    const int rsub = lane / 32, slot = lane & 31;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int c = slot ^ swz(RPI * p + rsub);
+      coff[p] = c * 8 < op.rows ? (uint32_t)c * 16u : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(int i, const Operand& op, int k0, uint32_t tile) const {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int blk = wave * PER + i;
+    const uint32_t k = (uint32_t)(k0 + RPI * blk + lane / 32);
+    const uint32_t co = coff[i & 1];
+    const uint32_t off = (co == kOOB || k >= (uint32_t)op.kdim) ? kOOB : k * op.ld * (uint32_t)sizeof(T) + co;
+    dma16(op.desc, off, tile + (uint32_t)(blk * 1024));
+  }
+  __device__ __forceinline__ void frag_init(int rc0) {
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4, sl = lane & 15;
+    const int krow = 8 * (grp >> 1) + (sl >> 2);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = rc0 + 32 * j + 16 * (grp & 1) + 4 * (sl & 3);
+      foff[j] = (uint32_t)(krow * ROWB + (((col >> 3) ^ swz(krow)) << 4) + ((col & 7) << 1));
+    }
+  }
+  __device__ __forceinline__ void read(Frag<T>& f, const lds_u8* st, int g, int j) const {
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + foff[j] + 16 * g * ROWB));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + foff[j] + (16 * g + 4) * ROWB));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    f.v = u32x4{ua[0], ua[1], ub[0], ub[1]};
+  }
+};
 
 // acc[fm][fn] += sum over the K steps of A_tile * B_tile^T, as mainloop()
 // (same step/offset conventions), both operands K-major and DMA-fed.
@@ -552,12 +627,12 @@ __device__ __forceinline__ void lds_frag_at(Frag<float>& f, const lds_u8* st, ui
 // group, and part p in group p-1 of the following step, each spread one or two
 // instructions between MFMAs so the issue never stalls the matrix core.
 // Steps past the end (the count is padded to even) read zeros.
-template <class C, int SPB, int NPARTS = (C::KGROUPS > 2 ? 3 : 1)>
+template <class C, int SPB, bool B_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1)>
 __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const Operand& A, const Operand& B,
                                              int nsteps, const uint16_t* blocks, void* smem) {
   using T = typename C::T;
   using TA = DmaTile<C, C::BM>;
-  using TB = DmaTile<C, C::BN>;
+  using TB = std::conditional_t<B_MN, DmaTileMN<C, C::BN>, DmaTile<C, C::BN>>;
   constexpr int KG = C::KGROUPS;
   static_assert(KG % 2 == 0, "fragment buffers alternate per K group");
   static_assert(NPARTS >= 1 && NPARTS < KG, "the last DMA part must precede the wait");
@@ -596,21 +671,12 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   wait_vmcnt<P0>();  // step 0 has landed
   __syncthreads();
 
-  uint32_t alo[KG], ahi[KG], blo[KG], bhi[KG];
-#pragma unroll
-  for (int g = 0; g < KG; ++g) {
-    TA::frag_off(wm * C::WM, g, alo[g], ahi[g]);
-    TB::frag_off(wn * C::WN, g, blo[g], bhi[g]);
-    blo[g] += TA::BYTES;
-    bhi[g] += TA::BYTES;
-  }
+  ta.frag_init(wm * C::WM);
+  tb.frag_init(wn * C::WN);
   Frag<T> fa[2][C::FM], fb[2][C::FN];
   auto read_one = [&](int buf, const lds_u8* st, int g, int q) {
-    if (q < C::FM)
-      lds_frag_at(fa[buf][q], st, alo[g] + q * 32 * TA::ROWB, ahi[g] + q * 32 * TA::ROWB);
-    else
-      lds_frag_at(fb[buf][q - C::FM], st, blo[g] + (q - C::FM) * 32 * TB::ROWB,
-                  bhi[g] + (q - C::FM) * 32 * TB::ROWB);
+    if (q < C::FM) ta.read(fa[buf][q], st, g, q);
+    else tb.read(fb[buf][q - C::FM], st + TA::BYTES, g, q - C::FM);
   };
 #pragma unroll
   for (int q = 0; q < C::FM + C::FN; ++q) read_one(0, base, 0, q);

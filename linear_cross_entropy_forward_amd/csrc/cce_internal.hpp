@@ -37,6 +37,8 @@ constexpr size_t kDefaultGBudget = size_t(512) << 20;
 // Extra elements per row of the transposed gradient tiles (row pitch
 // Npad + kGtPad).  Zero: measured no faster with a padded pitch.
 constexpr int kGtPad = 0;
+// Work-groups that run at once with one per CU (256 CUs).
+constexpr int kWaveSlots = 256;
 
 struct Problem {
   const void* e;

@@ -654,7 +654,10 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     int cnvb, int tiles_n, int tiles_d, int splits, int Vc, size_t g_bytes, float* __restrict__ dE,
     float* __restrict__ dE_part, int accumulate, int atomic) {
   using T = typename C::T;
-  __shared__ __attribute__((aligned(16))) T smem[C::LDS_BYTES / sizeof(T)];
+  // bf16: LDS-DMA main loop (C fragments through transposing reads); fp32:
+  // register-staged main loop (no 32-bit transposing read exists)
+  constexpr bool kDma = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kDma ? C::LDS_DMA_BYTES : C::LDS_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
   const int total = tiles_n * tiles_d * splits;
   const int tile = xcd_remap(blockIdx.x, total);
@@ -678,17 +681,21 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   constexpr int SPB = kTileV / C::BK;
+  auto loop = [&](const Operand& a, const Operand& b, const uint16_t* bl) {
+    if constexpr (kDma) mainloop_dma<C, SPB, true>(acc, a, b, nk * SPB, bl, smem);
+    else mainloop<C, false, true, SPB>(acc, a, b, nk * SPB, bl, (T*)smem);
+  };
   // every vocab block of the split kept: contiguous K from the split's start
   if (nk == vb_hi - vb_lo) {
-    A.r = make_rsrc(G + (size_t)n0 * Vc + (size_t)vb_lo * kTileV,
-                    g_bytes - ((size_t)n0 * Vc + (size_t)vb_lo * kTileV) * sizeof(T));
-    A.kdim = clen - vb_lo * kTileV;
-    B.r = make_rsrc(c + ((size_t)cv0 + (size_t)vb_lo * kTileV) * D + d0,
-                    ((uint64_t)(V - cv0 - vb_lo * kTileV) * D - d0) * sizeof(T));
-    B.kdim = A.kdim;
-    mainloop<C, false, true, SPB>(acc, A, B, nk * SPB, nullptr, smem);
+    const size_t ka = (size_t)vb_lo * kTileV;
+    const Operand A1 = make_operand(G + (size_t)n0 * Vc + ka, g_bytes - ((size_t)n0 * Vc + ka) * sizeof(T),
+                                    (uint32_t)Vc, min(C::BM, N - n0), clen - (int)ka);
+    const Operand B1 = make_operand(c + ((size_t)cv0 + ka) * D + d0,
+                                    ((uint64_t)(V - cv0 - (int64_t)ka) * D - d0) * sizeof(T), (uint32_t)D,
+                                    min(C::BN, D - d0), clen - (int)ka);
+    loop(A1, B1, nullptr);
   } else {
-    mainloop<C, false, true, SPB>(acc, A, B, nk * SPB, blocks, smem);
+    loop(A, B, blocks);
   }
 
   if (nk == 0 && (accumulate || atomic)) return;  // nothing to add
@@ -696,31 +703,37 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   float* out = (atomic || s == 0) ? dE : dE_part + (size_t)(s - 1) * N * D;
   float* ob = out + (size_t)n0 * D;
   rsrc_t ro = make_rsrc(ob, (uint64_t)(N - n0) * D * sizeof(float));
+  auto offset = [&](int fm, int fn, int r) -> uint32_t {
+    const int d = d0 + am.colj(fn), nr = am.row(fm, r);
+    return (d < D && n0 + nr < N) ? ((uint32_t)nr * (uint32_t)D + (uint32_t)d) * 4u : kOOB;
+  };
+  if (atomic) {
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
+    for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn) {
-      const int d = d0 + am.colj(fn);
-      uint32_t off[16];
+      for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int nr = am.row(fm, r);
-        off[r] = (d < D && n0 + nr < N) ? ((uint32_t)nr * (uint32_t)D + (uint32_t)d) * 4u : kOOB;
-      }
-      f32x16 v = acc[fm][fn];
-      if (atomic) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (off[r] != kOOB) unsafeAtomicAdd(ob + off[r] / 4u, v[r]);
-      } else {
-        if (accumulate) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] += ldf(ro, off[r]);
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t o = offset(fm, fn, r);
+          if (o != kOOB) unsafeAtomicAdd(ob + o / 4u, acc[fm][fn][r]);
         }
+    return;
+  }
+  // Accumulating into the previous chunks' sum: the old values of a row of
+  // FN blocks are fetched together (one memory round trip per fm, not per
+  // block), then added and stored.
 #pragma unroll
-        for (int r = 0; r < 16; ++r) stf(ro, off[r], v[r]);
-      }
-    }
+  for (int fm = 0; fm < C::FM; ++fm) {
+    float old[C::FN][16];
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) old[fn][r] = accumulate ? ldf(ro, offset(fm, fn, r)) : 0.f;
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) stf(ro, offset(fm, fn, r), acc[fm][fn][r] + old[fn][r]);
+  }
 }
 
 // dE += dE_part[0] + dE_part[1] + ... in that order (deterministic).
