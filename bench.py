@@ -33,10 +33,36 @@ PEAK_HBM_GBS = 8000.0
 KERNELS = ["fwd_tile", "rows", "reduce", "bwd_prep", "filter", "grad_tile", "dC_gemm", "dE_gemm", "dE_reduce",
            "fill_zero", "transpose_e"]
 MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
-# Measured HBM traffic per launch of the dominant kernel (rocprofv3 FETCH_SIZE
-# + WRITE_SIZE, scaled by a plain-copy calibration).  Set only when the
-# counters were taken on the current kernel source.
-TRAFFIC_BYTES: dict = {}
+# Measured memory traffic per launch (bytes past L2: rocprofv3 FETCH_SIZE x 2.0
+# + WRITE_SIZE x 1.0, the factors a 1 GiB device copy calibrates in the same
+# runs), averaged over a step's launches.  Valid only for the kernel sources
+# they were taken on: reported when the source hash matches, null otherwise.
+TRAFFIC = {
+    "source_sha256": "a6117a3be1a97a98bf52ea65acdad967cd2b879fa2b16c82f12ed3a87f994b9e",
+    "workload": "llama8b",
+    "bytes_per_launch": {
+        "fwd_tile": 9154.1e6, "grad_tile": 2199.5e6, "dC_gemm": 2293.6e6, "dE_gemm": 1811.0e6,
+        "rows": 121.5e6, "filter": 3.3e6, "transpose_e": 67.1e6,
+    },
+}
+
+
+def source_sha256() -> str:
+    import hashlib
+    d = os.path.join(ROOT, "linear_cross_entropy_forward_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel: str, workload: str):
+    if TRAFFIC["workload"] != workload or TRAFFIC["source_sha256"] != source_sha256():
+        return None
+    return TRAFFIC["bytes_per_launch"].get(kernel)
 
 
 def parse():
@@ -246,19 +272,20 @@ def main():
         d = dict(d)
         d["tflops"] = fl / (d["avg_ms"] * 1e-3) / 1e12 if fl else None
         d["gbs"] = by / (d["avg_ms"] * 1e-3) / 1e9 if by else None
+        d["traffic_bytes"] = traffic_for(name, args.workload)
         kernels[name] = d
     dom = max(per, key=lambda k: per[k]["ms_per_step"])
     fl, by = algorithmic(dom, N, D, V, es, nVB, chunk_lens)
     if dom in MFMA_KERNELS:
         ach = fl / (per[dom]["avg_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
-                "traffic": TRAFFIC_BYTES.get(dom), "kernel": dom, "avg_launch_ms": per[dom]["avg_ms"],
-                "algorithmic_flops_per_launch": fl}
+                "traffic": traffic_for(dom, args.workload), "kernel": dom,
+                "avg_launch_ms": per[dom]["avg_ms"], "algorithmic_flops_per_launch": fl}
     else:
         ach = by / (per[dom]["avg_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                "traffic": TRAFFIC_BYTES.get(dom), "kernel": dom, "avg_launch_ms": per[dom]["avg_ms"],
-                "algorithmic_bytes_per_launch": by}
+                "traffic": traffic_for(dom, args.workload), "kernel": dom,
+                "avg_launch_ms": per[dom]["avg_ms"], "algorithmic_bytes_per_launch": by}
 
     # device memory this path needs beyond its inputs: workspace, loss/LSE and
     # the two gradient outputs
