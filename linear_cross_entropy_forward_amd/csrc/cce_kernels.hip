@@ -480,25 +480,36 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   // tile-local) of one token column at a time.  Rows of the last tile past V
   // are zeroed (their logits read zero rows of c); all other tiles take the
   // branch-free path.
+  // A column's target row lies in this wave's 128 rows for few tiles (about
+  // 128 / V of them per column): a wave-uniform test skips the one-hot compare
+  // everywhere else.
   auto compute = [&](auto ragged, auto&& sink) {
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
+      auto body = [&](auto with_target) {
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm) {
+        for (int fm = 0; fm < C::FM; ++fm) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float g[4];
-          const int rl = am.row(fm, 4 * q);
+          for (int q = 0; q < 4; ++q) {
+            float g[4];
+            const int rl = am.row(fm, 4 * q);
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float p = fast_exp2(__builtin_fmaf(acc[fm][fn][4 * q + u], kLog2e, -lsel[fn]));
-            const float tsc = trow[fn] == fm * 32 + 8 * q + u ? sc[fn] : 0.f;
-            g[u] = __builtin_fmaf(p, sc[fn], -tsc);
-            if constexpr (decltype(ragged)::value) g[u] = v0 + rl + u < V ? g[u] : 0.f;
+            for (int u = 0; u < 4; ++u) {
+              const float p = fast_exp2(__builtin_fmaf(acc[fm][fn][4 * q + u], kLog2e, -lsel[fn]));
+              if constexpr (decltype(with_target)::value) {
+                const float tsc = trow[fn] == fm * 32 + 8 * q + u ? sc[fn] : 0.f;
+                g[u] = __builtin_fmaf(p, sc[fn], -tsc);
+              } else {
+                g[u] = p * sc[fn];
+              }
+              if constexpr (decltype(ragged)::value) g[u] = v0 + rl + u < V ? g[u] : 0.f;
+            }
+            sink(fn, fm, q, rl, g);
           }
-          sink(fn, fm, q, rl, g);
         }
-      }
+      };
+      if (__builtin_amdgcn_ballot_w64(trow[fn] >= 0 && trow[fn] < C::WM) != 0) body(std::true_type{});
+      else body(std::false_type{});
     }
   };
   auto run = [&](auto&& sink) {
@@ -513,8 +524,8 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     // pieces over 64 rows).  A staging tile holds 256 rows of 512 bytes;
     // 16-byte chunk j of row r sits in slot j ^ f(r).  Any f keeps the row
     // drains conflict free; f is chosen per pass for its writes: pass 1 writes
-    // one chunk of 32 consecutive rows (f = r % 32), pass 2 two chunks of
-    // rows R..R+3 from each lane quad (f swaps the two low bit pairs of r).
+    // one chunk of 32 consecutive rows (f = r % 32), pass 2 four chunks of
+    // one row per half-wave (f swaps the two low bit pairs of r).
     static_assert(C::BM == 256 && C::BN == 256 && C::LDS_DMA_BYTES >= 256 * 512, "tile staging");
     lds_u8* tile = (lds_u8*)smem;
     auto slot = [](int r, int col, auto pass2) -> uint32_t {
@@ -544,20 +555,19 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     __syncthreads();
     drain(rg, (uint32_t)Vc, (uint32_t)n0, (uint32_t)vl0, std::false_type{});
     __syncthreads();
-    // pass 2: quad transposes turn each lane's four vocab rows of one token
-    // into four tokens of one vocab row; [vocab][token] -> G^T rows
-    const int k = lane & 3;
+    // pass 2: [vocab][token] -> G^T rows, one 16-bit store per element (the
+    // 32 lanes of a half-wave write 64 consecutive bytes of one vocab row)
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t d0 = pk[fn][fm][q][0], d1 = pk[fn][fm][q][1];
-          quad_transpose16(d0, d1);
-          *(__attribute__((address_space(3))) u32x2*)(
-              tile + slot(am.row(fm, 4 * q) + k, am.colj(fn) & ~3, std::true_type{})) = u32x2{d0, d1};
-        }
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            *(__attribute__((address_space(3))) uint16_t*)(
+                tile + slot(am.row(fm, 4 * q) + u, am.colj(fn), std::true_type{})) =
+                (uint16_t)(pk[fn][fm][q][u >> 1] >> (16 * (u & 1)));
     __syncthreads();
     drain(rgt, (uint32_t)gt_ld, (uint32_t)vl0, (uint32_t)n0, std::true_type{});
   } else {
