@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-materialized", action="store_true",
                     help="skip the materialised-logits PyTorch comparison")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the compact figures for the other workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run one plain device copy of BYTES first (HBM-counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -159,6 +161,107 @@ def materialized(e, c, t, reduction, steps):
     del ec, cc
     torch.cuda.empty_cache()
     return s0.elapsed_time(s1) / steps, peak
+
+
+def hipblaslt_gemm_tflops(c, e, reps=5):
+    """torch.mm (hipBLASLt) on the forward contraction's shape, c [V, D] x e^T:
+    a practical MFMA ceiling for the same M, N, K."""
+    import torch
+    et = e.t().contiguous()
+    out = torch.mm(c, et)
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        torch.mm(c, et, out=out)
+    s1.record()
+    torch.cuda.synchronize()
+    ms = s0.elapsed_time(s1) / reps
+    del out, et
+    return 2.0 * c.shape[0] * c.shape[1] * e.shape[0] / (ms * 1e-3) / 1e12
+
+
+def config_summary(name, steps=5, warmup=2, materialized_too=True):
+    """Compact forward / forward+backward figures for one workload (defaults:
+    filter on, deterministic, the workload's own reduction)."""
+    import torch
+    import workloads as W
+    import linear_cross_entropy_forward_amd as M
+    w = W.WORKLOADS[name]
+    inp = W.generate(w)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    e = torch.from_numpy(inp["e"]).to(tdt).to(dev)
+    c = torch.from_numpy(inp["c"]).to(tdt).to(dev)
+    t = torch.from_numpy(inp["targets"]).to(dev)
+    N, D = e.shape
+    V = c.shape[0]
+    n_valid = max(1, int((inp["targets"] != -100).sum()))
+    del inp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    base = torch.cuda.memory_allocated()
+    ws = torch.empty(M.workspace_size(N, D, V, tdt), dtype=torch.uint8, device=dev)
+    red = {"none": 0, "sum": 1, "mean": 2}[w.reduction]
+    loss = torch.empty(N if red == 0 else 1, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    nv = torch.empty(1, dtype=torch.int32, device=dev)
+    g = torch.full((N,) if red == 0 else (1,), 1.0 / n_valid if red == 0 else 1.0, dtype=torch.float32,
+                   device=dev)
+    dE = torch.empty((N, D), dtype=torch.float32, device=dev)
+    dC = torch.empty((V, D), dtype=torch.float32, device=dev)
+    extra = torch.cuda.memory_allocated() - base
+    L = M.lib()
+    dcode = 0 if w.dtype == "bf16" else 1
+    st = torch.cuda.current_stream()
+
+    def fwd():
+        r = L.cce_forward(e.data_ptr(), c.data_ptr(), t.data_ptr(), N, D, V, dcode, -100, red, 0.0,
+                          loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(), ws.numel(), st.cuda_stream)
+        if r:
+            raise RuntimeError(f"cce_forward failed: {r}")
+
+    def step():
+        fwd()
+        r = L.cce_backward(e.data_ptr(), c.data_ptr(), t.data_ptr(), N, D, V, dcode, -100, red, 0.0,
+                           lse.data_ptr(), g.data_ptr(), 1, 0, 0, dE.data_ptr(), dC.data_ptr(), ws.data_ptr(),
+                           ws.numel(), st.cuda_stream)
+        if r:
+            raise RuntimeError(f"cce_backward failed: {r}")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(steps):
+            fn()
+        b.record(st)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    step_ms = timed(step)
+    fwd_ms = timed(fwd)
+    stats = M.read_stats(ws, N, V)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    eff = 8.0 * N * V * D / (step_ms * 1e-3) / 1e12
+    out = {"N": N, "D": D, "V": V, "dtype": w.dtype, "reduction": w.reduction, "fwd_ms": fwd_ms,
+           "fwd_tokens_per_s": N / (fwd_ms * 1e-3), "step_ms": step_ms, "tokens_per_s": N / (step_ms * 1e-3),
+           "tflops_effective": eff, "pct_of_peak": 100.0 * eff / peak,
+           "tiles_skipped_frac": 1.0 - stats["tiles_kept"] / max(1, stats["tiles_total"]),
+           "extra_hbm_bytes": int(extra)}
+    if w.dtype == "bf16":
+        out["hipblaslt_fwd_gemm_tflops"] = hipblaslt_gemm_tflops(c, e)
+    del ws, loss, lse, nv, g, dE, dC
+    torch.cuda.empty_cache()
+    if materialized_too:
+        mat_ms, mat_peak = materialized(e, c, t, w.reduction, max(1, min(steps, 3)))
+        out["materialized_step_ms"] = mat_ms
+        out["materialized_peak_extra_bytes"] = int(mat_peak)
+    del e, c, t
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -290,6 +393,8 @@ def main():
     # device memory this path needs beyond its inputs: workspace, loss/LSE and
     # the two gradient outputs
     extra_bytes = torch.cuda.memory_allocated() - base_alloc
+    ws_bytes = ws.numel()
+    hip_tf = hipblaslt_gemm_tflops(c, e) if dt_name == "bf16" else None
     mat = None
     if not args.no_materialized:
         del dE, dC
@@ -297,6 +402,16 @@ def main():
         mat_ms, mat_peak = materialized(e, c, t, reduction, max(1, min(args.steps, 3)))
         mat = {"ms_per_step": mat_ms, "tokens_per_s": N / (mat_ms * 1e-3), "peak_extra_bytes": int(mat_peak),
                "what": "PyTorch: fp32 logits = e @ c^T, F.cross_entropy(mean), backward"}
+
+    configs = None
+    if not args.no_configs:
+        del e, c, t, ws, loss, lse, nv, g
+        dE = dC = None
+        torch.cuda.empty_cache()
+        configs = {}
+        for name in ("tiny", "llama1b", "gemma2b", "gemma2b_cal", "long8b", "long8b_cal"):
+            if name != args.workload:
+                configs[name] = config_summary(name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -323,11 +438,13 @@ def main():
         "fwd_ms": fwd_ms,
         "fwd_tokens_per_s": N / (fwd_ms * 1e-3),
         "tiles_kept_frac": stats["tiles_kept"] / max(1, stats["tiles_total"]),
-        "workspace_bytes": ws.numel(),
+        "workspace_bytes": ws_bytes,
         "extra_hbm_bytes": int(extra_bytes),
         "loss_path_overhead_bytes": int(N * nVB * 8 + N * 8),
         "materialized_logits_fp32_bytes": N * V * 4,
         "materialized_baseline": mat,
+        "hipblaslt_fwd_gemm_tflops": hip_tf,
+        "other_workloads": configs,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
