@@ -9,9 +9,11 @@ logits, and is slow on purpose.
 What is computed (all in float64, from operands passed in exactly as the GPU
 sees them: bf16 values upcast exactly, or fp32):
 
-  Z = E C^T                       logits, materialised here only
+  Z = E C^T (+ b)                 logits, materialised here only
                                   (mlx-cross-entropy README, "Usage": the
-                                  standard path that forms hidden @ classifier.T)
+                                  standard path that forms hidden @ classifier.T;
+                                  the optional classifier bias b [V] of the
+                                  README "API" table is added to every row)
   LSE_i = m_i + ln sum_j exp(Z_ij - m_i),  m_i = max_j Z_ij
                                   (tirogla "Loss functions", "How it works"
                                   step 1: log-sum-exp with max subtraction)
@@ -28,7 +30,8 @@ sees them: bf16 values upcast exactly, or fp32):
   G = (softmax(Z) - onehot(y)) * scale_i
                                   (tirogla step 2: fused softmax+CE gradient
                                   p - y)
-  dE = G C,  dC = G^T E           (chain rule through Z = E C^T)
+  dE = G C,  dC = G^T E,  db = G^T 1
+                                  (chain rule through Z = E C^T + 1 b^T)
   scale_i = g / max(n_valid,1) (mean), g (sum), g_i (none); 0 on ignored rows.
 
 Gradient filtering (README "How it works" item 2; Wijmans et al. abstract:
@@ -67,9 +70,12 @@ def valid_rows(targets, V: int, ignore_index: int = -100) -> np.ndarray:
     return valid
 
 
-def logits(e, c) -> np.ndarray:
-    """Z = E C^T in float64 (the materialised logit matrix)."""
-    return _f64(e) @ _f64(c).T
+def logits(e, c, bias=None) -> np.ndarray:
+    """Z = E C^T (+ b on every row) in float64 (the materialised logit matrix)."""
+    z = _f64(e) @ _f64(c).T
+    if bias is not None:
+        z += _f64(bias)[None, :]
+    return z
 
 
 def row_logsumexp(z: np.ndarray) -> np.ndarray:
@@ -99,7 +105,7 @@ def reduce_loss(nll: np.ndarray, n_valid: int, reduction: str) -> np.ndarray:
 
 
 def forward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
-            rows=None) -> Forward:
+            rows=None, bias=None) -> Forward:
     """Loss and per-row LSE.  `rows` restricts the work to a subset of rows
     (then `loss` is the reduction over that subset only and n_valid counts it)."""
     e = _f64(e)
@@ -112,7 +118,7 @@ def forward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
     nll = np.zeros(len(idx))
     for s in range(0, len(idx), _ROW_CHUNK):
         sl = slice(s, s + _ROW_CHUNK)
-        z = logits(e[idx[sl]], c)
+        z = logits(e[idx[sl]], c, bias)
         lse[sl] = row_logsumexp(z)
         v = valid[sl]
         r = np.nonzero(v)[0]
@@ -147,7 +153,7 @@ def tile_row_max(z: np.ndarray, Bv: int) -> np.ndarray:
 
 
 def filter_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100,
-                lse=None) -> np.ndarray:
+                lse=None, bias=None) -> np.ndarray:
     """Keep map [ceil(N/Bn), ceil(V/Bv)] of (row block, vocab block) tiles of G.
 
     Kept iff some valid row i of the block has max_j softmax_ij >= 2^-12 on the
@@ -163,7 +169,7 @@ def filter_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100,
     keep = np.zeros((nb, nvb), dtype=bool)
     for b in range(nb):
         r0, r1 = b * Bn, min(N, (b + 1) * Bn)
-        z = logits(e[r0:r1], c)
+        z = logits(e[r0:r1], c, bias)
         l = row_logsumexp(z) if lse is None else _f64(lse)[r0:r1]
         tm = tile_row_max(z, Bv) - l[:, None]          # log of the tile's max softmax
         v = valid[r0:r1]
@@ -188,12 +194,13 @@ def softmax_grad_rows(z: np.ndarray, lse: np.ndarray, t: np.ndarray, scale: np.n
 class Backward:
     dE: np.ndarray
     dC: np.ndarray
+    db: np.ndarray          # [V] column sums of G (the bias gradient)
 
 
 def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
-             grad_loss=1.0, keep=None, tile=None) -> Backward:
-    """dE = G C and dC = G^T E.  With `keep` (a filter_keep map for `tile` =
-    (Bn, Bv)) G is zeroed on the dropped tiles first."""
+             grad_loss=1.0, keep=None, tile=None, bias=None) -> Backward:
+    """dE = G C, dC = G^T E and db = G^T 1.  With `keep` (a filter_keep map for
+    `tile` = (Bn, Bv)) G is zeroed on the dropped tiles first."""
     e = _f64(e)
     c = _f64(c)
     t = np.asarray(targets, dtype=np.int64)
@@ -202,10 +209,11 @@ def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
     scale = grad_scale(valid, reduction, grad_loss)
     dE = np.zeros_like(e)
     dC = np.zeros_like(c)
+    db = np.zeros(V)
     chunk = _ROW_CHUNK if keep is None else tile[0]
     for s in range(0, N, chunk):
         sl = slice(s, min(N, s + chunk))
-        z = logits(e[sl], c)
+        z = logits(e[sl], c, bias)
         lse = row_logsumexp(z)
         g = softmax_grad_rows(z, lse, t[sl], scale[sl], valid[sl])
         if keep is not None:
@@ -214,7 +222,8 @@ def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
             g[:, ~colmask] = 0.0
         dE[sl] = g @ c
         dC += g.T @ e[sl]
-    return Backward(dE, dC)
+        db += g.sum(axis=0)
+    return Backward(dE, dC, db)
 
 
 # ---------------------------------------------------------------------------
@@ -222,17 +231,17 @@ def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
 # output rows, so full-size checks stay within seconds to a minute.
 # ---------------------------------------------------------------------------
 
-def lse_all(e, c, chunk: int = _ROW_CHUNK) -> np.ndarray:
+def lse_all(e, c, chunk: int = _ROW_CHUNK, bias=None) -> np.ndarray:
     """LSE of every row (the full materialised pass, row chunk by row chunk)."""
     e = _f64(e)
     c = _f64(c)
     out = np.empty(e.shape[0])
     for s in range(0, e.shape[0], chunk):
-        out[s:s + chunk] = row_logsumexp(logits(e[s:s + chunk], c))
+        out[s:s + chunk] = row_logsumexp(logits(e[s:s + chunk], c, bias))
     return out
 
 
-def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100):
+def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias=None):
     """One pass over all row blocks giving LSE [N] and the filter keep map."""
     e = _f64(e)
     c = _f64(c)
@@ -244,7 +253,7 @@ def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100):
     lse = np.empty(N)
     for b in range(nb):
         r0, r1 = b * Bn, min(N, (b + 1) * Bn)
-        z = logits(e[r0:r1], c)
+        z = logits(e[r0:r1], c, bias)
         l = row_logsumexp(z)
         lse[r0:r1] = l
         tm = tile_row_max(z, Bv) - l[:, None]
@@ -256,7 +265,7 @@ def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100):
 
 
 def dE_rows(e, c, targets, rows, ignore_index: int = -100, reduction: str = "mean",
-            grad_loss=1.0, n_valid: int | None = None, keep=None, tile=None) -> np.ndarray:
+            grad_loss=1.0, n_valid: int | None = None, keep=None, tile=None, bias=None) -> np.ndarray:
     """dE for selected rows: row i of G C needs only row i of Z.  For mean,
     n_valid is the whole batch's count (pass it in); for none, grad_loss is [N]."""
     e = _f64(e)
@@ -271,7 +280,7 @@ def dE_rows(e, c, targets, rows, ignore_index: int = -100, reduction: str = "mea
         scale = np.where(valid_all[rows], float(grad_loss) / max(n_valid, 1), 0.0)
     else:
         scale = grad_scale(valid_all, reduction, grad_loss)[rows]
-    z = logits(e[rows], c)
+    z = logits(e[rows], c, bias)
     lse = row_logsumexp(z)
     g = softmax_grad_rows(z, lse, t[rows], scale, valid_all[rows])
     if keep is not None:
@@ -282,10 +291,10 @@ def dE_rows(e, c, targets, rows, ignore_index: int = -100, reduction: str = "mea
     return g @ c
 
 
-def dC_rows(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction: str = "mean",
-            grad_loss=1.0, keep=None, tile=None) -> np.ndarray:
-    """dC for selected vocabulary rows j: dC_j = sum_i G_ij e_i, which needs
-    column j of Z for all rows and every row's LSE (pass the oracle's own)."""
+def G_columns(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction: str = "mean",
+              grad_loss=1.0, keep=None, tile=None, bias=None) -> np.ndarray:
+    """Columns j of G for selected vocabulary ids, [N, k]: they need column j of
+    Z for all rows and every row's LSE (pass the oracle's own)."""
     e = _f64(e)
     c = _f64(c)
     t = np.asarray(targets, dtype=np.int64)
@@ -294,6 +303,8 @@ def dC_rows(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction: 
     valid = valid_rows(t, V, ignore_index)
     scale = grad_scale(valid, reduction, grad_loss)
     zc = e @ c[vocab_ids].T                              # [N, k] = Z[:, vocab_ids]
+    if bias is not None:
+        zc += _f64(bias)[vocab_ids][None, :]
     g = np.exp(zc - _f64(lse)[:, None])
     g -= (t[:, None] == vocab_ids[None, :])
     g *= scale[:, None]
@@ -302,4 +313,18 @@ def dC_rows(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction: 
         Bn, Bv = tile
         rowblk = np.arange(e.shape[0]) // Bn
         g *= keep[rowblk][:, vocab_ids // Bv]
-    return g.T @ e
+    return g
+
+
+def db_rows(e, c, targets, vocab_ids, lse, **kw) -> np.ndarray:
+    """db for selected vocabulary ids: db_j = sum_i G_ij."""
+    return G_columns(e, c, targets, vocab_ids, lse, **kw).sum(axis=0)
+
+
+def dC_rows(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction: str = "mean",
+            grad_loss=1.0, keep=None, tile=None, bias=None) -> np.ndarray:
+    """dC for selected vocabulary rows j: dC_j = sum_i G_ij e_i, which needs
+    column j of Z for all rows and every row's LSE (pass the oracle's own)."""
+    g = G_columns(e, c, targets, vocab_ids, lse, ignore_index=ignore_index, reduction=reduction,
+                  grad_loss=grad_loss, keep=keep, tile=tile, bias=bias)
+    return g.T @ _f64(e)

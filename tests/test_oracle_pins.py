@@ -374,3 +374,126 @@ def test_sampled_forms_match_full():
                        rtol=1e-12, atol=1e-15)
     assert np.allclose(O.dC_rows(e, c, t, [2, 33], lse, keep=keep, tile=(Bn, Bv)), bf.dC[[2, 33]],
                        rtol=1e-12, atol=1e-15)
+
+
+# --------------------------------------------------------------------------- classifier bias
+# The bias b [V] (README "API": classifier bias) is added to every row of the
+# logits; its gradient is db = G^T 1.
+
+
+def test_bias_closed_form_zero_classifier():
+    """c = 0 and b_j = ln(j + 1): every row's logits are b, so
+    sum_j exp(b_j) = V (V + 1) / 2 exactly, LSE = ln(V (V + 1) / 2),
+    loss_i = LSE - ln(y_i + 1), p_j = (j + 1) / (V (V + 1) / 2), dE = 0 and
+    db_j = sum_i scale_i (p_j - [y_i = j])."""
+    N, D, V = 6, 3, 9
+    g = np.random.default_rng(41)
+    e = g.standard_normal((N, D))
+    c = np.zeros((V, D))
+    b = np.log(np.arange(1, V + 1, dtype=np.float64))
+    t = np.array([0, 8, 3, -100, 3, 5])
+    tot = V * (V + 1) / 2.0
+    f = O.forward(e, c, t, reduction="sum", bias=b)
+    assert np.allclose(f.lse, math.log(tot), rtol=0, atol=1e-13)
+    want = sum(math.log(tot) - math.log(y + 1) for y in t if y != -100)
+    assert abs(float(f.loss) - want) < 1e-12
+    bw = O.backward(e, c, t, reduction="sum", bias=b)
+    assert not bw.dE.any()
+    p = np.arange(1, V + 1) / tot
+    db = np.zeros(V)
+    for y in t:
+        if y != -100:
+            db += p
+            db[y] -= 1.0
+    assert np.allclose(bw.db, db, rtol=1e-12, atol=1e-14)
+
+
+def test_bias_as_extra_feature():
+    """(e, c, b) equals the bias-free problem with e' = [e, 1], c' = [c, b]:
+    same loss and LSE, the same dE and dC in the first D columns, and db is
+    the extra column of dC'."""
+    g = np.random.default_rng(42)
+    N, D, V = 9, 5, 13
+    e, c = g.standard_normal((N, D)), g.standard_normal((V, D))
+    b = g.standard_normal(V) * 2.0
+    t = g.integers(0, V, N)
+    t[4] = -100
+    ea = np.concatenate([e, np.ones((N, 1))], axis=1)
+    ca = np.concatenate([c, b[:, None]], axis=1)
+    for red in ("mean", "none"):
+        gl = g.standard_normal(N) if red == "none" else 0.7
+        f1 = O.forward(e, c, t, reduction=red, bias=b)
+        f2 = O.forward(ea, ca, t, reduction=red)
+        assert np.allclose(f1.lse, f2.lse, rtol=1e-13) and np.allclose(f1.loss, f2.loss, rtol=1e-13)
+        b1 = O.backward(e, c, t, reduction=red, grad_loss=gl, bias=b)
+        b2 = O.backward(ea, ca, t, reduction=red, grad_loss=gl)
+        assert np.allclose(b1.dE, b2.dE[:, :D], rtol=1e-12, atol=1e-15)
+        assert np.allclose(b1.dC, b2.dC[:, :D], rtol=1e-12, atol=1e-15)
+        assert np.allclose(b1.db, b2.dC[:, D], rtol=1e-12, atol=1e-15)
+
+
+def test_bias_constant_shift_and_sum():
+    """A constant bias shifts every LSE by the constant and changes neither the
+    loss nor any gradient; db sums to zero (each valid row of G sums to 0)."""
+    e, c, t = _rand(43, 7, 4, 10)
+    t[2] = -100
+    f0 = O.forward(e, c, t, reduction="none")
+    fk = O.forward(e, c, t, reduction="none", bias=np.full(10, 3.25))
+    assert np.allclose(fk.lse, f0.lse + 3.25, rtol=1e-14)
+    assert np.allclose(fk.nll, f0.nll, rtol=1e-12, atol=1e-14)
+    b0 = O.backward(e, c, t, reduction="mean")
+    bk = O.backward(e, c, t, reduction="mean", bias=np.full(10, 3.25))
+    assert np.allclose(bk.dE, b0.dE, rtol=1e-12, atol=1e-15) and np.allclose(bk.dC, b0.dC, rtol=1e-12, atol=1e-15)
+    bb = O.backward(e, c, t, reduction="mean", bias=np.linspace(-2, 2, 10))
+    assert abs(bb.db.sum()) < 1e-14
+
+
+def test_bias_finite_differences():
+    g = np.random.default_rng(44)
+    N, D, V = 5, 3, 8
+    e, c = g.standard_normal((N, D)), g.standard_normal((V, D))
+    b = g.standard_normal(V)
+    t = g.integers(0, V, N)
+    t[0] = -100
+    bw = O.backward(e, c, t, reduction="mean", bias=b)
+    h = 1e-6
+    for j in range(V):
+        bp, bm = b.copy(), b.copy()
+        bp[j] += h
+        bm[j] -= h
+        fd = (float(O.forward(e, c, t, reduction="mean", bias=bp).loss)
+              - float(O.forward(e, c, t, reduction="mean", bias=bm).loss)) / (2 * h)
+        assert abs(fd - bw.db[j]) < 1e-8 + 1e-6 * abs(fd), (j, fd, bw.db[j])
+
+
+def test_bias_brute_force_filter_and_sampled():
+    """Filtering with a bias: a strongly negative bias on one vocab block drops
+    its tiles except where a target lies; the keep map matches loops over the
+    biased softmax; sampled db / dC / dE forms match the full backward."""
+    g = np.random.default_rng(45)
+    N, D, V, Bn, Bv = 10, 4, 24, 5, 8
+    e, c = g.standard_normal((N, D)), g.standard_normal((V, D)) * 0.5
+    b = np.zeros(V)
+    b[8:16] = -40.0
+    t = g.choice(np.r_[0:8, 16:24], N)        # targets outside the suppressed block ...
+    t[1] = 9                                  # ... except one
+    keep = O.filter_keep(e, c, t, Bn, Bv, bias=b)
+    z = e @ c.T + b[None, :]
+    want = np.zeros_like(keep)
+    for i in range(N):
+        den = sum(math.exp(z[i, j]) for j in range(V))
+        for j in range(V):
+            if math.exp(z[i, j]) / den >= 2.0 ** -12 or j == t[i]:
+                want[i // Bn, j // Bv] = True
+    assert np.array_equal(keep, want)
+    assert keep[0, 1] and not keep[1, 1]      # block 1 kept only for row block 0 (target 9)
+    lse, keep2 = O.lse_and_keep(e, c, t, Bn, Bv, bias=b)
+    assert np.array_equal(keep, keep2)
+    full = O.backward(e, c, t, reduction="sum", bias=b, keep=keep, tile=(Bn, Bv))
+    vid = np.array([0, 9, 12, 23])
+    assert np.allclose(O.db_rows(e, c, t, vid, lse, reduction="sum", bias=b, keep=keep, tile=(Bn, Bv)),
+                       full.db[vid], rtol=1e-12, atol=1e-15)
+    assert np.allclose(O.dC_rows(e, c, t, vid, lse, reduction="sum", bias=b, keep=keep, tile=(Bn, Bv)),
+                       full.dC[vid], rtol=1e-12, atol=1e-15)
+    assert np.allclose(O.dE_rows(e, c, t, [0, 7], reduction="sum", bias=b, keep=keep, tile=(Bn, Bv)),
+                       full.dE[[0, 7]], rtol=1e-12, atol=1e-15)
