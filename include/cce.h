@@ -96,8 +96,10 @@ size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vo
 int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk);
 
 /*
- * Forward.  e (device) [N, D], c (device) [V, D] of `dtype`; targets (device)
- * int64 [N].  reduction: CCE_REDUCTION_NONE writes loss[N] (0 on ignored rows);
+ * Forward.  e (device) [N, D], c (device) [V, D] of `dtype`; bias (device)
+ * [V] of `dtype` or NULL: the optional classifier bias of the mlx-cross-entropy
+ * README ("API" table), added to every row of the logits, z = e c^T + b;
+ * targets (device) int64 [N].  reduction: CCE_REDUCTION_NONE writes loss[N] (0 on ignored rows);
  * SUM / MEAN write loss[0] (MEAN divides by max(n_valid, 1)).  lse (device)
  * float [N] receives every row's LSE (ignored rows included).  n_valid
  * (device) int32 [1] receives the non-ignored count; may be NULL.  softcap must
@@ -106,27 +108,30 @@ int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk);
  * the vocab_chunk the backward will use; it holds the per-block partials the
  * backward's filter reads, so keep it unmodified between the two calls.
  */
-cce_status cce_forward(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D,
-                       int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
+cce_status cce_forward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
+                       int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
                        float* loss, float* lse, int32_t* n_valid, void* ws, size_t ws_bytes,
                        cce_stream_t stream);
 
 /*
- * Backward.  Same e, c, targets, sizes, dtype, ignore_index, reduction and
- * softcap as the forward; lse (device) float [N] is the forward's output and
+ * Backward.  Same e, c, bias, targets, sizes, dtype, ignore_index, reduction
+ * and softcap as the forward; lse (device) float [N] is the forward's output and
  * ws is the forward's workspace, unmodified.  grad_loss (device) float is the
  * upstream gradient: [N] for NONE, [1] otherwise.  filter = 1 skips tiles
  * whose softmax is below 2^-12 everywhere (and that hold no target); 0
  * computes every tile.  accum = CCE_ACCUM_DETERMINISTIC gives run-to-run
  * bitwise-identical results (fixed-order split reduction);
  * CCE_ACCUM_ATOMIC accumulates dE with fp32 atomics.  dE (device) float
- * [N, D] and dC (device) float [V, D] are overwritten.  vocab_chunk as in
- * cce_workspace_size.
+ * [N, D] and dC (device) float [V, D] are overwritten.  dbias (device) float
+ * [V] or NULL: when given, overwritten with the bias gradient db_j =
+ * sum_i G_ij (column sums of the filtered gradient tiles, in a fixed order
+ * in both accum modes); it is defined with or without a bias.  vocab_chunk as
+ * in cce_workspace_size.
  */
-cce_status cce_backward(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D,
-                        int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
+cce_status cce_backward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
+                        int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
                         const float* lse, const float* grad_loss, int filter, int accum,
-                        int64_t vocab_chunk, float* dE, float* dC, void* ws, size_t ws_bytes,
+                        int64_t vocab_chunk, float* dE, float* dC, float* dbias, void* ws, size_t ws_bytes,
                         cce_stream_t stream);
 
 /*
@@ -150,8 +155,8 @@ void cce_tile_shape(int* filter_rows, int* filter_vocab, int* partial_vocab);
  * cce_profile_stop waits for those events and returns the summed elapsed time
  * (host double, ms) and the number of launches timed (host int).  The hook
  * holds process-wide state: it is meant for benchmarks and is not
- * thread-safe.  Kernel ids 0..10 are fwd_tile, rows, reduce, bwd_prep, filter,
- * grad_tile, dC_gemm, dE_gemm, dE_reduce, fill_zero, transpose_e
+ * thread-safe.  Kernel ids 0..11 are fwd_tile, rows, reduce, bwd_prep, filter,
+ * grad_tile, dC_gemm, dE_gemm, dE_reduce, fill_zero, transpose_e, db_reduce
  * (cce_kernel_name).
  */
 cce_status cce_profile_start(int kernel_id, int max_launches);

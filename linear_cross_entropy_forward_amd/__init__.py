@@ -58,10 +58,10 @@ def lib() -> ctypes.CDLL:
     L.cce_vocab_chunk.restype = i64
     L.cce_vocab_chunk.argtypes = [i64, i64, i32, i64]
     L.cce_forward.restype = i32
-    L.cce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.cce_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, vp, vp, vp, vp, sz, vp]
     L.cce_backward.restype = i32
-    L.cce_backward.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, vp, vp, i32, i32, i64, vp, vp,
-                               vp, sz, vp]
+    L.cce_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, vp, vp, i32, i32, i64, vp, vp,
+                               vp, vp, sz, vp]
     L.cce_read_stats.restype = i32
     L.cce_read_stats.argtypes = [vp, sz, i64, i64, vp, ctypes.POINTER(_Stats)]
     L.cce_status_string.restype = ctypes.c_char_p
@@ -137,13 +137,23 @@ def _validate(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor) -> None:
         raise CCEError("e, c and targets must be contiguous")
 
 
+def _validate_bias(bias, c):
+    if bias is None:
+        return
+    if not bias.is_cuda or bias.dtype != c.dtype or bias.dim() != 1 or bias.shape[0] != c.shape[0] \
+            or not bias.is_contiguous():
+        raise CCEError(f"bias must be a contiguous device tensor [{c.shape[0]}] of dtype {c.dtype}")
+
+
 def forward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, ignore_index: int = -100,
             reduction: str = "mean", softcap: float = 0.0, ws: torch.Tensor | None = None,
-            vocab_chunk: int = 0):
+            vocab_chunk: int = 0, bias: torch.Tensor | None = None):
     """cce_forward.  Returns (loss, lse, n_valid, ws); loss is [N] for
     reduction='none', else a 0-dim tensor.  `ws` (uint8, device) is allocated
-    if not given and must be passed unchanged to backward()."""
+    if not given and must be passed unchanged to backward().  `bias` [V] (the
+    classifier's dtype) is optional."""
     _validate(e, c, targets)
+    _validate_bias(bias, c)
     N, D = e.shape
     V = c.shape[0]
     dev = e.device
@@ -154,7 +164,8 @@ def forward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, ignore_inde
     loss = torch.empty(N if red == 0 else 1, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev)
     n_valid = torch.empty(1, dtype=torch.int32, device=dev)
-    _check(lib().cce_forward(_ptr(e), _ptr(c), _ptr(targets), N, D, V, _dtype_code(e), ignore_index, red,
+    _check(lib().cce_forward(_ptr(e), _ptr(c), _ptr(bias) if bias is not None else None, _ptr(targets), N, D, V,
+                             _dtype_code(e), ignore_index, red,
                              softcap, _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(ws), ws.numel(), _stream()),
            "cce_forward")
     return (loss if red == 0 else loss[0]), lse, n_valid, ws
@@ -163,10 +174,12 @@ def forward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, ignore_inde
 def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor,
              grad_loss: torch.Tensor, ws: torch.Tensor, ignore_index: int = -100, reduction: str = "mean",
              filter: bool = True, accum: str = "deterministic", softcap: float = 0.0, vocab_chunk: int = 0,
-             dE: torch.Tensor | None = None, dC: torch.Tensor | None = None):
+             dE: torch.Tensor | None = None, dC: torch.Tensor | None = None, bias: torch.Tensor | None = None,
+             want_dbias: bool = False):
     """cce_backward.  grad_loss is float32 [N] ('none') or [1]/0-dim.  Returns
-    float32 (dE [N, D], dC [V, D])."""
+    float32 (dE [N, D], dC [V, D]), plus db [V] when want_dbias."""
     _validate(e, c, targets)
+    _validate_bias(bias, c)
     N, D = e.shape
     V = c.shape[0]
     dev = e.device
@@ -175,11 +188,13 @@ def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch
         dE = torch.empty((N, D), dtype=torch.float32, device=dev)
     if dC is None:
         dC = torch.empty((V, D), dtype=torch.float32, device=dev)
-    _check(lib().cce_backward(_ptr(e), _ptr(c), _ptr(targets), N, D, V, _dtype_code(e), ignore_index,
-                              _REDUCTIONS[reduction], softcap, _ptr(lse), _ptr(g), int(bool(filter)),
-                              _ACCUM[accum], vocab_chunk, _ptr(dE), _ptr(dC), _ptr(ws), ws.numel(), _stream()),
+    db = torch.empty(V, dtype=torch.float32, device=dev) if want_dbias else None
+    _check(lib().cce_backward(_ptr(e), _ptr(c), _ptr(bias) if bias is not None else None, _ptr(targets), N, D, V,
+                              _dtype_code(e), ignore_index, _REDUCTIONS[reduction], softcap, _ptr(lse), _ptr(g),
+                              int(bool(filter)), _ACCUM[accum], vocab_chunk, _ptr(dE), _ptr(dC),
+                              _ptr(db) if db is not None else None, _ptr(ws), ws.numel(), _stream()),
            "cce_backward")
-    return dE, dC
+    return (dE, dC, db) if want_dbias else (dE, dC)
 
 
 def read_stats(ws: torch.Tensor, N: int, V: int) -> dict:
@@ -191,40 +206,42 @@ def read_stats(ws: torch.Tensor, N: int, V: int) -> dict:
 
 class _CCEFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, e, c, targets, reduction, ignore_index, filter, accum):
-        loss, lse, _, ws = forward(e, c, targets, ignore_index=ignore_index, reduction=reduction)
-        ctx.save_for_backward(e, c, targets, lse, ws)
+    def forward(ctx, e, c, bias, targets, reduction, ignore_index, filter, accum):
+        loss, lse, _, ws = forward(e, c, targets, ignore_index=ignore_index, reduction=reduction, bias=bias)
+        ctx.save_for_backward(e, c, bias, targets, lse, ws)
         ctx.cfg = (reduction, ignore_index, filter, accum)
         return loss
 
     @staticmethod
     def backward(ctx, grad):
-        e, c, targets, lse, ws = ctx.saved_tensors
+        e, c, bias, targets, lse, ws = ctx.saved_tensors
         reduction, ignore_index, filter, accum = ctx.cfg
-        dE, dC = backward(e, c, targets, lse, grad, ws, ignore_index=ignore_index, reduction=reduction,
-                          filter=filter, accum=accum)
+        want_db = bias is not None and ctx.needs_input_grad[2]
+        out = backward(e, c, targets, lse, grad, ws, ignore_index=ignore_index, reduction=reduction,
+                       filter=filter, accum=accum, bias=bias, want_dbias=want_db)
+        dE, dC = out[0], out[1]
+        db = out[2].to(bias.dtype) if want_db else None
         # autograd wants gradients in the inputs' dtype
-        return dE.to(e.dtype), dC.to(c.dtype), None, None, None, None, None
+        return dE.to(e.dtype), dC.to(c.dtype), db, None, None, None, None, None
 
 
 def cce_loss(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, reduction: str = "mean",
-             ignore_index: int = -100, filter: bool = True, accum: str = "deterministic") -> torch.Tensor:
-    """Flat form: e [N, D], c [V, D], targets [N]."""
-    return _CCEFunction.apply(e.contiguous(), c.contiguous(), targets.contiguous().to(torch.int64), reduction,
-                              ignore_index, filter, accum)
+             ignore_index: int = -100, filter: bool = True, accum: str = "deterministic",
+             bias: torch.Tensor | None = None) -> torch.Tensor:
+    """Flat form: e [N, D], c [V, D], targets [N], optional bias [V]."""
+    return _CCEFunction.apply(e.contiguous(), c.contiguous(), None if bias is None else bias.contiguous(),
+                              targets.contiguous().to(torch.int64), reduction, ignore_index, filter, accum)
 
 
 def linear_cross_entropy(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, bias=None,
                          reduction: str = "mean", ignore_index: int = -100, filter: bool = True,
                          accum: str = "deterministic") -> torch.Tensor:
-    """Cross-entropy of softmax(e @ c.T) against targets without forming the
-    logits.  e [..., D], c [V, D], targets [...]; 'none' returns a tensor
-    shaped like targets."""
-    if bias is not None:
-        raise NotImplementedError("classifier bias is not supported by this build")
+    """Cross-entropy of softmax(e @ c.T + bias) against targets without forming
+    the logits.  e [..., D], c [V, D], targets [...], bias [V] or None;
+    'none' returns a tensor shaped like targets."""
     if reduction not in _REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(_REDUCTIONS)}")
     shape = targets.shape
     D = e.shape[-1]
-    out = cce_loss(e.reshape(-1, D), c, targets.reshape(-1), reduction, ignore_index, filter, accum)
+    out = cce_loss(e.reshape(-1, D), c, targets.reshape(-1), reduction, ignore_index, filter, accum, bias=bias)
     return out.reshape(shape) if reduction == "none" else out

@@ -67,6 +67,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const size_t o_gt = take(L.gt_bytes);
   const size_t o_et = take((size_t)D * (size_t)L.Npad * es);
   const size_t o_dep = take((size_t)(L.splits - 1) * (size_t)N * (size_t)D * 4);
+  const size_t o_dbp = take((size_t)L.nb * (size_t)V * 4);
   L.total = off;
   if (base) {
     char* b = (char*)base;
@@ -79,6 +80,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     L.Gt = b + o_gt;
     L.Et = b + o_et;
     L.dE_part = (float*)(b + o_dep);
+    L.db_part = (float*)(b + o_dbp);
   }
   return L;
 }
@@ -142,7 +144,7 @@ static void prof_release(ProfSlot& p) {
 
 static const char* const kKernelNames[kNumKernels] = {
     "fwd_tile", "rows", "reduce", "bwd_prep", "filter", "grad_tile", "dC_gemm", "dE_gemm", "dE_reduce",
-    "fill_zero", "transpose_e"};
+    "fill_zero", "transpose_e", "db_reduce"};
 
 }  // namespace cce
 
@@ -162,11 +164,16 @@ int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk) {
   return make_layout(N, 1, V, dtype, vocab_chunk, nullptr).Vc;
 }
 
-cce_status cce_forward(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D, int64_t V,
-                       int dtype, int64_t ignore_index, int reduction, float softcap, float* loss, float* lse,
-                       int32_t* n_valid, void* ws, size_t ws_bytes, cce_stream_t stream) {
+static bool bias_ok(const void* bias, int dtype) {
+  return ((uintptr_t)bias & (dtype == kDtypeBf16 ? 1u : 3u)) == 0;
+}
+
+cce_status cce_forward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
+                       int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
+                       float* loss, float* lse, int32_t* n_valid, void* ws, size_t ws_bytes, cce_stream_t stream) {
   cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, ws, 0);
   if (st != CCE_OK) return st;
+  if (!bias_ok(bias, dtype)) return CCE_ERR_INVALID_ARG;
   if (!loss || !lse) return CCE_ERR_INVALID_ARG;
   // The forward only touches the leading (chunk-independent) part of the
   // layout; any workspace sized for some vocab_chunk is large enough for it.
@@ -177,6 +184,7 @@ cce_status cce_forward(const void* e, const void* c, const int64_t* targets, int
   Problem P{};
   P.e = e;
   P.c = c;
+  P.bias = bias;
   P.targets = targets;
   P.N = (int)N;
   P.D = (int)D;
@@ -191,12 +199,13 @@ cce_status cce_forward(const void* e, const void* c, const int64_t* targets, int
   return err == hipSuccess ? CCE_OK : CCE_ERR_HIP;
 }
 
-cce_status cce_backward(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D, int64_t V,
-                        int dtype, int64_t ignore_index, int reduction, float softcap, const float* lse,
-                        const float* grad_loss, int filter, int accum, int64_t vocab_chunk, float* dE, float* dC,
-                        void* ws, size_t ws_bytes, cce_stream_t stream) {
+cce_status cce_backward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
+                        int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
+                        const float* lse, const float* grad_loss, int filter, int accum, int64_t vocab_chunk,
+                        float* dE, float* dC, float* dbias, void* ws, size_t ws_bytes, cce_stream_t stream) {
   cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, ws, vocab_chunk);
   if (st != CCE_OK) return st;
+  if (!bias_ok(bias, dtype) || ((uintptr_t)dbias & 3u)) return CCE_ERR_INVALID_ARG;
   if (!lse || !grad_loss || !dE || !dC) return CCE_ERR_INVALID_ARG;
   if ((filter != 0 && filter != 1) || (accum != kAccumDeterministic && accum != kAccumAtomic))
     return CCE_ERR_INVALID_ARG;
@@ -206,6 +215,7 @@ cce_status cce_backward(const void* e, const void* c, const int64_t* targets, in
   Problem P{};
   P.e = e;
   P.c = c;
+  P.bias = bias;
   P.targets = targets;
   P.N = (int)N;
   P.D = (int)D;
@@ -219,6 +229,7 @@ cce_status cce_backward(const void* e, const void* c, const int64_t* targets, in
   P.accum = accum;
   P.dE = dE;
   P.dC = dC;
+  P.dbias = dbias;
   hipError_t err = launch_backward(P, L, (hipStream_t)stream);
   return err == hipSuccess ? CCE_OK : CCE_ERR_HIP;
 }

@@ -43,6 +43,7 @@ constexpr int kWaveSlots = 256;
 struct Problem {
   const void* e;
   const void* c;
+  const void* bias;  // [V] operand type, or null
   const int64_t* targets;
   int N, D, V;
   int dtype;
@@ -58,6 +59,7 @@ struct Problem {
   int accum;
   float* dE;
   float* dC;
+  float* dbias;      // [V] or null
 };
 
 struct Layout {
@@ -66,6 +68,7 @@ struct Layout {
   float2* part;     // [N][nVB]
   float* nll_out;   // [N] per-row loss (the caller's loss buffer for 'none')
   float* scale;     // [Npad]
+  float* db_part;   // [Npad/256][V] per token block column sums of G (bias gradient)
   uint8_t* keep;    // [nb][nvb_t]
   void* G;          // [Npad][Vc] operand type: gradient tiles of one vocab chunk
   void* Gt;         // [Vc][gt_ld] the same tiles transposed (columns past Npad unused)
@@ -84,7 +87,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
 // Kernel ids of the profiling hook (cce_profile_start / cce_profile_stop).
 enum KernelId {
   kKFwdTile = 0, kKRows, kKReduce, kKBwdPrep, kKFilter, kKGradTile, kKDC, kKDE, kKDEReduce, kKFill,
-  kKTransE, kNumKernels
+  kKTransE, kKDbReduce, kNumKernels
 };
 // Records start/stop events around one launch of kernel `id` when profiling of
 // that id is active (no-op otherwise).

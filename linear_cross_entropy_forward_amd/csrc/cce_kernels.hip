@@ -76,6 +76,18 @@ template <> __device__ __forceinline__ float to_f<uint16_t>(uint16_t v) {
 }
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
 
+// The classifier bias of a 256-row vocabulary tile, as fp32, into LDS (rows
+// past V read 0).  Visible to the waves after the main loop's first barrier.
+template <typename T, int ROWS>
+__device__ __forceinline__ void stage_bias(float* sb, const T* __restrict__ bias, int v0, int V) {
+  for (int i = threadIdx.x; i < ROWS; i += blockDim.x) sb[i] = v0 + i < V ? to_f<T>(bias[v0 + i]) : 0.f;
+}
+// Bias of the four consecutive tile rows r..r+3 (r a multiple of 4).
+__device__ __forceinline__ f32x4 bias4(const float* sb, int r) {
+  return *(const __attribute__((address_space(3))) f32x4*)(
+      (const __attribute__((address_space(3))) float*)sb + r);
+}
+
 // Four consecutive fp32 values in the operand type, packed for one store.
 __device__ __forceinline__ void store4(rsrc_t r, uint32_t off, float a, float b, float c, float d,
                                        const uint16_t*) {
@@ -182,13 +194,16 @@ __global__ __launch_bounds__(256) void transpose_e_kernel(const T* __restrict__ 
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T* __restrict__ c,
                                                             const typename C::T* __restrict__ e,
+                                                            const typename C::T* __restrict__ bias,
                                                             int N, int D, int V, float2* __restrict__ part,
                                                             int nVB, int tiles_n, int total) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
+  __shared__ __attribute__((aligned(16))) float sbias[C::BM];
   int tv, tn;
   grouped_tile(xcd_remap(blockIdx.x, total), total / tiles_n, tiles_n, kRasterGroup, tv, tn);
   const int v0 = tv * C::BM, n0 = tn * C::BN;
+  if (bias) stage_bias<T, C::BM>(sbias, bias, v0, V);
 
   Operand A = make_operand(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T), (uint32_t)D,
                min(C::BM, V - v0), D);
@@ -205,26 +220,37 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
   const int lane = threadIdx.x & 63;
   const int wm = (threadIdx.x >> 6) / C::WAVES_N;
   const int vblk = (v0 + wm * C::WM) / C::WM;
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) {
-    const int n = n0 + am.colj(fn);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (v0 + am.row(fm, r) < V) mx = fmaxf(mx, acc[fm][fn][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mxl = mx * kLog2e;
-    float s = 0.f;
+  // logits of this lane's 64 rows of column fn (plus the rows' bias)
+  auto emit = [&](auto has_bias) {
+    f32x4 bz[C::FM][4];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (v0 + am.row(fm, r) < V) s += fast_exp2(__builtin_fmaf(acc[fm][fn][r], kLog2e, -mxl));
-    s += __shfl_xor(s, 32, 64);
-    if (lane < 32 && n < N && vblk < nVB) part[(size_t)n * nVB + vblk] = make_float2(mx, s);
-  }
+      for (int q = 0; q < 4; ++q) bz[fm][q] = decltype(has_bias)::value ? bias4(sbias, am.row(fm, 4 * q)) : f32x4{};
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int n = n0 + am.colj(fn);
+      auto z = [&](int fm, int r) { return acc[fm][fn][r] + bz[fm][r >> 2][r & 3]; };
+      float mx = -INFINITY;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (v0 + am.row(fm, r) < V) mx = fmaxf(mx, z(fm, r));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mxl = mx * kLog2e;
+      float s = 0.f;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (v0 + am.row(fm, r) < V) s += fast_exp2(__builtin_fmaf(z(fm, r), kLog2e, -mxl));
+      s += __shfl_xor(s, 32, 64);
+      if (lane < 32 && n < N && vblk < nVB) part[(size_t)n * nVB + vblk] = make_float2(mx, s);
+    }
+  };
+  if (bias) emit(std::true_type{});
+  else emit(std::false_type{});
 }
 
 // ============================================================================
@@ -233,6 +259,7 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
 // ============================================================================
 template <typename T>
 __global__ __launch_bounds__(256) void rows_kernel(const T* __restrict__ e, const T* __restrict__ c,
+                                                   const T* __restrict__ bias,
                                                    const int64_t* __restrict__ targets, int N, int D,
                                                    int V, int64_t ignore_index,
                                                    const float2* __restrict__ part, int nVB,
@@ -270,6 +297,7 @@ __global__ __launch_bounds__(256) void rows_kernel(const T* __restrict__ e, cons
       }
     }
     zy = wave_sum(acc);
+    if (bias) zy += to_f<T>(bias[t]);
   }
 
   const float2* p = part + (size_t)i * nVB;
@@ -430,19 +458,21 @@ __global__ __launch_bounds__(256) void filter_kernel(const int64_t* __restrict__
 // ============================================================================
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
-    const typename C::T* __restrict__ c, const typename C::T* __restrict__ e,
+    const typename C::T* __restrict__ c, const typename C::T* __restrict__ e, const typename C::T* __restrict__ bias,
     const int64_t* __restrict__ targets, const float* __restrict__ lse, const float* __restrict__ scale,
     const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int tiles_v,
     int tiles_n, int Vc, int gt_ld, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes,
-    size_t gt_bytes) {
+    size_t gt_bytes, float* __restrict__ db_part) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
+  __shared__ __attribute__((aligned(16))) float sbias[C::BM];
   const int total = tiles_v * tiles_n;
   int tvl, tn;
   grouped_tile(xcd_remap(blockIdx.x, total), tiles_v, tiles_n, kRasterGroup, tvl, tn);
   const int tv = cvb0 + tvl;
   if (!keep[(size_t)tn * nvb_t + tv]) return;
   const int v0 = tv * C::BM, n0 = tn * C::BN;
+  if (bias) stage_bias<T, C::BM>(sbias, bias, v0, V);
 
   Operand A = make_operand(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T), (uint32_t)D,
                min(C::BM, V - v0), D);
@@ -483,7 +513,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   // A column's target row lies in this wave's 128 rows for few tiles (about
   // 128 / V of them per column): a wave-uniform test skips the one-hot compare
   // everywhere else.
-  auto compute = [&](auto ragged, auto&& sink) {
+  auto compute = [&](auto ragged, auto has_bias, auto&& sink) {
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       auto body = [&](auto with_target) {
@@ -493,9 +523,11 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
           for (int q = 0; q < 4; ++q) {
             float g[4];
             const int rl = am.row(fm, 4 * q);
+            const f32x4 bz = decltype(has_bias)::value ? bias4(sbias, rl) : f32x4{};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              const float p = fast_exp2(__builtin_fmaf(acc[fm][fn][4 * q + u], kLog2e, -lsel[fn]));
+              const float z = decltype(has_bias)::value ? acc[fm][fn][4 * q + u] + bz[u] : acc[fm][fn][4 * q + u];
+              const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lsel[fn]));
               if constexpr (decltype(with_target)::value) {
                 const float tsc = trow[fn] == fm * 32 + 8 * q + u ? sc[fn] : 0.f;
                 g[u] = __builtin_fmaf(p, sc[fn], -tsc);
@@ -513,8 +545,12 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     }
   };
   auto run = [&](auto&& sink) {
-    if (v0 + C::BM <= V) compute(std::false_type{}, sink);
-    else compute(std::true_type{}, sink);
+    auto rag = [&](auto hb) {
+      if (v0 + C::BM <= V) compute(std::false_type{}, hb, sink);
+      else compute(std::true_type{}, hb, sink);
+    };
+    if (bias) rag(std::true_type{});
+    else rag(std::false_type{});
   };
 
   if constexpr (sizeof(T) == 2) {
@@ -535,25 +571,40 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // rows of 256 bf16 out of the staging tile, two per instruction: row
     // `wave * 64 + 2 it + lane / 32`, chunk lane % 32, to row-major memory
-    auto drain = [&](rsrc_t r, uint32_t pitch, uint32_t row0, uint32_t col0, auto pass2) {
+    // With `sums` (the G^T pass, when the bias gradient is wanted) each
+    // vocabulary row's 256 tokens are also added up: 8 per lane, then across
+    // the 32 lanes of the half-wave, giving this token block's share of db.
+    auto drain = [&](rsrc_t r, uint32_t pitch, uint32_t row0, uint32_t col0, auto pass2, bool sums) {
 #pragma unroll 4
       for (int it = 0; it < 32; ++it) {
         const int rr = wave * 64 + it * 2 + (lane >> 5), jc = lane & 31;
         const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(rr, jc * 8, pass2));
         __builtin_amdgcn_raw_buffer_store_b128(val, r, ((row0 + (uint32_t)rr) * pitch + col0 + (uint32_t)jc * 8u) * 2u,
                                                0, 0);
+        if (sums) {
+          float t8 = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w = val[q];
+            t8 += __builtin_bit_cast(float, w << 16) + __builtin_bit_cast(float, w & 0xffff0000u);
+          }
+#pragma unroll
+          for (int m = 16; m >= 1; m >>= 1) t8 += __shfl_xor(t8, m, 64);
+          if (jc == 0 && v0 + rr < V) db_part[(size_t)tn * V + v0 + rr] = t8;
+        }
       }
     };
     uint32_t pk[C::FN][C::FM][4][2];
     // pass 1: [token][vocab] -> G rows
-    run([&](int fn, int fm, int q, int rl, const float (&g)[4]) {
+    run([&](int fn, int fm, int q, int, const float (&g)[4]) {
+      const int rl = am.row(fm, 4 * q);
       pk[fn][fm][q][0] = pack_bf16(g[0], g[1]);
       pk[fn][fm][q][1] = pack_bf16(g[2], g[3]);
       *(__attribute__((address_space(3))) u32x2*)(tile + slot(am.colj(fn), rl, std::false_type{})) =
           u32x2{pk[fn][fm][q][0], pk[fn][fm][q][1]};
     });
     __syncthreads();
-    drain(rg, (uint32_t)Vc, (uint32_t)n0, (uint32_t)vl0, std::false_type{});
+    drain(rg, (uint32_t)Vc, (uint32_t)n0, (uint32_t)vl0, std::false_type{}, false);
     __syncthreads();
     // pass 2: [vocab][token] -> G^T rows, one 16-bit store per element (the
     // 32 lanes of a half-wave write 64 consecutive bytes of one vocab row)
@@ -569,16 +620,43 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
                 tile + slot(am.row(fm, 4 * q) + u, am.colj(fn), std::true_type{})) =
                 (uint16_t)(pk[fn][fm][q][u >> 1] >> (16 * (u & 1)));
     __syncthreads();
-    drain(rgt, (uint32_t)gt_ld, (uint32_t)vl0, (uint32_t)n0, std::true_type{});
+    drain(rgt, (uint32_t)gt_ld, (uint32_t)vl0, (uint32_t)n0, std::true_type{}, db_part != nullptr);
   } else {
-    run([&](int fn, int, int, int rl, const float (&g)[4]) {
+    float rs[C::FM][4][4] = {};  // this lane's share of each row's token sum (for db)
+    run([&](int fn, int fm, int q, int rl, const float (&g)[4]) {
       const int n = n0 + am.colj(fn);
       store4(rg, ((uint32_t)n * (uint32_t)Vc + (uint32_t)(vl0 + rl)) * (uint32_t)sizeof(T), g[0], g[1], g[2], g[3],
              (const T*)nullptr);
       // G^T[v][n]: the quad's four tokens of vocab rows rl..rl+3
       store_quad_t(rgt, ((uint32_t)(vl0 + rl) * (uint32_t)gt_ld + (uint32_t)(n & ~3)) * (uint32_t)sizeof(T),
                    (uint32_t)gt_ld * (uint32_t)sizeof(T), g, (const T*)nullptr);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rs[fm][q][u] += g[u];
     });
+    if (db_part) {
+      // token sums per vocabulary row: across the 32 lanes of a half-wave,
+      // then the two waves that share the rows, through LDS, in a fixed order
+      float* red = (float*)smem;  // [WAVES_N][BM]
+      const int wn = (threadIdx.x >> 6) % C::WAVES_N;
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float x = rs[fm][q][u];
+#pragma unroll
+            for (int m = 16; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+            if ((lane & 31) == 0) red[wn * C::BM + am.row(fm, 4 * q) + u] = x;
+          }
+      __syncthreads();
+      for (int r = threadIdx.x; r < C::BM; r += C::NT) {
+        float x = 0.f;
+        for (int w = 0; w < C::WAVES_N; ++w) x += red[w * C::BM + r];
+        if (v0 + r < V) db_part[(size_t)tn * V + v0 + r] = x;
+      }
+    }
   }
 }
 
@@ -600,6 +678,20 @@ __device__ __forceinline__ int collect_blocks(const uint8_t* __restrict__ keep, 
   }
   __syncthreads();
   return s_cnt;
+}
+
+// ============================================================================
+// db[v] = sum over token blocks (in order) of the kept tiles' column sums.
+// ============================================================================
+__global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict__ db_part,
+                                                        const uint8_t* __restrict__ keep, int nb, int nvb_t, int V,
+                                                        float* __restrict__ db) {
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  float s = 0.f;
+  for (int b = 0; b < nb; ++b)
+    if (keep[(size_t)b * nvb_t + v / kTileV]) s += db_part[(size_t)b * V + v];
+  db[v] = s;
 }
 
 // ============================================================================
@@ -776,11 +868,12 @@ static hipError_t launch_forward_t(const Problem& P, const Layout& L, hipStream_
   const int tiles_v = (P.V + C::BM - 1) / C::BM, tiles_n = (P.N + C::BN - 1) / C::BN;
   const int total = tiles_v * tiles_n;
   prof_before(kKFwdTile, st);
-  hipLaunchKernelGGL(fwd_tile_kernel<C>, dim3(total), dim3(C::NT), 0, st, c, e, P.N, P.D, P.V, L.part, L.nVB,
-                     tiles_n, total);
+  hipLaunchKernelGGL(fwd_tile_kernel<C>, dim3(total), dim3(C::NT), 0, st, c, e, (const T*)P.bias, P.N, P.D, P.V,
+                     L.part, L.nVB, tiles_n, total);
   prof_after(kKFwdTile, st);
   prof_before(kKRows, st);
-  hipLaunchKernelGGL(rows_kernel<T>, dim3((P.N + 3) / 4), dim3(256), 0, st, e, c, P.targets, P.N, P.D, P.V,
+  hipLaunchKernelGGL(rows_kernel<T>, dim3((P.N + 3) / 4), dim3(256), 0, st, e, c, (const T*)P.bias, P.targets,
+                     P.N, P.D, P.V,
                      P.ignore_index, L.part, L.nVB, P.lse, L.nll_out);
   prof_after(kKRows, st);
   prof_before(kKReduce, st);
@@ -827,9 +920,9 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     const int cnvb = (clen + kTileV - 1) / kTileV;
     const int cvb0 = cv0 / kTileV;
     prof_before(kKGradTile, st);
-    hipLaunchKernelGGL(grad_tile_kernel<C>, dim3(cnvb * tiles_n), dim3(C::NT), 0, st, c, e, P.targets, P.lse,
-                       L.scale, L.keep, P.N, P.D, P.V, L.nvb_t, cvb0, cnvb, tiles_n, L.Vc, L.gt_ld, G, (T*)L.Gt,
-                       L.g_bytes, L.gt_bytes);
+    hipLaunchKernelGGL(grad_tile_kernel<C>, dim3(cnvb * tiles_n), dim3(C::NT), 0, st, c, e, (const T*)P.bias,
+                       P.targets, P.lse, L.scale, L.keep, P.N, P.D, P.V, L.nvb_t, cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
+                       G, (T*)L.Gt, L.g_bytes, L.gt_bytes, P.dbias ? L.db_part : nullptr);
     prof_after(kKGradTile, st);
     prof_before(kKDC, st);
     hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(cnvb * tiles_d), dim3(C::NT), 0, st, (const T*)L.Gt,
@@ -842,6 +935,12 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
                        P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits, L.Vc, L.g_bytes,
                        P.dE, L.dE_part, ch > 0 ? 1 : 0, P.accum == kAccumAtomic ? 1 : 0);
     prof_after(kKDE, st);
+  }
+  if (P.dbias) {
+    prof_before(kKDbReduce, st);
+    hipLaunchKernelGGL(db_reduce_kernel, dim3((P.V + 255) / 256), dim3(256), 0, st, L.db_part, L.keep, L.nb,
+                       L.nvb_t, P.V, P.dbias);
+    prof_after(kKDbReduce, st);
   }
   if (P.accum != kAccumAtomic && L.splits > 1) {
     const size_t n4 = (size_t)P.N * P.D / 4;

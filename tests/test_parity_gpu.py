@@ -37,22 +37,25 @@ def _grad_arg(reduction, N, seed=0):
 
 
 def run(M, inp, reduction="mean", filter=False, accum="deterministic", vocab_chunk=0, ignore_index=-100,
-        backward=True, grad_seed=0):
+        backward=True, grad_seed=0, bias=None, want_db=False):
     import torch
     dt = inp.get("dtype") or inp["workload"].dtype
     e, c, t = dev(inp["e"], dt), dev(inp["c"], dt), dev_targets(inp["targets"])
+    b = dev(bias, dt) if bias is not None else None
     N, V = e.shape[0], c.shape[0]
     loss, lse, nv, ws = M.forward(e, c, t, ignore_index=ignore_index, reduction=reduction,
-                                  vocab_chunk=vocab_chunk)
+                                  vocab_chunk=vocab_chunk, bias=b)
     out = {"loss": None, "lse": None}
     torch.cuda.synchronize()
     out["stats_fwd"] = M.read_stats(ws, N, V)
     if backward:
         g_np, g = _grad_arg(reduction, N, grad_seed)
-        dE, dC = M.backward(e, c, t, lse, g, ws, ignore_index=ignore_index, reduction=reduction, filter=filter,
-                            accum=accum, vocab_chunk=vocab_chunk)
+        res = M.backward(e, c, t, lse, g, ws, ignore_index=ignore_index, reduction=reduction, filter=filter,
+                         accum=accum, vocab_chunk=vocab_chunk, bias=b, want_dbias=want_db)
         torch.cuda.synchronize()
-        out["dE"], out["dC"], out["g"] = dE.cpu().numpy(), dC.cpu().numpy(), g_np
+        out["dE"], out["dC"], out["g"] = res[0].cpu().numpy(), res[1].cpu().numpy(), g_np
+        if want_db:
+            out["db"] = res[2].cpu().numpy()
         out["stats"] = M.read_stats(ws, N, V)
     out["loss"] = loss.cpu().numpy()
     out["lse"] = lse.cpu().numpy()
@@ -68,32 +71,38 @@ def filtered_bound(filtered_oracle, exact_oracle):
     return max(GRAD_RTOL_FILTERED, rel_fro(filtered_oracle, exact_oracle) + GRAD_RTOL)
 
 
-def full_check(M, inp, reduction, filter, accum="deterministic", vocab_chunk=0, ignore_index=-100, label=""):
+def full_check(M, inp, reduction, filter, accum="deterministic", vocab_chunk=0, ignore_index=-100, label="",
+               bias=None, want_db=False):
     e, c, t = inp["e"], inp["c"], inp["targets"]
-    r = run(M, inp, reduction, filter, accum, vocab_chunk, ignore_index)
-    f = O.forward(e, c, t, ignore_index=ignore_index, reduction=reduction)
+    r = run(M, inp, reduction, filter, accum, vocab_chunk, ignore_index, bias=bias, want_db=want_db)
+    f = O.forward(e, c, t, ignore_index=ignore_index, reduction=reduction, bias=bias)
     assert r["n_valid"] == f.n_valid, label
     assert r["stats_fwd"]["n_valid"] == f.n_valid
     check_loss(r["loss"], f.loss, reduction, label, f.n_valid)
     check_lse(r["lse"], f.lse, label)
     if reduction == "none":
         assert (r["loss"][~f.valid] == 0.0).all(), "ignored rows must give exactly 0"
-    b = O.backward(e, c, t, ignore_index=ignore_index, reduction=reduction, grad_loss=r["g"])
+    b = O.backward(e, c, t, ignore_index=ignore_index, reduction=reduction, grad_loss=r["g"], bias=bias)
     assert (r["dE"][~f.valid] == 0.0).all(), "ignored rows must give exactly 0 gradient"
     Bn, Bv, _ = M.tile_shape()
     if filter:
-        lse_o, keep = O.lse_and_keep(e, c, t, Bn, Bv, ignore_index=ignore_index)
+        lse_o, keep = O.lse_and_keep(e, c, t, Bn, Bv, ignore_index=ignore_index, bias=bias)
         bf = O.backward(e, c, t, ignore_index=ignore_index, reduction=reduction, grad_loss=r["g"], keep=keep,
-                        tile=(Bn, Bv))
+                        tile=(Bn, Bv), bias=bias)
         check_grad(r["dE"], bf.dE, GRAD_RTOL, label + " dE vs filtered oracle")
         check_grad(r["dC"], bf.dC, GRAD_RTOL, label + " dC vs filtered oracle")
         check_grad(r["dE"], b.dE, filtered_bound(bf.dE, b.dE), label + " dE vs exact")
         check_grad(r["dC"], b.dC, filtered_bound(bf.dC, b.dC), label + " dC vs exact")
+        if want_db:
+            check_grad(r["db"], bf.db, GRAD_RTOL, label + " db vs filtered oracle")
+            check_grad(r["db"], b.db, filtered_bound(bf.db, b.db), label + " db vs exact")
         kept = r["stats"]["tiles_kept"]
         assert abs(kept - int(keep.sum())) <= max(2, keep.size // 100), (kept, int(keep.sum()), keep.size)
     else:
         check_grad(r["dE"], b.dE, GRAD_RTOL, label + " dE")
         check_grad(r["dC"], b.dC, GRAD_RTOL, label + " dC")
+        if want_db:
+            check_grad(r["db"], b.db, GRAD_RTOL, label + " db")
         assert r["stats"]["tiles_kept"] == r["stats"]["tiles_total"]
     return r
 
@@ -208,54 +217,124 @@ def test_bad_target_is_loud(M):
     assert np.isnan(r["dE"][5]).all()
 
 
+# ----------------------------------------------------------------------------- classifier bias
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_bias_ragged_bf16(M, reduction):
+    inp = W.custom(600, 136, 1100, "bf16", seed=31, c_std=0.1, ignore_frac=0.05)
+    bias = W.bias(1100, "bf16", seed=31)
+    full_check(M, inp, reduction, False, label=f"bias {reduction}", bias=bias, want_db=True)
+
+
+def test_bias_ragged_fp32_filtered(M):
+    inp = W.custom(300, 68, 513, "f32", seed=32, c_std=0.2, ignore_frac=0.1)
+    bias = W.bias(513, "f32", seed=32, std=1.0)
+    full_check(M, inp, "mean", True, label="bias fp32", bias=bias, want_db=True)
+
+
+def test_bias_suppressed_block_is_filtered(M):
+    """A strongly negative bias on vocab block 1 makes the filter drop its
+    tiles (except those holding a target); forward, dE, dC and db agree with
+    the filtered oracle, and the kept count matches its keep map."""
+    inp = W.custom(700, 136, 1300, "bf16", seed=33, c_std=0.1)
+    t = inp["targets"]
+    inp["targets"] = np.where((t >= 256) & (t < 512), t - 256, t)   # no target inside the suppressed block
+    bias = W.bias(1300, "bf16", seed=33, block_offsets={(256, 512): -40.0})
+    r = full_check(M, inp, "sum", True, label="bias suppressed block", bias=bias, want_db=True)
+    assert r["stats"]["tiles_kept"] < r["stats"]["tiles_total"]
+
+
+@pytest.mark.parametrize("accum", ["deterministic", "atomic"])
+def test_bias_with_vocab_chunks(M, accum):
+    inp = W.custom(520, 72, 1400, "bf16", seed=34, c_std=0.1, ignore_frac=0.02)
+    bias = W.bias(1400, "bf16", seed=34)
+    full_check(M, inp, "mean", False, accum=accum, vocab_chunk=512, label=f"bias chunks {accum}", bias=bias,
+               want_db=True)
+
+
+def test_no_bias_gradient_is_column_sum(M):
+    """Without a bias, dbias is still the gradient at b = 0: G's column sums."""
+    inp = W.custom(400, 64, 700, "bf16", seed=35, c_std=0.1)
+    full_check(M, inp, "mean", False, label="db without bias", want_db=True)
+
+
+def test_bias_autograd(M):
+    import torch
+    inp = W.custom(260, 64, 900, "bf16", seed=36, c_std=0.1, ignore_frac=0.05)
+    bias = W.bias(900, "bf16", seed=36)
+    e = dev(inp["e"], "bf16").requires_grad_(True)
+    c = dev(inp["c"], "bf16").requires_grad_(True)
+    b = dev(bias, "bf16").requires_grad_(True)
+    t = dev_targets(inp["targets"]).reshape(20, 13)
+    loss = M.linear_cross_entropy(e.reshape(20, 13, 64), c, t, bias=b)
+    loss.backward()
+    f = O.forward(inp["e"], inp["c"], inp["targets"], bias=bias)
+    bo = O.backward(inp["e"], inp["c"], inp["targets"], bias=bias)
+    check_loss(loss.detach().float().cpu().numpy(), f.loss, "mean", "autograd bias", f.n_valid)
+    assert b.grad is not None and b.grad.dtype == torch.bfloat16
+    # gradients come back in bf16 (the inputs' dtype): allow the rounding
+    check_grad(b.grad.float().cpu().numpy(), bo.db, GRAD_RTOL * 2, "autograd db")
+    check_grad(c.grad.float().cpu().numpy(), bo.dC, GRAD_RTOL * 2, "autograd dC")
+    check_grad(e.grad.float().cpu().numpy(), bo.dE, GRAD_RTOL * 2, "autograd dE")
+
+
 # ----------------------------------------------------------------------------- full-size, sampled
-def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, n_vocab=24, dC_check=True):
+def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, n_vocab=24, dC_check=True,
+                  with_bias=False):
     import torch
     inp = W.get(name)
     e, c, t = inp["e"], inp["c"], inp["targets"]
     N, V = e.shape[0], c.shape[0]
-    print(f"[full] {name} N={N} V={V} reduction={reduction} filter={filter} accum={accum}", flush=True)
-    r = run(M, inp, reduction, filter, accum)
+    bias = W.bias(V, inp["workload"].dtype, seed=5) if with_bias else None
+    print(f"[full] {name} N={N} V={V} reduction={reduction} filter={filter} accum={accum} bias={with_bias}",
+          flush=True)
+    r = run(M, inp, reduction, filter, accum, bias=bias, want_db=with_bias)
     print(f"[full] {name}: GPU done, oracle checks", flush=True)
     rng = np.random.default_rng(99)
     rows = np.sort(rng.choice(N, n_rows, replace=False))
     valid = t != -100
     assert r["n_valid"] == int(valid.sum())
-    fo = O.forward(e, c, t, reduction="none", rows=rows)
+    fo = O.forward(e, c, t, reduction="none", rows=rows, bias=bias)
     check_lse(r["lse"][rows], fo.lse, name)
     if reduction == "none":
         check_loss(r["loss"][rows], fo.nll, "none", name)
     Bn, Bv, _ = M.tile_shape()
     tile = (Bn, Bv)
     if dC_check or filter:
-        lse_all, keep = O.lse_and_keep(e, c, t, Bn, Bv)
+        lse_all, keep = O.lse_and_keep(e, c, t, Bn, Bv, bias=bias)
         print(f"[full] {name}: oracle LSE pass done", flush=True)
         if reduction != "none":
             # the reduced loss from the oracle's full pass
-            nll = np.where(valid, lse_all - np.einsum("ij,ij->i", e.astype(np.float64),
-                                                      c[np.where(valid, t, 0)].astype(np.float64)), 0.0)
+            zt = np.einsum("ij,ij->i", e.astype(np.float64), c[np.where(valid, t, 0)].astype(np.float64))
+            if bias is not None:
+                zt = zt + bias.astype(np.float64)[np.where(valid, t, 0)]
+            nll = np.where(valid, lse_all - zt, 0.0)
             want = nll.sum() / max(valid.sum(), 1) if reduction == "mean" else nll.sum()
             check_loss(r["loss"], want, reduction, name, int(valid.sum()))
         kept = r["stats"]["tiles_kept"]
         if filter:
             assert abs(kept - int(keep.sum())) <= max(2, keep.size // 100), (kept, int(keep.sum()))
     g = r["g"]
-    dE_x = O.dE_rows(e, c, t, rows, reduction=reduction, grad_loss=g)
+    dE_x = O.dE_rows(e, c, t, rows, reduction=reduction, grad_loss=g, bias=bias)
     if filter:
-        dE_f = O.dE_rows(e, c, t, rows, reduction=reduction, grad_loss=g, keep=keep, tile=tile)
+        dE_f = O.dE_rows(e, c, t, rows, reduction=reduction, grad_loss=g, keep=keep, tile=tile, bias=bias)
         check_grad(r["dE"][rows], dE_f, GRAD_RTOL, name + " dE vs filtered")
         check_grad(r["dE"][rows], dE_x, filtered_bound(dE_f, dE_x), name + " dE vs exact")
     else:
         check_grad(r["dE"][rows], dE_x, GRAD_RTOL, name + " dE")
     if dC_check:
         vid = np.unique(np.concatenate([rng.choice(V, n_vocab, replace=False), t[valid][:8]]))
-        dC_x = O.dC_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g)
+        dC_x = O.dC_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g, bias=bias)
         if filter:
-            dC_f = O.dC_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g, keep=keep, tile=tile)
+            dC_f = O.dC_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g, keep=keep, tile=tile,
+                             bias=bias)
             check_grad(r["dC"][vid], dC_f, GRAD_RTOL, name + " dC vs filtered")
             check_grad(r["dC"][vid], dC_x, filtered_bound(dC_f, dC_x), name + " dC vs exact")
         else:
             check_grad(r["dC"][vid], dC_x, GRAD_RTOL, name + " dC")
+        if with_bias:
+            db_f = O.db_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g, bias=bias,
+                             keep=keep if filter else None, tile=tile if filter else None)
+            check_grad(r["db"][vid], db_f, GRAD_RTOL, name + " db")
     torch.cuda.empty_cache()
     return r
 
@@ -280,3 +359,8 @@ def test_full_llama1b(M):
 @pytest.mark.slow
 def test_full_gemma2b_calibrated(M):
     _sampled_full(M, "gemma2b_cal", "mean", True)
+
+
+@pytest.mark.slow
+def test_full_llama1b_bias(M):
+    _sampled_full(M, "llama1b", "mean", True, with_bias=True)

@@ -170,5 +170,16 @@ def custom(N: int, D: int, V: int, dtype: str = "bf16", *, seed: int = 0, e_std:
     return generate(w, threads)
 
 
+def bias(V: int, dtype: str = "bf16", *, seed: int = 0, std: float = 0.5, block_offsets=None) -> np.ndarray:
+    """Seeded classifier bias [V] ~ N(0, std^2), rounded to bf16 for bf16
+    problems.  `block_offsets` {(v0, v1): value} adds a constant to vocab ranges
+    (e.g. a strongly negative block, which the gradient filter then drops)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xB1A5]))
+    b = (rng.standard_normal(V) * std).astype(np.float32)
+    for (v0, v1), val in (block_offsets or {}).items():
+        b[v0:v1] += np.float32(val)
+    return round_to_bf16(b) if dtype == "bf16" else b
+
+
 def get(name: str, threads: int | None = None) -> dict:
     return generate(WORKLOADS[name], threads)
