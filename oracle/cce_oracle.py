@@ -34,13 +34,31 @@ sees them: bf16 values upcast exactly, or fp32):
                                   (chain rule through Z = E C^T + 1 b^T)
   scale_i = g / max(n_valid,1) (mean), g (sum), g_i (none); 0 on ignored rows.
 
+Optional loss terms (both default to 0, which gives the plain loss above):
+
+  label smoothing eps:  the target row becomes the soft target
+        T_i = (1 - eps) onehot(y_i) + eps / V   (spread over all V classes,
+        the true one included), and loss_i = -sum_j T_ij log softmax_ij
+                                  (tirogla "Loss functions", "How it works"
+                                  step 3: soft targets; the gradient stays
+                                  softmax minus the target)
+  z-loss lam:           loss_i += lam * LSE_i^2, whose gradient with respect
+                        to Z_ij is 2 lam LSE_i softmax_ij
+                                  (tirogla "Implementation notes": z-loss
+                                  adds a multiple of the squared log-sum-exp)
+  so that G_ij = (softmax_ij (1 + 2 lam LSE_i) - T_ij) * scale_i.
+
 Gradient filtering (README "How it works" item 2; Wijmans et al. abstract:
 skip gradient entries below numerical precision) is modelled by
 `filter_keep`: a tile (row block b, vocab block v) of G is kept iff some valid
 row i in b has max_{j in v} softmax_ij >= 2^-12, or some valid row in b has
 its target in v.  `backward(..., keep=...)` zeroes G on dropped tiles.  The
 target-tile rule and the strict "< 2^-12 everywhere" reading are this
-implementation's readings of a criterion the pages state only loosely.
+implementation's readings of a criterion the pages state only loosely.  With
+label smoothing the filter still decides on the softmax alone and drops only
+the softmax term (and the one-hot term, which never lies in a dropped tile);
+the uniform -eps/V * scale_i part of G is kept on every entry (a reading: that
+part is known exactly, so nothing is gained by dropping it).
 
 Every function here is pinned by tests/test_oracle_pins.py against closed
 forms, brute force, finite differences and invariants.
@@ -104,10 +122,20 @@ def reduce_loss(nll: np.ndarray, n_valid: int, reduction: str) -> np.ndarray:
     raise ValueError(reduction)
 
 
+def soft_target_rows(t: np.ndarray, V: int, valid: np.ndarray, label_smoothing: float) -> np.ndarray:
+    """T rows: (1 - eps) onehot(t) + eps / V on valid rows, zero rows elsewhere."""
+    T = np.zeros((len(t), V))
+    r = np.nonzero(valid)[0]
+    T[r] = label_smoothing / V
+    T[r, t[r]] += 1.0 - label_smoothing
+    return T
+
+
 def forward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
-            rows=None, bias=None) -> Forward:
+            rows=None, bias=None, label_smoothing: float = 0.0, z_loss: float = 0.0) -> Forward:
     """Loss and per-row LSE.  `rows` restricts the work to a subset of rows
-    (then `loss` is the reduction over that subset only and n_valid counts it)."""
+    (then `loss` is the reduction over that subset only and n_valid counts it).
+    loss_i = -sum_j T_ij (Z_ij - LSE_i) + z_loss * LSE_i^2 on valid rows."""
     e = _f64(e)
     c = _f64(c)
     t = np.asarray(targets, dtype=np.int64)
@@ -122,7 +150,9 @@ def forward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
         lse[sl] = row_logsumexp(z)
         v = valid[sl]
         r = np.nonzero(v)[0]
-        nll[sl][r] = lse[sl][r] - z[r, t[idx[sl]][r]]
+        T = soft_target_rows(t[idx[sl]], V, v, label_smoothing)
+        logp = z - lse[sl][:, None]
+        nll[sl][r] = -(T[r] * logp[r]).sum(axis=1) + z_loss * lse[sl][r] ** 2
     n_valid = int(valid.sum())
     return Forward(reduce_loss(nll, n_valid, reduction), nll, lse, n_valid, valid)
 
@@ -180,11 +210,18 @@ def filter_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100,
 
 
 def softmax_grad_rows(z: np.ndarray, lse: np.ndarray, t: np.ndarray, scale: np.ndarray,
-                      valid: np.ndarray) -> np.ndarray:
-    """G rows: (exp(Z - LSE) - onehot(t)) * scale, zero on ignored rows."""
-    g = np.exp(z - lse[:, None])
+                      valid: np.ndarray, label_smoothing: float = 0.0, z_loss: float = 0.0,
+                      colmask=None) -> np.ndarray:
+    """G rows: (exp(Z - LSE) (1 + 2 z_loss LSE) - T) * scale, zero on ignored
+    rows.  colmask [rows, V] (bool), when given, marks the entries the filter
+    keeps: elsewhere only the uniform -eps/V part of -T remains."""
+    V = z.shape[1]
+    g = np.exp(z - lse[:, None]) * (1.0 + 2.0 * z_loss * lse)[:, None]
     r = np.nonzero(valid)[0]
-    g[r, t[r]] -= 1.0
+    g[r, t[r]] -= 1.0 - label_smoothing
+    if colmask is not None:
+        g[~colmask] = 0.0
+    g -= label_smoothing / V
     g *= scale[:, None]
     g[~valid] = 0.0
     return g
@@ -198,9 +235,10 @@ class Backward:
 
 
 def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
-             grad_loss=1.0, keep=None, tile=None, bias=None) -> Backward:
+             grad_loss=1.0, keep=None, tile=None, bias=None, label_smoothing: float = 0.0,
+             z_loss: float = 0.0) -> Backward:
     """dE = G C, dC = G^T E and db = G^T 1.  With `keep` (a filter_keep map for
-    `tile` = (Bn, Bv)) G is zeroed on the dropped tiles first."""
+    `tile` = (Bn, Bv)) the softmax part of G is zeroed on the dropped tiles."""
     e = _f64(e)
     c = _f64(c)
     t = np.asarray(targets, dtype=np.int64)
@@ -215,11 +253,11 @@ def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
         sl = slice(s, min(N, s + chunk))
         z = logits(e[sl], c, bias)
         lse = row_logsumexp(z)
-        g = softmax_grad_rows(z, lse, t[sl], scale[sl], valid[sl])
+        cm = None
         if keep is not None:
             Bn, Bv = tile
-            colmask = np.repeat(keep[s // Bn], Bv)[:V]
-            g[:, ~colmask] = 0.0
+            cm = np.broadcast_to(np.repeat(keep[s // Bn], Bv)[:V], z.shape)
+        g = softmax_grad_rows(z, lse, t[sl], scale[sl], valid[sl], label_smoothing, z_loss, cm)
         dE[sl] = g @ c
         dC += g.T @ e[sl]
         db += g.sum(axis=0)
@@ -265,7 +303,8 @@ def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias
 
 
 def dE_rows(e, c, targets, rows, ignore_index: int = -100, reduction: str = "mean",
-            grad_loss=1.0, n_valid: int | None = None, keep=None, tile=None, bias=None) -> np.ndarray:
+            grad_loss=1.0, n_valid: int | None = None, keep=None, tile=None, bias=None,
+            label_smoothing: float = 0.0, z_loss: float = 0.0) -> np.ndarray:
     """dE for selected rows: row i of G C needs only row i of Z.  For mean,
     n_valid is the whole batch's count (pass it in); for none, grad_loss is [N]."""
     e = _f64(e)
@@ -282,17 +321,17 @@ def dE_rows(e, c, targets, rows, ignore_index: int = -100, reduction: str = "mea
         scale = grad_scale(valid_all, reduction, grad_loss)[rows]
     z = logits(e[rows], c, bias)
     lse = row_logsumexp(z)
-    g = softmax_grad_rows(z, lse, t[rows], scale, valid_all[rows])
+    cm = None
     if keep is not None:
         Bn, Bv = tile
-        for k, i in enumerate(rows):
-            colmask = np.repeat(keep[i // Bn], Bv)[:V]
-            g[k, ~colmask] = 0.0
+        cm = np.stack([np.repeat(keep[i // Bn], Bv)[:V] for i in rows])
+    g = softmax_grad_rows(z, lse, t[rows], scale, valid_all[rows], label_smoothing, z_loss, cm)
     return g @ c
 
 
 def G_columns(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction: str = "mean",
-              grad_loss=1.0, keep=None, tile=None, bias=None) -> np.ndarray:
+              grad_loss=1.0, keep=None, tile=None, bias=None, label_smoothing: float = 0.0,
+              z_loss: float = 0.0) -> np.ndarray:
     """Columns j of G for selected vocabulary ids, [N, k]: they need column j of
     Z for all rows and every row's LSE (pass the oracle's own)."""
     e = _f64(e)
@@ -305,14 +344,16 @@ def G_columns(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction
     zc = e @ c[vocab_ids].T                              # [N, k] = Z[:, vocab_ids]
     if bias is not None:
         zc += _f64(bias)[vocab_ids][None, :]
-    g = np.exp(zc - _f64(lse)[:, None])
-    g -= (t[:, None] == vocab_ids[None, :])
-    g *= scale[:, None]
-    g[~valid] = 0.0
+    lse = _f64(lse)
+    g = np.exp(zc - lse[:, None]) * (1.0 + 2.0 * z_loss * lse)[:, None]
+    g -= (1.0 - label_smoothing) * (t[:, None] == vocab_ids[None, :])
     if keep is not None:
         Bn, Bv = tile
         rowblk = np.arange(e.shape[0]) // Bn
         g *= keep[rowblk][:, vocab_ids // Bv]
+    g -= label_smoothing / V
+    g *= scale[:, None]
+    g[~valid] = 0.0
     return g
 
 
@@ -322,9 +363,11 @@ def db_rows(e, c, targets, vocab_ids, lse, **kw) -> np.ndarray:
 
 
 def dC_rows(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction: str = "mean",
-            grad_loss=1.0, keep=None, tile=None, bias=None) -> np.ndarray:
+            grad_loss=1.0, keep=None, tile=None, bias=None, label_smoothing: float = 0.0,
+            z_loss: float = 0.0) -> np.ndarray:
     """dC for selected vocabulary rows j: dC_j = sum_i G_ij e_i, which needs
     column j of Z for all rows and every row's LSE (pass the oracle's own)."""
     g = G_columns(e, c, targets, vocab_ids, lse, ignore_index=ignore_index, reduction=reduction,
-                  grad_loss=grad_loss, keep=keep, tile=tile, bias=bias)
+                  grad_loss=grad_loss, keep=keep, tile=tile, bias=bias,
+                  label_smoothing=label_smoothing, z_loss=z_loss)
     return g.T @ _f64(e)

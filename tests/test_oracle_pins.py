@@ -497,3 +497,164 @@ def test_bias_brute_force_filter_and_sampled():
                        full.dC[vid], rtol=1e-12, atol=1e-15)
     assert np.allclose(O.dE_rows(e, c, t, [0, 7], reduction="sum", bias=b, keep=keep, tile=(Bn, Bv)),
                        full.dE[[0, 7]], rtol=1e-12, atol=1e-15)
+
+
+# --------------------------------------------------------------------------- label smoothing, z-loss
+# Label smoothing eps replaces the one-hot target by (1 - eps) onehot + eps / V
+# (tirogla "Loss functions", "How it works" step 3); the z-loss adds
+# lam * LSE^2 per row (same page, "Implementation notes").
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_label_smoothing_matches_torch_cross_entropy(reduction):
+    """Smoothed loss and gradients equal PyTorch's cross_entropy with
+    label_smoothing (which spreads eps over all V classes, the true one
+    included), differentiated by autograd in float64 on the CPU through
+    Z = E C^T + b."""
+    import torch
+    g = np.random.default_rng(50)
+    N, D, V, eps = 11, 6, 17, 0.15
+    e, c = g.standard_normal((N, D)), g.standard_normal((V, D))
+    b = g.standard_normal(V)
+    t = g.integers(0, V, N)
+    t[[3, 8]] = -100
+    gl = g.standard_normal(N) if reduction == "none" else 0.6
+    te, tc, tb = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (e, c, b))
+    z = te @ tc.T + tb
+    ref = torch.nn.functional.cross_entropy(z, torch.tensor(t), ignore_index=-100, reduction=reduction,
+                                            label_smoothing=eps)
+    ref.backward(torch.tensor(gl, dtype=torch.float64))
+    f = O.forward(e, c, t, reduction=reduction, bias=b, label_smoothing=eps)
+    assert np.allclose(f.loss, ref.detach().numpy(), rtol=1e-12, atol=1e-14)
+    bw = O.backward(e, c, t, reduction=reduction, grad_loss=gl, bias=b, label_smoothing=eps)
+    assert np.allclose(bw.dE, te.grad.numpy(), rtol=1e-11, atol=1e-14)
+    assert np.allclose(bw.dC, tc.grad.numpy(), rtol=1e-11, atol=1e-14)
+    assert np.allclose(bw.db, tb.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+def test_full_smoothing_closed_form():
+    """eps = 1 (uniform target), c = 0, b_j = ln(j + 1): loss_i is
+    LSE - (1/V) sum_j b_j = ln(V (V + 1) / 2) - ln(V!) / V on every valid row,
+    independent of the target, and db_j = sum_i scale_i (p_j - 1/V)."""
+    N, D, V = 5, 3, 7
+    e = np.random.default_rng(51).standard_normal((N, D))
+    c = np.zeros((V, D))
+    b = np.log(np.arange(1, V + 1, dtype=np.float64))
+    t = np.array([0, 6, -100, 2, 2])
+    tot = V * (V + 1) / 2.0
+    f = O.forward(e, c, t, reduction="none", bias=b, label_smoothing=1.0)
+    want = math.log(tot) - math.lgamma(V + 1) / V
+    assert np.allclose(f.nll, [want, want, 0.0, want, want], rtol=1e-13, atol=0)
+    bw = O.backward(e, c, t, reduction="sum", grad_loss=2.0, bias=b, label_smoothing=1.0)
+    assert not bw.dE.any()
+    p = np.arange(1, V + 1) / tot
+    assert np.allclose(bw.db, 4 * 2.0 * (p - 1.0 / V), rtol=1e-12, atol=1e-15)
+
+
+def test_z_loss_closed_form():
+    """c = 0, b_j = ln(j + 1), z-loss lam: LSE = ln(V (V + 1) / 2) = L on every
+    row, loss_i = L - ln(y_i + 1) + lam L^2, and
+    db_j = sum_i scale_i (p_j (1 + 2 lam L) - [y_i = j])."""
+    N, D, V, lam = 6, 2, 9, 0.03
+    e = np.random.default_rng(52).standard_normal((N, D))
+    c = np.zeros((V, D))
+    b = np.log(np.arange(1, V + 1, dtype=np.float64))
+    t = np.array([1, 8, 3, -100, 3, 0])
+    L = math.log(V * (V + 1) / 2.0)
+    f = O.forward(e, c, t, reduction="mean", bias=b, z_loss=lam)
+    want = sum(L - math.log(y + 1) + lam * L * L for y in t if y != -100) / 5
+    assert abs(float(f.loss) - want) < 1e-13
+    bw = O.backward(e, c, t, reduction="mean", bias=b, z_loss=lam)
+    p = np.arange(1, V + 1) / (V * (V + 1) / 2.0)
+    db = np.zeros(V)
+    for y in t:
+        if y != -100:
+            db += p * (1 + 2 * lam * L)
+            db[y] -= 1.0
+    assert np.allclose(bw.db, db / 5, rtol=1e-12, atol=1e-15)
+    assert not bw.dE.any()
+
+
+@pytest.mark.parametrize("eps,lam", [(0.0, 0.05), (0.2, 0.0), (0.2, 0.05)])
+def test_smoothing_z_loss_finite_differences(eps, lam):
+    """Central differences of the oracle's own forward loss against its
+    backward, for every entry of e, c and b (so a dropped factor 2 in the
+    z-loss gradient, or a smoothing term with the wrong sign, fails)."""
+    g = np.random.default_rng(53)
+    N, D, V = 4, 3, 6
+    e, c = g.standard_normal((N, D)), g.standard_normal((V, D))
+    b = g.standard_normal(V)
+    t = g.integers(0, V, N)
+    t[2] = -100
+    kw = dict(reduction="mean", label_smoothing=eps, z_loss=lam)
+    bw = O.backward(e, c, t, bias=b, **kw)
+
+    def loss(e_, c_, b_):
+        return float(O.forward(e_, c_, t, bias=b_, **kw).loss)
+    h = 1e-6
+    for arr, grad, which in ((e, bw.dE, 0), (c, bw.dC, 1), (b, bw.db, 2)):
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            ix = it.multi_index
+            args_p, args_m = [e.copy(), c.copy(), b.copy()], [e.copy(), c.copy(), b.copy()]
+            args_p[which][ix] += h
+            args_m[which][ix] -= h
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grad[ix]) < 1e-8 + 1e-6 * abs(fd), (which, ix, fd, grad[ix])
+
+
+def test_smoothing_filter_keeps_uniform_term():
+    """Filtering with smoothing: a vocab block suppressed by a bias of -60 has
+    softmax below e^-50 everywhere, so its tiles are dropped (but for the one
+    that holds a target), yet the filtered gradients equal the unfiltered ones
+    to 1e-12: the -eps/V term of those entries is kept.  The classifier rows of
+    the block have mean 3, so dropping that term would move dE by about
+    eps/V * 8 * 3 per unit scale.  The sampled forms agree with the full one."""
+    g = np.random.default_rng(54)
+    N, D, V, Bn, Bv, eps, lam = 10, 4, 24, 5, 8, 0.3, 0.01
+    e, c = g.standard_normal((N, D)) * 0.5, g.standard_normal((V, D)) * 0.5
+    c[8:16] += 3.0
+    b = np.zeros(V)
+    b[8:16] = -60.0
+    t = g.choice(np.r_[0:8, 16:24], N)
+    t[1] = 9
+    kw = dict(reduction="sum", bias=b, label_smoothing=eps, z_loss=lam)
+    keep = O.filter_keep(e, c, t, Bn, Bv, bias=b)
+    assert keep[0, 1] and not keep[1, 1]
+    flt = O.backward(e, c, t, keep=keep, tile=(Bn, Bv), **kw)
+    full = O.backward(e, c, t, **kw)
+    for a, w in ((flt.dE, full.dE), (flt.dC, full.dC), (flt.db, full.db)):
+        assert np.allclose(a, w, rtol=0, atol=1e-12)
+    assert np.abs(full.dE).max() > 0.05
+    lse, _ = O.lse_and_keep(e, c, t, Bn, Bv, bias=b)
+    vid = np.array([0, 9, 12, 23])
+    kk = dict(keep=keep, tile=(Bn, Bv), **kw)
+    assert np.allclose(O.db_rows(e, c, t, vid, lse, **kk), flt.db[vid], rtol=1e-12, atol=1e-15)
+    assert np.allclose(O.dC_rows(e, c, t, vid, lse, **kk), flt.dC[vid], rtol=1e-12, atol=1e-15)
+    assert np.allclose(O.dE_rows(e, c, t, [0, 7], **kk), flt.dE[[0, 7]], rtol=1e-12, atol=1e-15)
+
+
+def test_smoothing_filtered_drops_only_softmax_part():
+    """With ordinary logits some tiles are dropped; the filtered and unfiltered
+    dE then differ by exactly the dropped softmax entries times C, each entry
+    below 2^-12 (1 + 2 lam LSE) scale, computed here by loops over entries."""
+    g = np.random.default_rng(55)
+    N, D, V, Bn, Bv, eps, lam = 6, 3, 40, 3, 8, 0.1, 0.02
+    e, c = g.standard_normal((N, D)) * 2.0, g.standard_normal((V, D)) * 2.0
+    t = g.integers(0, V, N)
+    keep = O.filter_keep(e, c, t, Bn, Bv)
+    assert not keep.all()
+    kw = dict(reduction="sum", label_smoothing=eps, z_loss=lam)
+    flt = O.backward(e, c, t, keep=keep, tile=(Bn, Bv), **kw)
+    full = O.backward(e, c, t, **kw)
+    want = full.dE.copy()
+    for i in range(N):
+        zi = [float(np.dot(e[i], c[j])) for j in range(V)]
+        mx = max(zi)
+        L = mx + math.log(sum(math.exp(z - mx) for z in zi))
+        for j in range(V):
+            if not keep[i // Bn, j // Bv]:
+                p = math.exp(zi[j] - L) * (1 + 2 * lam * L)
+                assert p < 2.0 ** -12 * (1 + 2 * lam * L)
+                want[i] -= p * c[j]
+    assert np.allclose(flt.dE, want, rtol=1e-11, atol=1e-14)
