@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 KERNELS = ["fwd_tile", "rows", "reduce", "bwd_prep", "filter", "grad_tile", "dC_gemm", "dE_gemm", "dE_reduce",
-           "fill_zero", "transpose_e", "db_reduce"]
+           "fill_zero", "transpose_e", "db_reduce", "colsum", "colsum_reduce", "vec_sum", "fill_rank1"]
 MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # Measured memory traffic per launch (bytes past L2: rocprofv3 FETCH_SIZE x 2.0
 # + WRITE_SIZE x 1.0, the factors a 1 GiB device copy calibrates in the same
@@ -188,10 +188,12 @@ def make_bias(V, dtype, dev, seed=7):
     return (torch.randn(V, generator=g) * 0.5).to(dtype).to(dev)
 
 
-def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=False):
+def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=False, label_smoothing=0.0,
+                   z_loss=0.0):
     """Compact forward / forward+backward figures for one workload (defaults:
     filter on, deterministic, the workload's own reduction; with_bias adds a
-    classifier bias and asks for its gradient)."""
+    classifier bias and asks for its gradient; label_smoothing / z_loss add
+    those loss terms)."""
     import torch
     import workloads as W
     import linear_cross_entropy_forward_amd as M
@@ -229,15 +231,16 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
 
     def fwd():
         r = L.cce_forward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, 0.0,
-                          loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(), ws.numel(), st.cuda_stream)
+                          label_smoothing, z_loss, loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(),
+                          ws.numel(), st.cuda_stream)
         if r:
             raise RuntimeError(f"cce_forward failed: {r}")
 
     def step():
         fwd()
         r = L.cce_backward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, 0.0,
-                           lse.data_ptr(), g.data_ptr(), 1, 0, 0, dE.data_ptr(), dC.data_ptr(), dbp, ws.data_ptr(),
-                           ws.numel(), st.cuda_stream)
+                           label_smoothing, z_loss, lse.data_ptr(), g.data_ptr(), 1, 0, 0, dE.data_ptr(),
+                           dC.data_ptr(), dbp, ws.data_ptr(), ws.numel(), st.cuda_stream)
         if r:
             raise RuntimeError(f"cce_backward failed: {r}")
 
@@ -262,12 +265,14 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
            "fwd_tokens_per_s": N / (fwd_ms * 1e-3), "step_ms": step_ms, "tokens_per_s": N / (step_ms * 1e-3),
            "tflops_effective": eff, "pct_of_peak": 100.0 * eff / peak,
            "tiles_skipped_frac": 1.0 - stats["tiles_kept"] / max(1, stats["tiles_total"]),
-           "extra_hbm_bytes": int(extra), "bias": bool(with_bias)}
-    if w.dtype == "bf16" and not with_bias:
+           "extra_hbm_bytes": int(extra), "bias": bool(with_bias), "label_smoothing": label_smoothing,
+           "z_loss": z_loss}
+    plain = not with_bias and label_smoothing == 0.0 and z_loss == 0.0
+    if w.dtype == "bf16" and plain:
         out["hipblaslt_fwd_gemm_tflops"] = hipblaslt_gemm_tflops(c, e)
     del ws, loss, lse, nv, g, dE, dC, bias, db
     torch.cuda.empty_cache()
-    if materialized_too and not with_bias:
+    if materialized_too and plain:
         mat_ms, mat_peak = materialized(e, c, t, w.reduction, max(1, min(steps, 3)))
         out["materialized_step_ms"] = mat_ms
         out["materialized_peak_extra_bytes"] = int(mat_peak)
@@ -326,10 +331,10 @@ def main():
 
     def step():
         s = stream.cuda_stream
-        r1 = L.cce_forward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0,
+        r1 = L.cce_forward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0, 0.0,
                            loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(), ws.numel(), s)
-        r2 = L.cce_backward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0,
-                            lse.data_ptr(), g.data_ptr(), flt, acc, args.vocab_chunk, dE.data_ptr(), dC.data_ptr(),
+        r2 = L.cce_backward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0,
+                            0.0, lse.data_ptr(), g.data_ptr(), flt, acc, args.vocab_chunk, dE.data_ptr(), dC.data_ptr(),
                             None, ws.data_ptr(), ws.numel(), s)
         if r1 or r2:
             raise RuntimeError(f"cce call failed: {r1} {r2}")
@@ -365,7 +370,8 @@ def main():
     f1 = torch.cuda.Event(enable_timing=True)
     f0.record(stream)
     for _ in range(args.steps):
-        L.cce_forward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, loss.data_ptr(),
+        L.cce_forward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0, 0.0,
+                      loss.data_ptr(),
                       lse.data_ptr(), nv.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
     f1.record(stream)
     torch.cuda.synchronize()
@@ -426,6 +432,9 @@ def main():
                 configs[name] = config_summary(name)
         # the headline workload with a classifier bias and its gradient
         configs[args.workload + "+bias"] = config_summary(args.workload, with_bias=True)
+        # ... and with label smoothing 0.1 and z-loss 1e-4
+        configs[args.workload + "+smoothing+zloss"] = config_summary(args.workload, label_smoothing=0.1,
+                                                                     z_loss=1e-4)
 
     cpu = None
     if not args.no_cpu_baseline:

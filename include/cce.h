@@ -22,6 +22,15 @@
  * skipping (token block, vocab block) tiles on which every softmax value is
  * below 2^-12 (README "How it works" item 2; Wijmans et al. abstract).
  *
+ * Two optional loss terms follow tirogla "Loss functions": label smoothing
+ * eps ("How it works" step 3) replaces the one-hot target by the soft target
+ * T_i = (1 - eps) onehot(y_i) + eps / V (over all V classes, the true one
+ * included), so loss_i = -sum_j T_ij log softmax_ij and G = (softmax - T) *
+ * scale; the z-loss lam ("Implementation notes") adds lam * LSE_i^2 to
+ * loss_i, which adds 2 lam LSE_i softmax_ij to G.  Filtering still decides on
+ * the softmax and drops only its part of G: the uniform -eps/V * scale_i part
+ * is applied to every entry (as a rank-one term of dE, dC and dbias).
+ *
  * Conventions for every call:
  *  - Pointers marked (device) are device memory on the current HIP device;
  *    (host) are host memory.  The library never allocates, frees or
@@ -32,7 +41,8 @@
  *    [N, D], c is [V, D] (D contiguous); e and c share one dtype; outputs are
  *    float32.  D must be a multiple of 8 (bf16) or 4 (float32).
  *  - Errors: argument and size faults are reported synchronously, before any
- *    launch, as a negative cce_status.  A target outside [0, V) that is not
+ *    launch, as a negative cce_status (label_smoothing outside [0, 1] or a
+ *    negative or non-finite z_loss is CCE_ERR_INVALID_ARG).  A target outside [0, V) that is not
  *    ignore_index is not a host-visible fault: its row's loss is NaN (so a
  *    mean or sum is NaN), its gradient row is NaN, and cce_read_stats
  *    reports it in bad_targets.  No exception crosses the ABI.
@@ -83,7 +93,7 @@ typedef struct {
  * the two by default), plus e transposed (N*D elements); a positive
  * value (a multiple of 256) sets the chunk width, trading workspace for
  * launches.  The forward uses only the first part (per-row partials,
- * O(N + N*V/128) floats).  Returns 0 for invalid arguments.
+ * O(N + N*V/128 + 512*D) floats).  Returns 0 for invalid arguments.
  */
 size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk);
 
@@ -99,7 +109,10 @@ int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk);
  * Forward.  e (device) [N, D], c (device) [V, D] of `dtype`; bias (device)
  * [V] of `dtype` or NULL: the optional classifier bias of the mlx-cross-entropy
  * README ("API" table), added to every row of the logits, z = e c^T + b;
- * targets (device) int64 [N].  reduction: CCE_REDUCTION_NONE writes loss[N] (0 on ignored rows);
+ * targets (device) int64 [N].  label_smoothing (eps in [0, 1]) and z_loss (lam >= 0)
+ * are the optional terms above, 0 for the plain loss; eps > 0 adds two
+ * HBM-bound passes (a column sum of c over the vocabulary, and of the bias).
+ * reduction: CCE_REDUCTION_NONE writes loss[N] (0 on ignored rows);
  * SUM / MEAN write loss[0] (MEAN divides by max(n_valid, 1)).  lse (device)
  * float [N] receives every row's LSE (ignored rows included).  n_valid
  * (device) int32 [1] receives the non-ignored count; may be NULL.  softcap must
@@ -110,13 +123,14 @@ int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk);
  */
 cce_status cce_forward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
                        int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
-                       float* loss, float* lse, int32_t* n_valid, void* ws, size_t ws_bytes,
-                       cce_stream_t stream);
+                       float label_smoothing, float z_loss, float* loss, float* lse, int32_t* n_valid, void* ws,
+                       size_t ws_bytes, cce_stream_t stream);
 
 /*
- * Backward.  Same e, c, bias, targets, sizes, dtype, ignore_index, reduction
- * and softcap as the forward; lse (device) float [N] is the forward's output and
- * ws is the forward's workspace, unmodified.  grad_loss (device) float is the
+ * Backward.  Same e, c, bias, targets, sizes, dtype, ignore_index, reduction,
+ * softcap, label_smoothing and z_loss as the forward; lse (device) float [N] is
+ * the forward's output and ws is the forward's workspace, unmodified (with
+ * label smoothing it also holds the forward's column sum of c).  grad_loss (device) float is the
  * upstream gradient: [N] for NONE, [1] otherwise.  filter = 1 skips tiles
  * whose softmax is below 2^-12 everywhere (and that hold no target); 0
  * computes every tile.  accum = CCE_ACCUM_DETERMINISTIC gives run-to-run
@@ -130,9 +144,9 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
  */
 cce_status cce_backward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
                         int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
-                        const float* lse, const float* grad_loss, int filter, int accum,
-                        int64_t vocab_chunk, float* dE, float* dC, float* dbias, void* ws, size_t ws_bytes,
-                        cce_stream_t stream);
+                        float label_smoothing, float z_loss, const float* lse, const float* grad_loss, int filter,
+                        int accum, int64_t vocab_chunk, float* dE, float* dC, float* dbias, void* ws,
+                        size_t ws_bytes, cce_stream_t stream);
 
 /*
  * Copies the workspace counters to `out` (host) after the work queued on
@@ -155,9 +169,9 @@ void cce_tile_shape(int* filter_rows, int* filter_vocab, int* partial_vocab);
  * cce_profile_stop waits for those events and returns the summed elapsed time
  * (host double, ms) and the number of launches timed (host int).  The hook
  * holds process-wide state: it is meant for benchmarks and is not
- * thread-safe.  Kernel ids 0..11 are fwd_tile, rows, reduce, bwd_prep, filter,
- * grad_tile, dC_gemm, dE_gemm, dE_reduce, fill_zero, transpose_e, db_reduce
- * (cce_kernel_name).
+ * thread-safe.  Kernel ids 0..15 are fwd_tile, rows, reduce, bwd_prep, filter,
+ * grad_tile, dC_gemm, dE_gemm, dE_reduce, fill_zero, transpose_e, db_reduce,
+ * colsum, colsum_reduce, vec_sum, fill_rank1 (cce_kernel_name).
  */
 cce_status cce_profile_start(int kernel_id, int max_launches);
 cce_status cce_profile_stop(int kernel_id, double* total_ms, int* launches);

@@ -58,10 +58,11 @@ def lib() -> ctypes.CDLL:
     L.cce_vocab_chunk.restype = i64
     L.cce_vocab_chunk.argtypes = [i64, i64, i32, i64]
     L.cce_forward.restype = i32
-    L.cce_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.cce_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, f32, f32, vp, vp, vp, vp, sz,
+                              vp]
     L.cce_backward.restype = i32
-    L.cce_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, vp, vp, i32, i32, i64, vp, vp,
-                               vp, vp, sz, vp]
+    L.cce_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, f32, f32, vp, vp, i32, i32, i64,
+                               vp, vp, vp, vp, sz, vp]
     L.cce_read_stats.restype = i32
     L.cce_read_stats.argtypes = [vp, sz, i64, i64, vp, ctypes.POINTER(_Stats)]
     L.cce_status_string.restype = ctypes.c_char_p
@@ -147,11 +148,13 @@ def _validate_bias(bias, c):
 
 def forward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, ignore_index: int = -100,
             reduction: str = "mean", softcap: float = 0.0, ws: torch.Tensor | None = None,
-            vocab_chunk: int = 0, bias: torch.Tensor | None = None):
+            vocab_chunk: int = 0, bias: torch.Tensor | None = None, label_smoothing: float = 0.0,
+            z_loss: float = 0.0):
     """cce_forward.  Returns (loss, lse, n_valid, ws); loss is [N] for
     reduction='none', else a 0-dim tensor.  `ws` (uint8, device) is allocated
     if not given and must be passed unchanged to backward().  `bias` [V] (the
-    classifier's dtype) is optional."""
+    classifier's dtype) is optional; label_smoothing (eps in [0, 1]) and
+    z_loss (lam >= 0) add the soft-target and lam * LSE^2 terms."""
     _validate(e, c, targets)
     _validate_bias(bias, c)
     N, D = e.shape
@@ -165,8 +168,8 @@ def forward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, ignore_inde
     lse = torch.empty(N, dtype=torch.float32, device=dev)
     n_valid = torch.empty(1, dtype=torch.int32, device=dev)
     _check(lib().cce_forward(_ptr(e), _ptr(c), _ptr(bias) if bias is not None else None, _ptr(targets), N, D, V,
-                             _dtype_code(e), ignore_index, red,
-                             softcap, _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(ws), ws.numel(), _stream()),
+                             _dtype_code(e), ignore_index, red, softcap, label_smoothing, z_loss,
+                             _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(ws), ws.numel(), _stream()),
            "cce_forward")
     return (loss if red == 0 else loss[0]), lse, n_valid, ws
 
@@ -175,9 +178,10 @@ def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch
              grad_loss: torch.Tensor, ws: torch.Tensor, ignore_index: int = -100, reduction: str = "mean",
              filter: bool = True, accum: str = "deterministic", softcap: float = 0.0, vocab_chunk: int = 0,
              dE: torch.Tensor | None = None, dC: torch.Tensor | None = None, bias: torch.Tensor | None = None,
-             want_dbias: bool = False):
+             want_dbias: bool = False, label_smoothing: float = 0.0, z_loss: float = 0.0):
     """cce_backward.  grad_loss is float32 [N] ('none') or [1]/0-dim.  Returns
-    float32 (dE [N, D], dC [V, D]), plus db [V] when want_dbias."""
+    float32 (dE [N, D], dC [V, D]), plus db [V] when want_dbias.  bias,
+    label_smoothing and z_loss must be those of the forward that filled ws."""
     _validate(e, c, targets)
     _validate_bias(bias, c)
     N, D = e.shape
@@ -190,7 +194,8 @@ def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch
         dC = torch.empty((V, D), dtype=torch.float32, device=dev)
     db = torch.empty(V, dtype=torch.float32, device=dev) if want_dbias else None
     _check(lib().cce_backward(_ptr(e), _ptr(c), _ptr(bias) if bias is not None else None, _ptr(targets), N, D, V,
-                              _dtype_code(e), ignore_index, _REDUCTIONS[reduction], softcap, _ptr(lse), _ptr(g),
+                              _dtype_code(e), ignore_index, _REDUCTIONS[reduction], softcap, label_smoothing,
+                              z_loss, _ptr(lse), _ptr(g),
                               int(bool(filter)), _ACCUM[accum], vocab_chunk, _ptr(dE), _ptr(dC),
                               _ptr(db) if db is not None else None, _ptr(ws), ws.numel(), _stream()),
            "cce_backward")
@@ -206,42 +211,48 @@ def read_stats(ws: torch.Tensor, N: int, V: int) -> dict:
 
 class _CCEFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, e, c, bias, targets, reduction, ignore_index, filter, accum):
-        loss, lse, _, ws = forward(e, c, targets, ignore_index=ignore_index, reduction=reduction, bias=bias)
+    def forward(ctx, e, c, bias, targets, reduction, ignore_index, filter, accum, label_smoothing, z_loss):
+        loss, lse, _, ws = forward(e, c, targets, ignore_index=ignore_index, reduction=reduction, bias=bias,
+                                   label_smoothing=label_smoothing, z_loss=z_loss)
         ctx.save_for_backward(e, c, bias, targets, lse, ws)
-        ctx.cfg = (reduction, ignore_index, filter, accum)
+        ctx.cfg = (reduction, ignore_index, filter, accum, label_smoothing, z_loss)
         return loss
 
     @staticmethod
     def backward(ctx, grad):
         e, c, bias, targets, lse, ws = ctx.saved_tensors
-        reduction, ignore_index, filter, accum = ctx.cfg
+        reduction, ignore_index, filter, accum, label_smoothing, z_loss = ctx.cfg
         want_db = bias is not None and ctx.needs_input_grad[2]
         out = backward(e, c, targets, lse, grad, ws, ignore_index=ignore_index, reduction=reduction,
-                       filter=filter, accum=accum, bias=bias, want_dbias=want_db)
+                       filter=filter, accum=accum, bias=bias, want_dbias=want_db,
+                       label_smoothing=label_smoothing, z_loss=z_loss)
         dE, dC = out[0], out[1]
         db = out[2].to(bias.dtype) if want_db else None
         # autograd wants gradients in the inputs' dtype
-        return dE.to(e.dtype), dC.to(c.dtype), db, None, None, None, None, None
+        return dE.to(e.dtype), dC.to(c.dtype), db, None, None, None, None, None, None, None
 
 
 def cce_loss(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, reduction: str = "mean",
              ignore_index: int = -100, filter: bool = True, accum: str = "deterministic",
-             bias: torch.Tensor | None = None) -> torch.Tensor:
+             bias: torch.Tensor | None = None, label_smoothing: float = 0.0, z_loss: float = 0.0) -> torch.Tensor:
     """Flat form: e [N, D], c [V, D], targets [N], optional bias [V]."""
     return _CCEFunction.apply(e.contiguous(), c.contiguous(), None if bias is None else bias.contiguous(),
-                              targets.contiguous().to(torch.int64), reduction, ignore_index, filter, accum)
+                              targets.contiguous().to(torch.int64), reduction, ignore_index, filter, accum,
+                              float(label_smoothing), float(z_loss))
 
 
 def linear_cross_entropy(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, bias=None,
                          reduction: str = "mean", ignore_index: int = -100, filter: bool = True,
-                         accum: str = "deterministic") -> torch.Tensor:
+                         accum: str = "deterministic", label_smoothing: float = 0.0,
+                         z_loss: float = 0.0) -> torch.Tensor:
     """Cross-entropy of softmax(e @ c.T + bias) against targets without forming
     the logits.  e [..., D], c [V, D], targets [...], bias [V] or None;
-    'none' returns a tensor shaped like targets."""
+    'none' returns a tensor shaped like targets.  label_smoothing spreads eps
+    over all V classes; z_loss adds z_loss * LSE^2 per row."""
     if reduction not in _REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(_REDUCTIONS)}")
     shape = targets.shape
     D = e.shape[-1]
-    out = cce_loss(e.reshape(-1, D), c, targets.reshape(-1), reduction, ignore_index, filter, accum, bias=bias)
+    out = cce_loss(e.reshape(-1, D), c, targets.reshape(-1), reduction, ignore_index, filter, accum, bias=bias,
+                   label_smoothing=label_smoothing, z_loss=z_loss)
     return out.reshape(shape) if reduction == "none" else out

@@ -61,6 +61,12 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const size_t o_hdr = take(kHdrWords * 4);
   const size_t o_part = take((size_t)N * L.nVB * sizeof(float2));
   const size_t o_nll = take((size_t)N * 4);
+  const size_t o_csum = take((size_t)D * 4);
+  const size_t o_aux = take(64);
+  const size_t o_colp = take((size_t)kColBlocks * (size_t)D * 4);
+  const size_t o_r1c = take((size_t)D * 4);
+  // the offsets above do not depend on the vocab chunk; the forward uses
+  // only that leading part
   const size_t o_scale = take((size_t)L.Npad * 4);
   const size_t o_keep = take((size_t)L.nb * L.nvb_t);
   const size_t o_g = take(L.g_bytes);
@@ -81,6 +87,10 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     L.Et = b + o_et;
     L.dE_part = (float*)(b + o_dep);
     L.db_part = (float*)(b + o_dbp);
+    L.csum = (float*)(b + o_csum);
+    L.r1c = (float*)(b + o_r1c);
+    L.aux = (float*)(b + o_aux);
+    L.colpart = (float*)(b + o_colp);
   }
   return L;
 }
@@ -144,7 +154,7 @@ static void prof_release(ProfSlot& p) {
 
 static const char* const kKernelNames[kNumKernels] = {
     "fwd_tile", "rows", "reduce", "bwd_prep", "filter", "grad_tile", "dC_gemm", "dE_gemm", "dE_reduce",
-    "fill_zero", "transpose_e", "db_reduce"};
+    "fill_zero", "transpose_e", "db_reduce", "colsum", "colsum_reduce", "vec_sum", "fill_rank1"};
 
 }  // namespace cce
 
@@ -168,12 +178,18 @@ static bool bias_ok(const void* bias, int dtype) {
   return ((uintptr_t)bias & (dtype == kDtypeBf16 ? 1u : 3u)) == 0;
 }
 
+// eps in [0, 1] and lam >= 0, both finite (NaN fails every comparison)
+static bool terms_ok(float label_smoothing, float z_loss) {
+  return label_smoothing >= 0.0f && label_smoothing <= 1.0f && z_loss >= 0.0f && z_loss <= 3.0e38f;
+}
+
 cce_status cce_forward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
                        int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
-                       float* loss, float* lse, int32_t* n_valid, void* ws, size_t ws_bytes, cce_stream_t stream) {
+                       float label_smoothing, float z_loss, float* loss, float* lse, int32_t* n_valid, void* ws,
+                       size_t ws_bytes, cce_stream_t stream) {
   cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, ws, 0);
   if (st != CCE_OK) return st;
-  if (!bias_ok(bias, dtype)) return CCE_ERR_INVALID_ARG;
+  if (!bias_ok(bias, dtype) || !terms_ok(label_smoothing, z_loss)) return CCE_ERR_INVALID_ARG;
   if (!loss || !lse) return CCE_ERR_INVALID_ARG;
   // The forward only touches the leading (chunk-independent) part of the
   // layout; any workspace sized for some vocab_chunk is large enough for it.
@@ -192,6 +208,8 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
   P.dtype = dtype;
   P.ignore_index = ignore_index;
   P.reduction = reduction;
+  P.label_smoothing = label_smoothing;
+  P.z_loss = z_loss;
   P.loss = loss;
   P.lse = lse;
   P.n_valid = n_valid;
@@ -201,11 +219,13 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
 
 cce_status cce_backward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
                         int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
-                        const float* lse, const float* grad_loss, int filter, int accum, int64_t vocab_chunk,
-                        float* dE, float* dC, float* dbias, void* ws, size_t ws_bytes, cce_stream_t stream) {
+                        float label_smoothing, float z_loss, const float* lse, const float* grad_loss, int filter,
+                        int accum, int64_t vocab_chunk, float* dE, float* dC, float* dbias, void* ws,
+                        size_t ws_bytes, cce_stream_t stream) {
   cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, ws, vocab_chunk);
   if (st != CCE_OK) return st;
-  if (!bias_ok(bias, dtype) || ((uintptr_t)dbias & 3u)) return CCE_ERR_INVALID_ARG;
+  if (!bias_ok(bias, dtype) || ((uintptr_t)dbias & 3u) || !terms_ok(label_smoothing, z_loss))
+    return CCE_ERR_INVALID_ARG;
   if (!lse || !grad_loss || !dE || !dC) return CCE_ERR_INVALID_ARG;
   if ((filter != 0 && filter != 1) || (accum != kAccumDeterministic && accum != kAccumAtomic))
     return CCE_ERR_INVALID_ARG;
@@ -223,6 +243,8 @@ cce_status cce_backward(const void* e, const void* c, const void* bias, const in
   P.dtype = dtype;
   P.ignore_index = ignore_index;
   P.reduction = reduction;
+  P.label_smoothing = label_smoothing;
+  P.z_loss = z_loss;
   P.lse = (float*)lse;
   P.grad_loss = grad_loss;
   P.filter = filter;

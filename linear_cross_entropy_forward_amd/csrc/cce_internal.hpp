@@ -16,6 +16,10 @@ constexpr int kTileV = 256;
 constexpr int kTileN = 256;
 constexpr int kPartialWidth = 128;
 constexpr int kMaxBlocks = 4096;  // K blocks one contraction tile can list
+// Row blocks of the column-sum kernel (partials [kColBlocks][D] in the
+// workspace) and the fewest rows one block takes.
+constexpr int kColBlocks = 512;
+constexpr int kColMinRows = 64;
 
 constexpr int kDtypeBf16 = 0;
 constexpr int kDtypeF32 = 1;
@@ -49,6 +53,8 @@ struct Problem {
   int dtype;
   int64_t ignore_index;
   int reduction;
+  float label_smoothing;  // eps in [0, 1]: soft target (1 - eps) onehot + eps / V
+  float z_loss;           // lam >= 0: loss_i += lam * LSE_i^2
   // forward outputs / backward inputs
   float* loss;
   float* lse;
@@ -69,6 +75,10 @@ struct Layout {
   float* nll_out;   // [N] per-row loss (the caller's loss buffer for 'none')
   float* scale;     // [Npad]
   float* db_part;   // [Npad/256][V] per token block column sums of G (bias gradient)
+  float* csum;      // [D] sum over the vocabulary of the classifier rows (label smoothing)
+  float* r1c;       // [D] -eps/V * sum_i scale_i e_i: the smoothing term of every dC row
+  float* aux;       // [0] sum of the bias, [1] sum_i scale_i
+  float* colpart;   // [kColBlocks][D] column-sum partials
   uint8_t* keep;    // [nb][nvb_t]
   void* G;          // [Npad][Vc] operand type: gradient tiles of one vocab chunk
   void* Gt;         // [Vc][gt_ld] the same tiles transposed (columns past Npad unused)
@@ -87,7 +97,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
 // Kernel ids of the profiling hook (cce_profile_start / cce_profile_stop).
 enum KernelId {
   kKFwdTile = 0, kKRows, kKReduce, kKBwdPrep, kKFilter, kKGradTile, kKDC, kKDE, kKDEReduce, kKFill,
-  kKTransE, kKDbReduce, kNumKernels
+  kKTransE, kKDbReduce, kKColSum, kKColReduce, kKVecSum, kKFillRank1, kNumKernels
 };
 // Records start/stop events around one launch of kernel `id` when profiling of
 // that id is active (no-op otherwise).

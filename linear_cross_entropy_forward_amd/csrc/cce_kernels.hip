@@ -10,6 +10,9 @@
 //           rows          correct-token gather-dot, LSE = combine of partials,
 //                         per-row loss (ignore mask)
 //           reduce        fixed-order mean / sum and the exact valid count
+//           colsum(+reduce) with label smoothing: sum over the vocabulary of
+//                         the classifier rows (and vec_sum of the bias), so
+//                         that sum_j z_ij = e_i . csum + sum_j b_j
 // Backward: bwd_prep      per-row gradient scale (mean/sum/none, ignore mask)
 //           filter        tile keep map: a (token block, vocab block) tile is
 //                         kept iff some valid row's softmax reaches 2^-12 on it
@@ -21,6 +24,14 @@
 //           dE_gemm       dE   += sum over kept vocab blocks of G C
 //                         (split over vocab, fixed-order partial reduce, or
 //                         fp32 atomics)
+// Label smoothing eps makes the target (1 - eps) onehot + eps / V and z-loss
+// lam adds lam LSE^2 (tirogla "Loss functions", step 3 and "Implementation
+// notes"), so G = (p (1 + 2 lam LSE) - (1 - eps) onehot) * scale - eps / V *
+// scale.  The last term is the same for every vocabulary entry of a row: the
+// tiles carry the rest, and its rank-one share of dE, dC and db (a row scale
+// times the classifier column sum, minus eps/V times sum_i scale_i e_i, minus
+// eps/V times sum_i scale_i) is added in the epilogues, exactly, kept tile or
+// not.
 #include "cce_gemm.hpp"
 #include "cce_internal.hpp"
 
@@ -257,12 +268,17 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
 // Per-row: correct-token logit (gather-dot), LSE from the partials, loss.
 // One wave per row.
 // ============================================================================
-template <typename T>
+// With SMOOTH, also e_i . csum (plus the bias sum aux[0]) = sum_j z_ij, the
+// smoothing term's logit sum.  loss_i = LSE - (1 - eps) z_y - eps / V sum_j
+// z_ij + lam LSE^2 (the soft-target cross-entropy, since the target sums to 1).
+template <typename T, bool SMOOTH>
 __global__ __launch_bounds__(256) void rows_kernel(const T* __restrict__ e, const T* __restrict__ c,
                                                    const T* __restrict__ bias,
                                                    const int64_t* __restrict__ targets, int N, int D,
                                                    int V, int64_t ignore_index,
                                                    const float2* __restrict__ part, int nVB,
+                                                   const float* __restrict__ csum, const float* __restrict__ aux,
+                                                   float eps, float lam,
                                                    float* __restrict__ lse_out, float* __restrict__ nll) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -272,32 +288,51 @@ __global__ __launch_bounds__(256) void rows_kernel(const T* __restrict__ e, cons
   const bool inrange = t >= 0 && t < V;
   constexpr int VEC = Elem<T>::VEC;
 
-  float zy = 0.f;
+  float zy = 0.f, zs = 0.f;
   if (valid && inrange) {
     // plain global loads: the row pointers differ per wave, and the loop bound
     // keeps every 16-byte access inside the row
     const T* er = e + (size_t)i * D;
     const T* cr = c + (size_t)t * D;
-    float acc = 0.f;
+    float acc = 0.f, accs = 0.f;
     for (int k = lane * VEC; k < D; k += 64 * VEC) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(er + k);
       const u32x4 b = *reinterpret_cast<const u32x4*>(cr + k);
+      float cs[VEC];
+      if constexpr (SMOOTH) {
+#pragma unroll
+        for (int h = 0; h < VEC / 4; ++h) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(csum + k + 4 * h);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) cs[4 * h + u] = v[u];
+        }
+      }
       // (vector elements are copied to scalars before any bit cast: clang
       // mis-lowers a bit cast applied directly to a vector-element lvalue)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t x = a[q], y = b[q];
         if constexpr (sizeof(T) == 2) {
-          acc = __builtin_fmaf(__builtin_bit_cast(float, x << 16), __builtin_bit_cast(float, y << 16), acc);
-          acc = __builtin_fmaf(__builtin_bit_cast(float, x & 0xffff0000u), __builtin_bit_cast(float, y & 0xffff0000u),
-                               acc);
+          const float x0 = __builtin_bit_cast(float, x << 16), x1 = __builtin_bit_cast(float, x & 0xffff0000u);
+          acc = __builtin_fmaf(x0, __builtin_bit_cast(float, y << 16), acc);
+          acc = __builtin_fmaf(x1, __builtin_bit_cast(float, y & 0xffff0000u), acc);
+          if constexpr (SMOOTH) {
+            accs = __builtin_fmaf(x0, cs[2 * q], accs);
+            accs = __builtin_fmaf(x1, cs[2 * q + 1], accs);
+          }
         } else {
-          acc = __builtin_fmaf(__builtin_bit_cast(float, x), __builtin_bit_cast(float, y), acc);
+          const float x0 = __builtin_bit_cast(float, x);
+          acc = __builtin_fmaf(x0, __builtin_bit_cast(float, y), acc);
+          if constexpr (SMOOTH) accs = __builtin_fmaf(x0, cs[q], accs);
         }
       }
     }
     zy = wave_sum(acc);
     if (bias) zy += to_f<T>(bias[t]);
+    if constexpr (SMOOTH) {
+      zs = wave_sum(accs);
+      if (bias) zs += aux[0];
+    }
   }
 
   const float2* p = part + (size_t)i * nVB;
@@ -314,7 +349,9 @@ __global__ __launch_bounds__(256) void rows_kernel(const T* __restrict__ e, cons
   const float lse = m + fast_log2(s) * kLn2;
   if (lane == 0) {
     lse_out[i] = lse;
-    nll[i] = valid ? (inrange ? lse - zy : __builtin_nanf("")) : 0.f;
+    float l = lse - (1.f - eps) * zy + lam * lse * lse;
+    if constexpr (SMOOTH) l -= eps / (float)V * zs;
+    nll[i] = valid ? (inrange ? l : __builtin_nanf("")) : 0.f;
   }
 }
 
@@ -362,14 +399,96 @@ __global__ __launch_bounds__(1024) void reduce_kernel(const float* __restrict__ 
 }
 
 // ============================================================================
+// Column sums for the label-smoothing term.  part[b][d] = sum over the rows r
+// of row block b (rows [b rpb, (b + 1) rpb)) of w_r x[r][d], w = 1 when null;
+// then out[d] = factor * sum_b part[b][d].  A thread owns one 16-byte column
+// group and walks its block's rows in order, eight loads in flight; both
+// passes add in a fixed order (deterministic).
+// ============================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ x, const float* __restrict__ w, int R,
+                                                     int D, int rpb, float* __restrict__ part) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int d = (blockIdx.x * 256 + threadIdx.x) * VEC;
+  if (d >= D) return;
+  const int r0 = blockIdx.y * rpb, r1 = min(R, r0 + rpb);
+  float acc[VEC] = {};
+  auto add = [&](const u32x4& v, float wr) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t u = v[q];
+      if constexpr (sizeof(T) == 2) {
+        acc[2 * q] = __builtin_fmaf(wr, __builtin_bit_cast(float, u << 16), acc[2 * q]);
+        acc[2 * q + 1] = __builtin_fmaf(wr, __builtin_bit_cast(float, u & 0xffff0000u), acc[2 * q + 1]);
+      } else {
+        acc[q] = __builtin_fmaf(wr, __builtin_bit_cast(float, u), acc[q]);
+      }
+    }
+  };
+  int r = r0;
+  for (; r + 8 <= r1; r += 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const u32x4*>(x + (size_t)(r + k) * D + d);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) add(v[k], w ? w[r + k] : 1.f);
+  }
+  for (; r < r1; ++r) add(*reinterpret_cast<const u32x4*>(x + (size_t)r * D + d), w ? w[r] : 1.f);
+  float* o = part + (size_t)blockIdx.y * D + d;
+#pragma unroll
+  for (int h = 0; h < VEC / 4; ++h)
+    *reinterpret_cast<f32x4*>(o + 4 * h) = f32x4{acc[4 * h], acc[4 * h + 1], acc[4 * h + 2], acc[4 * h + 3]};
+}
+
+// 64 columns per work-group: wave w adds the blocks [w nblk/16, (w+1) nblk/16)
+// of its lane's column, then the 16 wave sums are added in wave order.
+__global__ __launch_bounds__(1024) void colsum_reduce_kernel(const float* __restrict__ part, int nblk, int D,
+                                                             float factor, float* __restrict__ out) {
+  __shared__ float sw[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int d = blockIdx.x * 64 + lane;
+  const int b0 = nblk * w / 16, b1 = nblk * (w + 1) / 16;
+  float s = 0.f;
+  if (d < D) {
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) s += part[(size_t)b * D + d];
+  }
+  sw[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && d < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t += sw[k][lane];
+    out[d] = factor * t;
+  }
+}
+
+// out[0] = sum of x[0..n) (one work-group, fixed order).
+template <typename T>
+__global__ __launch_bounds__(1024) void vec_sum_kernel(const T* __restrict__ x, int n, float* __restrict__ out) {
+  __shared__ float s[1024];
+  float a = 0.f;
+  for (int i = threadIdx.x; i < n; i += 1024) a += to_f<T>(x[i]);
+  s[threadIdx.x] = a;
+  __syncthreads();
+  for (int o = 512; o >= 1; o >>= 1) {
+    if ((int)threadIdx.x < o) s[threadIdx.x] += s[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = s[0];
+}
+
+// ============================================================================
 // Backward: per-row scale  d(loss)/d(nll_i) * upstream gradient, 0 if ignored,
 // NaN for an out-of-range target; rows in [N, Npad) get 0.
 // ============================================================================
 __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int64_t* __restrict__ targets, int N,
                                                         int Npad, int V, int64_t ignore_index,
                                                         int reduction, const float* __restrict__ grad_loss,
-                                                        float* __restrict__ scale, int32_t* __restrict__ hdr) {
+                                                        float* __restrict__ scale, int32_t* __restrict__ hdr,
+                                                        float* __restrict__ scale_sum) {
   __shared__ int scnt[1024];
+  __shared__ float ssum[1024];
   const int tid = threadIdx.x;
   int cnt = 0;
   for (int i = tid; i < N; i += 1024) cnt += targets[i] != ignore_index;
@@ -382,6 +501,7 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int64_t* __restric
   const int nv = scnt[0];
   const float g0 = reduction == kReductionNone ? 0.f : grad_loss[0];
   const float gm = reduction == kReductionMean ? (float)((double)g0 / (double)(nv > 0 ? nv : 1)) : g0;
+  float acc = 0.f;
   for (int i = tid; i < Npad; i += 1024) {
     float s = 0.f;
     if (i < N) {
@@ -392,10 +512,20 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int64_t* __restric
       }
     }
     scale[i] = s;
+    acc += s;
   }
   if (tid == 0) {
     hdr[kHdrNValidBwd] = nv;
     hdr[kHdrTilesKept] = 0;
+  }
+  if (scale_sum) {  // sum_i scale_i, fixed order (the smoothing share of db)
+    ssum[tid] = acc;
+    __syncthreads();
+    for (int o = 512; o >= 1; o >>= 1) {
+      if (tid < o) ssum[tid] += ssum[tid + o];
+      __syncthreads();
+    }
+    if (tid == 0) scale_sum[0] = ssum[0];
   }
 }
 
@@ -460,7 +590,7 @@ template <class C>
 __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     const typename C::T* __restrict__ c, const typename C::T* __restrict__ e, const typename C::T* __restrict__ bias,
     const int64_t* __restrict__ targets, const float* __restrict__ lse, const float* __restrict__ scale,
-    const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int tiles_v,
+    float eps, float lam, const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int tiles_v,
     int tiles_n, int Vc, int gt_ld, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes,
     size_t gt_bytes, float* __restrict__ db_part) {
   using T = typename C::T;
@@ -484,18 +614,22 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   // per-column constants, fetched before the main loop so that their latency
-  // is hidden: lse in log2 units, the gradient scale, and the target's row
-  // relative to this lane's first accumulator row (outside the tile: -1, which
-  // no row offset matches)
+  // is hidden: lse in log2 units, the coefficients of p (scale times
+  // 1 + 2 lam LSE, the z-loss share) and of the one-hot target (scale times
+  // 1 - eps), and the target's row relative to this lane's first accumulator
+  // row (outside the tile: -1, which no row offset matches)
   AccMap<C> am;
-  float lsel[C::FN], sc[C::FN];
+  float lsel[C::FN], sc[C::FN], st[C::FN];
   int trow[C::FN];
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn) {
     const int n = n0 + am.colj(fn);
     const bool vn = n < N;
-    lsel[fn] = vn ? lse[n] * kLog2e : 0.f;
-    sc[fn] = vn ? scale[n] : 0.f;  // zero for padding columns: their G is zero
+    const float l = vn ? lse[n] : 0.f;
+    const float s = vn ? scale[n] : 0.f;  // zero for padding columns: their G is zero
+    lsel[fn] = l * kLog2e;
+    sc[fn] = s * (1.f + 2.f * lam * l);
+    st[fn] = s * (1.f - eps);
     const int64_t tg = vn ? targets[n] : -1;
     const int64_t rel = tg - (int64_t)(v0 + am.row0);
     trow[fn] = (tg >= v0 && tg < v0 + C::BM) ? (int)rel : -1;
@@ -529,7 +663,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
               const float z = decltype(has_bias)::value ? acc[fm][fn][4 * q + u] + bz[u] : acc[fm][fn][4 * q + u];
               const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lsel[fn]));
               if constexpr (decltype(with_target)::value) {
-                const float tsc = trow[fn] == fm * 32 + 8 * q + u ? sc[fn] : 0.f;
+                const float tsc = trow[fn] == fm * 32 + 8 * q + u ? st[fn] : 0.f;
                 g[u] = __builtin_fmaf(p, sc[fn], -tsc);
               } else {
                 g[u] = p * sc[fn];
@@ -683,15 +817,17 @@ __device__ __forceinline__ int collect_blocks(const uint8_t* __restrict__ keep, 
 // ============================================================================
 // db[v] = sum over token blocks (in order) of the kept tiles' column sums.
 // ============================================================================
+// With label smoothing, plus r1 * aux[1] = -eps/V * sum_i scale_i.
 __global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict__ db_part,
                                                         const uint8_t* __restrict__ keep, int nb, int nvb_t, int V,
+                                                        const float* __restrict__ aux, float r1,
                                                         float* __restrict__ db) {
   const int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= V) return;
   float s = 0.f;
   for (int b = 0; b < nb; ++b)
     if (keep[(size_t)b * nvb_t + v / kTileV]) s += db_part[(size_t)b * V + v];
-  db[v] = s;
+  db[v] = aux ? s + r1 * aux[1] : s;
 }
 
 // ============================================================================
@@ -702,7 +838,7 @@ template <class C>
 __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
     const typename C::T* __restrict__ Gt, const typename C::T* __restrict__ Et,
     const uint8_t* __restrict__ keep, int Npad, int gt_ld, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
-    int tiles_v, int tiles_d, size_t gt_bytes, float* __restrict__ dC) {
+    int tiles_v, int tiles_d, size_t gt_bytes, const float* __restrict__ r1c, float* __restrict__ dC) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
@@ -730,6 +866,13 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
   AccMap<C> am;
   const int vg0 = cv0 + vl0;
   rsrc_t ro = make_rsrc(dC + (size_t)vg0 * D, (uint64_t)(V - vg0) * D * sizeof(float));
+  // the smoothing term, the same for every vocabulary row (r1c: null without)
+  float add[C::FN];
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int d = d0 + am.colj(fn);
+    add[fn] = (r1c && d < D) ? r1c[d] : 0.f;
+  }
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -739,7 +882,7 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
       for (int r = 0; r < 16; ++r) {
         const int vr = am.row(fm, r);
         const bool ok = d < D && vl0 + vr < clen;
-        stf(ro, ok ? ((uint32_t)vr * (uint32_t)D + (uint32_t)d) * 4u : kOOB, acc[fm][fn][r]);
+        stf(ro, ok ? ((uint32_t)vr * (uint32_t)D + (uint32_t)d) * 4u : kOOB, acc[fm][fn][r] + add[fn]);
       }
     }
 }
@@ -754,7 +897,8 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     const typename C::T* __restrict__ G, const typename C::T* __restrict__ c,
     const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
     int cnvb, int tiles_n, int tiles_d, int splits, int Vc, size_t g_bytes, float* __restrict__ dE,
-    float* __restrict__ dE_part, int accumulate, int atomic) {
+    float* __restrict__ dE_part, int accumulate, int atomic, const float* __restrict__ scale,
+    const float* __restrict__ csum, float r1) {
   using T = typename C::T;
   // bf16: LDS-DMA main loop (C fragments through transposing reads); fp32:
   // register-staged main loop (no 32-bit transposing read exists)
@@ -823,7 +967,15 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   }
   // Accumulating into the previous chunks' sum: the old values of a row of
   // FN blocks are fetched together (one memory round trip per fm, not per
-  // block), then added and stored.
+  // block), then added and stored.  The first write of dE (chunk 0, split 0)
+  // adds the smoothing term r1 scale_n csum_d when csum is given.
+  const bool rank1 = csum != nullptr && !accumulate && s == 0;
+  float cs[C::FN];
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int d = d0 + am.colj(fn);
+    cs[fn] = (rank1 && d < D) ? r1 * csum[d] : 0.f;
+  }
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm) {
     float old[C::FN][16];
@@ -831,6 +983,15 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
       for (int r = 0; r < 16; ++r) old[fn][r] = accumulate ? ldf(ro, offset(fm, fn, r)) : 0.f;
+    if (rank1) {
+      // scale has Npad entries: every row of the tile is inside it
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float sr = scale[n0 + am.row(fm, r)];
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) old[fn][r] = sr * cs[fn];
+      }
+    }
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
@@ -853,6 +1014,16 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, s
   if (i < n) p[i] = 0.f;
 }
 
+// dE[n][d] = r1 * scale[n] * csum[d]: the smoothing term, written before the
+// fp32 atomics add the tiles' share.
+__global__ __launch_bounds__(256) void fill_rank1_kernel(float* __restrict__ dE, const float* __restrict__ scale,
+                                                         const float* __restrict__ csum, float r1, int N, int D) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)N * D) return;
+  const int n = (int)(i / (size_t)D), d = (int)(i % (size_t)D);
+  dE[i] = r1 * scale[n] * csum[d];
+}
+
 // ============================================================================
 // Host launchers.
 // ============================================================================
@@ -860,11 +1031,39 @@ using CfgBf16 = Cfg<uint16_t, kTileV, kTileN, 2, 2>;
 using CfgF32 = Cfg<float, kTileV, kTileN, 2, 2>;
 static_assert(CfgBf16::WM == kPartialWidth && CfgF32::WM == kPartialWidth, "partial width");
 
+// out[d] = factor * sum_r w_r x[r][d] over R rows (colsum + colsum_reduce).
+template <typename T>
+static void launch_colsum(const T* x, const float* w, int R, int D, float factor, const Layout& L, float* out,
+                          hipStream_t st) {
+  constexpr int VEC = Elem<T>::VEC;
+  const int rpb = max(kColMinRows, (R + kColBlocks - 1) / kColBlocks);
+  const int nblk = (R + rpb - 1) / rpb;  // <= kColBlocks
+  prof_before(kKColSum, st);
+  hipLaunchKernelGGL(colsum_kernel<T>, dim3((D / VEC + 255) / 256, nblk), dim3(256), 0, st, x, w, R, D, rpb,
+                     L.colpart);
+  prof_after(kKColSum, st);
+  prof_before(kKColReduce, st);
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((D + 63) / 64), dim3(1024), 0, st, L.colpart, nblk, D, factor,
+                     out);
+  prof_after(kKColReduce, st);
+}
+
 template <class C>
 static hipError_t launch_forward_t(const Problem& P, const Layout& L, hipStream_t st) {
   using T = typename C::T;
   const T* e = (const T*)P.e;
   const T* c = (const T*)P.c;
+  const bool smooth = P.label_smoothing != 0.f;
+  if (smooth) {
+    // sum over the vocabulary of the classifier rows (and of the bias), kept
+    // in the workspace for the backward's dE term
+    launch_colsum<T>(c, nullptr, P.V, P.D, 1.f, L, L.csum, st);
+    if (P.bias) {
+      prof_before(kKVecSum, st);
+      hipLaunchKernelGGL(vec_sum_kernel<T>, dim3(1), dim3(1024), 0, st, (const T*)P.bias, P.V, L.aux);
+      prof_after(kKVecSum, st);
+    }
+  }
   const int tiles_v = (P.V + C::BM - 1) / C::BM, tiles_n = (P.N + C::BN - 1) / C::BN;
   const int total = tiles_v * tiles_n;
   prof_before(kKFwdTile, st);
@@ -872,9 +1071,14 @@ static hipError_t launch_forward_t(const Problem& P, const Layout& L, hipStream_
                      L.part, L.nVB, tiles_n, total);
   prof_after(kKFwdTile, st);
   prof_before(kKRows, st);
-  hipLaunchKernelGGL(rows_kernel<T>, dim3((P.N + 3) / 4), dim3(256), 0, st, e, c, (const T*)P.bias, P.targets,
-                     P.N, P.D, P.V,
-                     P.ignore_index, L.part, L.nVB, P.lse, L.nll_out);
+  if (smooth)
+    hipLaunchKernelGGL((rows_kernel<T, true>), dim3((P.N + 3) / 4), dim3(256), 0, st, e, c, (const T*)P.bias,
+                       P.targets, P.N, P.D, P.V, P.ignore_index, L.part, L.nVB, (const float*)L.csum,
+                       (const float*)L.aux, P.label_smoothing, P.z_loss, P.lse, L.nll_out);
+  else
+    hipLaunchKernelGGL((rows_kernel<T, false>), dim3((P.N + 3) / 4), dim3(256), 0, st, e, c, (const T*)P.bias,
+                       P.targets, P.N, P.D, P.V, P.ignore_index, L.part, L.nVB, (const float*)nullptr,
+                       (const float*)nullptr, 0.f, P.z_loss, P.lse, L.nll_out);
   prof_after(kKRows, st);
   prof_before(kKReduce, st);
   hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(1024), 0, st, L.nll_out, P.targets, P.N, P.V, P.ignore_index,
@@ -893,10 +1097,15 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   const T* e = (const T*)P.e;
   const T* c = (const T*)P.c;
   T* G = (T*)L.G;
+  const bool smooth = P.label_smoothing != 0.f;
+  // the smoothing term's coefficient -eps / V
+  const float r1 = smooth ? (float)(-(double)P.label_smoothing / (double)P.V) : 0.f;
   prof_before(kKBwdPrep, st);
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(1024), 0, st, P.targets, P.N, L.Npad, P.V, P.ignore_index,
-                     P.reduction, P.grad_loss, L.scale, L.hdr);
+                     P.reduction, P.grad_loss, L.scale, L.hdr, smooth ? L.aux + 1 : nullptr);
   prof_after(kKBwdPrep, st);
+  // -eps/V * sum_i scale_i e_i: the smoothing share of every dC row
+  if (smooth) launch_colsum<T>(e, L.scale, P.N, P.D, r1, L, L.r1c, st);
   prof_before(kKFilter, st);
   hipLaunchKernelGGL(filter_kernel, dim3((L.nvb_t + 255) / 256, L.nb), dim3(256), 0, st, P.targets, P.lse,
                      L.part, P.N, P.V, L.nVB, P.ignore_index, kTileN, kTileV, kPartialWidth, L.nvb_t, P.filter,
@@ -908,9 +1117,16 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   prof_after(kKTransE, st);
   if (P.accum == kAccumAtomic) {
     const size_t n = (size_t)P.N * P.D;
-    prof_before(kKFill, st);
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P.dE, n);
-    prof_after(kKFill, st);
+    if (smooth) {
+      prof_before(kKFillRank1, st);
+      hipLaunchKernelGGL(fill_rank1_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P.dE, L.scale,
+                         (const float*)L.csum, r1, P.N, P.D);
+      prof_after(kKFillRank1, st);
+    } else {
+      prof_before(kKFill, st);
+      hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P.dE, n);
+      prof_after(kKFill, st);
+    }
   }
   const int tiles_n = L.Npad / kTileN;
   const int tiles_d = (P.D + C::BN - 1) / C::BN;
@@ -921,25 +1137,27 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     const int cvb0 = cv0 / kTileV;
     prof_before(kKGradTile, st);
     hipLaunchKernelGGL(grad_tile_kernel<C>, dim3(cnvb * tiles_n), dim3(C::NT), 0, st, c, e, (const T*)P.bias,
-                       P.targets, P.lse, L.scale, L.keep, P.N, P.D, P.V, L.nvb_t, cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
+                       P.targets, P.lse, L.scale, P.label_smoothing, P.z_loss, L.keep, P.N, P.D, P.V, L.nvb_t,
+                       cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
                        G, (T*)L.Gt, L.g_bytes, L.gt_bytes, P.dbias ? L.db_part : nullptr);
     prof_after(kKGradTile, st);
     prof_before(kKDC, st);
     hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(cnvb * tiles_d), dim3(C::NT), 0, st, (const T*)L.Gt,
                        (const T*)L.Et, L.keep, L.Npad, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_d,
-                       L.gt_bytes, P.dC);
+                       L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC);
     prof_after(kKDC, st);
     const int splits = P.accum == kAccumAtomic ? L.splits_atomic : L.splits;
     prof_before(kKDE, st);
     hipLaunchKernelGGL(dE_gemm_kernel<C>, dim3(tiles_n * tiles_d * splits), dim3(C::NT), 0, st, G, c, L.keep,
                        P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits, L.Vc, L.g_bytes,
-                       P.dE, L.dE_part, ch > 0 ? 1 : 0, P.accum == kAccumAtomic ? 1 : 0);
+                       P.dE, L.dE_part, ch > 0 ? 1 : 0, P.accum == kAccumAtomic ? 1 : 0, (const float*)L.scale,
+                       smooth ? (const float*)L.csum : nullptr, r1);
     prof_after(kKDE, st);
   }
   if (P.dbias) {
     prof_before(kKDbReduce, st);
     hipLaunchKernelGGL(db_reduce_kernel, dim3((P.V + 255) / 256), dim3(256), 0, st, L.db_part, L.keep, L.nb,
-                       L.nvb_t, P.V, P.dbias);
+                       L.nvb_t, P.V, smooth ? (const float*)L.aux : nullptr, r1, P.dbias);
     prof_after(kKDbReduce, st);
   }
   if (P.accum != kAccumAtomic && L.splits > 1) {

@@ -302,6 +302,36 @@ def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias
     return lse, keep
 
 
+def lse_keep_nll(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias=None,
+                 label_smoothing: float = 0.0, z_loss: float = 0.0):
+    """One pass over all row blocks giving LSE [N], the filter keep map and
+    the per-row loss [N] (0 on ignored rows), the same definitions as
+    `forward` and `filter_keep`."""
+    e = _f64(e)
+    c = _f64(c)
+    t = np.asarray(targets, dtype=np.int64)
+    N, V = e.shape[0], c.shape[0]
+    valid = valid_rows(t, V, ignore_index)
+    nb, nvb = -(-N // Bn), -(-V // Bv)
+    keep = np.zeros((nb, nvb), dtype=bool)
+    lse = np.empty(N)
+    nll = np.zeros(N)
+    for b in range(nb):
+        r0, r1 = b * Bn, min(N, (b + 1) * Bn)
+        z = logits(e[r0:r1], c, bias)
+        l = row_logsumexp(z)
+        lse[r0:r1] = l
+        tm = tile_row_max(z, Bv) - l[:, None]
+        v = valid[r0:r1]
+        if v.any():
+            keep[b] |= (tm[v] >= FILTER_LOG_THRESHOLD).any(axis=0)
+            keep[b, t[r0:r1][v] // Bv] = True
+            T = soft_target_rows(t[r0:r1], V, v, label_smoothing)
+            r = np.nonzero(v)[0]
+            nll[r0 + r] = -(T[r] * (z[r] - l[r, None])).sum(axis=1) + z_loss * l[r] ** 2
+    return lse, keep, nll
+
+
 def dE_rows(e, c, targets, rows, ignore_index: int = -100, reduction: str = "mean",
             grad_loss=1.0, n_valid: int | None = None, keep=None, tile=None, bias=None,
             label_smoothing: float = 0.0, z_loss: float = 0.0) -> np.ndarray:

@@ -39,9 +39,9 @@ def test_status_strings_and_tiles(L):
     import linear_cross_entropy_forward_amd as M
     bn, bv, pw = M.tile_shape()
     assert bn == 256 and bv == 256 and pw == 128 and bv % pw == 0
-    for k in range(12):
+    for k in range(16):
         assert L.cce_kernel_name(k) != b"unknown"
-    assert L.cce_kernel_name(12) == b"unknown"
+    assert L.cce_kernel_name(16) == b"unknown"
 
 
 def test_workspace_size(L):
@@ -69,14 +69,14 @@ def test_vocab_chunk(L):
 
 
 def _fwd(L, e=FAKE, c=FAKE, t=FAKE, N=64, D=64, V=100, dt=0, ign=-100, red=2, cap=0.0, loss=FAKE, lse=FAKE,
-         ws=FAKE, wsb=1 << 30, bias=None):
-    return L.cce_forward(e, c, bias, t, N, D, V, dt, ign, red, cap, loss, lse, None, ws, wsb, None)
+         ws=FAKE, wsb=1 << 30, bias=None, ls=0.0, zl=0.0):
+    return L.cce_forward(e, c, bias, t, N, D, V, dt, ign, red, cap, ls, zl, loss, lse, None, ws, wsb, None)
 
 
 def _bwd(L, e=FAKE, N=64, D=64, V=100, dt=0, red=2, cap=0.0, flt=1, acc=0, chunk=0, dE=FAKE, wsb=1 << 30,
-         bias=None, db=None):
-    return L.cce_backward(e, FAKE, bias, FAKE, N, D, V, dt, -100, red, cap, FAKE, FAKE, flt, acc, chunk, dE, FAKE,
-                          db, FAKE, wsb, None)
+         bias=None, db=None, ls=0.0, zl=0.0):
+    return L.cce_backward(e, FAKE, bias, FAKE, N, D, V, dt, -100, red, cap, ls, zl, FAKE, FAKE, flt, acc, chunk, dE,
+                          FAKE, db, FAKE, wsb, None)
 
 
 def test_forward_argument_errors(L):
@@ -95,6 +95,11 @@ def test_forward_argument_errors(L):
     assert _fwd(L, wsb=16) == WORKSPACE
     assert _fwd(L, bias=FAKE + 1) == INVALID         # bias not aligned to its element
     assert _fwd(L, dt=1, bias=FAKE + 2) == INVALID
+    for ls in (-0.1, 1.5, float("nan")):            # label smoothing outside [0, 1]
+        assert _fwd(L, ls=ls) == INVALID
+    for zl in (-1e-4, float("inf"), float("nan")):  # z-loss weight negative or not finite
+        assert _fwd(L, zl=zl) == INVALID
+    assert _fwd(L, ls=1.0, zl=1e-4, wsb=16) == WORKSPACE   # valid terms pass to the size check
 
 
 def test_backward_argument_errors(L):
@@ -102,6 +107,7 @@ def test_backward_argument_errors(L):
     assert _bwd(L, dE=None) == INVALID
     assert _bwd(L, bias=FAKE + 1) == INVALID
     assert _bwd(L, db=FAKE + 2) == INVALID          # dbias is float
+    assert _bwd(L, ls=2.0) == INVALID and _bwd(L, zl=-1.0) == INVALID
     assert _bwd(L, flt=2) == INVALID
     assert _bwd(L, acc=5) == INVALID
     assert _bwd(L, chunk=100) == INVALID
@@ -123,10 +129,10 @@ def test_stats_and_profile_argument_errors(L):
     assert L.cce_read_stats(None, 1024, 1, 1, None, ctypes.byref(st)) == INVALID
     assert L.cce_read_stats(FAKE, 8, 1, 1, None, ctypes.byref(st)) == INVALID
     assert L.cce_profile_start(-1, 4) == INVALID
-    assert L.cce_profile_start(12, 4) == INVALID
+    assert L.cce_profile_start(16, 4) == INVALID
     assert L.cce_profile_start(0, 0) == INVALID
     ms, n = ctypes.c_double(), ctypes.c_int()
-    assert L.cce_profile_stop(12, ctypes.byref(ms), ctypes.byref(n)) == INVALID
+    assert L.cce_profile_stop(16, ctypes.byref(ms), ctypes.byref(n)) == INVALID
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

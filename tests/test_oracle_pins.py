@@ -658,3 +658,19 @@ def test_smoothing_filtered_drops_only_softmax_part():
                 assert p < 2.0 ** -12 * (1 + 2 * lam * L)
                 want[i] -= p * c[j]
     assert np.allclose(flt.dE, want, rtol=1e-11, atol=1e-14)
+
+
+def test_one_pass_lse_keep_nll_matches_separate_forms():
+    """lse_keep_nll (the single pass full-size checks use) gives the same LSE,
+    keep map and per-row loss as forward and filter_keep, with bias,
+    smoothing and z-loss."""
+    g = np.random.default_rng(56)
+    N, D, V, Bn, Bv = 23, 5, 41, 8, 16
+    e, c = g.standard_normal((N, D)) * 1.5, g.standard_normal((V, D))
+    b = g.standard_normal(V)
+    t = g.integers(0, V, N)
+    t[[2, 19]] = -100
+    lse, keep, nll = O.lse_keep_nll(e, c, t, Bn, Bv, bias=b, label_smoothing=0.2, z_loss=0.01)
+    f = O.forward(e, c, t, reduction="none", bias=b, label_smoothing=0.2, z_loss=0.01)
+    assert np.allclose(lse, f.lse, rtol=1e-14) and np.allclose(nll, f.nll, rtol=1e-13, atol=0)
+    assert np.array_equal(keep, O.filter_keep(e, c, t, Bn, Bv, bias=b))

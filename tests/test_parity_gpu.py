@@ -37,21 +37,22 @@ def _grad_arg(reduction, N, seed=0):
 
 
 def run(M, inp, reduction="mean", filter=False, accum="deterministic", vocab_chunk=0, ignore_index=-100,
-        backward=True, grad_seed=0, bias=None, want_db=False):
+        backward=True, grad_seed=0, bias=None, want_db=False, ls=0.0, zl=0.0):
     import torch
     dt = inp.get("dtype") or inp["workload"].dtype
     e, c, t = dev(inp["e"], dt), dev(inp["c"], dt), dev_targets(inp["targets"])
     b = dev(bias, dt) if bias is not None else None
     N, V = e.shape[0], c.shape[0]
     loss, lse, nv, ws = M.forward(e, c, t, ignore_index=ignore_index, reduction=reduction,
-                                  vocab_chunk=vocab_chunk, bias=b)
+                                  vocab_chunk=vocab_chunk, bias=b, label_smoothing=ls, z_loss=zl)
     out = {"loss": None, "lse": None}
     torch.cuda.synchronize()
     out["stats_fwd"] = M.read_stats(ws, N, V)
     if backward:
         g_np, g = _grad_arg(reduction, N, grad_seed)
         res = M.backward(e, c, t, lse, g, ws, ignore_index=ignore_index, reduction=reduction, filter=filter,
-                         accum=accum, vocab_chunk=vocab_chunk, bias=b, want_dbias=want_db)
+                         accum=accum, vocab_chunk=vocab_chunk, bias=b, want_dbias=want_db, label_smoothing=ls,
+                         z_loss=zl)
         torch.cuda.synchronize()
         out["dE"], out["dC"], out["g"] = res[0].cpu().numpy(), res[1].cpu().numpy(), g_np
         if want_db:
@@ -72,23 +73,24 @@ def filtered_bound(filtered_oracle, exact_oracle):
 
 
 def full_check(M, inp, reduction, filter, accum="deterministic", vocab_chunk=0, ignore_index=-100, label="",
-               bias=None, want_db=False):
+               bias=None, want_db=False, ls=0.0, zl=0.0):
     e, c, t = inp["e"], inp["c"], inp["targets"]
-    r = run(M, inp, reduction, filter, accum, vocab_chunk, ignore_index, bias=bias, want_db=want_db)
-    f = O.forward(e, c, t, ignore_index=ignore_index, reduction=reduction, bias=bias)
+    r = run(M, inp, reduction, filter, accum, vocab_chunk, ignore_index, bias=bias, want_db=want_db, ls=ls, zl=zl)
+    terms = dict(label_smoothing=ls, z_loss=zl)
+    f = O.forward(e, c, t, ignore_index=ignore_index, reduction=reduction, bias=bias, **terms)
     assert r["n_valid"] == f.n_valid, label
     assert r["stats_fwd"]["n_valid"] == f.n_valid
     check_loss(r["loss"], f.loss, reduction, label, f.n_valid)
     check_lse(r["lse"], f.lse, label)
     if reduction == "none":
         assert (r["loss"][~f.valid] == 0.0).all(), "ignored rows must give exactly 0"
-    b = O.backward(e, c, t, ignore_index=ignore_index, reduction=reduction, grad_loss=r["g"], bias=bias)
+    b = O.backward(e, c, t, ignore_index=ignore_index, reduction=reduction, grad_loss=r["g"], bias=bias, **terms)
     assert (r["dE"][~f.valid] == 0.0).all(), "ignored rows must give exactly 0 gradient"
     Bn, Bv, _ = M.tile_shape()
     if filter:
         lse_o, keep = O.lse_and_keep(e, c, t, Bn, Bv, ignore_index=ignore_index, bias=bias)
         bf = O.backward(e, c, t, ignore_index=ignore_index, reduction=reduction, grad_loss=r["g"], keep=keep,
-                        tile=(Bn, Bv), bias=bias)
+                        tile=(Bn, Bv), bias=bias, **terms)
         check_grad(r["dE"], bf.dE, GRAD_RTOL, label + " dE vs filtered oracle")
         check_grad(r["dC"], bf.dC, GRAD_RTOL, label + " dC vs filtered oracle")
         check_grad(r["dE"], b.dE, filtered_bound(bf.dE, b.dE), label + " dE vs exact")
@@ -277,63 +279,126 @@ def test_bias_autograd(M):
     check_grad(e.grad.float().cpu().numpy(), bo.dE, GRAD_RTOL * 2, "autograd dE")
 
 
+# ----------------------------------------------------------------------------- label smoothing, z-loss
+@pytest.mark.parametrize("reduction,ls,zl", [("mean", 0.1, 1e-4), ("none", 0.1, 0.0), ("sum", 0.0, 0.05),
+                                             ("mean", 1.0, 0.0)])
+def test_smoothing_zloss_ragged_bf16(M, reduction, ls, zl):
+    inp = W.custom(600, 136, 1100, "bf16", seed=41, c_std=0.1, ignore_frac=0.05)
+    full_check(M, inp, reduction, False, label=f"terms {reduction} ls={ls} zl={zl}", ls=ls, zl=zl)
+
+
+def test_smoothing_zloss_bias_fp32_filtered(M):
+    inp = W.custom(300, 68, 513, "f32", seed=42, c_std=0.2, ignore_frac=0.1)
+    bias = W.bias(513, "f32", seed=42, std=1.0)
+    full_check(M, inp, "mean", True, label="terms fp32 bias", bias=bias, want_db=True, ls=0.2, zl=1e-3)
+
+
+def test_smoothing_suppressed_block_keeps_uniform_term(M):
+    """A bias of -40 on vocab block 1 makes the filter drop its tiles, while the
+    block's classifier rows are shifted by +0.5 so that the uniform -eps/V
+    term over them is far above the tolerance: filtered dE, dC and db must
+    still carry it (the filtered oracle keeps it on every entry)."""
+    inp = W.custom(700, 136, 1300, "bf16", seed=43, c_std=0.1)
+    t = inp["targets"]
+    inp["targets"] = np.where((t >= 256) & (t < 512), t - 256, t)
+    inp["c"][256:512] = W.round_to_bf16(inp["c"][256:512] + 0.5)
+    bias = W.bias(1300, "bf16", seed=43, block_offsets={(256, 512): -40.0})
+    r = full_check(M, inp, "sum", True, label="terms suppressed block", bias=bias, want_db=True, ls=0.3, zl=1e-4)
+    assert r["stats"]["tiles_kept"] < r["stats"]["tiles_total"]
+
+
+@pytest.mark.parametrize("accum", ["deterministic", "atomic"])
+def test_smoothing_vocab_chunks(M, accum):
+    # several chunks and dE splits: the smoothing term enters dE once (chunk 0,
+    # split 0, or the atomic mode's initial fill)
+    inp = W.custom(530, 200, 1900, "bf16", seed=44, c_std=0.08, ignore_frac=0.05)
+    full_check(M, inp, "mean", False, accum=accum, vocab_chunk=256, label=f"terms chunks {accum}", ls=0.1,
+               zl=1e-4)
+    full_check(M, inp, "none", True, accum=accum, vocab_chunk=512, label=f"terms chunks filtered {accum}",
+               ls=0.1, zl=1e-4)
+
+
+def test_smoothing_deterministic_bitwise(M):
+    inp = W.custom(700, 256, 3000, "bf16", seed=45, c_std=0.05, ignore_frac=0.02)
+    runs = [run(M, inp, "mean", True, "deterministic", ls=0.1, zl=1e-4) for _ in range(2)]
+    for k in ("loss", "lse", "dE", "dC"):
+        assert np.array_equal(runs[1][k], runs[0][k]), k
+
+
+def test_smoothing_autograd(M):
+    import torch
+    inp = W.custom(260, 64, 900, "bf16", seed=46, c_std=0.1, ignore_frac=0.05)
+    bias = W.bias(900, "bf16", seed=46)
+    e = dev(inp["e"], "bf16").requires_grad_(True)
+    c = dev(inp["c"], "bf16").requires_grad_(True)
+    b = dev(bias, "bf16").requires_grad_(True)
+    t = dev_targets(inp["targets"]).reshape(20, 13)
+    loss = M.linear_cross_entropy(e.reshape(20, 13, 64), c, t, bias=b, label_smoothing=0.1, z_loss=1e-3)
+    loss.backward()
+    kw = dict(bias=bias, label_smoothing=0.1, z_loss=1e-3)
+    f = O.forward(inp["e"], inp["c"], inp["targets"], **kw)
+    bo = O.backward(inp["e"], inp["c"], inp["targets"], **kw)
+    check_loss(loss.detach().float().cpu().numpy(), f.loss, "mean", "autograd terms", f.n_valid)
+    check_grad(b.grad.float().cpu().numpy(), bo.db, GRAD_RTOL * 2, "autograd terms db")
+    check_grad(c.grad.float().cpu().numpy(), bo.dC, GRAD_RTOL * 2, "autograd terms dC")
+    check_grad(e.grad.float().cpu().numpy(), bo.dE, GRAD_RTOL * 2, "autograd terms dE")
+
+
 # ----------------------------------------------------------------------------- full-size, sampled
 def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, n_vocab=24, dC_check=True,
-                  with_bias=False):
+                  with_bias=False, ls=0.0, zl=0.0):
     import torch
     inp = W.get(name)
     e, c, t = inp["e"], inp["c"], inp["targets"]
     N, V = e.shape[0], c.shape[0]
     bias = W.bias(V, inp["workload"].dtype, seed=5) if with_bias else None
-    print(f"[full] {name} N={N} V={V} reduction={reduction} filter={filter} accum={accum} bias={with_bias}",
-          flush=True)
-    r = run(M, inp, reduction, filter, accum, bias=bias, want_db=with_bias)
+    terms = dict(label_smoothing=ls, z_loss=zl)
+    print(f"[full] {name} N={N} V={V} reduction={reduction} filter={filter} accum={accum} bias={with_bias} "
+          f"ls={ls} zl={zl}", flush=True)
+    r = run(M, inp, reduction, filter, accum, bias=bias, want_db=with_bias, ls=ls, zl=zl)
     print(f"[full] {name}: GPU done, oracle checks", flush=True)
     rng = np.random.default_rng(99)
     rows = np.sort(rng.choice(N, n_rows, replace=False))
     valid = t != -100
     assert r["n_valid"] == int(valid.sum())
-    fo = O.forward(e, c, t, reduction="none", rows=rows, bias=bias)
+    fo = O.forward(e, c, t, reduction="none", rows=rows, bias=bias, **terms)
     check_lse(r["lse"][rows], fo.lse, name)
     if reduction == "none":
         check_loss(r["loss"][rows], fo.nll, "none", name)
     Bn, Bv, _ = M.tile_shape()
     tile = (Bn, Bv)
     if dC_check or filter:
-        lse_all, keep = O.lse_and_keep(e, c, t, Bn, Bv, bias=bias)
+        lse_all, keep, nll = O.lse_keep_nll(e, c, t, Bn, Bv, bias=bias, **terms)
         print(f"[full] {name}: oracle LSE pass done", flush=True)
         if reduction != "none":
             # the reduced loss from the oracle's full pass
-            zt = np.einsum("ij,ij->i", e.astype(np.float64), c[np.where(valid, t, 0)].astype(np.float64))
-            if bias is not None:
-                zt = zt + bias.astype(np.float64)[np.where(valid, t, 0)]
-            nll = np.where(valid, lse_all - zt, 0.0)
-            want = nll.sum() / max(valid.sum(), 1) if reduction == "mean" else nll.sum()
+            want = O.reduce_loss(nll, int(valid.sum()), reduction)
             check_loss(r["loss"], want, reduction, name, int(valid.sum()))
         kept = r["stats"]["tiles_kept"]
         if filter:
             assert abs(kept - int(keep.sum())) <= max(2, keep.size // 100), (kept, int(keep.sum()))
     g = r["g"]
-    dE_x = O.dE_rows(e, c, t, rows, reduction=reduction, grad_loss=g, bias=bias)
+    dE_x = O.dE_rows(e, c, t, rows, reduction=reduction, grad_loss=g, bias=bias, **terms)
     if filter:
-        dE_f = O.dE_rows(e, c, t, rows, reduction=reduction, grad_loss=g, keep=keep, tile=tile, bias=bias)
+        dE_f = O.dE_rows(e, c, t, rows, reduction=reduction, grad_loss=g, keep=keep, tile=tile, bias=bias,
+                         **terms)
         check_grad(r["dE"][rows], dE_f, GRAD_RTOL, name + " dE vs filtered")
         check_grad(r["dE"][rows], dE_x, filtered_bound(dE_f, dE_x), name + " dE vs exact")
     else:
         check_grad(r["dE"][rows], dE_x, GRAD_RTOL, name + " dE")
     if dC_check:
         vid = np.unique(np.concatenate([rng.choice(V, n_vocab, replace=False), t[valid][:8]]))
-        dC_x = O.dC_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g, bias=bias)
+        dC_x = O.dC_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g, bias=bias, **terms)
         if filter:
             dC_f = O.dC_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g, keep=keep, tile=tile,
-                             bias=bias)
+                             bias=bias, **terms)
             check_grad(r["dC"][vid], dC_f, GRAD_RTOL, name + " dC vs filtered")
             check_grad(r["dC"][vid], dC_x, filtered_bound(dC_f, dC_x), name + " dC vs exact")
         else:
             check_grad(r["dC"][vid], dC_x, GRAD_RTOL, name + " dC")
         if with_bias:
             db_f = O.db_rows(e, c, t, vid, lse_all, reduction=reduction, grad_loss=g, bias=bias,
-                             keep=keep if filter else None, tile=tile if filter else None)
+                             keep=keep if filter else None, tile=tile if filter else None, **terms)
             check_grad(r["db"][vid], db_f, GRAD_RTOL, name + " db")
     torch.cuda.empty_cache()
     return r
@@ -364,3 +429,8 @@ def test_full_gemma2b_calibrated(M):
 @pytest.mark.slow
 def test_full_llama1b_bias(M):
     _sampled_full(M, "llama1b", "mean", True, with_bias=True)
+
+
+@pytest.mark.slow
+def test_full_llama1b_smoothing_zloss(M):
+    _sampled_full(M, "llama1b", "mean", True, with_bias=True, ls=0.1, zl=1e-4)
