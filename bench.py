@@ -38,11 +38,11 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "a6117a3be1a97a98bf52ea65acdad967cd2b879fa2b16c82f12ed3a87f994b9e",
+    "source_sha256": "a34b291b383eafe675a9794b31bd2134dfab6edbbb19f5cd0c438a7135e2fb15",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9154.1e6, "grad_tile": 2199.5e6, "dC_gemm": 2293.6e6, "dE_gemm": 1811.0e6,
-        "rows": 121.5e6, "filter": 3.3e6, "transpose_e": 67.1e6,
+        "fwd_tile": 9269.7e6, "grad_tile": 2234.6e6, "dC_gemm": 2257.0e6, "dE_gemm": 1858.8e6,
+        "rows": 121.4e6, "filter": 3.3e6, "transpose_e": 67.1e6,
     },
 }
 
