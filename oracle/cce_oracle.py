@@ -48,6 +48,13 @@ Optional loss terms (both default to 0, which gives the plain loss above):
                                   adds a multiple of the squared log-sum-exp)
   so that G_ij = (softmax_ij (1 + 2 lam LSE_i) - T_ij) * scale_i.
 
+Logit soft-capping s > 0 (NOT defined on the pages; the form used by Gemma 2:
+Z'_ij = s tanh(Z_ij / s), applied after the bias): every definition above then
+takes Z' in place of Z, and the chain rule multiplies G by
+dZ'/dZ = 1 - tanh^2(Z / s) = 1 - (Z' / s)^2.  Soft-capping together with label
+smoothing under filtering has no reading here (the smoothing part of G is no
+longer uniform) and raises.
+
 Gradient filtering (README "How it works" item 2; Wijmans et al. abstract:
 skip gradient entries below numerical precision) is modelled by
 `filter_keep`: a tile (row block b, vocab block v) of G is kept iff some valid
@@ -88,11 +95,14 @@ def valid_rows(targets, V: int, ignore_index: int = -100) -> np.ndarray:
     return valid
 
 
-def logits(e, c, bias=None) -> np.ndarray:
-    """Z = E C^T (+ b on every row) in float64 (the materialised logit matrix)."""
+def logits(e, c, bias=None, softcap: float = 0.0) -> np.ndarray:
+    """Z = E C^T (+ b on every row) in float64 (the materialised logit matrix),
+    soft-capped to s tanh(Z / s) when softcap = s > 0."""
     z = _f64(e) @ _f64(c).T
     if bias is not None:
         z += _f64(bias)[None, :]
+    if softcap:
+        z = softcap * np.tanh(z / softcap)
     return z
 
 
@@ -132,7 +142,8 @@ def soft_target_rows(t: np.ndarray, V: int, valid: np.ndarray, label_smoothing: 
 
 
 def forward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
-            rows=None, bias=None, label_smoothing: float = 0.0, z_loss: float = 0.0) -> Forward:
+            rows=None, bias=None, label_smoothing: float = 0.0, z_loss: float = 0.0,
+            softcap: float = 0.0) -> Forward:
     """Loss and per-row LSE.  `rows` restricts the work to a subset of rows
     (then `loss` is the reduction over that subset only and n_valid counts it).
     loss_i = -sum_j T_ij (Z_ij - LSE_i) + z_loss * LSE_i^2 on valid rows."""
@@ -146,7 +157,7 @@ def forward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
     nll = np.zeros(len(idx))
     for s in range(0, len(idx), _ROW_CHUNK):
         sl = slice(s, s + _ROW_CHUNK)
-        z = logits(e[idx[sl]], c, bias)
+        z = logits(e[idx[sl]], c, bias, softcap)
         lse[sl] = row_logsumexp(z)
         v = valid[sl]
         r = np.nonzero(v)[0]
@@ -183,7 +194,7 @@ def tile_row_max(z: np.ndarray, Bv: int) -> np.ndarray:
 
 
 def filter_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100,
-                lse=None, bias=None) -> np.ndarray:
+                lse=None, bias=None, softcap: float = 0.0) -> np.ndarray:
     """Keep map [ceil(N/Bn), ceil(V/Bv)] of (row block, vocab block) tiles of G.
 
     Kept iff some valid row i of the block has max_j softmax_ij >= 2^-12 on the
@@ -199,7 +210,7 @@ def filter_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100,
     keep = np.zeros((nb, nvb), dtype=bool)
     for b in range(nb):
         r0, r1 = b * Bn, min(N, (b + 1) * Bn)
-        z = logits(e[r0:r1], c, bias)
+        z = logits(e[r0:r1], c, bias, softcap)
         l = row_logsumexp(z) if lse is None else _f64(lse)[r0:r1]
         tm = tile_row_max(z, Bv) - l[:, None]          # log of the tile's max softmax
         v = valid[r0:r1]
@@ -211,10 +222,13 @@ def filter_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100,
 
 def softmax_grad_rows(z: np.ndarray, lse: np.ndarray, t: np.ndarray, scale: np.ndarray,
                       valid: np.ndarray, label_smoothing: float = 0.0, z_loss: float = 0.0,
-                      colmask=None) -> np.ndarray:
+                      colmask=None, softcap: float = 0.0) -> np.ndarray:
     """G rows: (exp(Z - LSE) (1 + 2 z_loss LSE) - T) * scale, zero on ignored
     rows.  colmask [rows, V] (bool), when given, marks the entries the filter
-    keeps: elsewhere only the uniform -eps/V part of -T remains."""
+    keeps: elsewhere only the uniform -eps/V part of -T remains.  With
+    softcap, z holds the capped logits and G is multiplied by 1 - (z / s)^2."""
+    if softcap and label_smoothing and colmask is not None:
+        raise NotImplementedError("filtered soft-capping with label smoothing has no reading")
     V = z.shape[1]
     g = np.exp(z - lse[:, None]) * (1.0 + 2.0 * z_loss * lse)[:, None]
     r = np.nonzero(valid)[0]
@@ -222,6 +236,8 @@ def softmax_grad_rows(z: np.ndarray, lse: np.ndarray, t: np.ndarray, scale: np.n
     if colmask is not None:
         g[~colmask] = 0.0
     g -= label_smoothing / V
+    if softcap:
+        g *= 1.0 - (z / softcap) ** 2
     g *= scale[:, None]
     g[~valid] = 0.0
     return g
@@ -236,7 +252,7 @@ class Backward:
 
 def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
              grad_loss=1.0, keep=None, tile=None, bias=None, label_smoothing: float = 0.0,
-             z_loss: float = 0.0) -> Backward:
+             z_loss: float = 0.0, softcap: float = 0.0) -> Backward:
     """dE = G C, dC = G^T E and db = G^T 1.  With `keep` (a filter_keep map for
     `tile` = (Bn, Bv)) the softmax part of G is zeroed on the dropped tiles."""
     e = _f64(e)
@@ -251,13 +267,13 @@ def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
     chunk = _ROW_CHUNK if keep is None else tile[0]
     for s in range(0, N, chunk):
         sl = slice(s, min(N, s + chunk))
-        z = logits(e[sl], c, bias)
+        z = logits(e[sl], c, bias, softcap)
         lse = row_logsumexp(z)
         cm = None
         if keep is not None:
             Bn, Bv = tile
             cm = np.broadcast_to(np.repeat(keep[s // Bn], Bv)[:V], z.shape)
-        g = softmax_grad_rows(z, lse, t[sl], scale[sl], valid[sl], label_smoothing, z_loss, cm)
+        g = softmax_grad_rows(z, lse, t[sl], scale[sl], valid[sl], label_smoothing, z_loss, cm, softcap)
         dE[sl] = g @ c
         dC += g.T @ e[sl]
         db += g.sum(axis=0)
@@ -269,17 +285,18 @@ def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
 # output rows, so full-size checks stay within seconds to a minute.
 # ---------------------------------------------------------------------------
 
-def lse_all(e, c, chunk: int = _ROW_CHUNK, bias=None) -> np.ndarray:
+def lse_all(e, c, chunk: int = _ROW_CHUNK, bias=None, softcap: float = 0.0) -> np.ndarray:
     """LSE of every row (the full materialised pass, row chunk by row chunk)."""
     e = _f64(e)
     c = _f64(c)
     out = np.empty(e.shape[0])
     for s in range(0, e.shape[0], chunk):
-        out[s:s + chunk] = row_logsumexp(logits(e[s:s + chunk], c, bias))
+        out[s:s + chunk] = row_logsumexp(logits(e[s:s + chunk], c, bias, softcap))
     return out
 
 
-def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias=None):
+def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias=None,
+                 softcap: float = 0.0):
     """One pass over all row blocks giving LSE [N] and the filter keep map."""
     e = _f64(e)
     c = _f64(c)
@@ -291,7 +308,7 @@ def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias
     lse = np.empty(N)
     for b in range(nb):
         r0, r1 = b * Bn, min(N, (b + 1) * Bn)
-        z = logits(e[r0:r1], c, bias)
+        z = logits(e[r0:r1], c, bias, softcap)
         l = row_logsumexp(z)
         lse[r0:r1] = l
         tm = tile_row_max(z, Bv) - l[:, None]
@@ -303,7 +320,7 @@ def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias
 
 
 def lse_keep_nll(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias=None,
-                 label_smoothing: float = 0.0, z_loss: float = 0.0):
+                 label_smoothing: float = 0.0, z_loss: float = 0.0, softcap: float = 0.0):
     """One pass over all row blocks giving LSE [N], the filter keep map and
     the per-row loss [N] (0 on ignored rows), the same definitions as
     `forward` and `filter_keep`."""
@@ -318,7 +335,7 @@ def lse_keep_nll(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias
     nll = np.zeros(N)
     for b in range(nb):
         r0, r1 = b * Bn, min(N, (b + 1) * Bn)
-        z = logits(e[r0:r1], c, bias)
+        z = logits(e[r0:r1], c, bias, softcap)
         l = row_logsumexp(z)
         lse[r0:r1] = l
         tm = tile_row_max(z, Bv) - l[:, None]
@@ -334,7 +351,7 @@ def lse_keep_nll(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias
 
 def dE_rows(e, c, targets, rows, ignore_index: int = -100, reduction: str = "mean",
             grad_loss=1.0, n_valid: int | None = None, keep=None, tile=None, bias=None,
-            label_smoothing: float = 0.0, z_loss: float = 0.0) -> np.ndarray:
+            label_smoothing: float = 0.0, z_loss: float = 0.0, softcap: float = 0.0) -> np.ndarray:
     """dE for selected rows: row i of G C needs only row i of Z.  For mean,
     n_valid is the whole batch's count (pass it in); for none, grad_loss is [N]."""
     e = _f64(e)
@@ -349,19 +366,19 @@ def dE_rows(e, c, targets, rows, ignore_index: int = -100, reduction: str = "mea
         scale = np.where(valid_all[rows], float(grad_loss) / max(n_valid, 1), 0.0)
     else:
         scale = grad_scale(valid_all, reduction, grad_loss)[rows]
-    z = logits(e[rows], c, bias)
+    z = logits(e[rows], c, bias, softcap)
     lse = row_logsumexp(z)
     cm = None
     if keep is not None:
         Bn, Bv = tile
         cm = np.stack([np.repeat(keep[i // Bn], Bv)[:V] for i in rows])
-    g = softmax_grad_rows(z, lse, t[rows], scale, valid_all[rows], label_smoothing, z_loss, cm)
+    g = softmax_grad_rows(z, lse, t[rows], scale, valid_all[rows], label_smoothing, z_loss, cm, softcap)
     return g @ c
 
 
 def G_columns(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction: str = "mean",
               grad_loss=1.0, keep=None, tile=None, bias=None, label_smoothing: float = 0.0,
-              z_loss: float = 0.0) -> np.ndarray:
+              z_loss: float = 0.0, softcap: float = 0.0) -> np.ndarray:
     """Columns j of G for selected vocabulary ids, [N, k]: they need column j of
     Z for all rows and every row's LSE (pass the oracle's own)."""
     e = _f64(e)
@@ -374,6 +391,10 @@ def G_columns(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction
     zc = e @ c[vocab_ids].T                              # [N, k] = Z[:, vocab_ids]
     if bias is not None:
         zc += _f64(bias)[vocab_ids][None, :]
+    if softcap:
+        if label_smoothing and keep is not None:
+            raise NotImplementedError("filtered soft-capping with label smoothing has no reading")
+        zc = softcap * np.tanh(zc / softcap)
     lse = _f64(lse)
     g = np.exp(zc - lse[:, None]) * (1.0 + 2.0 * z_loss * lse)[:, None]
     g -= (1.0 - label_smoothing) * (t[:, None] == vocab_ids[None, :])
@@ -382,6 +403,8 @@ def G_columns(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction
         rowblk = np.arange(e.shape[0]) // Bn
         g *= keep[rowblk][:, vocab_ids // Bv]
     g -= label_smoothing / V
+    if softcap:
+        g *= 1.0 - (zc / softcap) ** 2
     g *= scale[:, None]
     g[~valid] = 0.0
     return g
@@ -394,10 +417,10 @@ def db_rows(e, c, targets, vocab_ids, lse, **kw) -> np.ndarray:
 
 def dC_rows(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction: str = "mean",
             grad_loss=1.0, keep=None, tile=None, bias=None, label_smoothing: float = 0.0,
-            z_loss: float = 0.0) -> np.ndarray:
+            z_loss: float = 0.0, softcap: float = 0.0) -> np.ndarray:
     """dC for selected vocabulary rows j: dC_j = sum_i G_ij e_i, which needs
     column j of Z for all rows and every row's LSE (pass the oracle's own)."""
     g = G_columns(e, c, targets, vocab_ids, lse, ignore_index=ignore_index, reduction=reduction,
                   grad_loss=grad_loss, keep=keep, tile=tile, bias=bias,
-                  label_smoothing=label_smoothing, z_loss=z_loss)
+                  label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap)
     return g.T @ _f64(e)

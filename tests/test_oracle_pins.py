@@ -674,3 +674,111 @@ def test_one_pass_lse_keep_nll_matches_separate_forms():
     f = O.forward(e, c, t, reduction="none", bias=b, label_smoothing=0.2, z_loss=0.01)
     assert np.allclose(lse, f.lse, rtol=1e-14) and np.allclose(nll, f.nll, rtol=1e-13, atol=0)
     assert np.array_equal(keep, O.filter_keep(e, c, t, Bn, Bv, bias=b))
+
+
+# --------------------------------------------------------------------------- logit soft-capping
+# Not defined on the pages: the Gemma 2 form Z' = s tanh(Z / s), after the bias.
+
+
+@pytest.mark.parametrize("reduction,eps,lam", [("mean", 0.0, 0.0), ("none", 0.1, 0.0), ("sum", 0.0, 0.02),
+                                               ("mean", 0.2, 0.01)])
+def test_softcap_matches_torch_autograd(reduction, eps, lam):
+    """Capped loss and gradients equal PyTorch's cross_entropy on
+    s * tanh((E C^T + b) / s), plus lam * logsumexp^2 on valid rows,
+    differentiated by autograd in float64 on the CPU."""
+    import torch
+    g = np.random.default_rng(60)
+    N, D, V, s = 12, 5, 19, 2.5
+    e, c = g.standard_normal((N, D)) * 1.5, g.standard_normal((V, D)) * 1.5
+    b = g.standard_normal(V)
+    t = g.integers(0, V, N)
+    t[[1, 7]] = -100
+    gl = g.standard_normal(N) if reduction == "none" else 0.8
+    te, tc, tb = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (e, c, b))
+    zc = s * torch.tanh((te @ tc.T + tb) / s)
+    tt = torch.tensor(t)
+    ce = torch.nn.functional.cross_entropy(zc, tt, ignore_index=-100, reduction="none", label_smoothing=eps)
+    valid = torch.tensor(t != -100, dtype=torch.float64)
+    per = ce + lam * torch.logsumexp(zc, dim=1) ** 2 * valid
+    nv = max(int(valid.sum()), 1)
+    ref = per if reduction == "none" else (per.sum() if reduction == "sum" else per.sum() / nv)
+    ref.backward(torch.tensor(gl, dtype=torch.float64))
+    kw = dict(reduction=reduction, bias=b, label_smoothing=eps, z_loss=lam, softcap=s)
+    f = O.forward(e, c, t, **kw)
+    assert np.allclose(f.loss, ref.detach().numpy(), rtol=1e-12, atol=1e-14)
+    bw = O.backward(e, c, t, grad_loss=gl, **kw)
+    assert np.allclose(bw.dE, te.grad.numpy(), rtol=1e-11, atol=1e-14)
+    assert np.allclose(bw.dC, tc.grad.numpy(), rtol=1e-11, atol=1e-14)
+    assert np.allclose(bw.db, tb.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+def test_softcap_saturated_closed_form():
+    """Logits of +-1e4 with s = 5 saturate: tanh(2000) is 1 in fp64, so every
+    capped logit is +-5 exactly, LSE = ln(k e^5 + (V - k) e^-5) for k
+    positive logits, and every gradient is exactly 0 (the cap's derivative
+    1 - tanh^2 vanishes)."""
+    N, D, V, s = 4, 2, 6, 5.0
+    e = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [-1.0, 0.0]]) * 100.0
+    c = np.array([[1, 1], [-1, 1], [1, -1], [-1, -1], [1, 0.5], [-1, 0.5]], dtype=np.float64) * 100.0
+    # every product is +-1e4 or +-5e3 (or +-1.5e4 / 0 for row 2: keep only nonzero rows' logic simple)
+    z = e @ c.T
+    t = np.array([0, 3, -100, 5])
+    f = O.forward(e, c, t, reduction="none", softcap=s)
+    for i in range(N):
+        zi = np.where(z[i] > 0, s, np.where(z[i] < 0, -s, 0.0))
+        want = math.log(sum(math.exp(x) for x in zi))
+        assert abs(f.lse[i] - want) < 1e-12
+        if t[i] != -100:
+            assert abs(f.nll[i] - (want - zi[t[i]])) < 1e-12
+    bw = O.backward(e, c, t, reduction="sum", softcap=s)
+    sat = np.abs(z[[0, 1, 3]]) >= 1e3
+    assert sat.all()
+    assert np.abs(bw.dE[[0, 1, 3]]).max() < 1e-300 and np.abs(bw.dC).max() < 1e-300
+
+
+def test_softcap_large_cap_is_uncapped():
+    e, c, t = _rand(61, 7, 4, 11)
+    t[3] = -100
+    a = O.forward(e, c, t, reduction="none", softcap=1e7)
+    b = O.forward(e, c, t, reduction="none")
+    assert np.allclose(a.nll, b.nll, rtol=1e-9) and np.allclose(a.lse, b.lse, rtol=1e-9)
+    ga = O.backward(e, c, t, reduction="mean", softcap=1e7)
+    gb = O.backward(e, c, t, reduction="mean")
+    assert np.allclose(ga.dE, gb.dE, rtol=1e-8, atol=1e-14) and np.allclose(ga.dC, gb.dC, rtol=1e-8, atol=1e-14)
+
+
+def test_softcap_filter_brute_force_and_sampled():
+    """Keep map on the capped softmax against loops over entries (a block
+    pushed down by the bias is dropped); sampled dE, dC and db forms against
+    the full filtered backward, with z-loss."""
+    g = np.random.default_rng(62)
+    N, D, V, Bn, Bv, s = 10, 4, 48, 5, 8, 6.0
+    e, c = g.standard_normal((N, D)) * 2.0, g.standard_normal((V, D)) * 2.0
+    b = g.standard_normal(V)
+    b[16:24] -= 40.0                            # capped to about -s: below 2^-12 for every row
+    t = g.choice(np.r_[0:16, 24:48], N)
+    t[4] = -100
+    keep = O.filter_keep(e, c, t, Bn, Bv, bias=b, softcap=s)
+    want = np.zeros_like(keep)
+    for i in range(N):
+        if t[i] == -100:
+            continue
+        zi = [s * math.tanh((float(np.dot(e[i], c[j])) + b[j]) / s) for j in range(V)]
+        den = sum(math.exp(x) for x in zi)
+        for j in range(V):
+            if math.exp(zi[j]) / den >= 2.0 ** -12 or j == t[i]:
+                want[i // Bn, j // Bv] = True
+    assert np.array_equal(keep, want)
+    assert not keep.all()
+    kw = dict(reduction="sum", bias=b, softcap=s, z_loss=0.01)
+    full = O.backward(e, c, t, keep=keep, tile=(Bn, Bv), **kw)
+    lse, keep2, _ = O.lse_keep_nll(e, c, t, Bn, Bv, bias=b, softcap=s, z_loss=0.01)
+    assert np.array_equal(keep, keep2)
+    assert np.allclose(lse, O.lse_all(e, c, bias=b, softcap=s), rtol=1e-14)
+    vid = np.array([0, 9, 30, 47])
+    kk = dict(keep=keep, tile=(Bn, Bv), **kw)
+    assert np.allclose(O.db_rows(e, c, t, vid, lse, **kk), full.db[vid], rtol=1e-12, atol=1e-15)
+    assert np.allclose(O.dC_rows(e, c, t, vid, lse, **kk), full.dC[vid], rtol=1e-12, atol=1e-15)
+    assert np.allclose(O.dE_rows(e, c, t, [0, 7], **kk), full.dE[[0, 7]], rtol=1e-12, atol=1e-15)
+    with pytest.raises(NotImplementedError):
+        O.backward(e, c, t, keep=keep, tile=(Bn, Bv), reduction="sum", softcap=s, label_smoothing=0.1)
