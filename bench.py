@@ -189,11 +189,11 @@ def make_bias(V, dtype, dev, seed=7):
 
 
 def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=False, label_smoothing=0.0,
-                   z_loss=0.0):
+                   z_loss=0.0, softcap=0.0):
     """Compact forward / forward+backward figures for one workload (defaults:
     filter on, deterministic, the workload's own reduction; with_bias adds a
     classifier bias and asks for its gradient; label_smoothing / z_loss add
-    those loss terms)."""
+    those loss terms; softcap soft-caps the logits)."""
     import torch
     import workloads as W
     import linear_cross_entropy_forward_amd as M
@@ -230,7 +230,7 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
     dbp = db.data_ptr() if with_bias else None
 
     def fwd():
-        r = L.cce_forward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, 0.0,
+        r = L.cce_forward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, softcap,
                           label_smoothing, z_loss, loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(),
                           ws.numel(), st.cuda_stream)
         if r:
@@ -238,7 +238,7 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
 
     def step():
         fwd()
-        r = L.cce_backward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, 0.0,
+        r = L.cce_backward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, softcap,
                            label_smoothing, z_loss, lse.data_ptr(), g.data_ptr(), 1, 0, 0, dE.data_ptr(),
                            dC.data_ptr(), dbp, ws.data_ptr(), ws.numel(), st.cuda_stream)
         if r:
@@ -266,8 +266,8 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
            "tflops_effective": eff, "pct_of_peak": 100.0 * eff / peak,
            "tiles_skipped_frac": 1.0 - stats["tiles_kept"] / max(1, stats["tiles_total"]),
            "extra_hbm_bytes": int(extra), "bias": bool(with_bias), "label_smoothing": label_smoothing,
-           "z_loss": z_loss}
-    plain = not with_bias and label_smoothing == 0.0 and z_loss == 0.0
+           "z_loss": z_loss, "softcap": softcap}
+    plain = not with_bias and label_smoothing == 0.0 and z_loss == 0.0 and softcap == 0.0
     if w.dtype == "bf16" and plain:
         out["hipblaslt_fwd_gemm_tflops"] = hipblaslt_gemm_tflops(c, e)
     del ws, loss, lse, nv, g, dE, dC, bias, db
@@ -435,6 +435,8 @@ def main():
         # ... and with label smoothing 0.1 and z-loss 1e-4
         configs[args.workload + "+smoothing+zloss"] = config_summary(args.workload, label_smoothing=0.1,
                                                                      z_loss=1e-4)
+        # Gemma 2's final-logit soft-capping (30) on the calibrated Gemma-2-2B head
+        configs["gemma2b_cal+softcap30"] = config_summary("gemma2b_cal", softcap=30.0)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -31,6 +31,14 @@
  * the softmax and drops only its part of G: the uniform -eps/V * scale_i part
  * is applied to every entry (as a rank-one term of dE, dC and dbias).
  *
+ * Logit soft-capping s > 0 is not defined on those pages: it takes the form
+ * Gemma 2 uses, z' = s tanh(z / s) after the bias, in place of z everywhere
+ * (LSE, the correct-token logit, the filter's softmax), and multiplies G by
+ * dz'/dz = 1 - (z' / s)^2.  It cannot be combined with label smoothing (the
+ * smoothing part of G is then no longer the same for every entry):
+ * CCE_ERR_UNSUPPORTED.  It is built for bf16 operands only: with float32
+ * operands a softcap > 0 is CCE_ERR_UNSUPPORTED.
+ *
  * Conventions for every call:
  *  - Pointers marked (device) are device memory on the current HIP device;
  *    (host) are host memory.  The library never allocates, frees or
@@ -67,7 +75,7 @@ typedef struct ihipStream_t* cce_stream_t;
 typedef enum {
   CCE_OK = 0,
   CCE_ERR_INVALID_ARG = -1, /* null pointer, negative or zero size, bad enum, misalignment */
-  CCE_ERR_UNSUPPORTED = -2, /* softcap != 0, D not a multiple of the vector width, size limits */
+  CCE_ERR_UNSUPPORTED = -2, /* softcap with label smoothing, D not a multiple of the vector width, size limits */
   CCE_ERR_WORKSPACE = -3,   /* workspace smaller than cce_workspace_size() */
   CCE_ERR_HIP = -4          /* a HIP launch or copy reported an error */
 } cce_status;
@@ -115,8 +123,9 @@ int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk);
  * reduction: CCE_REDUCTION_NONE writes loss[N] (0 on ignored rows);
  * SUM / MEAN write loss[0] (MEAN divides by max(n_valid, 1)).  lse (device)
  * float [N] receives every row's LSE (ignored rows included).  n_valid
- * (device) int32 [1] receives the non-ignored count; may be NULL.  softcap must
- * be 0 (no logit soft-capping; other values return CCE_ERR_UNSUPPORTED).  ws
+ * (device) int32 [1] receives the non-ignored count; may be NULL.  softcap: 0 for
+ * none, s > 0 (finite) for s tanh(z / s); negative or non-finite values are
+ * CCE_ERR_INVALID_ARG.  ws
  * (device) of ws_bytes >= cce_workspace_size(N, D, V, dtype, vocab_chunk) for
  * the vocab_chunk the backward will use; it holds the per-block partials the
  * backward's filter reads, so keep it unmodified between the two calls.

@@ -154,7 +154,8 @@ def forward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, ignore_inde
     reduction='none', else a 0-dim tensor.  `ws` (uint8, device) is allocated
     if not given and must be passed unchanged to backward().  `bias` [V] (the
     classifier's dtype) is optional; label_smoothing (eps in [0, 1]) and
-    z_loss (lam >= 0) add the soft-target and lam * LSE^2 terms."""
+    z_loss (lam >= 0) add the soft-target and lam * LSE^2 terms; softcap = s > 0
+    replaces the logits by s * tanh(z / s) (not with label smoothing)."""
     _validate(e, c, targets)
     _validate_bias(bias, c)
     N, D = e.shape
@@ -181,7 +182,8 @@ def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch
              want_dbias: bool = False, label_smoothing: float = 0.0, z_loss: float = 0.0):
     """cce_backward.  grad_loss is float32 [N] ('none') or [1]/0-dim.  Returns
     float32 (dE [N, D], dC [V, D]), plus db [V] when want_dbias.  bias,
-    label_smoothing and z_loss must be those of the forward that filled ws."""
+    label_smoothing, z_loss and softcap must be those of the forward that
+    filled ws."""
     _validate(e, c, targets)
     _validate_bias(bias, c)
     N, D = e.shape
@@ -211,48 +213,51 @@ def read_stats(ws: torch.Tensor, N: int, V: int) -> dict:
 
 class _CCEFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, e, c, bias, targets, reduction, ignore_index, filter, accum, label_smoothing, z_loss):
+    def forward(ctx, e, c, bias, targets, reduction, ignore_index, filter, accum, label_smoothing, z_loss,
+                softcap):
         loss, lse, _, ws = forward(e, c, targets, ignore_index=ignore_index, reduction=reduction, bias=bias,
-                                   label_smoothing=label_smoothing, z_loss=z_loss)
+                                   label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap)
         ctx.save_for_backward(e, c, bias, targets, lse, ws)
-        ctx.cfg = (reduction, ignore_index, filter, accum, label_smoothing, z_loss)
+        ctx.cfg = (reduction, ignore_index, filter, accum, label_smoothing, z_loss, softcap)
         return loss
 
     @staticmethod
     def backward(ctx, grad):
         e, c, bias, targets, lse, ws = ctx.saved_tensors
-        reduction, ignore_index, filter, accum, label_smoothing, z_loss = ctx.cfg
+        reduction, ignore_index, filter, accum, label_smoothing, z_loss, softcap = ctx.cfg
         want_db = bias is not None and ctx.needs_input_grad[2]
         out = backward(e, c, targets, lse, grad, ws, ignore_index=ignore_index, reduction=reduction,
                        filter=filter, accum=accum, bias=bias, want_dbias=want_db,
-                       label_smoothing=label_smoothing, z_loss=z_loss)
+                       label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap)
         dE, dC = out[0], out[1]
         db = out[2].to(bias.dtype) if want_db else None
         # autograd wants gradients in the inputs' dtype
-        return dE.to(e.dtype), dC.to(c.dtype), db, None, None, None, None, None, None, None
+        return dE.to(e.dtype), dC.to(c.dtype), db, None, None, None, None, None, None, None, None
 
 
 def cce_loss(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, reduction: str = "mean",
              ignore_index: int = -100, filter: bool = True, accum: str = "deterministic",
-             bias: torch.Tensor | None = None, label_smoothing: float = 0.0, z_loss: float = 0.0) -> torch.Tensor:
+             bias: torch.Tensor | None = None, label_smoothing: float = 0.0, z_loss: float = 0.0,
+             softcap: float = 0.0) -> torch.Tensor:
     """Flat form: e [N, D], c [V, D], targets [N], optional bias [V]."""
     return _CCEFunction.apply(e.contiguous(), c.contiguous(), None if bias is None else bias.contiguous(),
                               targets.contiguous().to(torch.int64), reduction, ignore_index, filter, accum,
-                              float(label_smoothing), float(z_loss))
+                              float(label_smoothing), float(z_loss), float(softcap))
 
 
 def linear_cross_entropy(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, bias=None,
                          reduction: str = "mean", ignore_index: int = -100, filter: bool = True,
                          accum: str = "deterministic", label_smoothing: float = 0.0,
-                         z_loss: float = 0.0) -> torch.Tensor:
+                         z_loss: float = 0.0, softcap: float = 0.0) -> torch.Tensor:
     """Cross-entropy of softmax(e @ c.T + bias) against targets without forming
     the logits.  e [..., D], c [V, D], targets [...], bias [V] or None;
     'none' returns a tensor shaped like targets.  label_smoothing spreads eps
-    over all V classes; z_loss adds z_loss * LSE^2 per row."""
+    over all V classes; z_loss adds z_loss * LSE^2 per row; softcap = s > 0
+    soft-caps the logits to s * tanh(z / s)."""
     if reduction not in _REDUCTIONS:
         raise ValueError(f"reduction must be one of {sorted(_REDUCTIONS)}")
     shape = targets.shape
     D = e.shape[-1]
     out = cce_loss(e.reshape(-1, D), c, targets.reshape(-1), reduction, ignore_index, filter, accum, bias=bias,
-                   label_smoothing=label_smoothing, z_loss=z_loss)
+                   label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap)
     return out.reshape(shape) if reduction == "none" else out

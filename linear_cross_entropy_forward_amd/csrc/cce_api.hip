@@ -108,7 +108,9 @@ static cce_status check_common(const void* e, const void* c, const int64_t* targ
     return CCE_ERR_INVALID_ARG;
   if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return CCE_ERR_INVALID_ARG;
   if (!aligned16(e) || !aligned16(c) || !aligned16(ws) || ((uintptr_t)targets & 7u)) return CCE_ERR_INVALID_ARG;
-  if (softcap != 0.0f) return CCE_ERR_UNSUPPORTED;
+  if (!(softcap >= 0.0f && softcap <= 3.0e38f)) return CCE_ERR_INVALID_ARG;
+  // soft-capping is built for bf16 operands only (the fp32 variant is off)
+  if (softcap > 0.0f && dtype != kDtypeBf16) return CCE_ERR_UNSUPPORTED;
   const int64_t es = dtype == kDtypeBf16 ? 2 : 4;
   if (D % (16 / es) != 0) return CCE_ERR_UNSUPPORTED;
   // 32-bit buffer offsets: every operand a kernel addresses from one base
@@ -190,6 +192,7 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
   cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, ws, 0);
   if (st != CCE_OK) return st;
   if (!bias_ok(bias, dtype) || !terms_ok(label_smoothing, z_loss)) return CCE_ERR_INVALID_ARG;
+  if (softcap > 0.0f && label_smoothing > 0.0f) return CCE_ERR_UNSUPPORTED;
   if (!loss || !lse) return CCE_ERR_INVALID_ARG;
   // The forward only touches the leading (chunk-independent) part of the
   // layout; any workspace sized for some vocab_chunk is large enough for it.
@@ -210,6 +213,7 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
   P.reduction = reduction;
   P.label_smoothing = label_smoothing;
   P.z_loss = z_loss;
+  P.softcap = softcap;
   P.loss = loss;
   P.lse = lse;
   P.n_valid = n_valid;
@@ -226,6 +230,7 @@ cce_status cce_backward(const void* e, const void* c, const void* bias, const in
   if (st != CCE_OK) return st;
   if (!bias_ok(bias, dtype) || ((uintptr_t)dbias & 3u) || !terms_ok(label_smoothing, z_loss))
     return CCE_ERR_INVALID_ARG;
+  if (softcap > 0.0f && label_smoothing > 0.0f) return CCE_ERR_UNSUPPORTED;
   if (!lse || !grad_loss || !dE || !dC) return CCE_ERR_INVALID_ARG;
   if ((filter != 0 && filter != 1) || (accum != kAccumDeterministic && accum != kAccumAtomic))
     return CCE_ERR_INVALID_ARG;
@@ -245,6 +250,7 @@ cce_status cce_backward(const void* e, const void* c, const void* bias, const in
   P.reduction = reduction;
   P.label_smoothing = label_smoothing;
   P.z_loss = z_loss;
+  P.softcap = softcap;
   P.lse = (float*)lse;
   P.grad_loss = grad_loss;
   P.filter = filter;

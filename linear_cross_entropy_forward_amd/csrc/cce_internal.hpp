@@ -55,6 +55,7 @@ struct Problem {
   int reduction;
   float label_smoothing;  // eps in [0, 1]: soft target (1 - eps) onehot + eps / V
   float z_loss;           // lam >= 0: loss_i += lam * LSE_i^2
+  float softcap;          // s >= 0: logits s tanh(z / s) when s > 0
   // forward outputs / backward inputs
   float* loss;
   float* lse;

@@ -47,6 +47,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Logit soft-capping s tanh(z / s) (the Gemma 2 form; the pages do not define
+// it), from tanh(x) = 1 - 2 / (exp(2x) + 1): s - 2s / (exp2(z k) + 1) with
+// k = 2 log2(e) / s.  Saturates to +-s exactly (exp2 gives inf or 0); near 0
+// the absolute error is a few ulp of s.
+__device__ __forceinline__ float softcap_f(float z, float s, float k) {
+  return __builtin_fmaf(-2.f * s, __builtin_amdgcn_rcpf(fast_exp2(z * k) + 1.f), s);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -88,10 +96,11 @@ template <> __device__ __forceinline__ float to_f<uint16_t>(uint16_t v) {
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
 
 // The classifier bias of a 256-row vocabulary tile, as fp32, into LDS (rows
-// past V read 0).  Visible to the waves after the main loop's first barrier.
+// past V, and every row without a bias, read 0).  Visible to the waves after
+// the main loop's first barrier.
 template <typename T, int ROWS>
 __device__ __forceinline__ void stage_bias(float* sb, const T* __restrict__ bias, int v0, int V) {
-  for (int i = threadIdx.x; i < ROWS; i += blockDim.x) sb[i] = v0 + i < V ? to_f<T>(bias[v0 + i]) : 0.f;
+  for (int i = threadIdx.x; i < ROWS; i += blockDim.x) sb[i] = (bias && v0 + i < V) ? to_f<T>(bias[v0 + i]) : 0.f;
 }
 // Bias of the four consecutive tile rows r..r+3 (r a multiple of 4).
 __device__ __forceinline__ f32x4 bias4(const float* sb, int r) {
@@ -206,15 +215,16 @@ template <class C>
 __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T* __restrict__ c,
                                                             const typename C::T* __restrict__ e,
                                                             const typename C::T* __restrict__ bias,
-                                                            int N, int D, int V, float2* __restrict__ part,
-                                                            int nVB, int tiles_n, int total) {
+                                                            int N, int D, int V, float softcap,
+                                                            float2* __restrict__ part, int nVB, int tiles_n,
+                                                            int total) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ __attribute__((aligned(16))) float sbias[C::BM];
   int tv, tn;
   grouped_tile(xcd_remap(blockIdx.x, total), total / tiles_n, tiles_n, kRasterGroup, tv, tn);
   const int v0 = tv * C::BM, n0 = tn * C::BN;
-  if (bias) stage_bias<T, C::BM>(sbias, bias, v0, V);
+  if (bias || softcap > 0.f) stage_bias<T, C::BM>(sbias, bias, v0, V);
 
   Operand A = make_operand(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T), (uint32_t)D,
                min(C::BM, V - v0), D);
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
   const int wm = (threadIdx.x >> 6) / C::WAVES_N;
   const int vblk = (v0 + wm * C::WM) / C::WM;
   // logits of this lane's 64 rows of column fn (plus the rows' bias)
-  auto emit = [&](auto has_bias) {
+  auto emit = [&](auto has_bias) __attribute__((always_inline)) {
     f32x4 bz[C::FM][4];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
@@ -260,8 +270,27 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
       if (lane < 32 && n < N && vblk < nVB) part[(size_t)n * nVB + vblk] = make_float2(mx, s);
     }
   };
-  if (bias) emit(std::true_type{});
-  else emit(std::false_type{});
+  if (sizeof(T) == 2 && softcap > 0.f) {
+    // capped logits (bias included) in place, then the plain epilogue (bf16
+    // operands only: the host rejects soft-capping with fp32)
+    const float kc = 2.f * kLog2e / softcap;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 bz = bias4(sbias, am.row(fm, 4 * q));
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            acc[fm][fn][4 * q + u] = softcap_f(acc[fm][fn][4 * q + u] + bz[u], softcap, kc);
+      }
+    emit(std::false_type{});
+  } else if (bias) {
+    emit(std::true_type{});
+  } else {
+    emit(std::false_type{});
+  }
 }
 
 // ============================================================================
@@ -278,7 +307,7 @@ __global__ __launch_bounds__(256) void rows_kernel(const T* __restrict__ e, cons
                                                    int V, int64_t ignore_index,
                                                    const float2* __restrict__ part, int nVB,
                                                    const float* __restrict__ csum, const float* __restrict__ aux,
-                                                   float eps, float lam,
+                                                   float eps, float lam, float softcap,
                                                    float* __restrict__ lse_out, float* __restrict__ nll) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -329,6 +358,7 @@ __global__ __launch_bounds__(256) void rows_kernel(const T* __restrict__ e, cons
     }
     zy = wave_sum(acc);
     if (bias) zy += to_f<T>(bias[t]);
+    if (softcap > 0.f) zy = softcap_f(zy, softcap, 2.f * kLog2e / softcap);
     if constexpr (SMOOTH) {
       zs = wave_sum(accs);
       if (bias) zs += aux[0];
@@ -590,7 +620,8 @@ template <class C>
 __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     const typename C::T* __restrict__ c, const typename C::T* __restrict__ e, const typename C::T* __restrict__ bias,
     const int64_t* __restrict__ targets, const float* __restrict__ lse, const float* __restrict__ scale,
-    float eps, float lam, const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int tiles_v,
+    float eps, float lam, float softcap, const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0,
+    int tiles_v,
     int tiles_n, int Vc, int gt_ld, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes,
     size_t gt_bytes, float* __restrict__ db_part) {
   using T = typename C::T;
@@ -602,7 +633,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   const int tv = cvb0 + tvl;
   if (!keep[(size_t)tn * nvb_t + tv]) return;
   const int v0 = tv * C::BM, n0 = tn * C::BN;
-  if (bias) stage_bias<T, C::BM>(sbias, bias, v0, V);
+  if (bias || softcap > 0.f) stage_bias<T, C::BM>(sbias, bias, v0, V);
 
   Operand A = make_operand(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T), (uint32_t)D,
                min(C::BM, V - v0), D);
@@ -647,26 +678,36 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   // A column's target row lies in this wave's 128 rows for few tiles (about
   // 128 / V of them per column): a wave-uniform test skips the one-hot compare
   // everywhere else.
-  auto compute = [&](auto ragged, auto has_bias, auto&& sink) {
+  // mode 0: plain logits; 1: plus the bias; 2: bias (zero without one), then
+  // soft-capped, G scaled by the cap's derivative 1 - (z'/s)^2
+  const float kcap = softcap > 0.f ? 2.f * kLog2e / softcap : 0.f;
+  const float rcap = softcap > 0.f ? 1.f / softcap : 0.f;
+  auto compute = [&](auto ragged, auto mode, auto&& sink) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode)::value;
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
-      auto body = [&](auto with_target) {
+      auto body = [&](auto with_target) __attribute__((always_inline)) {
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             float g[4];
             const int rl = am.row(fm, 4 * q);
-            const f32x4 bz = decltype(has_bias)::value ? bias4(sbias, rl) : f32x4{};
+            const f32x4 bz = MODE ? bias4(sbias, rl) : f32x4{};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              const float z = decltype(has_bias)::value ? acc[fm][fn][4 * q + u] + bz[u] : acc[fm][fn][4 * q + u];
+              float z = MODE ? acc[fm][fn][4 * q + u] + bz[u] : acc[fm][fn][4 * q + u];
+              if constexpr (MODE == 2) z = softcap_f(z, softcap, kcap);
               const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lsel[fn]));
               if constexpr (decltype(with_target)::value) {
                 const float tsc = trow[fn] == fm * 32 + 8 * q + u ? st[fn] : 0.f;
                 g[u] = __builtin_fmaf(p, sc[fn], -tsc);
               } else {
                 g[u] = p * sc[fn];
+              }
+              if constexpr (MODE == 2) {
+                const float y = z * rcap;
+                g[u] *= __builtin_fmaf(-y, y, 1.f);
               }
               if constexpr (decltype(ragged)::value) g[u] = v0 + rl + u < V ? g[u] : 0.f;
             }
@@ -678,13 +719,20 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
       else body(std::false_type{});
     }
   };
-  auto run = [&](auto&& sink) {
-    auto rag = [&](auto hb) {
-      if (v0 + C::BM <= V) compute(std::false_type{}, hb, sink);
-      else compute(std::true_type{}, hb, sink);
+  auto run = [&](auto&& sink) __attribute__((always_inline)) {
+    auto rag = [&](auto mode) __attribute__((always_inline)) {
+      if (v0 + C::BM <= V) compute(std::false_type{}, mode, sink);
+      else compute(std::true_type{}, mode, sink);
     };
-    if (bias) rag(std::true_type{});
-    else rag(std::false_type{});
+    // soft-capping exists for bf16 operands only (the host rejects fp32)
+    if constexpr (sizeof(T) == 2) {
+      if (softcap > 0.f) {
+        rag(std::integral_constant<int, 2>{});
+        return;
+      }
+    }
+    if (bias) rag(std::integral_constant<int, 1>{});
+    else rag(std::integral_constant<int, 0>{});
   };
 
   if constexpr (sizeof(T) == 2) {
@@ -730,7 +778,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     };
     uint32_t pk[C::FN][C::FM][4][2];
     // pass 1: [token][vocab] -> G rows
-    run([&](int fn, int fm, int q, int, const float (&g)[4]) {
+    run([&](int fn, int fm, int q, int, const float (&g)[4]) __attribute__((always_inline)) {
       const int rl = am.row(fm, 4 * q);
       pk[fn][fm][q][0] = pack_bf16(g[0], g[1]);
       pk[fn][fm][q][1] = pack_bf16(g[2], g[3]);
@@ -757,7 +805,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     drain(rgt, (uint32_t)gt_ld, (uint32_t)vl0, (uint32_t)n0, std::true_type{}, db_part != nullptr);
   } else {
     float rs[C::FM][4][4] = {};  // this lane's share of each row's token sum (for db)
-    run([&](int fn, int fm, int q, int rl, const float (&g)[4]) {
+    run([&](int fn, int fm, int q, int rl, const float (&g)[4]) __attribute__((always_inline)) {
       const int n = n0 + am.colj(fn);
       store4(rg, ((uint32_t)n * (uint32_t)Vc + (uint32_t)(vl0 + rl)) * (uint32_t)sizeof(T), g[0], g[1], g[2], g[3],
              (const T*)nullptr);
@@ -1068,17 +1116,17 @@ static hipError_t launch_forward_t(const Problem& P, const Layout& L, hipStream_
   const int total = tiles_v * tiles_n;
   prof_before(kKFwdTile, st);
   hipLaunchKernelGGL(fwd_tile_kernel<C>, dim3(total), dim3(C::NT), 0, st, c, e, (const T*)P.bias, P.N, P.D, P.V,
-                     L.part, L.nVB, tiles_n, total);
+                     P.softcap, L.part, L.nVB, tiles_n, total);
   prof_after(kKFwdTile, st);
   prof_before(kKRows, st);
   if (smooth)
     hipLaunchKernelGGL((rows_kernel<T, true>), dim3((P.N + 3) / 4), dim3(256), 0, st, e, c, (const T*)P.bias,
                        P.targets, P.N, P.D, P.V, P.ignore_index, L.part, L.nVB, (const float*)L.csum,
-                       (const float*)L.aux, P.label_smoothing, P.z_loss, P.lse, L.nll_out);
+                       (const float*)L.aux, P.label_smoothing, P.z_loss, P.softcap, P.lse, L.nll_out);
   else
     hipLaunchKernelGGL((rows_kernel<T, false>), dim3((P.N + 3) / 4), dim3(256), 0, st, e, c, (const T*)P.bias,
                        P.targets, P.N, P.D, P.V, P.ignore_index, L.part, L.nVB, (const float*)nullptr,
-                       (const float*)nullptr, 0.f, P.z_loss, P.lse, L.nll_out);
+                       (const float*)nullptr, 0.f, P.z_loss, P.softcap, P.lse, L.nll_out);
   prof_after(kKRows, st);
   prof_before(kKReduce, st);
   hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(1024), 0, st, L.nll_out, P.targets, P.N, P.V, P.ignore_index,
@@ -1137,7 +1185,7 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     const int cvb0 = cv0 / kTileV;
     prof_before(kKGradTile, st);
     hipLaunchKernelGGL(grad_tile_kernel<C>, dim3(cnvb * tiles_n), dim3(C::NT), 0, st, c, e, (const T*)P.bias,
-                       P.targets, P.lse, L.scale, P.label_smoothing, P.z_loss, L.keep, P.N, P.D, P.V, L.nvb_t,
+                       P.targets, P.lse, L.scale, P.label_smoothing, P.z_loss, P.softcap, L.keep, P.N, P.D, P.V, L.nvb_t,
                        cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
                        G, (T*)L.Gt, L.g_bytes, L.gt_bytes, P.dbias ? L.db_part : nullptr);
     prof_after(kKGradTile, st);

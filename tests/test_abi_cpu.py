@@ -89,7 +89,11 @@ def test_forward_argument_errors(L):
     assert _fwd(L, dt=2) == INVALID
     assert _fwd(L, red=3) == INVALID
     assert _fwd(L, e=FAKE + 4) == INVALID            # misaligned
-    assert _fwd(L, cap=30.0) == UNSUPPORTED         # soft-capping is not defined here
+    for cap in (-1.0, float("inf"), float("nan")):  # softcap negative or not finite
+        assert _fwd(L, cap=cap) == INVALID
+    assert _fwd(L, cap=30.0, ls=0.1) == UNSUPPORTED    # soft-capping with label smoothing
+    assert _fwd(L, cap=30.0, zl=1e-4, wsb=16) == WORKSPACE  # a valid cap passes to the size check
+    assert _fwd(L, cap=30.0, dt=1) == UNSUPPORTED      # soft-capping is built for bf16 only
     assert _fwd(L, D=60) == UNSUPPORTED             # bf16 rows must be 16-byte multiples
     assert _fwd(L, dt=1, D=62) == UNSUPPORTED
     assert _fwd(L, wsb=16) == WORKSPACE
@@ -111,7 +115,9 @@ def test_backward_argument_errors(L):
     assert _bwd(L, flt=2) == INVALID
     assert _bwd(L, acc=5) == INVALID
     assert _bwd(L, chunk=100) == INVALID
-    assert _bwd(L, cap=1.0) == UNSUPPORTED
+    assert _bwd(L, cap=-1.0) == INVALID
+    assert _bwd(L, cap=1.0, ls=0.2) == UNSUPPORTED
+    assert _bwd(L, cap=1.0, wsb=1024) == WORKSPACE
     assert _bwd(L, wsb=1024) == WORKSPACE
     need = L.cce_workspace_size(64, 64, 100, 0, 0)
     assert _bwd(L, wsb=need - 1) == WORKSPACE
