@@ -59,7 +59,10 @@ Gradient filtering (README "How it works" item 2; Wijmans et al. abstract:
 skip gradient entries below numerical precision) is modelled by
 `filter_keep`: a tile (row block b, vocab block v) of G is kept iff some valid
 row i in b has max_{j in v} softmax_ij >= 2^-12, or some valid row in b has
-its target in v.  `backward(..., keep=...)` zeroes G on dropped tiles.  The
+its target in v.  Row blocks are cut from the non-ignored rows only, in order
+(`tile_blocks`): ignored (padding) rows belong to no tile, as the Loss
+functions page's "Efficiency" list has padded rows skipped rather than
+computed; their G is zero either way.  `backward(..., keep=...)` zeroes G on dropped tiles.  The
 target-tile rule and the strict "< 2^-12 everywhere" reading are this
 implementation's readings of a criterion the pages state only loosely.  With
 label smoothing the filter still decides on the softmax alone and drops only
@@ -193,9 +196,28 @@ def tile_row_max(z: np.ndarray, Bv: int) -> np.ndarray:
     return z.reshape(n, nvb, Bv).max(axis=2)
 
 
+def tile_blocks(valid: np.ndarray, Bn: int) -> np.ndarray:
+    """Row block of each row in the tiles of G: the non-ignored rows, in
+    order, cut into blocks of Bn; ignored rows belong to no block (-1)."""
+    v = np.asarray(valid, dtype=bool)
+    rank = np.cumsum(v) - 1
+    return np.where(v, rank // Bn, -1)
+
+
+def _mark_keep(keep: np.ndarray, blk: np.ndarray, tm: np.ndarray, t: np.ndarray, Bv: int) -> None:
+    """Add rows (block blk >= 0, log tile maxima tm [rows, nvb], targets t) to
+    the keep map: a tile is kept by a row whose tile maximum reaches 2^-12,
+    and by a row whose target lies in it."""
+    r = np.nonzero(blk >= 0)[0]
+    if len(r):
+        np.logical_or.at(keep, blk[r], tm[r] >= FILTER_LOG_THRESHOLD)
+        keep[blk[r], t[r] // Bv] = True
+
+
 def filter_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100,
                 lse=None, bias=None, softcap: float = 0.0) -> np.ndarray:
-    """Keep map [ceil(N/Bn), ceil(V/Bv)] of (row block, vocab block) tiles of G.
+    """Keep map [ceil(N/Bn), ceil(V/Bv)] of (row block, vocab block) tiles of G
+    (row blocks from `tile_blocks`; blocks past the valid rows stay empty).
 
     Kept iff some valid row i of the block has max_j softmax_ij >= 2^-12 on the
     tile, i.e. max_j Z_ij - LSE_i >= -12 ln 2, or some valid row of the block
@@ -206,17 +228,13 @@ def filter_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100,
     t = np.asarray(targets, dtype=np.int64)
     N, V = e.shape[0], c.shape[0]
     valid = valid_rows(t, V, ignore_index)
-    nb, nvb = -(-N // Bn), -(-V // Bv)
-    keep = np.zeros((nb, nvb), dtype=bool)
-    for b in range(nb):
-        r0, r1 = b * Bn, min(N, (b + 1) * Bn)
+    blk = tile_blocks(valid, Bn)
+    keep = np.zeros((-(-N // Bn), -(-V // Bv)), dtype=bool)
+    for r0 in range(0, N, _ROW_CHUNK):
+        r1 = min(N, r0 + _ROW_CHUNK)
         z = logits(e[r0:r1], c, bias, softcap)
         l = row_logsumexp(z) if lse is None else _f64(lse)[r0:r1]
-        tm = tile_row_max(z, Bv) - l[:, None]          # log of the tile's max softmax
-        v = valid[r0:r1]
-        if v.any():
-            keep[b] |= (tm[v] >= FILTER_LOG_THRESHOLD).any(axis=0)
-            keep[b, t[r0:r1][v] // Bv] = True
+        _mark_keep(keep, blk[r0:r1], tile_row_max(z, Bv) - l[:, None], t[r0:r1], Bv)
     return keep
 
 
@@ -243,6 +261,14 @@ def softmax_grad_rows(z: np.ndarray, lse: np.ndarray, t: np.ndarray, scale: np.n
     return g
 
 
+def _colmask(keep: np.ndarray, blk: np.ndarray, Bv: int, V: int) -> np.ndarray:
+    """[rows, V] mask of the entries in kept tiles (rows of no block: none)."""
+    m = np.zeros((len(blk), V), dtype=bool)
+    r = np.nonzero(blk >= 0)[0]
+    m[r] = np.repeat(keep[blk[r]], Bv, axis=1)[:, :V]
+    return m
+
+
 @dataclass
 class Backward:
     dE: np.ndarray
@@ -264,15 +290,14 @@ def backward(e, c, targets, ignore_index: int = -100, reduction: str = "mean",
     dE = np.zeros_like(e)
     dC = np.zeros_like(c)
     db = np.zeros(V)
-    chunk = _ROW_CHUNK if keep is None else tile[0]
-    for s in range(0, N, chunk):
-        sl = slice(s, min(N, s + chunk))
+    blk = tile_blocks(valid, tile[0]) if keep is not None else None
+    for s in range(0, N, _ROW_CHUNK):
+        sl = slice(s, min(N, s + _ROW_CHUNK))
         z = logits(e[sl], c, bias, softcap)
         lse = row_logsumexp(z)
         cm = None
         if keep is not None:
-            Bn, Bv = tile
-            cm = np.broadcast_to(np.repeat(keep[s // Bn], Bv)[:V], z.shape)
+            cm = _colmask(keep, blk[sl], tile[1], V)
         g = softmax_grad_rows(z, lse, t[sl], scale[sl], valid[sl], label_smoothing, z_loss, cm, softcap)
         dE[sl] = g @ c
         dC += g.T @ e[sl]
@@ -303,19 +328,15 @@ def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias
     t = np.asarray(targets, dtype=np.int64)
     N, V = e.shape[0], c.shape[0]
     valid = valid_rows(t, V, ignore_index)
-    nb, nvb = -(-N // Bn), -(-V // Bv)
-    keep = np.zeros((nb, nvb), dtype=bool)
+    blk = tile_blocks(valid, Bn)
+    keep = np.zeros((-(-N // Bn), -(-V // Bv)), dtype=bool)
     lse = np.empty(N)
-    for b in range(nb):
-        r0, r1 = b * Bn, min(N, (b + 1) * Bn)
+    for r0 in range(0, N, _ROW_CHUNK):
+        r1 = min(N, r0 + _ROW_CHUNK)
         z = logits(e[r0:r1], c, bias, softcap)
         l = row_logsumexp(z)
         lse[r0:r1] = l
-        tm = tile_row_max(z, Bv) - l[:, None]
-        v = valid[r0:r1]
-        if v.any():
-            keep[b] |= (tm[v] >= FILTER_LOG_THRESHOLD).any(axis=0)
-            keep[b, t[r0:r1][v] // Bv] = True
+        _mark_keep(keep, blk[r0:r1], tile_row_max(z, Bv) - l[:, None], t[r0:r1], Bv)
     return lse, keep
 
 
@@ -329,20 +350,18 @@ def lse_keep_nll(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias
     t = np.asarray(targets, dtype=np.int64)
     N, V = e.shape[0], c.shape[0]
     valid = valid_rows(t, V, ignore_index)
-    nb, nvb = -(-N // Bn), -(-V // Bv)
-    keep = np.zeros((nb, nvb), dtype=bool)
+    blk = tile_blocks(valid, Bn)
+    keep = np.zeros((-(-N // Bn), -(-V // Bv)), dtype=bool)
     lse = np.empty(N)
     nll = np.zeros(N)
-    for b in range(nb):
-        r0, r1 = b * Bn, min(N, (b + 1) * Bn)
+    for r0 in range(0, N, _ROW_CHUNK):
+        r1 = min(N, r0 + _ROW_CHUNK)
         z = logits(e[r0:r1], c, bias, softcap)
         l = row_logsumexp(z)
         lse[r0:r1] = l
-        tm = tile_row_max(z, Bv) - l[:, None]
+        _mark_keep(keep, blk[r0:r1], tile_row_max(z, Bv) - l[:, None], t[r0:r1], Bv)
         v = valid[r0:r1]
         if v.any():
-            keep[b] |= (tm[v] >= FILTER_LOG_THRESHOLD).any(axis=0)
-            keep[b, t[r0:r1][v] // Bv] = True
             T = soft_target_rows(t[r0:r1], V, v, label_smoothing)
             r = np.nonzero(v)[0]
             nll[r0 + r] = -(T[r] * (z[r] - l[r, None])).sum(axis=1) + z_loss * l[r] ** 2
@@ -370,8 +389,7 @@ def dE_rows(e, c, targets, rows, ignore_index: int = -100, reduction: str = "mea
     lse = row_logsumexp(z)
     cm = None
     if keep is not None:
-        Bn, Bv = tile
-        cm = np.stack([np.repeat(keep[i // Bn], Bv)[:V] for i in rows])
+        cm = _colmask(keep, tile_blocks(valid_all, tile[0])[rows], tile[1], V)
     g = softmax_grad_rows(z, lse, t[rows], scale, valid_all[rows], label_smoothing, z_loss, cm, softcap)
     return g @ c
 
@@ -400,8 +418,8 @@ def G_columns(e, c, targets, vocab_ids, lse, ignore_index: int = -100, reduction
     g -= (1.0 - label_smoothing) * (t[:, None] == vocab_ids[None, :])
     if keep is not None:
         Bn, Bv = tile
-        rowblk = np.arange(e.shape[0]) // Bn
-        g *= keep[rowblk][:, vocab_ids // Bv]
+        blk = tile_blocks(valid, Bn)
+        g *= np.where(blk[:, None] >= 0, keep[np.maximum(blk, 0)][:, vocab_ids // Bv], False)
     g -= label_smoothing / V
     if softcap:
         g *= 1.0 - (zc / softcap) ** 2

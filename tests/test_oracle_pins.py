@@ -290,17 +290,20 @@ def test_out_of_range_target_raises():
 
 # --------------------------------------------------------------------------- filtering
 def _brute_keep(e, c, t, Bn, Bv, ignore=-100):
+    """Loops: the k-th non-ignored row (k = 0, 1, ...) is in row block k // Bn."""
     N, V = len(e), len(c)
     z = e @ c.T
     nb, nvb = -(-N // Bn), -(-V // Bv)
     keep = np.zeros((nb, nvb), dtype=bool)
+    k = 0
     for i in range(N):
         if t[i] == ignore:
             continue
         den = sum(math.exp(z[i, j]) for j in range(V))
         for j in range(V):
             if math.exp(z[i, j]) / den >= 2.0 ** -12 or j == t[i]:
-                keep[i // Bn, j // Bv] = True
+                keep[k // Bn, j // Bv] = True
+        k += 1
     return keep
 
 
@@ -760,6 +763,7 @@ def test_softcap_filter_brute_force_and_sampled():
     t[4] = -100
     keep = O.filter_keep(e, c, t, Bn, Bv, bias=b, softcap=s)
     want = np.zeros_like(keep)
+    k = 0                                       # rank among the non-ignored rows
     for i in range(N):
         if t[i] == -100:
             continue
@@ -767,7 +771,8 @@ def test_softcap_filter_brute_force_and_sampled():
         den = sum(math.exp(x) for x in zi)
         for j in range(V):
             if math.exp(zi[j]) / den >= 2.0 ** -12 or j == t[i]:
-                want[i // Bn, j // Bv] = True
+                want[k // Bn, j // Bv] = True
+        k += 1
     assert np.array_equal(keep, want)
     assert not keep.all()
     kw = dict(reduction="sum", bias=b, softcap=s, z_loss=0.01)
@@ -782,3 +787,36 @@ def test_softcap_filter_brute_force_and_sampled():
     assert np.allclose(O.dE_rows(e, c, t, [0, 7], **kk), full.dE[[0, 7]], rtol=1e-12, atol=1e-15)
     with pytest.raises(NotImplementedError):
         O.backward(e, c, t, keep=keep, tile=(Bn, Bv), reduction="sum", softcap=s, label_smoothing=0.1)
+
+
+# --------------------------------------------------------------------------- padded-row compaction
+def test_filter_tiles_skip_ignored_rows():
+    """Tiles are cut from the non-ignored rows (padding skipped, the Loss
+    functions page's "Efficiency"): with ignored rows interleaved, the
+    filtered gradients equal those of the same problem with the ignored rows
+    deleted (their dE rows are 0), with 'sum' so the scales agree; the keep
+    maps agree block for block."""
+    g = np.random.default_rng(63)
+    N, D, V, Bn, Bv = 23, 4, 45, 4, 8
+    e, c = g.standard_normal((N, D)) * 2.0, g.standard_normal((V, D)) * 2.0
+    t = g.integers(0, V, N)
+    ign = np.array([1, 2, 7, 8, 9, 15, 22])
+    t[ign] = -100
+    keep = O.filter_keep(e, c, t, Bn, Bv)
+    v = t != -100
+    keep_d = O.filter_keep(e[v], c, t[v], Bn, Bv)
+    nb = keep_d.shape[0]
+    assert np.array_equal(keep[:nb], keep_d) and not keep[nb:].any()
+    assert 0 < keep.sum() < keep.size
+    kw = dict(reduction="sum", label_smoothing=0.1, z_loss=0.01)
+    a = O.backward(e, c, t, keep=keep, tile=(Bn, Bv), **kw)
+    b = O.backward(e[v], c, t[v], keep=keep_d, tile=(Bn, Bv), **kw)
+    assert np.allclose(a.dE[v], b.dE, rtol=1e-12, atol=1e-15) and not a.dE[~v].any()
+    assert np.allclose(a.dC, b.dC, rtol=1e-12, atol=1e-15) and np.allclose(a.db, b.db, rtol=1e-12, atol=1e-15)
+    lse, keep2, _ = O.lse_keep_nll(e, c, t, Bn, Bv)
+    assert np.array_equal(keep, keep2)
+    vid = np.array([0, 13, 44])
+    assert np.allclose(O.dC_rows(e, c, t, vid, lse, keep=keep, tile=(Bn, Bv), **kw), a.dC[vid], rtol=1e-12,
+                       atol=1e-15)
+    assert np.allclose(O.dE_rows(e, c, t, [0, 3, 21], keep=keep, tile=(Bn, Bv), **kw), a.dE[[0, 3, 21]],
+                       rtol=1e-12, atol=1e-15)
