@@ -427,7 +427,7 @@ def main():
         dE = dC = None
         torch.cuda.empty_cache()
         configs = {}
-        for name in ("tiny", "llama1b", "gemma2b", "gemma2b_cal", "long8b", "long8b_cal"):
+        for name in ("tiny", "llama1b", "gemma2b", "gemma2b_cal", "long8b", "long8b_cal", "llama8b_pad25"):
             if name != args.workload:
                 configs[name] = config_summary(name)
         # the headline workload with a classifier bias and its gradient

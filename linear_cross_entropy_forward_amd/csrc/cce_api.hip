@@ -37,13 +37,15 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const int cvb = (int)(vc / kTileV);
   // dE work-groups: enough vocabulary splits to fill one round of the chip
   // (kWaveSlots work-groups, one per CU); each further split adds a partial
-  // buffer that the epilogue writes and a final pass re-reads.
+  // buffer that the epilogue writes and a final pass re-reads.  (Taking more
+  // splits when padding rows empty some token blocks measured slower: the
+  // extra epilogues and partial traffic outweigh the fuller chip.)
   int sp = (kWaveSlots + tiles_de - 1) / tiles_de;
   if (sp > 8) sp = 8;
   if (sp > cvb) sp = cvb;
   if (sp < 1) sp = 1;
   L.splits = sp;
-  int spa = (512 + tiles_de - 1) / tiles_de;
+  int spa = (2 * kWaveSlots + tiles_de - 1) / tiles_de;
   if (spa > 16) spa = 16;
   if (spa > cvb) spa = cvb;
   if (spa < 1) spa = 1;
@@ -68,6 +70,10 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   // the offsets above do not depend on the vocab chunk; the forward uses
   // only that leading part
   const size_t o_scale = take((size_t)L.Npad * 4);
+  const size_t o_rowmap = take((size_t)L.Npad * 4);
+  const size_t o_scale_c = take((size_t)L.Npad * 4);
+  const size_t o_lse_c = take((size_t)L.Npad * 4);
+  const size_t o_tgt_c = take((size_t)L.Npad * 4);
   const size_t o_keep = take((size_t)L.nb * L.nvb_t);
   const size_t o_g = take(L.g_bytes);
   const size_t o_gt = take(L.gt_bytes);
@@ -81,6 +87,10 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     L.part = (float2*)(b + o_part);
     L.nll_out = (float*)(b + o_nll);
     L.scale = (float*)(b + o_scale);
+    L.rowmap = (int*)(b + o_rowmap);
+    L.scale_c = (float*)(b + o_scale_c);
+    L.lse_c = (float*)(b + o_lse_c);
+    L.tgt_c = (int*)(b + o_tgt_c);
     L.keep = (uint8_t*)(b + o_keep);
     L.G = b + o_g;
     L.Gt = b + o_gt;

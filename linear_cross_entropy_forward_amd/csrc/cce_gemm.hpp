@@ -515,13 +515,15 @@ struct DmaTile {
   uint32_t roff[PER];  // byte offset of the lane's row, kOOB past the valid rows
   uint32_t kc;         // K offset (elements) of the lane's chunk within a step
   uint32_t flo[KG], fhi[KG];  // fragment chunk offsets by K group (fp32: two chunks)
-  __device__ __forceinline__ void init(const Operand& op) {
+  // With `rowmap`, tile row r is row rowmap[r] of the operand (-1: none).
+  __device__ __forceinline__ void init(const Operand& op, const int* __restrict__ rowmap = nullptr) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     kc = (uint32_t)(((lane & 7) ^ (lane >> 3)) * C::VEC);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int row = 8 * (wave * PER + i) + (lane >> 3);
-      roff[i] = row < op.rows ? (uint32_t)row * op.ld * (uint32_t)sizeof(T) : kOOB;
+      const int src = row < op.rows ? (rowmap ? rowmap[row] : row) : -1;
+      roff[i] = src >= 0 ? (uint32_t)src * op.ld * (uint32_t)sizeof(T) : kOOB;
     }
   }
   // DMA instruction i of this wave for the step at K offset k0 into the tile
@@ -629,7 +631,8 @@ struct DmaTileMN {
 // Steps past the end (the count is padded to even) read zeros.
 template <class C, int SPB, bool B_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1)>
 __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const Operand& A, const Operand& B,
-                                             int nsteps, const uint16_t* blocks, void* smem) {
+                                             int nsteps, const uint16_t* blocks, void* smem,
+                                             const int* __restrict__ brow = nullptr) {
   using T = typename C::T;
   using TA = DmaTile<C, C::BM>;
   using TB = std::conditional_t<B_MN, DmaTileMN<C, C::BN>, DmaTile<C, C::BN>>;
@@ -657,7 +660,9 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   TA ta;
   TB tb;
   ta.init(A);
-  tb.init(B);
+  // B rows through `brow` (K-major B only): the gathered token rows
+  if constexpr (B_MN) tb.init(B);
+  else tb.init(B, brow);
   auto dma = [&](int d, int k0, uint32_t st) {
     if (d < TA::PER) ta.issue(d, A, k0, st);
     else tb.issue(d - TA::PER, B, k0, st + TA::BYTES);

@@ -44,6 +44,7 @@ constexpr int kGtPad = 0;
 // Work-groups that run at once with one per CU (256 CUs).
 constexpr int kWaveSlots = 256;
 
+
 struct Problem {
   const void* e;
   const void* c;
@@ -74,7 +75,11 @@ struct Layout {
   int32_t* hdr;
   float2* part;     // [N][nVB]
   float* nll_out;   // [N] per-row loss (the caller's loss buffer for 'none')
-  float* scale;     // [Npad]
+  float* scale;     // [Npad] per token row (original order), 0 past N
+  int* rowmap;      // [Npad] token row of each compacted slot: valid rows, ignored rows, -1
+  float* scale_c;   // [Npad] scale per compacted slot (0 for ignored rows and padding)
+  float* lse_c;     // [Npad] LSE per compacted slot (+inf for ignored rows and padding)
+  int* tgt_c;       // [Npad] target per compacted slot (-1 for ignored rows and padding)
   float* db_part;   // [Npad/256][V] per token block column sums of G (bias gradient)
   float* csum;      // [D] sum over the vocabulary of the classifier rows (label smoothing)
   float* r1c;       // [D] -eps/V * sum_i scale_i e_i: the smoothing term of every dC row

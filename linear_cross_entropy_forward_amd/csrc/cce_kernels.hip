@@ -14,6 +14,10 @@
 //                         the classifier rows (and vec_sum of the bias), so
 //                         that sum_j z_ij = e_i . csum + sum_j b_j
 // Backward: bwd_prep      per-row gradient scale (mean/sum/none, ignore mask)
+//                         and the compaction of the token rows: the backward
+//                         works on the valid rows first, ignored rows after
+//                         (whole blocks of them drop out), reading and writing
+//                         token rows through that permutation
 //           filter        tile keep map: a (token block, vocab block) tile is
 //                         kept iff some valid row's softmax reaches 2^-12 on it
 //                         (README "How it works" item 2, using the forward's
@@ -186,17 +190,19 @@ __device__ __forceinline__ void store_quad_t(rsrc_t r, uint32_t off_row0, uint32
 }
 
 // ============================================================================
-// e^T [D][Npad] (rows past N zero) for the dC contraction, via 64x64 LDS tiles.
+// e^T [D][Npad] in compacted slot order (padding slots zero) for the dC
+// contraction, via 64x64 LDS tiles.
 // ============================================================================
 template <typename T>
-__global__ __launch_bounds__(256) void transpose_e_kernel(const T* __restrict__ e, T* __restrict__ et, int N, int D,
-                                                          int Npad) {
+__global__ __launch_bounds__(256) void transpose_e_kernel(const T* __restrict__ e, const int* __restrict__ rowmap,
+                                                          T* __restrict__ et, int N, int D, int Npad) {
   __shared__ T tile[64][65];
   const int d0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int r = ty; r < 64; r += 4) {
     const int n = n0 + r, d = d0 + tx;
-    tile[r][tx] = (n < N && d < D) ? e[(size_t)n * D + d] : (T)0;
+    const int src = rowmap[n];  // token row of compacted slot n (-1: padding)
+    tile[r][tx] = (src >= 0 && d < D) ? e[(size_t)src * D + d] : (T)0;
   }
   __syncthreads();
   for (int r = ty; r < 64; r += 4) {
@@ -509,40 +515,74 @@ __global__ __launch_bounds__(1024) void vec_sum_kernel(const T* __restrict__ x, 
 }
 
 // ============================================================================
-// Backward: per-row scale  d(loss)/d(nll_i) * upstream gradient, 0 if ignored,
-// NaN for an out-of-range target; rows in [N, Npad) get 0.
+// Backward preparation (one work-group).  Per row, in the original order, the
+// scale d(loss)/d(nll_i) times the upstream gradient: 0 if ignored, NaN for an
+// out-of-range target, 0 past N.  The compaction of the token rows (the Loss
+// functions page, "Efficiency": skip padded rows): slot n' of rowmap holds the
+// valid rows in order, then the ignored rows in order, then -1 for the slots
+// [N, Npad); per slot, scale_c, lse_c and tgt_c give the row's scale, LSE and
+// target, with scale 0, LSE +inf and target -1 for ignored rows and padding,
+// so that their gradient entries come out exactly 0.
 // ============================================================================
 __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int64_t* __restrict__ targets, int N,
                                                         int Npad, int V, int64_t ignore_index,
                                                         int reduction, const float* __restrict__ grad_loss,
-                                                        float* __restrict__ scale, int32_t* __restrict__ hdr,
+                                                        const float* __restrict__ lse,
+                                                        float* __restrict__ scale, int* __restrict__ rowmap,
+                                                        float* __restrict__ scale_c, float* __restrict__ lse_c,
+                                                        int* __restrict__ tgt_c, int32_t* __restrict__ hdr,
                                                         float* __restrict__ scale_sum) {
   __shared__ int scnt[1024];
   __shared__ float ssum[1024];
   const int tid = threadIdx.x;
+  // each thread owns a contiguous run of rows; an inclusive scan of the runs'
+  // valid counts places them
+  const int chunk = (N + 1023) / 1024;
+  const int i0 = min(N, tid * chunk), i1 = min(N, i0 + chunk);
   int cnt = 0;
-  for (int i = tid; i < N; i += 1024) cnt += targets[i] != ignore_index;
+  for (int i = i0; i < i1; ++i) cnt += targets[i] != ignore_index;
   scnt[tid] = cnt;
   __syncthreads();
-  for (int o = 512; o >= 1; o >>= 1) {
-    if (tid < o) scnt[tid] += scnt[tid + o];
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? scnt[tid - o] : 0;
+    __syncthreads();
+    scnt[tid] += v;
     __syncthreads();
   }
-  const int nv = scnt[0];
+  const int nv = scnt[1023];
+  int vslot = scnt[tid] - cnt;        // valid rows before this run
+  int islot = nv + (i0 - vslot);      // slot of this run's first ignored row
   const float g0 = reduction == kReductionNone ? 0.f : grad_loss[0];
   const float gm = reduction == kReductionMean ? (float)((double)g0 / (double)(nv > 0 ? nv : 1)) : g0;
   float acc = 0.f;
-  for (int i = tid; i < Npad; i += 1024) {
-    float s = 0.f;
-    if (i < N) {
-      const int64_t t = targets[i];
-      if (t != ignore_index) {
-        s = reduction == kReductionNone ? grad_loss[i] : gm;
-        if (t < 0 || t >= V) s = __builtin_nanf("");
-      }
+  for (int i = i0; i < i1; ++i) {
+    const int64_t t = targets[i];
+    if (t != ignore_index) {
+      const bool inrange = t >= 0 && t < V;
+      float sv = reduction == kReductionNone ? grad_loss[i] : gm;
+      if (!inrange) sv = __builtin_nanf("");
+      scale[i] = sv;
+      acc += sv;
+      rowmap[vslot] = i;
+      scale_c[vslot] = sv;
+      lse_c[vslot] = lse[i];
+      tgt_c[vslot] = inrange ? (int)t : -1;
+      ++vslot;
+    } else {
+      scale[i] = 0.f;
+      rowmap[islot] = i;
+      scale_c[islot] = 0.f;
+      lse_c[islot] = INFINITY;
+      tgt_c[islot] = -1;
+      ++islot;
     }
-    scale[i] = s;
-    acc += s;
+  }
+  for (int n = N + tid; n < Npad; n += 1024) {
+    scale[n] = 0.f;
+    rowmap[n] = -1;
+    scale_c[n] = 0.f;
+    lse_c[n] = INFINITY;
+    tgt_c[n] = -1;
   }
   if (tid == 0) {
     hdr[kHdrNValidBwd] = nv;
@@ -564,42 +604,49 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int64_t* __restric
 // ============================================================================
 __global__ __launch_bounds__(256) void filter_kernel(const int64_t* __restrict__ targets,
                                                      const float* __restrict__ lse,
-                                                     const float2* __restrict__ part, int N, int V,
-                                                     int nVB, int64_t ignore_index, int Bn, int Bv,
+                                                     const float2* __restrict__ part, const int* __restrict__ rowmap,
+                                                     int N, int V, int nVB, int64_t ignore_index, int Bn, int Bv,
                                                      int PW, int nvb_t, int filter,
                                                      uint8_t* __restrict__ keep, int32_t* __restrict__ hdr) {
   __shared__ float s_lse[kTileN];
-  __shared__ int s_tb[kTileN];
-  const int b = blockIdx.y;
+  __shared__ int s_tb[kTileN], s_row[kTileN];
+  __shared__ int s_any;
+  const int b = blockIdx.y;  // block of compacted token slots
   const int tid = threadIdx.x;
+  if (tid == 0) s_any = 0;
+  __syncthreads();
   for (int r = tid; r < Bn; r += blockDim.x) {
-    const int i = b * Bn + r;
+    const int slot = b * Bn + r;
+    const int i = slot < N ? rowmap[slot] : -1;
     float l = INFINITY;
     int tb = -1;
-    if (i < N) {
+    if (i >= 0) {
       const int64_t t = targets[i];
-      if (t != ignore_index && t >= 0 && t < V) {
-        l = lse[i];
-        tb = (int)(t / Bv);
+      if (t != ignore_index) {
+        s_any = 1;
+        if (t >= 0 && t < V) {
+          l = lse[i];
+          tb = (int)(t / Bv);
+        }
       }
     }
     s_lse[r] = l;
     s_tb[r] = tb;
+    s_row[r] = i;
   }
   __syncthreads();
   const int vb = blockIdx.x * blockDim.x + tid;
   bool k = false;
   if (vb < nvb_t) {
     if (!filter) {
-      k = true;
+      k = s_any != 0;  // a block of ignored rows only has G = 0: never computed
     } else {
       const int ppb = Bv / PW;
-      const int rows = min(Bn, N - b * Bn);
       const float thr = -12.0f * kLn2;
-      for (int r = 0; r < rows && !k; ++r) {
+      for (int r = 0; r < Bn && !k; ++r) {
         if (s_tb[r] == vb) { k = true; break; }
         if (s_tb[r] < 0) continue;
-        const float2* p = part + (size_t)(b * Bn + r) * nVB + (size_t)vb * ppb;
+        const float2* p = part + (size_t)s_row[r] * nVB + (size_t)vb * ppb;
         float m = -INFINITY;
         for (int q = 0; q < ppb; ++q)
           if (vb * ppb + q < nVB) m = fmaxf(m, p[q].x);
@@ -619,10 +666,9 @@ __global__ __launch_bounds__(256) void filter_kernel(const int64_t* __restrict__
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     const typename C::T* __restrict__ c, const typename C::T* __restrict__ e, const typename C::T* __restrict__ bias,
-    const int64_t* __restrict__ targets, const float* __restrict__ lse, const float* __restrict__ scale,
-    float eps, float lam, float softcap, const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0,
-    int tiles_v,
-    int tiles_n, int Vc, int gt_ld, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes,
+    const int* __restrict__ rowmap, const int* __restrict__ tgt_c, const float* __restrict__ lse_c,
+    const float* __restrict__ scale_c, float eps, float lam, float softcap, const uint8_t* __restrict__ keep, int N,
+    int D, int V, int nvb_t, int cvb0, int tiles_v, int tiles_n, int Vc, int gt_ld, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes,
     size_t gt_bytes, float* __restrict__ db_part) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
@@ -637,35 +683,34 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
 
   Operand A = make_operand(c + (size_t)v0 * D, (uint64_t)(V - v0) * D * sizeof(T), (uint32_t)D,
                min(C::BM, V - v0), D);
-  Operand B = make_operand(e + (size_t)n0 * D, (uint64_t)max(N - n0, 0) * D * sizeof(T), (uint32_t)D,
-               min(C::BN, N - n0), D);
+  // token rows of the tile's compacted slots n0.. through rowmap
+  Operand B = make_operand(e, (uint64_t)N * D * sizeof(T), (uint32_t)D, C::BN, D);
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
-  // per-column constants, fetched before the main loop so that their latency
-  // is hidden: lse in log2 units, the coefficients of p (scale times
+  // per-column (slot) constants, fetched before the main loop so that their
+  // latency is hidden: lse in log2 units, the coefficients of p (scale times
   // 1 + 2 lam LSE, the z-loss share) and of the one-hot target (scale times
   // 1 - eps), and the target's row relative to this lane's first accumulator
-  // row (outside the tile: -1, which no row offset matches)
+  // row (outside the tile: -1, which no row offset matches).  Ignored and
+  // padding slots have LSE +inf (p = 0) and scale 0: their G is exactly 0.
   AccMap<C> am;
   float lsel[C::FN], sc[C::FN], st[C::FN];
   int trow[C::FN];
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn) {
-    const int n = n0 + am.colj(fn);
-    const bool vn = n < N;
-    const float l = vn ? lse[n] : 0.f;
-    const float s = vn ? scale[n] : 0.f;  // zero for padding columns: their G is zero
+    const int n = n0 + am.colj(fn);  // < Npad: the grid covers the padded slots exactly
+    const float l = lse_c[n];
+    const float s = scale_c[n];
     lsel[fn] = l * kLog2e;
-    sc[fn] = s * (1.f + 2.f * lam * l);
+    sc[fn] = s != 0.f ? s * (1.f + 2.f * lam * l) : 0.f;
     st[fn] = s * (1.f - eps);
-    const int64_t tg = vn ? targets[n] : -1;
-    const int64_t rel = tg - (int64_t)(v0 + am.row0);
-    trow[fn] = (tg >= v0 && tg < v0 + C::BM) ? (int)rel : -1;
+    const int tg = tgt_c[n];
+    trow[fn] = (tg >= v0 && tg < v0 + C::BM) ? tg - (v0 + am.row0) : -1;
   }
-  mainloop_dma<C, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem);
+  mainloop_dma<C, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem, rowmap + n0);
 
   rsrc_t rg = make_rsrc(G, g_bytes);
   rsrc_t rgt = make_rsrc(Gt, gt_bytes);
@@ -842,6 +887,11 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   }
 }
 
+// Token blocks that hold valid rows (compacted slots: they come first).
+__device__ __forceinline__ int valid_blocks(const int32_t* __restrict__ hdr) {
+  return (hdr[kHdrNValidBwd] + kTileN - 1) / kTileN;
+}
+
 // Kept K blocks of one output tile into LDS; returns their count.
 __device__ __forceinline__ int collect_blocks(const uint8_t* __restrict__ keep, size_t base, int stride,
                                              int count, uint16_t* list) {
@@ -907,8 +957,9 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   constexpr int SPB = kTileN / C::BK;
-  // all token blocks kept (no filtering effect on this tile): contiguous K
-  if (nk == nb) mainloop_dma<C, SPB>(acc, A, B, nk * SPB, nullptr, smem);
+  // the kept token blocks are the first nk (no filtering effect on this tile;
+  // compacted slots put the blocks of ignored rows last): contiguous K
+  if (nk > 0 && blocks[nk - 1] == nk - 1) mainloop_dma<C, SPB>(acc, A, B, nk * SPB, nullptr, smem);
   else mainloop_dma<C, SPB>(acc, A, B, nk * SPB, blocks, smem);
 
   AccMap<C> am;
@@ -944,21 +995,50 @@ template <class C>
 __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     const typename C::T* __restrict__ G, const typename C::T* __restrict__ c,
     const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
-    int cnvb, int tiles_n, int tiles_d, int splits, int Vc, size_t g_bytes, float* __restrict__ dE,
-    float* __restrict__ dE_part, int accumulate, int atomic, const float* __restrict__ scale,
-    const float* __restrict__ csum, float r1) {
+    int cnvb, int tiles_n, int tiles_d, int splits, const int32_t* __restrict__ hdr, int Vc, size_t g_bytes,
+    float* __restrict__ dE,
+    float* __restrict__ dE_part, int accumulate, int atomic, const int* __restrict__ rowmap,
+    const float* __restrict__ scale_c, const float* __restrict__ csum, float r1) {
   using T = typename C::T;
   // bf16: LDS-DMA main loop (C fragments through transposing reads); fp32:
   // register-staged main loop (no 32-bit transposing read exists)
   constexpr bool kDma = sizeof(T) == 2;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kDma ? C::LDS_DMA_BYTES : C::LDS_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
-  const int total = tiles_n * tiles_d * splits;
-  const int tile = xcd_remap(blockIdx.x, total);
-  const int s = tile / (tiles_n * tiles_d);
-  int tn, td;
-  grouped_tile(tile % (tiles_n * tiles_d), tiles_n, tiles_d, kRasterGroup, tn, td);
+  // The grid holds tiles_n x tiles_d x splits work-groups.  The first
+  // nbv x tiles_d x splits work on the token blocks that hold valid rows
+  // (tile order remapped over exactly these, so they spread over all XCDs);
+  // the next (tiles_n - nbv) x tiles_d cover the blocks of padding rows,
+  // which only need zeros; the rest exit.
+  static_assert(C::NT == C::BN, "a padding tile is zeroed one column per thread");
+  const int nbv = valid_blocks(hdr);
+  const int work = nbv * tiles_d * splits;
+  int s, tn, td;
+  if ((int)blockIdx.x < work) {
+    const int tile = xcd_remap(blockIdx.x, work);
+    s = tile / (nbv * tiles_d);
+    grouped_tile(tile % (nbv * tiles_d), nbv, tiles_d, kRasterGroup, tn, td);
+  } else {
+    const int p = (int)blockIdx.x - work;
+    if (p >= (tiles_n - nbv) * tiles_d) return;
+    // a block of padding rows: zeros into dE and every partial in use, once
+    if (accumulate || atomic) return;
+    tn = nbv + p / tiles_d;
+    const int d = (p % tiles_d) * C::BN + (int)threadIdx.x;
+    for (int ps = 0; ps < splits; ++ps) {
+      float* o = ps == 0 ? dE : dE_part + (size_t)(ps - 1) * N * D;
+      for (int r = 0; r < C::BM; ++r) {
+        const int row = rowmap[tn * C::BM + r];
+        if (row >= 0 && d < D) o[(size_t)row * D + d] = 0.f;
+      }
+    }
+    return;
+  }
   const int n0 = tn * C::BM, d0 = td * C::BN;
+  // token rows of the tile's compacted slots, for the epilogue (visible after
+  // the barrier that ends collect_blocks)
+  __shared__ int srow[C::BM];
+  for (int i = threadIdx.x; i < C::BM; i += C::NT) srow[i] = rowmap[n0 + i];
   // this split's vocab blocks of the chunk
   const int vb_lo = (int)((int64_t)cnvb * s / splits), vb_hi = (int)((int64_t)cnvb * (s + 1) / splits);
   const int nk = collect_blocks(keep, (size_t)tn * nvb_t + cvb0 + vb_lo, 1, vb_hi - vb_lo, blocks);
@@ -993,24 +1073,32 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   }
 
   if (nk == 0 && (accumulate || atomic)) return;  // nothing to add
+  // Rows of the tile are compacted slots n0..; slot n' is token row
+  // srow[n' - n0] (ignored rows after the valid ones, -1 past N), so the first
+  // write of dE also zeroes the ignored rows.  64-bit row pointers: the rows
+  // of one tile may lie anywhere in dE.  Loads of old values are never
+  // conditional (a masked-off element reads row 0), so each fm's loads stay
+  // in flight together.
   AccMap<C> am;
   float* out = (atomic || s == 0) ? dE : dE_part + (size_t)(s - 1) * N * D;
-  float* ob = out + (size_t)n0 * D;
-  rsrc_t ro = make_rsrc(ob, (uint64_t)(N - n0) * D * sizeof(float));
-  auto offset = [&](int fm, int fn, int r) -> uint32_t {
-    const int d = d0 + am.colj(fn), nr = am.row(fm, r);
-    return (d < D && n0 + nr < N) ? ((uint32_t)nr * (uint32_t)D + (uint32_t)d) * 4u : kOOB;
-  };
+  const bool full = n0 + C::BM <= N && d0 + C::BN <= D;  // no masked element
+  int dcol[C::FN];
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn) {
+    const int d = d0 + am.colj(fn);
+    dcol[fn] = d < D ? d : -1;
+  }
   if (atomic) {
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
+      for (int r = 0; r < 16; ++r) {
+        const int row = srow[am.row(fm, r)];
+        float* rp = out + (size_t)(row >= 0 ? row : 0) * D;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t o = offset(fm, fn, r);
-          if (o != kOOB) unsafeAtomicAdd(ob + o / 4u, acc[fm][fn][r]);
-        }
+        for (int fn = 0; fn < C::FN; ++fn)
+          if (row >= 0 && dcol[fn] >= 0) unsafeAtomicAdd(rp + dcol[fn], acc[fm][fn][r]);
+      }
     return;
   }
   // Accumulating into the previous chunks' sum: the old values of a row of
@@ -1020,31 +1108,49 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   const bool rank1 = csum != nullptr && !accumulate && s == 0;
   float cs[C::FN];
 #pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) {
-    const int d = d0 + am.colj(fn);
-    cs[fn] = (rank1 && d < D) ? r1 * csum[d] : 0.f;
-  }
+  for (int fn = 0; fn < C::FN; ++fn) cs[fn] = (rank1 && dcol[fn] >= 0) ? r1 * csum[dcol[fn]] : 0.f;
+  auto epilogue = [&](auto full_tile) __attribute__((always_inline)) {
+    constexpr bool F = decltype(full_tile)::value;
 #pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm) {
-    float old[C::FN][16];
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) old[fn][r] = accumulate ? ldf(ro, offset(fm, fn, r)) : 0.f;
-    if (rank1) {
-      // scale has Npad entries: every row of the tile is inside it
+    for (int fm = 0; fm < C::FM; ++fm) {
+      float* rp[16];
+      bool rok[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float sr = scale[n0 + am.row(fm, r)];
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) old[fn][r] = sr * cs[fn];
+        const int row = srow[am.row(fm, r)];
+        rok[r] = F || row >= 0;
+        rp[r] = out + (size_t)(F || row >= 0 ? row : 0) * D;
       }
+      float old[C::FN][16];
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int dc = F || dcol[fn] >= 0 ? dcol[fn] : 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) old[fn][r] = accumulate ? rp[r][dc] : 0.f;
+      }
+      if (rank1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float sr = scale_c[n0 + am.row(fm, r)];  // slots past the valid rows: 0
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn) old[fn][r] = sr * cs[fn];
+        }
+      }
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = acc[fm][fn][r] + old[fn][r];
+          if constexpr (F) {
+            rp[r][dcol[fn]] = v;
+          } else {
+            if (rok[r] && dcol[fn] >= 0) rp[r][dcol[fn]] = v;
+          }
+        }
     }
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) stf(ro, offset(fm, fn, r), acc[fm][fn][r] + old[fn][r]);
-  }
+  };
+  if (full) epilogue(std::true_type{});
+  else epilogue(std::false_type{});
 }
 
 // dE += dE_part[0] + dE_part[1] + ... in that order (deterministic).
@@ -1150,18 +1256,19 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   const float r1 = smooth ? (float)(-(double)P.label_smoothing / (double)P.V) : 0.f;
   prof_before(kKBwdPrep, st);
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(1024), 0, st, P.targets, P.N, L.Npad, P.V, P.ignore_index,
-                     P.reduction, P.grad_loss, L.scale, L.hdr, smooth ? L.aux + 1 : nullptr);
+                     P.reduction, P.grad_loss, (const float*)P.lse, L.scale, L.rowmap, L.scale_c, L.lse_c, L.tgt_c,
+                     L.hdr, smooth ? L.aux + 1 : nullptr);
   prof_after(kKBwdPrep, st);
   // -eps/V * sum_i scale_i e_i: the smoothing share of every dC row
   if (smooth) launch_colsum<T>(e, L.scale, P.N, P.D, r1, L, L.r1c, st);
   prof_before(kKFilter, st);
   hipLaunchKernelGGL(filter_kernel, dim3((L.nvb_t + 255) / 256, L.nb), dim3(256), 0, st, P.targets, P.lse,
-                     L.part, P.N, P.V, L.nVB, P.ignore_index, kTileN, kTileV, kPartialWidth, L.nvb_t, P.filter,
+                     L.part, (const int*)L.rowmap, P.N, P.V, L.nVB, P.ignore_index, kTileN, kTileV, kPartialWidth, L.nvb_t, P.filter,
                      L.keep, L.hdr);
   prof_after(kKFilter, st);
   prof_before(kKTransE, st);
-  hipLaunchKernelGGL(transpose_e_kernel<T>, dim3((P.D + 63) / 64, L.Npad / 64), dim3(256), 0, st, e, (T*)L.Et, P.N,
-                     P.D, L.Npad);
+  hipLaunchKernelGGL(transpose_e_kernel<T>, dim3((P.D + 63) / 64, L.Npad / 64), dim3(256), 0, st, e,
+                     (const int*)L.rowmap, (T*)L.Et, P.N, P.D, L.Npad);
   prof_after(kKTransE, st);
   if (P.accum == kAccumAtomic) {
     const size_t n = (size_t)P.N * P.D;
@@ -1185,7 +1292,8 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     const int cvb0 = cv0 / kTileV;
     prof_before(kKGradTile, st);
     hipLaunchKernelGGL(grad_tile_kernel<C>, dim3(cnvb * tiles_n), dim3(C::NT), 0, st, c, e, (const T*)P.bias,
-                       P.targets, P.lse, L.scale, P.label_smoothing, P.z_loss, P.softcap, L.keep, P.N, P.D, P.V, L.nvb_t,
+                       (const int*)L.rowmap, (const int*)L.tgt_c, (const float*)L.lse_c, (const float*)L.scale_c,
+                       P.label_smoothing, P.z_loss, P.softcap, L.keep, P.N, P.D, P.V, L.nvb_t,
                        cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
                        G, (T*)L.Gt, L.g_bytes, L.gt_bytes, P.dbias ? L.db_part : nullptr);
     prof_after(kKGradTile, st);
@@ -1197,8 +1305,10 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     const int splits = P.accum == kAccumAtomic ? L.splits_atomic : L.splits;
     prof_before(kKDE, st);
     hipLaunchKernelGGL(dE_gemm_kernel<C>, dim3(tiles_n * tiles_d * splits), dim3(C::NT), 0, st, G, c, L.keep,
-                       P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits, L.Vc, L.g_bytes,
-                       P.dE, L.dE_part, ch > 0 ? 1 : 0, P.accum == kAccumAtomic ? 1 : 0, (const float*)L.scale,
+                       P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits,
+                       (const int32_t*)L.hdr, L.Vc, L.g_bytes,
+                       P.dE, L.dE_part, ch > 0 ? 1 : 0, P.accum == kAccumAtomic ? 1 : 0, (const int*)L.rowmap,
+                       (const float*)L.scale_c,
                        smooth ? (const float*)L.csum : nullptr, r1);
     prof_after(kKDE, st);
   }

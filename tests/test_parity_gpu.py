@@ -106,7 +106,9 @@ def full_check(M, inp, reduction, filter, accum="deterministic", vocab_chunk=0, 
         check_grad(r["dC"], b.dC, GRAD_RTOL, label + " dC")
         if want_db:
             check_grad(r["db"], b.db, GRAD_RTOL, label + " db")
-        assert r["stats"]["tiles_kept"] == r["stats"]["tiles_total"]
+        # every tile of the blocks of non-ignored rows (blocks of padding only drop out)
+        nvb = -(-c.shape[0] // Bv)
+        assert r["stats"]["tiles_kept"] == -(-f.n_valid // Bn) * nvb, (r["stats"], f.n_valid)
     return r
 
 
@@ -218,6 +220,29 @@ def test_bad_target_is_loud(M):
     assert math.isnan(r["loss"][5]) and np.isfinite(np.delete(r["loss"], 5)).all()
     assert r["stats_fwd"]["bad_targets"] == 1
     assert np.isnan(r["dE"][5]).all()
+
+
+# ----------------------------------------------------------------------------- padded-row compaction
+@pytest.mark.parametrize("accum", ["deterministic", "atomic"])
+def test_padding_compacted(M, accum):
+    """40% of the rows ignored, as trailing padding and scattered: the
+    backward works on the valid rows only (blocks of padding drop out of every
+    contraction), dE rows of ignored rows are exactly 0, and results match
+    the oracle, whose filter tiles are cut from the valid rows."""
+    inp = W.custom(1100, 136, 1300, "bf16", seed=61, c_std=0.1)
+    t = inp["targets"]
+    t[700:] = -100
+    t[::9] = -100
+    r = full_check(M, inp, "mean", False, accum=accum, label=f"padding {accum}")
+    assert r["stats"]["tiles_kept"] < r["stats"]["tiles_total"]
+    full_check(M, inp, "none", True, accum=accum, vocab_chunk=512, label=f"padding filtered {accum}")
+
+
+def test_padding_with_all_terms(M):
+    inp = W.custom(900, 72, 1100, "bf16", seed=62, c_std=0.1, ignore_frac=0.3)
+    bias = W.bias(1100, "bf16", seed=62)
+    full_check(M, inp, "sum", True, label="padding smoothing", bias=bias, want_db=True, ls=0.1, zl=1e-4)
+    full_check(M, inp, "mean", True, label="padding softcap", bias=bias, want_db=True, zl=1e-4, cap=5.0)
 
 
 # ----------------------------------------------------------------------------- classifier bias
@@ -518,3 +543,10 @@ def test_full_llama1b_smoothing_zloss(M):
 def test_full_gemma2b_softcap(M):
     """Gemma 2's own final-logit cap (30) on the calibrated Gemma-2-2B head."""
     _sampled_full(M, "gemma2b_cal", "mean", True, cap=30.0)
+
+
+@pytest.mark.slow
+def test_full_llama8b_padded(M):
+    """The 8B head with a quarter of the rows padding: the compacted backward."""
+    r = _sampled_full(M, "llama8b_pad25", "mean", True)
+    assert r["stats"]["tiles_kept"] <= 12 * 502

@@ -13,6 +13,7 @@ table and "Performance" section):
   gemma2b   N=4096  D=2304 V=256000  bf16  "trained-like" e (see below), Zipf(1.1) targets, none ignored
   llama8b   N=4096  D=4096 V=128256  bf16  e~N(0,1), c~N(0,0.02^2), uniform targets, none ignored
   long8b    N=16384 D=4096 V=128256  bf16  trained-like e, Zipf(1.1) targets, 3% ignored
+  llama8b_pad25  as llama8b (seed 6) with 25% of the rows ignored (padding)
 
 "trained-like" literal construction: e_i = 3 * c_{y_i}/||c_{y_i}|| * sqrt(D) + N(0, I).
 The "calibrated" variants (gemma2b_cal, long8b_cal) instead use
@@ -115,6 +116,8 @@ WORKLOADS: dict[str, Workload] = {
                         reduction="none"),
     "long8b": Workload("long8b", 16384, 4096, 128256, "bf16", "trained", 1.0, 0.02, "zipf", 0.03, 5),
     "long8b_cal": Workload("long8b_cal", 16384, 4096, 128256, "bf16", "calibrated", 1.0, 0.02, "zipf", 0.03, 5),
+    # the 8B head with a quarter of the rows padding (variable-length batches)
+    "llama8b_pad25": Workload("llama8b_pad25", 4096, 4096, 128256, "bf16", "normal", 1.0, 0.02, "uniform", 0.25, 6),
 }
 
 
