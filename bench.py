@@ -38,11 +38,11 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "a34b291b383eafe675a9794b31bd2134dfab6edbbb19f5cd0c438a7135e2fb15",
+    "source_sha256": "68e9d3b5895e7ff10436e4155c515271f4c06a10855610fcadef9565f45dc45d",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9269.7e6, "grad_tile": 2234.6e6, "dC_gemm": 2257.0e6, "dE_gemm": 1858.8e6,
-        "rows": 121.4e6, "filter": 3.3e6, "transpose_e": 67.1e6,
+        "fwd_tile": 9094.6e6, "grad_tile": 2231.5e6, "dC_gemm": 2206.0e6, "dE_gemm": 1925.5e6,
+        "rows": 121.4e6, "filter": 3.3e6, "transpose_e": 67.3e6,
     },
 }
 
