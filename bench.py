@@ -31,7 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 KERNELS = ["fwd_tile", "rows", "reduce", "bwd_prep", "filter", "grad_tile", "dC_gemm", "dE_gemm", "dE_reduce",
-           "fill_zero", "transpose_e", "db_reduce", "colsum", "colsum_reduce", "vec_sum", "fill_rank1"]
+           "fill_zero", "transpose_e", "db_reduce", "colsum", "colsum_reduce", "vec_sum", "fill_rank1", "tile_list"]
 MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # Measured memory traffic per launch (bytes past L2: rocprofv3 FETCH_SIZE x 2.0
 # + WRITE_SIZE x 1.0, the factors a 1 GiB device copy calibrates in the same

@@ -75,6 +75,8 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const size_t o_lse_c = take((size_t)L.Npad * 4);
   const size_t o_tgt_c = take((size_t)L.Npad * 4);
   const size_t o_keep = take((size_t)L.nb * L.nvb_t);
+  const size_t o_tlist = take((size_t)L.nb * L.nvb_t * 4);
+  const size_t o_tcount = take((size_t)L.nchunks * 4);
   const size_t o_g = take(L.g_bytes);
   const size_t o_gt = take(L.gt_bytes);
   const size_t o_et = take((size_t)D * (size_t)L.Npad * es);
@@ -92,6 +94,8 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     L.lse_c = (float*)(b + o_lse_c);
     L.tgt_c = (int*)(b + o_tgt_c);
     L.keep = (uint8_t*)(b + o_keep);
+    L.tlist = (int*)(b + o_tlist);
+    L.tcount = (int*)(b + o_tcount);
     L.G = b + o_g;
     L.Gt = b + o_gt;
     L.Et = b + o_et;
@@ -166,7 +170,7 @@ static void prof_release(ProfSlot& p) {
 
 static const char* const kKernelNames[kNumKernels] = {
     "fwd_tile", "rows", "reduce", "bwd_prep", "filter", "grad_tile", "dC_gemm", "dE_gemm", "dE_reduce",
-    "fill_zero", "transpose_e", "db_reduce", "colsum", "colsum_reduce", "vec_sum", "fill_rank1"};
+    "fill_zero", "transpose_e", "db_reduce", "colsum", "colsum_reduce", "vec_sum", "fill_rank1", "tile_list"};
 
 }  // namespace cce
 

@@ -36,8 +36,10 @@ constexpr int kHdrTilesKept = 2;
 constexpr int kHdrNValidBwd = 3;
 constexpr int kHdrWords = 64;  // 256 bytes
 
-// Default byte budget of the per-chunk gradient tile buffers G and G^T together.
-constexpr size_t kDefaultGBudget = size_t(512) << 20;
+// Default byte budget of the per-chunk gradient tile buffers G and G^T together
+// (2 GiB: one chunk for the whole vocabulary at N = 4096; fewer, longer
+// launches measured faster than 512 MiB chunks).
+constexpr size_t kDefaultGBudget = size_t(2048) << 20;
 // Extra elements per row of the transposed gradient tiles (row pitch
 // Npad + kGtPad).  Zero: measured no faster with a padded pitch.
 constexpr int kGtPad = 0;
@@ -86,6 +88,8 @@ struct Layout {
   float* aux;       // [0] sum of the bias, [1] sum_i scale_i
   float* colpart;   // [kColBlocks][D] column-sum partials
   uint8_t* keep;    // [nb][nvb_t]
+  int* tlist;       // per chunk, its kept gradient tiles in launch order (chunk ch at cvb0 * nb)
+  int* tcount;      // [nchunks] kept gradient tiles per chunk
   void* G;          // [Npad][Vc] operand type: gradient tiles of one vocab chunk
   void* Gt;         // [Vc][gt_ld] the same tiles transposed (columns past Npad unused)
   void* Et;         // [D][Npad] e transposed (zero rows past N)
@@ -103,7 +107,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
 // Kernel ids of the profiling hook (cce_profile_start / cce_profile_stop).
 enum KernelId {
   kKFwdTile = 0, kKRows, kKReduce, kKBwdPrep, kKFilter, kKGradTile, kKDC, kKDE, kKDEReduce, kKFill,
-  kKTransE, kKDbReduce, kKColSum, kKColReduce, kKVecSum, kKFillRank1, kNumKernels
+  kKTransE, kKDbReduce, kKColSum, kKColReduce, kKVecSum, kKFillRank1, kKTileList, kNumKernels
 };
 // Records start/stop events around one launch of kernel `id` when profiling of
 // that id is active (no-op otherwise).

@@ -660,6 +660,45 @@ __global__ __launch_bounds__(256) void filter_kernel(const int64_t* __restrict__
 }
 
 // ============================================================================
+// Per vocabulary chunk (one work-group each): the chunk's kept gradient tiles,
+// in the grouped order the gradient kernel would visit them, as a list and a
+// count.  The gradient kernel spreads the list evenly over the XCDs: with
+// filtering the kept tiles gather where the frequent targets are, and a
+// mapping over all tiles would hand most of them to one XCD.
+// ============================================================================
+__global__ __launch_bounds__(1024) void tile_list_kernel(const uint8_t* __restrict__ keep, int nvb_t, int tiles_n,
+                                                         int cvb, int* __restrict__ tlist,
+                                                         int* __restrict__ tcount) {
+  __shared__ int scnt[1024];
+  const int ch = blockIdx.x, tid = threadIdx.x;
+  const int cvb0 = ch * cvb;
+  const int cnvb = min(cvb, nvb_t - cvb0);
+  const int n = cnvb * tiles_n;
+  const int run = (n + 1023) / 1024;
+  const int i0 = min(n, tid * run), i1 = min(n, i0 + run);
+  auto kept = [&](int idx) {
+    int tvl, tn;
+    grouped_tile(idx, cnvb, tiles_n, kRasterGroup, tvl, tn);
+    return keep[(size_t)tn * nvb_t + cvb0 + tvl] != 0;
+  };
+  int cnt = 0;
+  for (int i = i0; i < i1; ++i) cnt += kept(i);
+  scnt[tid] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? scnt[tid - o] : 0;
+    __syncthreads();
+    scnt[tid] += v;
+    __syncthreads();
+  }
+  int* out = tlist + (size_t)cvb0 * tiles_n;
+  int pos = scnt[tid] - cnt;
+  for (int i = i0; i < i1; ++i)
+    if (kept(i)) out[pos++] = i;
+  if (tid == 1023) tcount[ch] = scnt[1023];
+}
+
+// ============================================================================
 // Backward: recompute kept logit tiles and write G = (p - onehot) * scale for
 // one vocabulary chunk [cv0, cv0 + Vc) into G [Npad][Vc] (token-major).
 // ============================================================================
@@ -667,17 +706,19 @@ template <class C>
 __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     const typename C::T* __restrict__ c, const typename C::T* __restrict__ e, const typename C::T* __restrict__ bias,
     const int* __restrict__ rowmap, const int* __restrict__ tgt_c, const float* __restrict__ lse_c,
-    const float* __restrict__ scale_c, float eps, float lam, float softcap, const uint8_t* __restrict__ keep, int N,
-    int D, int V, int nvb_t, int cvb0, int tiles_v, int tiles_n, int Vc, int gt_ld, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes,
+    const float* __restrict__ scale_c, float eps, float lam, float softcap, const int* __restrict__ tlist,
+    const int* __restrict__ tcount, int N, int D, int V, int cvb0, int tiles_v, int tiles_n, int Vc, int gt_ld, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes,
     size_t gt_bytes, float* __restrict__ db_part) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ __attribute__((aligned(16))) float sbias[C::BM];
-  const int total = tiles_v * tiles_n;
+  // the chunk's kept tiles (listed in grouped order), XCD-contiguous runs of
+  // the list: the same share of kept tiles on every XCD
+  const int cnt = *tcount;
+  if ((int)blockIdx.x >= cnt) return;
   int tvl, tn;
-  grouped_tile(xcd_remap(blockIdx.x, total), tiles_v, tiles_n, kRasterGroup, tvl, tn);
+  grouped_tile(tlist[xcd_remap(blockIdx.x, cnt)], tiles_v, tiles_n, kRasterGroup, tvl, tn);
   const int tv = cvb0 + tvl;
-  if (!keep[(size_t)tn * nvb_t + tv]) return;
   const int v0 = tv * C::BM, n0 = tn * C::BN;
   if (bias || softcap > 0.f) stage_bias<T, C::BM>(sbias, bias, v0, V);
 
@@ -940,9 +981,19 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
-  const int total = tiles_v * tiles_d;
-  int tvl, td;
-  grouped_tile(xcd_remap(blockIdx.x, total), tiles_v, tiles_d, kRasterGroup, tvl, td);
+  // Groups of kRasterGroup vocab tiles (each with all its d tiles) are dealt
+  // to the XCDs in turn, group g to XCD g % 8 (work-group i runs on XCD
+  // i % 8): the vocab tiles with many kept token blocks (frequent targets)
+  // sit next to each other, and this spreads them over the XCDs.  Inside a
+  // group the order is the grouped raster (L2 reuse).  The grid has
+  // 8 x kRasterGroup x tiles_d x ceil(groups / 8) work-groups; the spare exit.
+  constexpr int GR = kRasterGroup;
+  const int per = GR * tiles_d;
+  const int x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
+  const int g = x + 8 * (j / per), r = j % per;
+  const int gm = min(GR, tiles_v - g * GR);  // vocab tiles in group g
+  if (gm <= 0 || r >= gm * tiles_d) return;
+  const int tvl = g * GR + r % gm, td = r / gm;
   const int vl0 = tvl * C::BM, d0 = td * C::BN;
   const int nb = Npad / kTileN;
   const int nk = collect_blocks(keep, (size_t)(cvb0 + tvl), nvb_t, nb, blocks);
@@ -1266,6 +1317,10 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
                      L.part, (const int*)L.rowmap, P.N, P.V, L.nVB, P.ignore_index, kTileN, kTileV, kPartialWidth, L.nvb_t, P.filter,
                      L.keep, L.hdr);
   prof_after(kKFilter, st);
+  prof_before(kKTileList, st);
+  hipLaunchKernelGGL(tile_list_kernel, dim3(L.nchunks), dim3(1024), 0, st, (const uint8_t*)L.keep, L.nvb_t,
+                     L.Npad / kTileN, L.Vc / kTileV, L.tlist, L.tcount);
+  prof_after(kKTileList, st);
   prof_before(kKTransE, st);
   hipLaunchKernelGGL(transpose_e_kernel<T>, dim3((P.D + 63) / 64, L.Npad / 64), dim3(256), 0, st, e,
                      (const int*)L.rowmap, (T*)L.Et, P.N, P.D, L.Npad);
@@ -1293,12 +1348,15 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     prof_before(kKGradTile, st);
     hipLaunchKernelGGL(grad_tile_kernel<C>, dim3(cnvb * tiles_n), dim3(C::NT), 0, st, c, e, (const T*)P.bias,
                        (const int*)L.rowmap, (const int*)L.tgt_c, (const float*)L.lse_c, (const float*)L.scale_c,
-                       P.label_smoothing, P.z_loss, P.softcap, L.keep, P.N, P.D, P.V, L.nvb_t,
-                       cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
+                       P.label_smoothing, P.z_loss, P.softcap, (const int*)L.tlist + (size_t)cvb0 * tiles_n,
+                       (const int*)L.tcount + ch, P.N, P.D, P.V, cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
                        G, (T*)L.Gt, L.g_bytes, L.gt_bytes, P.dbias ? L.db_part : nullptr);
     prof_after(kKGradTile, st);
     prof_before(kKDC, st);
-    hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(cnvb * tiles_d), dim3(C::NT), 0, st, (const T*)L.Gt,
+    // vocab-tile groups dealt to the XCDs in turn: a whole number of rounds of 8
+    const int dc_groups = (cnvb + kRasterGroup - 1) / kRasterGroup;
+    const int dc_grid = 8 * kRasterGroup * tiles_d * ((dc_groups + 7) / 8);
+    hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(dc_grid), dim3(C::NT), 0, st, (const T*)L.Gt,
                        (const T*)L.Et, L.keep, L.Npad, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_d,
                        L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC);
     prof_after(kKDC, st);

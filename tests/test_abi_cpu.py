@@ -39,9 +39,9 @@ def test_status_strings_and_tiles(L):
     import linear_cross_entropy_forward_amd as M
     bn, bv, pw = M.tile_shape()
     assert bn == 256 and bv == 256 and pw == 128 and bv % pw == 0
-    for k in range(16):
+    for k in range(17):
         assert L.cce_kernel_name(k) != b"unknown"
-    assert L.cce_kernel_name(16) == b"unknown"
+    assert L.cce_kernel_name(17) == b"unknown"
 
 
 def test_workspace_size(L):
@@ -61,8 +61,10 @@ def test_vocab_chunk(L):
     assert vc(0, 100, 0, 0) == 0 and vc(4, 100, 7, 0) == 0 and vc(4, 100, 0, 100) == 0
     d = vc(4096, 128256, 0, 0)
     assert d % 256 == 0 and 256 <= d <= 128256 + 255
-    # the default keeps both orientations of a chunk's bf16 tiles within 512 MiB
-    assert 2 * 4096 * d * 2 <= 512 << 20
+    # the default keeps both orientations of a chunk's bf16 tiles within 2 GiB:
+    # the whole vocabulary at N = 4096, a quarter of it at N = 16384
+    assert d >= 128256 and vc(16384, 128256, 0, 0) == 32768
+    assert 2 * 16384 * vc(16384, 128256, 0, 0) * 2 <= 2048 << 20
     assert vc(4096, 128256, 0, 1024) == 1024
     assert vc(64, 1000, 1, 0) == 1024          # clamped to the vocabulary, in whole tiles
     assert vc(64, 1000, 1, 4096) == 1024
@@ -135,10 +137,10 @@ def test_stats_and_profile_argument_errors(L):
     assert L.cce_read_stats(None, 1024, 1, 1, None, ctypes.byref(st)) == INVALID
     assert L.cce_read_stats(FAKE, 8, 1, 1, None, ctypes.byref(st)) == INVALID
     assert L.cce_profile_start(-1, 4) == INVALID
-    assert L.cce_profile_start(16, 4) == INVALID
+    assert L.cce_profile_start(17, 4) == INVALID
     assert L.cce_profile_start(0, 0) == INVALID
     ms, n = ctypes.c_double(), ctypes.c_int()
-    assert L.cce_profile_stop(16, ctypes.byref(ms), ctypes.byref(n)) == INVALID
+    assert L.cce_profile_stop(17, ctypes.byref(ms), ctypes.byref(n)) == INVALID
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
