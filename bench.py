@@ -38,10 +38,10 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "68e9d3b5895e7ff10436e4155c515271f4c06a10855610fcadef9565f45dc45d",
+    "source_sha256": "501c1975936936155fe9790e98daa2ced3d7cc6c4999b0bb101c6de9e452866c",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9094.6e6, "grad_tile": 2231.5e6, "dC_gemm": 2206.0e6, "dE_gemm": 1925.5e6,
+        "fwd_tile": 9137.5e6, "grad_tile": 9960.0e6, "dC_gemm": 8421.6e6, "dE_gemm": 6789.2e6,
         "rows": 121.4e6, "filter": 3.3e6, "transpose_e": 67.3e6,
     },
 }
