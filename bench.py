@@ -284,7 +284,7 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import torch
     import workloads as W
