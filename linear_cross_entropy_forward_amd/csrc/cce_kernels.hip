@@ -247,8 +247,9 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
   const int lane = threadIdx.x & 63;
   const int wm = (threadIdx.x >> 6) / C::WAVES_N;
   const int vblk = (v0 + wm * C::WM) / C::WM;
-  // logits of this lane's 64 rows of column fn (plus the rows' bias)
-  auto emit = [&](auto has_bias) __attribute__((always_inline)) {
+  // logits of this lane's 64 rows of column fn (plus the rows' bias); rows
+  // past V are left out only in the last vocab tile (ragged)
+  auto emit = [&](auto has_bias, auto ragged) __attribute__((always_inline)) {
     f32x4 bz[C::FM][4];
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
@@ -258,12 +259,13 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
     for (int fn = 0; fn < C::FN; ++fn) {
       const int n = n0 + am.colj(fn);
       auto z = [&](int fm, int r) { return acc[fm][fn][r] + bz[fm][r >> 2][r & 3]; };
+      auto in = [&](int fm, int r) { return !decltype(ragged)::value || v0 + am.row(fm, r) < V; };
       float mx = -INFINITY;
 #pragma unroll
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (v0 + am.row(fm, r) < V) mx = fmaxf(mx, z(fm, r));
+          if (in(fm, r)) mx = fmaxf(mx, z(fm, r));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mxl = mx * kLog2e;
       float s = 0.f;
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
       for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (v0 + am.row(fm, r) < V) s += fast_exp2(__builtin_fmaf(z(fm, r), kLog2e, -mxl));
+          if (in(fm, r)) s += fast_exp2(__builtin_fmaf(z(fm, r), kLog2e, -mxl));
       s += __shfl_xor(s, 32, 64);
       if (lane < 32 && n < N && vblk < nVB) part[(size_t)n * nVB + vblk] = make_float2(mx, s);
     }
@@ -291,11 +293,14 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
           for (int u = 0; u < 4; ++u)
             acc[fm][fn][4 * q + u] = softcap_f(acc[fm][fn][4 * q + u] + bz[u], softcap, kc);
       }
-    emit(std::false_type{});
+    if (v0 + C::BM <= V) emit(std::false_type{}, std::false_type{});
+    else emit(std::false_type{}, std::true_type{});
   } else if (bias) {
-    emit(std::true_type{});
+    if (v0 + C::BM <= V) emit(std::true_type{}, std::false_type{});
+    else emit(std::true_type{}, std::true_type{});
   } else {
-    emit(std::false_type{});
+    if (v0 + C::BM <= V) emit(std::false_type{}, std::false_type{});
+    else emit(std::false_type{}, std::true_type{});
   }
 }
 
