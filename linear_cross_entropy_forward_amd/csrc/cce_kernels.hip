@@ -853,7 +853,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
         const int rr = wave * 64 + it * 2 + (lane >> 5), jc = lane & 31;
         const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(rr, jc * 8, pass2));
         __builtin_amdgcn_raw_buffer_store_b128(val, r, ((row0 + (uint32_t)rr) * pitch + col0 + (uint32_t)jc * 8u) * 2u,
-                                               0, 0);
+                                               0, kStoreNT);
         if (sums) {
           float t8 = 0.f;
 #pragma unroll
@@ -1037,7 +1037,7 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
       for (int r = 0; r < 16; ++r) {
         const int vr = am.row(fm, r);
         const bool ok = d < D && vl0 + vr < clen;
-        stf(ro, ok ? ((uint32_t)vr * (uint32_t)D + (uint32_t)d) * 4u : kOOB, acc[fm][fn][r] + add[fn]);
+        stf_nt(ro, ok ? ((uint32_t)vr * (uint32_t)D + (uint32_t)d) * 4u : kOOB, acc[fm][fn][r] + add[fn]);
       }
     }
 }
