@@ -38,11 +38,11 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "501c1975936936155fe9790e98daa2ced3d7cc6c4999b0bb101c6de9e452866c",
+    "source_sha256": "3fc7e37a35e642172d0b888eb96985053fbca9b8600d1f0559bcd5d76342a4a0",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9137.5e6, "grad_tile": 9960.0e6, "dC_gemm": 8421.6e6, "dE_gemm": 6789.2e6,
-        "rows": 121.4e6, "filter": 3.3e6, "transpose_e": 67.3e6,
+        "fwd_tile": 9188.0e6, "grad_tile": 11438.3e6, "dC_gemm": 8415.5e6, "dE_gemm": 6529.6e6,
+        "rows": 121.3e6, "filter": 3.3e6, "transpose_e": 67.3e6,
     },
 }
 
