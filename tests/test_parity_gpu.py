@@ -550,3 +550,38 @@ def test_full_llama8b_padded(M):
     """The 8B head with a quarter of the rows padding: the compacted backward."""
     r = _sampled_full(M, "llama8b_pad25", "mean", True)
     assert r["stats"]["tiles_kept"] <= 12 * 502
+
+
+# ----------------------------------------------------------------------------- seeded random configurations
+def _random_case(k):
+    """Case k of a fixed list: shapes, dtype, reduction, filter, accumulation,
+    chunking and loss terms drawn from a seeded generator (combinations the
+    library accepts: no softcap with fp32 operands or with label smoothing)."""
+    g = np.random.default_rng(1000 + k)
+    dt = "f32" if g.random() < 0.2 else "bf16"
+    N = int(g.integers(1, 700))
+    D = int(g.integers(1, 40)) * (4 if dt == "f32" else 8)
+    V = int(g.integers(1, 2100))
+    case = dict(dt=dt, N=N, D=D, V=V,
+                reduction=str(g.choice(["mean", "sum", "none"])),
+                filter=bool(g.random() < 0.5),
+                accum=str(g.choice(["deterministic", "atomic"])),
+                vocab_chunk=int(g.choice([0, 256, 512])),
+                ignore_frac=float(g.choice([0.0, 0.1, 0.5])),
+                c_std=float(g.choice([0.05, 0.2, 0.5])),
+                bias=bool(g.random() < 0.4),
+                ls=float(g.choice([0.0, 0.0, 0.1])),
+                zl=float(g.choice([0.0, 1e-3])))
+    case["cap"] = float(g.choice([0.0, 5.0])) if dt == "bf16" and case["ls"] == 0.0 else 0.0
+    return case
+
+
+@pytest.mark.parametrize("k", range(16))
+def test_random_configuration(M, k):
+    cs = _random_case(k)
+    print(f"[random {k}] {cs}", flush=True)
+    inp = W.custom(cs["N"], cs["D"], cs["V"], cs["dt"], seed=2000 + k, c_std=cs["c_std"],
+                   ignore_frac=cs["ignore_frac"])
+    bias = W.bias(cs["V"], cs["dt"], seed=2000 + k) if cs["bias"] else None
+    full_check(M, inp, cs["reduction"], cs["filter"], accum=cs["accum"], vocab_chunk=cs["vocab_chunk"],
+               label=f"random {k}", bias=bias, want_db=cs["bias"], ls=cs["ls"], zl=cs["zl"], cap=cs["cap"])
