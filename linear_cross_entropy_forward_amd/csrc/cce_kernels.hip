@@ -1095,11 +1095,13 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   // the barrier that ends collect_blocks)
   __shared__ int srow[C::BM];
   for (int i = threadIdx.x; i < C::BM; i += C::NT) srow[i] = rowmap[n0 + i];
-  // this split's vocab blocks of the chunk
-  const int vb_lo = (int)((int64_t)cnvb * s / splits), vb_hi = (int)((int64_t)cnvb * (s + 1) / splits);
-  const int nk = collect_blocks(keep, (size_t)tn * nvb_t + cvb0 + vb_lo, 1, vb_hi - vb_lo, blocks);
-  for (int j = threadIdx.x; j < nk; j += blockDim.x) blocks[j] += vb_lo;
-  __syncthreads();
+  // this split's share of the token block's kept vocab blocks in the chunk:
+  // the kept list cut into equal counts (with filtering, kept blocks gather
+  // at the frequent targets, so equal vocab ranges would load one split)
+  const int nall = collect_blocks(keep, (size_t)tn * nvb_t + cvb0, 1, cnvb, blocks);
+  const int lo = (int)((int64_t)nall * s / splits), hi = (int)((int64_t)nall * (s + 1) / splits);
+  const int nk = hi - lo;
+  const uint16_t* bl = blocks + lo;
 
   Operand A = make_operand(G + (size_t)n0 * Vc, g_bytes - (size_t)n0 * Vc * sizeof(T), (uint32_t)Vc,
                min(C::BM, N - n0), clen);
@@ -1115,9 +1117,10 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     if constexpr (kDma) mainloop_dma<C, SPB, true>(acc, a, b, nk * SPB, bl, smem);
     else mainloop<C, false, true, SPB>(acc, a, b, nk * SPB, bl, (T*)smem);
   };
-  // every vocab block of the split kept: contiguous K from the split's start
-  if (nk == vb_hi - vb_lo) {
-    const size_t ka = (size_t)vb_lo * kTileV;
+  // the split's blocks consecutive (every block kept): contiguous K from its
+  // first block
+  if (nk > 0 && (int)bl[nk - 1] - (int)bl[0] == nk - 1) {
+    const size_t ka = (size_t)bl[0] * kTileV;
     const Operand A1 = make_operand(G + (size_t)n0 * Vc + ka, g_bytes - ((size_t)n0 * Vc + ka) * sizeof(T),
                                     (uint32_t)Vc, min(C::BM, N - n0), clen - (int)ka);
     const Operand B1 = make_operand(c + ((size_t)cv0 + ka) * D + d0,
@@ -1125,7 +1128,7 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
                                     min(C::BN, D - d0), clen - (int)ka);
     loop(A1, B1, nullptr);
   } else {
-    loop(A, B, blocks);
+    loop(A, B, bl);
   }
 
   if (nk == 0 && (accumulate || atomic)) return;  // nothing to add
