@@ -241,7 +241,7 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
         fwd()
         r = L.cce_backward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, softcap,
                            label_smoothing, z_loss, lse.data_ptr(), g.data_ptr(), 1 if filter else 0,
-                           0 if accum == "deterministic" else 1, 0, dE.data_ptr(),
+                           0 if accum == "deterministic" else 1, 0, 0, dE.data_ptr(),
                            dC.data_ptr(), dbp, ws.data_ptr(), ws.numel(), st.cuda_stream)
         if r:
             raise RuntimeError(f"cce_backward failed: {r}")
@@ -338,7 +338,8 @@ def main():
         r1 = L.cce_forward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0, 0.0,
                            loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(), ws.numel(), s)
         r2 = L.cce_backward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0,
-                            0.0, lse.data_ptr(), g.data_ptr(), flt, acc, args.vocab_chunk, dE.data_ptr(), dC.data_ptr(),
+                            0.0, lse.data_ptr(), g.data_ptr(), flt, acc, args.vocab_chunk, 0, dE.data_ptr(),
+                            dC.data_ptr(),
                             None, ws.data_ptr(), ws.numel(), s)
         if r1 or r2:
             raise RuntimeError(f"cce call failed: {r1} {r2}")

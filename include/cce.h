@@ -83,6 +83,9 @@ typedef enum {
 typedef enum { CCE_DTYPE_BF16 = 0, CCE_DTYPE_F32 = 1 } cce_dtype;
 typedef enum { CCE_REDUCTION_NONE = 0, CCE_REDUCTION_SUM = 1, CCE_REDUCTION_MEAN = 2 } cce_reduction;
 typedef enum { CCE_ACCUM_DETERMINISTIC = 0, CCE_ACCUM_ATOMIC = 1 } cce_accum;
+/* Element type of dE and dC: float32, or the operands' dtype (bf16 for bf16
+ * operands; rounded to nearest even from the fp32 accumulation). */
+typedef enum { CCE_GRAD_FLOAT32 = 0, CCE_GRAD_OPERAND = 1 } cce_grad_dtype;
 
 typedef struct {
   int64_t n_valid;      /* rows whose target != ignore_index (last forward)        */
@@ -101,7 +104,9 @@ typedef struct {
  * 2 GiB for the two by default: the whole vocabulary for N up to about 4096
  * with bf16), plus e transposed (N*D elements); a positive value (a multiple
  * of 256) sets the chunk width, trading workspace for launches (a 512 MiB
- * chunk measured about 2% slower at N = 4096, D = 4096, V = 128256).  The forward uses only the first part (per-row partials,
+ * chunk measured about 2% slower at N = 4096, D = 4096, V = 128256).  It also
+ * holds an fp32 [N, D] accumulation of dE for bf16 gradients that more than
+ * one pass adds up.  The forward uses only the first part (per-row partials,
  * O(N + N*V/128 + 512*D) floats).  Returns 0 for invalid arguments.
  */
 size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk);
@@ -145,8 +150,11 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
  * whose softmax is below 2^-12 everywhere (and that hold no target); 0
  * computes every tile.  accum = CCE_ACCUM_DETERMINISTIC gives run-to-run
  * bitwise-identical results (fixed-order split reduction);
- * CCE_ACCUM_ATOMIC accumulates dE with fp32 atomics.  dE (device) float
- * [N, D] and dC (device) float [V, D] are overwritten.  dbias (device) float
+ * CCE_ACCUM_ATOMIC accumulates dE with fp32 atomics.  grad_dtype
+ * (cce_grad_dtype) picks the element type of dE (device) [N, D] and dC
+ * (device) [V, D], both overwritten: float32, or the operand dtype (bf16
+ * gradients written by the kernels themselves, every accumulation still
+ * fp32, so a caller training in bf16 needs no conversion pass).  dbias (device) float
  * [V] or NULL: when given, overwritten with the bias gradient db_j =
  * sum_i G_ij (column sums of the filtered gradient tiles, in a fixed order
  * in both accum modes); it is defined with or without a bias.  vocab_chunk as
@@ -155,7 +163,7 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
 cce_status cce_backward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
                         int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
                         float label_smoothing, float z_loss, const float* lse, const float* grad_loss, int filter,
-                        int accum, int64_t vocab_chunk, float* dE, float* dC, float* dbias, void* ws,
+                        int accum, int64_t vocab_chunk, int grad_dtype, void* dE, void* dC, float* dbias, void* ws,
                         size_t ws_bytes, cce_stream_t stream);
 
 /*

@@ -28,6 +28,7 @@ library_path = os.path.join(_HERE, "libcce.so")
 CCE_OK = 0
 _REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
 _ACCUM = {"deterministic": 0, "atomic": 1}
+_GRAD_DTYPE = {"float32": 0, "operand": 1}
 
 
 class CCEError(RuntimeError):
@@ -62,7 +63,7 @@ def lib() -> ctypes.CDLL:
                               vp]
     L.cce_backward.restype = i32
     L.cce_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, f32, f32, vp, vp, i32, i32, i64,
-                               vp, vp, vp, vp, sz, vp]
+                               i32, vp, vp, vp, vp, sz, vp]
     L.cce_read_stats.restype = i32
     L.cce_read_stats.argtypes = [vp, sz, i64, i64, vp, ctypes.POINTER(_Stats)]
     L.cce_status_string.restype = ctypes.c_char_p
@@ -179,26 +180,32 @@ def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch
              grad_loss: torch.Tensor, ws: torch.Tensor, ignore_index: int = -100, reduction: str = "mean",
              filter: bool = True, accum: str = "deterministic", softcap: float = 0.0, vocab_chunk: int = 0,
              dE: torch.Tensor | None = None, dC: torch.Tensor | None = None, bias: torch.Tensor | None = None,
-             want_dbias: bool = False, label_smoothing: float = 0.0, z_loss: float = 0.0):
+             want_dbias: bool = False, label_smoothing: float = 0.0, z_loss: float = 0.0,
+             grad_dtype: str = "float32"):
     """cce_backward.  grad_loss is float32 [N] ('none') or [1]/0-dim.  Returns
-    float32 (dE [N, D], dC [V, D]), plus db [V] when want_dbias.  bias,
-    label_smoothing, z_loss and softcap must be those of the forward that
-    filled ws."""
+    (dE [N, D], dC [V, D]), plus float32 db [V] when want_dbias; dE and dC are
+    float32, or with grad_dtype='operand' in e's dtype (written by the kernels,
+    accumulated in fp32).  bias, label_smoothing, z_loss and softcap must be
+    those of the forward that filled ws."""
     _validate(e, c, targets)
     _validate_bias(bias, c)
     N, D = e.shape
     V = c.shape[0]
     dev = e.device
     g = grad_loss.reshape(-1).to(torch.float32).contiguous()
+    gdt = torch.float32 if grad_dtype == "float32" else e.dtype
     if dE is None:
-        dE = torch.empty((N, D), dtype=torch.float32, device=dev)
+        dE = torch.empty((N, D), dtype=gdt, device=dev)
     if dC is None:
-        dC = torch.empty((V, D), dtype=torch.float32, device=dev)
+        dC = torch.empty((V, D), dtype=gdt, device=dev)
+    if dE.dtype != gdt or dC.dtype != gdt or not (dE.is_contiguous() and dC.is_contiguous()):
+        raise CCEError(f"dE and dC must be contiguous {gdt} tensors")
     db = torch.empty(V, dtype=torch.float32, device=dev) if want_dbias else None
     _check(lib().cce_backward(_ptr(e), _ptr(c), _ptr(bias) if bias is not None else None, _ptr(targets), N, D, V,
                               _dtype_code(e), ignore_index, _REDUCTIONS[reduction], softcap, label_smoothing,
                               z_loss, _ptr(lse), _ptr(g),
-                              int(bool(filter)), _ACCUM[accum], vocab_chunk, _ptr(dE), _ptr(dC),
+                              int(bool(filter)), _ACCUM[accum], vocab_chunk, _GRAD_DTYPE[grad_dtype], _ptr(dE),
+                              _ptr(dC),
                               _ptr(db) if db is not None else None, _ptr(ws), ws.numel(), _stream()),
            "cce_backward")
     return (dE, dC, db) if want_dbias else (dE, dC)
@@ -226,13 +233,13 @@ class _CCEFunction(torch.autograd.Function):
         e, c, bias, targets, lse, ws = ctx.saved_tensors
         reduction, ignore_index, filter, accum, label_smoothing, z_loss, softcap = ctx.cfg
         want_db = bias is not None and ctx.needs_input_grad[2]
+        # gradients in the inputs' dtype, written so by the kernels
         out = backward(e, c, targets, lse, grad, ws, ignore_index=ignore_index, reduction=reduction,
                        filter=filter, accum=accum, bias=bias, want_dbias=want_db,
-                       label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap)
+                       label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap, grad_dtype="operand")
         dE, dC = out[0], out[1]
         db = out[2].to(bias.dtype) if want_db else None
-        # autograd wants gradients in the inputs' dtype
-        return dE.to(e.dtype), dC.to(c.dtype), db, None, None, None, None, None, None, None, None
+        return dE, dC, db, None, None, None, None, None, None, None, None
 
 
 def cce_loss(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, reduction: str = "mean",

@@ -82,6 +82,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const size_t o_et = take((size_t)D * (size_t)L.Npad * es);
   const size_t o_dep = take((size_t)(L.splits - 1) * (size_t)N * (size_t)D * 4);
   const size_t o_dbp = take((size_t)L.nb * (size_t)V * 4);
+  const size_t o_dacc = take((size_t)N * (size_t)D * 4);
   L.total = off;
   if (base) {
     char* b = (char*)base;
@@ -100,6 +101,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     L.Gt = b + o_gt;
     L.Et = b + o_et;
     L.dE_part = (float*)(b + o_dep);
+    L.dE_acc = (float*)(b + o_dacc);
     L.db_part = (float*)(b + o_dbp);
     L.csum = (float*)(b + o_csum);
     L.r1c = (float*)(b + o_r1c);
@@ -238,7 +240,7 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
 cce_status cce_backward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
                         int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
                         float label_smoothing, float z_loss, const float* lse, const float* grad_loss, int filter,
-                        int accum, int64_t vocab_chunk, float* dE, float* dC, float* dbias, void* ws,
+                        int accum, int64_t vocab_chunk, int grad_dtype, void* dE, void* dC, float* dbias, void* ws,
                         size_t ws_bytes, cce_stream_t stream) {
   cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, ws, vocab_chunk);
   if (st != CCE_OK) return st;
@@ -248,6 +250,7 @@ cce_status cce_backward(const void* e, const void* c, const void* bias, const in
   if (!lse || !grad_loss || !dE || !dC) return CCE_ERR_INVALID_ARG;
   if ((filter != 0 && filter != 1) || (accum != kAccumDeterministic && accum != kAccumAtomic))
     return CCE_ERR_INVALID_ARG;
+  if (grad_dtype != CCE_GRAD_FLOAT32 && grad_dtype != CCE_GRAD_OPERAND) return CCE_ERR_INVALID_ARG;
   if (!aligned16(dE) || !aligned16(dC)) return CCE_ERR_INVALID_ARG;
   Layout L = make_layout(N, D, V, dtype, vocab_chunk, ws);
   if (ws_bytes < L.total) return CCE_ERR_WORKSPACE;
@@ -272,6 +275,7 @@ cce_status cce_backward(const void* e, const void* c, const void* bias, const in
   P.dE = dE;
   P.dC = dC;
   P.dbias = dbias;
+  P.grad_bf16 = grad_dtype == CCE_GRAD_OPERAND && dtype == kDtypeBf16 ? 1 : 0;
   hipError_t err = launch_backward(P, L, (hipStream_t)stream);
   return err == hipSuccess ? CCE_OK : CCE_ERR_HIP;
 }

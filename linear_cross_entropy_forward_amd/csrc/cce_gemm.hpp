@@ -67,6 +67,10 @@ constexpr int kStoreNT = 2;
 __device__ __forceinline__ void stf_nt(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kStoreNT);
 }
+// One value rounded to bf16 (to nearest even), non-temporal 16-bit store.
+__device__ __forceinline__ void stbf_nt(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), r, off, 0, kStoreNT);
+}
 __device__ __forceinline__ void st64(rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }

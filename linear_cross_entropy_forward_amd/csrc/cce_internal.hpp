@@ -67,9 +67,10 @@ struct Problem {
   const float* grad_loss;
   int filter;
   int accum;
-  float* dE;
-  float* dC;
+  void* dE;          // [N][D], float or (grad_bf16) bf16
+  void* dC;          // [V][D], float or (grad_bf16) bf16
   float* dbias;      // [V] or null
+  int grad_bf16;     // dE and dC in bf16 (bf16 operands, grad_dtype = operand dtype)
 };
 
 struct Layout {
@@ -97,6 +98,7 @@ struct Layout {
   size_t gt_bytes;  // bytes of Gt
   int gt_ld;        // row pitch of Gt in elements: Npad + kGtPad
   float* dE_part;   // [splits-1][N][D]
+  float* dE_acc;    // [N][D] fp32 accumulation of dE when dE itself is bf16 and more than one pass adds to it
   int nVB, Npad, nb, nvb_t, Vc, nchunks, splits, splits_atomic;
 };
 

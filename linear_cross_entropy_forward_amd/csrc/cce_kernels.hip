@@ -982,7 +982,8 @@ template <class C>
 __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
     const typename C::T* __restrict__ Gt, const typename C::T* __restrict__ Et,
     const uint8_t* __restrict__ keep, int Npad, int gt_ld, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
-    int tiles_v, int tiles_d, size_t gt_bytes, const float* __restrict__ r1c, float* __restrict__ dC) {
+    int tiles_v, int tiles_d, size_t gt_bytes, const float* __restrict__ r1c, void* __restrict__ dC,
+    int out_bf16) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
@@ -1020,7 +1021,9 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
 
   AccMap<C> am;
   const int vg0 = cv0 + vl0;
-  rsrc_t ro = make_rsrc(dC + (size_t)vg0 * D, (uint64_t)(V - vg0) * D * sizeof(float));
+  // dC rows of the tile, float or bf16 (out_bf16)
+  const size_t es = out_bf16 ? 2 : 4;
+  rsrc_t ro = make_rsrc((char*)dC + (size_t)vg0 * D * es, (uint64_t)(V - vg0) * D * es);
   // the smoothing term, the same for every vocabulary row (r1c: null without)
   float add[C::FN];
 #pragma unroll
@@ -1037,7 +1040,9 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
       for (int r = 0; r < 16; ++r) {
         const int vr = am.row(fm, r);
         const bool ok = d < D && vl0 + vr < clen;
-        stf_nt(ro, ok ? ((uint32_t)vr * (uint32_t)D + (uint32_t)d) * 4u : kOOB, acc[fm][fn][r] + add[fn]);
+        const uint32_t e = (uint32_t)vr * (uint32_t)D + (uint32_t)d;
+        if (out_bf16) stbf_nt(ro, ok ? e * 2u : kOOB, acc[fm][fn][r] + add[fn]);
+        else stf_nt(ro, ok ? e * 4u : kOOB, acc[fm][fn][r] + add[fn]);
       }
     }
 }
@@ -1052,13 +1057,17 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     const typename C::T* __restrict__ G, const typename C::T* __restrict__ c,
     const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
     int cnvb, int tiles_n, int tiles_d, int splits, const int32_t* __restrict__ hdr, int Vc, size_t g_bytes,
-    float* __restrict__ dE,
+    void* __restrict__ dE_out, int out_bf16,
     float* __restrict__ dE_part, int accumulate, int atomic, const int* __restrict__ rowmap,
     const float* __restrict__ scale_c, const float* __restrict__ csum, float r1) {
   using T = typename C::T;
   // bf16: LDS-DMA main loop (C fragments through transposing reads); fp32:
   // register-staged main loop (no 32-bit transposing read exists)
   constexpr bool kDma = sizeof(T) == 2;
+  // dE as float, or (out_bf16: one pass writes it, no split or chunk adds to
+  // it) as bf16
+  float* dE = out_bf16 ? nullptr : (float*)dE_out;
+  uint16_t* dEb = out_bf16 ? (uint16_t*)dE_out : nullptr;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kDma ? C::LDS_DMA_BYTES : C::LDS_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
   // The grid holds tiles_n x tiles_d x splits work-groups.  The first
@@ -1085,7 +1094,10 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
       float* o = ps == 0 ? dE : dE_part + (size_t)(ps - 1) * N * D;
       for (int r = 0; r < C::BM; ++r) {
         const int row = rowmap[tn * C::BM + r];
-        if (row >= 0 && d < D) o[(size_t)row * D + d] = 0.f;
+        if (row >= 0 && d < D) {
+          if (o) o[(size_t)row * D + d] = 0.f;
+          else dEb[(size_t)row * D + d] = 0;
+        }
       }
     }
     return;
@@ -1174,18 +1186,20 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     for (int fm = 0; fm < C::FM; ++fm) {
       float* rp[16];
       bool rok[16];
+      size_t rbase[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = srow[am.row(fm, r)];
         rok[r] = F || row >= 0;
-        rp[r] = out + (size_t)(F || row >= 0 ? row : 0) * D;
+        rbase[r] = (size_t)(F || row >= 0 ? row : 0) * D;
+        rp[r] = out + rbase[r];
       }
       float old[C::FN][16];
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn) {
         const int dc = F || dcol[fn] >= 0 ? dcol[fn] : 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) old[fn][r] = accumulate ? rp[r][dc] : 0.f;
+        for (int r = 0; r < 16; ++r) old[fn][r] = (accumulate && !out_bf16) ? rp[r][dc] : 0.f;
       }
       if (rank1) {
 #pragma unroll
@@ -1200,7 +1214,14 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float v = acc[fm][fn][r] + old[fn][r];
-          if constexpr (F) {
+          if (out_bf16) {
+            const uint16_t b = __builtin_bit_cast(uint16_t, (__bf16)v);
+            if constexpr (F) {
+              dEb[rbase[r] + dcol[fn]] = b;
+            } else {
+              if (rok[r] && dcol[fn] >= 0) dEb[rbase[r] + dcol[fn]] = b;
+            }
+          } else if constexpr (F) {
             rp[r][dcol[fn]] = v;
           } else {
             if (rok[r] && dcol[fn] >= 0) rp[r][dcol[fn]] = v;
@@ -1220,6 +1241,19 @@ __global__ __launch_bounds__(256) void dE_reduce_kernel(float* __restrict__ dE, 
   f32x4 v = reinterpret_cast<f32x4*>(dE)[i];
   for (int p = 0; p < nparts; ++p) v += reinterpret_cast<const f32x4*>(part)[(size_t)p * stride4 + i];
   reinterpret_cast<f32x4*>(dE)[i] = v;
+}
+
+// bf16 dE from its fp32 accumulation: dE = bf16(acc + part[0] + part[1] + ...)
+// in that order (deterministic), four elements per thread.
+__global__ __launch_bounds__(256) void dE_finish_kernel(const float* __restrict__ acc,
+                                                        const float* __restrict__ part, size_t n4, int nparts,
+                                                        size_t stride4, uint16_t* __restrict__ out) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 v = reinterpret_cast<const f32x4*>(acc)[i];
+  for (int p = 0; p < nparts; ++p) v += reinterpret_cast<const f32x4*>(part)[(size_t)p * stride4 + i];
+  const uint32_t lo = pack_bf16(v[0], v[1]), hi = pack_bf16(v[2], v[3]);
+  reinterpret_cast<u32x2*>(out)[i] = u32x2{lo, hi};
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, size_t n) {
@@ -1333,16 +1367,22 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   hipLaunchKernelGGL(transpose_e_kernel<T>, dim3((P.D + 63) / 64, L.Npad / 64), dim3(256), 0, st, e,
                      (const int*)L.rowmap, (T*)L.Et, P.N, P.D, L.Npad);
   prof_after(kKTransE, st);
+  // dE: float output, or bf16 written straight by dE_gemm when a single pass
+  // forms it (one vocab chunk, one split, no atomics), else accumulated in
+  // fp32 (dE_acc) and rounded to bf16 at the end
+  const int splits_used = P.accum == kAccumAtomic ? L.splits_atomic : L.splits;
+  const bool bf_direct = P.grad_bf16 && L.nchunks == 1 && splits_used == 1 && P.accum != kAccumAtomic;
+  float* dE32 = P.grad_bf16 ? (bf_direct ? nullptr : L.dE_acc) : (float*)P.dE;
   if (P.accum == kAccumAtomic) {
     const size_t n = (size_t)P.N * P.D;
     if (smooth) {
       prof_before(kKFillRank1, st);
-      hipLaunchKernelGGL(fill_rank1_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P.dE, L.scale,
+      hipLaunchKernelGGL(fill_rank1_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dE32, L.scale,
                          (const float*)L.csum, r1, P.N, P.D);
       prof_after(kKFillRank1, st);
     } else {
       prof_before(kKFill, st);
-      hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P.dE, n);
+      hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dE32, n);
       prof_after(kKFill, st);
     }
   }
@@ -1366,14 +1406,15 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     const int dc_grid = 8 * kRasterGroup * tiles_d * ((dc_groups + 7) / 8);
     hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(dc_grid), dim3(C::NT), 0, st, (const T*)L.Gt,
                        (const T*)L.Et, L.keep, L.Npad, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_d,
-                       L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC);
+                       L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC, P.grad_bf16);
     prof_after(kKDC, st);
-    const int splits = P.accum == kAccumAtomic ? L.splits_atomic : L.splits;
+    const int splits = splits_used;
     prof_before(kKDE, st);
     hipLaunchKernelGGL(dE_gemm_kernel<C>, dim3(tiles_n * tiles_d * splits), dim3(C::NT), 0, st, G, c, L.keep,
                        P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits,
                        (const int32_t*)L.hdr, L.Vc, L.g_bytes,
-                       P.dE, L.dE_part, ch > 0 ? 1 : 0, P.accum == kAccumAtomic ? 1 : 0, (const int*)L.rowmap,
+                       bf_direct ? P.dE : (void*)dE32, bf_direct ? 1 : 0, L.dE_part, ch > 0 ? 1 : 0,
+                       P.accum == kAccumAtomic ? 1 : 0, (const int*)L.rowmap,
                        (const float*)L.scale_c,
                        smooth ? (const float*)L.csum : nullptr, r1);
     prof_after(kKDE, st);
@@ -1384,11 +1425,17 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
                        L.nvb_t, P.V, smooth ? (const float*)L.aux : nullptr, r1, P.dbias);
     prof_after(kKDbReduce, st);
   }
-  if (P.accum != kAccumAtomic && L.splits > 1) {
-    const size_t n4 = (size_t)P.N * P.D / 4;
+  const size_t n4 = (size_t)P.N * P.D / 4;  // D is a multiple of 4
+  const int nparts = P.accum != kAccumAtomic ? L.splits - 1 : 0;
+  if (P.grad_bf16 && !bf_direct) {
     prof_before(kKDEReduce, st);
-    hipLaunchKernelGGL(dE_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, P.dE, L.dE_part,
-                       n4, L.splits - 1, n4);
+    hipLaunchKernelGGL(dE_finish_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                       (const float*)dE32, (const float*)L.dE_part, n4, nparts, n4, (uint16_t*)P.dE);
+    prof_after(kKDEReduce, st);
+  } else if (!P.grad_bf16 && nparts > 0) {
+    prof_before(kKDEReduce, st);
+    hipLaunchKernelGGL(dE_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, dE32, L.dE_part,
+                       n4, nparts, n4);
     prof_after(kKDEReduce, st);
   }
   return hipGetLastError();

@@ -76,9 +76,9 @@ def _fwd(L, e=FAKE, c=FAKE, t=FAKE, N=64, D=64, V=100, dt=0, ign=-100, red=2, ca
 
 
 def _bwd(L, e=FAKE, N=64, D=64, V=100, dt=0, red=2, cap=0.0, flt=1, acc=0, chunk=0, dE=FAKE, wsb=1 << 30,
-         bias=None, db=None, ls=0.0, zl=0.0):
-    return L.cce_backward(e, FAKE, bias, FAKE, N, D, V, dt, -100, red, cap, ls, zl, FAKE, FAKE, flt, acc, chunk, dE,
-                          FAKE, db, FAKE, wsb, None)
+         bias=None, db=None, ls=0.0, zl=0.0, gdt=0):
+    return L.cce_backward(e, FAKE, bias, FAKE, N, D, V, dt, -100, red, cap, ls, zl, FAKE, FAKE, flt, acc, chunk, gdt,
+                          dE, FAKE, db, FAKE, wsb, None)
 
 
 def test_forward_argument_errors(L):
@@ -117,6 +117,8 @@ def test_backward_argument_errors(L):
     assert _bwd(L, flt=2) == INVALID
     assert _bwd(L, acc=5) == INVALID
     assert _bwd(L, chunk=100) == INVALID
+    assert _bwd(L, gdt=2) == INVALID and _bwd(L, gdt=-1) == INVALID   # grad dtype: float32 or operand
+    assert _bwd(L, gdt=1, wsb=1024) == WORKSPACE
     assert _bwd(L, cap=-1.0) == INVALID
     assert _bwd(L, cap=1.0, ls=0.2) == UNSUPPORTED
     assert _bwd(L, cap=1.0, wsb=1024) == WORKSPACE

@@ -447,6 +447,50 @@ def test_softcap_with_smoothing_is_rejected(M):
         run(M, inp, "mean", backward=False, ls=0.1, cap=5.0)
 
 
+# ----------------------------------------------------------------------------- gradients in the operand dtype
+# (dtype, N, D, V, filter, accum, vocab_chunk, label smoothing): bf16 dE/dC
+# written by the kernels straight from one pass ('direct': one vocab chunk,
+# one dE split), or through the fp32 accumulation and a final rounding pass
+# (splits, chunks, atomics); fp32 operands keep fp32 gradients.
+_GRAD_DTYPE_CASES = {
+    "direct": ("bf16", 2048, 8192, 520, False, "deterministic", 0, 0.0),
+    "direct_filtered_padded": ("bf16", 2048, 8192, 520, True, "deterministic", 0, 0.1),
+    "splits": ("bf16", 600, 136, 1100, True, "deterministic", 0, 0.0),
+    "chunks": ("bf16", 530, 200, 1500, False, "deterministic", 512, 0.1),
+    "atomic": ("bf16", 530, 200, 1500, True, "atomic", 512, 0.0),
+    "fp32": ("f32", 300, 68, 513, True, "deterministic", 0, 0.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_GRAD_DTYPE_CASES))
+def test_grad_dtype_operand(M, case):
+    import torch
+    dt, N, D, V, flt, accum, chunk, ls = _GRAD_DTYPE_CASES[case]
+    inp = W.custom(N, D, V, dt, seed=71, c_std=0.05, ignore_frac=0.2 if "padded" in case else 0.05)
+    print(f"[grad dtype] {case}", flush=True)
+    e, c, t = dev(inp["e"], dt), dev(inp["c"], dt), dev_targets(inp["targets"])
+    loss, lse, nv, ws = M.forward(e, c, t, vocab_chunk=chunk, label_smoothing=ls)
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+    kw = dict(filter=flt, accum=accum, vocab_chunk=chunk, label_smoothing=ls)
+    dE32, dC32 = M.backward(e, c, t, lse, g, ws, **kw)
+    dEo, dCo = M.backward(e, c, t, lse, g, ws, grad_dtype="operand", **kw)
+    torch.cuda.synchronize()
+    assert dEo.dtype == e.dtype and dCo.dtype == c.dtype
+    if accum == "deterministic":
+        # the same fp32 sums in the same order, rounded once to nearest-even
+        assert torch.equal(dEo, dE32.to(e.dtype)), case
+        assert torch.equal(dCo, dC32.to(c.dtype)), case
+    f = O.forward(inp["e"], inp["c"], inp["targets"], label_smoothing=ls)
+    valid = torch.from_numpy(f.valid).cuda()
+    assert (dEo[~valid] == 0).all(), "ignored rows must give exactly 0 gradient"
+    Bn, Bv, _ = M.tile_shape()
+    keep = O.lse_and_keep(inp["e"], inp["c"], inp["targets"], Bn, Bv)[1] if flt else None
+    b = O.backward(inp["e"], inp["c"], inp["targets"], grad_loss=1.0, keep=keep,
+                   tile=(Bn, Bv) if flt else None, label_smoothing=ls)
+    check_grad(dEo.float().cpu().numpy(), b.dE, GRAD_RTOL, case + " dE")
+    check_grad(dCo.float().cpu().numpy(), b.dC, GRAD_RTOL, case + " dC")
+
+
 # ----------------------------------------------------------------------------- full-size, sampled
 def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, n_vocab=24, dC_check=True,
                   with_bias=False, ls=0.0, zl=0.0, cap=0.0):
