@@ -10,8 +10,10 @@
 //  * global traffic goes through buffer resources (raw buffer loads/stores)
 //    whose range check returns zero for, or drops, every out-of-range access:
 //    ragged tiles need no branches and cannot touch memory outside a tensor.
-//  * tiles are staged in LDS with a 16-byte row pad, so that the 8 lanes which
-//    share a ds_read_b128 cycle hit disjoint banks.
+//  * tiles written to LDS by the waves carry a 16-byte row pad (a 144-byte row
+//    stride puts any 16 consecutive rows, which one ds_read_b128 cycle of the
+//    64-bank LDS serves, on distinct banks); tiles the DMA path writes are
+//    swizzled instead (see DmaTile).
 //  * operands whose contraction index is the slow (row) index in memory
 //    ("MN-major", e.g. C read as C[v][d] when contracting over v) are loaded
 //    as VECxVEC blocks and transposed in registers before the LDS store, so the
@@ -469,12 +471,16 @@ __device__ __forceinline__ void mainloop(f32x16 (&acc)[C::FM][C::FN], const Oper
 // cycles, while a buffer load costs next to nothing.
 //
 // Tile layout: BK elements = 128 bytes per row, no padding.  The 16-byte chunk
-// c of row r is stored in slot c ^ (r % 8), so the eight rows that one
-// fragment read serves per LDS cycle (same chunk, consecutive rows) hit eight
-// different slots: the reads stay bank-conflict free without a pad, which a
-// contiguous 1 KB DMA write could not produce.  One DMA instruction fills 8
-// rows; lane l writes slot l % 8 of row l / 8 and therefore fetches logical
-// chunk (l % 8) ^ (l / 8) of that row.
+// c of row r is stored in slot c ^ swz(r), swz(r) = (r % 8) ^ (r / 8 % 2).  A
+// fragment read serves 16 lanes (one chunk of 16 consecutive rows, 256 bytes)
+// per cycle of the 64-bank LDS; two rows 128 bytes apart fall on the two bank
+// halves, so the 16 pieces are conflict free when the even rows take eight
+// distinct slots and so do the odd rows, which swz gives (it also keeps any 8
+// consecutive rows in distinct slots).  The plain (r % 8) swizzle repeats
+// every 8 rows and measured two-way conflicts on every read.  A contiguous
+// 1 KB DMA write could not produce a padded layout; this one needs none.  One
+// DMA instruction fills 8 rows; lane l writes slot l % 8 of row r = 8 i + l / 8
+// and therefore fetches logical chunk (l % 8) ^ swz(r) of that row.
 // ============================================================================
 
 // One 16-byte-per-lane buffer load into LDS at lds_addr + 16 * lane.  Written
@@ -522,14 +528,20 @@ struct DmaTile {
   static constexpr int NW = C::NT / 64;
   static constexpr int PER = BYTES / 1024 / NW;  // DMA instructions per wave per step
   static_assert(BYTES % (1024 * NW) == 0, "tile not evenly split");
+  static_assert(PER % 2 == 0, "instruction parity gives the row's swizzle");
   static constexpr int KG = C::KGROUPS;
+  // slot of logical chunk c in row r: c ^ swz(r)
+  __device__ static constexpr int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
   uint32_t roff[PER];  // byte offset of the lane's row, kOOB past the valid rows
-  uint32_t kc;         // K offset (elements) of the lane's chunk within a step
+  uint32_t kc[2];      // K offset (elements) of the lane's chunk within a step, by instruction parity
   uint32_t flo[KG], fhi[KG];  // fragment chunk offsets by K group (fp32: two chunks)
   // With `rowmap`, tile row r is row rowmap[r] of the operand (-1: none).
   __device__ __forceinline__ void init(const Operand& op, const int* __restrict__ rowmap = nullptr) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    kc = (uint32_t)(((lane & 7) ^ (lane >> 3)) * C::VEC);
+    // instruction i fills rows 8 (wave PER + i) .. +7: row % 16 / 8 is the
+    // parity of i (PER is even)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) kc[p] = (uint32_t)(((lane & 7) ^ swz(8 * p + (lane >> 3))) * C::VEC);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int row = 8 * (wave * PER + i) + (lane >> 3);
@@ -540,7 +552,7 @@ struct DmaTile {
   // DMA instruction i of this wave for the step at K offset k0 into the tile
   // whose LDS byte address is `tile` (wave-uniform).
   __device__ __forceinline__ void issue(int i, const Operand& op, int k0, uint32_t tile) const {
-    const uint32_t kk = (uint32_t)k0 + kc;
+    const uint32_t kk = (uint32_t)k0 + kc[i & 1];
     const uint32_t off = (roff[i] == kOOB || kk >= (uint32_t)op.kdim) ? kOOB : roff[i] + kk * (uint32_t)sizeof(T);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     dma16(op.desc, off, tile + (uint32_t)((wave * PER + i) * 1024));
@@ -550,7 +562,7 @@ struct DmaTile {
   __device__ __forceinline__ void frag_init(int rc0) {
     const int lane = threadIdx.x & 63;
     const int row = rc0 + (lane & 31);
-    const int sw = lane & 7;  // row % 8
+    const int sw = swz(row);
     constexpr int CPG = 16 / C::VEC;  // chunks per K group of 16
 #pragma unroll
     for (int g = 0; g < KG; ++g) {
@@ -566,14 +578,17 @@ struct DmaTile {
 
 // MN-major bf16 operand (element (col, k) at k*ld + col): BK rows, one per K
 // index, of COLS columns (512 bytes), loaded as they lie in memory.  Chunk c
-// (columns 8c..8c+7) of K row k sits in slot c ^ 2 (k % 4).  Fragments come
+// (columns 8c..8c+7) of K row k sits in slot c ^ swz(k), swz(k) = 2 (k % 4) ^
+// 8 (k % 2).  Fragments come
 // from the transposing read ds_read_b64_tr_b16: within each group of 16
 // lanes, output lane i element e is element i % 4 of the 8 bytes addressed by
 // source lane i / 4 + 4 e.  Source lane s addresses K row k0 + s / 4, columns
 // c0 + 4 (s % 4) .. +3, so output lane i receives column c0 + i at K rows
 // k0..k0+3; two such reads give a lane its 8 K elements.  The sixteen 8-byte
-// pieces of one group cover four rows and two chunks, eight distinct slots
-// under the swizzle: no bank conflicts.
+// pieces of one group cover four rows and two chunks, and the 32 pieces that
+// share a cycle of the 64-bank LDS (two groups: four rows, four chunks) cover
+// sixteen slots that are distinct modulo 16 (256 bytes) under the swizzle: no
+// bank conflicts.
 template <class C, int COLS>
 struct DmaTileMN {
   using T = typename C::T;
@@ -586,7 +601,7 @@ struct DmaTileMN {
   static constexpr int PER = BYTES / 1024 / NW;
   static_assert(BYTES % (1024 * NW) == 0 && PER % 2 == 0, "tile not evenly split");
   static constexpr int FN = C::FN;  // fragments per wave
-  __device__ static constexpr int swz(int k) { return 2 * (k & 3); }
+  __device__ static constexpr int swz(int k) { return 2 * (k & 3) ^ 8 * (k & 1); }
   uint32_t coff[2];  // byte offset of the lane's chunk in its K row, by instruction parity; kOOB past the columns
   uint32_t foff[FN];
   __device__ __forceinline__ void init(const Operand& op) {
