@@ -100,9 +100,9 @@ typedef struct {
  * Bytes of device workspace needed by cce_forward and cce_backward for this
  * problem.  vocab_chunk = 0 picks the library default: the backward forms
  * gradient tiles for a vocabulary chunk at a time and keeps that chunk's
- * bf16/fp32 G block, in both orientations, in the workspace (at most about
- * 2 GiB for the two by default: the whole vocabulary for N up to about 4096
- * with bf16), plus e transposed (N*D elements); a positive value (a multiple
+ * G block in the workspace (bf16: once, token-major; fp32: in both
+ * orientations; under 2 GiB by default: the whole vocabulary for N up to
+ * about 8192 with bf16), plus e transposed (N*D elements); a positive value (a multiple
  * of 256) sets the chunk width, trading workspace for launches (a 512 MiB
  * chunk measured about 2% slower at N = 4096, D = 4096, V = 128256).  It also
  * holds an fp32 [N, D] accumulation of dE for bf16 gradients that more than

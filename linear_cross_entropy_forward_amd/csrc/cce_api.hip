@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/cce.h"
@@ -25,7 +26,11 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   if (vocab_chunk > 0) {
     vc = vocab_chunk;
   } else {
-    vc = (int64_t)(kDefaultGBudget / ((2 * (size_t)L.Npad + kGtPad) * es)) / kTileV * kTileV;
+    // bf16 keeps G only; fp32 both G and G^T.  Each stays below 2 GiB (32-bit
+    // buffer offsets).
+    const size_t per_col = (size_t)L.Npad + (dtype == kDtypeBf16 ? 0 : (size_t)L.Npad + kGtPad);
+    const size_t cap = (((size_t)1 << 31) - 1) / (((size_t)L.Npad + kGtPad) * es);
+    vc = (int64_t)std::min(kDefaultGBudget / (per_col * es), cap) / kTileV * kTileV;
   }
   if (vc < kTileV) vc = kTileV;
   if (vc > vmax) vc = vmax;
@@ -52,7 +57,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   L.splits_atomic = spa;
   L.g_bytes = (size_t)L.Npad * (size_t)vc * es;
   L.gt_ld = L.Npad + kGtPad;
-  L.gt_bytes = (size_t)L.gt_ld * (size_t)vc * es;
+  L.gt_bytes = dtype == kDtypeBf16 ? 0 : (size_t)L.gt_ld * (size_t)vc * es;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {

@@ -589,7 +589,7 @@ struct DmaTile {
 // share a cycle of the 64-bank LDS (two groups: four rows, four chunks) cover
 // sixteen slots that are distinct modulo 16 (256 bytes) under the swizzle: no
 // bank conflicts.
-template <class C, int COLS>
+template <class C, int COLS, int NF>
 struct DmaTileMN {
   using T = typename C::T;
   static_assert(sizeof(T) == 2, "transposing fragment reads are for 16-bit operands");
@@ -600,7 +600,7 @@ struct DmaTileMN {
   static constexpr int NW = C::NT / 64;
   static constexpr int PER = BYTES / 1024 / NW;
   static_assert(BYTES % (1024 * NW) == 0 && PER % 2 == 0, "tile not evenly split");
-  static constexpr int FN = C::FN;  // fragments per wave
+  static constexpr int FN = NF;  // fragments per wave
   __device__ static constexpr int swz(int k) { return 2 * (k & 3) ^ 8 * (k & 1); }
   uint32_t coff[2];  // byte offset of the lane's chunk in its K row, by instruction parity; kOOB past the columns
   uint32_t foff[FN];
@@ -642,7 +642,10 @@ struct DmaTileMN {
 };
 
 // acc[fm][fn] += sum over the K steps of A_tile * B_tile^T, as mainloop()
-// (same step/offset conventions), both operands K-major and DMA-fed.
+// (same step/offset conventions), both operands DMA-fed: K-major (DmaTile),
+// or with A_MN / B_MN MN-major (DmaTileMN, 16-bit only).  The A and B
+// fragments of the MFMA share one lane layout (lane l: row or column l % 32,
+// K elements 8 (l / 32) .. +7), so either tile kind serves either operand.
 //
 // Two LDS stages.  Within a step the MFMAs of K group g run while the
 // fragments of group g+1 are read.  Before the last group each wave waits for
@@ -655,13 +658,13 @@ struct DmaTileMN {
 // group, and part p in group p-1 of the following step, each spread one or two
 // instructions between MFMAs so the issue never stalls the matrix core.
 // Steps past the end (the count is padded to even) read zeros.
-template <class C, int SPB, bool B_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1)>
+template <class C, int SPB, bool B_MN = false, bool A_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1)>
 __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const Operand& A, const Operand& B,
                                              int nsteps, const uint16_t* blocks, void* smem,
                                              const int* __restrict__ brow = nullptr) {
   using T = typename C::T;
-  using TA = DmaTile<C, C::BM>;
-  using TB = std::conditional_t<B_MN, DmaTileMN<C, C::BN>, DmaTile<C, C::BN>>;
+  using TA = std::conditional_t<A_MN, DmaTileMN<C, C::BM, C::FM>, DmaTile<C, C::BM>>;
+  using TB = std::conditional_t<B_MN, DmaTileMN<C, C::BN, C::FN>, DmaTile<C, C::BN>>;
   constexpr int KG = C::KGROUPS;
   static_assert(KG % 2 == 0, "fragment buffers alternate per K group");
   static_assert(NPARTS >= 1 && NPARTS < KG, "the last DMA part must precede the wait");

@@ -92,7 +92,7 @@ struct Layout {
   int* tlist;       // per chunk, its kept gradient tiles in launch order (chunk ch at cvb0 * nb)
   int* tcount;      // [nchunks] kept gradient tiles per chunk
   void* G;          // [Npad][Vc] operand type: gradient tiles of one vocab chunk
-  void* Gt;         // [Vc][gt_ld] the same tiles transposed (columns past Npad unused)
+  void* Gt;         // [Vc][gt_ld] the same tiles transposed, fp32 only (columns past Npad unused)
   void* Et;         // [D][Npad] e transposed (zero rows past N)
   size_t g_bytes;   // bytes of G
   size_t gt_bytes;  // bytes of Gt

@@ -826,76 +826,74 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     else rag(std::integral_constant<int, 0>{});
   };
 
+  // token sums per vocabulary row (db), from this lane's share rs: across the
+  // 32 lanes of a half-wave, then the waves that share the rows, through
+  // LDS, in a fixed order.  Called with the LDS free.
+  auto db_sums = [&](const float (&rs)[C::FM][4][4]) __attribute__((always_inline)) {
+    float* red = (float*)smem;  // [WAVES_N][BM]
+    const int wn = (threadIdx.x >> 6) % C::WAVES_N;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float x = rs[fm][q][u];
+#pragma unroll
+          for (int m = 16; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+          if ((lane & 31) == 0) red[wn * C::BM + am.row(fm, 4 * q) + u] = x;
+        }
+    __syncthreads();
+    for (int r = threadIdx.x; r < C::BM; r += C::NT) {
+      float x = 0.f;
+      for (int w = 0; w < C::WAVES_N; ++w) x += red[w * C::BM + r];
+      if (v0 + r < V) db_part[(size_t)tn * V + v0 + r] = x;
+    }
+  };
+  float rs[C::FM][4][4] = {};  // this lane's share of each vocab row's token sum (for db)
   if constexpr (sizeof(T) == 2) {
-    // Staged through LDS (free after the main loop) twice, so that both G and
-    // G^T leave as rows of 16-byte stores from consecutive lanes (stored
-    // straight from the accumulators, one instruction would scatter 8-byte
-    // pieces over 64 rows).  A staging tile holds 256 rows of 512 bytes;
-    // 16-byte chunk j of row r sits in slot j ^ f(r).  Any f keeps the row
-    // drains conflict free; f is chosen per pass for its writes: pass 1 writes
-    // one chunk of 32 consecutive rows (f = r % 32), pass 2 four chunks of
-    // one row per half-wave (f swaps the two low bit pairs of r).
+    // bf16: G only (dC reads it with transposing LDS reads; G^T is not
+    // formed), staged through LDS (free after the main loop) so that it
+    // leaves as rows of 16-byte stores from consecutive lanes (stored straight
+    // from the accumulators, one instruction would scatter 8-byte pieces over
+    // 64 rows).  A staging tile holds 256 token rows of 512 bytes; 16-byte
+    // chunk j of row r sits in slot j ^ (r % 32): the writes (one chunk of 32
+    // consecutive rows per half-wave) and the row drains are both conflict
+    // free.
     static_assert(C::BM == 256 && C::BN == 256 && C::LDS_DMA_BYTES >= 256 * 512, "tile staging");
     lds_u8* tile = (lds_u8*)smem;
-    auto slot = [](int r, int col, auto pass2) -> uint32_t {
-      const int f = decltype(pass2)::value ? (((r & 3) << 2) | ((r >> 2) & 3) | (r & 16)) : (r & 31);
-      return (uint32_t)(r * 512 + (((col >> 3) ^ f) << 4) + ((col & 7) << 1));
+    auto slot = [](int r, int col) -> uint32_t {
+      return (uint32_t)(r * 512 + (((col >> 3) ^ (r & 31)) << 4) + ((col & 7) << 1));
     };
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // rows of 256 bf16 out of the staging tile, two per instruction: row
-    // `wave * 64 + 2 it + lane / 32`, chunk lane % 32, to row-major memory
-    // With `sums` (the G^T pass, when the bias gradient is wanted) each
-    // vocabulary row's 256 tokens are also added up: 8 per lane, then across
-    // the 32 lanes of the half-wave, giving this token block's share of db.
-    auto drain = [&](rsrc_t r, uint32_t pitch, uint32_t row0, uint32_t col0, auto pass2, bool sums) {
-#pragma unroll 4
-      for (int it = 0; it < 32; ++it) {
-        const int rr = wave * 64 + it * 2 + (lane >> 5), jc = lane & 31;
-        const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(rr, jc * 8, pass2));
-        __builtin_amdgcn_raw_buffer_store_b128(val, r, ((row0 + (uint32_t)rr) * pitch + col0 + (uint32_t)jc * 8u) * 2u,
-                                               0, kStoreNT);
-        if (sums) {
-          float t8 = 0.f;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t w = val[q];
-            t8 += __builtin_bit_cast(float, w << 16) + __builtin_bit_cast(float, w & 0xffff0000u);
-          }
-#pragma unroll
-          for (int m = 16; m >= 1; m >>= 1) t8 += __shfl_xor(t8, m, 64);
-          if (jc == 0 && v0 + rr < V) db_part[(size_t)tn * V + v0 + rr] = t8;
-        }
+    const bool sums = db_part != nullptr;
+    run([&](int fn, int fm, int q, int rl, const float (&g)[4]) __attribute__((always_inline)) {
+      const uint32_t lo = pack_bf16(g[0], g[1]), hi = pack_bf16(g[2], g[3]);
+      *(__attribute__((address_space(3))) u32x2*)(tile + slot(am.colj(fn), rl)) = u32x2{lo, hi};
+      if (sums) {  // the rounded values, as the contractions see them
+        rs[fm][q][0] += __builtin_bit_cast(float, lo << 16);
+        rs[fm][q][1] += __builtin_bit_cast(float, lo & 0xffff0000u);
+        rs[fm][q][2] += __builtin_bit_cast(float, hi << 16);
+        rs[fm][q][3] += __builtin_bit_cast(float, hi & 0xffff0000u);
       }
-    };
-    uint32_t pk[C::FN][C::FM][4][2];
-    // pass 1: [token][vocab] -> G rows
-    run([&](int fn, int fm, int q, int, const float (&g)[4]) __attribute__((always_inline)) {
-      const int rl = am.row(fm, 4 * q);
-      pk[fn][fm][q][0] = pack_bf16(g[0], g[1]);
-      pk[fn][fm][q][1] = pack_bf16(g[2], g[3]);
-      *(__attribute__((address_space(3))) u32x2*)(tile + slot(am.colj(fn), rl, std::false_type{})) =
-          u32x2{pk[fn][fm][q][0], pk[fn][fm][q][1]};
     });
     __syncthreads();
-    drain(rg, (uint32_t)Vc, (uint32_t)n0, (uint32_t)vl0, std::false_type{}, false);
-    __syncthreads();
-    // pass 2: [vocab][token] -> G^T rows, one 16-bit store per element (the
-    // 32 lanes of a half-wave write 64 consecutive bytes of one vocab row)
-#pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            *(__attribute__((address_space(3))) uint16_t*)(
-                tile + slot(am.row(fm, 4 * q) + u, am.colj(fn), std::true_type{})) =
-                (uint16_t)(pk[fn][fm][q][u >> 1] >> (16 * (u & 1)));
-    __syncthreads();
-    drain(rgt, (uint32_t)gt_ld, (uint32_t)vl0, (uint32_t)n0, std::true_type{}, db_part != nullptr);
+    // token rows of 256 bf16 out of the staging tile, two per instruction:
+    // row `wave * 64 + 2 it + lane / 32`, chunk lane % 32
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int rr = wave * 64 + it * 2 + (lane >> 5), jc = lane & 31;
+      const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(rr, jc * 8));
+      __builtin_amdgcn_raw_buffer_store_b128(
+          val, rg, (((uint32_t)n0 + (uint32_t)rr) * (uint32_t)Vc + (uint32_t)vl0 + (uint32_t)jc * 8u) * 2u, 0,
+          kStoreNT);
+    }
+    if (sums) {
+      __syncthreads();  // the drain's LDS reads are done
+      db_sums(rs);
+    }
   } else {
-    float rs[C::FM][4][4] = {};  // this lane's share of each row's token sum (for db)
     run([&](int fn, int fm, int q, int rl, const float (&g)[4]) __attribute__((always_inline)) {
       const int n = n0 + am.colj(fn);
       store4(rg, ((uint32_t)n * (uint32_t)Vc + (uint32_t)(vl0 + rl)) * (uint32_t)sizeof(T), g[0], g[1], g[2], g[3],
@@ -906,30 +904,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) rs[fm][q][u] += g[u];
     });
-    if (db_part) {
-      // token sums per vocabulary row: across the 32 lanes of a half-wave,
-      // then the two waves that share the rows, through LDS, in a fixed order
-      float* red = (float*)smem;  // [WAVES_N][BM]
-      const int wn = (threadIdx.x >> 6) % C::WAVES_N;
-      const int lane = threadIdx.x & 63;
-#pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            float x = rs[fm][q][u];
-#pragma unroll
-            for (int m = 16; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-            if ((lane & 31) == 0) red[wn * C::BM + am.row(fm, 4 * q) + u] = x;
-          }
-      __syncthreads();
-      for (int r = threadIdx.x; r < C::BM; r += C::NT) {
-        float x = 0.f;
-        for (int w = 0; w < C::WAVES_N; ++w) x += red[w * C::BM + r];
-        if (v0 + r < V) db_part[(size_t)tn * V + v0 + r] = x;
-      }
-    }
+    if (db_part) db_sums(rs);
   }
 }
 
@@ -976,15 +951,18 @@ __global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict_
 
 // ============================================================================
 // dC rows of one vocabulary chunk: dC[v][d] = sum_n G^T[v][n] E^T[d][n] over
-// the kept token blocks of the tile's vocab block (both operands K-major).
+// the kept token blocks of the tile's vocab block.  B = E^T (K-major); A = G^T:
+// bf16 reads G [Npad][Vc] (MN-major) through transposing LDS reads, fp32 the
+// K-major G^T [Vc][gt_ld].
 // ============================================================================
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
-    const typename C::T* __restrict__ Gt, const typename C::T* __restrict__ Et,
-    const uint8_t* __restrict__ keep, int Npad, int gt_ld, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
-    int tiles_v, int tiles_d, size_t gt_bytes, const float* __restrict__ r1c, void* __restrict__ dC,
-    int out_bf16) {
+    const typename C::T* __restrict__ G, const typename C::T* __restrict__ Gt, const typename C::T* __restrict__ Et,
+    const uint8_t* __restrict__ keep, int Npad, int Vc, int gt_ld, int D, int V, int nvb_t, int cvb0, int cv0,
+    int clen, int tiles_v, int tiles_d, size_t g_bytes, size_t gt_bytes, const float* __restrict__ r1c,
+    void* __restrict__ dC, int out_bf16) {
   using T = typename C::T;
+  constexpr bool kMN = sizeof(T) == 2;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
   // Groups of kRasterGroup vocab tiles (each with all its d tiles) are dealt
@@ -1004,8 +982,10 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
   const int nb = Npad / kTileN;
   const int nk = collect_blocks(keep, (size_t)(cvb0 + tvl), nvb_t, nb, blocks);
 
-  Operand A = make_operand(Gt + (size_t)vl0 * gt_ld, gt_bytes - (size_t)vl0 * gt_ld * sizeof(T), (uint32_t)gt_ld,
-               min(C::BM, clen - vl0), Npad);
+  const Operand A =
+      kMN ? make_operand(G + vl0, g_bytes - (size_t)vl0 * sizeof(T), (uint32_t)Vc, min(C::BM, clen - vl0), Npad)
+          : make_operand(Gt + (size_t)vl0 * gt_ld, gt_bytes - (size_t)vl0 * gt_ld * sizeof(T), (uint32_t)gt_ld,
+                         min(C::BM, clen - vl0), Npad);
   Operand B = make_operand(Et + (size_t)d0 * Npad, (uint64_t)(D - d0) * Npad * sizeof(T), (uint32_t)Npad,
                min(C::BN, D - d0), Npad);
   f32x16 acc[C::FM][C::FN];
@@ -1016,8 +996,8 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
   constexpr int SPB = kTileN / C::BK;
   // the kept token blocks are the first nk (no filtering effect on this tile;
   // compacted slots put the blocks of ignored rows last): contiguous K
-  if (nk > 0 && blocks[nk - 1] == nk - 1) mainloop_dma<C, SPB>(acc, A, B, nk * SPB, nullptr, smem);
-  else mainloop_dma<C, SPB>(acc, A, B, nk * SPB, blocks, smem);
+  if (nk > 0 && blocks[nk - 1] == nk - 1) mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, nullptr, smem);
+  else mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, blocks, smem);
 
   AccMap<C> am;
   const int vg0 = cv0 + vl0;
@@ -1115,8 +1095,12 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   const int nk = hi - lo;
   const uint16_t* bl = blocks + lo;
 
-  Operand A = make_operand(G + (size_t)n0 * Vc, g_bytes - (size_t)n0 * Vc * sizeof(T), (uint32_t)Vc,
-               min(C::BM, N - n0), clen);
+  // G rows n0.. over the chunk's vocabulary (K-major), from vocab offset ka
+  auto a_op = [&](size_t ka) -> Operand {
+    const size_t o = (size_t)n0 * Vc + ka;
+    return make_operand(G + o, g_bytes - o * sizeof(T), (uint32_t)Vc, min(C::BM, N - n0), clen - (int)ka);
+  };
+  const Operand A = a_op(0);
   Operand B = make_operand(c + (size_t)cv0 * D + d0, ((uint64_t)(V - cv0) * D - d0) * sizeof(T), (uint32_t)D,
                min(C::BN, D - d0), clen);
   f32x16 acc[C::FM][C::FN];
@@ -1133,8 +1117,7 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   // first block
   if (nk > 0 && (int)bl[nk - 1] - (int)bl[0] == nk - 1) {
     const size_t ka = (size_t)bl[0] * kTileV;
-    const Operand A1 = make_operand(G + (size_t)n0 * Vc + ka, g_bytes - ((size_t)n0 * Vc + ka) * sizeof(T),
-                                    (uint32_t)Vc, min(C::BM, N - n0), clen - (int)ka);
+    const Operand A1 = a_op(ka);
     const Operand B1 = make_operand(c + ((size_t)cv0 + ka) * D + d0,
                                     ((uint64_t)(V - cv0 - (int64_t)ka) * D - d0) * sizeof(T), (uint32_t)D,
                                     min(C::BN, D - d0), clen - (int)ka);
@@ -1404,9 +1387,9 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     // vocab-tile groups dealt to the XCDs in turn: a whole number of rounds of 8
     const int dc_groups = (cnvb + kRasterGroup - 1) / kRasterGroup;
     const int dc_grid = 8 * kRasterGroup * tiles_d * ((dc_groups + 7) / 8);
-    hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(dc_grid), dim3(C::NT), 0, st, (const T*)L.Gt,
-                       (const T*)L.Et, L.keep, L.Npad, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_d,
-                       L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC, P.grad_bf16);
+    hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(dc_grid), dim3(C::NT), 0, st, (const T*)G, (const T*)L.Gt,
+                       (const T*)L.Et, L.keep, L.Npad, L.Vc, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb,
+                       tiles_d, L.g_bytes, L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC, P.grad_bf16);
     prof_after(kKDC, st);
     const int splits = splits_used;
     prof_before(kKDE, st);

@@ -61,10 +61,13 @@ def test_vocab_chunk(L):
     assert vc(0, 100, 0, 0) == 0 and vc(4, 100, 7, 0) == 0 and vc(4, 100, 0, 100) == 0
     d = vc(4096, 128256, 0, 0)
     assert d % 256 == 0 and 256 <= d <= 128256 + 255
-    # the default keeps both orientations of a chunk's bf16 tiles within 2 GiB:
-    # the whole vocabulary at N = 4096, a quarter of it at N = 16384
-    assert d >= 128256 and vc(16384, 128256, 0, 0) == 32768
-    assert 2 * 16384 * vc(16384, 128256, 0, 0) * 2 <= 2048 << 20
+    # the default keeps a chunk's gradient tiles within 2 GiB, each buffer
+    # below 2^31 bytes: bf16 stores them once (token-major), the whole
+    # vocabulary at N = 4096 and about half of it at N = 16384; fp32 stores
+    # both orientations
+    assert d >= 128256 and vc(16384, 128256, 0, 0) == 65280
+    assert 16384 * vc(16384, 128256, 0, 0) * 2 < 1 << 31
+    assert vc(16384, 128256, 1, 0) == 16384 and 2 * 16384 * 16384 * 4 <= 2048 << 20
     assert vc(4096, 128256, 0, 1024) == 1024
     assert vc(64, 1000, 1, 0) == 1024          # clamped to the vocabulary, in whole tiles
     assert vc(64, 1000, 1, 4096) == 1024
