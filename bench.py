@@ -38,11 +38,11 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "cda333196f6c7626b1467f3d8e65be4cfce548a1c572cff1def8b422e73ba177",
+    "source_sha256": "31ffcecaa534aaa0cb94092bf3b98dd5bb2edb073a03c19999c573c21f05b924",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9212.1e6, "grad_tile": 11376.9e6, "dC_gemm": 8429.0e6, "dE_gemm": 6381.1e6,
-        "rows": 121.3e6, "filter": 3.3e6, "transpose_e": 67.3e6,
+        "fwd_tile": 9079.9e6, "grad_tile": 10551.9e6, "dC_gemm": 8413.0e6, "dE_gemm": 6591.8e6,
+        "rows": 121.4e6, "filter": 3.3e6, "transpose_e": 67.3e6,
     },
 }
 
