@@ -448,7 +448,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        rows_n = args.cpu_rows or (640 if dt_name == "bf16" else N)
+        rows_n = args.cpu_rows or (2048 if dt_name == "bf16" else N)
         cpu = cpu_baseline(inp, min(rows_n, N))
 
     out = {

@@ -45,5 +45,29 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+ROOT = os.path.dirname(HERE)
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "cce_abi_check.c")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "cce_abi_check")
+
+
+def build_c_check(out: str = C_CHECK_BIN) -> str:
+    """Compile the plain-C caller of the ABI (tests/c_abi) against libcce.so
+    with the host C compiler; returns the executable's path."""
+    cc = os.environ.get("CC") or shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        raise RuntimeError("no C compiler for the C ABI check")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [cc, "-O2", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"), C_CHECK_SRC,
+           "-L", HERE, "-lcce", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/../../linear_cross_entropy_forward_amd", f"-Wl,-rpath,{HERE}",
+           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C ABI check failed to build ({r.returncode}):\n{r.stdout}{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_c_check())

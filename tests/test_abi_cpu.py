@@ -154,3 +154,11 @@ def test_binding_fails_loudly_without_gpu_tensors():
     e = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(M.CCEError):
         M.forward(e, e, torch.zeros(4, dtype=torch.int64))
+
+
+def test_c_caller_builds(tmp_path):
+    """The plain-C caller (tests/c_abi) compiles and links against the
+    library through include/cce.h alone (it runs in the GPU tests)."""
+    from linear_cross_entropy_forward_amd import build as b
+    out = b.build_c_check(str(tmp_path / "cce_abi_check"))
+    assert os.path.exists(out)

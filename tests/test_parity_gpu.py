@@ -447,6 +447,21 @@ def test_softcap_with_smoothing_is_rejected(M):
         run(M, inp, "mean", backward=False, ls=0.1, cap=5.0)
 
 
+# ----------------------------------------------------------------------------- a plain C caller
+def test_c_caller(M):
+    """tests/c_abi/cce_abi_check.c: HIP runtime memory and a non-default
+    stream, every entry point from C, checked against the c = 0 closed form."""
+    import os
+    import subprocess
+    from linear_cross_entropy_forward_amd import build as b
+    exe = b.C_CHECK_BIN
+    assert os.path.exists(exe), "build the C check first (__graft_entry__.build())"
+    print("[c caller]", exe, flush=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "cce C ABI check ok" in r.stdout
+
+
 # ----------------------------------------------------------------------------- gradients in the operand dtype
 # (dtype, N, D, V, filter, accum, vocab_chunk, label smoothing): bf16 dE/dC
 # written by the kernels straight from one pass ('direct': one vocab chunk,
