@@ -189,7 +189,7 @@ def make_bias(V, dtype, dev, seed=7):
 
 
 def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=False, label_smoothing=0.0,
-                   z_loss=0.0, softcap=0.0, filter=True, accum="deterministic"):
+                   z_loss=0.0, softcap=0.0, filter=True, accum="deterministic", frozen_classifier=False):
     """Compact forward / forward+backward figures for one workload (defaults:
     filter on, deterministic, the workload's own reduction; with_bias adds a
     classifier bias and asks for its gradient; label_smoothing / z_loss add
@@ -220,7 +220,7 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
     g = torch.full((N,) if red == 0 else (1,), 1.0 / n_valid if red == 0 else 1.0, dtype=torch.float32,
                    device=dev)
     dE = torch.empty((N, D), dtype=torch.float32, device=dev)
-    dC = torch.empty((V, D), dtype=torch.float32, device=dev)
+    dC = None if frozen_classifier else torch.empty((V, D), dtype=torch.float32, device=dev)
     bias = make_bias(V, tdt, dev) if with_bias else None
     db = torch.empty(V, dtype=torch.float32, device=dev) if with_bias else None
     extra = torch.cuda.memory_allocated() - base
@@ -242,7 +242,7 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
         r = L.cce_backward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, softcap,
                            label_smoothing, z_loss, lse.data_ptr(), g.data_ptr(), 1 if filter else 0,
                            0 if accum == "deterministic" else 1, 0, 0, dE.data_ptr(),
-                           dC.data_ptr(), dbp, ws.data_ptr(), ws.numel(), st.cuda_stream)
+                           None if dC is None else dC.data_ptr(), dbp, ws.data_ptr(), ws.numel(), st.cuda_stream)
         if r:
             raise RuntimeError(f"cce_backward failed: {r}")
 
@@ -262,16 +262,18 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
     fwd_ms = timed(fwd)
     stats = M.read_stats(ws, N, V)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    eff = 8.0 * N * V * D / (step_ms * 1e-3) / 1e12
+    # effective work: 2NVD per contraction (forward, recompute, dE, dC)
+    eff = (6.0 if frozen_classifier else 8.0) * N * V * D / (step_ms * 1e-3) / 1e12
     out = {"N": N, "D": D, "V": V, "dtype": w.dtype, "reduction": w.reduction, "fwd_ms": fwd_ms,
            "fwd_tokens_per_s": N / (fwd_ms * 1e-3), "step_ms": step_ms, "tokens_per_s": N / (step_ms * 1e-3),
            "tflops_effective": eff, "pct_of_peak": 100.0 * eff / peak,
-           "tflops_useful": eff * 0.75, "filter": bool(filter), "accum": accum,
+           "tflops_useful": eff * (4.0 / 6.0 if frozen_classifier else 0.75), "filter": bool(filter),
+           "accum": accum, "frozen_classifier": bool(frozen_classifier),
            "tiles_skipped_frac": 1.0 - stats["tiles_kept"] / max(1, stats["tiles_total"]),
            "extra_hbm_bytes": int(extra), "bias": bool(with_bias), "label_smoothing": label_smoothing,
            "z_loss": z_loss, "softcap": softcap}
     plain = (not with_bias and label_smoothing == 0.0 and z_loss == 0.0 and softcap == 0.0 and filter
-             and accum == "deterministic")
+             and accum == "deterministic" and not frozen_classifier)
     if w.dtype == "bf16" and plain:
         out["hipblaslt_fwd_gemm_tflops"] = hipblaslt_gemm_tflops(c, e)
     del ws, loss, lse, nv, g, dE, dC, bias, db
@@ -445,6 +447,9 @@ def main():
         # the filter off (Llama-3.2-1B) and fp32 atomic accumulation (long context)
         configs["llama1b+nofilter"] = config_summary("llama1b", filter=False, materialized_too=False)
         configs["long8b_cal+atomic"] = config_summary("long8b_cal", accum="atomic", materialized_too=False)
+        # a frozen classifier: dE alone (dC's contraction does not run)
+        configs[args.workload + "+frozen_classifier"] = config_summary(args.workload, frozen_classifier=True,
+                                                                       materialized_too=False)
 
     cpu = None
     if not args.no_cpu_baseline:

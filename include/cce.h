@@ -154,7 +154,10 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
  * (cce_grad_dtype) picks the element type of dE (device) [N, D] and dC
  * (device) [V, D], both overwritten: float32, or the operand dtype (bf16
  * gradients written by the kernels themselves, every accumulation still
- * fp32, so a caller training in bf16 needs no conversion pass).  dbias (device) float
+ * fp32, so a caller training in bf16 needs no conversion pass).  dE or dC
+ * may be NULL: that gradient is not formed and its contraction does not run
+ * (a frozen classifier or frozen inputs); at least one of dE, dC and dbias
+ * must be given.  dbias (device) float
  * [V] or NULL: when given, overwritten with the bias gradient db_j =
  * sum_i G_ij (column sums of the filtered gradient tiles, in a fixed order
  * in both accum modes); it is defined with or without a bias.  vocab_chunk as

@@ -181,12 +181,13 @@ def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch
              filter: bool = True, accum: str = "deterministic", softcap: float = 0.0, vocab_chunk: int = 0,
              dE: torch.Tensor | None = None, dC: torch.Tensor | None = None, bias: torch.Tensor | None = None,
              want_dbias: bool = False, label_smoothing: float = 0.0, z_loss: float = 0.0,
-             grad_dtype: str = "float32"):
+             grad_dtype: str = "float32", want_dE: bool = True, want_dC: bool = True):
     """cce_backward.  grad_loss is float32 [N] ('none') or [1]/0-dim.  Returns
     (dE [N, D], dC [V, D]), plus float32 db [V] when want_dbias; dE and dC are
     float32, or with grad_dtype='operand' in e's dtype (written by the kernels,
-    accumulated in fp32).  bias, label_smoothing, z_loss and softcap must be
-    those of the forward that filled ws."""
+    accumulated in fp32).  want_dE / want_dC = False leaves that gradient out
+    (None; its contraction does not run).  bias, label_smoothing, z_loss and
+    softcap must be those of the forward that filled ws."""
     _validate(e, c, targets)
     _validate_bias(bias, c)
     N, D = e.shape
@@ -194,18 +195,19 @@ def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch
     dev = e.device
     g = grad_loss.reshape(-1).to(torch.float32).contiguous()
     gdt = torch.float32 if grad_dtype == "float32" else e.dtype
-    if dE is None:
+    if dE is None and want_dE:
         dE = torch.empty((N, D), dtype=gdt, device=dev)
-    if dC is None:
+    if dC is None and want_dC:
         dC = torch.empty((V, D), dtype=gdt, device=dev)
-    if dE.dtype != gdt or dC.dtype != gdt or not (dE.is_contiguous() and dC.is_contiguous()):
-        raise CCEError(f"dE and dC must be contiguous {gdt} tensors")
+    for x in (dE, dC):
+        if x is not None and (x.dtype != gdt or not x.is_contiguous()):
+            raise CCEError(f"dE and dC must be contiguous {gdt} tensors")
     db = torch.empty(V, dtype=torch.float32, device=dev) if want_dbias else None
     _check(lib().cce_backward(_ptr(e), _ptr(c), _ptr(bias) if bias is not None else None, _ptr(targets), N, D, V,
                               _dtype_code(e), ignore_index, _REDUCTIONS[reduction], softcap, label_smoothing,
                               z_loss, _ptr(lse), _ptr(g),
-                              int(bool(filter)), _ACCUM[accum], vocab_chunk, _GRAD_DTYPE[grad_dtype], _ptr(dE),
-                              _ptr(dC),
+                              int(bool(filter)), _ACCUM[accum], vocab_chunk, _GRAD_DTYPE[grad_dtype],
+                              _ptr(dE) if dE is not None else None, _ptr(dC) if dC is not None else None,
                               _ptr(db) if db is not None else None, _ptr(ws), ws.numel(), _stream()),
            "cce_backward")
     return (dE, dC, db) if want_dbias else (dE, dC)
@@ -233,10 +235,14 @@ class _CCEFunction(torch.autograd.Function):
         e, c, bias, targets, lse, ws = ctx.saved_tensors
         reduction, ignore_index, filter, accum, label_smoothing, z_loss, softcap = ctx.cfg
         want_db = bias is not None and ctx.needs_input_grad[2]
-        # gradients in the inputs' dtype, written so by the kernels
+        if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1] or want_db):
+            return None, None, None, None, None, None, None, None, None, None, None
+        # gradients in the inputs' dtype, written so by the kernels; a frozen
+        # input's gradient is not formed
         out = backward(e, c, targets, lse, grad, ws, ignore_index=ignore_index, reduction=reduction,
                        filter=filter, accum=accum, bias=bias, want_dbias=want_db,
-                       label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap, grad_dtype="operand")
+                       label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap, grad_dtype="operand",
+                       want_dE=ctx.needs_input_grad[0], want_dC=ctx.needs_input_grad[1])
         dE, dC = out[0], out[1]
         db = out[2].to(bias.dtype) if want_db else None
         return dE, dC, db, None, None, None, None, None, None, None, None

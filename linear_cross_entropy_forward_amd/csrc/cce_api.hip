@@ -252,11 +252,12 @@ cce_status cce_backward(const void* e, const void* c, const void* bias, const in
   if (!bias_ok(bias, dtype) || ((uintptr_t)dbias & 3u) || !terms_ok(label_smoothing, z_loss))
     return CCE_ERR_INVALID_ARG;
   if (softcap > 0.0f && label_smoothing > 0.0f) return CCE_ERR_UNSUPPORTED;
-  if (!lse || !grad_loss || !dE || !dC) return CCE_ERR_INVALID_ARG;
+  // each gradient is optional (null: not formed), at least one is asked for
+  if (!lse || !grad_loss || (!dE && !dC && !dbias)) return CCE_ERR_INVALID_ARG;
   if ((filter != 0 && filter != 1) || (accum != kAccumDeterministic && accum != kAccumAtomic))
     return CCE_ERR_INVALID_ARG;
   if (grad_dtype != CCE_GRAD_FLOAT32 && grad_dtype != CCE_GRAD_OPERAND) return CCE_ERR_INVALID_ARG;
-  if (!aligned16(dE) || !aligned16(dC)) return CCE_ERR_INVALID_ARG;
+  if ((dE && !aligned16(dE)) || (dC && !aligned16(dC))) return CCE_ERR_INVALID_ARG;
   Layout L = make_layout(N, D, V, dtype, vocab_chunk, ws);
   if (ws_bytes < L.total) return CCE_ERR_WORKSPACE;
   Problem P{};

@@ -1335,8 +1335,10 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
                      P.reduction, P.grad_loss, (const float*)P.lse, L.scale, L.rowmap, L.scale_c, L.lse_c, L.tgt_c,
                      L.hdr, smooth ? L.aux + 1 : nullptr);
   prof_after(kKBwdPrep, st);
+  // dE, dC and db are each optional (a null output is not formed)
+  const bool want_dE = P.dE != nullptr, want_dC = P.dC != nullptr;
   // -eps/V * sum_i scale_i e_i: the smoothing share of every dC row
-  if (smooth) launch_colsum<T>(e, L.scale, P.N, P.D, r1, L, L.r1c, st);
+  if (smooth && want_dC) launch_colsum<T>(e, L.scale, P.N, P.D, r1, L, L.r1c, st);
   prof_before(kKFilter, st);
   hipLaunchKernelGGL(filter_kernel, dim3((L.nvb_t + 255) / 256, L.nb), dim3(256), 0, st, P.targets, P.lse,
                      L.part, (const int*)L.rowmap, P.N, P.V, L.nVB, P.ignore_index, kTileN, kTileV, kPartialWidth, L.nvb_t, P.filter,
@@ -1346,17 +1348,19 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   hipLaunchKernelGGL(tile_list_kernel, dim3(L.nchunks), dim3(1024), 0, st, (const uint8_t*)L.keep, L.nvb_t,
                      L.Npad / kTileN, L.Vc / kTileV, L.tlist, L.tcount);
   prof_after(kKTileList, st);
-  prof_before(kKTransE, st);
-  hipLaunchKernelGGL(transpose_e_kernel<T>, dim3((P.D + 63) / 64, L.Npad / 64), dim3(256), 0, st, e,
-                     (const int*)L.rowmap, (T*)L.Et, P.N, P.D, L.Npad);
-  prof_after(kKTransE, st);
+  if (want_dC) {
+    prof_before(kKTransE, st);
+    hipLaunchKernelGGL(transpose_e_kernel<T>, dim3((P.D + 63) / 64, L.Npad / 64), dim3(256), 0, st, e,
+                       (const int*)L.rowmap, (T*)L.Et, P.N, P.D, L.Npad);
+    prof_after(kKTransE, st);
+  }
   // dE: float output, or bf16 written straight by dE_gemm when a single pass
   // forms it (one vocab chunk, one split, no atomics), else accumulated in
   // fp32 (dE_acc) and rounded to bf16 at the end
   const int splits_used = P.accum == kAccumAtomic ? L.splits_atomic : L.splits;
   const bool bf_direct = P.grad_bf16 && L.nchunks == 1 && splits_used == 1 && P.accum != kAccumAtomic;
   float* dE32 = P.grad_bf16 ? (bf_direct ? nullptr : L.dE_acc) : (float*)P.dE;
-  if (P.accum == kAccumAtomic) {
+  if (want_dE && P.accum == kAccumAtomic) {
     const size_t n = (size_t)P.N * P.D;
     if (smooth) {
       prof_before(kKFillRank1, st);
@@ -1383,24 +1387,29 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
                        (const int*)L.tcount + ch, P.N, P.D, P.V, cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
                        G, (T*)L.Gt, L.g_bytes, L.gt_bytes, P.dbias ? L.db_part : nullptr);
     prof_after(kKGradTile, st);
-    prof_before(kKDC, st);
-    // vocab-tile groups dealt to the XCDs in turn: a whole number of rounds of 8
-    const int dc_groups = (cnvb + kRasterGroup - 1) / kRasterGroup;
-    const int dc_grid = 8 * kRasterGroup * tiles_d * ((dc_groups + 7) / 8);
-    hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(dc_grid), dim3(C::NT), 0, st, (const T*)G, (const T*)L.Gt,
-                       (const T*)L.Et, L.keep, L.Npad, L.Vc, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb,
-                       tiles_d, L.g_bytes, L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC, P.grad_bf16);
-    prof_after(kKDC, st);
-    const int splits = splits_used;
-    prof_before(kKDE, st);
-    hipLaunchKernelGGL(dE_gemm_kernel<C>, dim3(tiles_n * tiles_d * splits), dim3(C::NT), 0, st, G, c, L.keep,
-                       P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits,
-                       (const int32_t*)L.hdr, L.Vc, L.g_bytes,
-                       bf_direct ? P.dE : (void*)dE32, bf_direct ? 1 : 0, L.dE_part, ch > 0 ? 1 : 0,
-                       P.accum == kAccumAtomic ? 1 : 0, (const int*)L.rowmap,
-                       (const float*)L.scale_c,
-                       smooth ? (const float*)L.csum : nullptr, r1);
-    prof_after(kKDE, st);
+    if (want_dC) {
+      prof_before(kKDC, st);
+      // vocab-tile groups dealt to the XCDs in turn: a whole number of rounds of 8
+      const int dc_groups = (cnvb + kRasterGroup - 1) / kRasterGroup;
+      const int dc_grid = 8 * kRasterGroup * tiles_d * ((dc_groups + 7) / 8);
+      hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(dc_grid), dim3(C::NT), 0, st, (const T*)G, (const T*)L.Gt,
+                         (const T*)L.Et, L.keep, L.Npad, L.Vc, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb,
+                         tiles_d, L.g_bytes, L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC,
+                         P.grad_bf16);
+      prof_after(kKDC, st);
+    }
+    if (want_dE) {
+      const int splits = splits_used;
+      prof_before(kKDE, st);
+      hipLaunchKernelGGL(dE_gemm_kernel<C>, dim3(tiles_n * tiles_d * splits), dim3(C::NT), 0, st, G, c, L.keep,
+                         P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits,
+                         (const int32_t*)L.hdr, L.Vc, L.g_bytes,
+                         bf_direct ? P.dE : (void*)dE32, bf_direct ? 1 : 0, L.dE_part, ch > 0 ? 1 : 0,
+                         P.accum == kAccumAtomic ? 1 : 0, (const int*)L.rowmap,
+                         (const float*)L.scale_c,
+                         smooth ? (const float*)L.csum : nullptr, r1);
+      prof_after(kKDE, st);
+    }
   }
   if (P.dbias) {
     prof_before(kKDbReduce, st);
@@ -1410,6 +1419,7 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   }
   const size_t n4 = (size_t)P.N * P.D / 4;  // D is a multiple of 4
   const int nparts = P.accum != kAccumAtomic ? L.splits - 1 : 0;
+  if (!want_dE) return hipGetLastError();
   if (P.grad_bf16 && !bf_direct) {
     prof_before(kKDEReduce, st);
     hipLaunchKernelGGL(dE_finish_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,

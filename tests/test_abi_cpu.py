@@ -113,13 +113,18 @@ def test_forward_argument_errors(L):
 
 def test_backward_argument_errors(L):
     assert _bwd(L, e=None) == INVALID
-    assert _bwd(L, dE=None) == INVALID
+    assert _bwd(L, dE=FAKE + 8) == INVALID          # outputs 16-byte aligned
     assert _bwd(L, bias=FAKE + 1) == INVALID
     assert _bwd(L, db=FAKE + 2) == INVALID          # dbias is float
     assert _bwd(L, ls=2.0) == INVALID and _bwd(L, zl=-1.0) == INVALID
     assert _bwd(L, flt=2) == INVALID
     assert _bwd(L, acc=5) == INVALID
     assert _bwd(L, chunk=100) == INVALID
+    # dE, dC, dbias each optional, but one of them is needed
+    assert L.cce_backward(FAKE, FAKE, None, FAKE, 64, 64, 100, 0, -100, 2, 0.0, 0.0, 0.0, FAKE, FAKE, 1, 0, 0, 0,
+                          None, None, None, FAKE, 1 << 30, None) == INVALID
+    assert L.cce_backward(FAKE, FAKE, None, FAKE, 64, 64, 100, 0, -100, 2, 0.0, 0.0, 0.0, FAKE, FAKE, 1, 0, 0, 0,
+                          None, FAKE, None, FAKE, 1024, None) == WORKSPACE
     assert _bwd(L, gdt=2) == INVALID and _bwd(L, gdt=-1) == INVALID   # grad dtype: float32 or operand
     assert _bwd(L, gdt=1, wsb=1024) == WORKSPACE
     assert _bwd(L, cap=-1.0) == INVALID

@@ -447,6 +447,52 @@ def test_softcap_with_smoothing_is_rejected(M):
         run(M, inp, "mean", backward=False, ls=0.1, cap=5.0)
 
 
+# ----------------------------------------------------------------------------- optional gradients
+@pytest.mark.parametrize("dt,accum,chunk,ls", [("bf16", "deterministic", 0, 0.0), ("bf16", "deterministic", 512, 0.1),
+                                             ("bf16", "atomic", 512, 0.0), ("f32", "deterministic", 0, 0.1)])
+def test_optional_gradients(M, dt, accum, chunk, ls):
+    """dE alone, dC alone and db alone equal the same gradients of a full
+    call (bitwise where the accumulation order is fixed)."""
+    import torch
+    inp = W.custom(530, 200, 1500, dt, seed=81, c_std=0.05, ignore_frac=0.1)
+    print(f"[optional grads] {dt} {accum} chunk={chunk} ls={ls}", flush=True)
+    e, c, t = dev(inp["e"], dt), dev(inp["c"], dt), dev_targets(inp["targets"])
+    b = dev(W.bias(1500, dt, seed=3), dt)
+    loss, lse, nv, ws = M.forward(e, c, t, vocab_chunk=chunk, bias=b, label_smoothing=ls)
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+    kw = dict(filter=True, accum=accum, vocab_chunk=chunk, bias=b, label_smoothing=ls)
+    dE, dC, db = M.backward(e, c, t, lse, g, ws, want_dbias=True, **kw)
+    dE1, none1 = M.backward(e, c, t, lse, g, ws, want_dC=False, **kw)
+    none2, dC2 = M.backward(e, c, t, lse, g, ws, want_dE=False, **kw)
+    none3, none4, db3 = M.backward(e, c, t, lse, g, ws, want_dE=False, want_dC=False, want_dbias=True, **kw)
+    torch.cuda.synchronize()
+    assert none1 is None and none2 is None and none3 is None and none4 is None
+    assert torch.equal(dC2, dC) and torch.equal(db3, db)
+    if accum == "deterministic":
+        assert torch.equal(dE1, dE)
+    else:
+        check_grad(dE1.cpu().numpy(), dE.cpu().numpy(), 1e-5, "atomic dE alone")
+
+
+def test_autograd_frozen_classifier(M):
+    """c.requires_grad = False: only e's gradient is formed (dC's contraction
+    does not run) and it matches the full gradient."""
+    import torch
+    inp = W.custom(400, 136, 1100, "bf16", seed=83, c_std=0.1, ignore_frac=0.05)
+    e = dev(inp["e"], "bf16").requires_grad_(True)
+    c = dev(inp["c"], "bf16")
+    t = dev_targets(inp["targets"])
+    M.linear_cross_entropy(e, c, t).backward()
+    assert c.grad is None and e.grad is not None and e.grad.dtype == torch.bfloat16
+    bo = O.backward(inp["e"], inp["c"], inp["targets"])
+    check_grad(e.grad.float().cpu().numpy(), bo.dE, GRAD_RTOL_FILTERED, "frozen-classifier dE")
+    c2 = dev(inp["c"], "bf16").requires_grad_(True)
+    e2 = dev(inp["e"], "bf16")
+    M.linear_cross_entropy(e2, c2, t).backward()
+    assert e2.grad is None and c2.grad is not None
+    check_grad(c2.grad.float().cpu().numpy(), bo.dC, GRAD_RTOL_FILTERED, "frozen-inputs dC")
+
+
 # ----------------------------------------------------------------------------- a plain C caller
 def test_c_caller(M):
     """tests/c_abi/cce_abi_check.c: HIP runtime memory and a non-default
