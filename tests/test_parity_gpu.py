@@ -657,6 +657,16 @@ def test_full_llama8b_padded(M):
     assert r["stats"]["tiles_kept"] <= 12 * 502
 
 
+@pytest.mark.slow
+def test_full_long8b_calibrated(M):
+    """The long-context 8B head (N = 16384): two vocabulary chunks, dE added
+    up across them, in the deterministic and the fp32-atomic modes (per-row
+    checks: the oracle's whole-vocabulary pass over 16384 rows would take
+    minutes)."""
+    _sampled_full(M, "long8b_cal", "none", False, dC_check=False)
+    _sampled_full(M, "long8b_cal", "none", False, accum="atomic", dC_check=False)
+
+
 # ----------------------------------------------------------------------------- seeded random configurations
 def _random_case(k):
     """Case k of a fixed list: shapes, dtype, reduction, filter, accumulation,
