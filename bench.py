@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--no-filter", action="store_true")
     ap.add_argument("--accum", default="deterministic", choices=["deterministic", "atomic"])
     ap.add_argument("--vocab-chunk", type=int, default=0)
+    ap.add_argument("--grad-dtype", default="operand", choices=["operand", "float32"],
+                    help="element type of dE and dC: the operands' (as the autograd path returns them) or fp32")
     ap.add_argument("--cpu-rows", type=int, default=None, help="rows of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-materialized", action="store_true",
@@ -189,7 +191,8 @@ def make_bias(V, dtype, dev, seed=7):
 
 
 def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=False, label_smoothing=0.0,
-                   z_loss=0.0, softcap=0.0, filter=True, accum="deterministic", frozen_classifier=False):
+                   z_loss=0.0, softcap=0.0, filter=True, accum="deterministic", frozen_classifier=False,
+                   grad_dtype="operand"):
     """Compact forward / forward+backward figures for one workload (defaults:
     filter on, deterministic, the workload's own reduction; with_bias adds a
     classifier bias and asks for its gradient; label_smoothing / z_loss add
@@ -219,8 +222,9 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
     nv = torch.empty(1, dtype=torch.int32, device=dev)
     g = torch.full((N,) if red == 0 else (1,), 1.0 / n_valid if red == 0 else 1.0, dtype=torch.float32,
                    device=dev)
-    dE = torch.empty((N, D), dtype=torch.float32, device=dev)
-    dC = None if frozen_classifier else torch.empty((V, D), dtype=torch.float32, device=dev)
+    gdt = tdt if grad_dtype == "operand" else torch.float32
+    dE = torch.empty((N, D), dtype=gdt, device=dev)
+    dC = None if frozen_classifier else torch.empty((V, D), dtype=gdt, device=dev)
     bias = make_bias(V, tdt, dev) if with_bias else None
     db = torch.empty(V, dtype=torch.float32, device=dev) if with_bias else None
     extra = torch.cuda.memory_allocated() - base
@@ -241,7 +245,8 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
         fwd()
         r = L.cce_backward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, softcap,
                            label_smoothing, z_loss, lse.data_ptr(), g.data_ptr(), 1 if filter else 0,
-                           0 if accum == "deterministic" else 1, 0, 0, dE.data_ptr(),
+                           0 if accum == "deterministic" else 1, 0, 1 if grad_dtype == "operand" else 0,
+                           dE.data_ptr(),
                            None if dC is None else dC.data_ptr(), dbp, ws.data_ptr(), ws.numel(), st.cuda_stream)
         if r:
             raise RuntimeError(f"cce_backward failed: {r}")
@@ -269,11 +274,12 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
            "tflops_effective": eff, "pct_of_peak": 100.0 * eff / peak,
            "tflops_useful": eff * (4.0 / 6.0 if frozen_classifier else 0.75), "filter": bool(filter),
            "accum": accum, "frozen_classifier": bool(frozen_classifier),
+           "grad_dtype": "bf16" if gdt == torch.bfloat16 else "f32",
            "tiles_skipped_frac": 1.0 - stats["tiles_kept"] / max(1, stats["tiles_total"]),
            "extra_hbm_bytes": int(extra), "bias": bool(with_bias), "label_smoothing": label_smoothing,
            "z_loss": z_loss, "softcap": softcap}
     plain = (not with_bias and label_smoothing == 0.0 and z_loss == 0.0 and softcap == 0.0 and filter
-             and accum == "deterministic" and not frozen_classifier)
+             and accum == "deterministic" and not frozen_classifier and grad_dtype == "operand")
     if w.dtype == "bf16" and plain:
         out["hipblaslt_fwd_gemm_tflops"] = hipblaslt_gemm_tflops(c, e)
     del ws, loss, lse, nv, g, dE, dC, bias, db
@@ -328,8 +334,10 @@ def main():
     # upstream gradient: for per-token loss, 1/n_valid per row (the mean's gradient)
     g = torch.full((N,) if red == 0 else (1,), 1.0 / n_valid if red == 0 else 1.0, dtype=torch.float32,
                    device=dev)
-    dE = torch.empty((N, D), dtype=torch.float32, device=dev)
-    dC = torch.empty((V, D), dtype=torch.float32, device=dev)
+    gdt = tdt if args.grad_dtype == "operand" else torch.float32
+    gcode = 1 if args.grad_dtype == "operand" else 0
+    dE = torch.empty((N, D), dtype=gdt, device=dev)
+    dC = torch.empty((V, D), dtype=gdt, device=dev)
     dcode = 0 if dt_name == "bf16" else 1
     flt = 0 if args.no_filter else 1
     acc = 0 if args.accum == "deterministic" else 1
@@ -340,7 +348,7 @@ def main():
         r1 = L.cce_forward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0, 0.0,
                            loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(), ws.numel(), s)
         r2 = L.cce_backward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0,
-                            0.0, lse.data_ptr(), g.data_ptr(), flt, acc, args.vocab_chunk, 0, dE.data_ptr(),
+                            0.0, lse.data_ptr(), g.data_ptr(), flt, acc, args.vocab_chunk, gcode, dE.data_ptr(),
                             dC.data_ptr(),
                             None, ws.data_ptr(), ws.numel(), s)
         if r1 or r2:
@@ -447,6 +455,9 @@ def main():
         # the filter off (Llama-3.2-1B) and fp32 atomic accumulation (long context)
         configs["llama1b+nofilter"] = config_summary("llama1b", filter=False, materialized_too=False)
         configs["long8b_cal+atomic"] = config_summary("long8b_cal", accum="atomic", materialized_too=False)
+        # fp32 gradient outputs
+        configs[args.workload + "+fp32_grads"] = config_summary(args.workload, grad_dtype="float32",
+                                                                materialized_too=False)
         # a frozen classifier: dE alone (dC's contraction does not run)
         configs[args.workload + "+frozen_classifier"] = config_summary(args.workload, frozen_classifier=True,
                                                                        materialized_too=False)
@@ -470,7 +481,8 @@ def main():
         "dtype": "bf16" if dt_name == "bf16" else "f32",
         "data": "synthetic (seeded; e ~ N(0,1), c ~ N(0,0.02^2) bf16, uniform targets)",
         "config": {"workload": args.workload, "N": N, "D": D, "V": V, "reduction": reduction,
-                   "filter": bool(flt), "accum": args.accum, "vocab_chunk": Vc},
+                   "filter": bool(flt), "accum": args.accum, "vocab_chunk": Vc,
+                   "grad_dtype": "bf16" if gdt == torch.bfloat16 else "f32"},
         "mfma_util_pct": 100.0 * tflops / peak,
         "tflops_effective": tflops,
         "tflops_useful": tflops * 0.75,  # 6NVD: the step without the recompute

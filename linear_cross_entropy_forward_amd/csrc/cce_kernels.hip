@@ -136,37 +136,16 @@ __device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
 }
 
-// 4x4 transpose of 16-bit values across a lane quad: on entry lane k holds
-// x[k][0..3] as d0 = x[k][0] | x[k][1] << 16, d1 = x[k][2] | x[k][3] << 16;
-// on exit it holds x[0..3][k] the same way.
-__device__ __forceinline__ void quad_transpose16(uint32_t& d0, uint32_t& d1) {
-  const int k = threadIdx.x & 3;
-  // rows {2,3} of lanes {0,1} <-> rows {0,1} of lanes {2,3}
-  const bool k2 = (k & 2) != 0, k1 = (k & 1) != 0;
-  const uint32_t rcv = quad_xor2(k2 ? d0 : d1);
-  d0 = k2 ? rcv : d0;
-  d1 = k2 ? d1 : rcv;
-  // 16-bit halves between neighbouring lanes (v_perm_b32 byte selects)
-  const uint32_t p0 = quad_xor1(d0), p1 = quad_xor1(d1);
-  d0 = k1 ? __builtin_amdgcn_perm(d0, p0, 0x07060302u) : __builtin_amdgcn_perm(p0, d0, 0x05040100u);
-  d1 = k1 ? __builtin_amdgcn_perm(d1, p1, 0x07060302u) : __builtin_amdgcn_perm(p1, d1, 0x05040100u);
-}
-
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
-// Transposed store of the 4x4 fp32 block held by a lane quad.  Lane k holds
-// x[k][0..3], four consecutive rows of its own column (the accumulator
-// layout); after two quad exchanges it holds x[0..3][k] and writes them as
-// four consecutive columns of row k (one 16-byte store).  `off_row0` is the
-// byte offset of (row 0, the quad's first column), `ld` the row pitch in bytes.
-__device__ __forceinline__ void store_quad_t(rsrc_t r, uint32_t off_row0, uint32_t ld, const float (&x)[4],
-                                             const float*) {
+// 4x4 transpose of 32-bit values across a lane quad: on entry lane k holds
+// d[u] = x[k][u] (in the accumulator layout: four consecutive rows u of the
+// lane's own column k), on exit d[u] = x[u][k] (row k, four consecutive
+// columns u), after two quad exchanges.
+__device__ __forceinline__ void quad_transpose(uint32_t (&d)[4]) {
   const int k = threadIdx.x & 3;
-  uint32_t d[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) d[u] = __builtin_bit_cast(uint32_t, x[u]);
   // rows {2,3} of lanes {0,1} <-> rows {0,1} of lanes {2,3}
   const bool k2 = (k & 2) != 0, k1 = (k & 1) != 0;
   {
@@ -186,7 +165,20 @@ __device__ __forceinline__ void store_quad_t(rsrc_t r, uint32_t off_row0, uint32
     d[1] = k1 ? d[1] : s0;
     d[3] = k1 ? d[3] : s1;
   }
-  __builtin_amdgcn_raw_buffer_store_b128(u32x4{d[0], d[1], d[2], d[3]}, r, off_row0 + (uint32_t)k * ld, 0, 0);
+}
+
+// Transposed store of the 4x4 fp32 block held by a lane quad (see
+// quad_transpose): lane k writes row k, the quad's four columns, as one
+// 16-byte store.  `off_row0` is the byte offset of (row 0, the quad's first
+// column), `ld` the row pitch in bytes.
+__device__ __forceinline__ void store_quad_t(rsrc_t r, uint32_t off_row0, uint32_t ld, const float (&x)[4],
+                                             const float*) {
+  uint32_t d[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) d[u] = __builtin_bit_cast(uint32_t, x[u]);
+  quad_transpose(d);
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{d[0], d[1], d[2], d[3]}, r,
+                                         off_row0 + (uint32_t)(threadIdx.x & 3) * ld, 0, 0);
 }
 
 // ============================================================================
@@ -1011,18 +1003,33 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
     const int d = d0 + am.colj(fn);
     add[fn] = (r1c && d < D) ? r1c[d] : 0.f;
   }
+  // Each lane quad transposes its 4x4 blocks (four rows of four columns),
+  // so a lane writes four consecutive columns of one row: one 16-byte (fp32)
+  // or 8-byte (bf16) store instead of four.  D is a multiple of 4: a quad's
+  // columns are all inside or all outside.
+  const int k = (int)threadIdx.x & 3;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
-      const int d = d0 + am.colj(fn);
+      const int dq = d0 + (am.colj(fn) & ~3);  // the quad's first column
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int vr = am.row(fm, r);
-        const bool ok = d < D && vl0 + vr < clen;
-        const uint32_t e = (uint32_t)vr * (uint32_t)D + (uint32_t)d;
-        if (out_bf16) stbf_nt(ro, ok ? e * 2u : kOOB, acc[fm][fn][r] + add[fn]);
-        else stf_nt(ro, ok ? e * 4u : kOOB, acc[fm][fn][r] + add[fn]);
+      for (int q = 0; q < 4; ++q) {
+        uint32_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = __builtin_bit_cast(uint32_t, acc[fm][fn][4 * q + u] + add[fn]);
+        quad_transpose(x);
+        const int vr = am.row(fm, 4 * q) + k;
+        const bool ok = dq < D && vl0 + vr < clen;
+        const uint32_t e = (uint32_t)vr * (uint32_t)D + (uint32_t)dq;
+        if (out_bf16) {
+          const u32x2 b = {pack_bf16(__builtin_bit_cast(float, x[0]), __builtin_bit_cast(float, x[1])),
+                           pack_bf16(__builtin_bit_cast(float, x[2]), __builtin_bit_cast(float, x[3]))};
+          __builtin_amdgcn_raw_buffer_store_b64(b, ro, ok ? e * 2u : kOOB, 0, kStoreNT);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{x[0], x[1], x[2], x[3]}, ro, ok ? e * 4u : kOOB, 0,
+                                                 kStoreNT);
+        }
       }
     }
 }
