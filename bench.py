@@ -38,10 +38,10 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "31ffcecaa534aaa0cb94092bf3b98dd5bb2edb073a03c19999c573c21f05b924",
+    "source_sha256": "7fcd20a93189c714333b614eba9270d2be8e06a0b7c259d1f2997b340a2a0d40",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9079.9e6, "grad_tile": 10551.9e6, "dC_gemm": 8413.0e6, "dE_gemm": 6591.8e6,
+        "fwd_tile": 9340.5e6, "grad_tile": 10901.9e6, "dC_gemm": 7501.6e6, "dE_gemm": 7535.9e6,
         "rows": 121.4e6, "filter": 3.3e6, "transpose_e": 67.3e6,
     },
 }
