@@ -192,7 +192,7 @@ def make_bias(V, dtype, dev, seed=7):
 
 def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=False, label_smoothing=0.0,
                    z_loss=0.0, softcap=0.0, filter=True, accum="deterministic", frozen_classifier=False,
-                   grad_dtype="operand"):
+                   grad_dtype="operand", graph=False):
     """Compact forward / forward+backward figures for one workload (defaults:
     filter on, deterministic, the workload's own reduction; with_bias adds a
     classifier bias and asks for its gradient; label_smoothing / z_loss add
@@ -235,9 +235,10 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
     dbp = db.data_ptr() if with_bias else None
 
     def fwd():
+        # on the current stream (a graph capture runs on its own)
         r = L.cce_forward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, softcap,
                           label_smoothing, z_loss, loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(),
-                          ws.numel(), st.cuda_stream)
+                          ws.numel(), torch.cuda.current_stream().cuda_stream)
         if r:
             raise RuntimeError(f"cce_forward failed: {r}")
 
@@ -247,7 +248,8 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
                            label_smoothing, z_loss, lse.data_ptr(), g.data_ptr(), 1 if filter else 0,
                            0 if accum == "deterministic" else 1, 0, 1 if grad_dtype == "operand" else 0,
                            dE.data_ptr(),
-                           None if dC is None else dC.data_ptr(), dbp, ws.data_ptr(), ws.numel(), st.cuda_stream)
+                           None if dC is None else dC.data_ptr(), dbp, ws.data_ptr(), ws.numel(),
+                           torch.cuda.current_stream().cuda_stream)
         if r:
             raise RuntimeError(f"cce_backward failed: {r}")
 
@@ -265,6 +267,19 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
 
     step_ms = timed(step)
     fwd_ms = timed(fwd)
+    graph_ms = None
+    if graph:
+        # the same step captured once in a HIP graph and replayed (no launch
+        # overhead per kernel; the library's calls are capture-safe)
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        with torch.cuda.stream(side):
+            step()
+        st.wait_stream(side)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        graph_ms = timed(gr.replay)
     stats = M.read_stats(ws, N, V)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     # effective work: 2NVD per contraction (forward, recompute, dE, dC)
@@ -274,7 +289,7 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
            "tflops_effective": eff, "pct_of_peak": 100.0 * eff / peak,
            "tflops_useful": eff * (4.0 / 6.0 if frozen_classifier else 0.75), "filter": bool(filter),
            "accum": accum, "frozen_classifier": bool(frozen_classifier),
-           "grad_dtype": "bf16" if gdt == torch.bfloat16 else "f32",
+           "grad_dtype": "bf16" if gdt == torch.bfloat16 else "f32", "step_ms_graph": graph_ms,
            "tiles_skipped_frac": 1.0 - stats["tiles_kept"] / max(1, stats["tiles_total"]),
            "extra_hbm_bytes": int(extra), "bias": bool(with_bias), "label_smoothing": label_smoothing,
            "z_loss": z_loss, "softcap": softcap}
@@ -444,7 +459,7 @@ def main():
         configs = {}
         for name in ("tiny", "llama1b", "gemma2b", "gemma2b_cal", "long8b", "long8b_cal", "llama8b_pad25"):
             if name != args.workload:
-                configs[name] = config_summary(name)
+                configs[name] = config_summary(name, graph=name == "tiny")
         # the headline workload with a classifier bias and its gradient
         configs[args.workload + "+bias"] = config_summary(args.workload, with_bias=True)
         # ... and with label smoothing 0.1 and z-loss 1e-4

@@ -493,6 +493,55 @@ def test_autograd_frozen_classifier(M):
     check_grad(c2.grad.float().cpu().numpy(), bo.dC, GRAD_RTOL_FILTERED, "frozen-inputs dC")
 
 
+# ----------------------------------------------------------------------------- HIP graph capture
+def test_hip_graph_capture(M):
+    """A forward+backward step captured in a HIP graph (torch.cuda.graph) and
+    replayed: forward and backward allocate, free, synchronise and memset
+    nothing, so the capture holds their kernels alone.  Each replay, with new
+    inputs copied in and eager work in between, equals the eager step
+    bitwise (deterministic mode), and the first matches the oracle."""
+    import torch
+    dt = "bf16"
+    inps = [W.custom(300, 136, 1100, dt, seed=s, c_std=0.1, ignore_frac=0.05) for s in (91, 92, 93)]
+    e, c, t = dev(inps[0]["e"], dt), dev(inps[0]["c"], dt), dev_targets(inps[0]["targets"])
+    N, D = e.shape
+    V = c.shape[0]
+    ws = torch.empty(M.workspace_size(N, D, V, e.dtype), dtype=torch.uint8, device="cuda")
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+
+    def step():
+        loss, lse, _, _ = M.forward(e, c, t, ws=ws)
+        dE, dC = M.backward(e, c, t, lse, g, ws, filter=True)
+        return loss, lse, dE, dC
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = step()
+    print("[graph] captured", flush=True)
+    for k, inp in enumerate(inps * 2):
+        e.copy_(dev(inp["e"], dt))
+        c.copy_(dev(inp["c"], dt))
+        t.copy_(dev_targets(inp["targets"]))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [x.clone() for x in out]
+        ref = step()
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"replay {k} differs from the eager step"
+        if k == 0:
+            fo = O.forward(inp["e"], inp["c"], inp["targets"])
+            check_loss(got[0].cpu().numpy(), fo.loss, "mean", "graph replay", fo.n_valid)
+            bo = O.backward(inp["e"], inp["c"], inp["targets"])
+            check_grad(got[2].cpu().numpy(), bo.dE, GRAD_RTOL_FILTERED, "graph replay dE")
+            check_grad(got[3].cpu().numpy(), bo.dC, GRAD_RTOL_FILTERED, "graph replay dC")
+
+
 # ----------------------------------------------------------------------------- a plain C caller
 def test_c_caller(M):
     """tests/c_abi/cce_abi_check.c: HIP runtime memory and a non-default
