@@ -597,17 +597,20 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int64_t* __restric
 }
 
 // ============================================================================
-// Backward: tile keep map.  Work-group = one token block x 256 vocab blocks.
+// Backward: tile keep map.  Work-group = one token block x 64 vocab blocks.
 // ============================================================================
-__global__ __launch_bounds__(256) void filter_kernel(const int64_t* __restrict__ targets,
+__global__ __launch_bounds__(1024) void filter_kernel(const int64_t* __restrict__ targets,
                                                      const float* __restrict__ lse,
                                                      const float2* __restrict__ part, const int* __restrict__ rowmap,
-                                                     int N, int V, int nVB, int64_t ignore_index, int Bn, int Bv,
-                                                     int PW, int nvb_t, int filter,
-                                                     uint8_t* __restrict__ keep, int32_t* __restrict__ hdr) {
-  __shared__ float s_lse[kTileN];
-  __shared__ int s_tb[kTileN], s_row[kTileN];
+                                                     int N, int V, int nVB, int64_t ignore_index, int nvb_t,
+                                                     int filter, uint8_t* __restrict__ keep,
+                                                     int32_t* __restrict__ hdr) {
+  constexpr int Bn = kTileN, PPB = kTileV / kPartialWidth;  // partial blocks per vocab tile
+  __shared__ float s_lse[Bn];
+  __shared__ int s_tb[Bn], s_row[Bn];
   __shared__ int s_any;
+  constexpr int NW = 16;  // waves
+  __shared__ uint8_t s_k[NW][64];
   const int b = blockIdx.y;  // block of compacted token slots
   const int tid = threadIdx.x;
   if (tid == 0) s_any = 0;
@@ -623,7 +626,7 @@ __global__ __launch_bounds__(256) void filter_kernel(const int64_t* __restrict__
         s_any = 1;
         if (t >= 0 && t < V) {
           l = lse[i];
-          tb = (int)(t / Bv);
+          tb = (int)(t / kTileV);
         }
       }
     }
@@ -632,28 +635,50 @@ __global__ __launch_bounds__(256) void filter_kernel(const int64_t* __restrict__
     s_row[r] = i;
   }
   __syncthreads();
-  const int vb = blockIdx.x * blockDim.x + tid;
+  // lane = vocab block (a wave reads consecutive partials of one row), wave w
+  // = rows w, w + 16, ...: all sixteen rows' loads in flight at once; the
+  // sixteen waves' answers are then combined
+  const int lane = tid & 63, w = tid >> 6;
+  const int vb = blockIdx.x * 64 + lane;
   bool k = false;
-  if (vb < nvb_t) {
-    if (!filter) {
-      k = s_any != 0;  // a block of ignored rows only has G = 0: never computed
-    } else {
-      const int ppb = Bv / PW;
-      const float thr = -12.0f * kLn2;
-      for (int r = 0; r < Bn && !k; ++r) {
-        if (s_tb[r] == vb) { k = true; break; }
-        if (s_tb[r] < 0) continue;
-        const float2* p = part + (size_t)s_row[r] * nVB + (size_t)vb * ppb;
-        float m = -INFINITY;
-        for (int q = 0; q < ppb; ++q)
-          if (vb * ppb + q < nVB) m = fmaxf(m, p[q].x);
-        if (m - s_lse[r] >= thr) k = true;
+  if (!filter) {
+    k = s_any != 0;  // a block of ignored rows only has G = 0: never computed
+  } else if (vb < nvb_t) {
+    const float thr = -12.0f * kLn2;
+    constexpr int U = Bn / NW;
+    static_assert(Bn % NW == 0, "rows per wave");
+    {
+      const int r0 = w;
+      float m[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + NW * u;
+        m[u] = -INFINITY;
+        if (r < Bn && s_tb[r] >= 0) {
+          const float2* p = part + (size_t)s_row[r] * nVB + (size_t)vb * PPB;
+#pragma unroll
+          for (int q = 0; q < PPB; ++q)
+            if (vb * PPB + q < nVB) m[u] = fmaxf(m[u], p[q].x);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + NW * u;
+        if (r < Bn && s_tb[r] >= 0 && (s_tb[r] == vb || m[u] - s_lse[r] >= thr)) k = true;
       }
     }
-    keep[(size_t)b * nvb_t + vb] = k ? 1 : 0;
   }
-  const uint64_t bal = __ballot(k);
-  if ((tid & 63) == 0) atomicAdd(&hdr[kHdrTilesKept], (int)__popcll(bal));
+  s_k[w][lane] = k ? 1 : 0;
+  __syncthreads();
+  if (w == 0) {
+    int any = 0;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) any |= s_k[x][lane];
+    const bool kk = any != 0 && vb < nvb_t;
+    if (vb < nvb_t) keep[(size_t)b * nvb_t + vb] = kk ? 1 : 0;
+    const uint64_t bal = __ballot(kk);
+    if (lane == 0) atomicAdd(&hdr[kHdrTilesKept], (int)__popcll(bal));
+  }
 }
 
 // ============================================================================
@@ -1347,9 +1372,9 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   // -eps/V * sum_i scale_i e_i: the smoothing share of every dC row
   if (smooth && want_dC) launch_colsum<T>(e, L.scale, P.N, P.D, r1, L, L.r1c, st);
   prof_before(kKFilter, st);
-  hipLaunchKernelGGL(filter_kernel, dim3((L.nvb_t + 255) / 256, L.nb), dim3(256), 0, st, P.targets, P.lse,
-                     L.part, (const int*)L.rowmap, P.N, P.V, L.nVB, P.ignore_index, kTileN, kTileV, kPartialWidth, L.nvb_t, P.filter,
-                     L.keep, L.hdr);
+  hipLaunchKernelGGL(filter_kernel, dim3((L.nvb_t + 63) / 64, L.nb), dim3(1024), 0, st, P.targets, P.lse,
+                     L.part, (const int*)L.rowmap, P.N, P.V, L.nVB, P.ignore_index, L.nvb_t, P.filter, L.keep,
+                     L.hdr);
   prof_after(kKFilter, st);
   prof_before(kKTileList, st);
   hipLaunchKernelGGL(tile_list_kernel, dim3(L.nchunks), dim3(1024), 0, st, (const uint8_t*)L.keep, L.nvb_t,
