@@ -542,6 +542,40 @@ def test_hip_graph_capture(M):
             check_grad(got[3].cpu().numpy(), bo.dC, GRAD_RTOL_FILTERED, "graph replay dC")
 
 
+# ----------------------------------------------------------------------------- two streams at once
+def test_concurrent_streams(M):
+    """The library keeps no mutable state of its own: two problems with their
+    own workspaces, run at the same time on two streams (default priority),
+    give the same results as one after the other."""
+    import torch
+    cases = [W.custom(600, 136, 1100, "bf16", seed=101, c_std=0.1, ignore_frac=0.05),
+             W.custom(300, 200, 2600, "bf16", seed=102, c_std=0.05, ignore_frac=0.1)]
+    tens = [(dev(x["e"], "bf16"), dev(x["c"], "bf16"), dev_targets(x["targets"])) for x in cases]
+    g = torch.ones(1, dtype=torch.float32, device="cuda")
+
+    def step(e, c, t):
+        loss, lse, _, ws = M.forward(e, c, t)
+        dE, dC = M.backward(e, c, t, lse, g, ws, filter=True)
+        return loss, lse, dE, dC
+
+    serial = [step(*x) for x in tens]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        for s, x in zip(streams, tens):
+            with torch.cuda.stream(s):
+                outs.append((s, step(*x)))
+    torch.cuda.synchronize()
+    print("[streams] done", flush=True)
+    for k, (s, got) in enumerate(outs):
+        want = serial[k % 2]
+        for a, b in zip(got, want):
+            assert torch.equal(a, b), f"stream run {k} differs"
+
+
 # ----------------------------------------------------------------------------- a plain C caller
 def test_c_caller(M):
     """tests/c_abi/cce_abi_check.c: HIP runtime memory and a non-default
