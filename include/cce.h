@@ -47,7 +47,12 @@
  *    workspace, and keeps them alive until the stream work completes.
  *  - Layout: row-major, contiguous, base pointers 16-byte aligned.  e is
  *    [N, D], c is [V, D] (D contiguous); e and c share one dtype; outputs are
- *    float32.  D must be a multiple of 8 (bf16) or 4 (float32).
+ *    float32 (dE, dC: see cce_backward).  D must be a multiple of 8 (bf16)
+ *    or 4 (float32); D and V are positive.
+ *  - An empty batch (N = 0) is valid: e, targets, lse, a per-row loss, dE and
+ *    grad_loss have no elements and may be NULL; the forward writes n_valid 0
+ *    and a sum or mean of 0 (the mean's count is floored at 1), the backward
+ *    writes dC and dbias as zeros.
  *  - Errors: argument and size faults are reported synchronously, before any
  *    launch, as a negative cce_status (label_smoothing outside [0, 1] or a
  *    negative or non-finite z_loss is CCE_ERR_INVALID_ARG).  A target outside [0, V) that is not

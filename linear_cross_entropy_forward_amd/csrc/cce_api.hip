@@ -16,6 +16,7 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk, void* base) {
   Layout L{};
+  if (N < 1) N = 1;  // an empty batch uses only the counters; sized like one row
   const size_t es = dtype == kDtypeBf16 ? 2 : 4;
   L.nVB = (int)((V + kPartialWidth - 1) / kPartialWidth);
   L.Npad = (int)((N + kTileN - 1) / kTileN * kTileN);
@@ -122,8 +123,9 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static cce_status check_common(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D,
                                int64_t V, int dtype, int reduction, float softcap, const void* ws,
                                int64_t vocab_chunk) {
-  if (!e || !c || !targets || !ws) return CCE_ERR_INVALID_ARG;
-  if (N <= 0 || D <= 0 || V <= 0) return CCE_ERR_INVALID_ARG;
+  // an empty batch (N = 0) may pass null e and targets
+  if (!c || !ws || (N > 0 && (!e || !targets))) return CCE_ERR_INVALID_ARG;
+  if (N < 0 || D <= 0 || V <= 0) return CCE_ERR_INVALID_ARG;
   if (dtype != kDtypeBf16 && dtype != kDtypeF32) return CCE_ERR_INVALID_ARG;
   if (reduction != kReductionNone && reduction != kReductionSum && reduction != kReductionMean)
     return CCE_ERR_INVALID_ARG;
@@ -186,13 +188,13 @@ using namespace cce;
 extern "C" {
 
 size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk) {
-  if (N <= 0 || D <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
+  if (N < 0 || D <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
   if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return 0;
   return make_layout(N, D, V, dtype, vocab_chunk, nullptr).total;
 }
 
 int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk) {
-  if (N <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
+  if (N < 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
   if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return 0;
   return make_layout(N, 1, V, dtype, vocab_chunk, nullptr).Vc;
 }
@@ -214,12 +216,18 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
   if (st != CCE_OK) return st;
   if (!bias_ok(bias, dtype) || !terms_ok(label_smoothing, z_loss)) return CCE_ERR_INVALID_ARG;
   if (softcap > 0.0f && label_smoothing > 0.0f) return CCE_ERR_UNSUPPORTED;
-  if (!loss || !lse) return CCE_ERR_INVALID_ARG;
+  // with N = 0, lse and a per-row loss have no elements (may be null)
+  if ((N > 0 && !lse) || ((N > 0 || reduction != kReductionNone) && !loss)) return CCE_ERR_INVALID_ARG;
   // The forward only touches the leading (chunk-independent) part of the
   // layout; any workspace sized for some vocab_chunk is large enough for it.
   Layout L = make_layout(N, D, V, dtype, kTileV, ws);
   const size_t need = (size_t)((char*)L.scale - (char*)ws);
   if (ws_bytes < need) return CCE_ERR_WORKSPACE;
+  if (N == 0) {
+    const hipError_t err = launch_empty(L, reduction == kReductionNone ? nullptr : loss, n_valid, nullptr, 0,
+                                        nullptr, 0, (hipStream_t)stream);
+    return err == hipSuccess ? CCE_OK : CCE_ERR_HIP;
+  }
   if (reduction == kReductionNone) L.nll_out = loss;
   Problem P{};
   P.e = e;
@@ -253,13 +261,21 @@ cce_status cce_backward(const void* e, const void* c, const void* bias, const in
     return CCE_ERR_INVALID_ARG;
   if (softcap > 0.0f && label_smoothing > 0.0f) return CCE_ERR_UNSUPPORTED;
   // each gradient is optional (null: not formed), at least one is asked for
-  if (!lse || !grad_loss || (!dE && !dC && !dbias)) return CCE_ERR_INVALID_ARG;
+  if ((N > 0 && (!lse || !grad_loss)) || (!dE && !dC && !dbias)) return CCE_ERR_INVALID_ARG;
   if ((filter != 0 && filter != 1) || (accum != kAccumDeterministic && accum != kAccumAtomic))
     return CCE_ERR_INVALID_ARG;
   if (grad_dtype != CCE_GRAD_FLOAT32 && grad_dtype != CCE_GRAD_OPERAND) return CCE_ERR_INVALID_ARG;
   if ((dE && !aligned16(dE)) || (dC && !aligned16(dC))) return CCE_ERR_INVALID_ARG;
   Layout L = make_layout(N, D, V, dtype, vocab_chunk, ws);
   if (ws_bytes < L.total) return CCE_ERR_WORKSPACE;
+  if (N == 0) {
+    // no rows: dC and db are zero (the smoothing term included), dE is empty
+    const size_t ges = grad_dtype == CCE_GRAD_OPERAND && dtype == kDtypeBf16 ? 2 : 4;
+    const hipError_t err =
+        launch_empty(L, nullptr, nullptr, dC, dC ? (size_t)V * (size_t)D * ges : 0, dbias, (size_t)V,
+                     (hipStream_t)stream);
+    return err == hipSuccess ? CCE_OK : CCE_ERR_HIP;
+  }
   Problem P{};
   P.e = e;
   P.c = c;
@@ -288,7 +304,7 @@ cce_status cce_backward(const void* e, const void* c, const void* bias, const in
 
 cce_status cce_read_stats(const void* ws, size_t ws_bytes, int64_t N, int64_t V, cce_stream_t stream,
                           cce_stats* out) {
-  if (!ws || !out || ws_bytes < (size_t)kHdrWords * 4 || N <= 0 || V <= 0) return CCE_ERR_INVALID_ARG;
+  if (!ws || !out || ws_bytes < (size_t)kHdrWords * 4 || N < 0 || V <= 0) return CCE_ERR_INVALID_ARG;
   int32_t h[kHdrWords];
   if (hipMemcpyAsync(h, ws, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
     return CCE_ERR_HIP;

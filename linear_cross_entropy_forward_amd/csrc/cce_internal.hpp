@@ -117,6 +117,11 @@ void prof_before(int id, hipStream_t st);
 void prof_after(int id, hipStream_t st);
 
 hipError_t launch_forward(const Problem& P, const Layout& L, hipStream_t st);
+// An empty batch (N = 0): zero counters, the reduced loss (when given), n_valid
+// (when given), `gbytes` bytes at `g` (dC; a multiple of 16) and `nb` floats at
+// `b` (db).
+hipError_t launch_empty(const Layout& L, float* loss, int32_t* n_valid, void* g, size_t gbytes, float* b, size_t nb,
+                        hipStream_t st);
 hipError_t launch_backward(const Problem& P, const Layout& L, hipStream_t st);
 
 }  // namespace cce

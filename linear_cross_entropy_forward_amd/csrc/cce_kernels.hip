@@ -1349,6 +1349,34 @@ static hipError_t launch_forward_t(const Problem& P, const Layout& L, hipStream_
   return hipGetLastError();
 }
 
+// An empty batch: the counters, the reduced loss (no term: 0 for sum, and
+// for mean with its count floored at 1) and n_valid.
+__global__ __launch_bounds__(64) void empty_batch_kernel(int32_t* __restrict__ hdr, float* __restrict__ loss,
+                                                        int32_t* __restrict__ n_valid) {
+  if (threadIdx.x < kHdrWords) hdr[threadIdx.x] = 0;
+  if (threadIdx.x == 0) {
+    if (loss) loss[0] = 0.f;
+    if (n_valid) n_valid[0] = 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_u32x4_kernel(u32x4* __restrict__ p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_empty(const Layout& L, float* loss, int32_t* n_valid, void* g, size_t gbytes, float* b, size_t nb,
+                        hipStream_t st) {
+  static_assert(kHdrWords <= 64, "one wave clears the counters");
+  hipLaunchKernelGGL(empty_batch_kernel, dim3(1), dim3(64), 0, st, L.hdr, loss, n_valid);
+  if (g && gbytes) {
+    const size_t n = gbytes / 16;
+    hipLaunchKernelGGL(zero_u32x4_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, (u32x4*)g, n);
+  }
+  if (b && nb) hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, b, nb);
+  return hipGetLastError();
+}
+
 hipError_t launch_forward(const Problem& P, const Layout& L, hipStream_t st) {
   return P.dtype == kDtypeBf16 ? launch_forward_t<CfgBf16>(P, L, st) : launch_forward_t<CfgF32>(P, L, st);
 }

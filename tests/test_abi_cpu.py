@@ -46,7 +46,8 @@ def test_status_strings_and_tiles(L):
 
 def test_workspace_size(L):
     ws = L.cce_workspace_size
-    assert ws(0, 64, 100, 0, 0) == 0 and ws(4, 64, 100, 7, 0) == 0 and ws(4, 64, 100, 0, 100) == 0
+    assert ws(-1, 64, 100, 0, 0) == 0 and ws(4, 64, 100, 7, 0) == 0 and ws(4, 64, 100, 0, 100) == 0
+    assert ws(0, 64, 100, 0, 0) > 0  # an empty batch: the counters
     a = ws(4096, 4096, 128256, 0, 0)
     b = ws(4096, 4096, 128256, 0, 1024)
     assert a > b > 0
@@ -58,7 +59,7 @@ def test_workspace_size(L):
 
 def test_vocab_chunk(L):
     vc = L.cce_vocab_chunk
-    assert vc(0, 100, 0, 0) == 0 and vc(4, 100, 7, 0) == 0 and vc(4, 100, 0, 100) == 0
+    assert vc(-1, 100, 0, 0) == 0 and vc(4, 100, 7, 0) == 0 and vc(4, 100, 0, 100) == 0
     d = vc(4096, 128256, 0, 0)
     assert d % 256 == 0 and 256 <= d <= 128256 + 255
     # the default keeps a chunk's gradient tiles within 2 GiB, each buffer
@@ -90,7 +91,10 @@ def test_forward_argument_errors(L):
     assert _fwd(L, loss=None) == INVALID
     assert _fwd(L, lse=None) == INVALID
     assert _fwd(L, ws=None) == INVALID
-    assert _fwd(L, N=0) == INVALID and _fwd(L, D=-1) == INVALID and _fwd(L, V=0) == INVALID
+    assert _fwd(L, N=-1) == INVALID and _fwd(L, D=-1) == INVALID and _fwd(L, V=0) == INVALID
+    # an empty batch is valid (null e / targets allowed); its size checks still apply
+    assert _fwd(L, N=0, e=None, t=None, lse=None, wsb=16) == WORKSPACE
+    assert L.cce_workspace_size(0, 64, 100, 0, 0) > 0 and L.cce_workspace_size(-1, 64, 100, 0, 0) == 0
     assert _fwd(L, dt=2) == INVALID
     assert _fwd(L, red=3) == INVALID
     assert _fwd(L, e=FAKE + 4) == INVALID            # misaligned

@@ -820,3 +820,16 @@ def test_filter_tiles_skip_ignored_rows():
                        atol=1e-15)
     assert np.allclose(O.dE_rows(e, c, t, [0, 3, 21], keep=keep, tile=(Bn, Bv), **kw), a.dE[[0, 3, 21]],
                        rtol=1e-12, atol=1e-15)
+
+
+def test_empty_batch_is_an_empty_sum():
+    """N = 0: every reduction is an empty sum (the mean's count is floored at
+    1, Loss functions page, "Code"), so the loss is 0 and dC, db are 0."""
+    c = np.random.default_rng(3).standard_normal((50, 8))
+    e0, t0 = np.zeros((0, 8)), np.zeros(0, np.int64)
+    for red in ("mean", "sum"):
+        f = O.forward(e0, c, t0, reduction=red)
+        assert f.loss == 0.0 and f.n_valid == 0
+    assert O.forward(e0, c, t0, reduction="none").loss.shape == (0,)
+    b = O.backward(e0, c, t0, reduction="mean", label_smoothing=0.1, bias=np.zeros(50))
+    assert b.dE.shape == (0, 8) and not b.dC.any() and not b.db.any()

@@ -542,6 +542,37 @@ def test_hip_graph_capture(M):
             check_grad(got[3].cpu().numpy(), bo.dC, GRAD_RTOL_FILTERED, "graph replay dC")
 
 
+# ----------------------------------------------------------------------------- an empty batch
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_empty_batch(M, dt):
+    """N = 0: loss 0 for sum and mean, an empty per-row loss, n_valid 0, dC and
+    db exactly 0 (through the C ABI and through autograd)."""
+    import torch
+    inp = W.custom(8, 64, 1100, dt, seed=111, c_std=0.1)
+    c = dev(inp["c"], dt)
+    b = dev(W.bias(1100, dt, seed=4), dt)
+    tdt = c.dtype
+    e = torch.empty((0, 64), dtype=tdt, device="cuda")
+    t = torch.empty(0, dtype=torch.int64, device="cuda")
+    for red in ("mean", "sum", "none"):
+        loss, lse, nv, ws = M.forward(e, c, t, reduction=red, bias=b, label_smoothing=0.1)
+        g = torch.ones(1 if red != "none" else 0, dtype=torch.float32, device="cuda")
+        dE, dC, db = M.backward(e, c, t, lse, g, ws, reduction=red, bias=b, want_dbias=True, label_smoothing=0.1)
+        torch.cuda.synchronize()
+        assert int(nv.item()) == 0 and lse.shape == (0,)
+        if red == "none":
+            assert loss.shape == (0,)
+        else:
+            assert float(loss) == 0.0
+        assert dE.shape == (0, 64) and not dC.any() and not db.any()
+        assert M.read_stats(ws, 0, 1100)["tiles_kept"] == 0
+    er = torch.empty((0, 64), dtype=tdt, device="cuda", requires_grad=True)
+    cr = c.clone().requires_grad_(True)
+    loss = M.linear_cross_entropy(er, cr, t)
+    loss.backward()
+    assert float(loss.detach()) == 0.0 and er.grad.shape == (0, 64) and not cr.grad.any()
+
+
 # ----------------------------------------------------------------------------- two streams at once
 def test_concurrent_streams(M):
     """The library keeps no mutable state of its own: two problems with their
