@@ -56,23 +56,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
 __device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
-__device__ __forceinline__ float ldf(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ __forceinline__ void stf(rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
-}
 // Cache-policy bit of a buffer store: non-temporal (streaming).  Used for
 // outputs written once and not read again soon (the gradient tiles, dC): the
 // writes then leave the caches sooner, measured faster for these bursts.
 constexpr int kStoreNT = 2;
-__device__ __forceinline__ void stf_nt(rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kStoreNT);
-}
-// One value rounded to bf16 (to nearest even), non-temporal 16-bit store.
-__device__ __forceinline__ void stbf_nt(rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)v), r, off, 0, kStoreNT);
-}
 __device__ __forceinline__ void st64(rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
