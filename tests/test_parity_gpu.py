@@ -781,6 +781,14 @@ def test_full_long8b_calibrated(M):
     _sampled_full(M, "long8b_cal", "none", False, accum="atomic", dC_check=False)
 
 
+@pytest.mark.slow
+def test_full_wide_head(M):
+    """D = 8192 with V = 128256: the classifier (2.1 GB of bf16) just under the
+    2^31-byte reach of one buffer descriptor, K loops of 128 steps, 32 tiles
+    across D; filtered, per-row and reduced checks."""
+    _sampled_full(M, "wide8192", "mean", True, n_rows=32, n_vocab=16)
+
+
 # ----------------------------------------------------------------------------- seeded random configurations
 def _random_case(k):
     """Case k of a fixed list: shapes, dtype, reduction, filter, accumulation,

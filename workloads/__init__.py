@@ -118,6 +118,9 @@ WORKLOADS: dict[str, Workload] = {
     "long8b_cal": Workload("long8b_cal", 16384, 4096, 128256, "bf16", "calibrated", 1.0, 0.02, "zipf", 0.03, 5),
     # the 8B head with a quarter of the rows padding (variable-length batches)
     "llama8b_pad25": Workload("llama8b_pad25", 4096, 4096, 128256, "bf16", "normal", 1.0, 0.02, "uniform", 0.25, 6),
+    # the widest head the 32-bit buffer offsets take whole: D = 8192 (a 70B-class
+    # model), the classifier 2.1 GB, just under 2^31 bytes
+    "wide8192": Workload("wide8192", 1024, 8192, 128256, "bf16", "normal", 1.0, 0.02, "uniform", 0.05, 7),
 }
 
 
