@@ -414,7 +414,7 @@ def main():
     tflops = eff_flops / (ms_step * 1e-3) / 1e12
 
     # chunk lengths of the backward, for per-launch algorithmic work
-    Vc = M.vocab_chunk(N, V, tdt, args.vocab_chunk)
+    Vc = M.vocab_chunk(N, D, V, tdt, args.vocab_chunk)
     chunk_lens = [min(Vc, V - s) for s in range(0, V, Vc)]
     nVB = -(-V // 128)
     kernels = {}

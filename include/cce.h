@@ -120,9 +120,12 @@ size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vo
  * Vocabulary entries per chunk that cce_backward uses for this problem and
  * vocab_chunk argument (the default when vocab_chunk = 0; the value passed,
  * clamped to the vocabulary, otherwise).  The backward launches its gradient
- * kernels once per chunk.  Returns 0 for invalid arguments.
+ * kernels once per chunk.  The default also keeps a chunk's classifier rows
+ * (chunk * D elements) under 2^31 bytes, the reach of one buffer descriptor,
+ * so a classifier of any size (V * D elements) is taken in chunks.  Returns 0
+ * for invalid arguments.
  */
-int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk);
+int64_t cce_vocab_chunk(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk);
 
 /*
  * Forward.  e (device) [N, D], c (device) [V, D] of `dtype`; bias (device)

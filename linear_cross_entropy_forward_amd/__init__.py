@@ -57,7 +57,7 @@ def lib() -> ctypes.CDLL:
     L.cce_workspace_size.restype = sz
     L.cce_workspace_size.argtypes = [i64, i64, i64, i32, i64]
     L.cce_vocab_chunk.restype = i64
-    L.cce_vocab_chunk.argtypes = [i64, i64, i32, i64]
+    L.cce_vocab_chunk.argtypes = [i64, i64, i64, i32, i64]
     L.cce_forward.restype = i32
     L.cce_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, f32, f32, vp, vp, vp, vp, sz,
                               vp]
@@ -117,10 +117,10 @@ def workspace_size(N: int, D: int, V: int, dtype: torch.dtype = torch.bfloat16, 
     return n
 
 
-def vocab_chunk(N: int, V: int, dtype: torch.dtype = torch.bfloat16, vocab_chunk: int = 0) -> int:
+def vocab_chunk(N: int, D: int, V: int, dtype: torch.dtype = torch.bfloat16, vocab_chunk: int = 0) -> int:
     """Vocabulary entries per backward chunk (cce_vocab_chunk)."""
     code = 0 if dtype == torch.bfloat16 else 1
-    n = lib().cce_vocab_chunk(N, V, code, vocab_chunk)
+    n = lib().cce_vocab_chunk(N, D, V, code, vocab_chunk)
     if n == 0:
         raise CCEError("invalid sizes for cce_vocab_chunk")
     return n

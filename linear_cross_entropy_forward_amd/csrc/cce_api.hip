@@ -31,7 +31,9 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     // buffer offsets).
     const size_t per_col = (size_t)L.Npad + (dtype == kDtypeBf16 ? 0 : (size_t)L.Npad + kGtPad);
     const size_t cap = (((size_t)1 << 31) - 1) / (((size_t)L.Npad + kGtPad) * es);
-    vc = (int64_t)std::min(kDefaultGBudget / (per_col * es), cap) / kTileV * kTileV;
+    // and the chunk's classifier rows (one descriptor in the dE contraction)
+    const size_t cap_c = (((size_t)1 << 31) - 1) / ((size_t)D * es);
+    vc = (int64_t)std::min(std::min(kDefaultGBudget / (per_col * es), cap), cap_c) / kTileV * kTileV;
   }
   if (vc < kTileV) vc = kTileV;
   if (vc > vmax) vc = vmax;
@@ -193,10 +195,10 @@ size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vo
   return make_layout(N, D, V, dtype, vocab_chunk, nullptr).total;
 }
 
-int64_t cce_vocab_chunk(int64_t N, int64_t V, int dtype, int64_t vocab_chunk) {
-  if (N < 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
+int64_t cce_vocab_chunk(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk) {
+  if (N < 0 || D <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
   if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return 0;
-  return make_layout(N, 1, V, dtype, vocab_chunk, nullptr).Vc;
+  return make_layout(N, D, V, dtype, vocab_chunk, nullptr).Vc;
 }
 
 static bool bias_ok(const void* bias, int dtype) {

@@ -59,19 +59,24 @@ def test_workspace_size(L):
 
 def test_vocab_chunk(L):
     vc = L.cce_vocab_chunk
-    assert vc(-1, 100, 0, 0) == 0 and vc(4, 100, 7, 0) == 0 and vc(4, 100, 0, 100) == 0
-    d = vc(4096, 128256, 0, 0)
+    assert vc(-1, 64, 100, 0, 0) == 0 and vc(4, 64, 100, 7, 0) == 0 and vc(4, 64, 100, 0, 100) == 0
+    assert vc(4, 0, 100, 0, 0) == 0
+    d = vc(4096, 4096, 128256, 0, 0)
     assert d % 256 == 0 and 256 <= d <= 128256 + 255
     # the default keeps a chunk's gradient tiles within 2 GiB, each buffer
     # below 2^31 bytes: bf16 stores them once (token-major), the whole
     # vocabulary at N = 4096 and about half of it at N = 16384; fp32 stores
     # both orientations
-    assert d >= 128256 and vc(16384, 128256, 0, 0) == 65280
-    assert 16384 * vc(16384, 128256, 0, 0) * 2 < 1 << 31
-    assert vc(16384, 128256, 1, 0) == 16384 and 2 * 16384 * 16384 * 4 <= 2048 << 20
-    assert vc(4096, 128256, 0, 1024) == 1024
-    assert vc(64, 1000, 1, 0) == 1024          # clamped to the vocabulary, in whole tiles
-    assert vc(64, 1000, 1, 4096) == 1024
+    assert d >= 128256 and vc(16384, 4096, 128256, 0, 0) == 65280
+    assert 16384 * vc(16384, 4096, 128256, 0, 0) * 2 < 1 << 31
+    assert vc(16384, 4096, 128256, 1, 0) == 16384 and 2 * 16384 * 16384 * 4 <= 2048 << 20
+    # ... and a chunk's classifier rows below 2^31 bytes: a classifier larger
+    # than that (Gemma-2-27B's 256000 x 4608 bf16, 2.4 GB) is taken in chunks
+    big = vc(4096, 4608, 256000, 0, 0)
+    assert big % 256 == 0 and big * 4608 * 2 < 1 << 31 and big < 256000
+    assert vc(4096, 4096, 128256, 0, 1024) == 1024
+    assert vc(64, 64, 1000, 1, 0) == 1024          # clamped to the vocabulary, in whole tiles
+    assert vc(64, 64, 1000, 1, 4096) == 1024
 
 
 def _fwd(L, e=FAKE, c=FAKE, t=FAKE, N=64, D=64, V=100, dt=0, ign=-100, red=2, cap=0.0, loss=FAKE, lse=FAKE,

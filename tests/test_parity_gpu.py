@@ -789,6 +789,15 @@ def test_full_wide_head(M):
     _sampled_full(M, "wide8192", "mean", True, n_rows=32, n_vocab=16)
 
 
+@pytest.mark.slow
+def test_full_classifier_beyond_2gib(M):
+    """Gemma-2-27B's head (V = 256000, D = 4608: a 2.4 GB bf16 classifier),
+    beyond one buffer descriptor's 2^31-byte reach: the backward takes it in
+    two vocabulary chunks."""
+    assert M.vocab_chunk(1024, 4608, 256000) < 256000
+    _sampled_full(M, "gemma27b_1k", "mean", True, n_rows=32, n_vocab=16)
+
+
 # ----------------------------------------------------------------------------- seeded random configurations
 def _random_case(k):
     """Case k of a fixed list: shapes, dtype, reduction, filter, accumulation,

@@ -121,6 +121,9 @@ WORKLOADS: dict[str, Workload] = {
     # the widest head the 32-bit buffer offsets take whole: D = 8192 (a 70B-class
     # model), the classifier 2.1 GB, just under 2^31 bytes
     "wide8192": Workload("wide8192", 1024, 8192, 128256, "bf16", "normal", 1.0, 0.02, "uniform", 0.05, 7),
+    # a classifier beyond 2^31 bytes (Gemma-2-27B's head: 256000 x 4608 bf16,
+    # 2.4 GB), which the backward takes in vocabulary chunks
+    "gemma27b_1k": Workload("gemma27b_1k", 1024, 4608, 256000, "bf16", "normal", 1.0, 0.02, "uniform", 0.05, 8),
 }
 
 
