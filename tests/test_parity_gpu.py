@@ -37,7 +37,7 @@ def _grad_arg(reduction, N, seed=0):
 
 
 def run(M, inp, reduction="mean", filter=False, accum="deterministic", vocab_chunk=0, ignore_index=-100,
-        backward=True, grad_seed=0, bias=None, want_db=False, ls=0.0, zl=0.0, cap=0.0):
+        backward=True, grad_seed=0, bias=None, want_db=False, ls=0.0, zl=0.0, cap=0.0, grad_dtype="float32"):
     import torch
     dt = inp.get("dtype") or inp["workload"].dtype
     e, c, t = dev(inp["e"], dt), dev(inp["c"], dt), dev_targets(inp["targets"])
@@ -52,9 +52,9 @@ def run(M, inp, reduction="mean", filter=False, accum="deterministic", vocab_chu
         g_np, g = _grad_arg(reduction, N, grad_seed)
         res = M.backward(e, c, t, lse, g, ws, ignore_index=ignore_index, reduction=reduction, filter=filter,
                          accum=accum, vocab_chunk=vocab_chunk, bias=b, want_dbias=want_db, label_smoothing=ls,
-                         z_loss=zl, softcap=cap)
+                         z_loss=zl, softcap=cap, grad_dtype=grad_dtype)
         torch.cuda.synchronize()
-        out["dE"], out["dC"], out["g"] = res[0].cpu().numpy(), res[1].cpu().numpy(), g_np
+        out["dE"], out["dC"], out["g"] = res[0].float().cpu().numpy(), res[1].float().cpu().numpy(), g_np
         if want_db:
             out["db"] = res[2].cpu().numpy()
         out["stats"] = M.read_stats(ws, N, V)
@@ -73,10 +73,10 @@ def filtered_bound(filtered_oracle, exact_oracle):
 
 
 def full_check(M, inp, reduction, filter, accum="deterministic", vocab_chunk=0, ignore_index=-100, label="",
-               bias=None, want_db=False, ls=0.0, zl=0.0, cap=0.0):
+               bias=None, want_db=False, ls=0.0, zl=0.0, cap=0.0, grad_dtype="float32"):
     e, c, t = inp["e"], inp["c"], inp["targets"]
     r = run(M, inp, reduction, filter, accum, vocab_chunk, ignore_index, bias=bias, want_db=want_db, ls=ls, zl=zl,
-            cap=cap)
+            cap=cap, grad_dtype=grad_dtype)
     terms = dict(label_smoothing=ls, z_loss=zl, softcap=cap)
     f = O.forward(e, c, t, ignore_index=ignore_index, reduction=reduction, bias=bias, **terms)
     assert r["n_valid"] == f.n_valid, label
@@ -819,10 +819,11 @@ def _random_case(k):
                 ls=float(g.choice([0.0, 0.0, 0.1])),
                 zl=float(g.choice([0.0, 1e-3])))
     case["cap"] = float(g.choice([0.0, 5.0])) if dt == "bf16" and case["ls"] == 0.0 else 0.0
+    case["grad_dtype"] = str(g.choice(["float32", "operand"]))
     return case
 
 
-@pytest.mark.parametrize("k", range(16))
+@pytest.mark.parametrize("k", range(40))
 def test_random_configuration(M, k):
     cs = _random_case(k)
     print(f"[random {k}] {cs}", flush=True)
@@ -830,4 +831,5 @@ def test_random_configuration(M, k):
                    ignore_frac=cs["ignore_frac"])
     bias = W.bias(cs["V"], cs["dt"], seed=2000 + k) if cs["bias"] else None
     full_check(M, inp, cs["reduction"], cs["filter"], accum=cs["accum"], vocab_chunk=cs["vocab_chunk"],
-               label=f"random {k}", bias=bias, want_db=cs["bias"], ls=cs["ls"], zl=cs["zl"], cap=cs["cap"])
+               label=f"random {k}", bias=bias, want_db=cs["bias"], ls=cs["ls"], zl=cs["zl"], cap=cs["cap"],
+               grad_dtype=cs["grad_dtype"])
