@@ -668,7 +668,7 @@ def test_grad_dtype_operand(M, case):
 
 # ----------------------------------------------------------------------------- full-size, sampled
 def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, n_vocab=24, dC_check=True,
-                  with_bias=False, ls=0.0, zl=0.0, cap=0.0):
+                  with_bias=False, ls=0.0, zl=0.0, cap=0.0, grad_dtype="float32"):
     import torch
     inp = W.get(name)
     e, c, t = inp["e"], inp["c"], inp["targets"]
@@ -677,7 +677,8 @@ def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, 
     terms = dict(label_smoothing=ls, z_loss=zl, softcap=cap)
     print(f"[full] {name} N={N} V={V} reduction={reduction} filter={filter} accum={accum} bias={with_bias} "
           f"ls={ls} zl={zl} cap={cap}", flush=True)
-    r = run(M, inp, reduction, filter, accum, bias=bias, want_db=with_bias, ls=ls, zl=zl, cap=cap)
+    r = run(M, inp, reduction, filter, accum, bias=bias, want_db=with_bias, ls=ls, zl=zl, cap=cap,
+            grad_dtype=grad_dtype)
     print(f"[full] {name}: GPU done, oracle checks", flush=True)
     rng = np.random.default_rng(99)
     rows = np.sort(rng.choice(N, n_rows, replace=False))
@@ -728,8 +729,10 @@ def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, 
 
 @pytest.mark.slow
 def test_full_llama8b_none_filtered(M):
-    """The benchmark's workload and launch configuration (filter on, deterministic)."""
-    _sampled_full(M, "llama8b", "none", True)
+    """The benchmark's workload and launch configuration (per-token loss,
+    filter on, deterministic, gradients in bf16), and with fp32 gradients."""
+    _sampled_full(M, "llama8b", "none", True, grad_dtype="operand")
+    _sampled_full(M, "llama8b", "none", True, dC_check=False)
 
 
 @pytest.mark.slow
