@@ -875,18 +875,36 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     // leaves as rows of 16-byte stores from consecutive lanes (stored straight
     // from the accumulators, one instruction would scatter 8-byte pieces over
     // 64 rows).  A staging tile holds 256 token rows of 512 bytes; 16-byte
-    // chunk j of row r sits in slot j ^ (r % 32): the writes (one chunk of 32
-    // consecutive rows per half-wave) and the row drains are both conflict
-    // free.
+    // chunk j of row r sits in slot j ^ (r % 32).  A lane holds four vocab
+    // rows of its token per accumulator group and the lane 32 apart the next
+    // four: one v_permlane32_swap per word pairs them, so that each lane
+    // writes a whole chunk (eight vocab rows; the lower half-wave for group
+    // q, the upper for q + 1).  Sixteen lanes of a ds_write_b128 cycle then
+    // write one chunk of 16 consecutive rows, sixteen distinct slots (the
+    // 8-byte writes of half chunks had two-way conflicts on the 64-bank LDS),
+    // and the row drains are conflict free.
     static_assert(C::BM == 256 && C::BN == 256 && C::LDS_DMA_BYTES >= 256 * 512, "tile staging");
     lds_u8* tile = (lds_u8*)smem;
     auto slot = [](int r, int col) -> uint32_t {
       return (uint32_t)(r * 512 + (((col >> 3) ^ (r & 31)) << 4) + ((col & 7) << 1));
     };
     const bool sums = db_part != nullptr;
-    run([&](int fn, int fm, int q, int rl, const float (&g)[4]) __attribute__((always_inline)) {
+    const int wrow = ((int)(threadIdx.x >> 6) / C::WAVES_N) * C::WM;  // the wave's first vocab row
+    const int upper = (int)(threadIdx.x >> 5) & 1;                     // lanes 32-63
+    uint32_t plo = 0, phi = 0;  // group q - 1's words, for odd q
+    run([&](int fn, int fm, int q, int, const float (&g)[4]) __attribute__((always_inline)) {
       const uint32_t lo = pack_bf16(g[0], g[1]), hi = pack_bf16(g[2], g[3]);
-      *(__attribute__((address_space(3))) u32x2*)(tile + slot(am.colj(fn), rl)) = u32x2{lo, hi};
+      if ((q & 1) == 0) {
+        plo = lo;
+        phi = hi;
+      } else {
+        // lower lanes: group q - 1 whole (own rows, then the upper lane's);
+        // upper lanes: group q whole (the lower lane's rows, then own)
+        const auto sl = __builtin_amdgcn_permlane32_swap(plo, lo, false, false);
+        const auto sh = __builtin_amdgcn_permlane32_swap(phi, hi, false, false);
+        const int col = wrow + fm * 32 + 8 * (q - 1 + upper);
+        *(__attribute__((address_space(3))) u32x4*)(tile + slot(am.colj(fn), col)) = u32x4{sl[0], sh[0], sl[1], sh[1]};
+      }
       if (sums) {  // the rounded values, as the contractions see them
         rs[fm][q][0] += __builtin_bit_cast(float, lo << 16);
         rs[fm][q][1] += __builtin_bit_cast(float, lo & 0xffff0000u);
