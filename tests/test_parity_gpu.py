@@ -305,6 +305,28 @@ def test_bias_autograd(M):
     check_grad(e.grad.float().cpu().numpy(), bo.dE, GRAD_RTOL * 2, "autograd dE")
 
 
+def test_autograd_per_token_loss(M):
+    """reduction='none' through autograd: the loss shaped like the targets
+    ([20, 13]), ignored positions exactly 0, and a non-uniform upstream
+    gradient (a weighted sum of the per-token losses) reaching dE and dC."""
+    import torch
+    inp = W.custom(260, 64, 900, "bf16", seed=37, c_std=0.1, ignore_frac=0.1)
+    e = dev(inp["e"], "bf16").requires_grad_(True)
+    c = dev(inp["c"], "bf16").requires_grad_(True)
+    t = dev_targets(inp["targets"]).reshape(20, 13)
+    w_np = np.random.default_rng(38).standard_normal(260).astype(np.float32)
+    w = torch.from_numpy(w_np).cuda().reshape(20, 13)
+    loss = M.linear_cross_entropy(e.reshape(20, 13, 64), c, t, reduction="none", filter=False)
+    assert loss.shape == (20, 13) and loss.dtype == torch.float32
+    (loss * w).sum().backward()
+    f = O.forward(inp["e"], inp["c"], inp["targets"], reduction="none")
+    check_loss(loss.detach().reshape(-1).cpu().numpy(), f.loss, "none", "autograd none")
+    assert (loss.detach().reshape(-1).cpu().numpy()[~f.valid] == 0.0).all()
+    bo = O.backward(inp["e"], inp["c"], inp["targets"], reduction="none", grad_loss=w_np.astype(np.float64))
+    check_grad(e.grad.float().cpu().numpy(), bo.dE, GRAD_RTOL * 2, "autograd none dE")
+    check_grad(c.grad.float().cpu().numpy(), bo.dC, GRAD_RTOL * 2, "autograd none dC")
+
+
 # ----------------------------------------------------------------------------- label smoothing, z-loss
 @pytest.mark.parametrize("reduction,ls,zl", [("mean", 0.1, 1e-4), ("none", 0.1, 0.0), ("sum", 0.0, 0.05),
                                              ("mean", 1.0, 0.0)])
