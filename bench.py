@@ -38,11 +38,11 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "7fcd20a93189c714333b614eba9270d2be8e06a0b7c259d1f2997b340a2a0d40",
+    "source_sha256": "99e69e5a32b34dee660d653fb6a310f7f7093a2355553751e41a6415f482f3e7",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9340.5e6, "grad_tile": 10901.9e6, "dC_gemm": 7501.6e6, "dE_gemm": 7535.9e6,
-        "rows": 121.4e6, "filter": 3.3e6, "transpose_e": 67.3e6,
+        "fwd_tile": 9149.2e6, "grad_tile": 10422.5e6, "dC_gemm": 7506.8e6, "dE_gemm": 6926.7e6,
+        "rows": 121.4e6, "filter": 37.2e6, "transpose_e": 67.3e6,
     },
 }
 
