@@ -79,7 +79,7 @@ typedef struct ihipStream_t* cce_stream_t;
 
 typedef enum {
   CCE_OK = 0,
-  CCE_ERR_INVALID_ARG = -1, /* null pointer, negative or zero size, bad enum, misalignment */
+  CCE_ERR_INVALID_ARG = -1, /* null pointer, negative N or non-positive D / V, bad enum, misalignment */
   CCE_ERR_UNSUPPORTED = -2, /* softcap with label smoothing, D not a multiple of the vector width, size limits */
   CCE_ERR_WORKSPACE = -3,   /* workspace smaller than cce_workspace_size() */
   CCE_ERR_HIP = -4          /* a HIP launch or copy reported an error */
