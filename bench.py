@@ -81,7 +81,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-materialized", action="store_true",
                     help="skip the materialised-logits PyTorch comparison")
-    ap.add_argument("--no-configs", action="store_true",
+    ap.add_argument("--no-others", action="store_true",
                     help="skip the compact figures for the other workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run one plain device copy of BYTES first (HBM-counter calibration under rocprofv3)")
@@ -451,30 +451,30 @@ def main():
         mat = {"ms_per_step": mat_ms, "tokens_per_s": N / (mat_ms * 1e-3), "peak_extra_bytes": int(mat_peak),
                "what": "PyTorch: fp32 logits = e @ c^T, F.cross_entropy(mean), backward"}
 
-    configs = None
+    others = None
     if not args.no_configs:
         del e, c, t, ws, loss, lse, nv, g
         dE = dC = None
         torch.cuda.empty_cache()
-        configs = {}
+        others = {}
         for name in ("tiny", "llama1b", "gemma2b", "gemma2b_cal", "long8b", "long8b_cal", "llama8b_pad25"):
             if name != args.workload:
-                configs[name] = config_summary(name, graph=name == "tiny")
+                others[name] = config_summary(name, graph=name == "tiny")
         # the headline workload with a classifier bias and its gradient
-        configs[args.workload + "+bias"] = config_summary(args.workload, with_bias=True)
+        others[args.workload + "+bias"] = config_summary(args.workload, with_bias=True)
         # ... and with label smoothing 0.1 and z-loss 1e-4
-        configs[args.workload + "+smoothing+zloss"] = config_summary(args.workload, label_smoothing=0.1,
+        others[args.workload + "+smoothing+zloss"] = config_summary(args.workload, label_smoothing=0.1,
                                                                      z_loss=1e-4)
         # Gemma 2's final-logit soft-capping (30) on the calibrated Gemma-2-2B head
-        configs["gemma2b_cal+softcap30"] = config_summary("gemma2b_cal", softcap=30.0)
+        others["gemma2b_cal+softcap30"] = config_summary("gemma2b_cal", softcap=30.0)
         # the filter off (Llama-3.2-1B) and fp32 atomic accumulation (long context)
-        configs["llama1b+nofilter"] = config_summary("llama1b", filter=False, materialized_too=False)
-        configs["long8b_cal+atomic"] = config_summary("long8b_cal", accum="atomic", materialized_too=False)
+        others["llama1b+nofilter"] = config_summary("llama1b", filter=False, materialized_too=False)
+        others["long8b_cal+atomic"] = config_summary("long8b_cal", accum="atomic", materialized_too=False)
         # fp32 gradient outputs
-        configs[args.workload + "+fp32_grads"] = config_summary(args.workload, grad_dtype="float32",
+        others[args.workload + "+fp32_grads"] = config_summary(args.workload, grad_dtype="float32",
                                                                 materialized_too=False)
         # a frozen classifier: dE alone (dC's contraction does not run)
-        configs[args.workload + "+frozen_classifier"] = config_summary(args.workload, frozen_classifier=True,
+        others[args.workload + "+frozen_classifier"] = config_summary(args.workload, frozen_classifier=True,
                                                                        materialized_too=False)
 
     cpu = None
@@ -510,7 +510,7 @@ def main():
         "materialized_logits_fp32_bytes": N * V * 4,
         "materialized_baseline": mat,
         "hipblaslt_fwd_gemm_tflops": hip_tf,
-        "other_workloads": configs,
+        "other_workloads": others,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
