@@ -81,7 +81,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-materialized", action="store_true",
                     help="skip the materialised-logits PyTorch comparison")
-    ap.add_argument("--no-others", action="store_true",
+    ap.add_argument("--no-configs", action="store_true",
                     help="skip the compact figures for the other workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run one plain device copy of BYTES first (HBM-counter calibration under rocprofv3)")
