@@ -18,7 +18,7 @@
  * over the non-ignored rows (README "API" table; tirogla "Loss functions",
  * "How it works" step 4 and the "Code" section, which floors the count at 1).
  * The backward returns dE = G C and dC = G^T E with
- * G = (softmax - onehot(y)) * scale (tirogla step 2: the fused gradient p - y),
+ * G = (softmax - onehot(y)) * scale ("Loss functions" step 2: the fused gradient p - y),
  * skipping (token block, vocab block) tiles on which every softmax value is
  * below 2^-12 (README "How it works" item 2; Wijmans et al. abstract).
  *

@@ -17,18 +17,20 @@ sees them: bf16 values upcast exactly, or fp32):
   LSE_i = m_i + ln sum_j exp(Z_ij - m_i),  m_i = max_j Z_ij
                                   (tirogla "Loss functions", "How it works"
                                   step 1: log-sum-exp with max subtraction)
-  loss_i = LSE_i - Z_{i,y_i}      (Kamath blog: loss = -correct_token + LSE;
-                                  Wijmans et al. abstract: only the correct
+  loss_i = LSE_i - Z_{i,y_i}      (blog "Cut Cross Entropy from first
+                                  principles": the LSE minus the
+                                  correct-token logit; Wijmans et al.
+                                  abstract: only the correct
                                   token's logit plus the log-sum-exp)
   rows with y_i == ignore_index give loss 0 and gradient 0, and are not counted
-                                  (README "API" ignore_index; tirogla "Code":
+                                  (README "API" ignore_index; "Loss functions" "Code":
                                   ignored rows' gradient is zero, mean over
                                   non-ignored rows with the count floored at 1)
   reduction: none -> loss_i; sum -> sum_i loss_i; mean -> sum / max(n_valid, 1)
                                   (README "API" and "Computing related
-                                  quantities"; tirogla step 4)
+                                  quantities"; "Loss functions" step 4)
   G = (softmax(Z) - onehot(y)) * scale_i
-                                  (tirogla step 2: fused softmax+CE gradient
+                                  ("Loss functions" step 2: fused softmax+CE gradient
                                   p - y)
   dE = G C,  dC = G^T E,  db = G^T 1
                                   (chain rule through Z = E C^T + 1 b^T)
