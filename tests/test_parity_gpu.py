@@ -637,7 +637,7 @@ def test_c_caller(M):
     import subprocess
     from linear_cross_entropy_forward_amd import build as b
     exe = b.C_CHECK_BIN
-    assert os.path.exists(exe), "build the C check first (__graft_entry__.build())"
+    assert os.path.exists(exe), "build the C check first (linear_cross_entropy_forward_amd/build.py)"
     print("[c caller]", exe, flush=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
