@@ -327,6 +327,21 @@ def test_autograd_per_token_loss(M):
     check_grad(c.grad.float().cpu().numpy(), bo.dC, GRAD_RTOL * 2, "autograd none dC")
 
 
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_scaled_upstream_gradient(M, reduction):
+    """A reduced loss scaled before backward (loss scaling): the upstream
+    gradient 3.5 multiplies every gradient."""
+    import torch
+    inp = W.custom(300, 72, 700, "bf16", seed=39, c_std=0.1, ignore_frac=0.1)
+    e = dev(inp["e"], "bf16").requires_grad_(True)
+    c = dev(inp["c"], "bf16").requires_grad_(True)
+    t = dev_targets(inp["targets"])
+    (3.5 * M.linear_cross_entropy(e, c, t, reduction=reduction, filter=False)).backward()
+    bo = O.backward(inp["e"], inp["c"], inp["targets"], reduction=reduction, grad_loss=3.5)
+    check_grad(e.grad.float().cpu().numpy(), bo.dE, GRAD_RTOL * 2, f"scaled {reduction} dE")
+    check_grad(c.grad.float().cpu().numpy(), bo.dC, GRAD_RTOL * 2, f"scaled {reduction} dC")
+
+
 # ----------------------------------------------------------------------------- label smoothing, z-loss
 @pytest.mark.parametrize("reduction,ls,zl", [("mean", 0.1, 1e-4), ("none", 0.1, 0.0), ("sum", 0.0, 0.05),
                                              ("mean", 1.0, 0.0)])
