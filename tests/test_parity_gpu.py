@@ -838,6 +838,15 @@ def test_full_classifier_beyond_2gib(M):
     _sampled_full(M, "gemma27b_1k", "mean", True, n_rows=32, n_vocab=16)
 
 
+@pytest.mark.slow
+def test_full_64k_tokens(M):
+    """65536 tokens on the 8B head: eight vocabulary chunks (the gradient
+    tiles of a chunk just under 2^31 bytes), 256 token blocks; per-row checks
+    (the oracle's whole-vocabulary pass over 65536 rows would take too long)."""
+    assert M.vocab_chunk(65536, 4096, 128256) * 8 >= 128256 > M.vocab_chunk(65536, 4096, 128256) * 7
+    _sampled_full(M, "long64k", "none", False, dC_check=False, n_rows=32)
+
+
 # ----------------------------------------------------------------------------- seeded random configurations
 def _random_case(k):
     """Case k of a fixed list: shapes, dtype, reduction, filter, accumulation,

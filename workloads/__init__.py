@@ -124,6 +124,8 @@ WORKLOADS: dict[str, Workload] = {
     # a classifier beyond 2^31 bytes (Gemma-2-27B's head: 256000 x 4608 bf16,
     # 2.4 GB), which the backward takes in vocabulary chunks
     "gemma27b_1k": Workload("gemma27b_1k", 1024, 4608, 256000, "bf16", "normal", 1.0, 0.02, "uniform", 0.05, 8),
+    # 64K tokens on the 8B head: eight vocabulary chunks in the backward
+    "long64k": Workload("long64k", 65536, 4096, 128256, "bf16", "normal", 1.0, 0.02, "uniform", 0.03, 9),
 }
 
 
