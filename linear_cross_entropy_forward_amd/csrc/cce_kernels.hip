@@ -1160,7 +1160,10 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   constexpr int SPB = kTileV / C::BK;
   auto loop = [&](const Operand& a, const Operand& b, const uint16_t* bl) {
-    if constexpr (kDma) mainloop_dma<C, SPB, true>(acc, a, b, nk * SPB, bl, smem);
+    // the step's DMA in two parts (right after the barrier and in the first
+    // K group) rather than three: measured faster for this kernel's
+    // MN-major classifier tile, slower for the K-major ones
+    if constexpr (kDma) mainloop_dma<C, SPB, true, false, 2>(acc, a, b, nk * SPB, bl, smem);
     else mainloop<C, false, true, SPB>(acc, a, b, nk * SPB, bl, (T*)smem);
   };
   // the split's blocks consecutive (every block kept): contiguous K from its
