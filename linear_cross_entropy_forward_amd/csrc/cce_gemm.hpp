@@ -642,8 +642,9 @@ struct DmaTileMN {
 // its DMA loads (which the memory pipeline delivers at about 64 bytes per
 // clock per CU, so a step's 64 KB needs about half a step) are issued in
 // NPARTS parts over that window: part 0 right after the barrier, in the last
-// group, and part p in group p-1 of the following step, each spread one or two
-// instructions between MFMAs so the issue never stalls the matrix core.
+// group, and part p in group p-1 of the following step, each spread about two
+// instructions per MFMA over the first half of its group so the issue never
+// stalls the matrix core.
 // Steps past the end (the count is padded to even) read zeros.
 template <class C, int SPB, bool B_MN = false, bool A_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1)>
 __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const Operand& A, const Operand& B,
@@ -735,7 +736,13 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
                 if constexpr (last) read_one(0, nx, 0, q);
                 else read_one((g + 1) & 1, st, g + 1, q);
               }
-              constexpr int d0 = b * dn / BLOCKS, d1 = (b + 1) * dn / BLOCKS;
+              // the part's DMA over the group's first half of MFMAs (about
+              // two per MFMA there): the loads start earlier than spread over
+              // the whole group (measured 1% faster), while more bunched
+              // issue (first quarter) stalls the matrix core (2% slower)
+              constexpr int HALF = BLOCKS / 2;
+              constexpr int d0 = b * dn / HALF < dn ? b * dn / HALF : dn;
+              constexpr int d1 = (b + 1) * dn / HALF < dn ? (b + 1) * dn / HALF : dn;
 #pragma unroll
               for (int d = d0; d < d1; ++d) {
                 if constexpr (last) dma(dlo + d, k2, st_addr);
