@@ -38,11 +38,11 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "99e69e5a32b34dee660d653fb6a310f7f7093a2355553751e41a6415f482f3e7",
+    "source_sha256": "874ffa88dadddba57865da167c60d8babd6e3f8a69386586c2f0001f416d1009",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9149.2e6, "grad_tile": 10422.5e6, "dC_gemm": 7506.8e6, "dE_gemm": 6926.7e6,
-        "rows": 121.4e6, "filter": 37.2e6, "transpose_e": 67.3e6,
+        "fwd_tile": 9399.1e6, "grad_tile": 12810.0e6, "dC_gemm": 7486.6e6, "dE_gemm": 6347.0e6,
+        "rows": 121.3e6, "filter": 37.1e6, "transpose_e": 67.3e6,
     },
 }
 
