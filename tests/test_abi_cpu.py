@@ -176,3 +176,16 @@ def test_c_caller_builds(tmp_path):
     from linear_cross_entropy_forward_amd import build as b
     out = b.build_c_check(str(tmp_path / "cce_abi_check"))
     assert os.path.exists(out)
+
+
+def test_bench_refuses_several_gpus():
+    """The benchmark runs on one GPU: asked for more it prints why and exits
+    non-zero, before touching a device."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
