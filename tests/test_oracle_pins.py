@@ -508,15 +508,16 @@ def test_bias_brute_force_filter_and_sampled():
 # lam * LSE^2 per row (same page, "Implementation notes").
 
 
+@pytest.mark.parametrize("eps", [0.0, 0.15])
 @pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
-def test_label_smoothing_matches_torch_cross_entropy(reduction):
-    """Smoothed loss and gradients equal PyTorch's cross_entropy with
-    label_smoothing (which spreads eps over all V classes, the true one
-    included), differentiated by autograd in float64 on the CPU through
-    Z = E C^T + b."""
+def test_label_smoothing_matches_torch_cross_entropy(reduction, eps):
+    """Loss and gradients equal PyTorch's cross_entropy (with label_smoothing
+    eps, which spreads eps over all V classes, the true one included; eps = 0
+    is the plain loss), differentiated by autograd in float64 on the CPU
+    through Z = E C^T + b."""
     import torch
     g = np.random.default_rng(50)
-    N, D, V, eps = 11, 6, 17, 0.15
+    N, D, V = 11, 6, 17
     e, c = g.standard_normal((N, D)), g.standard_normal((V, D))
     b = g.standard_normal(V)
     t = g.integers(0, V, N)
