@@ -231,7 +231,9 @@ class _CCEFunction(torch.autograd.Function):
         return loss
 
     @staticmethod
+    @torch.autograd.function.once_differentiable
     def backward(ctx, grad):
+        # first-order only: the kernels' gradients carry no graph of their own
         e, c, bias, targets, lse, ws = ctx.saved_tensors
         reduction, ignore_index, filter, accum, label_smoothing, z_loss, softcap = ctx.cfg
         want_db = bias is not None and ctx.needs_input_grad[2]
