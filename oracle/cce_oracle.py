@@ -343,10 +343,16 @@ def lse_and_keep(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias
 
 
 def lse_keep_nll(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias=None,
-                 label_smoothing: float = 0.0, z_loss: float = 0.0, softcap: float = 0.0):
+                 label_smoothing: float = 0.0, z_loss: float = 0.0, softcap: float = 0.0,
+                 margins: bool = False):
     """One pass over all row blocks giving LSE [N], the filter keep map and
     the per-row loss [N] (0 on ignored rows), the same definitions as
-    `forward` and `filter_keep`."""
+    `forward` and `filter_keep`.  With margins=True it also returns, per tile,
+    the largest log-softmax maximum of its valid rows, max_i (max_j Z_ij -
+    LSE_i) (-inf for a tile of no valid row), and whether a valid row's target
+    lies in it: the two quantities the keep rule compares (kept iff the first
+    reaches ln 2^-12 or the second holds), so that a test can tell how close
+    each tile's decision is to the threshold."""
     e = _f64(e)
     c = _f64(c)
     t = np.asarray(targets, dtype=np.int64)
@@ -356,17 +362,27 @@ def lse_keep_nll(e, c, targets, Bn: int, Bv: int, ignore_index: int = -100, bias
     keep = np.zeros((-(-N // Bn), -(-V // Bv)), dtype=bool)
     lse = np.empty(N)
     nll = np.zeros(N)
+    margin = np.full(keep.shape, -np.inf)
+    tgt = np.zeros(keep.shape, dtype=bool)
     for r0 in range(0, N, _ROW_CHUNK):
         r1 = min(N, r0 + _ROW_CHUNK)
         z = logits(e[r0:r1], c, bias, softcap)
         l = row_logsumexp(z)
         lse[r0:r1] = l
-        _mark_keep(keep, blk[r0:r1], tile_row_max(z, Bv) - l[:, None], t[r0:r1], Bv)
+        tm = tile_row_max(z, Bv) - l[:, None]
+        _mark_keep(keep, blk[r0:r1], tm, t[r0:r1], Bv)
+        if margins:
+            b = blk[r0:r1]
+            r = np.nonzero(b >= 0)[0]
+            np.maximum.at(margin, b[r], tm[r])
+            tgt[b[r], t[r0:r1][r] // Bv] = True
         v = valid[r0:r1]
         if v.any():
             T = soft_target_rows(t[r0:r1], V, v, label_smoothing)
             r = np.nonzero(v)[0]
             nll[r0 + r] = -(T[r] * (z[r] - l[r, None])).sum(axis=1) + z_loss * l[r] ** 2
+    if margins:
+        return lse, keep, nll, margin, tgt
     return lse, keep, nll
 
 

@@ -680,6 +680,40 @@ def test_one_pass_lse_keep_nll_matches_separate_forms():
     assert np.array_equal(keep, O.filter_keep(e, c, t, Bn, Bv, bias=b))
 
 
+def test_keep_margins_brute_force():
+    """The per-tile margins (largest log-softmax maximum over a tile's valid
+    rows) and target-tile flags, against explicit loops over rows and
+    entries; the keep map is exactly margin >= ln 2^-12 or a target inside."""
+    g = np.random.default_rng(57)
+    N, D, V, Bn, Bv = 19, 4, 45, 4, 8
+    e, c = g.standard_normal((N, D)) * 3.0, g.standard_normal((V, D)) * 2.0
+    t = g.integers(0, V, N)
+    t[[3, 4, 11]] = -100
+    lse, keep, nll, margin, tgt = O.lse_keep_nll(e, c, t, Bn, Bv, margins=True)
+    nb, nvb = -(-N // Bn), -(-V // Bv)
+    want_m = np.full((nb, nvb), -np.inf)
+    want_t = np.zeros((nb, nvb), dtype=bool)
+    k = 0
+    for i in range(N):
+        if t[i] == -100:
+            continue
+        zi = [sum(e[i, d] * c[j, d] for d in range(D)) for j in range(V)]
+        logden = math.log(sum(math.exp(x) for x in zi))
+        for j in range(V):
+            want_m[k // Bn, j // Bv] = max(want_m[k // Bn, j // Bv], zi[j] - logden)
+        want_t[k // Bn, t[i] // Bv] = True
+        k += 1
+    fin = np.isfinite(want_m)
+    assert np.array_equal(fin, np.isfinite(margin))
+    assert np.allclose(margin[fin], want_m[fin], rtol=0, atol=1e-11)
+    assert np.array_equal(tgt, want_t)
+    assert np.array_equal(keep, (margin >= O.FILTER_LOG_THRESHOLD) | tgt)
+    assert 0 < keep.sum() < keep.size and (keep & ~tgt).any()
+    # the same pass without margins returns the same three results
+    lse2, keep2, nll2 = O.lse_keep_nll(e, c, t, Bn, Bv)
+    assert np.array_equal(keep, keep2) and np.array_equal(lse, lse2) and np.array_equal(nll, nll2)
+
+
 # --------------------------------------------------------------------------- logit soft-capping
 # Not defined on the pages: the Gemma 2 form Z' = s tanh(Z / s), after the bias.
 
