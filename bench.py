@@ -165,6 +165,38 @@ def materialized(e, c, t, reduction, steps):
     return s0.elapsed_time(s1) / steps, peak
 
 
+def autograd_memory(e, c, t, reduction):
+    """Peak device memory of one training step through the autograd wrapper
+    (forward, backward, gradients of e and c in their dtype) beyond its
+    inputs, measured as for the materialised head, and the bytes autograd
+    keeps from the forward to the backward beyond the inputs (the forward
+    state, LSE and loss)."""
+    import torch
+    import linear_cross_entropy_forward_amd as M
+    ec = e.detach().clone().requires_grad_(True)
+    cc = c.detach().clone().requires_grad_(True)
+
+    def run():
+        loss = M.linear_cross_entropy(ec, cc, t, reduction="mean" if reduction != "none" else "none")
+        (loss.sum() if reduction == "none" else loss).backward()
+        ec.grad = None
+        cc.grad = None
+
+    run()
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    run()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    loss = M.linear_cross_entropy(ec, cc, t, reduction="mean")
+    torch.cuda.synchronize()
+    saved = torch.cuda.memory_allocated() - base
+    del loss, ec, cc
+    torch.cuda.empty_cache()
+    return peak, saved
+
+
 def hipblaslt_gemm_tflops(c, e, reps=5):
     """torch.mm (hipBLASLt) on the forward contraction's shape, c [V, D] x e^T:
     a practical MFMA ceiling for the same M, N, K."""
@@ -215,6 +247,7 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     base = torch.cuda.memory_allocated()
+    state = torch.empty(M.state_size(N, D, V, tdt), dtype=torch.uint8, device=dev)
     ws = torch.empty(M.workspace_size(N, D, V, tdt), dtype=torch.uint8, device=dev)
     red = {"none": 0, "sum": 1, "mean": 2}[w.reduction]
     loss = torch.empty(N if red == 0 else 1, dtype=torch.float32, device=dev)
@@ -237,8 +270,8 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
     def fwd():
         # on the current stream (a graph capture runs on its own)
         r = L.cce_forward(e.data_ptr(), c.data_ptr(), bp, t.data_ptr(), N, D, V, dcode, -100, red, softcap,
-                          label_smoothing, z_loss, loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(),
-                          ws.numel(), torch.cuda.current_stream().cuda_stream)
+                          label_smoothing, z_loss, loss.data_ptr(), lse.data_ptr(), nv.data_ptr(),
+                          state.data_ptr(), state.numel(), torch.cuda.current_stream().cuda_stream)
         if r:
             raise RuntimeError(f"cce_forward failed: {r}")
 
@@ -248,8 +281,8 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
                            label_smoothing, z_loss, lse.data_ptr(), g.data_ptr(), 1 if filter else 0,
                            0 if accum == "deterministic" else 1, 0, 1 if grad_dtype == "operand" else 0,
                            dE.data_ptr(),
-                           None if dC is None else dC.data_ptr(), dbp, ws.data_ptr(), ws.numel(),
-                           torch.cuda.current_stream().cuda_stream)
+                           None if dC is None else dC.data_ptr(), dbp, state.data_ptr(), state.numel(),
+                           ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
         if r:
             raise RuntimeError(f"cce_backward failed: {r}")
 
@@ -280,24 +313,31 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
         with torch.cuda.graph(gr):
             step()
         graph_ms = timed(gr.replay)
-    stats = M.read_stats(ws, N, V)
+    stats = M.read_stats(state, N, V)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     # effective work: 2NVD per contraction (forward, recompute, dE, dC)
     eff = (6.0 if frozen_classifier else 8.0) * N * V * D / (step_ms * 1e-3) / 1e12
+    # executed work: the forward in full, the backward's contractions on the
+    # kept tiles only
+    kept = stats["tiles_kept"] / max(1, stats["tiles_total"])
+    exec_frac = (2.0 + (4.0 if frozen_classifier else 6.0) * kept) / (6.0 if frozen_classifier else 8.0)
     out = {"N": N, "D": D, "V": V, "dtype": w.dtype, "reduction": w.reduction, "fwd_ms": fwd_ms,
            "fwd_tokens_per_s": N / (fwd_ms * 1e-3), "step_ms": step_ms, "tokens_per_s": N / (step_ms * 1e-3),
-           "tflops_effective": eff, "pct_of_peak": 100.0 * eff / peak,
+           "tflops_effective": eff, "pct_of_peak_effective": 100.0 * eff / peak,
+           "executed_flop_frac": exec_frac, "tflops_executed": eff * exec_frac,
+           "pct_of_peak_executed": 100.0 * eff * exec_frac / peak,
            "tflops_useful": eff * (4.0 / 6.0 if frozen_classifier else 0.75), "filter": bool(filter),
            "accum": accum, "frozen_classifier": bool(frozen_classifier),
            "grad_dtype": "bf16" if gdt == torch.bfloat16 else "f32", "step_ms_graph": graph_ms,
            "tiles_skipped_frac": 1.0 - stats["tiles_kept"] / max(1, stats["tiles_total"]),
-           "extra_hbm_bytes": int(extra), "bias": bool(with_bias), "label_smoothing": label_smoothing,
+           "extra_hbm_bytes": int(extra), "state_bytes": int(state.numel()), "workspace_bytes": int(ws.numel()),
+           "bias": bool(with_bias), "label_smoothing": label_smoothing,
            "z_loss": z_loss, "softcap": softcap}
     plain = (not with_bias and label_smoothing == 0.0 and z_loss == 0.0 and softcap == 0.0 and filter
              and accum == "deterministic" and not frozen_classifier and grad_dtype == "operand")
     if w.dtype == "bf16" and plain:
         out["hipblaslt_fwd_gemm_tflops"] = hipblaslt_gemm_tflops(c, e)
-    del ws, loss, lse, nv, g, dE, dC, bias, db
+    del state, ws, loss, lse, nv, g, dE, dC, bias, db
     torch.cuda.empty_cache()
     if materialized_too and plain:
         mat_ms, mat_peak = materialized(e, c, t, w.reduction, max(1, min(steps, 3)))
@@ -341,6 +381,7 @@ def main():
         torch.cuda.empty_cache()
 
     base_alloc = torch.cuda.memory_allocated()
+    state = torch.empty(M.state_size(N, D, V, tdt), dtype=torch.uint8, device=dev)
     ws = torch.empty(M.workspace_size(N, D, V, tdt, args.vocab_chunk), dtype=torch.uint8, device=dev)
     red = {"none": 0, "sum": 1, "mean": 2}[reduction]
     loss = torch.empty(N if red == 0 else 1, dtype=torch.float32, device=dev)
@@ -358,34 +399,45 @@ def main():
     acc = 0 if args.accum == "deterministic" else 1
     stream = torch.cuda.current_stream()
 
+    def fwd(s):
+        r = L.cce_forward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0, 0.0,
+                          loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), state.data_ptr(), state.numel(), s)
+        if r:
+            raise RuntimeError(f"cce_forward failed: {r}")
+
     def step():
         s = stream.cuda_stream
-        r1 = L.cce_forward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0, 0.0,
-                           loss.data_ptr(), lse.data_ptr(), nv.data_ptr(), ws.data_ptr(), ws.numel(), s)
-        r2 = L.cce_backward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0,
-                            0.0, lse.data_ptr(), g.data_ptr(), flt, acc, args.vocab_chunk, gcode, dE.data_ptr(),
-                            dC.data_ptr(),
-                            None, ws.data_ptr(), ws.numel(), s)
-        if r1 or r2:
-            raise RuntimeError(f"cce call failed: {r1} {r2}")
+        fwd(s)
+        r = L.cce_backward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0,
+                           0.0, lse.data_ptr(), g.data_ptr(), flt, acc, args.vocab_chunk, gcode, dE.data_ptr(),
+                           dC.data_ptr(), None, state.data_ptr(), state.numel(), ws.data_ptr(), ws.numel(), s)
+        if r:
+            raise RuntimeError(f"cce_backward failed: {r}")
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stats = M.read_stats(ws, N, V)
+    stats = M.read_stats(state, N, V)
 
-    # timed region: K steps, HIP events around every kernel launch
+    def timed_steps():
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    # timed region: K steps, nothing recorded between the kernels
+    total_ms = timed_steps()
+
+    # per-kernel split: the same K steps again with HIP events recorded by the
+    # library around every kernel launch on the launch stream
     for k in range(len(KERNELS)):
         L.cce_profile_start(k, 64 * max(1, args.steps))
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    t_stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_stop)
+    profiled_ms = timed_steps()
     import ctypes
     per = {}
     for k, name in enumerate(KERNELS):
@@ -400,9 +452,7 @@ def main():
     f1 = torch.cuda.Event(enable_timing=True)
     f0.record(stream)
     for _ in range(args.steps):
-        L.cce_forward(e.data_ptr(), c.data_ptr(), None, t.data_ptr(), N, D, V, dcode, -100, red, 0.0, 0.0, 0.0,
-                      loss.data_ptr(),
-                      lse.data_ptr(), nv.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream)
+        fwd(stream.cuda_stream)
     f1.record(stream)
     torch.cuda.synchronize()
     fwd_ms = f0.elapsed_time(f1) / args.steps
@@ -412,6 +462,8 @@ def main():
     eff_flops = 8.0 * N * V * D
     peak = PEAK_BF16_TFLOPS if dt_name == "bf16" else PEAK_F32_TFLOPS
     tflops = eff_flops / (ms_step * 1e-3) / 1e12
+    kept_frac = stats["tiles_kept"] / max(1, stats["tiles_total"])
+    exec_frac = (2.0 + 6.0 * kept_frac) / 8.0
 
     # chunk lengths of the backward, for per-launch algorithmic work
     Vc = M.vocab_chunk(N, D, V, tdt, args.vocab_chunk)
@@ -438,22 +490,25 @@ def main():
                 "traffic": traffic_for(dom, args.workload), "kernel": dom,
                 "avg_launch_ms": per[dom]["avg_ms"], "algorithmic_bytes_per_launch": by}
 
-    # device memory this path needs beyond its inputs: workspace, loss/LSE and
-    # the two gradient outputs
+    # device memory this path needs beyond its inputs: the forward state, the
+    # backward workspace, loss/LSE and the two gradient outputs
     extra_bytes = torch.cuda.memory_allocated() - base_alloc
     ws_bytes = ws.numel()
+    state_bytes = state.numel()
     hip_tf = hipblaslt_gemm_tflops(c, e) if dt_name == "bf16" else None
     mat = None
+    ag_peak = ag_saved = None
     if not args.no_materialized:
         del dE, dC
         torch.cuda.empty_cache()
+        ag_peak, ag_saved = autograd_memory(e, c, t, reduction)
         mat_ms, mat_peak = materialized(e, c, t, reduction, max(1, min(args.steps, 3)))
         mat = {"ms_per_step": mat_ms, "tokens_per_s": N / (mat_ms * 1e-3), "peak_extra_bytes": int(mat_peak),
                "what": "PyTorch: fp32 logits = e @ c^T, F.cross_entropy(mean), backward"}
 
     others = None
     if not args.no_configs:
-        del e, c, t, ws, loss, lse, nv, g
+        del e, c, t, state, ws, loss, lse, nv, g
         dE = dC = None
         torch.cuda.empty_cache()
         others = {}
@@ -498,14 +553,25 @@ def main():
         "config": {"workload": args.workload, "N": N, "D": D, "V": V, "reduction": reduction,
                    "filter": bool(flt), "accum": args.accum, "vocab_chunk": Vc,
                    "grad_dtype": "bf16" if gdt == torch.bfloat16 else "f32"},
+        # effective (unfiltered, 8NVD) flops of the step per second over the
+        # dense bf16 peak; not a hardware counter (the matrix cores' busy
+        # fraction per contraction, from SQ_VALU_MFMA_BUSY_CYCLES:
+        # profiles/llama8b_mfma_lds_counters.md)
         "mfma_util_pct": 100.0 * tflops / peak,
+        "mfma_util_what": "effective 8NVD flops / step time / dense bf16 peak (not a counter reading)",
         "tflops_effective": tflops,
         "tflops_useful": tflops * 0.75,  # 6NVD: the step without the recompute
+        "executed_flop_frac": exec_frac,
+        "tflops_executed": tflops * exec_frac,
+        "profiled_pass_ms_per_step": profiled_ms / args.steps,
         "fwd_ms": fwd_ms,
         "fwd_tokens_per_s": N / (fwd_ms * 1e-3),
         "tiles_kept_frac": stats["tiles_kept"] / max(1, stats["tiles_total"]),
+        "state_bytes": state_bytes,
         "workspace_bytes": ws_bytes,
         "extra_hbm_bytes": int(extra_bytes),
+        "autograd_peak_extra_bytes": ag_peak,
+        "autograd_saved_bytes": ag_saved,
         "loss_path_overhead_bytes": int(N * nVB * 8 + N * 8),
         "materialized_logits_fp32_bytes": N * V * 4,
         "materialized_baseline": mat,

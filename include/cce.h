@@ -43,8 +43,16 @@
  *  - Pointers marked (device) are device memory on the current HIP device;
  *    (host) are host memory.  The library never allocates, frees or
  *    synchronises in cce_forward / cce_backward: it enqueues kernels on
- *    `stream` and returns.  The caller owns every buffer, including the
- *    workspace, and keeps them alive until the stream work completes.
+ *    `stream` and returns.  The caller owns every buffer, including the two
+ *    that carry the library's own data: the forward state (written by
+ *    cce_forward, read by cce_backward: O(N + N*V/128 + 512*D) floats, the
+ *    per-block partials the backward's filter reuses) and the backward
+ *    workspace (scratch of one cce_backward call: the gradient tiles of a
+ *    vocabulary chunk, e transposed, dE accumulation), and keeps them alive
+ *    until the stream work completes.  Between forward and backward only the
+ *    state needs to be kept (about 41 MB at N = 4096, D = 4096, V = 128256,
+ *    against 2.1 GB of fp32 logits); the workspace can be allocated for the
+ *    backward and freed after it.
  *  - Layout: row-major, contiguous, base pointers 16-byte aligned.  e is
  *    [N, D], c is [V, D] (D contiguous); e and c share one dtype; outputs are
  *    float32 (dE, dC: see cce_backward).  D must be a multiple of 8 (bf16)
@@ -60,9 +68,9 @@
  *    mean or sum is NaN), its gradient row is NaN, and cce_read_stats
  *    reports it in bad_targets.  No exception crosses the ABI.
  *  - Reentrancy: apart from the measurement hook at the end of this header,
- *    the library keeps no global mutable state; calls on different
- *    workspaces may run concurrently.  Two calls sharing one workspace must
- *    be ordered on one stream.
+ *    the library keeps no global mutable state; calls on different states and
+ *    workspaces may run concurrently.  Two calls sharing a state or a
+ *    workspace must be ordered on one stream.
  */
 #ifndef CCE_H_
 #define CCE_H_
@@ -81,7 +89,7 @@ typedef enum {
   CCE_OK = 0,
   CCE_ERR_INVALID_ARG = -1, /* null pointer, negative N or non-positive D / V, bad enum, misalignment */
   CCE_ERR_UNSUPPORTED = -2, /* softcap with label smoothing, D not a multiple of the vector width, size limits */
-  CCE_ERR_WORKSPACE = -3,   /* workspace smaller than cce_workspace_size() */
+  CCE_ERR_WORKSPACE = -3,   /* state or workspace smaller than cce_state_size() / cce_workspace_size() */
   CCE_ERR_HIP = -4          /* a HIP launch or copy reported an error */
 } cce_status;
 
@@ -102,17 +110,26 @@ typedef struct {
 } cce_stats;
 
 /*
- * Bytes of device workspace needed by cce_forward and cce_backward for this
- * problem.  vocab_chunk = 0 picks the library default: the backward forms
- * gradient tiles for a vocabulary chunk at a time and keeps that chunk's
- * G block in the workspace (bf16: once, token-major; fp32: in both
- * orientations; under 2 GiB by default: the whole vocabulary for N up to
- * about 8192 with bf16), plus e transposed (N*D elements); a positive value (a multiple
- * of 256) sets the chunk width, trading workspace for launches (a 512 MiB
- * chunk measured about 2% slower at N = 4096, D = 4096, V = 128256).  It also
- * holds an fp32 [N, D] accumulation of dE for bf16 gradients that more than
- * one pass adds up.  The forward uses only the first part (per-row partials,
- * O(N + N*V/128 + 512*D) floats).  Returns 0 for invalid arguments.
+ * Bytes of the forward state for this problem: the int32 counters, the
+ * per-(row, 128-vocab block) (max, sum-exp) partials, the per-row loss and,
+ * for label smoothing, the classifier column sum and its row-block partials.
+ * Returns 0 for invalid arguments.
+ */
+size_t cce_state_size(int64_t N, int64_t D, int64_t V, int dtype);
+
+/*
+ * Bytes of the backward workspace for this problem and vocab_chunk.
+ * vocab_chunk = 0 picks the library default: the backward forms the gradient
+ * tiles G of one vocabulary chunk at a time and keeps that chunk's G in the
+ * workspace (bf16: once, token-major; fp32: in both orientations), at most
+ * 256 MiB of it but never fewer than 8192 columns (the vocabulary cut into
+ * nearly equal chunks of whole 256-wide tiles: 4 chunks at N = 4096,
+ * V = 128256, 16 at N = 16384), plus e transposed (N*D elements), an fp32
+ * [N, D] accumulation of dE for bf16 gradients that more than one pass adds
+ * up, and the compaction and keep-map arrays: about 0.39 GB at N = 4096,
+ * D = 4096, V = 128256 (1.2 GB with the whole vocabulary in one chunk).  A
+ * positive value (a multiple of 256) sets the chunk width, trading workspace
+ * for launches.  Returns 0 for invalid arguments.
  */
 size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk);
 
@@ -139,21 +156,25 @@ int64_t cce_vocab_chunk(int64_t N, int64_t D, int64_t V, int dtype, int64_t voca
  * float [N] receives every row's LSE (ignored rows included).  n_valid
  * (device) int32 [1] receives the non-ignored count; may be NULL.  softcap: 0 for
  * none, s > 0 (finite) for s tanh(z / s); negative or non-finite values are
- * CCE_ERR_INVALID_ARG.  ws
- * (device) of ws_bytes >= cce_workspace_size(N, D, V, dtype, vocab_chunk) for
- * the vocab_chunk the backward will use; it holds the per-block partials the
- * backward's filter reads, so keep it unmodified between the two calls.
+ * CCE_ERR_INVALID_ARG.  state (device) of state_bytes >= cce_state_size(N, D,
+ * V, dtype) receives the forward state (the per-block partials the backward's
+ * filter reads, the counters cce_read_stats reports): keep it unmodified
+ * between this call and cce_backward.  A state smaller than that is
+ * CCE_ERR_WORKSPACE.
  */
 cce_status cce_forward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
                        int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
-                       float label_smoothing, float z_loss, float* loss, float* lse, int32_t* n_valid, void* ws,
-                       size_t ws_bytes, cce_stream_t stream);
+                       float label_smoothing, float z_loss, float* loss, float* lse, int32_t* n_valid, void* state,
+                       size_t state_bytes, cce_stream_t stream);
 
 /*
  * Backward.  Same e, c, bias, targets, sizes, dtype, ignore_index, reduction,
  * softcap, label_smoothing and z_loss as the forward; lse (device) float [N] is
- * the forward's output and ws is the forward's workspace, unmodified (with
- * label smoothing it also holds the forward's column sum of c).  grad_loss (device) float is the
+ * the forward's output and state is the forward's state, unmodified (with
+ * label smoothing it also holds the forward's column sum of c; the backward
+ * only updates its counters).  ws (device) of ws_bytes >=
+ * cce_workspace_size(N, D, V, dtype, vocab_chunk) is this call's scratch (its
+ * contents on entry do not matter).  grad_loss (device) float is the
  * upstream gradient: [N] for NONE, [1] otherwise.  filter = 1 skips tiles
  * whose softmax is below 2^-12 everywhere (and that hold no target); 0
  * computes every tile.  accum = CCE_ACCUM_DETERMINISTIC gives run-to-run
@@ -169,21 +190,34 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
  * [V] or NULL: when given, overwritten with the bias gradient db_j =
  * sum_i G_ij (column sums of the filtered gradient tiles, in a fixed order
  * in both accum modes); it is defined with or without a bias.  vocab_chunk as
- * in cce_workspace_size.
+ * in cce_workspace_size.  A state or workspace smaller than its size is
+ * CCE_ERR_WORKSPACE.
  */
 cce_status cce_backward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
                         int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
                         float label_smoothing, float z_loss, const float* lse, const float* grad_loss, int filter,
-                        int accum, int64_t vocab_chunk, int grad_dtype, void* dE, void* dC, float* dbias, void* ws,
-                        size_t ws_bytes, cce_stream_t stream);
+                        int accum, int64_t vocab_chunk, int grad_dtype, void* dE, void* dC, float* dbias,
+                        void* state, size_t state_bytes, void* ws, size_t ws_bytes, cce_stream_t stream);
 
 /*
- * Copies the workspace counters to `out` (host) after the work queued on
+ * Copies the state's counters to `out` (host) after the work queued on
  * `stream` so far; the one call here that synchronises (the stream).  N, V
- * describe the problem the workspace was used for (for tiles_total).
+ * describe the problem the state was used for (for tiles_total).
  */
-cce_status cce_read_stats(const void* ws, size_t ws_bytes, int64_t N, int64_t V, cce_stream_t stream,
+cce_status cce_read_stats(const void* state, size_t state_bytes, int64_t N, int64_t V, cce_stream_t stream,
                           cce_stats* out);
+
+/*
+ * Copies the tile keep map of the last cce_backward that used `ws` (device) to
+ * `out` (host), ceil(N/256) x ceil(V/256) bytes, row-major: 1 where that
+ * backward computed the gradient tile, 0 where the filter dropped it.  Row
+ * block b is the b-th group of 256 non-ignored rows in order (ignored rows
+ * belong to no block; blocks past the non-ignored rows are 0).  N, D, V,
+ * dtype and vocab_chunk are those of the backward (they fix the layout of
+ * ws).  Synchronises `stream`.  A test and measurement aid.
+ */
+cce_status cce_read_keep_map(const void* ws, size_t ws_bytes, int64_t N, int64_t D, int64_t V, int dtype,
+                             int64_t vocab_chunk, uint8_t* out, cce_stream_t stream);
 
 /* Static description of a status code. */
 const char* cce_status_string(int status);

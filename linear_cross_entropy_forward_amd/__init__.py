@@ -6,8 +6,8 @@ in the library's HIP kernels, on the caller's current torch stream.  PyTorch
 provides device memory and streams.
 
     loss = linear_cross_entropy(e, c, targets)             # [..., D], [V, D], [...]
-    loss, lse, n_valid, ws = forward(e, c, targets)        # raw C-ABI calls
-    dE, dC = backward(e, c, targets, lse, grad, ws)
+    loss, lse, n_valid, state = forward(e, c, targets)     # raw C-ABI calls
+    dE, dC = backward(e, c, targets, lse, grad, state)
 
 There is no fallback: without the built library (or without a GPU) every call
 raises.
@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["forward", "backward", "read_stats", "workspace_size", "linear_cross_entropy", "cce_loss",
+__all__ = ["forward", "backward", "read_stats", "state_size", "workspace_size", "linear_cross_entropy", "cce_loss",
            "tile_shape", "lib", "CCEError", "library_path"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
                        f"`python -m linear_cross_entropy_forward_amd.build`")
     L = ctypes.CDLL(library_path)
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.cce_state_size.restype = sz
+    L.cce_state_size.argtypes = [i64, i64, i64, i32]
     L.cce_workspace_size.restype = sz
     L.cce_workspace_size.argtypes = [i64, i64, i64, i32, i64]
     L.cce_vocab_chunk.restype = i64
@@ -63,9 +65,11 @@ def lib() -> ctypes.CDLL:
                               vp]
     L.cce_backward.restype = i32
     L.cce_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, f32, f32, vp, vp, i32, i32, i64,
-                               i32, vp, vp, vp, vp, sz, vp]
+                               i32, vp, vp, vp, vp, sz, vp, sz, vp]
     L.cce_read_stats.restype = i32
     L.cce_read_stats.argtypes = [vp, sz, i64, i64, vp, ctypes.POINTER(_Stats)]
+    L.cce_read_keep_map.restype = i32
+    L.cce_read_keep_map.argtypes = [vp, sz, i64, i64, i64, i32, i64, vp, vp]
     L.cce_status_string.restype = ctypes.c_char_p
     L.cce_status_string.argtypes = [i32]
     L.cce_tile_shape.restype = None
@@ -109,7 +113,18 @@ def tile_shape() -> tuple[int, int, int]:
     return a.value, b.value, c.value
 
 
+def state_size(N: int, D: int, V: int, dtype: torch.dtype = torch.bfloat16) -> int:
+    """Bytes of the forward state (cce_state_size): what the backward needs
+    from the forward."""
+    code = 0 if dtype == torch.bfloat16 else 1
+    n = lib().cce_state_size(N, D, V, code)
+    if n == 0:
+        raise CCEError("invalid sizes for cce_state_size")
+    return n
+
+
 def workspace_size(N: int, D: int, V: int, dtype: torch.dtype = torch.bfloat16, vocab_chunk: int = 0) -> int:
+    """Bytes of the backward's scratch workspace (cce_workspace_size)."""
     code = 0 if dtype == torch.bfloat16 else 1
     n = lib().cce_workspace_size(N, D, V, code, vocab_chunk)
     if n == 0:
@@ -148,12 +163,12 @@ def _validate_bias(bias, c):
 
 
 def forward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, ignore_index: int = -100,
-            reduction: str = "mean", softcap: float = 0.0, ws: torch.Tensor | None = None,
-            vocab_chunk: int = 0, bias: torch.Tensor | None = None, label_smoothing: float = 0.0,
-            z_loss: float = 0.0):
-    """cce_forward.  Returns (loss, lse, n_valid, ws); loss is [N] for
-    reduction='none', else a 0-dim tensor.  `ws` (uint8, device) is allocated
-    if not given and must be passed unchanged to backward().  `bias` [V] (the
+            reduction: str = "mean", softcap: float = 0.0, state: torch.Tensor | None = None,
+            bias: torch.Tensor | None = None, label_smoothing: float = 0.0, z_loss: float = 0.0):
+    """cce_forward.  Returns (loss, lse, n_valid, state); loss is [N] for
+    reduction='none', else a 0-dim tensor.  `state` (uint8, device; the
+    per-block partials and counters, O(N + N V / 128) floats) is allocated if
+    not given and must be passed unchanged to backward().  `bias` [V] (the
     classifier's dtype) is optional; label_smoothing (eps in [0, 1]) and
     z_loss (lam >= 0) add the soft-target and lam * LSE^2 terms; softcap = s > 0
     replaces the logits by s * tanh(z / s) (not with label smoothing)."""
@@ -162,32 +177,34 @@ def forward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, ignore_inde
     N, D = e.shape
     V = c.shape[0]
     dev = e.device
-    need = workspace_size(N, D, V, e.dtype, vocab_chunk)
-    if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if state is None:
+        state = torch.empty(state_size(N, D, V, e.dtype), dtype=torch.uint8, device=dev)
     red = _REDUCTIONS[reduction]
     loss = torch.empty(N if red == 0 else 1, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev)
     n_valid = torch.empty(1, dtype=torch.int32, device=dev)
     _check(lib().cce_forward(_ptr(e), _ptr(c), _ptr(bias) if bias is not None else None, _ptr(targets), N, D, V,
                              _dtype_code(e), ignore_index, red, softcap, label_smoothing, z_loss,
-                             _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(ws), ws.numel(), _stream()),
+                             _ptr(loss), _ptr(lse), _ptr(n_valid), _ptr(state), state.numel(), _stream()),
            "cce_forward")
-    return (loss if red == 0 else loss[0]), lse, n_valid, ws
+    return (loss if red == 0 else loss[0]), lse, n_valid, state
 
 
 def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch.Tensor,
-             grad_loss: torch.Tensor, ws: torch.Tensor, ignore_index: int = -100, reduction: str = "mean",
+             grad_loss: torch.Tensor, state: torch.Tensor, ignore_index: int = -100, reduction: str = "mean",
              filter: bool = True, accum: str = "deterministic", softcap: float = 0.0, vocab_chunk: int = 0,
              dE: torch.Tensor | None = None, dC: torch.Tensor | None = None, bias: torch.Tensor | None = None,
              want_dbias: bool = False, label_smoothing: float = 0.0, z_loss: float = 0.0,
-             grad_dtype: str = "float32", want_dE: bool = True, want_dC: bool = True):
-    """cce_backward.  grad_loss is float32 [N] ('none') or [1]/0-dim.  Returns
+             grad_dtype: str = "float32", want_dE: bool = True, want_dC: bool = True,
+             ws: torch.Tensor | None = None):
+    """cce_backward.  `state` is the forward's.  `ws` (uint8, device) is the
+    call's scratch workspace: allocated here when not given (and released
+    with the call's last reference).  grad_loss is float32 [N] ('none') or [1]/0-dim.  Returns
     (dE [N, D], dC [V, D]), plus float32 db [V] when want_dbias; dE and dC are
     float32, or with grad_dtype='operand' in e's dtype (written by the kernels,
     accumulated in fp32).  want_dE / want_dC = False leaves that gradient out
     (None; its contraction does not run).  bias, label_smoothing, z_loss and
-    softcap must be those of the forward that filled ws."""
+    softcap must be those of the forward that filled the state."""
     _validate(e, c, targets)
     _validate_bias(bias, c)
     N, D = e.shape
@@ -203,30 +220,48 @@ def backward(e: torch.Tensor, c: torch.Tensor, targets: torch.Tensor, lse: torch
         if x is not None and (x.dtype != gdt or not x.is_contiguous()):
             raise CCEError(f"dE and dC must be contiguous {gdt} tensors")
     db = torch.empty(V, dtype=torch.float32, device=dev) if want_dbias else None
+    if ws is None:
+        ws = torch.empty(workspace_size(N, D, V, e.dtype, vocab_chunk), dtype=torch.uint8, device=dev)
     _check(lib().cce_backward(_ptr(e), _ptr(c), _ptr(bias) if bias is not None else None, _ptr(targets), N, D, V,
                               _dtype_code(e), ignore_index, _REDUCTIONS[reduction], softcap, label_smoothing,
                               z_loss, _ptr(lse), _ptr(g),
                               int(bool(filter)), _ACCUM[accum], vocab_chunk, _GRAD_DTYPE[grad_dtype],
                               _ptr(dE) if dE is not None else None, _ptr(dC) if dC is not None else None,
-                              _ptr(db) if db is not None else None, _ptr(ws), ws.numel(), _stream()),
+                              _ptr(db) if db is not None else None, _ptr(state), state.numel(), _ptr(ws),
+                              ws.numel(), _stream()),
            "cce_backward")
     return (dE, dC, db) if want_dbias else (dE, dC)
 
 
-def read_stats(ws: torch.Tensor, N: int, V: int) -> dict:
-    """Counters of the last forward/backward on `ws` (synchronises the stream)."""
+def read_stats(state: torch.Tensor, N: int, V: int) -> dict:
+    """Counters of the last forward/backward on `state` (synchronises the stream)."""
     s = _Stats()
-    _check(lib().cce_read_stats(_ptr(ws), ws.numel(), N, V, _stream(), ctypes.byref(s)), "cce_read_stats")
+    _check(lib().cce_read_stats(_ptr(state), state.numel(), N, V, _stream(), ctypes.byref(s)), "cce_read_stats")
     return {k: getattr(s, k) for k, _ in _Stats._fields_}
+
+
+def read_keep_map(ws: torch.Tensor, N: int, D: int, V: int, dtype: torch.dtype = torch.bfloat16,
+                  vocab_chunk: int = 0):
+    """Tile keep map [ceil(N/256), ceil(V/256)] (numpy bool) of the last
+    backward that used the workspace `ws` (synchronises the stream)."""
+    import numpy as np
+    nb, nvb = -(-N // 256), -(-V // 256)
+    out = np.zeros((nb, nvb), dtype=np.uint8)
+    code = 0 if dtype == torch.bfloat16 else 1
+    _check(lib().cce_read_keep_map(_ptr(ws), ws.numel(), N, D, V, code, vocab_chunk,
+                                   out.ctypes.data_as(ctypes.c_void_p), _stream()), "cce_read_keep_map")
+    return out.astype(bool)
 
 
 class _CCEFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, e, c, bias, targets, reduction, ignore_index, filter, accum, label_smoothing, z_loss,
                 softcap):
-        loss, lse, _, ws = forward(e, c, targets, ignore_index=ignore_index, reduction=reduction, bias=bias,
-                                   label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap)
-        ctx.save_for_backward(e, c, bias, targets, lse, ws)
+        loss, lse, _, state = forward(e, c, targets, ignore_index=ignore_index, reduction=reduction, bias=bias,
+                                      label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap)
+        # only the forward state (partials and counters) is kept until the
+        # backward; the backward's scratch is allocated there
+        ctx.save_for_backward(e, c, bias, targets, lse, state)
         ctx.cfg = (reduction, ignore_index, filter, accum, label_smoothing, z_loss, softcap)
         return loss
 
@@ -234,14 +269,14 @@ class _CCEFunction(torch.autograd.Function):
     @torch.autograd.function.once_differentiable
     def backward(ctx, grad):
         # first-order only: the kernels' gradients carry no graph of their own
-        e, c, bias, targets, lse, ws = ctx.saved_tensors
+        e, c, bias, targets, lse, state = ctx.saved_tensors
         reduction, ignore_index, filter, accum, label_smoothing, z_loss, softcap = ctx.cfg
         want_db = bias is not None and ctx.needs_input_grad[2]
         if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1] or want_db):
             return None, None, None, None, None, None, None, None, None, None, None
         # gradients in the inputs' dtype, written so by the kernels; a frozen
         # input's gradient is not formed
-        out = backward(e, c, targets, lse, grad, ws, ignore_index=ignore_index, reduction=reduction,
+        out = backward(e, c, targets, lse, grad, state, ignore_index=ignore_index, reduction=reduction,
                        filter=filter, accum=accum, bias=bias, want_dbias=want_db,
                        label_smoothing=label_smoothing, z_loss=z_loss, softcap=softcap, grad_dtype="operand",
                        want_dE=ctx.needs_input_grad[0], want_dC=ctx.needs_input_grad[1])

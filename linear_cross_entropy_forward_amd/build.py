@@ -25,22 +25,39 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libcce.so; returns its path."""
+    """Compile every HIP source (one hipcc process per source, in parallel)
+    and link them into libcce.so; returns its path."""
+    flags = ["-O3", f"--offload-arch={ARCH}", "-std=c++20", "-fPIC",
+             # keep the compiler from forming packed fp32 ALU ops (v_pk_*_f32)
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument"]
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(CSRC, src + f".{os.getpid()}.o")
+        cmd = [hipcc()] + flags + ["-c", "-o", obj, os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        objs.append(obj)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    errs, failed = [], False
+    for p in procs:
+        out = p.communicate()[0]
+        errs += [l for l in out.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+        failed |= p.returncode != 0
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-O3", f"--offload-arch={ARCH}", "-std=c++20", "-fPIC", "-shared",
-           # keep the compiler from forming packed fp32 ALU ops (v_pk_*_f32)
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-command-line-argument",
-           "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                     if "packed-fp32-ops" not in l and l.strip())
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
+        r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs,
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed ({r.returncode}):\n{r.stdout}{r.stderr}")
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     if verbose and errs:
-        print(errs)
+        print("\n".join(errs))
     os.replace(tmp, LIB)
     return LIB
 

@@ -14,7 +14,15 @@ namespace cce {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk, void* base) {
+// Column-sum row blocks for R rows: at least kColMinRows rows per block, at
+// most kColBlocks blocks.
+int colsum_blocks(int64_t R, int& rows_per_block) {
+  const int64_t rpb = std::max<int64_t>(kColMinRows, (R + kColBlocks - 1) / kColBlocks);
+  rows_per_block = (int)rpb;
+  return (int)std::max<int64_t>(1, (R + rpb - 1) / rpb);
+}
+
+Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk, void* state, void* ws) {
   Layout L{};
   if (N < 1) N = 1;  // an empty batch uses only the counters; sized like one row
   const size_t es = dtype == kDtypeBf16 ? 2 : 4;
@@ -27,13 +35,20 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   if (vocab_chunk > 0) {
     vc = vocab_chunk;
   } else {
-    // bf16 keeps G only; fp32 both G and G^T.  Each stays below 2 GiB (32-bit
-    // buffer offsets).
-    const size_t per_col = (size_t)L.Npad + (dtype == kDtypeBf16 ? 0 : (size_t)L.Npad + kGtPad);
-    const size_t cap = (((size_t)1 << 31) - 1) / (((size_t)L.Npad + kGtPad) * es);
-    // and the chunk's classifier rows (one descriptor in the dE contraction)
-    const size_t cap_c = (((size_t)1 << 31) - 1) / ((size_t)D * es);
-    vc = (int64_t)std::min(std::min(kDefaultGBudget / (per_col * es), cap), cap_c) / kTileV * kTileV;
+    // bf16 keeps G only; fp32 both G and G^T.  The widest chunk within the
+    // budget (but at least kMinChunkTiles tiles), each buffer below 2 GiB
+    // (32-bit buffer offsets), and the chunk's classifier rows too (one
+    // descriptor in the dE contraction); then the vocabulary cut into that
+    // many nearly equal chunks of whole tiles.
+    const size_t per_col = ((size_t)L.Npad + kGtPad) * es * (dtype == kDtypeBf16 ? 1 : 2);
+    int64_t tiles = (int64_t)(kDefaultGBudget / (per_col * kTileV));
+    if (tiles < kMinChunkTiles) tiles = kMinChunkTiles;
+    const int64_t cap = (int64_t)((((size_t)1 << 31) - 1) / (((size_t)L.Npad + kGtPad) * es) / kTileV);
+    const int64_t cap_c = (int64_t)((((size_t)1 << 31) - 1) / ((size_t)D * es) / kTileV);
+    tiles = std::min(std::min(tiles, cap), std::min(cap_c, (int64_t)kMaxBlocks));
+    if (tiles < 1) tiles = 1;
+    const int64_t nch = (L.nvb_t + tiles - 1) / tiles;
+    vc = (L.nvb_t + nch - 1) / nch * kTileV;
   }
   if (vc < kTileV) vc = kTileV;
   if (vc > vmax) vc = vmax;
@@ -61,6 +76,8 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   L.g_bytes = (size_t)L.Npad * (size_t)vc * es;
   L.gt_ld = L.Npad + kGtPad;
   L.gt_bytes = dtype == kDtypeBf16 ? 0 : (size_t)L.gt_ld * (size_t)vc * es;
+  int rpb_unused;
+  L.bcol_blocks = colsum_blocks(N, rpb_unused);
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -68,15 +85,16 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     off = align_up(off + bytes, 256);
     return o;
   };
+  // forward state
   const size_t o_hdr = take(kHdrWords * 4);
   const size_t o_part = take((size_t)N * L.nVB * sizeof(float2));
   const size_t o_nll = take((size_t)N * 4);
   const size_t o_csum = take((size_t)D * 4);
   const size_t o_aux = take(64);
   const size_t o_colp = take((size_t)kColBlocks * (size_t)D * 4);
-  const size_t o_r1c = take((size_t)D * 4);
-  // the offsets above do not depend on the vocab chunk; the forward uses
-  // only that leading part
+  L.state_total = off;
+  // backward workspace
+  off = 0;
   const size_t o_scale = take((size_t)L.Npad * 4);
   const size_t o_rowmap = take((size_t)L.Npad * 4);
   const size_t o_scale_c = take((size_t)L.Npad * 4);
@@ -85,6 +103,9 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const size_t o_keep = take((size_t)L.nb * L.nvb_t);
   const size_t o_tlist = take((size_t)L.nb * L.nvb_t * 4);
   const size_t o_tcount = take((size_t)L.nchunks * 4);
+  const size_t o_r1c = take((size_t)D * 4);
+  const size_t o_ssum = take(64);
+  const size_t o_bcolp = take((size_t)L.bcol_blocks * (size_t)D * 4);
   const size_t o_g = take(L.g_bytes);
   const size_t o_gt = take(L.gt_bytes);
   const size_t o_et = take((size_t)D * (size_t)L.Npad * es);
@@ -92,11 +113,17 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const size_t o_dbp = take((size_t)L.nb * (size_t)V * 4);
   const size_t o_dacc = take((size_t)N * (size_t)D * 4);
   L.total = off;
-  if (base) {
-    char* b = (char*)base;
+  if (state) {
+    char* b = (char*)state;
     L.hdr = (int32_t*)(b + o_hdr);
     L.part = (float2*)(b + o_part);
     L.nll_out = (float*)(b + o_nll);
+    L.csum = (float*)(b + o_csum);
+    L.aux = (float*)(b + o_aux);
+    L.colpart = (float*)(b + o_colp);
+  }
+  if (ws) {
+    char* b = (char*)ws;
     L.scale = (float*)(b + o_scale);
     L.rowmap = (int*)(b + o_rowmap);
     L.scale_c = (float*)(b + o_scale_c);
@@ -105,16 +132,15 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     L.keep = (uint8_t*)(b + o_keep);
     L.tlist = (int*)(b + o_tlist);
     L.tcount = (int*)(b + o_tcount);
+    L.r1c = (float*)(b + o_r1c);
+    L.ssum = (float*)(b + o_ssum);
+    L.bcolpart = (float*)(b + o_bcolp);
     L.G = b + o_g;
     L.Gt = b + o_gt;
     L.Et = b + o_et;
     L.dE_part = (float*)(b + o_dep);
-    L.dE_acc = (float*)(b + o_dacc);
     L.db_part = (float*)(b + o_dbp);
-    L.csum = (float*)(b + o_csum);
-    L.r1c = (float*)(b + o_r1c);
-    L.aux = (float*)(b + o_aux);
-    L.colpart = (float*)(b + o_colp);
+    L.dE_acc = (float*)(b + o_dacc);
   }
   return L;
 }
@@ -123,16 +149,16 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Shared checks of forward and backward.  Returns CCE_OK or an error.
 static cce_status check_common(const void* e, const void* c, const int64_t* targets, int64_t N, int64_t D,
-                               int64_t V, int dtype, int reduction, float softcap, const void* ws,
+                               int64_t V, int dtype, int reduction, float softcap, const void* state,
                                int64_t vocab_chunk) {
   // an empty batch (N = 0) may pass null e and targets
-  if (!c || !ws || (N > 0 && (!e || !targets))) return CCE_ERR_INVALID_ARG;
+  if (!c || !state || (N > 0 && (!e || !targets))) return CCE_ERR_INVALID_ARG;
   if (N < 0 || D <= 0 || V <= 0) return CCE_ERR_INVALID_ARG;
   if (dtype != kDtypeBf16 && dtype != kDtypeF32) return CCE_ERR_INVALID_ARG;
   if (reduction != kReductionNone && reduction != kReductionSum && reduction != kReductionMean)
     return CCE_ERR_INVALID_ARG;
   if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return CCE_ERR_INVALID_ARG;
-  if (!aligned16(e) || !aligned16(c) || !aligned16(ws) || ((uintptr_t)targets & 7u)) return CCE_ERR_INVALID_ARG;
+  if (!aligned16(e) || !aligned16(c) || !aligned16(state) || ((uintptr_t)targets & 7u)) return CCE_ERR_INVALID_ARG;
   if (!(softcap >= 0.0f && softcap <= 3.0e38f)) return CCE_ERR_INVALID_ARG;
   // soft-capping is built for bf16 operands only (the fp32 variant is off)
   if (softcap > 0.0f && dtype != kDtypeBf16) return CCE_ERR_UNSUPPORTED;
@@ -143,7 +169,7 @@ static cce_status check_common(const void* e, const void* c, const int64_t* targ
   const int64_t lim = (int64_t)1 << 31;
   if ((N + kTileN) * D * es >= lim || N > (int64_t)kMaxBlocks * kTileN || V >= lim / 2 || D >= lim / 2)
     return CCE_ERR_UNSUPPORTED;
-  Layout L = make_layout(N, D, V, dtype, vocab_chunk, nullptr);
+  Layout L = make_layout(N, D, V, dtype, vocab_chunk, nullptr, nullptr);
   if ((int64_t)L.Vc * D * es >= lim || (int64_t)L.g_bytes >= lim || (int64_t)L.gt_bytes >= lim)
     return CCE_ERR_UNSUPPORTED;
   return CCE_OK;
@@ -189,16 +215,21 @@ using namespace cce;
 
 extern "C" {
 
+size_t cce_state_size(int64_t N, int64_t D, int64_t V, int dtype) {
+  if (N < 0 || D <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
+  return make_layout(N, D, V, dtype, 0, nullptr, nullptr).state_total;
+}
+
 size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk) {
   if (N < 0 || D <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
   if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return 0;
-  return make_layout(N, D, V, dtype, vocab_chunk, nullptr).total;
+  return make_layout(N, D, V, dtype, vocab_chunk, nullptr, nullptr).total;
 }
 
 int64_t cce_vocab_chunk(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk) {
   if (N < 0 || D <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32)) return 0;
   if (vocab_chunk < 0 || vocab_chunk % kTileV != 0) return 0;
-  return make_layout(N, D, V, dtype, vocab_chunk, nullptr).Vc;
+  return make_layout(N, D, V, dtype, vocab_chunk, nullptr, nullptr).Vc;
 }
 
 static bool bias_ok(const void* bias, int dtype) {
@@ -212,19 +243,16 @@ static bool terms_ok(float label_smoothing, float z_loss) {
 
 cce_status cce_forward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
                        int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
-                       float label_smoothing, float z_loss, float* loss, float* lse, int32_t* n_valid, void* ws,
-                       size_t ws_bytes, cce_stream_t stream) {
-  cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, ws, 0);
+                       float label_smoothing, float z_loss, float* loss, float* lse, int32_t* n_valid, void* state,
+                       size_t state_bytes, cce_stream_t stream) {
+  cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, state, 0);
   if (st != CCE_OK) return st;
   if (!bias_ok(bias, dtype) || !terms_ok(label_smoothing, z_loss)) return CCE_ERR_INVALID_ARG;
   if (softcap > 0.0f && label_smoothing > 0.0f) return CCE_ERR_UNSUPPORTED;
   // with N = 0, lse and a per-row loss have no elements (may be null)
   if ((N > 0 && !lse) || ((N > 0 || reduction != kReductionNone) && !loss)) return CCE_ERR_INVALID_ARG;
-  // The forward only touches the leading (chunk-independent) part of the
-  // layout; any workspace sized for some vocab_chunk is large enough for it.
-  Layout L = make_layout(N, D, V, dtype, kTileV, ws);
-  const size_t need = (size_t)((char*)L.scale - (char*)ws);
-  if (ws_bytes < need) return CCE_ERR_WORKSPACE;
+  Layout L = make_layout(N, D, V, dtype, 0, state, nullptr);
+  if (state_bytes < L.state_total) return CCE_ERR_WORKSPACE;
   if (N == 0) {
     const hipError_t err = launch_empty(L, reduction == kReductionNone ? nullptr : loss, n_valid, nullptr, 0,
                                         nullptr, 0, (hipStream_t)stream);
@@ -255,9 +283,9 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
 cce_status cce_backward(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
                         int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
                         float label_smoothing, float z_loss, const float* lse, const float* grad_loss, int filter,
-                        int accum, int64_t vocab_chunk, int grad_dtype, void* dE, void* dC, float* dbias, void* ws,
-                        size_t ws_bytes, cce_stream_t stream) {
-  cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, ws, vocab_chunk);
+                        int accum, int64_t vocab_chunk, int grad_dtype, void* dE, void* dC, float* dbias,
+                        void* state, size_t state_bytes, void* ws, size_t ws_bytes, cce_stream_t stream) {
+  cce_status st = check_common(e, c, targets, N, D, V, dtype, reduction, softcap, state, vocab_chunk);
   if (st != CCE_OK) return st;
   if (!bias_ok(bias, dtype) || ((uintptr_t)dbias & 3u) || !terms_ok(label_smoothing, z_loss))
     return CCE_ERR_INVALID_ARG;
@@ -267,9 +295,9 @@ cce_status cce_backward(const void* e, const void* c, const void* bias, const in
   if ((filter != 0 && filter != 1) || (accum != kAccumDeterministic && accum != kAccumAtomic))
     return CCE_ERR_INVALID_ARG;
   if (grad_dtype != CCE_GRAD_FLOAT32 && grad_dtype != CCE_GRAD_OPERAND) return CCE_ERR_INVALID_ARG;
-  if ((dE && !aligned16(dE)) || (dC && !aligned16(dC))) return CCE_ERR_INVALID_ARG;
-  Layout L = make_layout(N, D, V, dtype, vocab_chunk, ws);
-  if (ws_bytes < L.total) return CCE_ERR_WORKSPACE;
+  if ((dE && !aligned16(dE)) || (dC && !aligned16(dC)) || !ws || !aligned16(ws)) return CCE_ERR_INVALID_ARG;
+  Layout L = make_layout(N, D, V, dtype, vocab_chunk, state, ws);
+  if (state_bytes < L.state_total || ws_bytes < L.total) return CCE_ERR_WORKSPACE;
   if (N == 0) {
     // no rows: dC and db are zero (the smoothing term included), dE is empty
     const size_t ges = grad_dtype == CCE_GRAD_OPERAND && dtype == kDtypeBf16 ? 2 : 4;
@@ -304,11 +332,11 @@ cce_status cce_backward(const void* e, const void* c, const void* bias, const in
   return err == hipSuccess ? CCE_OK : CCE_ERR_HIP;
 }
 
-cce_status cce_read_stats(const void* ws, size_t ws_bytes, int64_t N, int64_t V, cce_stream_t stream,
+cce_status cce_read_stats(const void* state, size_t state_bytes, int64_t N, int64_t V, cce_stream_t stream,
                           cce_stats* out) {
-  if (!ws || !out || ws_bytes < (size_t)kHdrWords * 4 || N < 0 || V <= 0) return CCE_ERR_INVALID_ARG;
+  if (!state || !out || state_bytes < (size_t)kHdrWords * 4 || N < 0 || V <= 0) return CCE_ERR_INVALID_ARG;
   int32_t h[kHdrWords];
-  if (hipMemcpyAsync(h, ws, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+  if (hipMemcpyAsync(h, state, sizeof(h), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
     return CCE_ERR_HIP;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CCE_ERR_HIP;
   out->n_valid = h[kHdrNValid];
@@ -317,6 +345,20 @@ cce_status cce_read_stats(const void* ws, size_t ws_bytes, int64_t N, int64_t V,
   out->tiles_kept = h[kHdrTilesKept];
   out->filter_rows = kTileN;
   out->filter_vocab = kTileV;
+  return CCE_OK;
+}
+
+cce_status cce_read_keep_map(const void* ws, size_t ws_bytes, int64_t N, int64_t D, int64_t V, int dtype,
+                             int64_t vocab_chunk, uint8_t* out, cce_stream_t stream) {
+  if (!ws || !out || N < 0 || D <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32) ||
+      vocab_chunk < 0 || vocab_chunk % kTileV != 0)
+    return CCE_ERR_INVALID_ARG;
+  const Layout L = make_layout(N, D, V, dtype, vocab_chunk, nullptr, const_cast<void*>(ws));
+  if (ws_bytes < L.total) return CCE_ERR_WORKSPACE;
+  const size_t n = (size_t)((N + kTileN - 1) / kTileN) * (size_t)L.nvb_t;
+  if (n == 0) return CCE_OK;
+  if (hipMemcpyAsync(out, L.keep, n, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess) return CCE_ERR_HIP;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CCE_ERR_HIP;
   return CCE_OK;
 }
 

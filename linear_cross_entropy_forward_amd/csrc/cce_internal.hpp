@@ -36,10 +36,15 @@ constexpr int kHdrTilesKept = 2;
 constexpr int kHdrNValidBwd = 3;
 constexpr int kHdrWords = 64;  // 256 bytes
 
-// Default byte budget of the per-chunk gradient tile buffers G and G^T together
-// (2 GiB: one chunk for the whole vocabulary at N = 4096; fewer, longer
-// launches measured faster than 512 MiB chunks).
-constexpr size_t kDefaultGBudget = size_t(2048) << 20;
+// Default byte budget of one vocabulary chunk's gradient tiles (G, and for
+// fp32 operands G^T as well): 256 MiB, but never narrower than
+// kMinChunkTiles vocabulary tiles (so that each chunk's contractions keep
+// K long enough to outweigh the fp32 read-modify-write of dE that every
+// further chunk costs; at N = 16384 both give 8192 columns).  Chunks are
+// balanced: the vocabulary is cut into ceil(V / widest) nearly equal
+// chunks of whole tiles.
+constexpr size_t kDefaultGBudget = size_t(256) << 20;
+constexpr int kMinChunkTiles = 32;
 // Extra elements per row of the transposed gradient tiles (row pitch
 // Npad + kGtPad).  Zero: measured no faster with a padded pitch.
 constexpr int kGtPad = 0;
@@ -73,21 +78,31 @@ struct Problem {
   int grad_bf16;     // dE and dC in bf16 (bf16 operands, grad_dtype = operand dtype)
 };
 
+// Two device buffers, both owned by the caller.  The forward state is what
+// cce_forward writes and cce_backward reads (O(N + N V / 128 + 512 D)
+// floats: the per-block partials, the counters, the classifier column sum);
+// the backward workspace is scratch of one cce_backward call (the vocabulary
+// chunk's gradient tiles, e^T, the compaction arrays, dE accumulation).
 struct Layout {
-  size_t total;     // bytes
+  size_t state_total;  // bytes of the forward state
+  size_t total;        // bytes of the backward workspace
+  // -- forward state
   int32_t* hdr;
   float2* part;     // [N][nVB]
   float* nll_out;   // [N] per-row loss (the caller's loss buffer for 'none')
+  float* csum;      // [D] sum over the vocabulary of the classifier rows (label smoothing)
+  float* aux;       // [0] sum of the bias (label smoothing with a bias)
+  float* colpart;   // [kColBlocks][D] column-sum partials of the forward
+  // -- backward workspace
   float* scale;     // [Npad] per token row (original order), 0 past N
   int* rowmap;      // [Npad] token row of each compacted slot: valid rows, ignored rows, -1
   float* scale_c;   // [Npad] scale per compacted slot (0 for ignored rows and padding)
   float* lse_c;     // [Npad] LSE per compacted slot (+inf for ignored rows and padding)
   int* tgt_c;       // [Npad] target per compacted slot (-1 for ignored rows and padding)
   float* db_part;   // [Npad/256][V] per token block column sums of G (bias gradient)
-  float* csum;      // [D] sum over the vocabulary of the classifier rows (label smoothing)
   float* r1c;       // [D] -eps/V * sum_i scale_i e_i: the smoothing term of every dC row
-  float* aux;       // [0] sum of the bias, [1] sum_i scale_i
-  float* colpart;   // [kColBlocks][D] column-sum partials
+  float* ssum;      // [1] sum_i scale_i (label smoothing's share of db)
+  float* bcolpart;  // [bcol_blocks][D] column-sum partials of the backward
   uint8_t* keep;    // [nb][nvb_t]
   int* tlist;       // per chunk, its kept gradient tiles in launch order (chunk ch at cvb0 * nb)
   int* tcount;      // [nchunks] kept gradient tiles per chunk
@@ -99,12 +114,17 @@ struct Layout {
   int gt_ld;        // row pitch of Gt in elements: Npad + kGtPad
   float* dE_part;   // [splits-1][N][D]
   float* dE_acc;    // [N][D] fp32 accumulation of dE when dE itself is bf16 and more than one pass adds to it
-  int nVB, Npad, nb, nvb_t, Vc, nchunks, splits, splits_atomic;
+  int nVB, Npad, nb, nvb_t, Vc, nchunks, splits, splits_atomic, bcol_blocks;
 };
 
-// Computes the layout for (N, D, V, dtype, vocab_chunk); with base == nullptr
-// only sizes are filled in.
-Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk, void* base);
+
+// Computes the layout for (N, D, V, dtype, vocab_chunk); the pointers of the
+// forward state are set when `state` is given, those of the backward
+// workspace when `ws` is given (sizes are always filled in).
+Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk, void* state, void* ws);
+// Row blocks (the return value) and rows per block of the column sum over R
+// rows.
+int colsum_blocks(int64_t R, int& rows_per_block);
 
 // Kernel ids of the profiling hook (cce_profile_start / cce_profile_stop).
 enum KernelId {

@@ -971,17 +971,17 @@ __device__ __forceinline__ int collect_blocks(const uint8_t* __restrict__ keep, 
 // ============================================================================
 // db[v] = sum over token blocks (in order) of the kept tiles' column sums.
 // ============================================================================
-// With label smoothing, plus r1 * aux[1] = -eps/V * sum_i scale_i.
+// With label smoothing, plus r1 * ssum[0] = -eps/V * sum_i scale_i.
 __global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict__ db_part,
                                                         const uint8_t* __restrict__ keep, int nb, int nvb_t, int V,
-                                                        const float* __restrict__ aux, float r1,
+                                                        const float* __restrict__ ssum, float r1,
                                                         float* __restrict__ db) {
   const int v = blockIdx.x * 256 + threadIdx.x;
   if (v >= V) return;
   float s = 0.f;
   for (int b = 0; b < nb; ++b)
     if (keep[(size_t)b * nvb_t + v / kTileV]) s += db_part[(size_t)b * V + v];
-  db[v] = aux ? s + r1 * aux[1] : s;
+  db[v] = ssum ? s + r1 * ssum[0] : s;
 }
 
 // ============================================================================
@@ -994,19 +994,21 @@ template <class C>
 __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
     const typename C::T* __restrict__ G, const typename C::T* __restrict__ Gt, const typename C::T* __restrict__ Et,
     const uint8_t* __restrict__ keep, int Npad, int Vc, int gt_ld, int D, int V, int nvb_t, int cvb0, int cv0,
-    int clen, int tiles_v, int tiles_d, size_t g_bytes, size_t gt_bytes, const float* __restrict__ r1c,
+    int clen, int tiles_v, int tiles_d, int group, size_t g_bytes, size_t gt_bytes, const float* __restrict__ r1c,
     void* __restrict__ dC, int out_bf16) {
   using T = typename C::T;
   constexpr bool kMN = sizeof(T) == 2;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
-  // Groups of kRasterGroup vocab tiles (each with all its d tiles) are dealt
-  // to the XCDs in turn, group g to XCD g % 8 (work-group i runs on XCD
-  // i % 8): the vocab tiles with many kept token blocks (frequent targets)
-  // sit next to each other, and this spreads them over the XCDs.  Inside a
-  // group the order is the grouped raster (L2 reuse).  The grid has
-  // 8 x kRasterGroup x tiles_d x ceil(groups / 8) work-groups; the spare exit.
-  constexpr int GR = kRasterGroup;
+  // Groups of `group` vocab tiles (each with all its d tiles) are dealt to
+  // the XCDs in turn, group g to XCD g % 8 (work-group i runs on XCD i % 8):
+  // the vocab tiles with many kept token blocks (frequent targets) sit next
+  // to each other, and this spreads them over the XCDs.  Inside a group the
+  // order is the grouped raster (L2 reuse).  The host makes groups narrow
+  // enough that a chunk has at least 8 of them when it can (every XCD gets
+  // work).  The grid has 8 x group x tiles_d x ceil(groups / 8) work-groups;
+  // the spare exit.
+  const int GR = group;
   const int per = GR * tiles_d;
   const int x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
   const int g = x + 8 * (j / per), r = j % per;
@@ -1316,17 +1318,17 @@ static_assert(CfgBf16::WM == kPartialWidth && CfgF32::WM == kPartialWidth, "part
 
 // out[d] = factor * sum_r w_r x[r][d] over R rows (colsum + colsum_reduce).
 template <typename T>
-static void launch_colsum(const T* x, const float* w, int R, int D, float factor, const Layout& L, float* out,
+static void launch_colsum(const T* x, const float* w, int R, int D, float factor, float* colpart, float* out,
                           hipStream_t st) {
   constexpr int VEC = Elem<T>::VEC;
-  const int rpb = max(kColMinRows, (R + kColBlocks - 1) / kColBlocks);
-  const int nblk = (R + rpb - 1) / rpb;  // <= kColBlocks
+  int rpb;
+  const int nblk = colsum_blocks(R, rpb);  // <= kColBlocks: colpart holds [nblk][D]
   prof_before(kKColSum, st);
   hipLaunchKernelGGL(colsum_kernel<T>, dim3((D / VEC + 255) / 256, nblk), dim3(256), 0, st, x, w, R, D, rpb,
-                     L.colpart);
+                     colpart);
   prof_after(kKColSum, st);
   prof_before(kKColReduce, st);
-  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((D + 63) / 64), dim3(1024), 0, st, L.colpart, nblk, D, factor,
+  hipLaunchKernelGGL(colsum_reduce_kernel, dim3((D + 63) / 64), dim3(1024), 0, st, colpart, nblk, D, factor,
                      out);
   prof_after(kKColReduce, st);
 }
@@ -1340,7 +1342,7 @@ static hipError_t launch_forward_t(const Problem& P, const Layout& L, hipStream_
   if (smooth) {
     // sum over the vocabulary of the classifier rows (and of the bias), kept
     // in the workspace for the backward's dE term
-    launch_colsum<T>(c, nullptr, P.V, P.D, 1.f, L, L.csum, st);
+    launch_colsum<T>(c, nullptr, P.V, P.D, 1.f, L.colpart, L.csum, st);
     if (P.bias) {
       prof_before(kKVecSum, st);
       hipLaunchKernelGGL(vec_sum_kernel<T>, dim3(1), dim3(1024), 0, st, (const T*)P.bias, P.V, L.aux);
@@ -1414,12 +1416,12 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   prof_before(kKBwdPrep, st);
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(1024), 0, st, P.targets, P.N, L.Npad, P.V, P.ignore_index,
                      P.reduction, P.grad_loss, (const float*)P.lse, L.scale, L.rowmap, L.scale_c, L.lse_c, L.tgt_c,
-                     L.hdr, smooth ? L.aux + 1 : nullptr);
+                     L.hdr, smooth ? L.ssum : nullptr);
   prof_after(kKBwdPrep, st);
   // dE, dC and db are each optional (a null output is not formed)
   const bool want_dE = P.dE != nullptr, want_dC = P.dC != nullptr;
   // -eps/V * sum_i scale_i e_i: the smoothing share of every dC row
-  if (smooth && want_dC) launch_colsum<T>(e, L.scale, P.N, P.D, r1, L, L.r1c, st);
+  if (smooth && want_dC) launch_colsum<T>(e, L.scale, P.N, P.D, r1, L.bcolpart, L.r1c, st);
   prof_before(kKFilter, st);
   hipLaunchKernelGGL(filter_kernel, dim3((L.nvb_t + 63) / 64, L.nb), dim3(1024), 0, st, P.targets, P.lse,
                      L.part, (const int*)L.rowmap, P.N, P.V, L.nVB, P.ignore_index, L.nvb_t, P.filter, L.keep,
@@ -1470,12 +1472,14 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     prof_after(kKGradTile, st);
     if (want_dC) {
       prof_before(kKDC, st);
-      // vocab-tile groups dealt to the XCDs in turn: a whole number of rounds of 8
-      const int dc_groups = (cnvb + kRasterGroup - 1) / kRasterGroup;
-      const int dc_grid = 8 * kRasterGroup * tiles_d * ((dc_groups + 7) / 8);
+      // vocab-tile groups dealt to the XCDs in turn, at least 8 of them when
+      // the chunk has 8 vocab tiles: a whole number of rounds of 8
+      const int dc_gr = max(1, min(kRasterGroup, cnvb / 8));
+      const int dc_groups = (cnvb + dc_gr - 1) / dc_gr;
+      const int dc_grid = 8 * dc_gr * tiles_d * ((dc_groups + 7) / 8);
       hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(dc_grid), dim3(C::NT), 0, st, (const T*)G, (const T*)L.Gt,
                          (const T*)L.Et, L.keep, L.Npad, L.Vc, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb,
-                         tiles_d, L.g_bytes, L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC,
+                         tiles_d, dc_gr, L.g_bytes, L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC,
                          P.grad_bf16);
       prof_after(kKDC, st);
     }
@@ -1495,7 +1499,7 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   if (P.dbias) {
     prof_before(kKDbReduce, st);
     hipLaunchKernelGGL(db_reduce_kernel, dim3((P.V + 255) / 256), dim3(256), 0, st, L.db_part, L.keep, L.nb,
-                       L.nvb_t, P.V, smooth ? (const float*)L.aux : nullptr, r1, P.dbias);
+                       L.nvb_t, P.V, smooth ? (const float*)L.ssum : nullptr, r1, P.dbias);
     prof_after(kKDbReduce, st);
   }
   const size_t n4 = (size_t)P.N * P.D / 4;  // D is a multiple of 4

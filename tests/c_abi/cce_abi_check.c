@@ -70,14 +70,15 @@ int main(void) {
   }
   memset(c_h, 0, sizeof c_h);
 
-  void *e, *c, *ws;
+  void *e, *c, *state, *ws;
   int64_t* t;
   float *loss, *lse, *dE, *dC;
   int32_t* nv;
   hipStream_t st;
   HIP(hipStreamCreate(&st));
+  const size_t state_bytes = cce_state_size(N, D, V, CCE_DTYPE_BF16);
   const size_t ws_bytes = cce_workspace_size(N, D, V, CCE_DTYPE_BF16, 0);
-  CHECK(ws_bytes > 0, "workspace size");
+  CHECK(state_bytes > 0 && ws_bytes > 0, "state and workspace sizes");
   HIP(hipMalloc(&e, sizeof e_h));
   HIP(hipMalloc(&c, sizeof c_h));
   HIP(hipMalloc((void**)&t, sizeof t_h));
@@ -86,6 +87,7 @@ int main(void) {
   HIP(hipMalloc((void**)&nv, 4));
   HIP(hipMalloc((void**)&dE, N * D * 4));
   HIP(hipMalloc((void**)&dC, V * D * 4));
+  HIP(hipMalloc(&state, state_bytes));
   HIP(hipMalloc(&ws, ws_bytes));
   HIP(hipMemcpy(e, e_h, sizeof e_h, hipMemcpyHostToDevice));
   HIP(hipMemcpy(c, c_h, sizeof c_h, hipMemcpyHostToDevice));
@@ -93,26 +95,26 @@ int main(void) {
 
   /* argument faults come back before any launch */
   CHECK(cce_forward(NULL, c, NULL, t, N, D, V, CCE_DTYPE_BF16, IGNORE, CCE_REDUCTION_MEAN, 0.f, 0.f, 0.f, loss,
-                    lse, nv, ws, ws_bytes, (cce_stream_t)st) == CCE_ERR_INVALID_ARG,
+                    lse, nv, state, state_bytes, (cce_stream_t)st) == CCE_ERR_INVALID_ARG,
         "null e must be CCE_ERR_INVALID_ARG");
   CHECK(cce_forward(e, c, NULL, t, N, D, V, CCE_DTYPE_BF16, IGNORE, CCE_REDUCTION_MEAN, 0.f, 0.f, 0.f, loss, lse,
-                    nv, ws, 1024, (cce_stream_t)st) == CCE_ERR_WORKSPACE,
-        "a short workspace must be CCE_ERR_WORKSPACE");
+                    nv, state, 1024, (cce_stream_t)st) == CCE_ERR_WORKSPACE,
+        "a short state must be CCE_ERR_WORKSPACE");
   CHECK(strlen(cce_status_string(CCE_ERR_WORKSPACE)) > 0, "status string");
 
   int s = cce_forward(e, c, NULL, t, N, D, V, CCE_DTYPE_BF16, IGNORE, CCE_REDUCTION_MEAN, 0.f, 0.f, 0.f, loss, lse,
-                      nv, ws, ws_bytes, (cce_stream_t)st);
+                      nv, state, state_bytes, (cce_stream_t)st);
   CHECK(s == CCE_OK, "forward: %s", cce_status_string(s));
   const float one = 1.0f;
   float* g;
   HIP(hipMalloc((void**)&g, 4));
   HIP(hipMemcpy(g, &one, 4, hipMemcpyHostToDevice));
   s = cce_backward(e, c, NULL, t, N, D, V, CCE_DTYPE_BF16, IGNORE, CCE_REDUCTION_MEAN, 0.f, 0.f, 0.f, lse, g,
-                   1 /* filter */, CCE_ACCUM_DETERMINISTIC, 0, CCE_GRAD_FLOAT32, dE, dC, NULL, ws, ws_bytes,
-                   (cce_stream_t)st);
+                   1 /* filter */, CCE_ACCUM_DETERMINISTIC, 0, CCE_GRAD_FLOAT32, dE, dC, NULL, state, state_bytes,
+                   ws, ws_bytes, (cce_stream_t)st);
   CHECK(s == CCE_OK, "backward: %s", cce_status_string(s));
   cce_stats stats;
-  s = cce_read_stats(ws, ws_bytes, N, V, (cce_stream_t)st, &stats);
+  s = cce_read_stats(state, state_bytes, N, V, (cce_stream_t)st, &stats);
   CHECK(s == CCE_OK, "read_stats: %s", cce_status_string(s));
 
   static float lse_o[N], dE_o[N * D], dC_o[V * D];
@@ -158,7 +160,7 @@ int main(void) {
   CHECK(rel <= 5e-3, "dC relative Frobenius error %g", rel);
 
   hipFree(e); hipFree(c); hipFree(t); hipFree(loss); hipFree(lse); hipFree(nv);
-  hipFree(dE); hipFree(dC); hipFree(ws); hipFree(g);
+  hipFree(dE); hipFree(dC); hipFree(state); hipFree(ws); hipFree(g);
   hipStreamDestroy(st);
   if (fails) return 1;
   printf("cce C ABI check ok: loss %.6f (ln V %.6f), n_valid %d, dC rel err %.2e, %lld/%lld tiles\n", loss_o, lnV,

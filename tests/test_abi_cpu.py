@@ -44,16 +44,22 @@ def test_status_strings_and_tiles(L):
     assert L.cce_kernel_name(17) == b"unknown"
 
 
-def test_workspace_size(L):
-    ws = L.cce_workspace_size
+def test_state_and_workspace_size(L):
+    st, ws = L.cce_state_size, L.cce_workspace_size
+    assert st(-1, 64, 100, 0) == 0 and st(4, 64, 100, 7) == 0 and st(4, 0, 100, 0) == 0
     assert ws(-1, 64, 100, 0, 0) == 0 and ws(4, 64, 100, 7, 0) == 0 and ws(4, 64, 100, 0, 100) == 0
-    assert ws(0, 64, 100, 0, 0) > 0  # an empty batch: the counters
-    a = ws(4096, 4096, 128256, 0, 0)
-    b = ws(4096, 4096, 128256, 0, 1024)
-    assert a > b > 0
-    # loss-path part: partials of N x ceil(V/128) (max, sum-exp) pairs dominate
+    assert st(0, 64, 100, 0) > 0 and ws(0, 64, 100, 0, 0) > 0  # an empty batch: the counters
+    # the forward state: N x ceil(V/128) (max, sum-exp) partials dominate; at
+    # the 8B head it stays under 45 MB (the loss-path overhead O(N + N V / 128))
     part = 4096 * ((128256 + 127) // 128) * 8
-    assert b > part
+    s8 = st(4096, 4096, 128256, 0)
+    assert part < s8 < 45e6
+    # the backward workspace: 4 vocabulary chunks of G (<= 256 MiB) plus e^T and
+    # the fp32 dE accumulation; the whole vocabulary in one chunk is larger
+    a = ws(4096, 4096, 128256, 0, 0)
+    whole = ws(4096, 4096, 128256, 0, 128256 + 256 - 128256 % 256)
+    assert 256 << 20 < a < 450e6 < whole
+    assert ws(4096, 4096, 128256, 0, 1024) < a
     assert ws(4096, 4096, 128256, 1, 0) >= ws(4096, 4096, 128256, 0, 0) // 2
 
 
@@ -63,16 +69,16 @@ def test_vocab_chunk(L):
     assert vc(4, 0, 100, 0, 0) == 0
     d = vc(4096, 4096, 128256, 0, 0)
     assert d % 256 == 0 and 256 <= d <= 128256 + 255
-    # the default keeps a chunk's gradient tiles within 2 GiB, each buffer
-    # below 2^31 bytes: bf16 stores them once (token-major), the whole
-    # vocabulary at N = 4096 and about half of it at N = 16384; fp32 stores
-    # both orientations
-    assert d >= 128256 and vc(16384, 4096, 128256, 0, 0) == 65280
-    assert 16384 * vc(16384, 4096, 128256, 0, 0) * 2 < 1 << 31
-    assert vc(16384, 4096, 128256, 1, 0) == 16384 and 2 * 16384 * 16384 * 4 <= 2048 << 20
+    # the default keeps a chunk's gradient tiles G within 256 MiB (bf16 stores
+    # them once, fp32 in both orientations) but at least 8192 columns wide,
+    # in nearly equal chunks of whole tiles: 4 chunks of 126 tiles at N = 4096
+    assert d == 126 * 256 and 4096 * d * 2 <= 256 << 20
+    assert vc(16384, 4096, 128256, 0, 0) == 8192
+    assert vc(65536, 4096, 128256, 0, 0) == 8192 and 65536 * 8192 * 2 < 1 << 31
+    assert vc(4096, 4096, 128256, 1, 0) == 8192 and 2 * 4096 * 8192 * 4 <= 256 << 20
     # ... and a chunk's classifier rows below 2^31 bytes: a classifier larger
     # than that (Gemma-2-27B's 256000 x 4608 bf16, 2.4 GB) is taken in chunks
-    big = vc(4096, 4608, 256000, 0, 0)
+    big = vc(1024, 4608, 256000, 0, 0)
     assert big % 256 == 0 and big * 4608 * 2 < 1 << 31 and big < 256000
     assert vc(4096, 4096, 128256, 0, 1024) == 1024
     assert vc(64, 64, 1000, 1, 0) == 1024          # clamped to the vocabulary, in whole tiles
@@ -81,13 +87,14 @@ def test_vocab_chunk(L):
 
 def _fwd(L, e=FAKE, c=FAKE, t=FAKE, N=64, D=64, V=100, dt=0, ign=-100, red=2, cap=0.0, loss=FAKE, lse=FAKE,
          ws=FAKE, wsb=1 << 30, bias=None, ls=0.0, zl=0.0):
+    # ws / wsb: the forward state
     return L.cce_forward(e, c, bias, t, N, D, V, dt, ign, red, cap, ls, zl, loss, lse, None, ws, wsb, None)
 
 
 def _bwd(L, e=FAKE, N=64, D=64, V=100, dt=0, red=2, cap=0.0, flt=1, acc=0, chunk=0, dE=FAKE, wsb=1 << 30,
-         bias=None, db=None, ls=0.0, zl=0.0, gdt=0):
+         bias=None, db=None, ls=0.0, zl=0.0, gdt=0, stb=1 << 30, ws=FAKE, state=FAKE):
     return L.cce_backward(e, FAKE, bias, FAKE, N, D, V, dt, -100, red, cap, ls, zl, FAKE, FAKE, flt, acc, chunk, gdt,
-                          dE, FAKE, db, FAKE, wsb, None)
+                          dE, FAKE, db, state, stb, ws, wsb, None)
 
 
 def test_forward_argument_errors(L):
@@ -99,7 +106,7 @@ def test_forward_argument_errors(L):
     assert _fwd(L, N=-1) == INVALID and _fwd(L, D=-1) == INVALID and _fwd(L, V=0) == INVALID
     # an empty batch is valid (null e / targets allowed); its size checks still apply
     assert _fwd(L, N=0, e=None, t=None, lse=None, wsb=16) == WORKSPACE
-    assert L.cce_workspace_size(0, 64, 100, 0, 0) > 0 and L.cce_workspace_size(-1, 64, 100, 0, 0) == 0
+    assert L.cce_state_size(0, 64, 100, 0) > 0 and L.cce_state_size(-1, 64, 100, 0) == 0
     assert _fwd(L, dt=2) == INVALID
     assert _fwd(L, red=3) == INVALID
     assert _fwd(L, e=FAKE + 4) == INVALID            # misaligned
@@ -131,9 +138,13 @@ def test_backward_argument_errors(L):
     assert _bwd(L, chunk=100) == INVALID
     # dE, dC, dbias each optional, but one of them is needed
     assert L.cce_backward(FAKE, FAKE, None, FAKE, 64, 64, 100, 0, -100, 2, 0.0, 0.0, 0.0, FAKE, FAKE, 1, 0, 0, 0,
-                          None, None, None, FAKE, 1 << 30, None) == INVALID
+                          None, None, None, FAKE, 1 << 30, FAKE, 1 << 30, None) == INVALID
     assert L.cce_backward(FAKE, FAKE, None, FAKE, 64, 64, 100, 0, -100, 2, 0.0, 0.0, 0.0, FAKE, FAKE, 1, 0, 0, 0,
-                          None, FAKE, None, FAKE, 1024, None) == WORKSPACE
+                          None, FAKE, None, FAKE, 1 << 30, FAKE, 1024, None) == WORKSPACE
+    # the state and the workspace are both required, each checked against its size
+    assert _bwd(L, state=None) == INVALID and _bwd(L, ws=None) == INVALID
+    assert _bwd(L, ws=FAKE + 8) == INVALID
+    assert _bwd(L, stb=L.cce_state_size(64, 64, 100, 0) - 1) == WORKSPACE
     assert _bwd(L, gdt=2) == INVALID and _bwd(L, gdt=-1) == INVALID   # grad dtype: float32 or operand
     assert _bwd(L, gdt=1, wsb=1024) == WORKSPACE
     assert _bwd(L, cap=-1.0) == INVALID
@@ -189,3 +200,4 @@ def test_bench_refuses_several_gpus():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
