@@ -67,8 +67,9 @@
  *    ignore_index is not a host-visible fault: its row's loss is NaN (so a
  *    mean or sum is NaN), its gradient row is NaN, and cce_read_stats
  *    reports it in bad_targets.  No exception crosses the ABI.
- *  - Reentrancy: apart from the measurement hook at the end of this header,
- *    the library keeps no global mutable state; calls on different states and
+ *  - Reentrancy: apart from the measurement hook at the end of this header
+ *    (and the no-allocation forward, which shares one device array), the
+ *    library keeps no global mutable state; calls on different states and
  *    workspaces may run concurrently.  Two calls sharing a state or a
  *    workspace must be ordered on one stream.
  */
@@ -166,6 +167,28 @@ cce_status cce_forward(const void* e, const void* c, const void* bias, const int
                        int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
                        float label_smoothing, float z_loss, float* loss, float* lse, int32_t* n_valid, void* state,
                        size_t state_bytes, cce_stream_t stream);
+
+/*
+ * Forward without a state buffer, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments as cce_forward, minus the state: the state
+ * lives in one static device array of CCE_NOALLOC_SCRATCH_BYTES per GPU (the
+ * library's own, held by each GPU the library runs on until the process
+ * ends), so no cce_backward or cce_read_stats can follow this call.  Problems
+ * whose cce_state_size exceeds CCE_NOALLOC_SCRATCH_BYTES (64 MiB: e.g.
+ * N = 4096 tokens at V = 128256, or N = 2048 at V = 256000) return
+ * CCE_ERR_WORKSPACE before any HIP call.  It allocates, frees and
+ * synchronises nothing (the array's device address is looked up once per
+ * device, on the first call with that device current).  Every call on a GPU
+ * shares that GPU's array, which keeps the last call's contents: calls that
+ * overlap on one GPU (two streams, two threads) race and must be ordered by
+ * the caller.
+ */
+#define CCE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+cce_status cce_forward_noalloc(const void* e, const void* c, const void* bias, const int64_t* targets, int64_t N,
+                               int64_t D, int64_t V, int dtype, int64_t ignore_index, int reduction, float softcap,
+                               float label_smoothing, float z_loss, float* loss, float* lse, int32_t* n_valid,
+                               cce_stream_t stream);
 
 /*
  * Backward.  Same e, c, bias, targets, sizes, dtype, ignore_index, reduction,

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.cce_forward.restype = i32
     L.cce_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, f32, f32, vp, vp, vp, vp, sz,
                               vp]
+    L.cce_forward_noalloc.restype = i32
+    L.cce_forward_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, f32, f32, vp, vp, vp, vp]
     L.cce_backward.restype = i32
     L.cce_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i64, i32, f32, f32, f32, vp, vp, i32, i32, i64,
                                i32, vp, vp, vp, vp, sz, vp, sz, vp]

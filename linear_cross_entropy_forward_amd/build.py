@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcce.so")
-SOURCES = ["cce_kernels.hip", "cce_api.hip"]
+SOURCES = ["cce_kernels.hip", "cce_api.hip", "cce_noalloc.hip"]
 ARCH = os.environ.get("CCE_OFFLOAD_ARCH", "gfx950")
 
 

@@ -201,3 +201,14 @@ def test_bench_refuses_several_gpus():
     assert r.returncode != 0
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
 
+
+def test_noalloc_forward_refuses_before_any_launch(L):
+    """The no-allocation forward checks its sizes before any HIP call: a state
+    beyond the static array (64 MiB) and invalid sizes are refused on a
+    machine without a GPU."""
+    N, D, V = 8192, 64, 256000
+    assert L.cce_state_size(N, D, V, 0) > 64 << 20
+    assert L.cce_forward_noalloc(FAKE, FAKE, None, FAKE, N, D, V, 0, -100, 2, 0.0, 0.0, 0.0, FAKE, FAKE, None,
+                                 None) == WORKSPACE
+    assert L.cce_forward_noalloc(FAKE, FAKE, None, FAKE, 64, 0, 100, 0, -100, 2, 0.0, 0.0, 0.0, FAKE, FAKE, None,
+                                 None) == INVALID
