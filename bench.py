@@ -38,11 +38,11 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "874ffa88dadddba57865da167c60d8babd6e3f8a69386586c2f0001f416d1009",
+    "source_sha256": "5d129b15871b3224a3dbee8912d3a16d05a8cffe88f0f10e30af761e3ca67838",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9399.1e6, "grad_tile": 12810.0e6, "dC_gemm": 7486.6e6, "dE_gemm": 6347.0e6,
-        "rows": 121.3e6, "filter": 37.1e6, "transpose_e": 67.3e6,
+        "fwd_tile": 9408.3e6, "grad_tile": 2350.7e6, "dC_gemm": 1912.2e6, "dE_gemm": 1702.9e6,
+        "rows": 121.3e6, "filter": 37.1e6, "transpose_e": 67.3e6, "dE_reduce": 100.7e6,
     },
 }
 
@@ -327,7 +327,12 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
            "executed_flop_frac": exec_frac, "tflops_executed": eff * exec_frac,
            "pct_of_peak_executed": 100.0 * eff * exec_frac / peak,
            "tflops_useful": eff * (4.0 / 6.0 if frozen_classifier else 0.75), "filter": bool(filter),
-           "accum": accum, "frozen_classifier": bool(frozen_classifier),
+           "accum": accum,
+           # the accumulation mode concerns dE only: each dC element has one
+           # owning work-group (whole token contraction), so dC is the same
+           # kernel and the same bits in both modes
+           "accum_applies_to": "dE",
+           "frozen_classifier": bool(frozen_classifier),
            "grad_dtype": "bf16" if gdt == torch.bfloat16 else "f32", "step_ms_graph": graph_ms,
            "tiles_skipped_frac": 1.0 - stats["tiles_kept"] / max(1, stats["tiles_total"]),
            "extra_hbm_bytes": int(extra), "state_bytes": int(state.numel()), "workspace_bytes": int(ws.numel()),
@@ -551,7 +556,7 @@ def main():
         "dtype": "bf16" if dt_name == "bf16" else "f32",
         "data": "synthetic (seeded; e ~ N(0,1), c ~ N(0,0.02^2) bf16, uniform targets)",
         "config": {"workload": args.workload, "N": N, "D": D, "V": V, "reduction": reduction,
-                   "filter": bool(flt), "accum": args.accum, "vocab_chunk": Vc,
+                   "filter": bool(flt), "accum": args.accum, "accum_applies_to": "dE", "vocab_chunk": Vc,
                    "grad_dtype": "bf16" if gdt == torch.bfloat16 else "f32"},
         # effective (unfiltered, 8NVD) flops of the step per second over the
         # dense bf16 peak; not a hardware counter (the matrix cores' busy

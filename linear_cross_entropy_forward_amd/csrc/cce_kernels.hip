@@ -42,10 +42,15 @@
 namespace cce {
 
 constexpr float kLog2e = 1.4426950408889634f;
-#ifndef CCE_RASTER_GROUP
-#define CCE_RASTER_GROUP 8
-#endif
-constexpr int kRasterGroup = CCE_RASTER_GROUP;
+// M tiles per group of the grouped tile order (see grouped_tile), per kernel:
+// the forward and dE keep 8 (their groups share the classifier tiles / the G
+// rows of 8 tiles), the gradient tiles and dC 4 (measured: 8 -> 4 made both
+// about 1% faster at the 8B head, the forward and dE about 0.7% slower; 16
+// was slower everywhere).
+constexpr int kRasterFwd = 8;
+constexpr int kRasterGrad = 4;
+constexpr int kRasterDC = 4;
+constexpr int kRasterDE = 8;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(C::NT, 1) void fwd_tile_kernel(const typename C::T*
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ __attribute__((aligned(16))) float sbias[C::BM];
   int tv, tn;
-  grouped_tile(xcd_remap(blockIdx.x, total), total / tiles_n, tiles_n, kRasterGroup, tv, tn);
+  grouped_tile(xcd_remap(blockIdx.x, total), total / tiles_n, tiles_n, kRasterFwd, tv, tn);
   const int v0 = tv * C::BM, n0 = tn * C::BN;
   if (bias || softcap > 0.f) stage_bias<T, C::BM>(sbias, bias, v0, V);
 
@@ -700,7 +705,7 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const uint8_t* __restri
   const int i0 = min(n, tid * run), i1 = min(n, i0 + run);
   auto kept = [&](int idx) {
     int tvl, tn;
-    grouped_tile(idx, cnvb, tiles_n, kRasterGroup, tvl, tn);
+    grouped_tile(idx, cnvb, tiles_n, kRasterGrad, tvl, tn);
     return keep[(size_t)tn * nvb_t + cvb0 + tvl] != 0;
   };
   int cnt = 0;
@@ -739,7 +744,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   const int cnt = *tcount;
   if ((int)blockIdx.x >= cnt) return;
   int tvl, tn;
-  grouped_tile(tlist[xcd_remap(blockIdx.x, cnt)], tiles_v, tiles_n, kRasterGroup, tvl, tn);
+  grouped_tile(tlist[xcd_remap(blockIdx.x, cnt)], tiles_v, tiles_n, kRasterGrad, tvl, tn);
   const int tv = cvb0 + tvl;
   const int v0 = tv * C::BM, n0 = tn * C::BN;
   if (bias || softcap > 0.f) stage_bias<T, C::BM>(sbias, bias, v0, V);
@@ -914,11 +919,13 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     });
     __syncthreads();
     // token rows of 256 bf16 out of the staging tile, two per instruction:
-    // row `wave * 64 + 2 it + lane / 32`, chunk lane % 32
+    // wave w drains rows [w RPW, (w + 1) RPW), row `w RPW + 2 it + lane / 32`,
+    // chunk lane % 32
+    constexpr int RPW = 256 / (C::NT / 64);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int rr = wave * 64 + it * 2 + (lane >> 5), jc = lane & 31;
+    for (int it = 0; it < RPW / 2; ++it) {
+      const int rr = wave * RPW + it * 2 + (lane >> 5), jc = lane & 31;
       const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(rr, jc * 8));
       __builtin_amdgcn_raw_buffer_store_b128(
           val, rg, (((uint32_t)n0 + (uint32_t)rr) * (uint32_t)Vc + (uint32_t)vl0 + (uint32_t)jc * 8u) * 2u, 0,
@@ -1107,28 +1114,29 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   // (tile order remapped over exactly these, so they spread over all XCDs);
   // the next (tiles_n - nbv) x tiles_d cover the blocks of padding rows,
   // which only need zeros; the rest exit.
-  static_assert(C::NT == C::BN, "a padding tile is zeroed one column per thread");
   const int nbv = valid_blocks(hdr);
   const int work = nbv * tiles_d * splits;
   int s, tn, td;
   if ((int)blockIdx.x < work) {
     const int tile = xcd_remap(blockIdx.x, work);
     s = tile / (nbv * tiles_d);
-    grouped_tile(tile % (nbv * tiles_d), nbv, tiles_d, kRasterGroup, tn, td);
+    grouped_tile(tile % (nbv * tiles_d), nbv, tiles_d, kRasterDE, tn, td);
   } else {
     const int p = (int)blockIdx.x - work;
     if (p >= (tiles_n - nbv) * tiles_d) return;
     // a block of padding rows: zeros into dE and every partial in use, once
     if (accumulate || atomic) return;
     tn = nbv + p / tiles_d;
-    const int d = (p % tiles_d) * C::BN + (int)threadIdx.x;
-    for (int ps = 0; ps < splits; ++ps) {
-      float* o = ps == 0 ? dE : dE_part + (size_t)(ps - 1) * N * D;
-      for (int r = 0; r < C::BM; ++r) {
-        const int row = rowmap[tn * C::BM + r];
-        if (row >= 0 && d < D) {
-          if (o) o[(size_t)row * D + d] = 0.f;
-          else dEb[(size_t)row * D + d] = 0;
+    for (int dd = (int)threadIdx.x; dd < C::BN; dd += C::NT) {
+      const int d = (p % tiles_d) * C::BN + dd;
+      for (int ps = 0; ps < splits; ++ps) {
+        float* o = ps == 0 ? dE : dE_part + (size_t)(ps - 1) * N * D;
+        for (int r = 0; r < C::BM; ++r) {
+          const int row = rowmap[tn * C::BM + r];
+          if (row >= 0 && d < D) {
+            if (o) o[(size_t)row * D + d] = 0.f;
+            else dEb[(size_t)row * D + d] = 0;
+          }
         }
       }
     }
@@ -1312,9 +1320,36 @@ __global__ __launch_bounds__(256) void fill_rank1_kernel(float* __restrict__ dE,
 // ============================================================================
 // Host launchers.
 // ============================================================================
-using CfgBf16 = Cfg<uint16_t, kTileV, kTileN, 2, 2>;
-using CfgF32 = Cfg<float, kTileV, kTileN, 2, 2>;
-static_assert(CfgBf16::WM == kPartialWidth && CfgF32::WM == kPartialWidth, "partial width");
+// Tile configuration of each contraction kernel: 256x256 work-group tiles of
+// 2 x WN_x waves (one wave per SIMD with 2 x 2, two with 2 x 4).
+#ifndef CCE_WN_FWD
+#define CCE_WN_FWD 2
+#endif
+#ifndef CCE_WN_GRAD
+#define CCE_WN_GRAD 2
+#endif
+#ifndef CCE_WN_DC
+#define CCE_WN_DC 2
+#endif
+#ifndef CCE_WN_DE
+#define CCE_WN_DE 2
+#endif
+template <typename T> struct Cfgs;
+template <> struct Cfgs<uint16_t> {
+  using Fwd = Cfg<uint16_t, kTileV, kTileN, 2, CCE_WN_FWD>;
+  using Grad = Cfg<uint16_t, kTileV, kTileN, 2, CCE_WN_GRAD>;
+  using DC = Cfg<uint16_t, kTileV, kTileN, 2, CCE_WN_DC>;
+  using DE = Cfg<uint16_t, kTileV, kTileN, 2, CCE_WN_DE>;
+};
+template <> struct Cfgs<float> {
+  using Fwd = Cfg<float, kTileV, kTileN, 2, 2>;
+  using Grad = Fwd;
+  using DC = Fwd;
+  using DE = Fwd;
+};
+static_assert(Cfgs<uint16_t>::Fwd::WM == kPartialWidth && Cfgs<float>::Fwd::WM == kPartialWidth, "partial width");
+static_assert(Cfgs<uint16_t>::DC::BN == kTileN && Cfgs<uint16_t>::DE::BN == kTileN && Cfgs<float>::DE::BN == kTileN,
+              "d tiles of the gradient contractions");
 
 // out[d] = factor * sum_r w_r x[r][d] over R rows (colsum + colsum_reduce).
 template <typename T>
@@ -1333,9 +1368,9 @@ static void launch_colsum(const T* x, const float* w, int R, int D, float factor
   prof_after(kKColReduce, st);
 }
 
-template <class C>
+template <typename T>
 static hipError_t launch_forward_t(const Problem& P, const Layout& L, hipStream_t st) {
-  using T = typename C::T;
+  using C = typename Cfgs<T>::Fwd;
   const T* e = (const T*)P.e;
   const T* c = (const T*)P.c;
   const bool smooth = P.label_smoothing != 0.f;
@@ -1401,12 +1436,14 @@ hipError_t launch_empty(const Layout& L, float* loss, int32_t* n_valid, void* g,
 }
 
 hipError_t launch_forward(const Problem& P, const Layout& L, hipStream_t st) {
-  return P.dtype == kDtypeBf16 ? launch_forward_t<CfgBf16>(P, L, st) : launch_forward_t<CfgF32>(P, L, st);
+  return P.dtype == kDtypeBf16 ? launch_forward_t<uint16_t>(P, L, st) : launch_forward_t<float>(P, L, st);
 }
 
-template <class C>
+template <typename T>
 static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream_t st) {
-  using T = typename C::T;
+  using CG = typename Cfgs<T>::Grad;
+  using CC = typename Cfgs<T>::DC;
+  using CE = typename Cfgs<T>::DE;
   const T* e = (const T*)P.e;
   const T* c = (const T*)P.c;
   T* G = (T*)L.G;
@@ -1457,14 +1494,14 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     }
   }
   const int tiles_n = L.Npad / kTileN;
-  const int tiles_d = (P.D + C::BN - 1) / C::BN;
+  const int tiles_d = (P.D + kTileN - 1) / kTileN;  // d tiles of dC and dE (BN = 256)
   for (int ch = 0; ch < L.nchunks; ++ch) {
     const int cv0 = ch * L.Vc;
     const int clen = min(L.Vc, P.V - cv0);
     const int cnvb = (clen + kTileV - 1) / kTileV;
     const int cvb0 = cv0 / kTileV;
     prof_before(kKGradTile, st);
-    hipLaunchKernelGGL(grad_tile_kernel<C>, dim3(cnvb * tiles_n), dim3(C::NT), 0, st, c, e, (const T*)P.bias,
+    hipLaunchKernelGGL(grad_tile_kernel<CG>, dim3(cnvb * tiles_n), dim3(CG::NT), 0, st, c, e, (const T*)P.bias,
                        (const int*)L.rowmap, (const int*)L.tgt_c, (const float*)L.lse_c, (const float*)L.scale_c,
                        P.label_smoothing, P.z_loss, P.softcap, (const int*)L.tlist + (size_t)cvb0 * tiles_n,
                        (const int*)L.tcount + ch, P.N, P.D, P.V, cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
@@ -1474,10 +1511,10 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
       prof_before(kKDC, st);
       // vocab-tile groups dealt to the XCDs in turn, at least 8 of them when
       // the chunk has 8 vocab tiles: a whole number of rounds of 8
-      const int dc_gr = max(1, min(kRasterGroup, cnvb / 8));
+      const int dc_gr = max(1, min(kRasterDC, cnvb / 8));
       const int dc_groups = (cnvb + dc_gr - 1) / dc_gr;
       const int dc_grid = 8 * dc_gr * tiles_d * ((dc_groups + 7) / 8);
-      hipLaunchKernelGGL(dC_gemm_kernel<C>, dim3(dc_grid), dim3(C::NT), 0, st, (const T*)G, (const T*)L.Gt,
+      hipLaunchKernelGGL(dC_gemm_kernel<CC>, dim3(dc_grid), dim3(CC::NT), 0, st, (const T*)G, (const T*)L.Gt,
                          (const T*)L.Et, L.keep, L.Npad, L.Vc, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb,
                          tiles_d, dc_gr, L.g_bytes, L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC,
                          P.grad_bf16);
@@ -1486,7 +1523,7 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
     if (want_dE) {
       const int splits = splits_used;
       prof_before(kKDE, st);
-      hipLaunchKernelGGL(dE_gemm_kernel<C>, dim3(tiles_n * tiles_d * splits), dim3(C::NT), 0, st, G, c, L.keep,
+      hipLaunchKernelGGL(dE_gemm_kernel<CE>, dim3(tiles_n * tiles_d * splits), dim3(CE::NT), 0, st, G, c, L.keep,
                          P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits,
                          (const int32_t*)L.hdr, L.Vc, L.g_bytes,
                          bf_direct ? P.dE : (void*)dE32, bf_direct ? 1 : 0, L.dE_part, ch > 0 ? 1 : 0,
@@ -1520,7 +1557,7 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
 }
 
 hipError_t launch_backward(const Problem& P, const Layout& L, hipStream_t st) {
-  return P.dtype == kDtypeBf16 ? launch_backward_t<CfgBf16>(P, L, st) : launch_backward_t<CfgF32>(P, L, st);
+  return P.dtype == kDtypeBf16 ? launch_backward_t<uint16_t>(P, L, st) : launch_backward_t<float>(P, L, st);
 }
 
 }  // namespace cce
