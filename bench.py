@@ -88,13 +88,15 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic(name, N, D, V, es, nVB, chunk_lens):
-    """(flops, bytes) per launch of `name`, averaged over its launches in a step."""
+def algorithmic(name, N, D, V, es, nVB, chunk_lens, tiles_kept=1.0, blocks_kept=1.0):
+    """(flops, bytes) per launch of `name`, averaged over its launches in a
+    step: the work the filter leaves (the gradient tiles on the kept tiles,
+    the two contractions on the kept 32x32 blocks; 2 flops per multiply-add)."""
     if name == "fwd_tile":
         return 2.0 * N * V * D, (N + V) * D * es + N * nVB * 8.0
     if name in ("grad_tile", "dC_gemm", "dE_gemm"):
         f = [2.0 * N * cl * D for cl in chunk_lens]
-        return float(np.mean(f)), 0.0
+        return float(np.mean(f)) * (tiles_kept if name == "grad_tile" else blocks_kept), 0.0
     if name == "rows":
         return 2.0 * N * D, N * (2.0 * D * es + 8 + nVB * 8.0 + 8)
     if name == "reduce":
@@ -317,10 +319,11 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     # effective work: 2NVD per contraction (forward, recompute, dE, dC)
     eff = (6.0 if frozen_classifier else 8.0) * N * V * D / (step_ms * 1e-3) / 1e12
-    # executed work: the forward in full, the backward's contractions on the
-    # kept tiles only
+    # executed work: the forward in full, the recompute on the kept tiles,
+    # the gradient contractions on the kept 32x32 blocks
     kept = stats["tiles_kept"] / max(1, stats["tiles_total"])
-    exec_frac = (2.0 + (4.0 if frozen_classifier else 6.0) * kept) / (6.0 if frozen_classifier else 8.0)
+    kept_b = stats["blocks_kept"] / max(1, stats["blocks_total"])
+    exec_frac = (2.0 + 2.0 * kept + (2.0 if frozen_classifier else 4.0) * kept_b) / (6.0 if frozen_classifier else 8.0)
     out = {"N": N, "D": D, "V": V, "dtype": w.dtype, "reduction": w.reduction, "fwd_ms": fwd_ms,
            "fwd_tokens_per_s": N / (fwd_ms * 1e-3), "step_ms": step_ms, "tokens_per_s": N / (step_ms * 1e-3),
            "tflops_effective": eff, "pct_of_peak_effective": 100.0 * eff / peak,
@@ -335,6 +338,7 @@ def config_summary(name, steps=5, warmup=2, materialized_too=True, with_bias=Fal
            "frozen_classifier": bool(frozen_classifier),
            "grad_dtype": "bf16" if gdt == torch.bfloat16 else "f32", "step_ms_graph": graph_ms,
            "tiles_skipped_frac": 1.0 - stats["tiles_kept"] / max(1, stats["tiles_total"]),
+           "blocks_skipped_frac": 1.0 - stats["blocks_kept"] / max(1, stats["blocks_total"]),
            "extra_hbm_bytes": int(extra), "state_bytes": int(state.numel()), "workspace_bytes": int(ws.numel()),
            "bias": bool(with_bias), "label_smoothing": label_smoothing,
            "z_loss": z_loss, "softcap": softcap}
@@ -468,7 +472,9 @@ def main():
     peak = PEAK_BF16_TFLOPS if dt_name == "bf16" else PEAK_F32_TFLOPS
     tflops = eff_flops / (ms_step * 1e-3) / 1e12
     kept_frac = stats["tiles_kept"] / max(1, stats["tiles_total"])
-    exec_frac = (2.0 + 6.0 * kept_frac) / 8.0
+    kept_bfrac = stats["blocks_kept"] / max(1, stats["blocks_total"])
+    # executed: forward, recompute of the kept tiles, contractions of the kept blocks
+    exec_frac = (2.0 + 2.0 * kept_frac + 4.0 * kept_bfrac) / 8.0
 
     # chunk lengths of the backward, for per-launch algorithmic work
     Vc = M.vocab_chunk(N, D, V, tdt, args.vocab_chunk)
@@ -476,14 +482,14 @@ def main():
     nVB = -(-V // 128)
     kernels = {}
     for name, d in per.items():
-        fl, by = algorithmic(name, N, D, V, es, nVB, chunk_lens)
+        fl, by = algorithmic(name, N, D, V, es, nVB, chunk_lens, kept_frac, kept_bfrac)
         d = dict(d)
         d["tflops"] = fl / (d["avg_ms"] * 1e-3) / 1e12 if fl else None
         d["gbs"] = by / (d["avg_ms"] * 1e-3) / 1e9 if by else None
         d["traffic_bytes"] = traffic_for(name, args.workload)
         kernels[name] = d
     dom = max(per, key=lambda k: per[k]["ms_per_step"])
-    fl, by = algorithmic(dom, N, D, V, es, nVB, chunk_lens)
+    fl, by = algorithmic(dom, N, D, V, es, nVB, chunk_lens, kept_frac, kept_bfrac)
     if dom in MFMA_KERNELS:
         ach = fl / (per[dom]["avg_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
@@ -572,6 +578,7 @@ def main():
         "fwd_ms": fwd_ms,
         "fwd_tokens_per_s": N / (fwd_ms * 1e-3),
         "tiles_kept_frac": stats["tiles_kept"] / max(1, stats["tiles_total"]),
+        "blocks_kept_frac": kept_bfrac,
         "state_bytes": state_bytes,
         "workspace_bytes": ws_bytes,
         "extra_hbm_bytes": int(extra_bytes),

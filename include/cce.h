@@ -19,8 +19,12 @@
  * "How it works" step 4 and the "Code" section, which floors the count at 1).
  * The backward returns dE = G C and dC = G^T E with
  * G = (softmax - onehot(y)) * scale ("Loss functions" step 2: the fused gradient p - y),
- * skipping (token block, vocab block) tiles on which every softmax value is
- * below 2^-12 (README "How it works" item 2; Wijmans et al. abstract).
+ * dropping G on (32 token rows, 32 vocab entries) blocks on which every
+ * softmax value is below 2^-12 and that hold no target (README "How it
+ * works" items 1-2: 32x32 tiles, skipped below 2^-12; Wijmans et al.
+ * abstract): whole 256x256 gradient tiles are skipped from the forward's
+ * per-block maxima, and inside kept tiles the contractions skip the MFMAs of
+ * dropped blocks.
  *
  * Two optional loss terms follow tirogla "Loss functions": label smoothing
  * eps ("How it works" step 3) replaces the one-hot target by the soft target
@@ -108,6 +112,10 @@ typedef struct {
   int64_t tiles_kept;   /* tiles the last backward computed (filter decision)      */
   int64_t filter_rows;  /* Bn: token rows per gradient tile                        */
   int64_t filter_vocab; /* Bv: vocabulary entries per gradient tile                */
+  int64_t blocks_total; /* 32x32 blocks of the last backward: ceil(N/32)*ceil(V/32)  */
+  int64_t blocks_kept;  /* blocks of kept tiles whose G the last backward kept     */
+  int64_t block_rows;   /* 32: token rows per block                                */
+  int64_t block_vocab;  /* 32: vocabulary entries per block                        */
 } cce_stats;
 
 /*
@@ -198,9 +206,10 @@ cce_status cce_forward_noalloc(const void* e, const void* c, const void* bias, c
  * only updates its counters).  ws (device) of ws_bytes >=
  * cce_workspace_size(N, D, V, dtype, vocab_chunk) is this call's scratch (its
  * contents on entry do not matter).  grad_loss (device) float is the
- * upstream gradient: [N] for NONE, [1] otherwise.  filter = 1 skips tiles
- * whose softmax is below 2^-12 everywhere (and that hold no target); 0
- * computes every tile.  accum = CCE_ACCUM_DETERMINISTIC gives run-to-run
+ * upstream gradient: [N] for NONE, [1] otherwise.  filter = 1 drops G on
+ * the 32x32 blocks whose softmax is below 2^-12 everywhere (and that hold no
+ * target), skipping 256x256 tiles made only of such blocks; 0 computes every
+ * tile and block.  accum = CCE_ACCUM_DETERMINISTIC gives run-to-run
  * bitwise-identical results (fixed-order split reduction);
  * CCE_ACCUM_ATOMIC accumulates dE with fp32 atomics.  grad_dtype
  * (cce_grad_dtype) picks the element type of dE (device) [N, D] and dC
@@ -241,6 +250,17 @@ cce_status cce_read_stats(const void* state, size_t state_bytes, int64_t N, int6
  */
 cce_status cce_read_keep_map(const void* ws, size_t ws_bytes, int64_t N, int64_t D, int64_t V, int dtype,
                              int64_t vocab_chunk, uint8_t* out, cce_stream_t stream);
+
+/*
+ * Copies the 32x32 block keep map of the last cce_backward that used `ws`
+ * (device) to `out` (host), ceil(N/32) x ceil(V/32) bytes, row-major: 1 where
+ * that backward kept the block's gradient entries (a block of a kept tile on
+ * which some softmax value reaches 2^-12 or that holds a target), 0 where it
+ * zeroed them.  Row block b is the b-th group of 32 non-ignored rows in order.
+ * Arguments and synchronisation as cce_read_keep_map.
+ */
+cce_status cce_read_block_map(const void* ws, size_t ws_bytes, int64_t N, int64_t D, int64_t V, int dtype,
+                              int64_t vocab_chunk, uint8_t* out, cce_stream_t stream);
 
 /* Static description of a status code. */
 const char* cce_status_string(int status);

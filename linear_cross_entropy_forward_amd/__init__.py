@@ -38,7 +38,9 @@ class CCEError(RuntimeError):
 class _Stats(ctypes.Structure):
     _fields_ = [("n_valid", ctypes.c_int64), ("bad_targets", ctypes.c_int64),
                 ("tiles_total", ctypes.c_int64), ("tiles_kept", ctypes.c_int64),
-                ("filter_rows", ctypes.c_int64), ("filter_vocab", ctypes.c_int64)]
+                ("filter_rows", ctypes.c_int64), ("filter_vocab", ctypes.c_int64),
+                ("blocks_total", ctypes.c_int64), ("blocks_kept", ctypes.c_int64),
+                ("block_rows", ctypes.c_int64), ("block_vocab", ctypes.c_int64)]
 
 
 _lib = None
@@ -72,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.cce_read_stats.argtypes = [vp, sz, i64, i64, vp, ctypes.POINTER(_Stats)]
     L.cce_read_keep_map.restype = i32
     L.cce_read_keep_map.argtypes = [vp, sz, i64, i64, i64, i32, i64, vp, vp]
+    L.cce_read_block_map.restype = i32
+    L.cce_read_block_map.argtypes = [vp, sz, i64, i64, i64, i32, i64, vp, vp]
     L.cce_status_string.restype = ctypes.c_char_p
     L.cce_status_string.argtypes = [i32]
     L.cce_tile_shape.restype = None
@@ -252,6 +256,18 @@ def read_keep_map(ws: torch.Tensor, N: int, D: int, V: int, dtype: torch.dtype =
     code = 0 if dtype == torch.bfloat16 else 1
     _check(lib().cce_read_keep_map(_ptr(ws), ws.numel(), N, D, V, code, vocab_chunk,
                                    out.ctypes.data_as(ctypes.c_void_p), _stream()), "cce_read_keep_map")
+    return out.astype(bool)
+
+
+def read_block_map(ws: torch.Tensor, N: int, D: int, V: int, dtype: torch.dtype = torch.bfloat16,
+                   vocab_chunk: int = 0):
+    """32x32 block keep map [ceil(N/32), ceil(V/32)] (numpy bool) of the last
+    backward that used the workspace `ws` (synchronises the stream)."""
+    import numpy as np
+    out = np.zeros((-(-N // 32), -(-V // 32)), dtype=np.uint8)
+    code = 0 if dtype == torch.bfloat16 else 1
+    _check(lib().cce_read_block_map(_ptr(ws), ws.numel(), N, D, V, code, vocab_chunk,
+                                    out.ctypes.data_as(ctypes.c_void_p), _stream()), "cce_read_block_map")
     return out.astype(bool)
 
 

@@ -30,6 +30,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   L.Npad = (int)((N + kTileN - 1) / kTileN * kTileN);
   L.nb = L.Npad / kTileN;
   L.nvb_t = (int)((V + kTileV - 1) / kTileV);
+  L.nvg = L.nvb_t * kBlocksPerTile;
   const int64_t vmax = (int64_t)L.nvb_t * kTileV;
   int64_t vc;
   if (vocab_chunk > 0) {
@@ -101,6 +102,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const size_t o_lse_c = take((size_t)L.Npad * 4);
   const size_t o_tgt_c = take((size_t)L.Npad * 4);
   const size_t o_keep = take((size_t)L.nb * L.nvb_t);
+  const size_t o_bmask = take((size_t)L.nb * L.nvg);
   const size_t o_tlist = take((size_t)L.nb * L.nvb_t * 4);
   const size_t o_tcount = take((size_t)L.nchunks * 4);
   const size_t o_r1c = take((size_t)D * 4);
@@ -130,6 +132,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     L.lse_c = (float*)(b + o_lse_c);
     L.tgt_c = (int*)(b + o_tgt_c);
     L.keep = (uint8_t*)(b + o_keep);
+    L.bmask = (uint8_t*)(b + o_bmask);
     L.tlist = (int*)(b + o_tlist);
     L.tcount = (int*)(b + o_tcount);
     L.r1c = (float*)(b + o_r1c);
@@ -345,6 +348,10 @@ cce_status cce_read_stats(const void* state, size_t state_bytes, int64_t N, int6
   out->tiles_kept = h[kHdrTilesKept];
   out->filter_rows = kTileN;
   out->filter_vocab = kTileV;
+  out->blocks_total = ((N + kBlock - 1) / kBlock) * ((V + kBlock - 1) / kBlock);
+  out->blocks_kept = h[kHdrBlocksKept];
+  out->block_rows = kBlock;
+  out->block_vocab = kBlock;
   return CCE_OK;
 }
 
@@ -359,6 +366,27 @@ cce_status cce_read_keep_map(const void* ws, size_t ws_bytes, int64_t N, int64_t
   if (n == 0) return CCE_OK;
   if (hipMemcpyAsync(out, L.keep, n, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess) return CCE_ERR_HIP;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CCE_ERR_HIP;
+  return CCE_OK;
+}
+
+cce_status cce_read_block_map(const void* ws, size_t ws_bytes, int64_t N, int64_t D, int64_t V, int dtype,
+                              int64_t vocab_chunk, uint8_t* out, cce_stream_t stream) {
+  if (!ws || !out || N < 0 || D <= 0 || V <= 0 || (dtype != kDtypeBf16 && dtype != kDtypeF32) ||
+      vocab_chunk < 0 || vocab_chunk % kTileV != 0)
+    return CCE_ERR_INVALID_ARG;
+  const Layout L = make_layout(N, D, V, dtype, vocab_chunk, nullptr, const_cast<void*>(ws));
+  if (ws_bytes < L.total) return CCE_ERR_WORKSPACE;
+  const int64_t nrb = (N + kBlock - 1) / kBlock, nvg = (V + kBlock - 1) / kBlock;
+  if (nrb == 0) return CCE_OK;
+  const int64_t nbk = (N + kTileN - 1) / kTileN;
+  std::vector<uint8_t> bytes((size_t)(nbk * L.nvg));
+  if (hipMemcpyAsync(bytes.data(), L.bmask, bytes.size(), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+    return CCE_ERR_HIP;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return CCE_ERR_HIP;
+  // byte (token block, vocab group) holds one bit per 32-row group of the block
+  for (int64_t r = 0; r < nrb; ++r)
+    for (int64_t g = 0; g < nvg; ++g)
+      out[r * nvg + g] = (bytes[(size_t)((r / kBlocksPerTile) * L.nvg + g)] >> (r % kBlocksPerTile)) & 1u;
   return CCE_OK;
 }
 

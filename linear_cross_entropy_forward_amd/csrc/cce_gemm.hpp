@@ -646,10 +646,17 @@ struct DmaTileMN {
 // instructions per MFMA over the first half of its group so the issue never
 // stalls the matrix core.
 // Steps past the end (the count is padded to even) read zeros.
-template <class C, int SPB, bool B_MN = false, bool A_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1)>
+// MFMA block mask of a K step (see mainloop_dma): all blocks on.
+struct NoMask {
+  static constexpr bool kActive = false;
+  __device__ __forceinline__ uint32_t operator()(int) const { return 0xffffffffu; }
+};
+
+template <class C, int SPB, bool B_MN = false, bool A_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1),
+          class MaskT = NoMask>
 __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const Operand& A, const Operand& B,
                                              int nsteps, const uint16_t* blocks, void* smem,
-                                             const int* __restrict__ brow = nullptr) {
+                                             const int* __restrict__ brow = nullptr, const MaskT& mask = MaskT{}) {
   using T = typename C::T;
   using TA = std::conditional_t<A_MN, DmaTileMN<C, C::BM, C::FM>, DmaTile<C, C::BM>>;
   using TB = std::conditional_t<B_MN, DmaTileMN<C, C::BN, C::FN>, DmaTile<C, C::BN>>;
@@ -702,6 +709,12 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   };
 #pragma unroll
   for (int q = 0; q < C::FM + C::FN; ++q) read_one(0, base, 0, q);
+  // With a block mask (MaskT::kActive), mask(s) gives step s's bit
+  // h * FM + fm: the A rows of fragment fm times the K half h (K groups 2h,
+  // 2h + 1) hold nonzero values.  The MFMAs of a zero block are skipped (they
+  // would add exact zeros).  The bits of step s + 1 are read at the top of
+  // step s (LDS, after the first barrier has published them).
+  uint32_t mcur = MaskT::kActive ? (uint32_t)__builtin_amdgcn_readfirstlane((int)mask(0)) : 0xffffffffu;
 
   constexpr int NFR = C::FM + C::FN;
   constexpr int BLOCKS = C::FM * C::FN;
@@ -711,7 +724,11 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   // the top of the step, ahead of the step's fragment reads, so the waits for
   // those cover it and the loop never waits on that read alone.
   auto step = [&](int s, const lds_u8* st, const lds_u8* nx, uint32_t st_addr, uint32_t nx_addr, int k1) -> int {
-    const int k2 = kofs(s + 2);
+    // wave-uniform: kept in a scalar register
+    const int k2 = __builtin_amdgcn_readfirstlane(kofs(s + 2));
+    const uint32_t mnext =
+        MaskT::kActive ? (uint32_t)__builtin_amdgcn_readfirstlane((int)mask(s + 1 < nsteps ? s + 1 : nsteps - 1))
+                       : 0xffffffffu;
     auto group = [&](auto gc) {
       constexpr int g = decltype(gc)::value;
       constexpr bool last = g + 1 == KG;
@@ -725,11 +742,25 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
       constexpr bool has_dma = last || g + 1 < NPARTS;
       constexpr int dlo = has_dma ? dp * NDMA / NPARTS : 0;
       constexpr int dn = has_dma ? (dp + 1) * NDMA / NPARTS - dlo : 0;
+      // With a block mask: the group's fragments (read during the previous
+      // group) are awaited once here, so that the MFMAs of each A fragment
+      // sit under one scalar branch with no waits of their own.
+      if constexpr (MaskT::kActive) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       [&]<int... Q>(std::integer_sequence<int, Q...>) {
         (
             [&] {
               constexpr int b = Q;
-              mma16(acc[b / C::FN][b % C::FN], fa[g & 1][b / C::FN], fb[g & 1][b % C::FN]);
+              if constexpr (MaskT::kActive) {
+                if constexpr (b % C::FN == 0) {
+                  if ((mcur >> ((g >> 1) * C::FM + b / C::FN)) & 1u) {
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; ++fn)
+                      mma16(acc[b / C::FN][fn], fa[g & 1][b / C::FN], fb[g & 1][fn]);
+                  }
+                }
+              } else {
+                mma16(acc[b / C::FN][b % C::FN], fa[g & 1][b / C::FN], fb[g & 1][b % C::FN]);
+              }
               constexpr int r0 = b * NFR / BLOCKS, r1 = (b + 1) * NFR / BLOCKS;
 #pragma unroll
               for (int q = r0; q < r1; ++q) {
@@ -756,12 +787,13 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
     [&]<int... G>(std::integer_sequence<int, G...>) {
       (group(std::integral_constant<int, G>{}), ...);
     }(std::make_integer_sequence<int, KG>{});
+    mcur = mnext;
     return k2;
   };
 
   const lds_u8* st0 = base;
   const lds_u8* st1 = base + STAGE;
-  int kn = kofs(1);
+  int kn = __builtin_amdgcn_readfirstlane(kofs(1));
   for (int s = 0; s < nsteps; s += 2) {
     kn = step(s, st0, st1, base_addr, base_addr + STAGE, kn);
     kn = step(s + 1, st1, st0, base_addr + STAGE, base_addr, kn);

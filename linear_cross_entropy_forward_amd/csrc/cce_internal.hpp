@@ -15,7 +15,13 @@ namespace cce {
 constexpr int kTileV = 256;
 constexpr int kTileN = 256;
 constexpr int kPartialWidth = 128;
-constexpr int kMaxBlocks = 4096;  // K blocks one contraction tile can list
+// The filter's finer level: within a kept tile, 32 token rows x 32 vocab
+// entries, the MFMA output block; the gradient kernel zeroes G on blocks whose
+// softmax stays below 2^-12 (and that hold no target) and the two gradient
+// contractions skip their MFMAs there.
+constexpr int kBlock = 32;
+constexpr int kBlocksPerTile = kTileV / kBlock;  // 8 along either side
+constexpr int kMaxBlocks = 2048;  // K blocks one contraction tile can list
 // Row blocks of the column-sum kernel (partials [kColBlocks][D] in the
 // workspace) and the fewest rows one block takes.
 constexpr int kColBlocks = 512;
@@ -34,6 +40,7 @@ constexpr int kHdrNValid = 0;
 constexpr int kHdrBadTargets = 1;
 constexpr int kHdrTilesKept = 2;
 constexpr int kHdrNValidBwd = 3;
+constexpr int kHdrBlocksKept = 4;
 constexpr int kHdrWords = 64;  // 256 bytes
 
 // Default byte budget of one vocabulary chunk's gradient tiles (G, and for
@@ -104,6 +111,7 @@ struct Layout {
   float* ssum;      // [1] sum_i scale_i (label smoothing's share of db)
   float* bcolpart;  // [bcol_blocks][D] column-sum partials of the backward
   uint8_t* keep;    // [nb][nvb_t]
+  uint8_t* bmask;   // [nb][nvg] per 32-vocab group, bit t: 32-row group t of the token block kept
   int* tlist;       // per chunk, its kept gradient tiles in launch order (chunk ch at cvb0 * nb)
   int* tcount;      // [nchunks] kept gradient tiles per chunk
   void* G;          // [Npad][Vc] operand type: gradient tiles of one vocab chunk
@@ -114,7 +122,7 @@ struct Layout {
   int gt_ld;        // row pitch of Gt in elements: Npad + kGtPad
   float* dE_part;   // [splits-1][N][D]
   float* dE_acc;    // [N][D] fp32 accumulation of dE when dE itself is bf16 and more than one pass adds to it
-  int nVB, Npad, nb, nvb_t, Vc, nchunks, splits, splits_atomic, bcol_blocks;
+  int nVB, Npad, nb, nvb_t, nvg, Vc, nchunks, splits, splits_atomic, bcol_blocks;
 };
 
 

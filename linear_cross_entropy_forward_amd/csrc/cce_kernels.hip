@@ -589,6 +589,7 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int64_t* __restric
   if (tid == 0) {
     hdr[kHdrNValidBwd] = nv;
     hdr[kHdrTilesKept] = 0;
+    hdr[kHdrBlocksKept] = 0;
   }
   if (scale_sum) {  // sum_i scale_i, fixed order (the smoothing share of db)
     ssum[tid] = acc;
@@ -609,6 +610,7 @@ __global__ __launch_bounds__(1024) void filter_kernel(const int64_t* __restrict_
                                                      const float2* __restrict__ part, const int* __restrict__ rowmap,
                                                      int N, int V, int nVB, int64_t ignore_index, int nvb_t,
                                                      int filter, uint8_t* __restrict__ keep,
+                                                     uint8_t* __restrict__ bmask, int nvg,
                                                      int32_t* __restrict__ hdr) {
   constexpr int Bn = kTileN, PPB = kTileV / kPartialWidth;  // partial blocks per vocab tile
   __shared__ float s_lse[Bn];
@@ -680,7 +682,12 @@ __global__ __launch_bounds__(1024) void filter_kernel(const int64_t* __restrict_
 #pragma unroll
     for (int x = 0; x < NW; ++x) any |= s_k[x][lane];
     const bool kk = any != 0 && vb < nvb_t;
-    if (vb < nvb_t) keep[(size_t)b * nvb_t + vb] = kk ? 1 : 0;
+    if (vb < nvb_t) {
+      keep[(size_t)b * nvb_t + vb] = kk ? 1 : 0;
+      // the tile's 32x32 block bits start cleared; the gradient kernel sets
+      // those of the tiles it computes
+      *reinterpret_cast<uint64_t*>(bmask + (size_t)b * nvg + (size_t)vb * kBlocksPerTile) = 0;
+    }
     const uint64_t bal = __ballot(kk);
     if (lane == 0) atomicAdd(&hdr[kHdrTilesKept], (int)__popcll(bal));
   }
@@ -734,15 +741,18 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     const typename C::T* __restrict__ c, const typename C::T* __restrict__ e, const typename C::T* __restrict__ bias,
     const int* __restrict__ rowmap, const int* __restrict__ tgt_c, const float* __restrict__ lse_c,
     const float* __restrict__ scale_c, float eps, float lam, float softcap, const int* __restrict__ tlist,
-    const int* __restrict__ tcount, int N, int D, int V, int cvb0, int tiles_v, int tiles_n, int Vc, int gt_ld, typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes,
-    size_t gt_bytes, float* __restrict__ db_part) {
+    const int* __restrict__ tcount, int N, int D, int V, int cvb0, int tiles_v, int tiles_n, int Vc, int gt_ld,
+    typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes, size_t gt_bytes,
+    float* __restrict__ db_part, uint8_t* __restrict__ bmask, int nvg, int32_t* __restrict__ hdr, int filter) {
   using T = typename C::T;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ __attribute__((aligned(16))) float sbias[C::BM];
+  __shared__ uint32_t sbm[kBlocksPerTile];  // kept 32x32 blocks: per vocab group, one bit per row group
   // the chunk's kept tiles (listed in grouped order), XCD-contiguous runs of
   // the list: the same share of kept tiles on every XCD
   const int cnt = *tcount;
   if ((int)blockIdx.x >= cnt) return;
+  if ((int)threadIdx.x < kBlocksPerTile) sbm[threadIdx.x] = 0;  // visible after the main loop's barriers
   int tvl, tn;
   grouped_tile(tlist[xcd_remap(blockIdx.x, cnt)], tiles_v, tiles_n, kRasterGrad, tvl, tn);
   const int tv = cvb0 + tvl;
@@ -795,6 +805,12 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   // soft-capped, G scaled by the cap's derivative 1 - (z'/s)^2
   const float kcap = softcap > 0.f ? 2.f * kLog2e / softcap : 0.f;
   const float rcap = softcap > 0.f ? 1.f / softcap : 0.f;
+  // The finer filter level (with filtering on): each 32x32 MFMA block (fm,
+  // fn) of the tile (32 vocab rows x 32 token slots) is kept iff one of its
+  // softmax values reaches 2^-12 (log2 argument >= -12) or it holds a target;
+  // a dropped block's G is exactly 0 (the contractions then skip its MFMAs).
+  // kbits bit fn * FM + fm records the wave's kept blocks.
+  uint32_t kbits = 0;
   auto compute = [&](auto ragged, auto mode, auto&& sink) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode)::value;
 #pragma unroll
@@ -802,35 +818,88 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
       auto body = [&](auto with_target) __attribute__((always_inline)) {
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
+          // G of the block's 16 values (this lane's share), kept in registers
+          // until the block's keep decision: the largest log2 softmax value
+          // x = z log2(e) - LSE log2(e) over the block's 32 x 32 entries
+          // against -12, or a target in the block
+          float gq[4][4];
+          float xm = -INFINITY;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            float g[4];
             const int rl = am.row(fm, 4 * q);
             const f32x4 bz = MODE ? bias4(sbias, rl) : f32x4{};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               float z = MODE ? acc[fm][fn][4 * q + u] + bz[u] : acc[fm][fn][4 * q + u];
               if constexpr (MODE == 2) z = softcap_f(z, softcap, kcap);
-              const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lsel[fn]));
+              const float x = __builtin_fmaf(z, kLog2e, -lsel[fn]);
+              const float p = fast_exp2(x);
+              float g;
               if constexpr (decltype(with_target)::value) {
                 const float tsc = trow[fn] == fm * 32 + 8 * q + u ? st[fn] : 0.f;
-                g[u] = __builtin_fmaf(p, sc[fn], -tsc);
+                g = __builtin_fmaf(p, sc[fn], -tsc);
               } else {
-                g[u] = p * sc[fn];
+                g = p * sc[fn];
               }
               if constexpr (MODE == 2) {
                 const float y = z * rcap;
-                g[u] *= __builtin_fmaf(-y, y, 1.f);
+                g *= __builtin_fmaf(-y, y, 1.f);
               }
-              if constexpr (decltype(ragged)::value) g[u] = v0 + rl + u < V ? g[u] : 0.f;
+              if constexpr (decltype(ragged)::value) {
+                const bool in = v0 + rl + u < V;
+                g = in ? g : 0.f;
+                if (in) xm = fmaxf(xm, x);
+              } else {
+                xm = fmaxf(xm, x);
+              }
+              gq[q][u] = g;
             }
-            sink(fn, fm, q, rl, g);
+          }
+          // a target in the block's rows (the lower half-wave's row offset is 0)
+          const bool tgt = decltype(with_target)::value && (threadIdx.x & 32) == 0 && trow[fn] >= 0 &&
+                           (trow[fn] >> 5) == fm;
+          // (filtering off: every block inside the problem is kept)
+          const int wave = (int)(threadIdx.x >> 6);
+          const bool kept = filter ? __builtin_amdgcn_ballot_w64(xm >= -12.f || tgt) != 0
+                                   : v0 + wave / C::WAVES_N * C::WM + fm * 32 < V &&
+                                         n0 + wave % C::WAVES_N * C::WN + fn * 32 < N;
+          kbits |= (kept ? 1u : 0u) << (fn * C::FM + fm);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float g[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) g[u] = kept ? gq[q][u] : 0.f;
+            sink(fn, fm, q, am.row(fm, 4 * q), g);
           }
         }
       };
       if (__builtin_amdgcn_ballot_w64(trow[fn] >= 0 && trow[fn] < C::WM) != 0) body(std::true_type{});
       else body(std::false_type{});
     }
+  };
+  // The wave's kept-block bits into the block mask: byte (token block tn,
+  // vocab group) holds one bit per 32-row group of the token block.  Waves
+  // that share vocab rows combine through LDS (sbm, zeroed before the main
+  // loop); one store per vocab group after `barrier`.
+  auto publish_blocks = [&]() __attribute__((always_inline)) {
+    const int wave = (int)(threadIdx.x >> 6);
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) bits |= ((kbits >> (fn * C::FM + fm)) & 1u) << (wn * C::FN + fn);
+        if (bits) atomicOr(&sbm[wm * C::FM + fm], bits);
+      }
+      const int cnt = __builtin_popcount(kbits);
+      if (cnt) atomicAdd(&hdr[kHdrBlocksKept], cnt);
+    }
+  };
+  auto store_blocks = [&]() __attribute__((always_inline)) {
+    // after a barrier that follows publish_blocks
+    if ((int)threadIdx.x < kBlocksPerTile)
+      bmask[(size_t)tn * nvg + (size_t)tv * kBlocksPerTile + threadIdx.x] = (uint8_t)sbm[threadIdx.x];
   };
   auto run = [&](auto&& sink) __attribute__((always_inline)) {
     auto rag = [&](auto mode) __attribute__((always_inline)) {
@@ -917,7 +986,9 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
         rs[fm][q][3] += __builtin_bit_cast(float, hi & 0xffff0000u);
       }
     });
+    publish_blocks();
     __syncthreads();
+    store_blocks();
     // token rows of 256 bf16 out of the staging tile, two per instruction:
     // wave w drains rows [w RPW, (w + 1) RPW), row `w RPW + 2 it + lane / 32`,
     // chunk lane % 32
@@ -946,6 +1017,9 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) rs[fm][q][u] += g[u];
     });
+    publish_blocks();
+    __syncthreads();
+    store_blocks();
     if (db_part) db_sums(rs);
   }
 }
@@ -976,6 +1050,49 @@ __device__ __forceinline__ int collect_blocks(const uint8_t* __restrict__ keep, 
 }
 
 // ============================================================================
+// 32x32 block masks of the gradient contractions (mainloop_dma MaskT).  The
+// work-group stages, per entry j of its K-block list, the eight block-mask
+// bytes of that K block in LDS (sm[j]); a K step is a quarter of a K block.
+// ============================================================================
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
+
+// dE: A rows are tokens (wave rows: 32-row groups 4 wm .. 4 wm + 3 of the
+// token block), K is vocabulary; sm[j] byte v is vocab group v of the K
+// block, bit t its token group t.
+struct DEMask {
+  static constexpr bool kActive = true;
+  const lds_u64* sm;
+  int shift;  // 4 wm
+  __device__ __forceinline__ uint32_t operator()(int s) const {
+    const uint64_t w = sm[s >> 2];
+    const int sub = s & 3;
+    const uint32_t b0 = (uint32_t)(w >> (16 * sub)) & 0xffu, b1 = (uint32_t)(w >> (16 * sub + 8)) & 0xffu;
+    return ((b0 >> shift) & 0xfu) | (((b1 >> shift) & 0xfu) << 4);
+  }
+};
+
+// dC: A rows are vocabulary (wave rows: vocab groups 4 wm .. 4 wm + 3 of the
+// tile), K is tokens; sm[j] byte v is the tile's vocab group v for token
+// block j, bit t its token group t.
+struct DCMask {
+  static constexpr bool kActive = true;
+  const lds_u64* sm;
+  int shift;  // 32 wm
+  __device__ __forceinline__ uint32_t operator()(int s) const {
+    const uint32_t w = (uint32_t)(sm[s >> 2] >> shift);
+    const int t0 = 2 * (s & 3);
+    uint32_t m = 0;
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      const uint32_t byte = (w >> (8 * fm)) & 0xffu;
+      m |= ((byte >> t0) & 1u) << fm;
+      m |= ((byte >> (t0 + 1)) & 1u) << (4 + fm);
+    }
+    return m;
+  }
+};
+
+// ============================================================================
 // db[v] = sum over token blocks (in order) of the kept tiles' column sums.
 // ============================================================================
 // With label smoothing, plus r1 * ssum[0] = -eps/V * sum_i scale_i.
@@ -997,16 +1114,18 @@ __global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict_
 // bf16 reads G [Npad][Vc] (MN-major) through transposing LDS reads, fp32 the
 // K-major G^T [Vc][gt_ld].
 // ============================================================================
-template <class C>
+template <class C, bool MASK>
 __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
     const typename C::T* __restrict__ G, const typename C::T* __restrict__ Gt, const typename C::T* __restrict__ Et,
     const uint8_t* __restrict__ keep, int Npad, int Vc, int gt_ld, int D, int V, int nvb_t, int cvb0, int cv0,
     int clen, int tiles_v, int tiles_d, int group, size_t g_bytes, size_t gt_bytes, const float* __restrict__ r1c,
-    void* __restrict__ dC, int out_bf16) {
+    void* __restrict__ dC, int out_bf16, const uint8_t* __restrict__ bmask, int nvg) {
   using T = typename C::T;
   constexpr bool kMN = sizeof(T) == 2;
+  static_assert(!MASK || (kMN && C::FM == 4), "block masks: bf16, four 32-row fragments per wave");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
+  __shared__ uint64_t smask[MASK ? kMaxBlocks : 1];
   // Groups of `group` vocab tiles (each with all its d tiles) are dealt to
   // the XCDs in turn, group g to XCD g % 8 (work-group i runs on XCD i % 8):
   // the vocab tiles with many kept token blocks (frequent targets) sit next
@@ -1038,10 +1157,24 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   constexpr int SPB = kTileN / C::BK;
-  // the kept token blocks are the first nk (no filtering effect on this tile;
-  // compacted slots put the blocks of ignored rows last): contiguous K
-  if (nk > 0 && blocks[nk - 1] == nk - 1) mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, nullptr, smem);
-  else mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, blocks, smem);
+  if constexpr (MASK) {
+    // the tile's block-mask bytes for each kept token block, published to the
+    // main loop by its first barrier
+    for (int j = threadIdx.x; j < nk; j += C::NT)
+      smask[j] = *reinterpret_cast<const uint64_t*>(bmask + (size_t)blocks[j] * nvg +
+                                                    (size_t)(cvb0 + tvl) * kBlocksPerTile);
+    const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
+    const DCMask mk{(const lds_u64*)smask, 32 * wm};
+    if (nk > 0 && blocks[nk - 1] == nk - 1)
+      mainloop_dma<C, SPB, false, kMN, 3, DCMask>(acc, A, B, nk * SPB, nullptr, smem, nullptr, mk);
+    else
+      mainloop_dma<C, SPB, false, kMN, 3, DCMask>(acc, A, B, nk * SPB, blocks, smem, nullptr, mk);
+  } else {
+    // the kept token blocks are the first nk (no filtering effect on this
+    // tile; compacted slots put the blocks of ignored rows last): contiguous K
+    if (nk > 0 && blocks[nk - 1] == nk - 1) mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, nullptr, smem);
+    else mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, blocks, smem);
+  }
 
   AccMap<C> am;
   const int vg0 = cv0 + vl0;
@@ -1091,18 +1224,21 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
 // kept vocab blocks of the tile's token block in split `s` of the chunk.
 // A = G (K-major), B = C (MN-major).
 // ============================================================================
-template <class C>
+template <class C, bool MASK>
 __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     const typename C::T* __restrict__ G, const typename C::T* __restrict__ c,
     const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
     int cnvb, int tiles_n, int tiles_d, int splits, const int32_t* __restrict__ hdr, int Vc, size_t g_bytes,
     void* __restrict__ dE_out, int out_bf16,
     float* __restrict__ dE_part, int accumulate, int atomic, const int* __restrict__ rowmap,
-    const float* __restrict__ scale_c, const float* __restrict__ csum, float r1) {
+    const float* __restrict__ scale_c, const float* __restrict__ csum, float r1, const uint8_t* __restrict__ bmask,
+    int nvg) {
   using T = typename C::T;
   // bf16: LDS-DMA main loop (C fragments through transposing reads); fp32:
   // register-staged main loop (no 32-bit transposing read exists)
   constexpr bool kDma = sizeof(T) == 2;
+  static_assert(!MASK || (kDma && C::FM == 4), "block masks: bf16, four 32-row fragments per wave");
+  __shared__ uint64_t smask[MASK ? kMaxBlocks : 1];
   // dE as float, or (out_bf16: one pass writes it, no split or chunk adds to
   // it) as bf16
   float* dE = out_bf16 ? nullptr : (float*)dE_out;
@@ -1169,12 +1305,26 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   constexpr int SPB = kTileV / C::BK;
+  if constexpr (MASK) {
+    // the block-mask bytes of the token block for each of the split's kept
+    // vocab blocks, published to the main loop by its first barrier
+    for (int j = threadIdx.x; j < nk; j += C::NT)
+      smask[j] = *reinterpret_cast<const uint64_t*>(bmask + (size_t)tn * nvg +
+                                                    (size_t)(cvb0 + bl[j]) * kBlocksPerTile);
+  }
   auto loop = [&](const Operand& a, const Operand& b, const uint16_t* bl) {
     // the step's DMA in two parts (right after the barrier and in the first
     // K group) rather than three: measured faster for this kernel's
     // MN-major classifier tile, slower for the K-major ones
-    if constexpr (kDma) mainloop_dma<C, SPB, true, false, 2>(acc, a, b, nk * SPB, bl, smem);
-    else mainloop<C, false, true, SPB>(acc, a, b, nk * SPB, bl, (T*)smem);
+    if constexpr (MASK) {
+      const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
+      const DEMask mk{(const lds_u64*)smask, 4 * wm};
+      mainloop_dma<C, SPB, true, false, 2, DEMask>(acc, a, b, nk * SPB, bl, smem, nullptr, mk);
+    } else if constexpr (kDma) {
+      mainloop_dma<C, SPB, true, false, 2>(acc, a, b, nk * SPB, bl, smem);
+    } else {
+      mainloop<C, false, true, SPB>(acc, a, b, nk * SPB, bl, (T*)smem);
+    }
   };
   // the split's blocks consecutive (every block kept): contiguous K from its
   // first block
@@ -1462,7 +1612,7 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   prof_before(kKFilter, st);
   hipLaunchKernelGGL(filter_kernel, dim3((L.nvb_t + 63) / 64, L.nb), dim3(1024), 0, st, P.targets, P.lse,
                      L.part, (const int*)L.rowmap, P.N, P.V, L.nVB, P.ignore_index, L.nvb_t, P.filter, L.keep,
-                     L.hdr);
+                     L.bmask, L.nvg, L.hdr);
   prof_after(kKFilter, st);
   prof_before(kKTileList, st);
   hipLaunchKernelGGL(tile_list_kernel, dim3(L.nchunks), dim3(1024), 0, st, (const uint8_t*)L.keep, L.nvb_t,
@@ -1495,6 +1645,10 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   }
   const int tiles_n = L.Npad / kTileN;
   const int tiles_d = (P.D + kTileN - 1) / kTileN;  // d tiles of dC and dE (BN = 256)
+  // block masks in the contractions: bf16 operands with filtering (fp32
+  // operands form the same zero blocks of G and contract them densely)
+  constexpr bool MaskOn = sizeof(T) == 2;
+  const bool mask = MaskOn && P.filter != 0;
   for (int ch = 0; ch < L.nchunks; ++ch) {
     const int cv0 = ch * L.Vc;
     const int clen = min(L.Vc, P.V - cv0);
@@ -1505,7 +1659,8 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
                        (const int*)L.rowmap, (const int*)L.tgt_c, (const float*)L.lse_c, (const float*)L.scale_c,
                        P.label_smoothing, P.z_loss, P.softcap, (const int*)L.tlist + (size_t)cvb0 * tiles_n,
                        (const int*)L.tcount + ch, P.N, P.D, P.V, cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
-                       G, (T*)L.Gt, L.g_bytes, L.gt_bytes, P.dbias ? L.db_part : nullptr);
+                       G, (T*)L.Gt, L.g_bytes, L.gt_bytes, P.dbias ? L.db_part : nullptr, L.bmask, L.nvg,
+                       L.hdr, P.filter);
     prof_after(kKGradTile, st);
     if (want_dC) {
       prof_before(kKDC, st);
@@ -1514,22 +1669,25 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
       const int dc_gr = max(1, min(kRasterDC, cnvb / 8));
       const int dc_groups = (cnvb + dc_gr - 1) / dc_gr;
       const int dc_grid = 8 * dc_gr * tiles_d * ((dc_groups + 7) / 8);
-      hipLaunchKernelGGL(dC_gemm_kernel<CC>, dim3(dc_grid), dim3(CC::NT), 0, st, (const T*)G, (const T*)L.Gt,
+      // with filtering (bf16), the 32x32 block masks let dC skip zero blocks
+      auto dck = mask ? dC_gemm_kernel<CC, MaskOn> : dC_gemm_kernel<CC, false>;
+      hipLaunchKernelGGL(dck, dim3(dc_grid), dim3(CC::NT), 0, st, (const T*)G, (const T*)L.Gt,
                          (const T*)L.Et, L.keep, L.Npad, L.Vc, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb,
                          tiles_d, dc_gr, L.g_bytes, L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC,
-                         P.grad_bf16);
+                         P.grad_bf16, (const uint8_t*)L.bmask, L.nvg);
       prof_after(kKDC, st);
     }
     if (want_dE) {
       const int splits = splits_used;
       prof_before(kKDE, st);
-      hipLaunchKernelGGL(dE_gemm_kernel<CE>, dim3(tiles_n * tiles_d * splits), dim3(CE::NT), 0, st, G, c, L.keep,
+      auto dek = mask ? dE_gemm_kernel<CE, MaskOn> : dE_gemm_kernel<CE, false>;
+      hipLaunchKernelGGL(dek, dim3(tiles_n * tiles_d * splits), dim3(CE::NT), 0, st, G, c, L.keep,
                          P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits,
                          (const int32_t*)L.hdr, L.Vc, L.g_bytes,
                          bf_direct ? P.dE : (void*)dE32, bf_direct ? 1 : 0, L.dE_part, ch > 0 ? 1 : 0,
                          P.accum == kAccumAtomic ? 1 : 0, (const int*)L.rowmap,
                          (const float*)L.scale_c,
-                         smooth ? (const float*)L.csum : nullptr, r1);
+                         smooth ? (const float*)L.csum : nullptr, r1, (const uint8_t*)L.bmask, L.nvg);
       prof_after(kKDE, st);
     }
   }

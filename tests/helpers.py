@@ -82,3 +82,20 @@ def check_grad(got, want, rtol, label=""):
     err = rel_fro(got, want)
     assert err <= rtol, (label, err)
     return err
+
+
+def coarsen_keep(margin, tgt, k):
+    """Margins and target flags of tiles made of k x k blocks, from those of
+    the blocks: a tile's largest log-softmax value is the largest of its
+    blocks', and it holds a target iff one of its blocks does (row blocks and
+    tiles are both cut from the non-ignored rows in order, so tile rows are
+    whole groups of k block rows)."""
+    margin = np.asarray(margin, dtype=np.float64)
+    tgt = np.asarray(tgt, dtype=bool)
+    nb, nv = margin.shape
+    NB, NV = -(-nb // k), -(-nv // k)
+    m = np.full((NB * k, NV * k), -np.inf)
+    m[:nb, :nv] = margin
+    t = np.zeros((NB * k, NV * k), dtype=bool)
+    t[:nb, :nv] = tgt
+    return m.reshape(NB, k, NV, k).max(axis=(1, 3)), t.reshape(NB, k, NV, k).any(axis=(1, 3))

@@ -714,6 +714,27 @@ def test_keep_margins_brute_force():
     assert np.array_equal(keep, keep2) and np.array_equal(lse, lse2) and np.array_equal(nll, nll2)
 
 
+def test_keep_margins_coarsen_across_tile_sizes():
+    """The filter at two granularities from one pass: the margins and target
+    flags of 8x8-entry tiles equal the 4x4-entry blocks' coarsened two by two
+    (tests.helpers.coarsen_keep), with ignored rows in the input (row blocks
+    are cut from the non-ignored rows at both sizes)."""
+    from helpers import coarsen_keep
+    g = np.random.default_rng(58)
+    N, D, V = 37, 4, 61
+    e, c = g.standard_normal((N, D)) * 2.5, g.standard_normal((V, D)) * 2.0
+    t = g.integers(0, V, N)
+    t[[0, 9, 10, 30]] = -100
+    _, keep4, _, m4, t4 = O.lse_keep_nll(e, c, t, 4, 4, margins=True)
+    _, keep8, _, m8, t8 = O.lse_keep_nll(e, c, t, 8, 8, margins=True)
+    mc, tc = coarsen_keep(m4, t4, 2)
+    fin = np.isfinite(m8)
+    assert np.array_equal(np.isfinite(mc), fin) and np.array_equal(mc[fin], m8[fin])
+    assert np.array_equal(tc, t8)
+    assert np.array_equal(keep8, (mc >= O.FILTER_LOG_THRESHOLD) | tc)
+    assert keep4.sum() < 4 * keep8.sum()   # the finer map drops entries the coarser keeps
+
+
 # --------------------------------------------------------------------------- logit soft-capping
 # Not defined on the pages: the Gemma 2 form Z' = s tanh(Z / s), after the bias.
 

@@ -13,8 +13,14 @@ import pytest
 
 import oracle as O
 import workloads as W
-from helpers import (GRAD_RTOL, GRAD_RTOL_FILTERED, check_grad, check_keep, check_loss, check_lse, dev,
-                     dev_targets, rel_fro)
+from helpers import (GRAD_RTOL, GRAD_RTOL_FILTERED, check_grad, check_keep, check_loss, check_lse, coarsen_keep,
+                     dev, dev_targets, rel_fro)
+
+# The filter's two levels: gradient tiles of 256 x 256 (decided from the
+# forward's partials) and, inside kept tiles, blocks of 32 x 32 (decided from
+# the recomputed softmax).  The oracle's filtered gradient applies the block
+# rule; the tile map is the block map coarsened.
+BLOCK = 32
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +63,7 @@ def run(M, inp, reduction="mean", filter=False, accum="deterministic", vocab_chu
                          z_loss=zl, softcap=cap, grad_dtype=grad_dtype, ws=bws)
         torch.cuda.synchronize()
         out["keep"] = M.read_keep_map(bws, N, D, V, e.dtype, vocab_chunk)
+        out["blocks"] = M.read_block_map(bws, N, D, V, e.dtype, vocab_chunk)
         del bws
         out["dE"], out["dC"], out["g"] = res[0].float().cpu().numpy(), res[1].float().cpu().numpy(), g_np
         if want_db:
@@ -93,11 +100,14 @@ def full_check(M, inp, reduction, filter, accum="deterministic", vocab_chunk=0, 
     assert (r["dE"][~f.valid] == 0.0).all(), "ignored rows must give exactly 0 gradient"
     Bn, Bv, _ = M.tile_shape()
     if filter:
-        lse_o, keep, _, margin, tgt = O.lse_keep_nll(e, c, t, Bn, Bv, ignore_index=ignore_index, bias=bias,
+        lse_o, keep, _, margin, tgt = O.lse_keep_nll(e, c, t, BLOCK, BLOCK, ignore_index=ignore_index, bias=bias,
                                                      softcap=cap, margins=True)
-        check_keep(r["keep"], margin, tgt, O.FILTER_LOG_THRESHOLD, label)
+        mt, tt = coarsen_keep(margin, tgt, Bn // BLOCK)
+        check_keep(r["keep"], mt, tt, O.FILTER_LOG_THRESHOLD, label + " tiles")
+        check_keep(r["blocks"], margin, tgt, O.FILTER_LOG_THRESHOLD, label + " blocks")
+        assert r["stats"]["blocks_kept"] == int(r["blocks"].sum())
         bf = O.backward(e, c, t, ignore_index=ignore_index, reduction=reduction, grad_loss=r["g"], keep=keep,
-                        tile=(Bn, Bv), bias=bias, **terms)
+                        tile=(BLOCK, BLOCK), bias=bias, **terms)
         check_grad(r["dE"], bf.dE, GRAD_RTOL, label + " dE vs filtered oracle")
         check_grad(r["dC"], bf.dC, GRAD_RTOL, label + " dC vs filtered oracle")
         check_grad(r["dE"], b.dE, filtered_bound(bf.dE, b.dE), label + " dE vs exact")
@@ -117,6 +127,11 @@ def full_check(M, inp, reduction, filter, accum="deterministic", vocab_chunk=0, 
         want_keep = np.zeros_like(r["keep"])
         want_keep[:-(-f.n_valid // Bn)] = True
         assert np.array_equal(r["keep"], want_keep)
+        # unfiltered: every block of the computed tiles is kept
+        want_blocks = np.zeros_like(r["blocks"])
+        want_blocks[:-(-f.n_valid // Bn) * (Bn // BLOCK)] = True
+        assert np.array_equal(r["blocks"], want_blocks)
+        assert r["stats"]["blocks_kept"] == int(r["blocks"].sum())
     return r
 
 
@@ -704,10 +719,9 @@ def test_grad_dtype_operand(M, case):
     f = O.forward(inp["e"], inp["c"], inp["targets"], label_smoothing=ls)
     valid = torch.from_numpy(f.valid).cuda()
     assert (dEo[~valid] == 0).all(), "ignored rows must give exactly 0 gradient"
-    Bn, Bv, _ = M.tile_shape()
-    keep = O.lse_and_keep(inp["e"], inp["c"], inp["targets"], Bn, Bv)[1] if flt else None
+    keep = O.lse_and_keep(inp["e"], inp["c"], inp["targets"], BLOCK, BLOCK)[1] if flt else None
     b = O.backward(inp["e"], inp["c"], inp["targets"], grad_loss=1.0, keep=keep,
-                   tile=(Bn, Bv) if flt else None, label_smoothing=ls)
+                   tile=(BLOCK, BLOCK) if flt else None, label_smoothing=ls)
     check_grad(dEo.float().cpu().numpy(), b.dE, GRAD_RTOL, case + " dE")
     check_grad(dCo.float().cpu().numpy(), b.dC, GRAD_RTOL, case + " dC")
 
@@ -719,8 +733,8 @@ def _oracle_pass(name, with_bias=False, ls=0.0, zl=0.0, cap=0.0):
     inp = W.get(name)
     bias = W.bias(inp["c"].shape[0], inp["workload"].dtype, seed=5) if with_bias else None
     print(f"[full] {name}: oracle full pass", flush=True)
-    return O.lse_keep_nll(inp["e"], inp["c"], inp["targets"], 256, 256, bias=bias, label_smoothing=ls, z_loss=zl,
-                          softcap=cap, margins=True)
+    return O.lse_keep_nll(inp["e"], inp["c"], inp["targets"], BLOCK, BLOCK, bias=bias, label_smoothing=ls,
+                          z_loss=zl, softcap=cap, margins=True)
 
 
 def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, n_vocab=24, dC_check=True,
@@ -761,7 +775,7 @@ def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, 
     nv = int(valid.sum())
     assert r["n_valid"] == nv
     Bn, Bv, _ = M.tile_shape()
-    tile = (Bn, Bv)
+    tile = (BLOCK, BLOCK)
     keep = None
     if full_pass:
         if oracle is None:
@@ -775,9 +789,15 @@ def _sampled_full(M, name, reduction, filter, accum="deterministic", n_rows=48, 
             check_loss(nll_gpu, nll, "none", name + " per-row loss (all rows)")
         check_loss(r["loss"], O.reduce_loss(nll, nv, reduction), reduction, name, nv)
         if filter:
-            nd = check_keep(r["keep"], margin, tgt, O.FILTER_LOG_THRESHOLD, name)
-            print(f"[full] {name}: keep map {int(r['keep'].sum())} of {keep.size} tiles kept "
-                  f"(oracle {int(keep.sum())}; {nd} near-threshold tiles differ)", flush=True)
+            mt, tt = coarsen_keep(margin, tgt, Bn // BLOCK)
+            nd = check_keep(r["keep"], mt, tt, O.FILTER_LOG_THRESHOLD, name + " tiles")
+            nb = check_keep(r["blocks"], margin, tgt, O.FILTER_LOG_THRESHOLD, name + " blocks")
+            kt = (mt >= O.FILTER_LOG_THRESHOLD) | tt
+            print(f"[full] {name}: keep map {int(r['keep'].sum())} of {kt.size} tiles kept "
+                  f"(oracle {int(kt.sum())}; {nd} near-threshold tiles differ), "
+                  f"{int(r['blocks'].sum())} of {keep.size} 32x32 blocks kept (oracle {int(keep.sum())}; "
+                  f"{nb} near-threshold blocks differ)", flush=True)
+            assert r["stats"]["blocks_kept"] == int(r["blocks"].sum())
         assert r["stats"]["tiles_kept"] == int(r["keep"].sum())
     else:
         fo = O.forward(e, c, t, reduction="none", rows=rows, bias=bias, **terms)
