@@ -808,9 +808,11 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   // The finer filter level (with filtering on): each 32x32 MFMA block (fm,
   // fn) of the tile (32 vocab rows x 32 token slots) is kept iff one of its
   // softmax values reaches 2^-12 (log2 argument >= -12) or it holds a target;
-  // a dropped block's G is exactly 0 (the contractions then skip its MFMAs).
+  // a dropped block's G is exactly 0: the bf16 contractions skip its MFMAs
+  // and it is not written at all, the fp32 ones (dense) read stored zeros.
   // kbits bit fn * FM + fm records the wave's kept blocks.
   uint32_t kbits = 0;
+  constexpr bool kSkipDropped = sizeof(T) == 2;
   auto compute = [&](auto ragged, auto mode, auto&& sink) __attribute__((always_inline)) {
     constexpr int MODE = decltype(mode)::value;
 #pragma unroll
@@ -818,12 +820,14 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
       auto body = [&](auto with_target) __attribute__((always_inline)) {
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
-          // G of the block's 16 values (this lane's share), kept in registers
-          // until the block's keep decision: the largest log2 softmax value
-          // x = z log2(e) - LSE log2(e) over the block's 32 x 32 entries
-          // against -12, or a target in the block
-          float gq[4][4];
-          float xm = -INFINITY;
+          // The block's 16 (biased, capped) logits of this lane, kept in
+          // registers until the block's keep decision: the largest log2
+          // softmax value x = z log2(e) - LSE log2(e) over the block's 32 x 32
+          // entries against -12, or a target in the block.  The lane's 16
+          // values share one token column (one LSE), and rounding is
+          // monotone, so the lane's largest x is that of its largest z.
+          float zq[4][4];
+          float zm = -INFINITY;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int rl = am.row(fm, 4 * q);
@@ -832,29 +836,15 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
             for (int u = 0; u < 4; ++u) {
               float z = MODE ? acc[fm][fn][4 * q + u] + bz[u] : acc[fm][fn][4 * q + u];
               if constexpr (MODE == 2) z = softcap_f(z, softcap, kcap);
-              const float x = __builtin_fmaf(z, kLog2e, -lsel[fn]);
-              const float p = fast_exp2(x);
-              float g;
-              if constexpr (decltype(with_target)::value) {
-                const float tsc = trow[fn] == fm * 32 + 8 * q + u ? st[fn] : 0.f;
-                g = __builtin_fmaf(p, sc[fn], -tsc);
-              } else {
-                g = p * sc[fn];
-              }
-              if constexpr (MODE == 2) {
-                const float y = z * rcap;
-                g *= __builtin_fmaf(-y, y, 1.f);
-              }
               if constexpr (decltype(ragged)::value) {
-                const bool in = v0 + rl + u < V;
-                g = in ? g : 0.f;
-                if (in) xm = fmaxf(xm, x);
+                if (v0 + rl + u < V) zm = fmaxf(zm, z);
               } else {
-                xm = fmaxf(xm, x);
+                zm = fmaxf(zm, z);
               }
-              gq[q][u] = g;
+              zq[q][u] = z;
             }
           }
+          const float xm = __builtin_fmaf(zm, kLog2e, -lsel[fn]);
           // a target in the block's rows (the lower half-wave's row offset is 0)
           const bool tgt = decltype(with_target)::value && (threadIdx.x & 32) == 0 && trow[fn] >= 0 &&
                            (trow[fn] >> 5) == fm;
@@ -864,12 +854,35 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
                                    : v0 + wave / C::WAVES_N * C::WM + fm * 32 < V &&
                                          n0 + wave % C::WAVES_N * C::WN + fn * 32 < N;
           kbits |= (kept ? 1u : 0u) << (fn * C::FM + fm);
+          // With filtering, bf16 operands: the contractions skip the MFMAs
+          // of a dropped block and never read its G, which is then neither
+          // formed nor stored.  Otherwise (fp32 operands, whose contractions
+          // are dense, or filtering off) a block outside the kept set is
+          // stored as zeros.
+          if (kSkipDropped && filter && !kept) continue;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
+            const int rl = am.row(fm, 4 * q);
             float g[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) g[u] = kept ? gq[q][u] : 0.f;
-            sink(fn, fm, q, am.row(fm, 4 * q), g);
+            for (int u = 0; u < 4; ++u) {
+              const float z = zq[q][u];
+              const float p = fast_exp2(__builtin_fmaf(z, kLog2e, -lsel[fn]));
+              float gv;
+              if constexpr (decltype(with_target)::value) {
+                const float tsc = trow[fn] == fm * 32 + 8 * q + u ? st[fn] : 0.f;
+                gv = __builtin_fmaf(p, sc[fn], -tsc);
+              } else {
+                gv = p * sc[fn];
+              }
+              if constexpr (MODE == 2) {
+                const float y = z * rcap;
+                gv *= __builtin_fmaf(-y, y, 1.f);
+              }
+              if constexpr (decltype(ragged)::value) gv = v0 + rl + u < V ? gv : 0.f;
+              g[u] = kept ? gv : 0.f;
+            }
+            sink(fn, fm, q, rl, g);
           }
         }
       };
@@ -991,16 +1004,20 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     store_blocks();
     // token rows of 256 bf16 out of the staging tile, two per instruction:
     // wave w drains rows [w RPW, (w + 1) RPW), row `w RPW + 2 it + lane / 32`,
-    // chunk lane % 32
+    // chunk lane % 32 (vocab group chunk / 4).  With filtering the chunks of
+    // dropped blocks (not staged) are skipped: the lane's vocab group's kept
+    // token groups, one bit each.
     constexpr int RPW = 256 / (C::NT / 64);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t kept_tg = filter ? sbm[(lane & 31) >> 2] : 0xffu;
 #pragma unroll 4
     for (int it = 0; it < RPW / 2; ++it) {
       const int rr = wave * RPW + it * 2 + (lane >> 5), jc = lane & 31;
       const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(rr, jc * 8));
-      __builtin_amdgcn_raw_buffer_store_b128(
-          val, rg, (((uint32_t)n0 + (uint32_t)rr) * (uint32_t)Vc + (uint32_t)vl0 + (uint32_t)jc * 8u) * 2u, 0,
-          kStoreNT);
+      if ((kept_tg >> (rr >> 5)) & 1u)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            val, rg, (((uint32_t)n0 + (uint32_t)rr) * (uint32_t)Vc + (uint32_t)vl0 + (uint32_t)jc * 8u) * 2u, 0,
+            kStoreNT);
     }
     if (sums) {
       __syncthreads();  // the drain's LDS reads are done
