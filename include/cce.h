@@ -128,28 +128,34 @@ size_t cce_state_size(int64_t N, int64_t D, int64_t V, int dtype);
 
 /*
  * Bytes of the backward workspace for this problem and vocab_chunk.
- * vocab_chunk = 0 picks the library default: the backward forms the gradient
- * tiles G of one vocabulary chunk at a time and keeps that chunk's G in the
- * workspace (bf16: once, token-major; fp32: in both orientations), at most
- * 256 MiB of it but never fewer than 8192 columns (the vocabulary cut into
- * nearly equal chunks of whole 256-wide tiles: 4 chunks at N = 4096,
- * V = 128256, 16 at N = 16384), plus e transposed (N*D elements), an fp32
- * [N, D] accumulation of dE for bf16 gradients that more than one pass adds
- * up, and the compaction and keep-map arrays: about 0.39 GB at N = 4096,
- * D = 4096, V = 128256 (1.2 GB with the whole vocabulary in one chunk).  A
- * positive value (a multiple of 256) sets the chunk width, trading workspace
- * for launches.  Returns 0 for invalid arguments.
+ * vocab_chunk = 0 picks the library default.  The backward forms the
+ * gradient tiles G one vocabulary chunk at a time and keeps that chunk's G
+ * in the workspace: with bf16 operands only the kept 256x256 tiles, one
+ * 128 KB slot each, room for the tiles of a chunk vocab_chunk wide (rounded
+ * up to 8 tiles) when every tile is kept, and the chunks are cut by kept
+ * tiles, so a filtered backward covers the vocabulary in as few chunks as
+ * that room allows (one at the pages' Gemma-2-2B head); with fp32 operands G
+ * and G^T of a chunk exactly vocab_chunk wide.  The default room is at most
+ * 256 MiB but never fewer than 8192 columns (the vocabulary cut into nearly
+ * equal chunks of whole 256-wide tiles: 4 chunks at N = 4096, V = 128256, 16
+ * at N = 16384, when nothing is filtered).  Plus e transposed (N*D
+ * elements), an fp32 [N, D] accumulation of dE for bf16 gradients that more
+ * than one pass adds up, and the compaction, keep-map and chunk arrays:
+ * about 0.38 GB at N = 4096, D = 4096, V = 128256 (1.2 GB with the whole
+ * vocabulary in one chunk).  A positive value (a multiple of 256) sets the
+ * chunk width, trading workspace for launches.  Returns 0 for invalid
+ * arguments.
  */
 size_t cce_workspace_size(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk);
 
 /*
- * Vocabulary entries per chunk that cce_backward uses for this problem and
- * vocab_chunk argument (the default when vocab_chunk = 0; the value passed,
- * clamped to the vocabulary, otherwise).  The backward launches its gradient
- * kernels once per chunk.  The default also keeps a chunk's classifier rows
- * (chunk * D elements) under 2^31 bytes, the reach of one buffer descriptor,
- * so a classifier of any size (V * D elements) is taken in chunks.  Returns 0
- * for invalid arguments.
+ * Vocabulary entries per chunk that cce_backward sizes its gradient tiles for,
+ * for this problem and vocab_chunk argument (the default when vocab_chunk = 0;
+ * the value passed, clamped to the vocabulary, otherwise): the chunk width
+ * when every tile is kept.  The backward launches its gradient kernels once
+ * per chunk.  A chunk's classifier rows stay under 2^31 bytes, the reach of
+ * one buffer descriptor, so a classifier of any size (V * D elements) is
+ * taken in chunks.  Returns 0 for invalid arguments.
  */
 int64_t cce_vocab_chunk(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chunk);
 

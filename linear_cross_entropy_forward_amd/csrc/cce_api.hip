@@ -55,10 +55,40 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   if (vc > vmax) vc = vmax;
   if (vc > (int64_t)kMaxBlocks * kTileV) vc = (int64_t)kMaxBlocks * kTileV;
   L.Vc = (int)vc;
-  L.nchunks = (int)((V + vc - 1) / vc);
   const int tiles_d = (int)((D + kTileV - 1) / kTileV);
   const int tiles_de = L.nb * tiles_d;
   const int cvb = (int)(vc / kTileV);
+  // bf16: compact gradient storage.  The vocabulary is cut into units of
+  // `unit` vocab tiles (8, one per XCD in dC's dealing, or fewer for narrow
+  // chunks) and consecutive units are packed greedily into chunks of at most
+  // S = nb * m * unit kept tiles (m = ceil(cvb / unit) units, the dense
+  // chunk rounded up to whole units) and at most span_u units (the block
+  // lists of the contractions, the chunk's classifier rows under one 32-bit
+  // buffer offset).  On a dense keep map that gives the dense chunks; on a
+  // sparse one, as few chunks as the slots allow.  Every chunk but the last
+  // holds at least min(m, span_u) units (a chunk cut for its count holds
+  // more than (m - 1) * nb * unit tiles), which bounds the chunk count.
+  L.compact = dtype == kDtypeBf16;
+  if (L.compact) {
+    const int64_t span_c = (int64_t)((((size_t)1 << 31) - 1) / ((size_t)D * es) / kTileV);
+    const int span = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxBlocks, span_c));
+    L.unit = std::min(std::min(8, cvb), span);
+    const int m = (cvb + L.unit - 1) / L.unit;
+    L.S = L.nb * m * L.unit;
+    L.cap = L.S;
+    L.span_u = std::max(1, span / L.unit);
+    const int nunits = (L.nvb_t + L.unit - 1) / L.unit;
+    const int per_chunk = std::min(m, L.span_u);
+    L.nchunks = (nunits + per_chunk - 1) / per_chunk;
+    L.list_stride = L.cap;
+  } else {
+    L.unit = cvb;
+    L.S = 0;
+    L.cap = 0;
+    L.span_u = 1;
+    L.nchunks = (int)((V + vc - 1) / vc);
+    L.list_stride = cvb * L.nb;
+  }
   // dE work-groups: enough vocabulary splits to fill one round of the chip
   // (kWaveSlots work-groups, one per CU); each further split adds a partial
   // buffer that the epilogue writes and a final pass re-reads.  (Taking more
@@ -74,7 +104,7 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   if (spa > cvb) spa = cvb;
   if (spa < 1) spa = 1;
   L.splits_atomic = spa;
-  L.g_bytes = (size_t)L.Npad * (size_t)vc * es;
+  L.g_bytes = L.compact ? (size_t)L.cap * kSlotRows * kTileV * es : (size_t)L.Npad * (size_t)vc * es;
   L.gt_ld = L.Npad + kGtPad;
   L.gt_bytes = dtype == kDtypeBf16 ? 0 : (size_t)L.gt_ld * (size_t)vc * es;
   int rpb_unused;
@@ -103,8 +133,10 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
   const size_t o_tgt_c = take((size_t)L.Npad * 4);
   const size_t o_keep = take((size_t)L.nb * L.nvb_t);
   const size_t o_bmask = take((size_t)L.nb * L.nvg);
-  const size_t o_tlist = take((size_t)L.nb * L.nvb_t * 4);
+  const size_t o_tlist = take((size_t)L.nchunks * L.list_stride * 4);
   const size_t o_tcount = take((size_t)L.nchunks * 4);
+  const size_t o_chvb = take((size_t)(L.nchunks + 1) * 4);
+  const size_t o_slot = take(L.compact ? (size_t)L.nb * L.nvb_t * 4 : 0);
   const size_t o_r1c = take((size_t)D * 4);
   const size_t o_ssum = take(64);
   const size_t o_bcolp = take((size_t)L.bcol_blocks * (size_t)D * 4);
@@ -135,6 +167,8 @@ Layout make_layout(int64_t N, int64_t D, int64_t V, int dtype, int64_t vocab_chu
     L.bmask = (uint8_t*)(b + o_bmask);
     L.tlist = (int*)(b + o_tlist);
     L.tcount = (int*)(b + o_tcount);
+    L.ch_vb = (int*)(b + o_chvb);
+    L.slot = (int*)(b + o_slot);
     L.r1c = (float*)(b + o_r1c);
     L.ssum = (float*)(b + o_ssum);
     L.bcolpart = (float*)(b + o_bcolp);
@@ -173,7 +207,8 @@ static cce_status check_common(const void* e, const void* c, const int64_t* targ
   if ((N + kTileN) * D * es >= lim || N > (int64_t)kMaxBlocks * kTileN || V >= lim / 2 || D >= lim / 2)
     return CCE_ERR_UNSUPPORTED;
   Layout L = make_layout(N, D, V, dtype, vocab_chunk, nullptr, nullptr);
-  if ((int64_t)L.Vc * D * es >= lim || (int64_t)L.g_bytes >= lim || (int64_t)L.gt_bytes >= lim)
+  // (compact storage keeps each chunk's classifier rows within `span`)
+  if ((!L.compact && (int64_t)L.Vc * D * es >= lim) || (int64_t)L.g_bytes >= lim || (int64_t)L.gt_bytes >= lim)
     return CCE_ERR_UNSUPPORTED;
   return CCE_OK;
 }

@@ -652,11 +652,16 @@ struct NoMask {
   __device__ __forceinline__ uint32_t operator()(int) const { return 0xffffffffu; }
 };
 
+//
+// With `ablocks` (SEPA), the A operand takes its own K blocks: step s reads A
+// at K offset ablocks[s / SPB] * astride + (s % SPB) * BK (the gradient
+// tiles stored one per slot), B as above.
 template <class C, int SPB, bool B_MN = false, bool A_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1),
-          class MaskT = NoMask>
+          class MaskT = NoMask, bool SEPA = false>
 __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const Operand& A, const Operand& B,
                                              int nsteps, const uint16_t* blocks, void* smem,
-                                             const int* __restrict__ brow = nullptr, const MaskT& mask = MaskT{}) {
+                                             const int* __restrict__ brow = nullptr, const MaskT& mask = MaskT{},
+                                             const uint16_t* ablocks = nullptr, int astride = 0) {
   using T = typename C::T;
   using TA = std::conditional_t<A_MN, DmaTileMN<C, C::BM, C::FM>, DmaTile<C, C::BM>>;
   using TB = std::conditional_t<B_MN, DmaTileMN<C, C::BN, C::FN>, DmaTile<C, C::BN>>;
@@ -677,6 +682,15 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
     const int k = blocks ? (int)blocks[b] * (SPB * C::BK) + (s % SPB) * C::BK : s * C::BK;
     return s < nsteps ? k : kend;
   };
+  // A's K offset of step s: kofs(s), or from its own block list
+  auto kofs_a = [&](int s) -> int {
+    if constexpr (SEPA) {
+      const int b = s / SPB < last_blk ? s / SPB : last_blk;
+      return s < nsteps ? (int)ablocks[b] * astride + (s % SPB) * C::BK : kend;
+    } else {
+      return kofs(s);
+    }
+  };
   const lds_u8* base = (const lds_u8*)smem;
   const uint32_t base_addr = (uint32_t)(uintptr_t)base;
 
@@ -687,16 +701,17 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   // B rows through `brow` (K-major B only): the gathered token rows
   if constexpr (B_MN) tb.init(B);
   else tb.init(B, brow);
-  auto dma = [&](int d, int k0, uint32_t st) {
-    if (d < TA::PER) ta.issue(d, A, k0, st);
-    else tb.issue(d - TA::PER, B, k0, st + TA::BYTES);
+  // ka: A's K offset, kb: B's (the same without SEPA)
+  auto dma = [&](int d, int ka, int kb, uint32_t st) {
+    if (d < TA::PER) ta.issue(d, A, ka, st);
+    else tb.issue(d - TA::PER, B, kb, st + TA::BYTES);
   };
   // prologue: step 0 whole, part 0 of step 1 (its other parts follow in step 0)
   constexpr int P0 = NDMA / NPARTS;
 #pragma unroll
-  for (int d = 0; d < NDMA; ++d) dma(d, kofs(0), base_addr);
+  for (int d = 0; d < NDMA; ++d) dma(d, kofs_a(0), kofs(0), base_addr);
 #pragma unroll
-  for (int d = 0; d < P0; ++d) dma(d, kofs(1), base_addr + STAGE);
+  for (int d = 0; d < P0; ++d) dma(d, kofs_a(1), kofs(1), base_addr + STAGE);
   wait_vmcnt<P0>();  // step 0 has landed
   __syncthreads();
 
@@ -723,9 +738,13 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   // after the barrier, is read (from the LDS block list when there is one) at
   // the top of the step, ahead of the step's fragment reads, so the waits for
   // those cover it and the loop never waits on that read alone.
+  // (With SEPA, A's offsets ka1 / ka2 likewise.)
+  int kan = SEPA ? __builtin_amdgcn_readfirstlane(kofs_a(1)) : 0;
   auto step = [&](int s, const lds_u8* st, const lds_u8* nx, uint32_t st_addr, uint32_t nx_addr, int k1) -> int {
     // wave-uniform: kept in a scalar register
     const int k2 = __builtin_amdgcn_readfirstlane(kofs(s + 2));
+    const int ka1 = SEPA ? kan : k1;
+    const int ka2 = SEPA ? __builtin_amdgcn_readfirstlane(kofs_a(s + 2)) : k2;
     const uint32_t mnext =
         MaskT::kActive ? (uint32_t)__builtin_amdgcn_readfirstlane((int)mask(s + 1 < nsteps ? s + 1 : nsteps - 1))
                        : 0xffffffffu;
@@ -776,8 +795,8 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
               constexpr int d1 = (b + 1) * dn / HALF < dn ? (b + 1) * dn / HALF : dn;
 #pragma unroll
               for (int d = d0; d < d1; ++d) {
-                if constexpr (last) dma(dlo + d, k2, st_addr);
-                else dma(dlo + d, k1, nx_addr);
+                if constexpr (last) dma(dlo + d, ka2, k2, st_addr);
+                else dma(dlo + d, ka1, k1, nx_addr);
               }
               __builtin_amdgcn_sched_barrier(0);
             }(),
@@ -788,6 +807,7 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
       (group(std::integral_constant<int, G>{}), ...);
     }(std::make_integer_sequence<int, KG>{});
     mcur = mnext;
+    if constexpr (SEPA) kan = ka2;
     return k2;
   };
 

@@ -22,6 +22,9 @@ constexpr int kPartialWidth = 128;
 constexpr int kBlock = 32;
 constexpr int kBlocksPerTile = kTileV / kBlock;  // 8 along either side
 constexpr int kMaxBlocks = 2048;  // K blocks one contraction tile can list
+// Compact gradient storage: one 256 x 256 tile per slot, rows of 256
+// elements (token-major); slot j starts at row j * kSlotRows.
+constexpr int kSlotRows = 256;
 // Row blocks of the column-sum kernel (partials [kColBlocks][D] in the
 // workspace) and the fewest rows one block takes.
 constexpr int kColBlocks = 512;
@@ -112,9 +115,14 @@ struct Layout {
   float* bcolpart;  // [bcol_blocks][D] column-sum partials of the backward
   uint8_t* keep;    // [nb][nvb_t]
   uint8_t* bmask;   // [nb][nvg] per 32-vocab group, bit t: 32-row group t of the token block kept
-  int* tlist;       // per chunk, its kept gradient tiles in launch order (chunk ch at cvb0 * nb)
+  int* tlist;       // [nchunks][list_stride] per chunk, its kept gradient tiles in launch order
   int* tcount;      // [nchunks] kept gradient tiles per chunk
-  void* G;          // [Npad][Vc] operand type: gradient tiles of one vocab chunk
+  int* ch_vb;       // [nchunks + 1] first vocab tile of each chunk (chunk ch: [ch_vb[ch], ch_vb[ch + 1]))
+  int* slot;        // [nb][nvb_t] compact: slot of each kept tile in its chunk's G
+  // G, bf16 (compact): cap slots of one 256 x 256 tile each ([256 tokens][256
+  // vocab], 128 KB), the kept tiles of one chunk in list order; fp32: [Npad][Vc],
+  // the chunk's tiles in place
+  void* G;
   void* Gt;         // [Vc][gt_ld] the same tiles transposed, fp32 only (columns past Npad unused)
   void* Et;         // [D][Npad] e transposed (zero rows past N)
   size_t g_bytes;   // bytes of G
@@ -123,6 +131,11 @@ struct Layout {
   float* dE_part;   // [splits-1][N][D]
   float* dE_acc;    // [N][D] fp32 accumulation of dE when dE itself is bf16 and more than one pass adds to it
   int nVB, Npad, nb, nvb_t, nvg, Vc, nchunks, splits, splits_atomic, bcol_blocks;
+  // compact gradient storage (bf16): chunks are packed from units of `unit`
+  // vocab tiles, at most S kept tiles (cap slots, cap = S) and span_u units
+  // each; dense (fp32): chunks of unit = Vc / 256 vocab tiles.
+  // list_stride = per-chunk list length
+  int compact, unit, S, cap, span_u, list_stride;
 };
 
 

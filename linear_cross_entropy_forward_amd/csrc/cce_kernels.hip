@@ -694,19 +694,63 @@ __global__ __launch_bounds__(1024) void filter_kernel(const int64_t* __restrict_
 }
 
 // ============================================================================
+// Vocabulary chunks of the backward (one work-group): chunk ch covers vocab
+// tiles [ch_vb[ch], ch_vb[ch + 1]).  Compact gradient storage (S > 0):
+// units of `unit` vocab tiles are packed greedily, in order, into chunks of
+// at most S kept tiles and span_u units (ucnt: scratch for the units' kept
+// counts); dense storage (S = 0): chunks of `unit` vocab tiles.  Chunk
+// numbers past the last chunk get empty ranges; ch_vb[nchunks] = nvb_t.
+// ============================================================================
+__global__ __launch_bounds__(1024) void chunk_plan_kernel(const uint8_t* __restrict__ keep, int nb, int nvb_t,
+                                                          int unit, int S, int span_u, int nchunks,
+                                                          int* __restrict__ ch_vb, int* __restrict__ ucnt) {
+  const int tid = threadIdx.x;
+  if (S == 0) {
+    for (int c = tid; c <= nchunks; c += 1024) ch_vb[c] = min(c * unit, nvb_t);
+    return;
+  }
+  const int nunits = (nvb_t + unit - 1) / unit;
+  for (int u = tid; u < nunits; u += 1024) {
+    int k = 0;
+    for (int v = u * unit; v < min(nvb_t, (u + 1) * unit); ++v)
+      for (int b = 0; b < nb; ++b) k += keep[(size_t)b * nvb_t + v] != 0;
+    ucnt[u] = k;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // each unit holds at most nb * unit <= S kept tiles: a chunk always
+    // takes its first unit
+    int c = 0, cnt = 0, u0 = 0;
+    ch_vb[0] = 0;
+    for (int u = 0; u < nunits; ++u) {
+      const int k = ucnt[u];
+      if (u > u0 && (cnt + k > S || u + 1 - u0 > span_u) && c + 1 < nchunks) {
+        ch_vb[++c] = u * unit;
+        cnt = 0;
+        u0 = u;
+      }
+      cnt += k;
+    }
+    for (int cc = c + 1; cc <= nchunks; ++cc) ch_vb[cc] = nvb_t;
+  }
+}
+
+// ============================================================================
 // Per vocabulary chunk (one work-group each): the chunk's kept gradient tiles,
 // in the grouped order the gradient kernel would visit them, as a list and a
-// count.  The gradient kernel spreads the list evenly over the XCDs: with
+// count, and (compact storage) the slot of each kept tile: its position in
+// the list.  The gradient kernel spreads the list evenly over the XCDs: with
 // filtering the kept tiles gather where the frequent targets are, and a
 // mapping over all tiles would hand most of them to one XCD.
 // ============================================================================
 __global__ __launch_bounds__(1024) void tile_list_kernel(const uint8_t* __restrict__ keep, int nvb_t, int tiles_n,
-                                                         int cvb, int* __restrict__ tlist,
-                                                         int* __restrict__ tcount) {
+                                                         const int* __restrict__ ch_vb, int list_stride,
+                                                         int* __restrict__ tlist, int* __restrict__ tcount,
+                                                         int* __restrict__ slot) {
   __shared__ int scnt[1024];
   const int ch = blockIdx.x, tid = threadIdx.x;
-  const int cvb0 = ch * cvb;
-  const int cnvb = min(cvb, nvb_t - cvb0);
+  const int cvb0 = ch_vb[ch];
+  const int cnvb = ch_vb[ch + 1] - cvb0;
   const int n = cnvb * tiles_n;
   const int run = (n + 1023) / 1024;
   const int i0 = min(n, tid * run), i1 = min(n, i0 + run);
@@ -725,23 +769,35 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const uint8_t* __restri
     scnt[tid] += v;
     __syncthreads();
   }
-  int* out = tlist + (size_t)cvb0 * tiles_n;
+  int* out = tlist + (size_t)ch * list_stride;
   int pos = scnt[tid] - cnt;
-  for (int i = i0; i < i1; ++i)
-    if (kept(i)) out[pos++] = i;
-  if (tid == 1023) tcount[ch] = scnt[1023];
+  // (the plan keeps every chunk within list_stride tiles; the bound is
+  // enforced here too so that no write leaves the chunk's list)
+  for (int i = i0; i < i1 && pos < list_stride; ++i)
+    if (kept(i)) {
+      if (slot) {
+        int tvl, tn;
+        grouped_tile(i, cnvb, tiles_n, kRasterGrad, tvl, tn);
+        slot[(size_t)tn * nvb_t + cvb0 + tvl] = pos;
+      }
+      out[pos++] = i;
+    }
+  if (tid == 1023) tcount[ch] = min(scnt[1023], list_stride);
 }
 
 // ============================================================================
 // Backward: recompute kept logit tiles and write G = (p - onehot) * scale for
-// one vocabulary chunk [cv0, cv0 + Vc) into G [Npad][Vc] (token-major).
+// one vocabulary chunk (vocab tiles [chv[0], chv[1])): bf16 (compact) one
+// tile per slot, slot j = the tile's position in the chunk's list, as
+// [256 tokens][256 vocab]; fp32 in place into G [Npad][Vc] (token-major) and
+// G^T [Vc][gt_ld].
 // ============================================================================
 template <class C>
 __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     const typename C::T* __restrict__ c, const typename C::T* __restrict__ e, const typename C::T* __restrict__ bias,
     const int* __restrict__ rowmap, const int* __restrict__ tgt_c, const float* __restrict__ lse_c,
     const float* __restrict__ scale_c, float eps, float lam, float softcap, const int* __restrict__ tlist,
-    const int* __restrict__ tcount, int N, int D, int V, int cvb0, int tiles_v, int tiles_n, int Vc, int gt_ld,
+    const int* __restrict__ tcount, int N, int D, int V, const int* __restrict__ chv, int tiles_n, int Vc, int gt_ld,
     typename C::T* __restrict__ G, typename C::T* __restrict__ Gt, size_t g_bytes, size_t gt_bytes,
     float* __restrict__ db_part, uint8_t* __restrict__ bmask, int nvg, int32_t* __restrict__ hdr, int filter) {
   using T = typename C::T;
@@ -753,8 +809,10 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   const int cnt = *tcount;
   if ((int)blockIdx.x >= cnt) return;
   if ((int)threadIdx.x < kBlocksPerTile) sbm[threadIdx.x] = 0;  // visible after the main loop's barriers
+  const int cvb0 = chv[0], tiles_v = chv[1] - cvb0;
+  const int li = xcd_remap(blockIdx.x, cnt);  // list position: the slot of the tile's G (bf16)
   int tvl, tn;
-  grouped_tile(tlist[xcd_remap(blockIdx.x, cnt)], tiles_v, tiles_n, kRasterGrad, tvl, tn);
+  grouped_tile(tlist[li], tiles_v, tiles_n, kRasterGrad, tvl, tn);
   const int tv = cvb0 + tvl;
   const int v0 = tv * C::BM, n0 = tn * C::BN;
   if (bias || softcap > 0.f) stage_bias<T, C::BM>(sbias, bias, v0, V);
@@ -1016,8 +1074,8 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
       const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(rr, jc * 8));
       if ((kept_tg >> (rr >> 5)) & 1u)
         __builtin_amdgcn_raw_buffer_store_b128(
-            val, rg, (((uint32_t)n0 + (uint32_t)rr) * (uint32_t)Vc + (uint32_t)vl0 + (uint32_t)jc * 8u) * 2u, 0,
-            kStoreNT);
+            val, rg, ((uint32_t)li * (uint32_t)(kSlotRows * kTileV) + (uint32_t)rr * kTileV + (uint32_t)jc * 8u) * 2u,
+            0, kStoreNT);
     }
     if (sums) {
       __syncthreads();  // the drain's LDS reads are done
@@ -1126,126 +1184,165 @@ __global__ __launch_bounds__(256) void db_reduce_kernel(const float* __restrict_
 }
 
 // ============================================================================
-// dC rows of one vocabulary chunk: dC[v][d] = sum_n G^T[v][n] E^T[d][n] over
-// the kept token blocks of the tile's vocab block.  B = E^T (K-major); A = G^T:
-// bf16 reads G [Npad][Vc] (MN-major) through transposing LDS reads, fp32 the
-// K-major G^T [Vc][gt_ld].
+// dC rows of one vocabulary chunk (vocab tiles [chv[0], chv[1])): dC[v][d] =
+// sum_n G^T[v][n] E^T[d][n] over the kept token blocks of the tile's vocab
+// block.  B = E^T (K-major); A = G^T: bf16 reads the compact G (each kept
+// tile in its slot, [256 tokens][256 vocab], MN-major) through transposing
+// LDS reads, fp32 the K-major G^T [Vc][gt_ld].
 // ============================================================================
 template <class C, bool MASK>
 __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
     const typename C::T* __restrict__ G, const typename C::T* __restrict__ Gt, const typename C::T* __restrict__ Et,
-    const uint8_t* __restrict__ keep, int Npad, int Vc, int gt_ld, int D, int V, int nvb_t, int cvb0, int cv0,
-    int clen, int tiles_v, int tiles_d, int group, size_t g_bytes, size_t gt_bytes, const float* __restrict__ r1c,
-    void* __restrict__ dC, int out_bf16, const uint8_t* __restrict__ bmask, int nvg) {
+    const uint8_t* __restrict__ keep, const int* __restrict__ slot, int cap, int Npad, int gt_ld, int D, int V,
+    int nvb_t, const int* __restrict__ chv, int tiles_d, size_t g_bytes, size_t gt_bytes,
+    const float* __restrict__ r1c, void* __restrict__ dC, int out_bf16, const uint8_t* __restrict__ bmask,
+    int nvg) {
   using T = typename C::T;
   constexpr bool kMN = sizeof(T) == 2;
   static_assert(!MASK || (kMN && C::FM == 4), "block masks: bf16, four 32-row fragments per wave");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
+  __shared__ uint16_t ablk[kMN ? kMaxBlocks : 1];  // bf16: the G slot of each listed token block
   __shared__ uint64_t smask[MASK ? kMaxBlocks : 1];
-  // Groups of `group` vocab tiles (each with all its d tiles) are dealt to
-  // the XCDs in turn, group g to XCD g % 8 (work-group i runs on XCD i % 8):
-  // the vocab tiles with many kept token blocks (frequent targets) sit next
-  // to each other, and this spreads them over the XCDs.  Inside a group the
-  // order is the grouped raster (L2 reuse).  The host makes groups narrow
-  // enough that a chunk has at least 8 of them when it can (every XCD gets
-  // work).  The grid has 8 x group x tiles_d x ceil(groups / 8) work-groups;
-  // the spare exit.
-  const int GR = group;
+  const int cvb0 = chv[0], tiles_v = chv[1] - cvb0;
+  const int cv0 = cvb0 * kTileV, clen = min(tiles_v * kTileV, V - cv0);
+  // Groups of GR vocab tiles (each with all its d tiles) are dealt to the
+  // XCDs in turn, group g to XCD g % 8 (work-group i runs on XCD i % 8): the
+  // vocab tiles with many kept token blocks (frequent targets) sit next to
+  // each other, and this spreads them over the XCDs.  Inside a group the
+  // order is the grouped raster (L2 reuse).  GR is the widest group (at
+  // most kRasterDC) whose busiest XCD gets at most 1/32 more vocab tiles
+  // than with the most even split (chunks are whole units of 8 vocab tiles
+  // but the last, so that is usually GR = kRasterDC).  The chunk's width is
+  // known on the device only: the grid covers 8 x GR x tiles_d x
+  // ceil(groups / 8) work-groups for the widest chunk possible, and the
+  // spare exit.
+  auto busiest = [&](int gr) {
+    // vocab tiles of XCD 0 (the busiest): groups 0, 8, 16, ..., of which
+    // only the last can be partial
+    const int g0 = ((tiles_v + gr - 1) / gr + 7) / 8;
+    return (g0 - 1) * gr + min(gr, tiles_v - (g0 - 1) * 8 * gr);
+  };
+  int lmin = tiles_v;
+  for (int gr = 1; gr <= kRasterDC; ++gr) lmin = min(lmin, busiest(gr));
+  int GR = 1;
+  for (int gr = kRasterDC; gr > 1; --gr)
+    if (busiest(gr) <= lmin + lmin / 32) {
+      GR = gr;
+      break;
+    }
   const int per = GR * tiles_d;
   const int x = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
   const int g = x + 8 * (j / per), r = j % per;
   const int gm = min(GR, tiles_v - g * GR);  // vocab tiles in group g
   if (gm <= 0 || r >= gm * tiles_d) return;
   const int tvl = g * GR + r % gm, td = r / gm;
-  const int vl0 = tvl * C::BM, d0 = td * C::BN;
-  const int nb = Npad / kTileN;
-  const int nk = collect_blocks(keep, (size_t)(cvb0 + tvl), nvb_t, nb, blocks);
+  {
+    const int vl0 = tvl * C::BM, d0 = td * C::BN;
+    const int nb = Npad / kTileN;
+    const int nk = collect_blocks(keep, (size_t)(cvb0 + tvl), nvb_t, nb, blocks);
 
-  const Operand A =
-      kMN ? make_operand(G + vl0, g_bytes - (size_t)vl0 * sizeof(T), (uint32_t)Vc, min(C::BM, clen - vl0), Npad)
-          : make_operand(Gt + (size_t)vl0 * gt_ld, gt_bytes - (size_t)vl0 * gt_ld * sizeof(T), (uint32_t)gt_ld,
-                         min(C::BM, clen - vl0), Npad);
-  Operand B = make_operand(Et + (size_t)d0 * Npad, (uint64_t)(D - d0) * Npad * sizeof(T), (uint32_t)Npad,
-               min(C::BN, D - d0), Npad);
-  f32x16 acc[C::FM][C::FN];
+    // bf16: A's K blocks are the tiles' slots (K rows slot * 256 ..); G seen
+    // as cap * 256 token rows of the 256 vocab columns
+    if constexpr (kMN) {
+      for (int j = threadIdx.x; j < nk; j += C::NT)
+        ablk[j] = (uint16_t)slot[(size_t)blocks[j] * nvb_t + cvb0 + tvl];
+      __syncthreads();
+    }
+    const Operand A =
+        kMN ? make_operand(G, g_bytes, (uint32_t)kTileV, min(C::BM, clen - vl0), cap * kSlotRows)
+            : make_operand(Gt + (size_t)vl0 * gt_ld, gt_bytes - (size_t)vl0 * gt_ld * sizeof(T), (uint32_t)gt_ld,
+                           min(C::BM, clen - vl0), Npad);
+    Operand B = make_operand(Et + (size_t)d0 * Npad, (uint64_t)(D - d0) * Npad * sizeof(T), (uint32_t)Npad,
+                 min(C::BN, D - d0), Npad);
+    f32x16 acc[C::FM][C::FN];
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
-  constexpr int SPB = kTileN / C::BK;
-  if constexpr (MASK) {
-    // the tile's block-mask bytes for each kept token block, published to the
-    // main loop by its first barrier
-    for (int j = threadIdx.x; j < nk; j += C::NT)
-      smask[j] = *reinterpret_cast<const uint64_t*>(bmask + (size_t)blocks[j] * nvg +
-                                                    (size_t)(cvb0 + tvl) * kBlocksPerTile);
-    const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
-    const DCMask mk{(const lds_u64*)smask, 32 * wm};
-    if (nk > 0 && blocks[nk - 1] == nk - 1)
-      mainloop_dma<C, SPB, false, kMN, 3, DCMask>(acc, A, B, nk * SPB, nullptr, smem, nullptr, mk);
-    else
-      mainloop_dma<C, SPB, false, kMN, 3, DCMask>(acc, A, B, nk * SPB, blocks, smem, nullptr, mk);
-  } else {
-    // the kept token blocks are the first nk (no filtering effect on this
-    // tile; compacted slots put the blocks of ignored rows last): contiguous K
-    if (nk > 0 && blocks[nk - 1] == nk - 1) mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, nullptr, smem);
-    else mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, blocks, smem);
-  }
+      for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
+    constexpr int SPB = kTileN / C::BK;
+    if constexpr (MASK) {
+      // the tile's block-mask bytes for each kept token block, published to the
+      // main loop by its first barrier
+      for (int j = threadIdx.x; j < nk; j += C::NT)
+        smask[j] = *reinterpret_cast<const uint64_t*>(bmask + (size_t)blocks[j] * nvg +
+                                                      (size_t)(cvb0 + tvl) * kBlocksPerTile);
+      const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
+      const DCMask mk{(const lds_u64*)smask, 32 * wm};
+      if (nk > 0 && blocks[nk - 1] == nk - 1)
+        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true>(acc, A, B, nk * SPB, nullptr, smem, nullptr, mk, ablk,
+                                                           kSlotRows);
+      else
+        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true>(acc, A, B, nk * SPB, blocks, smem, nullptr, mk, ablk,
+                                                           kSlotRows);
+    } else {
+      // the kept token blocks are the first nk (no filtering effect on this
+      // tile; compacted slots put the blocks of ignored rows last): contiguous
+      // K for B
+      const uint16_t* bl = nk > 0 && blocks[nk - 1] == nk - 1 ? nullptr : blocks;
+      if constexpr (kMN)
+        mainloop_dma<C, SPB, false, kMN, 3, NoMask, true>(acc, A, B, nk * SPB, bl, smem, nullptr, NoMask{}, ablk,
+                                                           kSlotRows);
+      else
+        mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, bl, smem);
+    }
 
-  AccMap<C> am;
-  const int vg0 = cv0 + vl0;
-  // dC rows of the tile, float or bf16 (out_bf16)
-  const size_t es = out_bf16 ? 2 : 4;
-  rsrc_t ro = make_rsrc((char*)dC + (size_t)vg0 * D * es, (uint64_t)(V - vg0) * D * es);
-  // the smoothing term, the same for every vocabulary row (r1c: null without)
-  float add[C::FN];
-#pragma unroll
-  for (int fn = 0; fn < C::FN; ++fn) {
-    const int d = d0 + am.colj(fn);
-    add[fn] = (r1c && d < D) ? r1c[d] : 0.f;
-  }
-  // Each lane quad transposes its 4x4 blocks (four rows of four columns),
-  // so a lane writes four consecutive columns of one row: one 16-byte (fp32)
-  // or 8-byte (bf16) store instead of four.  D is a multiple of 4: a quad's
-  // columns are all inside or all outside.
-  const int k = (int)threadIdx.x & 3;
-#pragma unroll
-  for (int fm = 0; fm < C::FM; ++fm)
+    AccMap<C> am;
+    const int vg0 = cv0 + vl0;
+    // dC rows of the tile, float or bf16 (out_bf16)
+    const size_t es = out_bf16 ? 2 : 4;
+    rsrc_t ro = make_rsrc((char*)dC + (size_t)vg0 * D * es, (uint64_t)(V - vg0) * D * es);
+    // the smoothing term, the same for every vocabulary row (r1c: null without)
+    float add[C::FN];
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
-      const int dq = d0 + (am.colj(fn) & ~3);  // the quad's first column
+      const int d = d0 + am.colj(fn);
+      add[fn] = (r1c && d < D) ? r1c[d] : 0.f;
+    }
+    // Each lane quad transposes its 4x4 blocks (four rows of four columns),
+    // so a lane writes four consecutive columns of one row: one 16-byte (fp32)
+    // or 8-byte (bf16) store instead of four.  D is a multiple of 4: a quad's
+    // columns are all inside or all outside.
+    const int k = (int)threadIdx.x & 3;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t x[4];
+    for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = __builtin_bit_cast(uint32_t, acc[fm][fn][4 * q + u] + add[fn]);
-        quad_transpose(x);
-        const int vr = am.row(fm, 4 * q) + k;
-        const bool ok = dq < D && vl0 + vr < clen;
-        const uint32_t e = (uint32_t)vr * (uint32_t)D + (uint32_t)dq;
-        if (out_bf16) {
-          const u32x2 b = {pack_bf16(__builtin_bit_cast(float, x[0]), __builtin_bit_cast(float, x[1])),
-                           pack_bf16(__builtin_bit_cast(float, x[2]), __builtin_bit_cast(float, x[3]))};
-          __builtin_amdgcn_raw_buffer_store_b64(b, ro, ok ? e * 2u : kOOB, 0, kStoreNT);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b128(u32x4{x[0], x[1], x[2], x[3]}, ro, ok ? e * 4u : kOOB, 0,
-                                                 kStoreNT);
+      for (int fn = 0; fn < C::FN; ++fn) {
+        const int dq = d0 + (am.colj(fn) & ~3);  // the quad's first column
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t x[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] = __builtin_bit_cast(uint32_t, acc[fm][fn][4 * q + u] + add[fn]);
+          quad_transpose(x);
+          const int vr = am.row(fm, 4 * q) + k;
+          const bool ok = dq < D && vl0 + vr < clen;
+          const uint32_t e = (uint32_t)vr * (uint32_t)D + (uint32_t)dq;
+          if (out_bf16) {
+            const u32x2 b = {pack_bf16(__builtin_bit_cast(float, x[0]), __builtin_bit_cast(float, x[1])),
+                             pack_bf16(__builtin_bit_cast(float, x[2]), __builtin_bit_cast(float, x[3]))};
+            __builtin_amdgcn_raw_buffer_store_b64(b, ro, ok ? e * 2u : kOOB, 0, kStoreNT);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{x[0], x[1], x[2], x[3]}, ro, ok ? e * 4u : kOOB, 0,
+                                                   kStoreNT);
+          }
         }
       }
-    }
+  }
 }
 
 // ============================================================================
-// dE for one vocabulary chunk: dE[n][d] (+)= sum_v G[n][v] C[v][d] over the
-// kept vocab blocks of the tile's token block in split `s` of the chunk.
-// A = G (K-major), B = C (MN-major).
+// dE for one vocabulary chunk (vocab tiles [chv[0], chv[1])): dE[n][d] (+)=
+// sum_v G[n][v] C[v][d] over the kept vocab blocks of the tile's token block
+// in split `s` of the chunk.  A = G (K-major: bf16 the compact tiles, K block
+// j in slot j's 65536 elements; fp32 [Npad][Vc]), B = C (MN-major).
 // ============================================================================
 template <class C, bool MASK>
 __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     const typename C::T* __restrict__ G, const typename C::T* __restrict__ c,
-    const uint8_t* __restrict__ keep, int N, int D, int V, int nvb_t, int cvb0, int cv0, int clen,
-    int cnvb, int tiles_n, int tiles_d, int splits, const int32_t* __restrict__ hdr, int Vc, size_t g_bytes,
+    const uint8_t* __restrict__ keep, const int* __restrict__ slot, int cap, int N, int D, int V, int nvb_t,
+    const int* __restrict__ chv, int tiles_n, int tiles_d, int splits, const int32_t* __restrict__ hdr, int Vc,
+    size_t g_bytes,
     void* __restrict__ dE_out, int out_bf16,
     float* __restrict__ dE_part, int accumulate, int atomic, const int* __restrict__ rowmap,
     const float* __restrict__ scale_c, const float* __restrict__ csum, float r1, const uint8_t* __restrict__ bmask,
@@ -1262,6 +1359,9 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   uint16_t* dEb = out_bf16 ? (uint16_t*)dE_out : nullptr;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kDma ? C::LDS_DMA_BYTES : C::LDS_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
+  __shared__ uint16_t ablk[kDma ? kMaxBlocks : 1];  // bf16: the G slot of each listed vocab block
+  const int cvb0 = chv[0], cnvb = chv[1] - cvb0;
+  const int cv0 = cvb0 * kTileV, clen = min(cnvb * kTileV, V - cv0);
   // The grid holds tiles_n x tiles_d x splits work-groups.  The first
   // nbv x tiles_d x splits work on the token blocks that hold valid rows
   // (tile order remapped over exactly these, so they spread over all XCDs);
@@ -1307,13 +1407,21 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   const int lo = (int)((int64_t)nall * s / splits), hi = (int)((int64_t)nall * (s + 1) / splits);
   const int nk = hi - lo;
   const uint16_t* bl = blocks + lo;
+  // bf16: A's K blocks are the tiles' slots (K offset slot * 65536 from row
+  // n' * 256 of a slot); published by this barrier
+  if constexpr (kDma) {
+    for (int j = threadIdx.x; j < nk; j += C::NT) ablk[j] = (uint16_t)slot[(size_t)tn * nvb_t + cvb0 + bl[j]];
+    __syncthreads();
+  }
 
   // G rows n0.. over the chunk's vocabulary (K-major), from vocab offset ka
+  // (fp32)
   auto a_op = [&](size_t ka) -> Operand {
     const size_t o = (size_t)n0 * Vc + ka;
     return make_operand(G + o, g_bytes - o * sizeof(T), (uint32_t)Vc, min(C::BM, N - n0), clen - (int)ka);
   };
-  const Operand A = a_op(0);
+  const Operand A = kDma ? make_operand(G, g_bytes, (uint32_t)kTileV, min(C::BM, N - n0), cap * kSlotRows * kTileV)
+                         : a_op(0);
   Operand B = make_operand(c + (size_t)cv0 * D + d0, ((uint64_t)(V - cv0) * D - d0) * sizeof(T), (uint32_t)D,
                min(C::BN, D - d0), clen);
   f32x16 acc[C::FM][C::FN];
@@ -1336,18 +1444,20 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     if constexpr (MASK) {
       const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
       const DEMask mk{(const lds_u64*)smask, 4 * wm};
-      mainloop_dma<C, SPB, true, false, 2, DEMask>(acc, a, b, nk * SPB, bl, smem, nullptr, mk);
+      mainloop_dma<C, SPB, true, false, 2, DEMask, true>(acc, a, b, nk * SPB, bl, smem, nullptr, mk, ablk,
+                                                         kSlotRows * kTileV);
     } else if constexpr (kDma) {
-      mainloop_dma<C, SPB, true, false, 2>(acc, a, b, nk * SPB, bl, smem);
+      mainloop_dma<C, SPB, true, false, 2, NoMask, true>(acc, a, b, nk * SPB, bl, smem, nullptr, NoMask{}, ablk,
+                                                         kSlotRows * kTileV);
     } else {
       mainloop<C, false, true, SPB>(acc, a, b, nk * SPB, bl, (T*)smem);
     }
   };
   // the split's blocks consecutive (every block kept): contiguous K from its
-  // first block
+  // first block (for bf16 in B only: A follows the slots)
   if (nk > 0 && (int)bl[nk - 1] - (int)bl[0] == nk - 1) {
     const size_t ka = (size_t)bl[0] * kTileV;
-    const Operand A1 = a_op(ka);
+    const Operand A1 = kDma ? A : a_op(ka);
     const Operand B1 = make_operand(c + ((size_t)cv0 + ka) * D + d0,
                                     ((uint64_t)(V - cv0 - (int64_t)ka) * D - d0) * sizeof(T), (uint32_t)D,
                                     min(C::BN, D - d0), clen - (int)ka);
@@ -1632,8 +1742,14 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
                      L.bmask, L.nvg, L.hdr);
   prof_after(kKFilter, st);
   prof_before(kKTileList, st);
+  // the chunks (compact storage: cut by kept tiles), then each chunk's list
+  // (the tile lists are written after the plan: their space holds the
+  // units' kept counts meanwhile)
+  hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(1024), 0, st, (const uint8_t*)L.keep, L.nb, L.nvb_t, L.unit,
+                     L.S, L.span_u, L.nchunks, L.ch_vb, L.tlist);
   hipLaunchKernelGGL(tile_list_kernel, dim3(L.nchunks), dim3(1024), 0, st, (const uint8_t*)L.keep, L.nvb_t,
-                     L.Npad / kTileN, L.Vc / kTileV, L.tlist, L.tcount);
+                     L.Npad / kTileN, (const int*)L.ch_vb, L.list_stride, L.tlist, L.tcount,
+                     L.compact ? L.slot : nullptr);
   prof_after(kKTileList, st);
   if (want_dC) {
     prof_before(kKTransE, st);
@@ -1666,31 +1782,33 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
   // operands form the same zero blocks of G and contract them densely)
   constexpr bool MaskOn = sizeof(T) == 2;
   const bool mask = MaskOn && P.filter != 0;
+  // The chunks' vocabulary ranges are on the device (compact storage cuts
+  // them by kept tiles): each grid covers the widest chunk possible and the
+  // spare work-groups exit.  Dense storage (fp32): chunks of Vc columns.
+  const int cvb = L.Vc / kTileV;
+  const int wide = L.compact ? min(L.nvb_t, L.span_u * L.unit) : cvb;  // vocab tiles of the widest chunk
+  const int gt_grid = L.compact ? L.cap : cvb * tiles_n;
+  // dC: vocab-tile groups of at most kRasterDC dealt to the XCDs in turn
+  // (dC_gemm_kernel): 8 x GR x tiles_d x ceil(groups / 8) <= tiles_d x
+  // (tiles_v + 8 kRasterDC) work-groups for any chunk
+  const int dc_grid = tiles_d * (wide + 8 * kRasterDC);
   for (int ch = 0; ch < L.nchunks; ++ch) {
-    const int cv0 = ch * L.Vc;
-    const int clen = min(L.Vc, P.V - cv0);
-    const int cnvb = (clen + kTileV - 1) / kTileV;
-    const int cvb0 = cv0 / kTileV;
+    const int* chv = (const int*)L.ch_vb + ch;
     prof_before(kKGradTile, st);
-    hipLaunchKernelGGL(grad_tile_kernel<CG>, dim3(cnvb * tiles_n), dim3(CG::NT), 0, st, c, e, (const T*)P.bias,
+    hipLaunchKernelGGL(grad_tile_kernel<CG>, dim3(gt_grid), dim3(CG::NT), 0, st, c, e, (const T*)P.bias,
                        (const int*)L.rowmap, (const int*)L.tgt_c, (const float*)L.lse_c, (const float*)L.scale_c,
-                       P.label_smoothing, P.z_loss, P.softcap, (const int*)L.tlist + (size_t)cvb0 * tiles_n,
-                       (const int*)L.tcount + ch, P.N, P.D, P.V, cvb0, cnvb, tiles_n, L.Vc, L.gt_ld,
+                       P.label_smoothing, P.z_loss, P.softcap, (const int*)L.tlist + (size_t)ch * L.list_stride,
+                       (const int*)L.tcount + ch, P.N, P.D, P.V, chv, tiles_n, L.Vc, L.gt_ld,
                        G, (T*)L.Gt, L.g_bytes, L.gt_bytes, P.dbias ? L.db_part : nullptr, L.bmask, L.nvg,
                        L.hdr, P.filter);
     prof_after(kKGradTile, st);
     if (want_dC) {
       prof_before(kKDC, st);
-      // vocab-tile groups dealt to the XCDs in turn, at least 8 of them when
-      // the chunk has 8 vocab tiles: a whole number of rounds of 8
-      const int dc_gr = max(1, min(kRasterDC, cnvb / 8));
-      const int dc_groups = (cnvb + dc_gr - 1) / dc_gr;
-      const int dc_grid = 8 * dc_gr * tiles_d * ((dc_groups + 7) / 8);
       // with filtering (bf16), the 32x32 block masks let dC skip zero blocks
       auto dck = mask ? dC_gemm_kernel<CC, MaskOn> : dC_gemm_kernel<CC, false>;
       hipLaunchKernelGGL(dck, dim3(dc_grid), dim3(CC::NT), 0, st, (const T*)G, (const T*)L.Gt,
-                         (const T*)L.Et, L.keep, L.Npad, L.Vc, L.gt_ld, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb,
-                         tiles_d, dc_gr, L.g_bytes, L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC,
+                         (const T*)L.Et, L.keep, (const int*)L.slot, L.cap, L.Npad, L.gt_ld, P.D, P.V, L.nvb_t,
+                         chv, tiles_d, L.g_bytes, L.gt_bytes, smooth ? (const float*)L.r1c : nullptr, P.dC,
                          P.grad_bf16, (const uint8_t*)L.bmask, L.nvg);
       prof_after(kKDC, st);
     }
@@ -1699,7 +1817,7 @@ static hipError_t launch_backward_t(const Problem& P, const Layout& L, hipStream
       prof_before(kKDE, st);
       auto dek = mask ? dE_gemm_kernel<CE, MaskOn> : dE_gemm_kernel<CE, false>;
       hipLaunchKernelGGL(dek, dim3(tiles_n * tiles_d * splits), dim3(CE::NT), 0, st, G, c, L.keep,
-                         P.N, P.D, P.V, L.nvb_t, cvb0, cv0, clen, cnvb, tiles_n, tiles_d, splits,
+                         (const int*)L.slot, L.cap, P.N, P.D, P.V, L.nvb_t, chv, tiles_n, tiles_d, splits,
                          (const int32_t*)L.hdr, L.Vc, L.g_bytes,
                          bf_direct ? P.dE : (void*)dE32, bf_direct ? 1 : 0, L.dE_part, ch > 0 ? 1 : 0,
                          P.accum == kAccumAtomic ? 1 : 0, (const int*)L.rowmap,

@@ -163,6 +163,23 @@ def test_filtering_peaked(M, mode):
 
 
 @pytest.mark.parametrize("accum", ["deterministic", "atomic"])
+def test_compact_chunks_sparse_keep(M, accum):
+    # bf16 gradient tiles are stored compactly and the backward's chunks are
+    # cut by kept tiles: with a 256-wide chunk basis a chunk holds at most
+    # S + nb - 1 = 2 * 4 - 1 kept tiles (N = 777: 4 token blocks) but spans
+    # as many vocab tiles as the peaked softmax leaves kept tiles for, so
+    # chunks of very different widths (and empty chunk numbers) occur.
+    inp = W.custom(777, 264, 9000, "bf16", seed=21, e_mode="trained", targets="zipf", ignore_frac=0.03)
+    r = full_check(M, inp, "mean", True, accum=accum, vocab_chunk=256, label=f"compact sparse {accum}")
+    assert r["stats"]["tiles_kept"] < r["stats"]["tiles_total"] // 2, "peaked softmax should skip most tiles"
+    # the same with a bias gradient and label smoothing (every vocab row's
+    # dC and db come from the chunk that owns it, kept tiles or not)
+    bias = W.bias(9000, "bf16", seed=22)
+    full_check(M, inp, "sum", True, accum=accum, vocab_chunk=512, label=f"compact sparse terms {accum}", bias=bias,
+               want_db=True, ls=0.1)
+
+
+@pytest.mark.parametrize("accum", ["deterministic", "atomic"])
 def test_vocab_chunks_and_splits(M, accum):
     # 256-wide vocabulary chunks: many chunks, several dE splits, ragged last chunk
     inp = W.custom(530, 200, 1900, "bf16", seed=14, c_std=0.08, ignore_frac=0.05)
