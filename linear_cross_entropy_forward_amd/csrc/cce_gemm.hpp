@@ -628,6 +628,111 @@ struct DmaTileMN {
   }
 };
 
+// ----------------------------------------------------------------------------
+// The gradient tiles stored by 32x32 blocks (compact storage, bf16): slot j
+// of G holds a 256 x 256 tile as 64 blocks, block (t, v) (token group t,
+// vocab group v) at element j * 65536 + (8 t + v) * 1024, each [32 tokens]
+// [32 vocab] row-major (rows of 64 bytes).  A K step of 64 reads 16 blocks,
+// each block 2 KB of the stage, by two DMA instructions of 16 rows (1 KB).
+// The step's slot and position come from the A K offset of the main loop
+// (SEPA): ka = slot * STRIDE + q * 64, q the step's quarter of the tile.
+// Past the last step ka is the slot count, whose offsets lie outside G: the
+// loads read zeros.  (Not issuing the loads of zero blocks, by a branch or
+// with EXEC off, measured 5-8% slower for dC and dE at the Llama-3.1-8B
+// head, where 36% of the blocks are kept; whole K steps without a kept block
+// are left out of the step list instead.)
+// ----------------------------------------------------------------------------
+// dE's A = G (rows: tokens, K: vocab).  Stage block k = 8 h + t: token group
+// t, vocab group 2 q + h.  In LDS the 16-byte chunk c of block row r sits in
+// slot c ^ ((r >> 2) & 3): the 16 rows one ds_read_b128 cycle serves then
+// cover 16 distinct slots modulo 256 bytes (conflict free).
+template <class C>
+struct DmaBlockK {
+  static_assert(sizeof(typename C::T) == 2 && C::BK == 64 && C::BM == 256, "bf16 256-row tiles, 64-deep steps");
+  using T = typename C::T;
+  static constexpr int BYTES = 16 * 2048;
+  static constexpr int NW = C::NT / 64;
+  static constexpr int PER = 32 / NW;  // DMA instructions per wave per step
+  static constexpr int KG = C::KGROUPS;
+  uint32_t lane_off;  // byte offset of the lane's 16 bytes within a half block (global)
+  uint32_t fbase[KG];  // fragment 0's LDS offset by K group
+  __device__ __forceinline__ void init(const Operand&) {
+    const int lane = threadIdx.x & 63;
+    // lane l writes LDS chunk l % 4 of half-block row l / 4: logical chunk
+    // (l % 4) ^ ((l >> 4) & 3) of that row
+    const int r = lane >> 2, c = (lane & 3) ^ ((lane >> 4) & 3);
+    lane_off = (uint32_t)((r * 32 + c * 8) * 2);
+  }
+  __device__ __forceinline__ void issue(int i, const Operand& op, int ka, uint32_t tile) const {
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int d = wave * PER + i, k = d >> 1, half = d & 1;
+    const int h = k >> 3, t = k & 7;
+    const uint32_t slot = (uint32_t)ka >> 16, q = ((uint32_t)ka >> 6) & 3u;
+    const uint32_t blk = slot * 64u + (uint32_t)t * 8u + 2u * q + (uint32_t)h;
+    dma16(op.desc, blk * 2048u + (uint32_t)half * 1024u + lane_off, tile + (uint32_t)d * 1024u);
+  }
+  // rows rc0 + 32 j + lane % 32: token group rc0 / 32 + j; K group g: vocab
+  // group half g / 2, chunk 2 (g % 2) + lane / 32
+  __device__ __forceinline__ void frag_init(int rc0) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 31, sw = (r >> 2) & 3;
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+      const int c = 2 * (g & 1) + (lane >> 5);
+      fbase[g] = (uint32_t)(((g >> 1) * 8 + (rc0 >> 5)) * 2048 + r * 64 + ((c ^ sw) << 4));
+    }
+  }
+  __device__ __forceinline__ void read(Frag<T>& f, const lds_u8* st, int g, int j) const {
+    f.v = *(const __attribute__((address_space(3))) u32x4*)(st + fbase[g] + j * 2048);
+  }
+};
+
+// dC's A = G^T (rows: vocab, K: tokens), read through transposing LDS reads.
+// Stage block k = 8 h + v: vocab group v, token group 2 q + h, stored as in
+// memory (rows of 64 bytes): the 32 lanes of one ds_read_b64_tr_b16 cycle
+// read 4 whole consecutive rows, 256 contiguous bytes (conflict free).
+template <class C>
+struct DmaBlockMN {
+  static_assert(sizeof(typename C::T) == 2 && C::BK == 64 && C::BM == 256, "bf16 256-column tiles, 64-deep steps");
+  using T = typename C::T;
+  static constexpr int BYTES = 16 * 2048;
+  static constexpr int NW = C::NT / 64;
+  static constexpr int PER = 32 / NW;
+  static constexpr int KG = C::KGROUPS;
+  uint32_t fbase[KG];
+  __device__ __forceinline__ void init(const Operand&) {}
+  __device__ __forceinline__ void issue(int i, const Operand& op, int ka, uint32_t tile) const {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int d = wave * PER + i, k = d >> 1, half = d & 1;
+    const int h = k >> 3, v = k & 7;
+    const uint32_t slot = (uint32_t)ka >> 8, q = ((uint32_t)ka >> 6) & 3u;
+    const uint32_t blk = slot * 64u + (2u * q + (uint32_t)h) * 8u + (uint32_t)v;
+    dma16(op.desc, blk * 2048u + (uint32_t)half * 1024u + (uint32_t)lane * 16u, tile + (uint32_t)d * 1024u);
+  }
+  // columns rc0 + 32 j ..: vocab group rc0 / 32 + j.  Within each group of
+  // 16 lanes, source lane s addresses K row 8 (lane / 32) + s / 4 of the K
+  // group's 16 (plus 4 for the second read) and columns 16 ((lane / 16) % 2)
+  // + 4 (s % 4) .. +3 of the block: output lane i then holds column 16
+  // ((lane / 16) % 2) + i at those K rows, as in DmaTileMN.
+  __device__ __forceinline__ void frag_init(int rc0) {
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4, sl = lane & 15;
+    const int krow = 8 * (grp >> 1) + (sl >> 2);
+    const int col = 16 * (grp & 1) + 4 * (sl & 3);
+#pragma unroll
+    for (int g = 0; g < KG; ++g)
+      fbase[g] = (uint32_t)(((g >> 1) * 8 + (rc0 >> 5)) * 2048 + (16 * (g & 1) + krow) * 64 + col * 2);
+  }
+  __device__ __forceinline__ void read(Frag<T>& f, const lds_u8* st, int g, int j) const {
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + fbase[g] + j * 2048));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(st + fbase[g] + j * 2048 + 4 * 64));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    f.v = u32x4{ua[0], ua[1], ub[0], ub[1]};
+  }
+};
+
 // acc[fm][fn] += sum over the K steps of A_tile * B_tile^T, as mainloop()
 // (same step/offset conventions), both operands DMA-fed: K-major (DmaTile),
 // or with A_MN / B_MN MN-major (DmaTileMN, 16-bit only).  The A and B
@@ -656,14 +761,19 @@ struct NoMask {
 // With `ablocks` (SEPA), the A operand takes its own K blocks: step s reads A
 // at K offset ablocks[s / SPB] * astride + (s % SPB) * BK (the gradient
 // tiles stored one per slot), B as above.
+//
+// With ATile (a DmaBlockK / DmaBlockMN), A is read from the block layout of
+// the compact gradient tiles.
 template <class C, int SPB, bool B_MN = false, bool A_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1),
-          class MaskT = NoMask, bool SEPA = false>
+          class MaskT = NoMask, bool SEPA = false, class ATile = void>
 __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const Operand& A, const Operand& B,
                                              int nsteps, const uint16_t* blocks, void* smem,
                                              const int* __restrict__ brow = nullptr, const MaskT& mask = MaskT{},
                                              const uint16_t* ablocks = nullptr, int astride = 0) {
   using T = typename C::T;
-  using TA = std::conditional_t<A_MN, DmaTileMN<C, C::BM, C::FM>, DmaTile<C, C::BM>>;
+  using TA = std::conditional_t<!std::is_void_v<ATile>, ATile,
+                                std::conditional_t<A_MN, DmaTileMN<C, C::BM, C::FM>, DmaTile<C, C::BM>>>;
+
   using TB = std::conditional_t<B_MN, DmaTileMN<C, C::BN, C::FN>, DmaTile<C, C::BN>>;
   constexpr int KG = C::KGROUPS;
   static_assert(KG % 2 == 0, "fragment buffers alternate per K group");

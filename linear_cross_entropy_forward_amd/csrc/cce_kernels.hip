@@ -1060,22 +1060,25 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
     publish_blocks();
     __syncthreads();
     store_blocks();
-    // token rows of 256 bf16 out of the staging tile, two per instruction:
-    // wave w drains rows [w RPW, (w + 1) RPW), row `w RPW + 2 it + lane / 32`,
-    // chunk lane % 32 (vocab group chunk / 4).  With filtering the chunks of
-    // dropped blocks (not staged) are skipped: the lane's vocab group's kept
-    // token groups, one bit each.
-    constexpr int RPW = 256 / (C::NT / 64);
+    // The tile leaves by 32x32 blocks (the slot's block layout: block (t, v)
+    // at element (8 t + v) * 1024, [32 tokens][32 vocab]), half a block (16
+    // rows of 64 bytes) per instruction: wave w drains half blocks
+    // [w HPW, (w + 1) HPW); lane l takes row l / 4, chunk l % 4 of its half
+    // block.  With filtering a dropped block (not staged) is not stored.
+    constexpr int HPW = 128 / (C::NT / 64);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t kept_tg = filter ? sbm[(lane & 31) >> 2] : 0xffu;
 #pragma unroll 4
-    for (int it = 0; it < RPW / 2; ++it) {
-      const int rr = wave * RPW + it * 2 + (lane >> 5), jc = lane & 31;
-      const u32x4 val = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(rr, jc * 8));
-      if ((kept_tg >> (rr >> 5)) & 1u)
-        __builtin_amdgcn_raw_buffer_store_b128(
-            val, rg, ((uint32_t)li * (uint32_t)(kSlotRows * kTileV) + (uint32_t)rr * kTileV + (uint32_t)jc * 8u) * 2u,
-            0, kStoreNT);
+    for (int it = 0; it < HPW; ++it) {
+      const int hb = wave * HPW + it, k = hb >> 1;  // k = 8 t + v
+      const int t = k >> 3, v = k & 7;
+      if (filter && !((sbm[v] >> t) & 1u)) continue;
+      const int r = 16 * (hb & 1) + (lane >> 2), c = lane & 3;
+      const u32x4 val =
+          *(const __attribute__((address_space(3))) u32x4*)(tile + slot(32 * t + r, 32 * v + 8 * c));
+      __builtin_amdgcn_raw_buffer_store_b128(
+          val, rg, ((uint32_t)li * (uint32_t)(kSlotRows * kTileV) + (uint32_t)k * 1024u + (uint32_t)r * 32u +
+                    (uint32_t)c * 8u) * 2u,
+          0, kStoreNT);
     }
     if (sums) {
       __syncthreads();  // the drain's LDS reads are done
@@ -1270,19 +1273,16 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
       const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
       const DCMask mk{(const lds_u64*)smask, 32 * wm};
       if (nk > 0 && blocks[nk - 1] == nk - 1)
-        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true>(acc, A, B, nk * SPB, nullptr, smem, nullptr, mk, ablk,
-                                                           kSlotRows);
+        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>>(acc, A, B, nk * SPB, nullptr, smem, nullptr, mk, ablk, kSlotRows);
       else
-        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true>(acc, A, B, nk * SPB, blocks, smem, nullptr, mk, ablk,
-                                                           kSlotRows);
+        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>>(acc, A, B, nk * SPB, blocks, smem, nullptr, mk, ablk, kSlotRows);
     } else {
       // the kept token blocks are the first nk (no filtering effect on this
       // tile; compacted slots put the blocks of ignored rows last): contiguous
       // K for B
       const uint16_t* bl = nk > 0 && blocks[nk - 1] == nk - 1 ? nullptr : blocks;
       if constexpr (kMN)
-        mainloop_dma<C, SPB, false, kMN, 3, NoMask, true>(acc, A, B, nk * SPB, bl, smem, nullptr, NoMask{}, ablk,
-                                                           kSlotRows);
+        mainloop_dma<C, SPB, false, kMN, 3, NoMask, true, DmaBlockMN<C>>(acc, A, B, nk * SPB, bl, smem, nullptr, NoMask{}, ablk, kSlotRows);
       else
         mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, bl, smem);
     }
@@ -1444,11 +1444,9 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     if constexpr (MASK) {
       const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
       const DEMask mk{(const lds_u64*)smask, 4 * wm};
-      mainloop_dma<C, SPB, true, false, 2, DEMask, true>(acc, a, b, nk * SPB, bl, smem, nullptr, mk, ablk,
-                                                         kSlotRows * kTileV);
+      mainloop_dma<C, SPB, true, false, 2, DEMask, true, DmaBlockK<C>>(acc, a, b, nk * SPB, bl, smem, nullptr, mk, ablk, kSlotRows * kTileV);
     } else if constexpr (kDma) {
-      mainloop_dma<C, SPB, true, false, 2, NoMask, true>(acc, a, b, nk * SPB, bl, smem, nullptr, NoMask{}, ablk,
-                                                         kSlotRows * kTileV);
+      mainloop_dma<C, SPB, true, false, 2, NoMask, true, DmaBlockK<C>>(acc, a, b, nk * SPB, bl, smem, nullptr, NoMask{}, ablk, kSlotRows * kTileV);
     } else {
       mainloop<C, false, true, SPB>(acc, a, b, nk * SPB, bl, (T*)smem);
     }
