@@ -764,12 +764,18 @@ struct NoMask {
 //
 // With ATile (a DmaBlockK / DmaBlockMN), A is read from the block layout of
 // the compact gradient tiles.
+//
+// With `steps`, only the listed steps run: steps[s] is the index, in the
+// full sequence above, of the s-th step of the loop (ascending; nsteps
+// listed), so K offsets, block lists and masks follow it (the steps whose
+// blocks are all zero are left out).
 template <class C, int SPB, bool B_MN = false, bool A_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1),
-          class MaskT = NoMask, bool SEPA = false, class ATile = void>
+          class MaskT = NoMask, bool SEPA = false, class ATile = void, bool STEPS = false>
 __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const Operand& A, const Operand& B,
                                              int nsteps, const uint16_t* blocks, void* smem,
                                              const int* __restrict__ brow = nullptr, const MaskT& mask = MaskT{},
-                                             const uint16_t* ablocks = nullptr, int astride = 0) {
+                                             const uint16_t* ablocks = nullptr, int astride = 0,
+                                             const uint16_t* steps = nullptr) {
   using T = typename C::T;
   using TA = std::conditional_t<!std::is_void_v<ATile>, ATile,
                                 std::conditional_t<A_MN, DmaTileMN<C, C::BM, C::FM>, DmaTile<C, C::BM>>>;
@@ -784,23 +790,31 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   const int wave = threadIdx.x >> 6;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int kend = A.kdim > B.kdim ? A.kdim : B.kdim;
-  // K offset of step s; steps past the end read zeros (offset kend).  The
-  // block-list index is clamped so that it stays inside the list.
-  const int last_blk = (nsteps - 1) / SPB;
-  auto kofs = [&](int s) -> int {
-    const int b = s / SPB < last_blk ? s / SPB : last_blk;
-    const int k = blocks ? (int)blocks[b] * (SPB * C::BK) + (s % SPB) * C::BK : s * C::BK;
+  // Index of step s in the full sequence (clamped to the last step), and
+  // K offsets of step s from it; steps past the end read zeros (offset kend).
+  // The loop reads step s + 3's index one step ahead of its offsets, so no
+  // LDS read waits on another.
+  auto full = [&](int s) -> int {
+    if constexpr (STEPS) return (int)steps[s < nsteps ? s : nsteps - 1];
+    else return s;
+  };
+  // block-list index of full step f, kept inside the list
+  const int last_blk = STEPS ? 0 : (nsteps - 1) / SPB;
+  auto blk = [&](int f) -> int {
+    if constexpr (STEPS) return f / SPB;
+    else return f / SPB < last_blk ? f / SPB : last_blk;
+  };
+  auto kofs_f = [&](int s, int f) -> int {
+    const int k = blocks ? (int)blocks[blk(f)] * (SPB * C::BK) + (f % SPB) * C::BK : f * C::BK;
     return s < nsteps ? k : kend;
   };
-  // A's K offset of step s: kofs(s), or from its own block list
-  auto kofs_a = [&](int s) -> int {
-    if constexpr (SEPA) {
-      const int b = s / SPB < last_blk ? s / SPB : last_blk;
-      return s < nsteps ? (int)ablocks[b] * astride + (s % SPB) * C::BK : kend;
-    } else {
-      return kofs(s);
-    }
+  // A's K offset: the same, or from its own block list
+  auto kofs_a_f = [&](int s, int f) -> int {
+    if constexpr (SEPA) return s < nsteps ? (int)ablocks[blk(f)] * astride + (f % SPB) * C::BK : kend;
+    else return kofs_f(s, f);
   };
+  auto kofs = [&](int s) -> int { return kofs_f(s, full(s)); };
+  auto kofs_a = [&](int s) -> int { return kofs_a_f(s, full(s)); };
   const lds_u8* base = (const lds_u8*)smem;
   const uint32_t base_addr = (uint32_t)(uintptr_t)base;
 
@@ -839,7 +853,7 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   // 2h + 1) hold nonzero values.  The MFMAs of a zero block are skipped (they
   // would add exact zeros).  The bits of step s + 1 are read at the top of
   // step s (LDS, after the first barrier has published them).
-  uint32_t mcur = MaskT::kActive ? (uint32_t)__builtin_amdgcn_readfirstlane((int)mask(0)) : 0xffffffffu;
+  uint32_t mcur = MaskT::kActive ? (uint32_t)__builtin_amdgcn_readfirstlane((int)mask(STEPS ? full(0) : 0)) : 0xffffffffu;
 
   constexpr int NFR = C::FM + C::FN;
   constexpr int BLOCKS = C::FM * C::FN;
@@ -850,14 +864,19 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   // those cover it and the loop never waits on that read alone.
   // (With SEPA, A's offsets ka1 / ka2 likewise.)
   int kan = SEPA ? __builtin_amdgcn_readfirstlane(kofs_a(1)) : 0;
+  // (with a step list) full indices of steps s + 1 and s + 2, carried from
+  // step to step
+  int fn1 = STEPS ? __builtin_amdgcn_readfirstlane(full(1)) : 0;
+  int fn2 = STEPS ? __builtin_amdgcn_readfirstlane(full(2)) : 0;
   auto step = [&](int s, const lds_u8* st, const lds_u8* nx, uint32_t st_addr, uint32_t nx_addr, int k1) -> int {
     // wave-uniform: kept in a scalar register
-    const int k2 = __builtin_amdgcn_readfirstlane(kofs(s + 2));
+    const int f1 = STEPS ? fn1 : (s + 1 < nsteps ? s + 1 : nsteps - 1), f2 = STEPS ? fn2 : s + 2;
+    const int f3 = STEPS ? __builtin_amdgcn_readfirstlane(full(s + 3)) : 0;
+    const int k2 = __builtin_amdgcn_readfirstlane(kofs_f(s + 2, f2));
     const int ka1 = SEPA ? kan : k1;
-    const int ka2 = SEPA ? __builtin_amdgcn_readfirstlane(kofs_a(s + 2)) : k2;
+    const int ka2 = SEPA ? __builtin_amdgcn_readfirstlane(kofs_a_f(s + 2, f2)) : k2;
     const uint32_t mnext =
-        MaskT::kActive ? (uint32_t)__builtin_amdgcn_readfirstlane((int)mask(s + 1 < nsteps ? s + 1 : nsteps - 1))
-                       : 0xffffffffu;
+        MaskT::kActive ? (uint32_t)__builtin_amdgcn_readfirstlane((int)mask(f1)) : 0xffffffffu;
     auto group = [&](auto gc) {
       constexpr int g = decltype(gc)::value;
       constexpr bool last = g + 1 == KG;
@@ -918,6 +937,10 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
     }(std::make_integer_sequence<int, KG>{});
     mcur = mnext;
     if constexpr (SEPA) kan = ka2;
+    if constexpr (STEPS) {
+      fn1 = f2;
+      fn2 = f3;
+    }
     return k2;
   };
 

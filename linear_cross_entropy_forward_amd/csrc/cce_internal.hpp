@@ -21,7 +21,7 @@ constexpr int kPartialWidth = 128;
 // contractions skip their MFMAs there.
 constexpr int kBlock = 32;
 constexpr int kBlocksPerTile = kTileV / kBlock;  // 8 along either side
-constexpr int kMaxBlocks = 2048;  // K blocks one contraction tile can list
+constexpr int kMaxBlocks = 1024;  // K blocks one contraction tile can list
 // Compact gradient storage: one 256 x 256 tile per slot, rows of 256
 // elements (token-major); slot j starts at row j * kSlotRows.
 constexpr int kSlotRows = 256;

@@ -1107,6 +1107,28 @@ __device__ __forceinline__ int valid_blocks(const int32_t* __restrict__ hdr) {
   return (hdr[kHdrNValidBwd] + kTileN - 1) / kTileN;
 }
 
+// The steps (of SPB = 4 per K block) that hold a nonzero block of the A
+// tile, by their index in the full step sequence, into LDS; returns their
+// count.  `nz(c)` tells whether step c of the full sequence does.
+template <class F>
+__device__ __forceinline__ int collect_steps(int nfull, const F& nz, uint16_t* list) {
+  __shared__ int s_ns;
+  if (threadIdx.x < 64) {
+    int total = 0;
+    for (int c0 = 0; c0 < nfull; c0 += 64) {
+      const int c = c0 + (int)threadIdx.x;
+      const bool k = c < nfull && nz(c);
+      const uint64_t bal = __ballot(k);
+      const int pre = __popcll(bal & ((1ull << threadIdx.x) - 1ull));
+      if (k) list[total + pre] = (uint16_t)c;
+      total += __popcll(bal);
+    }
+    if (threadIdx.x == 0) s_ns = total;
+  }
+  __syncthreads();
+  return s_ns;
+}
+
 // Kept K blocks of one output tile into LDS; returns their count.
 __device__ __forceinline__ int collect_blocks(const uint8_t* __restrict__ keep, size_t base, int stride,
                                              int count, uint16_t* list) {
@@ -1207,6 +1229,7 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
   __shared__ uint16_t blocks[kMaxBlocks];
   __shared__ uint16_t ablk[kMN ? kMaxBlocks : 1];  // bf16: the G slot of each listed token block
   __shared__ uint64_t smask[MASK ? kMaxBlocks : 1];
+  __shared__ uint16_t steps[MASK ? 4 * kMaxBlocks : 1];  // the steps with a nonzero block (masked)
   const int cvb0 = chv[0], tiles_v = chv[1] - cvb0;
   const int cv0 = cvb0 * kTileV, clen = min(tiles_v * kTileV, V - cv0);
   // Groups of GR vocab tiles (each with all its d tiles) are dealt to the
@@ -1265,24 +1288,34 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
       for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
     constexpr int SPB = kTileN / C::BK;
     if constexpr (MASK) {
-      // the tile's block-mask bytes for each kept token block, published to the
-      // main loop by its first barrier
+      // the tile's block-mask bytes for each kept token block, then the steps
+      // (16 token rows of a token block each) with a nonzero block: bits
+      // 8 v + 2 (c % 4) + h of the step's mask word
       for (int j = threadIdx.x; j < nk; j += C::NT)
         smask[j] = *reinterpret_cast<const uint64_t*>(bmask + (size_t)blocks[j] * nvg +
                                                       (size_t)(cvb0 + tvl) * kBlocksPerTile);
+      __syncthreads();
+      const int ns = collect_steps(
+          nk * SPB, [&](int c) { return ((smask[c >> 2] >> (2 * (c & 3))) & 0x0303030303030303ull) != 0; }, steps);
       const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
       const DCMask mk{(const lds_u64*)smask, 32 * wm};
-      if (nk > 0 && blocks[nk - 1] == nk - 1)
-        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>>(acc, A, B, nk * SPB, nullptr, smem, nullptr, mk, ablk, kSlotRows);
+      const uint16_t* bl = nk > 0 && blocks[nk - 1] == nk - 1 ? nullptr : blocks;
+      // the step list costs about 5% of the loop: taken when it leaves out
+      // at least an eighth of the steps
+      if (8 * ns <= 7 * nk * SPB)
+        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>, true>(acc, A, B, ns, bl, smem, nullptr,
+                                                                              mk, ablk, kSlotRows, steps);
       else
-        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>>(acc, A, B, nk * SPB, blocks, smem, nullptr, mk, ablk, kSlotRows);
+        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>>(acc, A, B, nk * SPB, bl, smem, nullptr, mk,
+                                                                        ablk, kSlotRows);
     } else {
       // the kept token blocks are the first nk (no filtering effect on this
       // tile; compacted slots put the blocks of ignored rows last): contiguous
       // K for B
       const uint16_t* bl = nk > 0 && blocks[nk - 1] == nk - 1 ? nullptr : blocks;
       if constexpr (kMN)
-        mainloop_dma<C, SPB, false, kMN, 3, NoMask, true, DmaBlockMN<C>>(acc, A, B, nk * SPB, bl, smem, nullptr, NoMask{}, ablk, kSlotRows);
+        mainloop_dma<C, SPB, false, kMN, 3, NoMask, true, DmaBlockMN<C>>(acc, A, B, nk * SPB, bl, smem, nullptr,
+                                                                        NoMask{}, ablk, kSlotRows);
       else
         mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, bl, smem);
     }
@@ -1360,6 +1393,7 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kDma ? C::LDS_DMA_BYTES : C::LDS_BYTES];
   __shared__ uint16_t blocks[kMaxBlocks];
   __shared__ uint16_t ablk[kDma ? kMaxBlocks : 1];  // bf16: the G slot of each listed vocab block
+  __shared__ uint16_t steps[MASK ? 4 * kMaxBlocks : 1];  // the steps with a nonzero block (masked)
   const int cvb0 = chv[0], cnvb = chv[1] - cvb0;
   const int cv0 = cvb0 * kTileV, clen = min(cnvb * kTileV, V - cv0);
   // The grid holds tiles_n x tiles_d x splits work-groups.  The first
@@ -1430,12 +1464,17 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
   constexpr int SPB = kTileV / C::BK;
+  int ns = nk * SPB;  // steps that run
   if constexpr (MASK) {
     // the block-mask bytes of the token block for each of the split's kept
-    // vocab blocks, published to the main loop by its first barrier
+    // vocab blocks, then the steps that hold a nonzero block
     for (int j = threadIdx.x; j < nk; j += C::NT)
       smask[j] = *reinterpret_cast<const uint64_t*>(bmask + (size_t)tn * nvg +
                                                     (size_t)(cvb0 + bl[j]) * kBlocksPerTile);
+    __syncthreads();
+    // the steps (64 vocab of a vocab block each) with a nonzero block: the
+    // 16 bits of the two vocab-group bytes 2 (c % 4), 2 (c % 4) + 1
+    ns = collect_steps(nk * SPB, [&](int c) { return ((smask[c >> 2] >> (16 * (c & 3))) & 0xffffu) != 0; }, steps);
   }
   auto loop = [&](const Operand& a, const Operand& b, const uint16_t* bl) {
     // the step's DMA in two parts (right after the barrier and in the first
@@ -1444,9 +1483,16 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     if constexpr (MASK) {
       const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
       const DEMask mk{(const lds_u64*)smask, 4 * wm};
-      mainloop_dma<C, SPB, true, false, 2, DEMask, true, DmaBlockK<C>>(acc, a, b, nk * SPB, bl, smem, nullptr, mk, ablk, kSlotRows * kTileV);
+      // the step list: when it leaves out at least an eighth of the steps
+      if (8 * ns <= 7 * nk * SPB)
+        mainloop_dma<C, SPB, true, false, 2, DEMask, true, DmaBlockK<C>, true>(acc, a, b, ns, bl, smem, nullptr, mk,
+                                                                               ablk, kSlotRows * kTileV, steps);
+      else
+        mainloop_dma<C, SPB, true, false, 2, DEMask, true, DmaBlockK<C>>(acc, a, b, nk * SPB, bl, smem, nullptr, mk,
+                                                                         ablk, kSlotRows * kTileV);
     } else if constexpr (kDma) {
-      mainloop_dma<C, SPB, true, false, 2, NoMask, true, DmaBlockK<C>>(acc, a, b, nk * SPB, bl, smem, nullptr, NoMask{}, ablk, kSlotRows * kTileV);
+      mainloop_dma<C, SPB, true, false, 2, NoMask, true, DmaBlockK<C>>(acc, a, b, nk * SPB, bl, smem, nullptr,
+                                                                       NoMask{}, ablk, kSlotRows * kTileV);
     } else {
       mainloop<C, false, true, SPB>(acc, a, b, nk * SPB, bl, (T*)smem);
     }
@@ -1464,7 +1510,7 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     loop(A, B, bl);
   }
 
-  if (nk == 0 && (accumulate || atomic)) return;  // nothing to add
+  if (ns == 0 && (accumulate || atomic)) return;  // nothing to add
   // Rows of the tile are compacted slots n0..; slot n' is token row
   // srow[n' - n0] (ignored rows after the valid ones, -1 past N), so the first
   // write of dE also zeroes the ignored rows.  64-bit row pointers: the rows
