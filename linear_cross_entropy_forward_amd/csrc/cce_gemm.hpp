@@ -853,7 +853,8 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   // 2h + 1) hold nonzero values.  The MFMAs of a zero block are skipped (they
   // would add exact zeros).  The bits of step s + 1 are read at the top of
   // step s (LDS, after the first barrier has published them).
-  uint32_t mcur = MaskT::kActive ? (uint32_t)__builtin_amdgcn_readfirstlane((int)mask(STEPS ? full(0) : 0)) : 0xffffffffu;
+  uint32_t mcur =
+      MaskT::kActive ? (uint32_t)__builtin_amdgcn_readfirstlane((int)mask(STEPS ? full(0) : 0)) : 0xffffffffu;
 
   constexpr int NFR = C::FM + C::FN;
   constexpr int BLOCKS = C::FM * C::FN;
