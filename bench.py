@@ -88,15 +88,18 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic(name, N, D, V, es, nVB, chunk_lens, tiles_kept=1.0, blocks_kept=1.0):
+def algorithmic(name, N, D, V, es, nVB, launches, tiles_kept=1.0):
     """(flops, bytes) per launch of `name`, averaged over its launches in a
-    step: the work the filter leaves (the gradient tiles on the kept tiles,
-    the two contractions on the kept 32x32 blocks; 2 flops per multiply-add)."""
+    step: the work the tile filter leaves (the backward's three contractions
+    on the kept 256x256 tiles; 2 flops per multiply-add).  Inside kept tiles
+    dC and dE also skip the MFMAs of dropped 32x32 blocks: that is a saving
+    of the kernels, not less work of the method, and is reported apart
+    (blocks_kept_frac, mfma_flops_executed_per_launch)."""
     if name == "fwd_tile":
         return 2.0 * N * V * D, (N + V) * D * es + N * nVB * 8.0
     if name in ("grad_tile", "dC_gemm", "dE_gemm"):
-        f = [2.0 * N * cl * D for cl in chunk_lens]
-        return float(np.mean(f)) * (tiles_kept if name == "grad_tile" else blocks_kept), 0.0
+        # one launch per vocabulary chunk: the chunks cover the vocabulary
+        return 2.0 * N * V * D * tiles_kept / max(1.0, launches), 0.0
     if name == "rows":
         return 2.0 * N * D, N * (2.0 * D * es + 8 + nVB * 8.0 + 8)
     if name == "reduce":
@@ -476,25 +479,26 @@ def main():
     # executed: forward, recompute of the kept tiles, contractions of the kept blocks
     exec_frac = (2.0 + 2.0 * kept_frac + 4.0 * kept_bfrac) / 8.0
 
-    # chunk lengths of the backward, for per-launch algorithmic work
     Vc = M.vocab_chunk(N, D, V, tdt, args.vocab_chunk)
-    chunk_lens = [min(Vc, V - s) for s in range(0, V, Vc)]
     nVB = -(-V // 128)
     kernels = {}
     for name, d in per.items():
-        fl, by = algorithmic(name, N, D, V, es, nVB, chunk_lens, kept_frac, kept_bfrac)
+        fl, by = algorithmic(name, N, D, V, es, nVB, d["launches_per_step"], kept_frac)
         d = dict(d)
         d["tflops"] = fl / (d["avg_ms"] * 1e-3) / 1e12 if fl else None
         d["gbs"] = by / (d["avg_ms"] * 1e-3) / 1e9 if by else None
         d["traffic_bytes"] = traffic_for(name, args.workload)
         kernels[name] = d
     dom = max(per, key=lambda k: per[k]["ms_per_step"])
-    fl, by = algorithmic(dom, N, D, V, es, nVB, chunk_lens, kept_frac, kept_bfrac)
+    fl, by = algorithmic(dom, N, D, V, es, nVB, per[dom]["launches_per_step"], kept_frac)
     if dom in MFMA_KERNELS:
         ach = fl / (per[dom]["avg_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
                 "traffic": traffic_for(dom, args.workload), "kernel": dom,
                 "avg_launch_ms": per[dom]["avg_ms"], "algorithmic_flops_per_launch": fl}
+        if dom in ("dC_gemm", "dE_gemm"):
+            # the MFMAs it issues: those of the kept 32x32 blocks
+            roof["mfma_flops_executed_per_launch"] = fl * kept_bfrac / max(kept_frac, 1e-30)
     else:
         ach = by / (per[dom]["avg_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,

@@ -1129,25 +1129,60 @@ __device__ __forceinline__ int collect_steps(int nfull, const F& nz, uint16_t* l
   return s_ns;
 }
 
-// Kept K blocks of one output tile into LDS; returns their count.
-__device__ __forceinline__ int collect_blocks(const uint8_t* __restrict__ keep, size_t base, int stride,
-                                             int count, uint16_t* list) {
-  __shared__ int s_cnt;
-  if (threadIdx.x < 64) {
-    int total = 0;
-    for (int j0 = 0; j0 < count; j0 += 64) {
-      const int j = j0 + (int)threadIdx.x;
-      const bool k = j < count && keep[base + (size_t)j * stride];
-      const uint64_t bal = __ballot(k);
-      const int pre = __popcll(bal & ((1ull << threadIdx.x) - 1ull));
-      if (k) list[total + pre] = (uint16_t)j;
-      total += __popcll(bal);
-    }
-    if (threadIdx.x == 0) s_cnt = total;
+// The kept K blocks of one contraction tile, in ascending order, into LDS
+// (list), with each listed block's G slot (SLOT: slots, compact storage) and
+// its block-mask word (WORDS: words, filtering); returns the count.
+// Candidate i is keep[kbase + i kstride] (its slot at the same index of the
+// [nb][nvb_t] slot map) with mask word at bmask + mbase + i mstride.  Every
+// thread loads its candidates' flag, slot and word at once, so the three
+// come in one memory round trip.  count <= kMaxBlocks.
+template <int NT, bool SLOT, bool WORDS>
+__device__ __forceinline__ int collect_kept(const uint8_t* __restrict__ keep, size_t kbase, int kstride, int count,
+                                            const int* __restrict__ slot, const uint8_t* __restrict__ bmask,
+                                            size_t mbase, int mstride, uint16_t* list, uint16_t* slots,
+                                            uint64_t* words) {
+  constexpr int R = kMaxBlocks / NT, NW = NT / 64;
+  static_assert(kMaxBlocks % NT == 0, "candidates per thread");
+  __shared__ int wcnt[NW];
+  const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  bool kp[R];
+  int sl[R];
+  uint64_t mw[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = r * NT + tid;
+    const bool in = i < count;
+    kp[r] = in && keep[kbase + (size_t)i * kstride] != 0;
+    if constexpr (SLOT) sl[r] = in ? slot[kbase + (size_t)i * kstride] : 0;
+    if constexpr (WORDS) mw[r] = in ? *reinterpret_cast<const uint64_t*>(bmask + mbase + (size_t)i * mstride) : 0;
   }
-  __syncthreads();
-  return s_cnt;
+  // (every pass ends on a barrier, and there is at least one: the caller
+  // relies on one after the call)
+  int base = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r > 0 && r * NT >= count) break;  // uniform
+    const uint64_t bal = __ballot(kp[r]);
+    if (lane == 0) wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) off += wcnt[w];
+      tot += wcnt[w];
+    }
+    if (kp[r]) {
+      const int pos = off + __popcll(bal & ((1ull << lane) - 1ull));
+      list[pos] = (uint16_t)(r * NT + tid);
+      if constexpr (SLOT) slots[pos] = (uint16_t)sl[r];
+      if constexpr (WORDS) words[pos] = mw[r];
+    }
+    __syncthreads();  // wcnt is rewritten next pass; the lists are published
+    base += tot;
+  }
+  return __builtin_amdgcn_readfirstlane(base);  // the same in every lane
 }
+
 
 // ============================================================================
 // 32x32 block masks of the gradient contractions (mainloop_dma MaskT).  The
@@ -1266,15 +1301,13 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
   {
     const int vl0 = tvl * C::BM, d0 = td * C::BN;
     const int nb = Npad / kTileN;
-    const int nk = collect_blocks(keep, (size_t)(cvb0 + tvl), nvb_t, nb, blocks);
-
-    // bf16: A's K blocks are the tiles' slots (K rows slot * 256 ..); G seen
-    // as cap * 256 token rows of the 256 vocab columns
-    if constexpr (kMN) {
-      for (int j = threadIdx.x; j < nk; j += C::NT)
-        ablk[j] = (uint16_t)slot[(size_t)blocks[j] * nvb_t + cvb0 + tvl];
-      __syncthreads();
-    }
+    // the kept token blocks of the vocab tile with, for bf16, their G slots
+    // (A's K blocks: K rows slot * 256 .., G seen as cap * 256 token rows of
+    // the 256 vocab columns) and, with block masks, the tile's block-mask
+    // bytes of each (byte v: vocab group v, bit t: token group t)
+    const int nk = collect_kept<C::NT, kMN, MASK>(keep, (size_t)(cvb0 + tvl), nvb_t, nb, slot, bmask,
+                                                  (size_t)(cvb0 + tvl) * kBlocksPerTile, nvg, blocks, ablk,
+                                                  (uint64_t*)smask);
     const Operand A =
         kMN ? make_operand(G, g_bytes, (uint32_t)kTileV, min(C::BM, clen - vl0), cap * kSlotRows)
             : make_operand(Gt + (size_t)vl0 * gt_ld, gt_bytes - (size_t)vl0 * gt_ld * sizeof(T), (uint32_t)gt_ld,
@@ -1288,13 +1321,8 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
       for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
     constexpr int SPB = kTileN / C::BK;
     if constexpr (MASK) {
-      // the tile's block-mask bytes for each kept token block, then the steps
-      // (16 token rows of a token block each) with a nonzero block: bits
-      // 8 v + 2 (c % 4) + h of the step's mask word
-      for (int j = threadIdx.x; j < nk; j += C::NT)
-        smask[j] = *reinterpret_cast<const uint64_t*>(bmask + (size_t)blocks[j] * nvg +
-                                                      (size_t)(cvb0 + tvl) * kBlocksPerTile);
-      __syncthreads();
+      // the steps (64 tokens of a token block each) with a nonzero block:
+      // bits 8 v + 2 (c % 4) + h of the step's mask word
       const int ns = collect_steps(
           nk * SPB, [&](int c) { return ((smask[c >> 2] >> (2 * (c & 3))) & 0x0303030303030303ull) != 0; }, steps);
       const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
@@ -1431,22 +1459,24 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   }
   const int n0 = tn * C::BM, d0 = td * C::BN;
   // token rows of the tile's compacted slots, for the epilogue (visible after
-  // the barrier that ends collect_blocks)
+  // the barriers that end collect_kept)
   __shared__ int srow[C::BM];
   for (int i = threadIdx.x; i < C::BM; i += C::NT) srow[i] = rowmap[n0 + i];
   // this split's share of the token block's kept vocab blocks in the chunk:
   // the kept list cut into equal counts (with filtering, kept blocks gather
   // at the frequent targets, so equal vocab ranges would load one split)
-  const int nall = collect_blocks(keep, (size_t)tn * nvb_t + cvb0, 1, cnvb, blocks);
+  // (with, for bf16, each kept vocab block's G slot: A's K blocks, K offset
+  // slot * 65536 from row n' * 256 of a slot; with block masks, the token
+  // block's block-mask bytes of each: byte v vocab group v, bit t token
+  // group t)
+  const int nall = collect_kept<C::NT, kDma, MASK>(keep, (size_t)tn * nvb_t + cvb0, 1, cnvb, slot, bmask,
+                                                   (size_t)tn * nvg + (size_t)cvb0 * kBlocksPerTile,
+                                                   kBlocksPerTile, blocks, ablk, (uint64_t*)smask);
   const int lo = (int)((int64_t)nall * s / splits), hi = (int)((int64_t)nall * (s + 1) / splits);
   const int nk = hi - lo;
   const uint16_t* bl = blocks + lo;
-  // bf16: A's K blocks are the tiles' slots (K offset slot * 65536 from row
-  // n' * 256 of a slot); published by this barrier
-  if constexpr (kDma) {
-    for (int j = threadIdx.x; j < nk; j += C::NT) ablk[j] = (uint16_t)slot[(size_t)tn * nvb_t + cvb0 + bl[j]];
-    __syncthreads();
-  }
+  const uint16_t* abl = ablk + lo;
+  const uint64_t* sml = (const uint64_t*)smask + lo;
 
   // G rows n0.. over the chunk's vocabulary (K-major), from vocab offset ka
   // (fp32)
@@ -1466,15 +1496,10 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   constexpr int SPB = kTileV / C::BK;
   int ns = nk * SPB;  // steps that run
   if constexpr (MASK) {
-    // the block-mask bytes of the token block for each of the split's kept
-    // vocab blocks, then the steps that hold a nonzero block
-    for (int j = threadIdx.x; j < nk; j += C::NT)
-      smask[j] = *reinterpret_cast<const uint64_t*>(bmask + (size_t)tn * nvg +
-                                                    (size_t)(cvb0 + bl[j]) * kBlocksPerTile);
-    __syncthreads();
-    // the steps (64 vocab of a vocab block each) with a nonzero block: the
-    // 16 bits of the two vocab-group bytes 2 (c % 4), 2 (c % 4) + 1
-    ns = collect_steps(nk * SPB, [&](int c) { return ((smask[c >> 2] >> (16 * (c & 3))) & 0xffffu) != 0; }, steps);
+    // the steps (64 vocab of one of the split's vocab blocks each) with a
+    // nonzero block: the 16 bits of the two vocab-group bytes 2 (c % 4),
+    // 2 (c % 4) + 1
+    ns = collect_steps(nk * SPB, [&](int c) { return ((sml[c >> 2] >> (16 * (c & 3))) & 0xffffu) != 0; }, steps);
   }
   auto loop = [&](const Operand& a, const Operand& b, const uint16_t* bl) {
     // the step's DMA in two parts (right after the barrier and in the first
@@ -1482,17 +1507,17 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     // MN-major classifier tile, slower for the K-major ones
     if constexpr (MASK) {
       const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
-      const DEMask mk{(const lds_u64*)smask, 4 * wm};
+      const DEMask mk{(const lds_u64*)sml, 4 * wm};
       // the step list: when it leaves out at least an eighth of the steps
       if (8 * ns <= 7 * nk * SPB)
         mainloop_dma<C, SPB, true, false, 2, DEMask, true, DmaBlockK<C>, true>(acc, a, b, ns, bl, smem, nullptr, mk,
-                                                                               ablk, kSlotRows * kTileV, steps);
+                                                                               abl, kSlotRows * kTileV, steps);
       else
         mainloop_dma<C, SPB, true, false, 2, DEMask, true, DmaBlockK<C>>(acc, a, b, nk * SPB, bl, smem, nullptr, mk,
-                                                                         ablk, kSlotRows * kTileV);
+                                                                         abl, kSlotRows * kTileV);
     } else if constexpr (kDma) {
       mainloop_dma<C, SPB, true, false, 2, NoMask, true, DmaBlockK<C>>(acc, a, b, nk * SPB, bl, smem, nullptr,
-                                                                       NoMask{}, ablk, kSlotRows * kTileV);
+                                                                       NoMask{}, abl, kSlotRows * kTileV);
     } else {
       mainloop<C, false, true, SPB>(acc, a, b, nk * SPB, bl, (T*)smem);
     }
@@ -1500,7 +1525,7 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   // the split's blocks consecutive (every block kept): contiguous K from its
   // first block (for bf16 in B only: A follows the slots)
   if (nk > 0 && (int)bl[nk - 1] - (int)bl[0] == nk - 1) {
-    const size_t ka = (size_t)bl[0] * kTileV;
+    const size_t ka = (size_t)__builtin_amdgcn_readfirstlane((int)bl[0]) * kTileV;
     const Operand A1 = kDma ? A : a_op(ka);
     const Operand B1 = make_operand(c + ((size_t)cv0 + ka) * D + d0,
                                     ((uint64_t)(V - cv0 - (int64_t)ka) * D - d0) * sizeof(T), (uint32_t)D,
