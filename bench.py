@@ -38,11 +38,11 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "57b903efabc626c9f9292423555773b06dc1f2877795c54a2951d8dbdd7a0d39",
+    "source_sha256": "2c9386b0e0820e1e636f8070ea372a385d7f3d103f26357399f48a405873fe9d",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9381.9e6, "grad_tile": 2248.9e6, "dC_gemm": 1904.8e6, "dE_gemm": 1702.9e6,
-        "rows": 120.8e6, "filter": 37.2e6, "transpose_e": 67.2e6, "dE_reduce": 100.7e6,
+        "fwd_tile": 9355.2e6, "grad_tile": 1827.0e6, "dC_gemm": 2004.9e6, "dE_gemm": 1715.9e6,
+        "rows": 121.3e6, "filter": 37.2e6, "transpose_e": 67.3e6, "dE_reduce": 100.7e6,
     },
 }
 

@@ -709,12 +709,31 @@ __global__ __launch_bounds__(1024) void chunk_plan_kernel(const uint8_t* __restr
     for (int c = tid; c <= nchunks; c += 1024) ch_vb[c] = min(c * unit, nvb_t);
     return;
   }
+  // the units' kept counts: in LDS when they fit (the greedy pass below
+  // reads them one by one), one (unit, token block) pair per thread;
+  // else in the scratch, one unit per thread
+  constexpr int kLdsUnits = 4096;
+  __shared__ int lcnt[kLdsUnits];
   const int nunits = (nvb_t + unit - 1) / unit;
-  for (int u = tid; u < nunits; u += 1024) {
-    int k = 0;
-    for (int v = u * unit; v < min(nvb_t, (u + 1) * unit); ++v)
-      for (int b = 0; b < nb; ++b) k += keep[(size_t)b * nvb_t + v] != 0;
-    ucnt[u] = k;
+  const bool lds = nunits <= kLdsUnits;
+  int* cnts = lds ? lcnt : ucnt;
+  if (lds) {
+    for (int u = tid; u < nunits; u += 1024) lcnt[u] = 0;
+    __syncthreads();
+    for (int w = tid; w < nunits * nb; w += 1024) {
+      const int u = w % nunits, b = w / nunits;
+      const uint8_t* kr = keep + (size_t)b * nvb_t;
+      int k = 0;
+      for (int v = u * unit; v < min(nvb_t, (u + 1) * unit); ++v) k += kr[v] != 0;
+      if (k) atomicAdd(&lcnt[u], k);
+    }
+  } else {
+    for (int u = tid; u < nunits; u += 1024) {
+      int k = 0;
+      for (int v = u * unit; v < min(nvb_t, (u + 1) * unit); ++v)
+        for (int b = 0; b < nb; ++b) k += keep[(size_t)b * nvb_t + v] != 0;
+      ucnt[u] = k;
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -723,7 +742,7 @@ __global__ __launch_bounds__(1024) void chunk_plan_kernel(const uint8_t* __restr
     int c = 0, cnt = 0, u0 = 0;
     ch_vb[0] = 0;
     for (int u = 0; u < nunits; ++u) {
-      const int k = ucnt[u];
+      const int k = cnts[u];
       if (u > u0 && (cnt + k > S || u + 1 - u0 > span_u) && c + 1 < nchunks) {
         ch_vb[++c] = u * unit;
         cnt = 0;
