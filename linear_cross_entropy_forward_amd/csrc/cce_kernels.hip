@@ -823,6 +823,7 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_DMA_BYTES];
   __shared__ __attribute__((aligned(16))) float sbias[C::BM];
   __shared__ uint32_t sbm[kBlocksPerTile];  // kept 32x32 blocks: per vocab group, one bit per row group
+  __shared__ f32x4 scol[C::BN];             // per token column: lse, the coefficients, the target row
   // the chunk's kept tiles (listed in grouped order), XCD-contiguous runs of
   // the list: the same share of kept tiles on every XCD
   const int cnt = *tcount;
@@ -845,28 +846,41 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
   for (int i = 0; i < C::FM; ++i)
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x16{};
-  // per-column (slot) constants, fetched before the main loop so that their
-  // latency is hidden: lse in log2 units, the coefficients of p (scale times
-  // 1 + 2 lam LSE, the z-loss share) and of the one-hot target (scale times
-  // 1 - eps), and the target's row relative to this lane's first accumulator
-  // row (outside the tile: -1, which no row offset matches).  Ignored and
-  // padding slots have LSE +inf (p = 0) and scale 0: their G is exactly 0.
+  // per-column (slot) constants, staged in LDS before the main loop (one
+  // column per thread, their latency hidden behind the loop; held in
+  // registers across it they would be spilled): lse in log2 units, the
+  // coefficients of p (scale times 1 + 2 lam LSE, the z-loss share) and of
+  // the one-hot target (scale times 1 - eps), and the target's row in the
+  // tile (outside the tile: -1024, below any lane's row offset).  Ignored
+  // and padding slots have LSE +inf (p = 0) and scale 0: their G is exactly 0.
+  for (int j = threadIdx.x; j < C::BN; j += C::NT) {
+    const int n = n0 + j;  // < Npad: the grid covers the padded slots exactly
+    const float l = lse_c[n];
+    const float s = scale_c[n];
+    const int tg = tgt_c[n];
+    scol[j] = f32x4{l * kLog2e, s != 0.f ? s * (1.f + 2.f * lam * l) : 0.f, s * (1.f - eps),
+                    __builtin_bit_cast(float, (tg >= v0 && tg < v0 + C::BM) ? tg - v0 : -1024)};
+  }
+  mainloop_dma<C, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem, rowmap + n0);
+
+  // this lane's columns' constants (the main loop's barriers order the
+  // staging before these reads); trow: the target's row relative to the
+  // lane's first accumulator row (outside [0, WM) when the target is not in
+  // the wave's rows)
   AccMap<C> am;
   float lsel[C::FN], sc[C::FN], st[C::FN];
   int trow[C::FN];
 #pragma unroll
   for (int fn = 0; fn < C::FN; ++fn) {
-    const int n = n0 + am.colj(fn);  // < Npad: the grid covers the padded slots exactly
-    const float l = lse_c[n];
-    const float s = scale_c[n];
-    lsel[fn] = l * kLog2e;
-    sc[fn] = s != 0.f ? s * (1.f + 2.f * lam * l) : 0.f;
-    st[fn] = s * (1.f - eps);
-    const int tg = tgt_c[n];
-    trow[fn] = (tg >= v0 && tg < v0 + C::BM) ? tg - (v0 + am.row0) : -1;
+    const f32x4 k = scol[am.colj(fn)];
+    lsel[fn] = k[0];
+    sc[fn] = k[1];
+    st[fn] = k[2];
+    // (the element is copied out first: a bit cast of a vector element
+    // lvalue read element 0 in this compiler)
+    const float k3 = k[3];
+    trow[fn] = __builtin_bit_cast(int, k3) - am.row0;
   }
-  mainloop_dma<C, 1>(acc, A, B, (D + C::BK - 1) / C::BK, nullptr, smem, rowmap + n0);
-
   rsrc_t rg = make_rsrc(G, g_bytes);
   rsrc_t rgt = make_rsrc(Gt, gt_bytes);
   const int vl0 = tvl * C::BM;  // chunk-local column of the tile
@@ -1032,7 +1046,6 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
       if (v0 + r < V) db_part[(size_t)tn * V + v0 + r] = x;
     }
   };
-  float rs[C::FM][4][4] = {};  // this lane's share of each vocab row's token sum (for db)
   if constexpr (sizeof(T) == 2) {
     // bf16: G only (dC reads it with transposing LDS reads; G^T is not
     // formed), staged through LDS (free after the main loop) so that it
@@ -1069,12 +1082,6 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
         const int col = wrow + fm * 32 + 8 * (q - 1 + upper);
         *(__attribute__((address_space(3))) u32x4*)(tile + slot(am.colj(fn), col)) = u32x4{sl[0], sh[0], sl[1], sh[1]};
       }
-      if (sums) {  // the rounded values, as the contractions see them
-        rs[fm][q][0] += __builtin_bit_cast(float, lo << 16);
-        rs[fm][q][1] += __builtin_bit_cast(float, lo & 0xffff0000u);
-        rs[fm][q][2] += __builtin_bit_cast(float, hi << 16);
-        rs[fm][q][3] += __builtin_bit_cast(float, hi & 0xffff0000u);
-      }
     });
     publish_blocks();
     __syncthreads();
@@ -1100,10 +1107,39 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
           0, kStoreNT);
     }
     if (sums) {
+      // db: each vocab row's sum over the tile's tokens of the staged
+      // (rounded) values, as the contractions see them.  Thread (chunk ch,
+      // token block t) sums eight vocab rows over 32 token rows (a dropped
+      // block is not staged and adds nothing), then the eight token blocks'
+      // sums are added through LDS in a fixed order.
+      static_assert(C::NT == 256, "db sums: one thread per (8-row chunk, token block)");
+      const int ch = threadIdx.x & 31, t = threadIdx.x >> 5;
+      float ps[8] = {};
+      if (!filter || ((sbm[ch >> 2] >> t) & 1u)) {
+#pragma unroll 4
+        for (int r = 32 * t; r < 32 * t + 32; ++r) {
+          const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(r, 8 * ch));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            ps[2 * k] += __builtin_bit_cast(float, w[k] << 16);
+            ps[2 * k + 1] += __builtin_bit_cast(float, w[k] & 0xffff0000u);
+          }
+        }
+      }
       __syncthreads();  // the drain's LDS reads are done
-      db_sums(rs);
+      float* red = (float*)smem;  // [8 token blocks][BM]
+#pragma unroll
+      for (int k = 0; k < 8; ++k) red[t * C::BM + 8 * ch + k] = ps[k];
+      __syncthreads();
+      for (int r = threadIdx.x; r < C::BM; r += C::NT) {
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) x += red[w * C::BM + r];
+        if (v0 + r < V) db_part[(size_t)tn * V + v0 + r] = x;
+      }
     }
   } else {
+    float rs[C::FM][4][4] = {};  // this lane's share of each vocab row's token sum (for db)
     run([&](int fn, int fm, int q, int rl, const float (&g)[4]) __attribute__((always_inline)) {
       const int n = n0 + am.colj(fn);
       store4(rg, ((uint32_t)n * (uint32_t)Vc + (uint32_t)(vl0 + rl)) * (uint32_t)sizeof(T), g[0], g[1], g[2], g[3],
