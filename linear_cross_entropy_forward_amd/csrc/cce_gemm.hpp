@@ -505,8 +505,10 @@ __device__ __forceinline__ void lds_frag_at(Frag<float>& f, const lds_u8* st, ui
 // frag_init(rc0) / read(f, st, g, j) for fragment j (the 32 rows or columns
 // starting at rc0 + 32 j) of K group g.
 
-// K-major operand: ROWS rows of BK elements (128 bytes).
-template <class C, int ROWS>
+// K-major operand: ROWS rows of BK elements (128 bytes).  KFULL: every step
+// inside the K extent is whole (kdim a multiple of BK, step offsets multiples
+// of BK), so only a step past the end needs zeros, a scalar decision.
+template <class C, int ROWS, bool KFULL = false>
 struct DmaTile {
   using T = typename C::T;
   static constexpr int ROWB = C::BK * (int)sizeof(T);
@@ -519,12 +521,16 @@ struct DmaTile {
   static constexpr int KG = C::KGROUPS;
   // slot of logical chunk c in row r: c ^ swz(r)
   __device__ static constexpr int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-  uint32_t roff[PER];  // byte offset of the lane's row, kOOB past the valid rows
+  // byte offset of the lane's row, kOOB past the valid rows (KFULL: plus the
+  // lane's chunk)
+  uint32_t roff[PER];
   uint32_t kc[2];      // K offset (elements) of the lane's chunk within a step, by instruction parity
+  uint32_t mwave;      // LDS byte offset of the wave's first rows in a stage
   uint32_t flo[KG], fhi[KG];  // fragment chunk offsets by K group (fp32: two chunks)
   // With `rowmap`, tile row r is row rowmap[r] of the operand (-1: none).
   __device__ __forceinline__ void init(const Operand& op, const int* __restrict__ rowmap = nullptr) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    mwave = (uint32_t)(wave * PER) * 1024u;
     // instruction i fills rows 8 (wave PER + i) .. +7: row % 16 / 8 is the
     // parity of i (PER is even)
 #pragma unroll
@@ -533,16 +539,25 @@ struct DmaTile {
     for (int i = 0; i < PER; ++i) {
       const int row = 8 * (wave * PER + i) + (lane >> 3);
       const int src = row < op.rows ? (rowmap ? rowmap[row] : row) : -1;
-      roff[i] = src >= 0 ? (uint32_t)src * op.ld * (uint32_t)sizeof(T) : kOOB;
+      roff[i] = src >= 0 ? (uint32_t)src * op.ld * (uint32_t)sizeof(T) + (KFULL ? kc[i & 1] * (uint32_t)sizeof(T) : 0u)
+                         : kOOB;
     }
   }
   // DMA instruction i of this wave for the step at K offset k0 into the tile
-  // whose LDS byte address is `tile` (wave-uniform).
+  // whose LDS byte address is `tile` (wave-uniform).  KFULL: a step past the
+  // end adds kOOB, which puts every valid row's offset at or past 2^31,
+  // beyond any buffer (a kOOB row then wraps to an offset inside the buffer:
+  // it feeds only output rows past the tile, and only in such a step, where
+  // the other operand is zero).
   __device__ __forceinline__ void issue(int i, const Operand& op, int k0, uint32_t tile) const {
-    const uint32_t kk = (uint32_t)k0 + kc[i & 1];
-    const uint32_t off = (roff[i] == kOOB || kk >= (uint32_t)op.kdim) ? kOOB : roff[i] + kk * (uint32_t)sizeof(T);
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    dma16(op.desc, off, tile + (uint32_t)((wave * PER + i) * 1024));
+    if constexpr (KFULL) {
+      const uint32_t sk = (uint32_t)k0 < (uint32_t)op.kdim ? (uint32_t)k0 * (uint32_t)sizeof(T) : kOOB;
+      dma16(op.desc, roff[i] + sk, tile + mwave + (uint32_t)i * 1024u);
+    } else {
+      const uint32_t kk = (uint32_t)k0 + kc[i & 1];
+      const uint32_t off = (roff[i] == kOOB || kk >= (uint32_t)op.kdim) ? kOOB : roff[i] + kk * (uint32_t)sizeof(T);
+      dma16(op.desc, off, tile + mwave + (uint32_t)i * 1024u);
+    }
   }
   // Lane l of a fragment reads row rc0 + 32 j + l % 32 (rc0 a multiple of 8),
   // K elements 8 (l / 32) .. +7 of the group.
@@ -589,25 +604,35 @@ struct DmaTileMN {
   static_assert(BYTES % (1024 * NW) == 0 && PER % 2 == 0, "tile not evenly split");
   static constexpr int FN = NF;  // fragments per wave
   __device__ static constexpr int swz(int k) { return 2 * (k & 3) ^ 8 * (k & 1); }
-  uint32_t coff[2];  // byte offset of the lane's chunk in its K row, by instruction parity; kOOB past the columns
+  // by instruction parity: the byte offset of the lane's chunk in its K row
+  // (K row RPI * (the wave's first instruction) + lane / 32), kOOB past the
+  // columns
+  uint32_t vrow[2];
+  uint32_t mwave;  // LDS byte offset of the wave's first instruction's rows in a stage
   uint32_t foff[FN];
   __device__ __forceinline__ void init(const Operand& op) {
     const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int rsub = lane / 32, slot = lane & 31;
+    mwave = (uint32_t)(wave * PER) * 1024u;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int c = slot ^ swz(RPI * p + rsub);
-      coff[p] = c * 8 < op.rows ? (uint32_t)c * 16u : kOOB;
+      vrow[p] = c * 8 < op.rows ? (uint32_t)(RPI * wave * PER + rsub) * op.ld * (uint32_t)sizeof(T) + (uint32_t)c * 16u
+                                : kOOB;
     }
   }
+  // K rows k0 + RPI (wave PER + i) + lane / 32.  A step past the K extent
+  // (k0 >= kdim) reads zeros: its scalar part kOOB puts every offset at or
+  // past 2^31, beyond any buffer (the lane parts stay below 2^31 - the
+  // scalar, or are kOOB: their sum then wraps to an offset inside the buffer,
+  // which only reaches output columns past the tile and only in such a step,
+  // where the other operand is zero).  A step that straddles kdim occurs only
+  // at the end of the operand's rows, whose buffer ends there.
   __device__ __forceinline__ void issue(int i, const Operand& op, int k0, uint32_t tile) const {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int blk = wave * PER + i;
-    const uint32_t k = (uint32_t)(k0 + RPI * blk + lane / 32);
-    const uint32_t co = coff[i & 1];
-    const uint32_t off = (co == kOOB || k >= (uint32_t)op.kdim) ? kOOB : k * op.ld * (uint32_t)sizeof(T) + co;
-    dma16(op.desc, off, tile + (uint32_t)(blk * 1024));
+    const uint32_t rb = op.ld * (uint32_t)sizeof(T);
+    const uint32_t sk = (uint32_t)k0 < (uint32_t)op.kdim ? (uint32_t)k0 * rb : kOOB;
+    dma16(op.desc, vrow[i & 1] + (sk + (uint32_t)(RPI * i) * rb), tile + mwave + (uint32_t)i * 1024u);
   }
   __device__ __forceinline__ void frag_init(int rc0) {
     const int lane = threadIdx.x & 63;
@@ -654,22 +679,40 @@ struct DmaBlockK {
   static constexpr int NW = C::NT / 64;
   static constexpr int PER = 32 / NW;  // DMA instructions per wave per step
   static constexpr int KG = C::KGROUPS;
-  uint32_t lane_off;  // byte offset of the lane's 16 bytes within a half block (global)
+  // Half block d of a step (d = 2 k + half, stage block k = 8 h + t: token
+  // group t, vocab group 2 q + h) lies at slot * 131072 + q * 4096 + part(d)
+  // in G (block t * 8 + 2 q + h of the slot).  part() is additive over the
+  // wave's first half block and the instruction index (their bit fields do
+  // not overlap), so an instruction's offset is a per-wave lane constant plus
+  // one scalar.
+  __device__ static constexpr uint32_t part(int d) {
+    return (uint32_t)((((d >> 1) & 7) * 8 + (d >> 4)) * 2048 + (d & 1) * 1024);
+  }
+  static constexpr bool additive() {
+    for (int w = 0; w < NW; ++w)
+      for (int i = 0; i < PER; ++i)
+        if (part(w * PER + i) != part(w * PER) + part(i)) return false;
+    return true;
+  }
+  static_assert(additive(), "half-block offsets split into wave and instruction parts");
+  uint32_t vlane;      // the lane's 16 bytes within its half block, plus the wave's part
+  uint32_t mwave;      // LDS byte offset of the wave's first half block in a stage
   uint32_t fbase[KG];  // fragment 0's LDS offset by K group
   __device__ __forceinline__ void init(const Operand&) {
     const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     // lane l writes LDS chunk l % 4 of half-block row l / 4: logical chunk
     // (l % 4) ^ ((l >> 4) & 3) of that row
     const int r = lane >> 2, c = (lane & 3) ^ ((lane >> 4) & 3);
-    lane_off = (uint32_t)((r * 32 + c * 8) * 2);
+    vlane = (uint32_t)((r * 32 + c * 8) * 2) + part(wave * PER);
+    mwave = (uint32_t)(wave * PER) * 1024u;
   }
+  // ka = slot * 65536 + 64 q (q: the step within the slot's vocab tile);
+  // past the last step ka = kend, slot >= cap: every offset lies past the
+  // buffer (zeros)
   __device__ __forceinline__ void issue(int i, const Operand& op, int ka, uint32_t tile) const {
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int d = wave * PER + i, k = d >> 1, half = d & 1;
-    const int h = k >> 3, t = k & 7;
-    const uint32_t slot = (uint32_t)ka >> 16, q = ((uint32_t)ka >> 6) & 3u;
-    const uint32_t blk = slot * 64u + (uint32_t)t * 8u + 2u * q + (uint32_t)h;
-    dma16(op.desc, blk * 2048u + (uint32_t)half * 1024u + lane_off, tile + (uint32_t)d * 1024u);
+    const uint32_t sbase = ((uint32_t)ka >> 16) * 131072u + (((uint32_t)ka >> 6) & 3u) * 4096u;
+    dma16(op.desc, vlane + (sbase + part(i)), tile + mwave + (uint32_t)i * 1024u);
   }
   // rows rc0 + 32 j + lane % 32: token group rc0 / 32 + j; K group g: vocab
   // group half g / 2, chunk 2 (g % 2) + lane / 32
@@ -700,17 +743,23 @@ struct DmaBlockMN {
   static constexpr int PER = 32 / NW;
   static constexpr int KG = C::KGROUPS;
   uint32_t fbase[KG];
-  __device__ __forceinline__ void init(const Operand&) {}
-  __device__ __forceinline__ void issue(int i, const Operand& op, int ka, uint32_t tile) const {
+  uint32_t vlane;  // the lane's 16 bytes plus the wave's first half block
+  uint32_t mwave;  // LDS byte offset of the wave's first half block in a stage
+  __device__ __forceinline__ void init(const Operand&) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int d = wave * PER + i, k = d >> 1, half = d & 1;
-    const int h = k >> 3, v = k & 7;
-    const uint32_t slot = (uint32_t)ka >> 8, q = ((uint32_t)ka >> 6) & 3u;
-    const uint32_t blk = slot * 64u + (2u * q + (uint32_t)h) * 8u + (uint32_t)v;
-    dma16(op.desc, blk * 2048u + (uint32_t)half * 1024u + (uint32_t)lane * 16u, tile + (uint32_t)d * 1024u);
+    mwave = (uint32_t)(wave * PER) * 1024u;
+    vlane = (uint32_t)lane * 16u + mwave;
   }
-  // columns rc0 + 32 j ..: vocab group rc0 / 32 + j.  Within each group of
+  // Half block d of a step (stage block k = d / 2 = 8 h + v: vocab group v,
+  // token group 2 q + h) is block 16 q + k of the slot: the step's 32 KB are
+  // contiguous, at slot * 131072 + q * 32768, half block d at d * 1024.
+  // ka = slot * 256 + 64 q; past the last step slot >= cap: every offset lies
+  // past the buffer (zeros).
+  __device__ __forceinline__ void issue(int i, const Operand& op, int ka, uint32_t tile) const {
+    const uint32_t sbase = ((uint32_t)ka >> 8) * 131072u + (((uint32_t)ka >> 6) & 3u) * 32768u;
+    dma16(op.desc, vlane + (sbase + (uint32_t)i * 1024u), tile + mwave + (uint32_t)i * 1024u);
+  }  // columns rc0 + 32 j ..: vocab group rc0 / 32 + j.  Within each group of
   // 16 lanes, source lane s addresses K row 8 (lane / 32) + s / 4 of the K
   // group's 16 (plus 4 for the second read) and columns 16 ((lane / 16) % 2)
   // + 4 (s % 4) .. +3 of the block: output lane i then holds column 16
@@ -770,7 +819,7 @@ struct NoMask {
 // listed), so K offsets, block lists and masks follow it (the steps whose
 // blocks are all zero are left out).
 template <class C, int SPB, bool B_MN = false, bool A_MN = false, int NPARTS = (C::KGROUPS > 2 ? 3 : 1),
-          class MaskT = NoMask, bool SEPA = false, class ATile = void, bool STEPS = false>
+          class MaskT = NoMask, bool SEPA = false, class ATile = void, bool STEPS = false, bool BKFULL = false>
 __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const Operand& A, const Operand& B,
                                              int nsteps, const uint16_t* blocks, void* smem,
                                              const int* __restrict__ brow = nullptr, const MaskT& mask = MaskT{},
@@ -780,7 +829,7 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   using TA = std::conditional_t<!std::is_void_v<ATile>, ATile,
                                 std::conditional_t<A_MN, DmaTileMN<C, C::BM, C::FM>, DmaTile<C, C::BM>>>;
 
-  using TB = std::conditional_t<B_MN, DmaTileMN<C, C::BN, C::FN>, DmaTile<C, C::BN>>;
+  using TB = std::conditional_t<B_MN, DmaTileMN<C, C::BN, C::FN>, DmaTile<C, C::BN, BKFULL>>;
   constexpr int KG = C::KGROUPS;
   static_assert(KG % 2 == 0, "fragment buffers alternate per K group");
   static_assert(NPARTS >= 1 && NPARTS < KG, "the last DMA part must precede the wait");

@@ -1191,7 +1191,10 @@ __device__ __forceinline__ int collect_steps(int nfull, const F& nz, uint16_t* l
 // [nb][nvb_t] slot map) with mask word at bmask + mbase + i mstride.  Every
 // thread loads its candidates' flag, slot and word at once, so the three
 // come in one memory round trip.  count <= kMaxBlocks.
-template <int NT, bool SLOT, bool WORDS>
+struct NoPerm {
+  __device__ __forceinline__ static uint64_t apply(uint64_t w) { return w; }
+};
+template <int NT, bool SLOT, bool WORDS, class Perm = NoPerm>
 __device__ __forceinline__ int collect_kept(const uint8_t* __restrict__ keep, size_t kbase, int kstride, int count,
                                             const int* __restrict__ slot, const uint8_t* __restrict__ bmask,
                                             size_t mbase, int mstride, uint16_t* list, uint16_t* slots,
@@ -1230,7 +1233,7 @@ __device__ __forceinline__ int collect_kept(const uint8_t* __restrict__ keep, si
       const int pos = off + __popcll(bal & ((1ull << lane) - 1ull));
       list[pos] = (uint16_t)(r * NT + tid);
       if constexpr (SLOT) slots[pos] = (uint16_t)sl[r];
-      if constexpr (WORDS) words[pos] = mw[r];
+      if constexpr (WORDS) words[pos] = Perm::apply(mw[r]);
     }
     __syncthreads();  // wcnt is rewritten next pass; the lists are published
     base += tot;
@@ -1246,39 +1249,56 @@ __device__ __forceinline__ int collect_kept(const uint8_t* __restrict__ keep, si
 // ============================================================================
 typedef __attribute__((address_space(3))) uint64_t lds_u64;
 
+// Staged mask words are permuted (Perm::apply, when collect_kept stages
+// them) so that bit 32 wm + 8 sub + 4 h + fm is the block of the wave's
+// 32-row group fm (waves with row half wm) in K half h of step sub of the K
+// block: a step's eight bits for a wave are one byte, and a step holds a
+// kept block iff (w >> 8 sub) & 0x000000ff000000ff is nonzero.
+constexpr uint64_t kStepBits = 0x000000ff000000ffull;
+
 // dE: A rows are tokens (wave rows: 32-row groups 4 wm .. 4 wm + 3 of the
-// token block), K is vocabulary; sm[j] byte v is vocab group v of the K
-// block, bit t its token group t.
+// token block), K is vocabulary; the block-mask word of a K block has byte v
+// for vocab group v, bit t for token group t: group fm of wave row half wm
+// in K half h of step sub is bit 4 wm + fm of byte 2 sub + h.
 struct DEMask {
   static constexpr bool kActive = true;
   const lds_u64* sm;
-  int shift;  // 4 wm
+  int shift;  // 32 wm
+  __device__ __forceinline__ static uint64_t apply(uint64_t w) {
+    uint64_t o = 0;
+#pragma unroll
+    for (int b = 0; b < 64; ++b) {
+      const int wm = b >> 5, sub = (b >> 3) & 3, h = (b >> 2) & 1, fm = b & 3;
+      o |= ((w >> (8 * (2 * sub + h) + 4 * wm + fm)) & 1ull) << b;
+    }
+    return o;
+  }
   __device__ __forceinline__ uint32_t operator()(int s) const {
-    const uint64_t w = sm[s >> 2];
-    const int sub = s & 3;
-    const uint32_t b0 = (uint32_t)(w >> (16 * sub)) & 0xffu, b1 = (uint32_t)(w >> (16 * sub + 8)) & 0xffu;
-    return ((b0 >> shift) & 0xfu) | (((b1 >> shift) & 0xfu) << 4);
+    const uint32_t w = ((const __attribute__((address_space(3))) uint32_t*)sm)[2 * (s >> 2) + (shift >> 5)];
+    return (w >> (8 * (s & 3))) & 0xffu;
   }
 };
 
 // dC: A rows are vocabulary (wave rows: vocab groups 4 wm .. 4 wm + 3 of the
-// tile), K is tokens; sm[j] byte v is the tile's vocab group v for token
-// block j, bit t its token group t.
+// tile), K is tokens; the block-mask word of a token block has byte v for
+// the tile's vocab group v, bit t for token group t: group fm of wave row
+// half wm in K half h of step sub is bit 2 sub + h of byte 4 wm + fm.
 struct DCMask {
   static constexpr bool kActive = true;
   const lds_u64* sm;
   int shift;  // 32 wm
-  __device__ __forceinline__ uint32_t operator()(int s) const {
-    const uint32_t w = (uint32_t)(sm[s >> 2] >> shift);
-    const int t0 = 2 * (s & 3);
-    uint32_t m = 0;
+  __device__ __forceinline__ static uint64_t apply(uint64_t w) {
+    uint64_t o = 0;
 #pragma unroll
-    for (int fm = 0; fm < 4; ++fm) {
-      const uint32_t byte = (w >> (8 * fm)) & 0xffu;
-      m |= ((byte >> t0) & 1u) << fm;
-      m |= ((byte >> (t0 + 1)) & 1u) << (4 + fm);
+    for (int b = 0; b < 64; ++b) {
+      const int wm = b >> 5, sub = (b >> 3) & 3, h = (b >> 2) & 1, fm = b & 3;
+      o |= ((w >> (8 * (4 * wm + fm) + 2 * sub + h)) & 1ull) << b;
     }
-    return m;
+    return o;
+  }
+  __device__ __forceinline__ uint32_t operator()(int s) const {
+    const uint32_t w = ((const __attribute__((address_space(3))) uint32_t*)sm)[2 * (s >> 2) + (shift >> 5)];
+    return (w >> (8 * (s & 3))) & 0xffu;
   }
 };
 
@@ -1360,7 +1380,7 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
     // (A's K blocks: K rows slot * 256 .., G seen as cap * 256 token rows of
     // the 256 vocab columns) and, with block masks, the tile's block-mask
     // bytes of each (byte v: vocab group v, bit t: token group t)
-    const int nk = collect_kept<C::NT, kMN, MASK>(keep, (size_t)(cvb0 + tvl), nvb_t, nb, slot, bmask,
+    const int nk = collect_kept<C::NT, kMN, MASK, DCMask>(keep, (size_t)(cvb0 + tvl), nvb_t, nb, slot, bmask,
                                                   (size_t)(cvb0 + tvl) * kBlocksPerTile, nvg, blocks, ablk,
                                                   (uint64_t*)smask);
     const Operand A =
@@ -1379,26 +1399,28 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
       // the steps (64 tokens of a token block each) with a nonzero block:
       // bits 8 v + 2 (c % 4) + h of the step's mask word
       const int ns = collect_steps(
-          nk * SPB, [&](int c) { return ((smask[c >> 2] >> (2 * (c & 3))) & 0x0303030303030303ull) != 0; }, steps);
+          nk * SPB, [&](int c) { return ((smask[c >> 2] >> (8 * (c & 3))) & kStepBits) != 0; }, steps);
       const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
       const DCMask mk{(const lds_u64*)smask, 32 * wm};
       const uint16_t* bl = nk > 0 && blocks[nk - 1] == nk - 1 ? nullptr : blocks;
       // the step list costs about 5% of the loop: taken when it leaves out
       // at least an eighth of the steps
       if (8 * ns <= 7 * nk * SPB)
-        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>, true>(acc, A, B, ns, bl, smem, nullptr,
-                                                                              mk, ablk, kSlotRows, steps);
+        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>, true, true>(acc, A, B, ns, bl, smem,
+                                                                                    nullptr, mk, ablk, kSlotRows,
+                                                                                    steps);
       else
-        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>>(acc, A, B, nk * SPB, bl, smem, nullptr, mk,
-                                                                        ablk, kSlotRows);
+        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>, false, true>(acc, A, B, nk * SPB, bl, smem,
+                                                                                     nullptr, mk, ablk, kSlotRows);
     } else {
       // the kept token blocks are the first nk (no filtering effect on this
       // tile; compacted slots put the blocks of ignored rows last): contiguous
       // K for B
       const uint16_t* bl = nk > 0 && blocks[nk - 1] == nk - 1 ? nullptr : blocks;
       if constexpr (kMN)
-        mainloop_dma<C, SPB, false, kMN, 3, NoMask, true, DmaBlockMN<C>>(acc, A, B, nk * SPB, bl, smem, nullptr,
-                                                                        NoMask{}, ablk, kSlotRows);
+        mainloop_dma<C, SPB, false, kMN, 3, NoMask, true, DmaBlockMN<C>, false, true>(acc, A, B, nk * SPB, bl, smem,
+                                                                                     nullptr, NoMask{}, ablk,
+                                                                                     kSlotRows);
       else
         mainloop_dma<C, SPB, false, kMN>(acc, A, B, nk * SPB, bl, smem);
     }
@@ -1524,7 +1546,7 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
   // slot * 65536 from row n' * 256 of a slot; with block masks, the token
   // block's block-mask bytes of each: byte v vocab group v, bit t token
   // group t)
-  const int nall = collect_kept<C::NT, kDma, MASK>(keep, (size_t)tn * nvb_t + cvb0, 1, cnvb, slot, bmask,
+  const int nall = collect_kept<C::NT, kDma, MASK, DEMask>(keep, (size_t)tn * nvb_t + cvb0, 1, cnvb, slot, bmask,
                                                    (size_t)tn * nvg + (size_t)cvb0 * kBlocksPerTile,
                                                    kBlocksPerTile, blocks, ablk, (uint64_t*)smask);
   const int lo = (int)((int64_t)nall * s / splits), hi = (int)((int64_t)nall * (s + 1) / splits);
@@ -1554,7 +1576,7 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     // the steps (64 vocab of one of the split's vocab blocks each) with a
     // nonzero block: the 16 bits of the two vocab-group bytes 2 (c % 4),
     // 2 (c % 4) + 1
-    ns = collect_steps(nk * SPB, [&](int c) { return ((sml[c >> 2] >> (16 * (c & 3))) & 0xffffu) != 0; }, steps);
+    ns = collect_steps(nk * SPB, [&](int c) { return ((sml[c >> 2] >> (8 * (c & 3))) & kStepBits) != 0; }, steps);
   }
   auto loop = [&](const Operand& a, const Operand& b, const uint16_t* bl) {
     // the step's DMA in two parts (right after the barrier and in the first
@@ -1562,7 +1584,7 @@ __global__ __launch_bounds__(C::NT, 1) void dE_gemm_kernel(
     // MN-major classifier tile, slower for the K-major ones
     if constexpr (MASK) {
       const int wm = (int)(threadIdx.x >> 6) / C::WAVES_N;
-      const DEMask mk{(const lds_u64*)sml, 4 * wm};
+      const DEMask mk{(const lds_u64*)sml, 32 * wm};
       // the step list: when it leaves out at least an eighth of the steps
       if (8 * ns <= 7 * nk * SPB)
         mainloop_dma<C, SPB, true, false, 2, DEMask, true, DmaBlockK<C>, true>(acc, a, b, ns, bl, smem, nullptr, mk,
