@@ -921,16 +921,28 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   auto step = [&](int s, const lds_u8* st, const lds_u8* nx, uint32_t st_addr, uint32_t nx_addr, int k1) -> int {
     // wave-uniform: kept in a scalar register
     const int f1 = STEPS ? fn1 : (s + 1 < nsteps ? s + 1 : nsteps - 1), f2 = STEPS ? fn2 : s + 2;
-    const int f3 = STEPS ? __builtin_amdgcn_readfirstlane(full(s + 3)) : 0;
-    const int k2 = __builtin_amdgcn_readfirstlane(kofs_f(s + 2, f2));
     const int ka1 = SEPA ? kan : k1;
-    const int ka2 = SEPA ? __builtin_amdgcn_readfirstlane(kofs_a_f(s + 2, f2)) : k2;
-    const uint32_t mnext =
-        MaskT::kActive ? (uint32_t)__builtin_amdgcn_readfirstlane((int)mask(f1)) : 0xffffffffu;
+    // The LDS reads behind the step's later scalars (step s + 3's index, the
+    // K offsets of step s + 2, the mask of step s + 1) are issued in the first
+    // group, after its fragment wait, and made wave-uniform in the last
+    // group, which first needs them: their latency passes under the MFMAs
+    // instead of stalling the step.  (The raw list entries only: the
+    // arithmetic on them is scalar, after.)
+    int f3v = 0, bv = 0, av = 0;
+    uint32_t mv = 0;
+    int f3 = 0, k2 = 0, ka2 = 0;
+    uint32_t mnext = 0xffffffffu;
     auto group = [&](auto gc) {
       constexpr int g = decltype(gc)::value;
       constexpr bool last = g + 1 == KG;
       if constexpr (last) {
+        if constexpr (STEPS) f3 = __builtin_amdgcn_readfirstlane(f3v);
+        const bool in = s + 2 < nsteps;
+        const int sub = (f2 % SPB) * C::BK;
+        k2 = !in ? kend : blocks ? __builtin_amdgcn_readfirstlane(bv) * (SPB * C::BK) + sub : f2 * C::BK;
+        if constexpr (SEPA) ka2 = in ? __builtin_amdgcn_readfirstlane(av) * astride + sub : kend;
+        else ka2 = k2;
+        if constexpr (MaskT::kActive) mnext = (uint32_t)__builtin_amdgcn_readfirstlane((int)mv);
         wait_vmcnt<0>();
         __syncthreads();
       }
@@ -944,6 +956,12 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
       // group) are awaited once here, so that the MFMAs of each A fragment
       // sit under one scalar branch with no waits of their own.
       if constexpr (MaskT::kActive) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      if constexpr (g == 0) {
+        if constexpr (STEPS) f3v = full(s + 3);
+        bv = blocks ? (int)blocks[blk(f2)] : 0;
+        if constexpr (SEPA) av = (int)ablocks[blk(f2)];
+        if constexpr (MaskT::kActive) mv = mask(f1);
+      }
       [&]<int... Q>(std::integer_sequence<int, Q...>) {
         (
             [&] {
