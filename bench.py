@@ -38,10 +38,10 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "2c9386b0e0820e1e636f8070ea372a385d7f3d103f26357399f48a405873fe9d",
+    "source_sha256": "4b7f8bffdd24a087e5a029e1c146480a3d51914e7a16e4d164641bf96b31167c",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9355.2e6, "grad_tile": 1827.0e6, "dC_gemm": 2004.9e6, "dE_gemm": 1715.9e6,
+        "fwd_tile": 9214.9e6, "grad_tile": 1780.5e6, "dC_gemm": 2026.0e6, "dE_gemm": 1702.9e6,
         "rows": 121.3e6, "filter": 37.2e6, "transpose_e": 67.3e6, "dE_reduce": 100.7e6,
     },
 }
