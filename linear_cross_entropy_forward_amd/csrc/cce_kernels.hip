@@ -1112,11 +1112,10 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
       // token block t) sums eight vocab rows over 32 token rows (a dropped
       // block is not staged and adds nothing), then the eight token blocks'
       // sums are added through LDS in a fixed order.
-      static_assert(C::NT >= 256, "db sums: one thread per (8-row chunk, token block)");
+      static_assert(C::NT == 256, "db sums: one thread per (8-row chunk, token block)");
       const int ch = threadIdx.x & 31, t = threadIdx.x >> 5;
-      const bool summer = threadIdx.x < 256;
       float ps[8] = {};
-      if (summer && (!filter || ((sbm[ch >> 2] >> t) & 1u))) {
+      if (!filter || ((sbm[ch >> 2] >> t) & 1u)) {
 #pragma unroll 4
         for (int r = 32 * t; r < 32 * t + 32; ++r) {
           const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(tile + slot(r, 8 * ch));
@@ -1129,9 +1128,8 @@ __global__ __launch_bounds__(C::NT, 1) void grad_tile_kernel(
       }
       __syncthreads();  // the drain's LDS reads are done
       float* red = (float*)smem;  // [8 token blocks][BM]
-      if (summer)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) red[t * C::BM + 8 * ch + k] = ps[k];
+      for (int k = 0; k < 8; ++k) red[t * C::BM + 8 * ch + k] = ps[k];
       __syncthreads();
       for (int r = threadIdx.x; r < C::BM; r += C::NT) {
         float x = 0.f;
