@@ -547,8 +547,8 @@ struct DmaTile {
   // whose LDS byte address is `tile` (wave-uniform).  KFULL: a step past the
   // end adds kOOB, which puts every valid row's offset at or past 2^31,
   // beyond any buffer (a kOOB row then wraps to an offset inside the buffer:
-  // it feeds only output rows past the tile, and only in such a step, where
-  // the other operand is zero).
+  // it feeds only outputs past the tile, and only in such a step, where the
+  // other operand is zero).
   __device__ __forceinline__ void issue(int i, const Operand& op, int k0, uint32_t tile) const {
     if constexpr (KFULL) {
       const uint32_t sk = (uint32_t)k0 < (uint32_t)op.kdim ? (uint32_t)k0 * (uint32_t)sizeof(T) : kOOB;
@@ -622,13 +622,15 @@ struct DmaTileMN {
                                 : kOOB;
     }
   }
-  // K rows k0 + RPI (wave PER + i) + lane / 32.  A step past the K extent
-  // (k0 >= kdim) reads zeros: its scalar part kOOB puts every offset at or
-  // past 2^31, beyond any buffer (the lane parts stay below 2^31 - the
-  // scalar, or are kOOB: their sum then wraps to an offset inside the buffer,
-  // which only reaches output columns past the tile and only in such a step,
-  // where the other operand is zero).  A step that straddles kdim occurs only
-  // at the end of the operand's rows, whose buffer ends there.
+  // K rows k0 + RPI (wave PER + i) + lane / 32.  In a step inside the K
+  // extent the scalar part is below 2^31, so a lane past the columns (lane
+  // part kOOB) lands at or past 2^31, beyond any buffer (zeros).  A step past
+  // the extent (k0 >= kdim) takes kOOB as its scalar part, which puts every
+  // lane with a valid column past the buffer as well; a lane past the
+  // columns then wraps to an offset inside the buffer, but it feeds only
+  // output columns past the tile, and only in a step whose other operand is
+  // zero.  A step that straddles kdim occurs only at the end of the
+  // operand's rows, where its buffer ends.
   __device__ __forceinline__ void issue(int i, const Operand& op, int k0, uint32_t tile) const {
     const uint32_t rb = op.ld * (uint32_t)sizeof(T);
     const uint32_t sk = (uint32_t)k0 < (uint32_t)op.kdim ? (uint32_t)k0 * rb : kOOB;
