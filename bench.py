@@ -38,10 +38,10 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "4b7f8bffdd24a087e5a029e1c146480a3d51914e7a16e4d164641bf96b31167c",
+    "source_sha256": "f9d8fb0f2fe69f699ad167d8187a6387d2b176201eb1fe0f758e4cb555d3fa83",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9214.9e6, "grad_tile": 1780.5e6, "dC_gemm": 2026.0e6, "dE_gemm": 1702.9e6,
+        "fwd_tile": 9141.8e6, "grad_tile": 1775.3e6, "dC_gemm": 2022.4e6, "dE_gemm": 1702.9e6,
         "rows": 121.3e6, "filter": 37.2e6, "transpose_e": 67.3e6, "dE_reduce": 100.7e6,
     },
 }
