@@ -482,6 +482,13 @@ __device__ __forceinline__ void dma16(const u32x4& desc, uint32_t voff, uint32_t
                : "s"(lds_addr), "v"(voff), "s"(desc)
                : "memory", "m0");
 }
+// The same, for loads issued under a wave-uniform branch (the block-layout
+// tiles, whose loads of all-zero blocks are skipped): readfirstlane keeps
+// lds_addr in a scalar register, where the compiler would otherwise carry
+// it in a vector one across the branch.
+__device__ __forceinline__ void dma16_branch(const u32x4& desc, uint32_t voff, uint32_t lds_addr) {
+  dma16(desc, voff, __builtin_amdgcn_readfirstlane(lds_addr));
+}
 
 // s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding).
 template <int n>
@@ -714,7 +721,7 @@ struct DmaBlockK {
   // buffer (zeros)
   __device__ __forceinline__ void issue(int i, const Operand& op, int ka, uint32_t tile) const {
     const uint32_t sbase = ((uint32_t)ka >> 16) * 131072u + (((uint32_t)ka >> 6) & 3u) * 4096u;
-    dma16(op.desc, vlane + (sbase + part(i)), tile + mwave + (uint32_t)i * 1024u);
+    dma16_branch(op.desc, vlane + (sbase + part(i)), tile + mwave + (uint32_t)i * 1024u);
   }
   // rows rc0 + 32 j + lane % 32: token group rc0 / 32 + j; K group g: vocab
   // group half g / 2, chunk 2 (g % 2) + lane / 32
@@ -760,7 +767,7 @@ struct DmaBlockMN {
   // past the buffer (zeros).
   __device__ __forceinline__ void issue(int i, const Operand& op, int ka, uint32_t tile) const {
     const uint32_t sbase = ((uint32_t)ka >> 8) * 131072u + (((uint32_t)ka >> 6) & 3u) * 32768u;
-    dma16(op.desc, vlane + (sbase + (uint32_t)i * 1024u), tile + mwave + (uint32_t)i * 1024u);
+    dma16_branch(op.desc, vlane + (sbase + (uint32_t)i * 1024u), tile + mwave + (uint32_t)i * 1024u);
   }  // columns rc0 + 32 j ..: vocab group rc0 / 32 + j.  Within each group of
   // 16 lanes, source lane s addresses K row 8 (lane / 32) + s / 4 of the K
   // group's 16 (plus 4 for the second read) and columns 16 ((lane / 16) % 2)
@@ -807,6 +814,14 @@ struct NoMask {
   static constexpr bool kActive = false;
   __device__ __forceinline__ uint32_t operator()(int) const { return 0xffffffffu; }
 };
+// MaskT::kSkipA (a block-layout A tile): mask.raw(f) is an LDS read of the
+// 64-bit word behind step f's bits and MaskT::dma_bits(lo, hi, f), from its
+// two (wave-uniform) halves, the step's sixteen A-stage blocks, bit k for
+// stage block k (half blocks 2 k, 2 k + 1).
+template <class M, class = void>
+struct SkipA : std::false_type {};
+template <class M>
+struct SkipA<M, std::void_t<decltype(M::kSkipA)>> : std::bool_constant<M::kSkipA> {};
 
 //
 // With `ablocks` (SEPA), the A operand takes its own K blocks: step s reads A
@@ -876,18 +891,50 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   // B rows through `brow` (K-major B only): the gathered token rows
   if constexpr (B_MN) tb.init(B);
   else tb.init(B, brow);
-  // ka: A's K offset, kb: B's (the same without SEPA)
-  auto dma = [&](int d, int ka, int kb, uint32_t st) {
-    if (d < TA::PER) ta.issue(d, A, ka, st);
-    else tb.issue(d - TA::PER, B, kb, st + TA::BYTES);
+  // With kSkipA, the A loads of a stage block whose bit is clear (an all-zero
+  // 32x32 block of the gradient, whose MFMAs the mask skips) are not issued
+  // at all: no request, no LDS write; the stage keeps stale bytes there,
+  // which no MFMA reads.  Steps past the end load every block (zeros).  The
+  // wave issues half blocks wave * PER .. + PER - 1, i.e. stage blocks from
+  // wave * PER / 2 on: wb = the step's bits shifted by that.
+  constexpr bool kSkipA = SkipA<MaskT>::value;
+  static_assert(!kSkipA || TA::PER % 2 == 0, "whole blocks per wave");
+  const int wsh = kSkipA ? __builtin_amdgcn_readfirstlane(wave) * (TA::PER / 2) : 0;
+  // step s (full index f): the raw word is read into vector registers,
+  // made wave-uniform, then decoded
+  auto uniform_bits = [&](int s, int f, uint64_t raw) -> uint32_t {
+    if constexpr (kSkipA) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)raw);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(raw >> 32));
+      return s < nsteps ? MaskT::dma_bits(lo, hi, __builtin_amdgcn_readfirstlane(f)) : 0xffffffffu;
+    } else {
+      return 0xffffffffu;
+    }
+  };
+  // the list entry of step s (past the end: the last, unused)
+  auto raw_at = [&](int f) -> uint64_t {
+    if constexpr (kSkipA) return mask.raw(f < nsteps || STEPS ? f : nsteps - 1);
+    else return 0;
+  };
+  // ka: A's K offset, kb: B's (the same without SEPA); wb: the A blocks to load
+  auto dma = [&](int d, int ka, int kb, uint32_t st, uint32_t wb) {
+    if (d < TA::PER) {
+      if (!kSkipA || ((wb >> (d >> 1)) & 1u)) ta.issue(d, A, ka, st);
+    } else {
+      tb.issue(d - TA::PER, B, kb, st + TA::BYTES);
+    }
   };
   // prologue: step 0 whole, part 0 of step 1 (its other parts follow in step 0)
   constexpr int P0 = NDMA / NPARTS;
+  const uint32_t wb0 = uniform_bits(0, full(0), raw_at(full(0))) >> wsh;
+  uint32_t db1 = uniform_bits(1, full(1), raw_at(full(1)));
 #pragma unroll
-  for (int d = 0; d < NDMA; ++d) dma(d, kofs_a(0), kofs(0), base_addr);
+  for (int d = 0; d < NDMA; ++d) dma(d, kofs_a(0), kofs(0), base_addr, wb0);
 #pragma unroll
-  for (int d = 0; d < P0; ++d) dma(d, kofs_a(1), kofs(1), base_addr + STAGE);
-  wait_vmcnt<P0>();  // step 0 has landed
+  for (int d = 0; d < P0; ++d) dma(d, kofs_a(1), kofs(1), base_addr + STAGE, db1 >> wsh);
+  // step 0 has landed (with kSkipA the count of step 1's loads varies: all)
+  if constexpr (kSkipA) wait_vmcnt<0>();
+  else wait_vmcnt<P0>();
   __syncthreads();
 
   ta.frag_init(wm * C::WM);
@@ -934,6 +981,8 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
     uint32_t mv = 0;
     int f3 = 0, k2 = 0, ka2 = 0;
     uint32_t mnext = 0xffffffffu;
+    uint64_t dv = 0;  // the raw word behind step s + 2's A blocks
+    uint32_t db2 = 0xffffffffu;
     auto group = [&](auto gc) {
       constexpr int g = decltype(gc)::value;
       constexpr bool last = g + 1 == KG;
@@ -945,6 +994,7 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
         if constexpr (SEPA) ka2 = in ? __builtin_amdgcn_readfirstlane(av) * astride + sub : kend;
         else ka2 = k2;
         if constexpr (MaskT::kActive) mnext = (uint32_t)__builtin_amdgcn_readfirstlane((int)mv);
+        if constexpr (kSkipA) db2 = uniform_bits(s + 2, f2, dv);
         wait_vmcnt<0>();
         __syncthreads();
       }
@@ -963,6 +1013,7 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
         bv = blocks ? (int)blocks[blk(f2)] : 0;
         if constexpr (SEPA) av = (int)ablocks[blk(f2)];
         if constexpr (MaskT::kActive) mv = mask(f1);
+        if constexpr (kSkipA) dv = raw_at(f2);
       }
       [&]<int... Q>(std::integer_sequence<int, Q...>) {
         (
@@ -994,8 +1045,8 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
               constexpr int d1 = (b + 1) * dn / HALF < dn ? (b + 1) * dn / HALF : dn;
 #pragma unroll
               for (int d = d0; d < d1; ++d) {
-                if constexpr (last) dma(dlo + d, ka2, k2, st_addr);
-                else dma(dlo + d, ka1, k1, nx_addr);
+                if constexpr (last) dma(dlo + d, ka2, k2, st_addr, db2 >> wsh);
+                else dma(dlo + d, ka1, k1, nx_addr, db1 >> wsh);
               }
               __builtin_amdgcn_sched_barrier(0);
             }(),
@@ -1006,6 +1057,7 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
       (group(std::integral_constant<int, G>{}), ...);
     }(std::make_integer_sequence<int, KG>{});
     mcur = mnext;
+    db1 = db2;
     if constexpr (SEPA) kan = ka2;
     if constexpr (STEPS) {
       fn1 = f2;

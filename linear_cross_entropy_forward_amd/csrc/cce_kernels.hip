@@ -1256,14 +1256,29 @@ typedef __attribute__((address_space(3))) uint64_t lds_u64;
 // kept block iff (w >> 8 sub) & 0x000000ff000000ff is nonzero.
 constexpr uint64_t kStepBits = 0x000000ff000000ffull;
 
+// The A-stage blocks of step f (for mainloop_dma's kSkipA) from the staged
+// word's halves: stage block k = 8 h + 4 wm + fm (K half h, wave row half
+// wm, group fm: the order of the block-layout DMA tiles) is bit 8 sub + 4 h +
+// fm of half wm, sub = f % 4.
+__device__ __forceinline__ uint32_t stage_block_bits(uint32_t lo, uint32_t hi, int f) {
+  const int sh = 8 * (f & 3);
+  const uint32_t a = (lo >> sh) & 0xffu, b = (hi >> sh) & 0xffu;
+  return (a & 0xfu) | ((b & 0xfu) << 4) | ((a >> 4) << 8) | ((b >> 4) << 12);
+}
+
 // dE: A rows are tokens (wave rows: 32-row groups 4 wm .. 4 wm + 3 of the
 // token block), K is vocabulary; the block-mask word of a K block has byte v
 // for vocab group v, bit t for token group t: group fm of wave row half wm
 // in K half h of step sub is bit 4 wm + fm of byte 2 sub + h.
 struct DEMask {
   static constexpr bool kActive = true;
+  static constexpr bool kSkipA = true;
   const lds_u64* sm;
   int shift;  // 32 wm
+  __device__ __forceinline__ uint64_t raw(int f) const { return sm[f >> 2]; }
+  __device__ __forceinline__ static uint32_t dma_bits(uint32_t lo, uint32_t hi, int f) {
+    return stage_block_bits(lo, hi, f);
+  }
   __device__ __forceinline__ static uint64_t apply(uint64_t w) {
     uint64_t o = 0;
 #pragma unroll
@@ -1285,8 +1300,13 @@ struct DEMask {
 // half wm in K half h of step sub is bit 2 sub + h of byte 4 wm + fm.
 struct DCMask {
   static constexpr bool kActive = true;
+  static constexpr bool kSkipA = true;
   const lds_u64* sm;
   int shift;  // 32 wm
+  __device__ __forceinline__ uint64_t raw(int f) const { return sm[f >> 2]; }
+  __device__ __forceinline__ static uint32_t dma_bits(uint32_t lo, uint32_t hi, int f) {
+    return stage_block_bits(lo, hi, f);
+  }
   __device__ __forceinline__ static uint64_t apply(uint64_t w) {
     uint64_t o = 0;
 #pragma unroll
