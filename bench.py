@@ -38,10 +38,10 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "f9d8fb0f2fe69f699ad167d8187a6387d2b176201eb1fe0f758e4cb555d3fa83",
+    "source_sha256": "f4dc6e5fd768e99ebe3f123acf3f49c0767528e0797b354d4aaf25378ae51f73",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9141.8e6, "grad_tile": 1775.3e6, "dC_gemm": 2022.4e6, "dE_gemm": 1702.9e6,
+        "fwd_tile": 9125.8e6, "grad_tile": 1774.6e6, "dC_gemm": 1664.6e6, "dE_gemm": 1058.3e6,
         "rows": 121.3e6, "filter": 37.2e6, "transpose_e": 67.3e6, "dE_reduce": 100.7e6,
     },
 }
