@@ -38,10 +38,10 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "f4dc6e5fd768e99ebe3f123acf3f49c0767528e0797b354d4aaf25378ae51f73",
+    "source_sha256": "4e573a800d4fa9797be2b9d8154a84ded91ed8f01c8fa1d8c089e0c7ddaafbf1",
     "workload": "llama8b",
     "bytes_per_launch": {
-        "fwd_tile": 9125.8e6, "grad_tile": 1774.6e6, "dC_gemm": 1664.6e6, "dE_gemm": 1058.3e6,
+        "fwd_tile": 9184.8e6, "grad_tile": 1778.7e6, "dC_gemm": 1658.6e6, "dE_gemm": 1058.8e6,
         "rows": 121.3e6, "filter": 37.2e6, "transpose_e": 67.3e6, "dE_reduce": 100.7e6,
     },
 }

@@ -1424,13 +1424,15 @@ __global__ __launch_bounds__(C::NT, 1) void dC_gemm_kernel(
       const DCMask mk{(const lds_u64*)smask, 32 * wm};
       const uint16_t* bl = nk > 0 && blocks[nk - 1] == nk - 1 ? nullptr : blocks;
       // the step list costs about 5% of the loop: taken when it leaves out
-      // at least an eighth of the steps
+      // at least an eighth of the steps.  The step's DMA in two parts
+      // (after the barrier and in the first K group): with the loads of
+      // all-zero G blocks skipped, measured 1-4% faster than three.
       if (8 * ns <= 7 * nk * SPB)
-        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>, true, true>(acc, A, B, ns, bl, smem,
+        mainloop_dma<C, SPB, false, kMN, 2, DCMask, true, DmaBlockMN<C>, true, true>(acc, A, B, ns, bl, smem,
                                                                                     nullptr, mk, ablk, kSlotRows,
                                                                                     steps);
       else
-        mainloop_dma<C, SPB, false, kMN, 3, DCMask, true, DmaBlockMN<C>, false, true>(acc, A, B, nk * SPB, bl, smem,
+        mainloop_dma<C, SPB, false, kMN, 2, DCMask, true, DmaBlockMN<C>, false, true>(acc, A, B, nk * SPB, bl, smem,
                                                                                      nullptr, mk, ablk, kSlotRows);
     } else {
       // the kept token blocks are the first nk (no filtering effect on this
