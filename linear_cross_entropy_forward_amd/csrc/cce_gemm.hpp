@@ -900,8 +900,9 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   constexpr bool kSkipA = SkipA<MaskT>::value;
   static_assert(!kSkipA || TA::PER % 2 == 0, "whole blocks per wave");
   const int wsh = kSkipA ? __builtin_amdgcn_readfirstlane(wave) * (TA::PER / 2) : 0;
-  // step s (full index f): the raw word is read into vector registers,
-  // made wave-uniform, then decoded
+  // The A blocks to load for step s (full index f), from the mask word
+  // `raw` (read from LDS into vector registers): made wave-uniform, then
+  // decoded; every block for a step past the end
   auto uniform_bits = [&](int s, int f, uint64_t raw) -> uint32_t {
     if constexpr (kSkipA) {
       const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)raw);
@@ -911,7 +912,8 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
       return 0xffffffffu;
     }
   };
-  // the list entry of step s (past the end: the last, unused)
+  // the mask word of full step f (without a step list, an index past the
+  // end reads the last word, whose bits are then not used)
   auto raw_at = [&](int f) -> uint64_t {
     if constexpr (kSkipA) return mask.raw(f < nsteps || STEPS ? f : nsteps - 1);
     else return 0;
@@ -932,7 +934,8 @@ __device__ __forceinline__ void mainloop_dma(f32x16 (&acc)[C::FM][C::FN], const 
   for (int d = 0; d < NDMA; ++d) dma(d, kofs_a(0), kofs(0), base_addr, wb0);
 #pragma unroll
   for (int d = 0; d < P0; ++d) dma(d, kofs_a(1), kofs(1), base_addr + STAGE, db1 >> wsh);
-  // step 0 has landed (with kSkipA the count of step 1's loads varies: all)
+  // step 0 has landed (with kSkipA the number of step 1's loads in flight
+  // varies, so all are awaited)
   if constexpr (kSkipA) wait_vmcnt<0>();
   else wait_vmcnt<P0>();
   __syncthreads();
